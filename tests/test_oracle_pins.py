@@ -1,0 +1,503 @@
+"""Pins of the CPU oracle to what the pages and the mathematics fix.
+
+None of these tests re-types the oracle's formulas: each compares the oracle
+with a hand-derived value, a library routine (scipy / numpy), a closed-form
+law, a brute-force enumeration, or a statistical test of the losslessness
+claim.  All run on the CPU.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy import special, stats
+
+import oracle
+from synthetic import f32_to_bf16_bits, bf16_bits_to_f32
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+S, G, K, TR = oracle.STOCHASTIC, oracle.GREEDY, oracle.NKL, oracle.TREE_GREEDY
+
+
+def run(target, draft, gamma, tokens, temps=None, ua=None, ur=None, mode=S, delta=0.15, parents=None,
+        dtype="f32", max_gamma=None, total=None):
+    gamma = np.asarray(gamma, np.int32)
+    B = len(gamma)
+    R_d = int(gamma[gamma > 0].sum())
+    if temps is None:
+        temps = np.ones(B, np.float32)
+    if ua is None:
+        ua = np.zeros(R_d, np.float32)
+    if ur is None:
+        ur = np.zeros(B, np.float32)
+    return oracle.verify(np.asarray(target), None if draft is None else np.asarray(draft), dtype, gamma,
+                         np.asarray(tokens, np.int32), np.asarray(temps, np.float32), np.asarray(ua, np.float32),
+                         np.asarray(ur, np.float32), mode, delta, parents, max_gamma, total)
+
+
+# --------------------------------------------------------------------------
+# worked example (closed forms), modified rejection sampling
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1.0, 2.0, 0.5])
+def test_worked_example_v4(T):
+    g = json.load(open(os.path.join(GOLD, "worked_v4.json")))
+    p, q, bonus = (np.array(g[k]) for k in ("p", "q", "bonus"))
+    tgt = (T * np.log(np.stack([p, bonus]))).astype(np.float32)
+    drf = (T * np.log(q[None, :])).astype(np.float32)
+    for case in g["cases"]:
+        r = run(tgt, drf, [1], [g["draft_token"]], [T], [case["u_accept"]], [case["u_resample"]])
+        assert r.num_accepted[0] == case["num_accepted"], case
+        assert r.tokens.tolist() == case["tokens"], case
+        assert abs(r.alpha[0] - g["alpha"]) < 1e-6
+        assert abs(r.p_x[0] - g["p_x"]) < 1e-6 and abs(r.q_x[0] - g["q_x"]) < 1e-6
+        if case["num_accepted"] == 0:
+            assert abs(r.resid_mass[0] - g["resid_mass"]) < 1e-6
+        else:
+            assert r.resid_mass[0] == 1.0
+
+
+def test_worked_example_bf16_matches_f32():
+    """bf16 inputs widen exactly: the same values given as bf16 and as fp32 give
+    identical results (pins the bf16 decode)."""
+    rng = np.random.default_rng(5)
+    V, gam = 300, 3
+    t = (3 * rng.standard_normal((gam + 1, V))).astype(np.float32)
+    d = (t[:gam] + rng.standard_normal((gam, V))).astype(np.float32)
+    tb, db = f32_to_bf16_bits(t), f32_to_bf16_bits(d)
+    tf, df = bf16_bits_to_f32(tb), bf16_bits_to_f32(db)
+    x = rng.integers(0, V, gam)
+    ua = rng.random(gam).astype(np.float32)
+    ur = rng.random(1).astype(np.float32)
+    a = run(tb, db, [gam], x, [0.8], ua, ur, dtype="bf16")
+    b = run(tf, df, [gam], x, [0.8], ua, ur, dtype="f32")
+    assert a.tokens.tolist() == b.tokens.tolist()
+    np.testing.assert_array_equal(a.p_x, b.p_x)
+    np.testing.assert_array_equal(a.alpha, b.alpha)
+    # and a decode mistake (e.g. reading the low byte) would change p_x
+    ref = special.softmax(tf[0].astype(np.float64) / np.float64(np.float32(0.8)))[x[0]]
+    assert abs(a.p_x[0] / ref - 1) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# log-softmax, alpha and residual against scipy on random rows
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [0.6, 1.0, 1.7])
+def test_probabilities_match_scipy(T):
+    rng = np.random.default_rng(int(T * 10))
+    V, gam, B = 777, 5, 6
+    t = (3 * rng.standard_normal((B * (gam + 1), V))).astype(np.float32)
+    d = np.concatenate([t[b * (gam + 1): b * (gam + 1) + gam] for b in range(B)]) + \
+        rng.standard_normal((B * gam, V)).astype(np.float32)
+    d = d.astype(np.float32)
+    x = rng.integers(0, V, B * gam)
+    ua = rng.random(B * gam).astype(np.float32)
+    ur = rng.random(B).astype(np.float32)
+    temps = np.full(B, T, np.float32)
+    r = run(t, d, [gam] * B, x, temps, ua, ur)
+    Td = np.float64(np.float32(T))
+    for b in range(B):
+        for i in range(gam):
+            P = special.softmax(t[b * (gam + 1) + i].astype(np.float64) / Td)
+            Q = special.softmax(d[b * gam + i].astype(np.float64) / Td)
+            k = b * gam + i
+            assert abs(r.p_x[k] / P[x[k]] - 1) < 1e-11
+            assert abs(r.q_x[k] / Q[x[k]] - 1) < 1e-11
+            assert abs(r.alpha[k] - min(1.0, P[x[k]] / Q[x[k]])) < 1e-12
+        # the decision and the terminal draw
+        n = r.num_accepted[b]
+        alphas = [min(1.0, r.p_x[b * gam + i] / r.q_x[b * gam + i]) for i in range(gam)]
+        exp_n = next((i for i in range(gam) if not (ua[b * gam + i] <= alphas[i])), gam)
+        assert n == exp_n
+        assert r.tokens[b * (gam + 1): b * (gam + 1) + n].tolist() == x[b * gam: b * gam + n].tolist()
+        P = special.softmax(t[b * (gam + 1) + n].astype(np.float64) / Td)
+        if n < gam:
+            Q = special.softmax(d[b * gam + n].astype(np.float64) / Td)
+            # identity: sum max(0, p - q) = 1 - sum min(p, q)
+            assert abs(r.resid_mass[b] - (1 - np.minimum(P, Q).sum())) < 1e-12
+            w = np.maximum(0, P - Q)
+        else:
+            w = P
+        cdf = np.cumsum(w) / w.sum()
+        u = np.float64(ur[b])
+        ystar = int(np.searchsorted(cdf, u, side="right"))
+        lo = cdf[ystar - 1] if ystar > 0 else 0.0
+        if min(u - lo, cdf[ystar] - u) > 1e-9:  # margin computed here, not by the oracle
+            assert r.tokens[b * (gam + 1) + n] == ystar
+        assert (r.tokens[b * (gam + 1) + n + 1: (b + 1) * (gam + 1)] == -1).all()
+
+
+# --------------------------------------------------------------------------
+# q == p: everything accepted, bonus drawn from p_gamma
+# --------------------------------------------------------------------------
+
+def test_q_equals_p_accepts_everything():
+    rng = np.random.default_rng(11)
+    V, gam, B = 64, 4, 4000
+    rows = (3 * rng.standard_normal((gam + 1, V))).astype(np.float32)
+    t = np.tile(rows, (B, 1))
+    d = np.tile(rows[:gam], (B, 1))
+    x = rng.integers(0, V, B * gam)  # any tokens: alpha = 1 exactly
+    ua = rng.random(B * gam).astype(np.float32)
+    ur = rng.random(B).astype(np.float32)
+    r = run(t, d, [gam] * B, x, np.full(B, 0.9, np.float32), ua, ur)
+    assert (r.num_accepted == gam).all()
+    assert (r.alpha == 1.0).all()
+    tok = r.tokens.reshape(B, gam + 1)
+    assert (tok[:, :gam] == x.reshape(B, gam)).all()
+    # bonus ~ p_gamma (chi-square)
+    P = special.softmax(rows[gam].astype(np.float64) / np.float64(np.float32(0.9)))
+    obs = np.bincount(tok[:, gam], minlength=V)
+    keep = P * B >= 5
+    exp = np.concatenate([P[keep] * B, [P[~keep].sum() * B]])
+    ob = np.concatenate([obs[keep], [obs[~keep].sum()]])
+    if exp[-1] == 0:
+        exp, ob = exp[:-1], ob[:-1]
+    assert stats.chisquare(ob, exp * ob.sum() / exp.sum()).pvalue > 1e-3
+
+
+# --------------------------------------------------------------------------
+# accepted-count law (closed form): P(n=k) = a^k (1-a), P(n=gamma) = a^gamma
+# --------------------------------------------------------------------------
+
+def test_accepted_count_law():
+    rng = np.random.default_rng(3)
+    V, gam, B = 8, 4, 200_000
+    t_row = (3 * rng.standard_normal(V)).astype(np.float32)
+    d_row = (t_row + rng.standard_normal(V)).astype(np.float32)
+    P = special.softmax(t_row.astype(np.float64))
+    Q = special.softmax(d_row.astype(np.float64))
+    a = np.minimum(P, Q).sum()
+    t = np.tile(t_row, (B * (gam + 1), 1))
+    d = np.tile(d_row, (B * gam, 1))
+    x = rng.choice(V, size=B * gam, p=Q)
+    r = run(t, d, [gam] * B, x, None, rng.random(B * gam).astype(np.float32),
+            rng.random(B).astype(np.float32))
+    obs = np.bincount(r.num_accepted, minlength=gam + 1)
+    law = np.array([a ** k * (1 - a) for k in range(gam)] + [a ** gam])
+    assert abs(law.sum() - 1) < 1e-12
+    assert stats.chisquare(obs, law * B).pvalue > 1e-3
+
+
+# --------------------------------------------------------------------------
+# losslessness at V = 8, gamma = 4, 10^6 trials; negative control
+# --------------------------------------------------------------------------
+
+def _lossless_setup(n_trials, seed=2026):
+    rng = np.random.default_rng(seed)
+    V, gam = 8, 4
+    t_rows = (3 * rng.standard_normal((gam + 1, V))).astype(np.float32)
+    d_rows = (t_rows[:gam] + rng.standard_normal((gam, V))).astype(np.float32)
+    P = special.softmax(t_rows.astype(np.float64), axis=1)
+    Q = special.softmax(d_rows.astype(np.float64), axis=1)
+    x = np.empty((n_trials, gam), np.int32)
+    for i in range(gam):
+        x[:, i] = rng.choice(V, size=n_trials, p=Q[i])
+    ua = rng.random(n_trials * gam).astype(np.float32)
+    ur = rng.random(n_trials).astype(np.float32)
+    return V, gam, t_rows, d_rows, P, Q, x, ua, ur
+
+
+def _position_pvalues(tok, n_acc, P, gam):
+    """p-values of 'token at slot k given the step reached k ~ p_k'."""
+    pv = []
+    for k in range(gam + 1):
+        reached = n_acc >= k
+        obs = np.bincount(tok[reached, k], minlength=P.shape[1])
+        pv.append(stats.chisquare(obs, P[k] * reached.sum()).pvalue)
+    return pv
+
+
+def test_losslessness_chi_square():
+    n = 1_000_000
+    V, gam, t_rows, d_rows, P, Q, x, ua, ur = _lossless_setup(n)
+    t = np.tile(t_rows, (n, 1))
+    d = np.tile(d_rows, (n, 1))
+    r = run(t, d, [gam] * n, x.ravel(), None, ua, ur)
+    tok = r.tokens.reshape(n, gam + 1)
+    pv = _position_pvalues(tok, r.num_accepted, P, gam)
+    alpha = 1e-3 / len(pv)  # Bonferroni
+    assert min(pv) > alpha, pv
+    # first emitted token ~ p_0 unconditionally
+    assert stats.chisquare(np.bincount(tok[:, 0], minlength=V), P[0] * n).pvalue > 1e-3
+
+    # Negative control: the listing's correction (emit argmax of p_j instead of
+    # redrawing from the residual) is not lossless, and the test must see it.
+    bad = tok.copy()
+    for k in range(gam):
+        rej = r.num_accepted == k
+        bad[rej, k] = int(np.argmax(P[k]))
+    pv_bad = _position_pvalues(bad, r.num_accepted, P, gam)
+    assert min(pv_bad) < 1e-30, pv_bad
+
+
+# --------------------------------------------------------------------------
+# greedy mode and ties (golden)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_greedy_golden(dtype):
+    g = json.load(open(os.path.join(GOLD, "greedy_tree_small.json")))["greedy"]
+    rows = np.array(g["rows"], np.float32)
+    tgt = f32_to_bf16_bits(rows) if dtype == "bf16" else rows
+    for case in g["cases"]:
+        r = run(tgt, None, [4], case["drafts"], mode=G, dtype=dtype)
+        assert r.num_accepted[0] == case["num_accepted"]
+        assert r.tokens.tolist() == case["tokens"]
+
+
+def test_greedy_argmax_drafts_fully_accepted_and_ties():
+    rng = np.random.default_rng(8)
+    V, gam, B = 513, 6, 50
+    # heavy ties: integer logits on a small range
+    t = rng.integers(-3, 4, size=(B * (gam + 1), V)).astype(np.float32)
+    x = np.concatenate([np.argmax(t[b * (gam + 1): b * (gam + 1) + gam], axis=1) for b in range(B)])
+    r = run(t, None, [gam] * B, x, mode=G)
+    assert (r.num_accepted == gam).all()
+    tok = r.tokens.reshape(B, gam + 1)
+    assert (tok[:, :gam] == x.reshape(B, gam)).all()
+    assert (tok[:, gam] == np.argmax(t[gam::gam + 1], axis=1)).all()
+    # break position j of each request: emitted token is np.argmax (first max)
+    j = rng.integers(0, gam, B)
+    x2 = x.copy().reshape(B, gam)
+    for b in range(B):
+        x2[b, j[b]] = (x2[b, j[b]] + 1) % V
+    r2 = run(t, None, [gam] * B, x2.ravel(), mode=G)
+    assert (r2.num_accepted == j).all()
+    tok2 = r2.tokens.reshape(B, gam + 1)
+    for b in range(B):
+        assert tok2[b, j[b]] == np.argmax(t[b * (gam + 1) + j[b]])
+        assert (tok2[b, j[b] + 1:] == -1).all()
+
+
+# --------------------------------------------------------------------------
+# NKL
+# --------------------------------------------------------------------------
+
+def test_nkl_identical_rows_zero():
+    rng = np.random.default_rng(1)
+    V, gam, B = 1000, 5, 4
+    t = (3 * rng.standard_normal((B * (gam + 1), V))).astype(np.float32)
+    d = np.concatenate([t[b * (gam + 1): b * (gam + 1) + gam] for b in range(B)])
+    r = run(t, d, [gam] * B, np.zeros(B * gam), np.full(B, 0.6, np.float32), mode=K, delta=1e-30)
+    assert (r.nkl == 0.0).all()
+    assert (r.num_accepted == gam).all()
+
+
+@pytest.mark.parametrize("T", [0.6, 1.0])
+def test_nkl_matches_scipy_entropy(T):
+    rng = np.random.default_rng(4)
+    V, gam, B = 4096, 4, 3
+    t = (3 * rng.standard_normal((B * (gam + 1), V))).astype(np.float32)
+    d = np.concatenate([t[b * (gam + 1): b * (gam + 1) + gam] for b in range(B)]) + \
+        (0.5 + rng.random((B * gam, 1))).astype(np.float32) * rng.standard_normal((B * gam, V)).astype(np.float32)
+    d = d.astype(np.float32)
+    r = run(t, d, [gam] * B, np.zeros(B * gam), np.full(B, T, np.float32), mode=K, delta=0.15)
+    Td = np.float64(np.float32(T))
+    for b in range(B):
+        for i in range(gam):
+            P = special.softmax(t[b * (gam + 1) + i].astype(np.float64) / Td)
+            Q = special.softmax(d[b * gam + i].astype(np.float64) / Td)
+            ref = stats.entropy(Q, P) / np.log(V)
+            assert abs(r.nkl[b * gam + i] / ref - 1) < 1e-10
+        n = r.num_accepted[b]
+        exp_n = next((i for i in range(gam) if not r.nkl[b * gam + i] < np.float32(0.15)), gam)
+        assert n == exp_n
+        assert r.tokens[b * (gam + 1) + n] == np.argmax(t[b * (gam + 1) + n])
+
+
+def test_nkl_range_on_long_drafts():
+    """NKL lies in [0, 1] on the long-draft workload (reduced batch), and the
+    true bound 0 <= KL <= max_y (l_d - l_t) holds."""
+    import synthetic
+    w = synthetic.make_long(B=2, mode=K)
+    r = oracle.verify_workload(w)
+    assert np.isfinite(r.nkl).all()
+    assert (r.nkl >= 0).all() and (r.nkl <= 1).all()
+    T = np.float64(w.temperature[0])
+    tf, df = w.target_f32(), w.draft_f32()
+    for k in (0, 7, 15, 16, 31):
+        b, i = divmod(k, 16)
+        lt = special.log_softmax(tf[b * 17 + i].astype(np.float64) / T)
+        ld = special.log_softmax(df[k].astype(np.float64) / T)
+        assert r.nkl[k] * np.log(w.vocab) <= (ld - lt).max() + 1e-12
+    # acceptance decays along the draft (noise ramps up)
+    assert r.nkl.reshape(2, 16)[:, :4].mean() < r.nkl.reshape(2, 16)[:, -4:].mean()
+
+
+# --------------------------------------------------------------------------
+# tree mode: golden, brute force, chain == greedy
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_tree_golden(dtype):
+    g = json.load(open(os.path.join(GOLD, "greedy_tree_small.json")))["tree"]
+    rows = np.array(g["rows"], np.float32)
+    tgt = f32_to_bf16_bits(rows) if dtype == "bf16" else rows
+    par = np.array(g["parents"][1:], np.int32)
+    r = run(tgt, None, [len(par)], g["node_tokens"], mode=TR, parents=par, dtype=dtype)
+    assert r.num_accepted[0] == g["num_accepted"]
+    assert r.tree_node[0] == g["deepest_node"]
+    assert r.tokens.tolist() == g["tokens"]
+
+
+def _brute_force_tree(rows, parents, toks):
+    """Enumerate every root->node path; a path is accepted iff each edge's token
+    equals the argmax (np.argmax: first maximum) of the edge's parent row."""
+    N = len(parents) + 1
+    par = [-1] + list(parents)
+    best, best_path = 0, []
+    for n in range(1, N):
+        path, v, ok = [], n, True
+        while v != 0:
+            if toks[v - 1] != int(np.argmax(rows[par[v]])):
+                ok = False
+            path.append(v)
+            v = par[v]
+        if ok and len(path) > len(best_path):
+            best, best_path = n, path
+    return best, [toks[v - 1] for v in reversed(best_path)] + [int(np.argmax(rows[best]))]
+
+
+def test_tree_brute_force_random():
+    rng = np.random.default_rng(21)
+    V = 12
+    for trial in range(300):
+        N = int(rng.integers(1, 10))
+        parents = np.array([rng.integers(0, k) for k in range(1, N)], np.int32)
+        rows = rng.integers(0, 4, size=(N, V)).astype(np.float32)  # ties on purpose
+        toks = np.array([int(np.argmax(rows[parents[k - 1]])) if rng.random() < 0.7 else int(rng.integers(0, V))
+                         for k in range(1, N)], np.int32)
+        r = run(rows, None, [N - 1], toks, mode=TR, parents=parents)
+        node, out = _brute_force_tree(rows, parents, list(toks))
+        assert r.tree_node[0] == node
+        assert r.num_accepted[0] == len(out) - 1
+        assert r.tokens[: len(out)].tolist() == out
+        assert (r.tokens[len(out):] == -1).all()
+
+
+def test_chain_tree_equals_greedy():
+    rng = np.random.default_rng(9)
+    V, gam, B = 257, 7, 40
+    t = rng.integers(-2, 3, size=(B * (gam + 1), V)).astype(np.float32)
+    x = np.concatenate([np.argmax(t[b * (gam + 1): b * (gam + 1) + gam], axis=1) for b in range(B)])
+    flip = rng.random(B * gam) < 0.15
+    x[flip] = rng.integers(0, V, flip.sum())
+    chain = np.tile(np.arange(gam, dtype=np.int32), B)  # parent of node k is k-1
+    a = run(t, None, [gam] * B, x, mode=G)
+    b = run(t, None, [gam] * B, x, mode=TR, parents=chain)
+    assert a.tokens.tolist() == b.tokens.tolist()
+    assert a.num_accepted.tolist() == b.num_accepted.tolist()
+
+
+# --------------------------------------------------------------------------
+# batching invariance and invalid data
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [S, G, K])
+def test_batch_equals_single_calls(mode):
+    import synthetic
+    w = synthetic.random_workload(7, mode, B=9, V=300, dtype="bf16", gmax=5, gmin=0)
+    full = oracle.verify_workload(w)
+    t_off, d_off = w.t_off, w.d_off
+    for b in range(w.batch):
+        ts, te, ds, de = t_off[b], t_off[b + 1], d_off[b], d_off[b + 1]
+        r = oracle.verify(w.target[ts:te], w.draft[ds:de], w.dtype, w.gamma[b:b + 1], w.draft_tokens[ds:de],
+                          w.temperature[b:b + 1], w.u_accept[ds:de], w.u_resample[b:b + 1], mode, w.delta,
+                          None, w.max_gamma)
+        assert r.tokens.tolist() == full.tokens[ts:te].tolist()
+        assert r.num_accepted[0] == full.num_accepted[b]
+
+
+def test_invalid_requests_isolated():
+    import synthetic
+    w = synthetic.random_workload(3, S, B=6, V=200, dtype="f32", gmax=4, gmin=2)
+    base = oracle.verify_workload(w)
+    d_off = w.d_off
+    bad = {1: "token", 2: "temp", 3: "uacc", 4: "ures"}
+    w.draft_tokens = w.draft_tokens.copy()
+    w.temperature = w.temperature.copy()
+    w.u_accept = w.u_accept.copy()
+    w.u_resample = w.u_resample.copy()
+    w.draft_tokens[d_off[1]] = w.vocab
+    w.temperature[2] = 0.0
+    w.u_accept[d_off[3] + 1] = 1.0
+    w.u_resample[4] = np.nan
+    r = oracle.verify_workload(w)
+    t_off = w.t_off
+    for b in range(w.batch):
+        seg = r.tokens[t_off[b]:t_off[b + 1]]
+        if b in bad:
+            assert r.num_accepted[b] == -1 and (seg == -1).all()
+            assert r.flags[b] & oracle.FLAG_INVALID
+        else:
+            assert r.num_accepted[b] == base.num_accepted[b]
+            assert seg.tolist() == base.tokens[t_off[b]:t_off[b + 1]].tolist()
+
+
+def test_layout_errors_mark_everything_invalid():
+    rng = np.random.default_rng(0)
+    t = rng.standard_normal((8, 10)).astype(np.float32)
+    d = rng.standard_normal((5, 10)).astype(np.float32)
+    r = run(t, d, [3, 2], np.zeros(5), total=4)  # sum(gamma) = 5 != 4
+    assert (r.num_accepted == -1).all()
+    r = run(t, d, [3, -1], np.zeros(5), total=2)
+    assert (r.num_accepted == -1).all()
+    # gamma above max_gamma: that request only
+    r = run(t, d, [3, 2], np.zeros(5), max_gamma=2)
+    assert r.num_accepted[0] == -1 and r.num_accepted[1] >= 0
+
+
+def test_flags_mark_boundary_decisions():
+    g = json.load(open(os.path.join(GOLD, "worked_v4.json")))
+    p, q = np.array(g["p"]), np.array(g["q"])
+    tgt = np.log(np.stack([p, q])).astype(np.float32)
+    drf = np.log(q[None, :]).astype(np.float32)
+    # u within 1e-5 of alpha = 2/3: flagged; far: not flagged
+    r = run(tgt, drf, [1], [2], None, [np.float32(2 / 3 + 3e-6)], [0.5])
+    assert r.flags[0] & oracle.FLAG_ACCEPT_BAND
+    r = run(tgt, drf, [1], [2], None, [0.9], [0.5])
+    assert not (r.flags[0] & oracle.FLAG_ACCEPT_BAND) and not (r.flags[0] & oracle.FLAG_DRAW_BAND)
+    # resample uniform at the residual CDF step 0.75 (= 0.3/0.4): flagged
+    r = run(tgt, drf, [1], [2], None, [0.9], [np.float32(0.75 + 2e-6)])
+    assert r.flags[0] & oracle.FLAG_DRAW_BAND
+
+
+def test_inverse_cdf_many_draws():
+    """Many terminal draws at V = 1000 against numpy's searchsorted on the
+    cumulative residual (margins computed independently of the oracle)."""
+    rng = np.random.default_rng(77)
+    V, B = 1000, 3000
+    t = (3 * rng.standard_normal((2 * B, V))).astype(np.float32)
+    d = (t[0::2] + rng.standard_normal((B, V))).astype(np.float32)
+    x = rng.integers(0, V, B)
+    ua = np.full(B, 0.999999, np.float32)  # reject unless alpha ~ 1
+    ur = rng.random(B).astype(np.float32)
+    r = run(t, d, [1] * B, x, None, ua, ur)
+    checked = 0
+    for b in range(B):
+        P = special.softmax(t[2 * b].astype(np.float64))
+        n = r.num_accepted[b]
+        if n == 0:
+            Q = special.softmax(d[b].astype(np.float64))
+            w = np.maximum(0.0, P - Q)
+        else:
+            w = special.softmax(t[2 * b + 1].astype(np.float64))
+        cdf = np.cumsum(w) / w.sum()
+        u = np.float64(ur[b])
+        y = int(np.searchsorted(cdf, u, side="right"))
+        lo = cdf[y - 1] if y > 0 else 0.0
+        if min(u - lo, cdf[y] - u) > 1e-10:
+            assert r.tokens[2 * b + n] == y, b
+            checked += 1
+    assert checked > 0.99 * B
+
+
+def test_cdf_steps_are_strict():
+    g = json.load(open(os.path.join(GOLD, "worked_v4.json")))["cdf_steps"]
+    t = np.zeros((1, 4), np.float32)
+    for case in g["cases"]:
+        r = run(t, np.zeros((0, 4), np.float32), [0], [], None, [], [case["u_resample"]])
+        assert r.num_accepted[0] == 0
+        assert r.tokens.tolist() == [case["token"]], case
