@@ -1,0 +1,212 @@
+"""Python binding of libspecverify, the gfx950 verify step of speculative /
+Chain-of-Draft decoding.
+
+The functions here only marshal arguments: every step of the verify path runs
+in the HIP kernels of ``libspecverify.so`` (built by ``build.py`` from
+``csrc/``).  PyTorch provides device memory and the stream.  Importing this
+package loads the library and fails loudly if it is missing.
+
+C entry points (``include/specverify.h``) and their Python counterparts:
+
+* ``spec_verify``                -> :func:`spec_verify` (raw pointers) and :func:`verify` (tensors)
+* ``spec_verify_workspace_size`` -> :func:`spec_verify_workspace_size`
+* ``spec_verify_status_string``  -> :func:`spec_verify_status_string`
+* ``spec_verify_version``        -> :func:`spec_verify_version`
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+
+SV_OK, SV_EINVAL, SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP = 0, -1, -2, -3, -4
+SV_MODE_STOCHASTIC, SV_MODE_GREEDY, SV_MODE_NKL, SV_MODE_TREE_GREEDY = 0, 1, 2, 3
+SV_DTYPE_F32, SV_DTYPE_BF16 = 0, 1
+SV_MAX_GAMMA = 4096
+SV_NUM_PHASE_EVENTS = 4
+MODES = {"stochastic": 0, "greedy": 1, "nkl": 2, "tree": 3}
+
+
+class sv_config(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("batch", ctypes.c_int32),
+        ("vocab", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("max_gamma", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("total_draft_rows", ctypes.c_int64),
+        ("stream", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_uint64),
+        ("out_p_x", ctypes.c_void_p),
+        ("out_q_x", ctypes.c_void_p),
+        ("out_resid_mass", ctypes.c_void_p),
+        ("out_tree_node", ctypes.c_void_p),
+        ("phase_events", ctypes.c_void_p),
+    ]
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"spec_verify failed: {spec_verify_status_string(status)} ({status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libspecverify.so is not built ({LIB_PATH}); run __graft_entry__.build() "
+                          "or python draft_token_verification_05_amd/build.py")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.spec_verify.restype = ctypes.c_int
+    lib.spec_verify.argtypes = [P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, P, P, ctypes.POINTER(sv_config)]
+    lib.spec_verify_workspace_size.restype = ctypes.c_size_t
+    lib.spec_verify_workspace_size.argtypes = [ctypes.POINTER(sv_config)]
+    lib.spec_verify_status_string.restype = ctypes.c_char_p
+    lib.spec_verify_status_string.argtypes = [ctypes.c_int]
+    lib.spec_verify_version.restype = ctypes.c_int
+    lib.spec_verify_version.argtypes = []
+    return lib
+
+
+_lib = _load()
+
+
+def make_config(batch: int, vocab: int, dtype: int, max_gamma: int, total_draft_rows: int, stream: int = 0,
+                workspace: int = 0, workspace_bytes: int = 0, out_p_x: int = 0, out_q_x: int = 0,
+                out_resid_mass: int = 0, out_tree_node: int = 0, phase_events: int = 0) -> sv_config:
+    return sv_config(ctypes.sizeof(sv_config), int(batch), int(vocab), int(dtype), int(max_gamma), 0,
+                     int(total_draft_rows), stream or None, workspace or None, int(workspace_bytes),
+                     out_p_x or None, out_q_x or None, out_resid_mass or None, out_tree_node or None,
+                     phase_events or None)
+
+
+def spec_verify(target_logits: int, draft_logits: int, draft_tokens: int, gamma_per_req: int, temperature: int,
+                u_accept: int, u_resample: int, mode: int, delta: float, tree_parents: int, out_tokens: int,
+                out_num_accepted: int, out_nkl: int, cfg: sv_config) -> int:
+    """The C entry point with raw device addresses (0 = NULL).  Returns the status."""
+    return int(_lib.spec_verify(target_logits or None, draft_logits or None, draft_tokens or None,
+                                gamma_per_req or None, temperature or None, u_accept or None, u_resample or None,
+                                int(mode), float(delta), tree_parents or None, out_tokens or None,
+                                out_num_accepted or None, out_nkl or None, ctypes.byref(cfg)))
+
+
+def spec_verify_workspace_size(cfg: sv_config) -> int:
+    return int(_lib.spec_verify_workspace_size(ctypes.byref(cfg)))
+
+
+def spec_verify_status_string(status: int) -> str:
+    return _lib.spec_verify_status_string(int(status)).decode()
+
+
+def spec_verify_version() -> int:
+    return int(_lib.spec_verify_version())
+
+
+# ----------------------------------------------------------------------------
+# tensor-level convenience wrapper (PyTorch = device memory + stream only)
+# ----------------------------------------------------------------------------
+
+@dataclass
+class VerifyOutput:
+    tokens: "torch.Tensor"  # int32 [sum(gamma+1)]
+    num_accepted: "torch.Tensor"  # int32 [B]
+    nkl: Optional["torch.Tensor"] = None  # float32 [sum(gamma)]
+    p_x: Optional["torch.Tensor"] = None
+    q_x: Optional["torch.Tensor"] = None
+    resid_mass: Optional["torch.Tensor"] = None
+    tree_node: Optional["torch.Tensor"] = None
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+def _check(t, name, dtype, numel=None, dev=None):
+    import torch
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} must be on {dev}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+
+
+def verify(target_logits, draft_logits, draft_tokens, gamma_per_req, temperature=None, u_accept=None,
+           u_resample=None, mode: int | str = SV_MODE_STOCHASTIC, delta: float = 0.15, tree_parents=None, *,
+           max_gamma: Optional[int] = None, workspace=None, diagnostics: bool = False, out_nkl: bool = False,
+           phase_events: int = 0, stream=None) -> VerifyOutput:
+    """Runs one verify step on device tensors (packed layout, see specverify.h).
+
+    ``target_logits`` [sum(gamma+1), V] and ``draft_logits`` [sum(gamma), V] are
+    torch.bfloat16 or torch.float32 on the GPU.  The call is asynchronous on
+    ``stream`` (default: torch's current stream)."""
+    import torch
+    if isinstance(mode, str):
+        mode = MODES[mode]
+    dev = target_logits.device
+    if dev.type != "cuda":
+        raise ValueError("target_logits must be a GPU tensor")
+    if target_logits.dtype == torch.bfloat16:
+        dt = SV_DTYPE_BF16
+    elif target_logits.dtype == torch.float32:
+        dt = SV_DTYPE_F32
+    else:
+        raise TypeError("logits must be bfloat16 or float32")
+    if target_logits.dim() != 2 or not target_logits.is_contiguous():
+        raise ValueError("target_logits must be a contiguous [rows, V] tensor")
+    B = int(gamma_per_req.numel())
+    V = int(target_logits.shape[1])
+    R_d = int(draft_tokens.numel()) if draft_tokens is not None else 0
+    _check(gamma_per_req, "gamma_per_req", torch.int32, B, dev)
+    _check(draft_tokens, "draft_tokens", torch.int32, None, dev)
+    _check(temperature, "temperature", torch.float32, B, dev)
+    _check(u_accept, "u_accept", torch.float32, R_d, dev)
+    _check(u_resample, "u_resample", torch.float32, B, dev)
+    _check(tree_parents, "tree_parents", torch.int32, R_d, dev)
+    if draft_logits is not None:
+        _check(draft_logits, "draft_logits", target_logits.dtype, None, dev)
+        if draft_logits.dim() != 2 or draft_logits.shape[1] != V or draft_logits.shape[0] != R_d:
+            raise ValueError("draft_logits must be [sum(gamma), V]")
+    if target_logits.shape[0] != R_d + B:
+        raise ValueError("target_logits must have sum(gamma)+B rows")
+    if max_gamma is None:
+        max_gamma = min(R_d, SV_MAX_GAMMA)
+    out_tokens = torch.empty(max(R_d + B, 1), dtype=torch.int32, device=dev)
+    out_num = torch.empty(B, dtype=torch.int32, device=dev)
+    nkl = torch.empty(max(R_d, 1), dtype=torch.float32, device=dev) if (mode == SV_MODE_NKL or out_nkl) else None
+    p_x = q_x = resid = tnode = None
+    if diagnostics:
+        p_x = torch.empty(max(R_d, 1), dtype=torch.float32, device=dev)
+        q_x = torch.empty(max(R_d, 1), dtype=torch.float32, device=dev)
+        resid = torch.empty(B, dtype=torch.float32, device=dev)
+        tnode = torch.empty(B, dtype=torch.int32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    cfg = make_config(B, V, dt, max_gamma, R_d, stream=int(stream.cuda_stream))
+    need = spec_verify_workspace_size(cfg)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    cfg.workspace = workspace.data_ptr()
+    cfg.workspace_bytes = workspace.numel()
+    cfg.out_p_x, cfg.out_q_x = _ptr(p_x) or None, _ptr(q_x) or None
+    cfg.out_resid_mass, cfg.out_tree_node = _ptr(resid) or None, _ptr(tnode) or None
+    cfg.phase_events = phase_events or None
+    st = spec_verify(_ptr(target_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(gamma_per_req),
+                     _ptr(temperature), _ptr(u_accept), _ptr(u_resample), mode, delta, _ptr(tree_parents),
+                     _ptr(out_tokens), _ptr(out_num), _ptr(nkl), cfg)
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return VerifyOutput(out_tokens[: R_d + B], out_num, None if nkl is None else nkl[:R_d],
+                        None if p_x is None else p_x[:R_d], None if q_x is None else q_x[:R_d], resid, tnode)

@@ -1,0 +1,158 @@
+// C-ABI entry points of libspecverify: argument validation, workspace layout,
+// launch sequence.  Declared in include/specverify.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "sv_internal.h"
+
+namespace {
+
+thread_local char g_hip_error[256] = "";
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Host-side checks of everything that needs no device data.
+int validate(const void* target, const void* draft, const int32_t* tokens, const int32_t* gamma, const float* temp,
+             const float* ua, const float* ur, int32_t mode, float delta, const int32_t* parents,
+             const int32_t* out_tokens, const int32_t* out_num, const float* out_nkl, const sv_config* cfg) {
+  if (!cfg || cfg->struct_size != sizeof(sv_config) || cfg->reserved != 0) return SV_EINVAL;
+  if (cfg->batch <= 0 || cfg->vocab <= 0) return SV_EINVAL;
+  if (cfg->dtype != SV_DTYPE_F32 && cfg->dtype != SV_DTYPE_BF16) return SV_EINVAL;
+  if (mode < SV_MODE_STOCHASTIC || mode > SV_MODE_TREE_GREEDY) return SV_EINVAL;
+  if (cfg->max_gamma < 0) return SV_EINVAL;
+  if (cfg->max_gamma > SV_MAX_GAMMA) return SV_EUNSUPPORTED;
+  const int64_t R_d = cfg->total_draft_rows;
+  if (R_d < 0 || R_d > (int64_t)cfg->batch * cfg->max_gamma) return SV_EINVAL;
+  if (R_d + cfg->batch > INT32_MAX) return SV_EUNSUPPORTED;
+  const int64_t nch_a = (cfg->vocab + sv::chunk_a(cfg->dtype) - 1) / sv::chunk_a(cfg->dtype);
+  const int64_t nch_c = (cfg->vocab + sv::chunk_c(cfg->dtype) - 1) / sv::chunk_c(cfg->dtype);
+  if ((R_d + cfg->batch) * nch_a > INT32_MAX || (int64_t)cfg->batch * nch_c > INT32_MAX) return SV_EUNSUPPORTED;
+
+  const bool soft = mode == SV_MODE_STOCHASTIC || mode == SV_MODE_NKL;
+  if (!target || !gamma || !out_tokens || !out_num) return SV_EINVAL;
+  if (R_d > 0 && !tokens) return SV_EINVAL;
+  if (soft && R_d > 0 && !draft) return SV_EINVAL;
+  if (soft && !temp) return SV_EINVAL;
+  if (mode == SV_MODE_STOCHASTIC && (!ur || (R_d > 0 && !ua))) return SV_EINVAL;
+  if (mode == SV_MODE_NKL && (!std::isfinite(delta) || (R_d > 0 && !out_nkl))) return SV_EINVAL;
+  if (mode == SV_MODE_TREE_GREEDY && R_d > 0 && !parents) return SV_EINVAL;
+
+  const size_t es = (size_t)sv::elem_size(cfg->dtype);
+  if (!aligned(target, es) || (draft && !aligned(draft, es))) return SV_EINVAL;
+  const void* p4[] = {tokens, gamma, temp, ua, ur, parents, out_tokens, out_num, out_nkl, cfg->out_p_x,
+                      cfg->out_q_x, cfg->out_resid_mass, cfg->out_tree_node};
+  for (const void* p : p4)
+    if (p && !aligned(p, 4)) return SV_EINVAL;
+
+  const sv::Layout L = sv::make_layout(cfg->batch, cfg->vocab, cfg->dtype, R_d);
+  if (!cfg->workspace || cfg->workspace_bytes < L.total || !aligned(cfg->workspace, 256)) return SV_EWORKSPACE;
+  return SV_OK;
+}
+
+int hip_fail(hipError_t e) {
+  std::snprintf(g_hip_error, sizeof(g_hip_error), "HIP error: %s (%d)", hipGetErrorString(e), (int)e);
+  return SV_EHIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_verify_workspace_size(const sv_config* cfg) {
+  if (!cfg || cfg->struct_size != sizeof(sv_config)) return 0;
+  if (cfg->batch <= 0 || cfg->vocab <= 0 || cfg->total_draft_rows < 0 || cfg->max_gamma < 0) return 0;
+  if (cfg->dtype != SV_DTYPE_F32 && cfg->dtype != SV_DTYPE_BF16) return 0;
+  return sv::make_layout(cfg->batch, cfg->vocab, cfg->dtype, cfg->total_draft_rows).total;
+}
+
+const char* spec_verify_status_string(int status) {
+  switch (status) {
+    case SV_OK: return "SV_OK: success";
+    case SV_EINVAL: return "SV_EINVAL: invalid argument";
+    case SV_EUNSUPPORTED: return "SV_EUNSUPPORTED: configuration not supported";
+    case SV_EWORKSPACE: return "SV_EWORKSPACE: workspace missing, misaligned or too small";
+    case SV_EHIP: return g_hip_error[0] ? g_hip_error : "SV_EHIP: HIP launch failure";
+    default: return "unknown status";
+  }
+}
+
+int spec_verify_version(void) { return SPECVERIFY_VERSION; }
+
+int spec_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                const int32_t* gamma_per_req, const float* temperature, const float* u_accept,
+                const float* u_resample, int32_t mode, float delta, const int32_t* tree_parents,
+                int32_t* out_tokens, int32_t* out_num_accepted, float* out_nkl, const sv_config* cfg) {
+  const int st = validate(target_logits, draft_logits, draft_tokens, gamma_per_req, temperature, u_accept,
+                          u_resample, mode, delta, tree_parents, out_tokens, out_num_accepted, out_nkl, cfg);
+  if (st != SV_OK) return st;
+
+  const int32_t B = cfg->batch, V = cfg->vocab;
+  const int64_t R_d = cfg->total_draft_rows;
+  const sv::Layout L = sv::make_layout(B, V, cfg->dtype, R_d);
+  char* ws = static_cast<char*>(cfg->workspace);
+
+  sv::Params p{};
+  p.target = target_logits;
+  p.draft = draft_logits;
+  p.tokens = draft_tokens;
+  p.gamma = gamma_per_req;
+  p.temp = temperature;
+  p.ua = u_accept;
+  p.ur = u_resample;
+  p.parents = tree_parents;
+  p.out_tokens = out_tokens;
+  p.out_num = out_num_accepted;
+  p.out_nkl = (mode == SV_MODE_STOCHASTIC || mode == SV_MODE_NKL) ? out_nkl : nullptr;
+  const bool soft = mode == SV_MODE_STOCHASTIC || mode == SV_MODE_NKL;
+  p.out_p_x = soft ? cfg->out_p_x : nullptr;
+  p.out_q_x = soft ? cfg->out_q_x : nullptr;
+  p.out_resid = mode == SV_MODE_STOCHASTIC ? cfg->out_resid_mass : nullptr;
+  p.out_tree_node = mode == SV_MODE_TREE_GREEDY ? cfg->out_tree_node : nullptr;
+  p.B = B;
+  p.V = V;
+  p.max_gamma = cfg->max_gamma;
+  p.mode = mode;
+  p.dtype = cfg->dtype;
+  p.R_d = (int32_t)R_d;
+  p.n_task = (int32_t)(mode == SV_MODE_STOCHASTIC ? R_d : R_d + B);
+  p.nch_a = (int32_t)L.nch_a;
+  p.nch_c = (int32_t)L.nch_c;
+  p.delta = delta;
+  p.want_w = (mode == SV_MODE_NKL || (mode == SV_MODE_STOCHASTIC && out_nkl)) ? 1 : 0;
+  p.hdr = reinterpret_cast<int32_t*>(ws + L.off_hdr);
+  p.t_off = reinterpret_cast<int32_t*>(ws + L.off_toff);
+  p.d_off = reinterpret_cast<int32_t*>(ws + L.off_doff);
+  p.pair2req = reinterpret_cast<int32_t*>(ws + L.off_pair2req);
+  p.row2req = reinterpret_cast<int32_t*>(ws + L.off_row2req);
+  p.part_a = reinterpret_cast<sv::PartA*>(ws + L.off_part_a);
+  p.stat = reinterpret_cast<sv::TaskStat*>(ws + L.off_stat);
+  p.gat = reinterpret_cast<float*>(ws + L.off_gat);
+  p.cnt_task = reinterpret_cast<uint32_t*>(ws + L.off_cnt_task);
+  p.cnt_req = reinterpret_cast<uint32_t*>(ws + L.off_cnt_req);
+  p.term = reinterpret_cast<sv::Term*>(ws + L.off_term);
+  p.part_c = reinterpret_cast<sv::PartC*>(ws + L.off_part_c);
+  p.cnt_draw = reinterpret_cast<uint32_t*>(ws + L.off_cnt_draw);
+
+  // 16-byte vector loads need every row to start on a 16-byte boundary
+  const size_t es = (size_t)sv::elem_size(cfg->dtype);
+  const bool vec = ((size_t)V * es) % 16 == 0 && aligned(target_logits, 16) &&
+                   (!draft_logits || aligned(draft_logits, 16));
+
+  hipStream_t s = static_cast<hipStream_t>(cfg->stream);
+  hipEvent_t* ev = static_cast<hipEvent_t*>(cfg->phase_events);
+  hipError_t e;
+  if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e);
+  if ((e = (hipError_t)sv::launch_prep(p, s)) != hipSuccess) return hip_fail(e);
+  if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e);
+  if ((e = (hipError_t)sv::launch_rowstats(p, vec, s)) != hipSuccess) return hip_fail(e);
+  if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e);
+  if (mode == SV_MODE_STOCHASTIC && (e = (hipError_t)sv::launch_draw(p, vec, s)) != hipSuccess) return hip_fail(e);
+  if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e);
+  return SV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+/*
+ * libspecverify -- the verify step of speculative / Chain-of-Draft decoding on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One call verifies a batch of B requests.  Request b drafted gamma_b tokens;
+ * the caller supplies the target model's logits for the gamma_b + 1 positions
+ * behind the draft, the draft model's logits for the gamma_b drafted positions,
+ * the drafted token ids and host-drawn uniforms.  The call returns, per
+ * request, the accepted prefix of the draft followed by one more token.
+ *
+ * Modes (what each computes is defined by the passages cited):
+ *
+ *   SV_MODE_STOCHASTIC  Modified rejection sampling -- "大模型推理的投机采样"
+ *       page, section "核心算法数学原理": with p = softmax(target_i / T) and
+ *       q = softmax(draft_i / T), draft token x_i is accepted when
+ *       u_accept_i <= alpha_i = min(1, p(x_i) / q(x_i)); at the first rejection
+ *       j the slot is redrawn from max(0, p_j - q_j) / norm and the remaining
+ *       drafts are discarded.  When all gamma_b drafts are accepted a bonus
+ *       token is drawn from p_gamma (target row gamma_b).  Each request uses
+ *       one uniform u_resample[b] for its terminal draw, by inverse CDF in
+ *       ascending token order: y* = min{y : C_y > u * C_{V-1}}.
+ *   SV_MODE_GREEDY      Greedy verification -- Gemma-4 MTP drafter page,
+ *       section 2.3: x_i is accepted while it equals argmax(target_i) (lowest
+ *       index on ties); the first mismatching slot (or slot gamma_b) gets the
+ *       target row's argmax.
+ *   SV_MODE_NKL         Normalised-KL filter -- "Chain of Draft" page, section
+ *       3.2: nkl_i = KL(q_i || p_i) / ln V at the request's temperature; x_i is
+ *       accepted while nkl_i < delta; the first failing slot (or slot gamma_b)
+ *       gets argmax(target row).
+ *   SV_MODE_TREE_GREEDY Greedy tree verification -- "Parallel Drafting" page,
+ *       section 2.2 (tree drafts), Gemma-4 MTP page, section 6.2 (keep the
+ *       longest accepted path): node n with parent pi(n) is accepted iff pi(n)
+ *       is accepted and its token equals argmax(target row of pi(n)); the
+ *       output is the path to the deepest accepted node (lowest node id on
+ *       equal depth) followed by that node's argmax.
+ *
+ * Packed (ragged) layout.  t_off[b] = sum_{b'<b}(gamma_b' + 1),
+ * d_off[b] = sum_{b'<b} gamma_b'.  Target row t_off[b] + i holds position i of
+ * request b (i = 0..gamma_b); draft row d_off[b] + i holds drafted position i
+ * (i = 0..gamma_b - 1).  Tree mode: request b is a tree of N_b = gamma_b + 1
+ * nodes, node 0 the root; target row t_off[b] + n belongs to node n;
+ * draft_tokens[d_off[b] + n - 1] and tree_parents[d_off[b] + n - 1] are node
+ * n's token and parent (0 <= parent < n).
+ *
+ * Memory.  Every array argument is DEVICE memory, row-major and packed.  The
+ * caller owns all buffers (including the workspace); the library allocates
+ * nothing, keeps no global state, and only enqueues work on cfg->stream.
+ * Outputs are valid once that stream has been synchronised.  Calls on
+ * different streams must use different workspaces.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPECVERIFY_VERSION 10000 /* 1.0.0 */
+
+/* status codes */
+#define SV_OK 0
+#define SV_EINVAL (-1)       /* bad argument (returned before any work is enqueued) */
+#define SV_EUNSUPPORTED (-2) /* valid but unsupported request (e.g. max_gamma above SV_MAX_GAMMA) */
+#define SV_EWORKSPACE (-3)   /* workspace missing or smaller than spec_verify_workspace_size() */
+#define SV_EHIP (-4)         /* a HIP launch failed; spec_verify_status_string(SV_EHIP) names it */
+
+/* modes */
+#define SV_MODE_STOCHASTIC 0
+#define SV_MODE_GREEDY 1
+#define SV_MODE_NKL 2
+#define SV_MODE_TREE_GREEDY 3
+
+/* logit element types */
+#define SV_DTYPE_F32 0
+#define SV_DTYPE_BF16 1
+
+#define SV_MAX_GAMMA 4096 /* largest accepted cfg->max_gamma (tree: nodes - 1) */
+
+/* Phase events (optional, for timing): cfg->phase_events points to
+ * SV_NUM_PHASE_EVENTS hipEvent_t handles created by the caller.  They are
+ * recorded on cfg->stream: [0] before the first kernel, [1] before the
+ * row-statistics kernel, [2] after it, [3] after the last kernel. */
+#define SV_NUM_PHASE_EVENTS 4
+
+typedef struct sv_config {
+  uint32_t struct_size;     /* = sizeof(sv_config); other values are rejected */
+  int32_t batch;            /* B > 0 */
+  int32_t vocab;            /* V > 0 */
+  int32_t dtype;            /* SV_DTYPE_F32 or SV_DTYPE_BF16 (both logit arrays) */
+  int32_t max_gamma;        /* bound on gamma_per_req[b]; 0 <= max_gamma <= SV_MAX_GAMMA */
+  int32_t reserved;         /* must be 0 */
+  int64_t total_draft_rows; /* sum_b gamma_per_req[b], known on the host (sizes the grids) */
+  void* stream;             /* hipStream_t to enqueue on; NULL = the default stream */
+  void* workspace;          /* device scratch, >= spec_verify_workspace_size(cfg) bytes, 256-byte aligned */
+  uint64_t workspace_bytes;
+  /* optional diagnostics (device pointers, NULL = not written) */
+  float* out_p_x;           /* [total_draft_rows] p_i(x_i) (stochastic and NKL modes) */
+  float* out_q_x;           /* [total_draft_rows] q_i(x_i) (stochastic and NKL modes) */
+  float* out_resid_mass;    /* [B] stochastic: sum_y max(0, p_j - q_j) after a rejection, 1 for a bonus */
+  int32_t* out_tree_node;   /* [B] tree mode: id of the deepest accepted node */
+  void* phase_events;       /* optional hipEvent_t[SV_NUM_PHASE_EVENTS] (see above) */
+} sv_config;
+
+/*
+ * Verifies one batch.
+ *
+ * target_logits  [sum(gamma+1)][V] of cfg->dtype (bf16 = IEEE bfloat16 bit patterns).
+ * draft_logits   [sum(gamma)][V]; read in stochastic and NKL modes only (may be NULL otherwise).
+ * draft_tokens   int32 [sum(gamma)]; must lie in [0, V).
+ * gamma_per_req  int32 [B]; 0 <= gamma_b <= cfg->max_gamma.
+ * temperature    float32 [B]; > 0 and finite (stochastic and NKL modes; may be NULL otherwise).
+ * u_accept       float32 [sum(gamma)] in [0, 1) (stochastic mode; may be NULL otherwise).
+ * u_resample     float32 [B] in [0, 1) (stochastic mode; may be NULL otherwise).
+ * mode           SV_MODE_*.
+ * delta          NKL threshold (NKL mode; must be finite there).
+ * tree_parents   int32 [sum(gamma)] (tree mode; may be NULL otherwise).
+ * out_tokens     int32 [sum(gamma+1)], same offsets as the target rows: accepted tokens, then the
+ *                terminal token, then -1 in the unused slots.
+ * out_num_accepted int32 [B]: number of accepted draft tokens (tree: depth of the deepest accepted node).
+ * out_nkl        float32 [sum(gamma)]: nkl_i for every drafted position (required in NKL mode;
+ *                in stochastic mode written when non-NULL).
+ * cfg            see sv_config.
+ *
+ * Synchronous errors (nothing enqueued): SV_EINVAL for a NULL pointer the mode needs, B <= 0,
+ * V <= 0, an unknown mode or dtype, a non-finite delta in NKL mode, a struct_size mismatch,
+ * total_draft_rows outside [0, B*max_gamma], or misaligned pointers (logits: element size;
+ * int32/float32 arrays: 4 bytes); SV_EUNSUPPORTED for max_gamma > SV_MAX_GAMMA or more than
+ * 2^31-1 rows; SV_EWORKSPACE; SV_EHIP.
+ * Data errors (found on the device, no host sync): a request with a token outside [0, V), a
+ * gamma_b above max_gamma, a temperature <= 0 or non-finite, a uniform outside [0, 1) or a bad
+ * parent gets out_num_accepted[b] = -1 and -1 in all its token slots; other requests are not
+ * affected.  A negative gamma_b, or sum(gamma) != total_draft_rows, makes the packed layout
+ * undefined: every out_num_accepted[b] is set to -1 and no token slot is written.
+ * Logits are expected to be finite.
+ */
+int spec_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                const int32_t* gamma_per_req, const float* temperature, const float* u_accept,
+                const float* u_resample, int32_t mode, float delta, const int32_t* tree_parents,
+                int32_t* out_tokens, int32_t* out_num_accepted, float* out_nkl, const sv_config* cfg);
+
+/* Workspace bytes spec_verify needs for this configuration (any mode); 0 for an invalid cfg.
+ * Reads batch, vocab, dtype, max_gamma and total_draft_rows only.  The workspace holds
+ * per-chunk partial results, counters and per-request records; it may be reused by
+ * successive calls on the same stream. */
+size_t spec_verify_workspace_size(const sv_config* cfg);
+
+/* Static description of a status code.  For SV_EHIP it includes the HIP error of the
+ * most recent failed launch on the calling thread. */
+const char* spec_verify_status_string(int status);
+
+/* SPECVERIFY_VERSION of the loaded library. */
+int spec_verify_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

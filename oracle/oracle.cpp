@@ -222,7 +222,7 @@ void verify_request(const Args& a, int32_t b, int64_t t0, int64_t d0) {
       if (a.out_nkl) {
         NSum kl;
         for (int64_t y = 0; y < V; ++y) kl.add(std::exp(ld[(size_t)y]) * (ld[(size_t)y] - lt[(size_t)y]));
-        a.out_nkl[d0 + i] = kl.value() / std::log((double)V);
+        a.out_nkl[d0 + i] = V > 1 ? kl.value() / std::log((double)V) : 0.0;
       }
     }
     double amargin = std::numeric_limits<double>::infinity();
@@ -284,7 +284,9 @@ void verify_request(const Args& a, int32_t b, int64_t t0, int64_t d0) {
       log_softmax(xd, T, ld);
       NSum kl;
       for (int64_t y = 0; y < V; ++y) kl.add(std::exp(ld[(size_t)y]) * (ld[(size_t)y] - lt[(size_t)y]));
-      nkl[(size_t)i] = kl.value() / lnV;
+      // A one-token vocabulary makes KL/ln V = 0/0: both distributions are the
+      // same point mass, so NKL is taken as 0.
+      nkl[(size_t)i] = V > 1 ? kl.value() / lnV : 0.0;
       if (a.out_nkl) a.out_nkl[d0 + i] = nkl[(size_t)i];
       if (a.out_p_x) a.out_p_x[d0 + i] = std::exp(lt[(size_t)a.tokens[d0 + i]]);
       if (a.out_q_x) a.out_q_x[d0 + i] = std::exp(ld[(size_t)a.tokens[d0 + i]]);

@@ -1,0 +1,141 @@
+"""Helpers of the GPU parity tests: move a synthetic workload to the GPU, run
+the HIP path through the C ABI, run the oracle on the same host arrays, and
+compare.
+
+Parity bars:
+* token ids and accepted counts bit-exact in greedy, NKL and tree modes (NKL
+  decisions within 1e-6*delta of delta are flagged by the oracle and excused);
+* stochastic mode exact except requests the oracle flags (|u - alpha| < 1e-5 or
+  the resample uniform within 1e-5 of a CDF step); every mismatch must be
+  flagged, and mismatches must stay below 1e-4 of all decisions;
+* p(x), q(x), residual mass and NKL within 2e-5 relative.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import oracle
+
+REL_TOL = 2e-5
+
+
+def to_device(w, dev="cuda:0"):
+    import torch
+    if w.dtype == "bf16":
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    return dict(
+        target=conv(w.target),
+        draft=None if w.draft is None else conv(w.draft),
+        tokens=i32(w.draft_tokens),
+        gamma=i32(w.gamma),
+        temp=f32(w.temperature),
+        ua=f32(w.u_accept),
+        ur=f32(w.u_resample),
+        parents=None if w.tree_parents is None else i32(w.tree_parents),
+    )
+
+
+def run_gpu(w, d=None, diagnostics=True, out_nkl=False, max_gamma=None, workspace=None):
+    import torch
+    import draft_token_verification_05_amd as sv
+    if d is None:
+        d = to_device(w)
+    mode = w.mode
+    soft = mode in (sv.SV_MODE_STOCHASTIC, sv.SV_MODE_NKL)
+    out = sv.verify(d["target"], d["draft"] if soft else None, d["tokens"], d["gamma"],
+                    d["temp"] if soft else None, d["ua"] if mode == 0 else None, d["ur"] if mode == 0 else None,
+                    mode, w.delta, d["parents"] if mode == 3 else None,
+                    max_gamma=w.max_gamma if max_gamma is None else max_gamma, diagnostics=diagnostics,
+                    out_nkl=out_nkl, workspace=workspace)
+    torch.cuda.synchronize()
+    host = lambda t: None if t is None else t.cpu().numpy()
+    return dict(tokens=host(out.tokens), num=host(out.num_accepted), nkl=host(out.nkl), p_x=host(out.p_x),
+                q_x=host(out.q_x), resid=host(out.resid_mass), tree_node=host(out.tree_node))
+
+
+@dataclass
+class Report:
+    requests: int = 0
+    decisions: int = 0
+    flagged_accept: int = 0
+    flagged_draw: int = 0
+    flagged_nkl: int = 0
+    mismatches: int = 0
+    unflagged_mismatches: int = 0
+    max_rel_px: float = 0.0
+    max_rel_qx: float = 0.0
+    max_rel_nkl: float = 0.0
+    max_rel_resid: float = 0.0
+    notes: list = field(default_factory=list)
+
+
+def _rel(a, b, mask=None, notes=None, what=""):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    idx = np.arange(a.size)
+    if mask is not None:
+        a, b, idx = a[mask], b[mask], idx[mask]
+    if a.size == 0:
+        return 0.0
+    denom = np.maximum(np.abs(b), 1e-300)
+    r = np.abs(a - b) / denom
+    r[(a == b)] = 0.0
+    k = int(np.nanargmax(r)) if np.isfinite(r).any() else 0
+    if notes is not None and (not np.isfinite(r).all() or r[k] > REL_TOL):
+        bad = np.where(~(r <= REL_TOL))[0][:4]
+        notes.append(f"{what}: " + "; ".join(f"[{idx[i]}] gpu={a[i]!r} oracle={b[i]!r}" for i in bad))
+    return float(np.max(r))
+
+
+def compare(w, g, o: oracle.OracleResult, check_diag=True) -> Report:
+    rep = Report(requests=w.batch)
+    t_off, d_off = w.t_off, w.d_off
+    valid = o.num_accepted >= 0
+    for b in range(w.batch):
+        n = int(o.num_accepted[b])
+        gam = int(w.gamma[b])
+        rep.decisions += (min(n, gam - 1) + 1 if gam > 0 else 0) + (1 if w.mode == 0 else 0) if n >= 0 else 0
+        fl = int(o.flags[b])
+        rep.flagged_accept += bool(fl & oracle.FLAG_ACCEPT_BAND)
+        rep.flagged_draw += bool(fl & oracle.FLAG_DRAW_BAND)
+        rep.flagged_nkl += bool(fl & oracle.FLAG_NKL_BAND)
+        ts, te = int(t_off[b]), int(t_off[b + 1])
+        same = g["num"][b] == o.num_accepted[b] and (n < 0 and g["num"][b] == -1 or
+                                                     (g["tokens"][ts:te] == o.tokens[ts:te]).all())
+        if not same:
+            rep.mismatches += 1
+            excused = fl & (oracle.FLAG_ACCEPT_BAND | oracle.FLAG_DRAW_BAND | oracle.FLAG_NKL_BAND)
+            if not excused:
+                rep.unflagged_mismatches += 1
+                if len(rep.notes) < 5:
+                    rep.notes.append(f"req {b}: gpu n={g['num'][b]} tok={g['tokens'][ts:te].tolist()} "
+                                     f"oracle n={o.num_accepted[b]} tok={o.tokens[ts:te].tolist()} flags={fl} "
+                                     f"am={o.accept_margin[b]:.3g} dm={o.draw_margin[b]:.3g}")
+    if check_diag and w.mode in (0, 2) and w.total_draft_rows > 0:
+        vrow = np.repeat(valid, w.gamma)
+        if g.get("p_x") is not None:
+            rep.max_rel_px = _rel(g["p_x"], o.p_x, vrow, rep.notes, "p_x")
+            rep.max_rel_qx = _rel(g["q_x"], o.q_x, vrow, rep.notes, "q_x")
+        if g.get("nkl") is not None:
+            rep.max_rel_nkl = _rel(g["nkl"], o.nkl, vrow, rep.notes, "nkl")
+    if check_diag and w.mode == 0 and g.get("resid") is not None:
+        rej = valid & (o.num_accepted < w.gamma)
+        rep.max_rel_resid = _rel(g["resid"], o.resid_mass, rej, rep.notes, "resid")
+    return rep
+
+
+def assert_parity(rep: Report, mode: int, exact: bool = False):
+    assert rep.unflagged_mismatches == 0, rep
+    if mode == 0:
+        # mismatches (all flagged) below 1e-4 of all decisions
+        assert rep.mismatches <= 1e-4 * max(rep.decisions, 1), rep
+    else:
+        assert rep.mismatches == 0 or (mode == 2 and rep.mismatches == rep.flagged_nkl), rep
+    assert rep.max_rel_px <= REL_TOL and rep.max_rel_qx <= REL_TOL, rep
+    assert rep.max_rel_nkl <= REL_TOL and rep.max_rel_resid <= REL_TOL, rep

@@ -1,0 +1,224 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on
+identical seeded inputs, for every workload and mode, plus edge cases."""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from parity import assert_parity, compare, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+S, G, K, TR = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import draft_token_verification_05_amd  # noqa: F401  (fails loudly if the library is missing)
+
+
+def check(w, **kw):
+    print(f"[parity] {w.name} mode={w.mode} B={w.batch} V={w.vocab} dtype={w.dtype} R_d={w.total_draft_rows}",
+          flush=True)
+    g = run_gpu(w, **kw)
+    o = oracle.verify_workload(w)
+    rep = compare(w, g, o)
+    print(f"[parity]   {rep}", flush=True)
+    assert_parity(rep, w.mode)
+    return g, o, rep
+
+
+# ---------------------------------------------------------------- the five workloads
+
+def test_tiny_stochastic_batched():
+    check(synthetic.make_tiny())
+
+
+def test_tiny_greedy_batched():
+    check(synthetic.make_tiny().with_mode(G))
+
+
+def test_tiny_single_steps_equal_batched():
+    """1000 independent steps: single-request calls give the batched call's answer."""
+    w = synthetic.make_tiny()
+    g_all = run_gpu(w, diagnostics=False)
+    t_off, d_off = w.t_off, w.d_off
+    for b in range(0, w.batch, 10):
+        ts, te, ds, de = t_off[b], t_off[b + 1], d_off[b], d_off[b + 1]
+        one = synthetic.Workload("tiny1", S, 1, w.vocab, w.dtype, w.gamma[b:b + 1], w.target[ts:te],
+                                 w.draft[ds:de], w.draft_tokens[ds:de], w.temperature[b:b + 1],
+                                 w.u_accept[ds:de], w.u_resample[b:b + 1], max_gamma=w.max_gamma)
+        g1 = run_gpu(one, diagnostics=False)
+        assert g1["num"][0] == g_all["num"][b]
+        assert (g1["tokens"] == g_all["tokens"][ts:te]).all()
+
+
+def test_llama3_stochastic():
+    check(synthetic.make_llama3(), out_nkl=True)
+
+
+def test_long_greedy():
+    check(synthetic.make_long(mode=G))
+
+
+def test_long_nkl():
+    check(synthetic.make_long(mode=K))
+
+
+def test_ragged_stochastic():
+    check(synthetic.make_ragged())
+
+
+@pytest.mark.parametrize("name", ["tree", "tree13"])
+def test_tree(name):
+    g, o, _ = check(synthetic.make(name))
+    assert (g["tree_node"] == o.tree_node).all()
+
+
+# ---------------------------------------------------------------- edge cases
+
+@pytest.mark.parametrize("mode", [S, G, K, TR])
+@pytest.mark.parametrize("V,dtype", [(1, "bf16"), (7, "f32"), (1000, "bf16"), (8191, "bf16"), (8193, "bf16"),
+                                     (20000, "f32"), (4099, "f32"), (16387, "bf16")])
+def test_ragged_small(mode, V, dtype):
+    """Ragged gamma including 0, V below / above one chunk, V not a multiple of
+    the 16-byte vector (unaligned rows take the scalar path)."""
+    w = synthetic.random_workload(seed=V % 97 + 3 * mode, mode=mode, B=13, V=V, dtype=dtype, gmax=6, gmin=0,
+                                  tree=(mode == TR), greedy_drafts=(mode == G))
+    check(w)
+
+
+@pytest.mark.parametrize("mode", [S, G, K, TR])
+def test_heavy_ties(mode):
+    """Integer-valued logits: many tied maxima, lowest index must win
+    everywhere (lanes, waves, chunks, workgroups)."""
+    w = synthetic.random_workload(seed=41 + mode, mode=mode, B=24, V=70000, dtype="bf16", gmax=5, gmin=1,
+                                  scale=1.5, spike=0.0, ties=True, tree=(mode == TR), greedy_drafts=(mode == G))
+    check(w)
+
+
+def test_tie_across_chunk_boundary():
+    """The maximum appears on both sides of a chunk boundary (8192 for bf16)
+    and at a later chunk: the lowest index is chosen."""
+    V = 3 * 8192 + 100
+    w = synthetic.random_workload(seed=5, mode=G, B=4, V=V, dtype="bf16", gmax=3, gmin=3, greedy_drafts=True)
+    tgt = synthetic.bf16_bits_to_f32(w.target).copy()
+    for r in range(tgt.shape[0]):
+        hi = np.float32(tgt[r].max() + 4.0)
+        for pos in (8191 + r % 2, 8192, 2 * 8192 + 5, V - 1):
+            tgt[r, pos] = hi
+    w.target = synthetic.f32_to_bf16_bits(tgt)
+    g, o, _ = check(w)
+    assert set(o.tokens[o.tokens >= 0].tolist()) <= {8191, 8192}
+
+
+def test_identical_rows():
+    """q == p: every draft accepted (stochastic), NKL exactly 0 (NKL mode)."""
+    w = synthetic.random_workload(seed=9, mode=S, B=8, V=50000, dtype="bf16", gmax=5, gmin=5)
+    t_off = w.t_off
+    rows = np.concatenate([np.arange(t_off[b], t_off[b] + w.gamma[b]) for b in range(w.batch)])
+    w.draft = w.target[rows].copy()
+    g, o, _ = check(w)
+    assert (g["num"] == w.gamma).all()
+    wk = w.with_mode(K, delta=1e-30)
+    g2, o2, _ = check(wk)
+    assert (g2["nkl"] == 0).all() and (g2["num"] == w.gamma).all()
+
+
+def test_invalid_requests_isolated():
+    w = synthetic.random_workload(seed=12, mode=S, B=10, V=3000, dtype="bf16", gmax=4, gmin=2)
+    d_off = w.d_off
+    w.draft_tokens = w.draft_tokens.copy()
+    w.temperature = w.temperature.copy()
+    w.u_accept = w.u_accept.copy()
+    w.u_resample = w.u_resample.copy()
+    w.draft_tokens[d_off[1]] = w.vocab       # token out of range
+    w.draft_tokens[d_off[2] + 1] = -5
+    w.temperature[3] = 0.0                   # bad temperature
+    w.temperature[4] = np.nan
+    w.u_accept[d_off[5]] = 1.0               # uniform out of [0, 1)
+    w.u_resample[6] = -0.25
+    g, o, _ = check(w)
+    for b in (1, 2, 3, 4, 5, 6):
+        assert g["num"][b] == -1
+    assert (g["num"][[0, 7, 8, 9]] >= 0).all()
+    for mode in (G, K):
+        wm = w.with_mode(mode)
+        wm.temperature = np.abs(np.nan_to_num(w.temperature, nan=1.0)) + 0.5
+        check(wm)
+
+
+def test_gamma_above_max_and_layout_errors():
+    w = synthetic.random_workload(seed=13, mode=G, B=6, V=2000, dtype="bf16", gmax=5, gmin=1,
+                                  greedy_drafts=True)
+    mg = int(np.sort(w.gamma)[-2])  # the largest gamma exceeds max_gamma
+    w.max_gamma = mg
+    g, o, _ = check(w)
+    assert (g["num"][w.gamma > mg] == -1).all()
+    # sum(gamma) disagrees with the host-known total: every request -1
+    import torch
+    import draft_token_verification_05_amd as sv
+    d = to_device(w)
+    d["gamma"][0] += 1
+    out = sv.verify(d["target"], None, d["tokens"], d["gamma"], None, None, None, G, max_gamma=64)
+    torch.cuda.synchronize()
+    assert (out.num_accepted.cpu().numpy() == -1).all()
+    d["gamma"][0] = -1
+    out = sv.verify(d["target"], None, d["tokens"], d["gamma"], None, None, None, G, max_gamma=64)
+    torch.cuda.synchronize()
+    assert (out.num_accepted.cpu().numpy() == -1).all()
+
+
+def test_tree_bad_parents():
+    w = synthetic.random_workload(seed=14, mode=TR, B=8, V=1000, dtype="bf16", gmax=6, gmin=2, tree=True)
+    w.tree_parents = w.tree_parents.copy()
+    d_off = w.d_off
+    w.tree_parents[d_off[2] + 1] = 2   # parent of node 2 must be < 2
+    w.tree_parents[d_off[5]] = -1
+    g, o, _ = check(w)
+    assert g["num"][2] == -1 and g["num"][5] == -1
+
+
+def test_chain_tree_equals_greedy_on_gpu():
+    w = synthetic.random_workload(seed=15, mode=G, B=20, V=9000, dtype="bf16", gmax=7, gmin=7,
+                                  greedy_drafts=True)
+    wt = w.with_mode(TR)
+    wt.tree_parents = np.tile(np.arange(7, dtype=np.int32), w.batch)
+    a = run_gpu(w)
+    b = run_gpu(wt)
+    assert (a["tokens"] == b["tokens"]).all() and (a["num"] == b["num"]).all()
+
+
+def test_deterministic_repeats():
+    w = synthetic.make_llama3(B=8)
+    d = to_device(w)
+    first = run_gpu(w, d)
+    for _ in range(10):
+        again = run_gpu(w, d)
+        for k in ("tokens", "num", "p_x", "q_x", "resid"):
+            assert np.array_equal(first[k], again[k], equal_nan=True), k
+
+
+def test_losslessness_chi_square_gpu():
+    """The HIP path's emitted tokens follow the target distribution (V = 8,
+    gamma = 4, 10^6 seeded trials, chi-square per position, Bonferroni)."""
+    from scipy import special, stats
+    n, V, gam = 1_000_000, 8, 4
+    rng = np.random.default_rng(2026)
+    t_rows = (3 * rng.standard_normal((gam + 1, V))).astype(np.float32)
+    d_rows = (t_rows[:gam] + rng.standard_normal((gam, V))).astype(np.float32)
+    P = special.softmax(t_rows.astype(np.float64), axis=1)
+    Q = special.softmax(d_rows.astype(np.float64), axis=1)
+    x = np.stack([rng.choice(V, size=n, p=Q[i]) for i in range(gam)], axis=1).astype(np.int32)
+    w = synthetic.Workload("chi2", S, n, V, "f32", np.full(n, gam, np.int32), np.tile(t_rows, (n, 1)),
+                           np.tile(d_rows, (n, 1)), x.ravel(), np.ones(n, np.float32),
+                           rng.random(n * gam).astype(np.float32), rng.random(n).astype(np.float32), max_gamma=gam)
+    g = run_gpu(w, diagnostics=False)
+    tok = g["tokens"].reshape(n, gam + 1)
+    pv = []
+    for k in range(gam + 1):
+        reached = g["num"] >= k
+        pv.append(stats.chisquare(np.bincount(tok[reached, k], minlength=V), P[k] * reached.sum()).pvalue)
+    assert min(pv) > 1e-3 / len(pv), pv

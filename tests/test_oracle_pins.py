@@ -501,3 +501,13 @@ def test_cdf_steps_are_strict():
         r = run(t, np.zeros((0, 4), np.float32), [0], [], None, [], [case["u_resample"]])
         assert r.num_accepted[0] == 0
         assert r.tokens.tolist() == [case["token"]], case
+
+
+def test_nkl_single_token_vocabulary():
+    """V = 1: KL / ln V is 0/0; both distributions are the same point mass, so
+    NKL is 0 and every draft is accepted (a reading, stated in the oracle)."""
+    t = np.array([[0.5], [1.0], [2.0]], np.float32)
+    d = np.array([[3.0], [-1.0]], np.float32)
+    r = run(t, d, [2], [0, 0], [0.7], mode=K, delta=0.15)
+    assert r.nkl.tolist() == [0.0, 0.0]
+    assert r.num_accepted[0] == 2 and r.tokens.tolist() == [0, 0, 0]
