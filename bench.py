@@ -1,0 +1,266 @@
+"""Benchmark of the verify step on one MI355X.
+
+One step = one spec_verify call over one batch of the Llama-3-shaped workload
+(B = 32 requests, gamma = 5 drafted tokens each, V = 128256, bf16 logits,
+stochastic mode: the whole path -- prep, row statistics with the fused
+decision, residual/bonus draw).  Inputs are resident in HBM; each step reads a
+different copy of them (enough copies to cover > 1 GiB), so the 256 MB
+Infinity Cache cannot serve the logits of the step before.
+
+Prints ONE JSON line with verified draft positions/s, the roofline of the
+dominant kernel (the row-statistics kernel, timed with HIP events recorded on
+the call's stream around it in every timed step) and the CPU oracle timed on
+the host cores on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3]
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_rowstats_llama3.txt")
+KERNEL_SRC = os.path.join(ROOT, "draft_token_verification_05_amd", "csrc", "kernels.hip")
+
+WORKLOADS = {
+    # name: (maker kwargs, mode, description)
+    "llama3": ({}, 0, "llama3-shaped stochastic verify: B=32, gamma=5, V=128256, bf16"),
+    "long_greedy": ({"mode": 1}, 1, "long parallel drafts, greedy: B=64, gamma=16, V=128256, bf16"),
+    "long_nkl": ({"mode": 2}, 2, "long parallel drafts, NKL delta=0.15, T=0.6: B=64, gamma=16, V=128256, bf16"),
+    "ragged": ({}, 0, "large-batch ragged stochastic: B=256, gamma~U{1..8}, V=152064, bf16"),
+    "tree": ({}, 3, "tree draft greedy verify: B=16, 16-node trees, V=128256, bf16"),
+}
+
+
+def kernel_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per row-statistics launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source (else None)."""
+    if not os.path.exists(PROFILE_TRAFFIC):
+        return None
+    kv = {}
+    for line in open(PROFILE_TRAFFIC):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernels_hip_sha256_16") != kernel_hash():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Hip:
+    """The few HIP event calls the benchmark needs (same runtime as torch)."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads torch's HIP runtime first)
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def events(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = ev.value
+        return arr
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, arr):
+        for e in arr:
+            self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def algorithmic_bytes(w, num_accepted):
+    """Bytes one step must read: every logit row the mode needs once, plus the
+    terminal draw's re-read (stochastic: 2 rows after a rejection, 1 row for a
+    bonus -- which the row-statistics pass never reads)."""
+    import numpy as np
+    s = 2 if w.dtype == "bf16" else 4
+    R_d, B, V = w.total_draft_rows, w.batch, w.vocab
+    if w.mode == 0:
+        rowstats = 2 * R_d * V * s
+        rej = int(np.sum(num_accepted < w.gamma))
+        draw = (2 * rej + (B - rej)) * V * s
+        return rowstats, rowstats + draw
+    if w.mode == 2:
+        rowstats = (2 * R_d + B) * V * s
+        return rowstats, rowstats
+    rowstats = (R_d + B) * V * s
+    return rowstats, rowstats
+
+
+def run_gpu(name, steps, warmup, copies_bytes=1 << 30):
+    import numpy as np
+    import torch
+
+    import synthetic
+    from parity import to_device
+
+    import draft_token_verification_05_amd as sv
+
+    kw, mode, desc = WORKLOADS[name]
+    maker = {"llama3": synthetic.make_llama3, "long_greedy": synthetic.make_long, "long_nkl": synthetic.make_long,
+             "ragged": synthetic.make_ragged, "tree": synthetic.make_tree}[name]
+    w = maker(**kw)
+    dev = torch.device("cuda:0")
+    soft = mode in (0, 2)
+    base = to_device(w)
+    per_copy = w.logit_bytes()
+    ncopies = max(2, min(64, -(-copies_bytes // per_copy)))
+    copies = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()} for _ in range(ncopies - 1)]
+    B, V, R_d = w.batch, w.vocab, w.total_draft_rows
+    stream = torch.cuda.current_stream(dev)
+    cfg0 = sv.make_config(B, V, sv.SV_DTYPE_BF16 if w.dtype == "bf16" else sv.SV_DTYPE_F32, w.max_gamma, R_d)
+    ws = torch.zeros(max(sv.spec_verify_workspace_size(cfg0), 256), dtype=torch.uint8, device=dev)
+    out_tokens = torch.empty(R_d + B, dtype=torch.int32, device=dev)
+    out_num = torch.empty(B, dtype=torch.int32, device=dev)
+    out_nkl = torch.empty(max(R_d, 1), dtype=torch.float32, device=dev)
+    hip = Hip()
+    ev = hip.events(4 * steps)
+    ev_all = hip.events(2)
+
+    def make_args(d, events_ptr):
+        cfg = sv.make_config(B, V, cfg0.dtype, w.max_gamma, R_d, stream.cuda_stream, ws.data_ptr(), ws.numel(),
+                             phase_events=events_ptr)
+        a = (d["target"].data_ptr(), d["draft"].data_ptr() if soft else 0, d["tokens"].data_ptr(),
+             d["gamma"].data_ptr(), d["temp"].data_ptr() if soft else 0, d["ua"].data_ptr() if mode == 0 else 0,
+             d["ur"].data_ptr() if mode == 0 else 0, mode, w.delta,
+             d["parents"].data_ptr() if mode == 3 else 0, out_tokens.data_ptr(), out_num.data_ptr(),
+             out_nkl.data_ptr() if mode == 2 else 0)
+        return a, cfg
+
+    plain = [make_args(d, 0) for d in copies]
+    ev_base = ctypes.addressof(ev)
+    timed = [make_args(copies[k % ncopies], ev_base + 4 * k * ctypes.sizeof(ctypes.c_void_p))
+             for k in range(steps)]
+    for k in range(warmup):
+        a, cfg = plain[k % ncopies]
+        st = sv.spec_verify(*a, cfg)
+        if st != 0:
+            raise RuntimeError(sv.spec_verify_status_string(st))
+    torch.cuda.synchronize()
+    num_acc = out_num.cpu().numpy()
+    t0 = time.perf_counter()
+    hip.lib.hipEventRecord(ctypes.c_void_p(ev_all[0]), ctypes.c_void_p(stream.cuda_stream))
+    for k in range(steps):
+        a, cfg = timed[k]
+        st = sv.spec_verify(*a, cfg)
+        if st != 0:
+            raise RuntimeError(sv.spec_verify_status_string(st))
+    hip.lib.hipEventRecord(ctypes.c_void_p(ev_all[1]), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = hip.elapsed_ms(ev_all[0], ev_all[1])
+    rs = np.array([hip.elapsed_ms(ev[4 * k + 1], ev[4 * k + 2]) for k in range(steps)])
+    hip.destroy(ev)
+    hip.destroy(ev_all)
+    rowstats_bytes, step_bytes = algorithmic_bytes(w, num_acc)
+    positions = int(w.gamma.sum())
+    return dict(w=w, desc=desc, mode=mode, steps=steps, ncopies=ncopies, total_ms=total_ms, wall_s=wall,
+                ms_per_step=total_ms / steps, rowstats_ms=float(rs.mean()), rowstats_med_ms=float(np.median(rs)),
+                rowstats_bytes=rowstats_bytes, step_bytes=step_bytes, positions=positions)
+
+
+def cpu_baseline(name, budget_s=8.0):
+    import synthetic
+    import oracle
+    kw, _, _ = WORKLOADS[name]
+    maker = {"llama3": synthetic.make_llama3, "long_greedy": synthetic.make_long, "long_nkl": synthetic.make_long,
+             "ragged": synthetic.make_ragged, "tree": synthetic.make_tree}[name]
+    w = maker(**kw)
+    threads = oracle.max_threads()
+    oracle.verify_workload(w, nthreads=threads)  # warm (page-in)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.verify_workload(w, nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    pos = int(w.gamma.sum()) * reps
+    return {"value": pos / el, "unit": "verified draft positions/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full batches of the {name} workload ({int(w.gamma.sum())} positions each), "
+                      f"{el:.1f} s wall on {threads} host threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="llama3", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="only run 10 device-to-device copies of MIB MiB (calibrates HBM byte counters)")
+    args = ap.parse_args()
+    if args.calib_copy:
+        import torch
+        src = torch.empty(args.calib_copy << 20, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": args.calib_copy << 20, "launches": 10}), flush=True)
+        return
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(requests are independent, so more GPUs would each run their own share).", file=sys.stderr)
+        sys.exit(2)
+    r = run_gpu(args.workload, args.steps, args.warmup)
+    w = r["w"]
+    value = r["positions"] / (r["ms_per_step"] * 1e-3)
+    achieved = r["rowstats_bytes"] / (r["rowstats_ms"] * 1e-3) / 1e9
+    traffic = load_traffic() if args.workload == "llama3" else None
+    line = {
+        "metric": "verified draft positions/sec at V=128256 (bf16); achieved HBM GB/s vs peak",
+        "value": round(value, 1),
+        "unit": "verified draft positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": r["desc"], "batch": w.batch, "gamma": int(w.gamma.max()), "vocab": w.vocab,
+                   "logits": w.dtype, "mode": ["stochastic", "greedy", "nkl", "tree"][r["mode"]],
+                   "positions_per_step": r["positions"], "input_copies_rotated": r["ncopies"],
+                   "step_GBps": round(r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1),
+                   "step_frac_of_peak": round(r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "roofline": {"bound": "hbm", "kernel": "k_rowstats", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": r["rowstats_bytes"],
+                     "avg_launch_us": round(r["rowstats_ms"] * 1e3, 3)},
+        "cpu_baseline": None if args.no_cpu else cpu_baseline(args.workload),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

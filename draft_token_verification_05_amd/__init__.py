@@ -58,6 +58,12 @@ class SpecVerifyError(RuntimeError):
 
 
 def _load() -> ctypes.CDLL:
+    # PyTorch ships its own HIP runtime; load it first so that this library
+    # binds to the same runtime (one HIP runtime per process).
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libspecverify.so is not built ({LIB_PATH}); run __graft_entry__.build() "
                           "or python draft_token_verification_05_amd/build.py")
@@ -121,6 +127,25 @@ class VerifyOutput:
     q_x: Optional["torch.Tensor"] = None
     resid_mass: Optional["torch.Tensor"] = None
     tree_node: Optional["torch.Tensor"] = None
+
+
+_WORKSPACES = {}
+
+
+def workspace_for(cfg: sv_config, device) -> "torch.Tensor":
+    """A zero-filled workspace for this configuration, cached per device and
+    configuration.  spec_verify leaves its counters at zero after every
+    completed call, so a workspace is reused as is by later calls with the
+    same configuration on the same stream."""
+    import torch
+    key = (str(device), cfg.batch, cfg.vocab, cfg.dtype, cfg.max_gamma, cfg.total_draft_rows)
+    ws = _WORKSPACES.get(key)
+    if ws is None:
+        ws = torch.zeros(max(spec_verify_workspace_size(cfg), 256), dtype=torch.uint8, device=device)
+        if len(_WORKSPACES) > 64:
+            _WORKSPACES.clear()
+        _WORKSPACES[key] = ws
+    return ws
 
 
 def _ptr(t) -> int:
@@ -196,8 +221,10 @@ def verify(target_logits, draft_logits, draft_tokens, gamma_per_req, temperature
         stream = torch.cuda.current_stream(dev)
     cfg = make_config(B, V, dt, max_gamma, R_d, stream=int(stream.cuda_stream))
     need = spec_verify_workspace_size(cfg)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    if workspace is None:
+        workspace = workspace_for(cfg, dev)
+    elif workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
     cfg.workspace = workspace.data_ptr()
     cfg.workspace_bytes = workspace.numel()
     cfg.out_p_x, cfg.out_q_x = _ptr(p_x) or None, _ptr(q_x) or None

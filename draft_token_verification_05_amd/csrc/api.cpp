@@ -146,7 +146,8 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   hipEvent_t* ev = static_cast<hipEvent_t*>(cfg->phase_events);
   hipError_t e;
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e);
-  if ((e = (hipError_t)sv::launch_prep(p, s)) != hipSuccess) return hip_fail(e);
+  // small batches scan their offsets inside the statistics kernel
+  if (B > sv::kLdsBatch && (e = (hipError_t)sv::launch_prep(p, s)) != hipSuccess) return hip_fail(e);
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e);
   if ((e = (hipError_t)sv::launch_rowstats(p, vec, s)) != hipSuccess) return hip_fail(e);
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e);

@@ -251,6 +251,91 @@ __device__ __forceinline__ float exp_hp(float dx, float Lhi, float Llo) {
 }
 
 // ----------------------------------------------------------------------------
+// Cross-workgroup publication.  Records that one workgroup hands to another
+// inside a launch are written and read with device-scope (sc1) accesses, which
+// go to the device-coherent level instead of an XCD's private L2; the writer
+// waits for its stores to complete before it bumps the completion counter, and
+// the reader only loads after it has seen the final count.  This gives the
+// release/acquire ordering the merge needs without an L2 writeback per
+// workgroup (an agent-scope release fence flushes the whole L2 of the XCD).
+// ----------------------------------------------------------------------------
+
+template <class T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T ld_dev(T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// all earlier memory operations of this thread have completed
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
+// counter increment after the thread's published stores completed; returns the old count
+__device__ __forceinline__ unsigned signal_n(uint32_t* cnt, unsigned n) {
+  wait_stores();
+  return __hip_atomic_fetch_add(cnt, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned signal(uint32_t* cnt) { return signal_n(cnt, 1u); }
+
+__device__ __forceinline__ void put_part_a(PartA* q, const PartA& v) {
+  st_dev(&q->s_t, v.s_t);
+  st_dev(&q->s_d, v.s_d);
+  st_dev(&q->w, v.w);
+  st_dev(&q->m_t, v.m_t);
+  st_dev(&q->m_d, v.m_d);
+  st_dev(&q->idx, v.idx);
+}
+__device__ __forceinline__ PartA get_part_a(PartA* q) {
+  PartA v;
+  v.s_t = ld_dev(&q->s_t);
+  v.s_d = ld_dev(&q->s_d);
+  v.w = ld_dev(&q->w);
+  v.m_t = ld_dev(&q->m_t);
+  v.m_d = ld_dev(&q->m_d);
+  v.idx = ld_dev(&q->idx);
+  v.pad = 0;
+  return v;
+}
+__device__ __forceinline__ void put_stat(TaskStat* q, const TaskStat& v) {
+  st_dev(&q->s_t, v.s_t);
+  st_dev(&q->s_d, v.s_d);
+  st_dev(&q->w, v.w);
+  st_dev(&q->m_t, v.m_t);
+  st_dev(&q->m_d, v.m_d);
+  st_dev(&q->kl, v.kl);
+  st_dev(&q->idx, v.idx);
+}
+__device__ __forceinline__ TaskStat get_stat(TaskStat* q) {
+  TaskStat v;
+  v.s_t = ld_dev(&q->s_t);
+  v.s_d = ld_dev(&q->s_d);
+  v.w = ld_dev(&q->w);
+  v.m_t = ld_dev(&q->m_t);
+  v.m_d = ld_dev(&q->m_d);
+  v.kl = ld_dev(&q->kl);
+  v.idx = ld_dev(&q->idx);
+  return v;
+}
+__device__ __forceinline__ int get_idx(TaskStat* q) { return ld_dev(&q->idx); }
+__device__ __forceinline__ void put_part_c(PartC* q, const PartC& v) {
+  st_dev(&q->a, v.a);
+  st_dev(&q->b, v.b);
+  st_dev(&q->ap, v.ap);
+  st_dev(&q->bp, v.bp);
+  st_dev(&q->m, v.m);
+}
+__device__ __forceinline__ PartC get_part_c(PartC* q) {
+  PartC v;
+  v.a = ld_dev(&q->a);
+  v.b = ld_dev(&q->b);
+  v.ap = ld_dev(&q->ap);
+  v.bp = ld_dev(&q->bp);
+  v.m = ld_dev(&q->m);
+  v.pad[0] = v.pad[1] = v.pad[2] = 0;
+  return v;
+}
+
+// ----------------------------------------------------------------------------
 // k_prep
 // ----------------------------------------------------------------------------
 
@@ -341,8 +426,7 @@ __device__ void finish_invalid(const Params& p, int b, int t0, int g) {
 // With a single token both distributions are the same point mass: NKL = 0.
 __device__ __forceinline__ float nkl_of(const TaskStat& s, int V) { return V > 1 ? s.kl / logf((float)V) : 0.0f; }
 
-__device__ void decide_stochastic(const Params& p, int b, DecideShared& sh) {
-  const int g = p.gamma[b], t0 = p.t_off[b], d0 = p.d_off[b];
+__device__ void decide_stochastic(const Params& p, int b, int g, int t0, int d0, DecideShared& sh) {
   const float T = p.temp[b];
   bool bad = !(g <= p.max_gamma) || !temp_ok(T) || !unit_ok(p.ur[b]);
   int first = INT_MAX;
@@ -353,8 +437,8 @@ __device__ void decide_stochastic(const Params& p, int b, DecideShared& sh) {
       bad = true;
       continue;
     }
-    const TaskStat s = p.stat[d0 + i];
-    const float tx = p.gat[2 * (d0 + i)], dx = p.gat[2 * (d0 + i) + 1];
+    const TaskStat s = get_stat(p.stat + d0 + i);
+    const float tx = ld_dev(p.gat + 2 * (d0 + i)), dx = ld_dev(p.gat + 2 * (d0 + i) + 1);
     // log p(x) - log q(x) = ((t_x - m_t) - (d_x - m_d)) / T + log(s_d / s_t)
     const float lr = ((tx - s.m_t) - (dx - s.m_d)) / T + (float)log(s.s_d / s.s_t);
     const float alpha = fminf(1.0f, expf(lr));
@@ -382,7 +466,7 @@ __device__ void decide_stochastic(const Params& p, int b, DecideShared& sh) {
     tm.trow = t0 + j;
     tm.pad = 0;
     if (j < g) {
-      const TaskStat s = p.stat[d0 + j];
+      const TaskStat s = get_stat(p.stat + d0 + j);
       tm.kind = kTermResidual;
       tm.drow = d0 + j;
       tm.m_t = s.m_t;
@@ -399,8 +483,7 @@ __device__ void decide_stochastic(const Params& p, int b, DecideShared& sh) {
 
 // greedy (mode 1) and NKL (mode 2)
 template <int MODE>
-__device__ void decide_argmax_chain(const Params& p, int b, DecideShared& sh) {
-  const int g = p.gamma[b], t0 = p.t_off[b], d0 = p.d_off[b];
+__device__ void decide_argmax_chain(const Params& p, int b, int g, int t0, int d0, DecideShared& sh) {
   bool bad = !(g <= p.max_gamma);
   float T = 1.0f;
   if (MODE == SV_MODE_NKL) {
@@ -416,13 +499,13 @@ __device__ void decide_argmax_chain(const Params& p, int b, DecideShared& sh) {
     }
     bool acc;
     if (MODE == SV_MODE_GREEDY) {
-      acc = (x == p.stat[t0 + i].idx);
+      acc = (x == get_idx(p.stat + t0 + i));
     } else {
-      const TaskStat s = p.stat[d0 + i];
+      const TaskStat s = get_stat(p.stat + t0 + i);  // NKL tasks are target rows
       const float nkl = nkl_of(s, p.V);
       p.out_nkl[d0 + i] = nkl;
       if (p.out_p_x || p.out_q_x) {
-        const float tx = p.gat[2 * (d0 + i)], dx = p.gat[2 * (d0 + i) + 1];
+        const float tx = ld_dev(p.gat + 2 * (d0 + i)), dx = ld_dev(p.gat + 2 * (d0 + i) + 1);
         if (p.out_p_x) p.out_p_x[d0 + i] = (float)((double)expf((tx - s.m_t) / T) / s.s_t);
         if (p.out_q_x) p.out_q_x[d0 + i] = (float)((double)expf((dx - s.m_d) / T) / s.s_d);
       }
@@ -441,9 +524,9 @@ __device__ void decide_argmax_chain(const Params& p, int b, DecideShared& sh) {
   }
   int term_tok;
   if (MODE == SV_MODE_GREEDY)
-    term_tok = p.stat[t0 + j].idx;
+    term_tok = get_idx(p.stat + t0 + j);
   else
-    term_tok = j < g ? p.stat[d0 + j].idx : p.stat[p.R_d + b].idx;
+    term_tok = get_idx(p.stat + t0 + j);
   for (int k = threadIdx.x; k <= g; k += kThreads)
     p.out_tokens[t0 + k] = k < j ? p.tokens[d0 + k] : (k == j ? term_tok : -1);
   if (threadIdx.x == 0) p.out_num[b] = j;
@@ -451,8 +534,8 @@ __device__ void decide_argmax_chain(const Params& p, int b, DecideShared& sh) {
 
 // Tree resolve.  node_info[n] packs (depth << 1) | accepted; parents precede
 // children, so one ordered pass settles every node.
-__device__ void decide_tree(const Params& p, int b, DecideShared& sh, int16_t* node_info, int16_t* par) {
-  const int g = p.gamma[b], t0 = p.t_off[b], d0 = p.d_off[b];
+__device__ void decide_tree(const Params& p, int b, int g, int t0, int d0, DecideShared& sh, int16_t* node_info,
+                            int16_t* par) {
   const int N = g + 1;
   bool bad = !(g <= p.max_gamma);
   if (threadIdx.x == 0) sh.bad = 0;
@@ -466,7 +549,7 @@ __device__ void decide_tree(const Params& p, int b, DecideShared& sh, int16_t* n
         continue;
       }
       par[n] = (int16_t)pa;
-      node_info[n] = (int16_t)((x == p.stat[t0 + pa].idx) ? 1 : 0);  // edge match, before ancestry
+      node_info[n] = (int16_t)((x == get_idx(p.stat + t0 + pa)) ? 1 : 0);  // edge match, before ancestry
     }
   }
   if (bad) sh.bad = 1;
@@ -495,7 +578,7 @@ __device__ void decide_tree(const Params& p, int b, DecideShared& sh, int16_t* n
   for (int k = depth + 1 + threadIdx.x; k <= g; k += kThreads) p.out_tokens[t0 + k] = -1;
   if (threadIdx.x == 0) {
     for (int v = best; v != 0; v = par[v]) p.out_tokens[t0 + (node_info[v] >> 1) - 1] = p.tokens[d0 + v - 1];
-    p.out_tokens[t0 + depth] = p.stat[t0 + best].idx;
+    p.out_tokens[t0 + depth] = get_idx(p.stat + t0 + best);
     p.out_num[b] = depth;
     if (p.out_tree_node) p.out_tree_node[b] = best;
   }
@@ -579,294 +662,459 @@ __device__ double kl_second_pass(const Params& p, int trow, int drow, float m_t,
   return block_sum_d(acc, shd);
 }
 
+// Lane-level running statistics of one row over the chunks a workgroup streams.
+struct LaneRow {
+  float m;    // running maximum (raw logits)
+  float s;    // sum exp2((x - m) * L) over the lane's elements so far
+  int idx;    // lowest index attaining m (argmax rows)
+};
+
+// Folds NE new elements v (positions pos0 + e, e in vector order) into r.
+template <int NE, int P, bool IDX>
+__device__ __forceinline__ void fold_row(LaneRow& r, const float* v, float Lhi, bool soft, int64_t pos_base,
+                                         int64_t pos_stride, float pad) {
+  float mc = v[0];
+#pragma unroll
+  for (int e = 1; e < NE; ++e) mc = fmaxf(mc, v[e]);
+  if (mc == pad) return;  // every element of this lane lies past the end of the row
+  if (IDX && mc > r.m) {
+    int ic = INT_MAX;
+#pragma unroll
+    for (int e = NE - 1; e >= 0; --e)
+      if (v[e] == mc) ic = (int)(pos_base + (int64_t)(e / P) * pos_stride + (e % P));
+    r.idx = ic;
+  }
+  const float M = fmaxf(r.m, mc);
+  if (soft) {
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int e = 0; e < NE; e += 4) {
+      a0 += __builtin_amdgcn_exp2f((v[e] - M) * Lhi);
+      a1 += __builtin_amdgcn_exp2f((v[e + 1] - M) * Lhi);
+      a2 += __builtin_amdgcn_exp2f((v[e + 2] - M) * Lhi);
+      a3 += __builtin_amdgcn_exp2f((v[e + 3] - M) * Lhi);
+    }
+    r.s = r.s * __builtin_amdgcn_exp2f((r.m - M) * Lhi) + ((a0 + a1) + (a2 + a3));
+  }
+  r.m = M;
+}
+
+// Draft row of a pair, with the KL cross term W = sum e^{(d - m_d)/T} (d - t);
+// the same accumulation pattern as fold_row keeps identical rows bit-identical.
+template <int NE>
+__device__ __forceinline__ void fold_draft_w(LaneRow& r, float& W, const float* vd, const float* vt, float Lhi,
+                                             float pad) {
+  float mc = vd[0];
+#pragma unroll
+  for (int e = 1; e < NE; ++e) mc = fmaxf(mc, vd[e]);
+  if (mc == pad) return;
+  const float M = fmaxf(r.m, mc);
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
+#pragma unroll
+  for (int e = 0; e < NE; e += 4) {
+    const float e0 = __builtin_amdgcn_exp2f((vd[e] - M) * Lhi);
+    const float e1 = __builtin_amdgcn_exp2f((vd[e + 1] - M) * Lhi);
+    const float e2 = __builtin_amdgcn_exp2f((vd[e + 2] - M) * Lhi);
+    const float e3 = __builtin_amdgcn_exp2f((vd[e + 3] - M) * Lhi);
+    a0 += e0;
+    a1 += e1;
+    a2 += e2;
+    a3 += e3;
+    w0 = fmaf(e0, vd[e] - vt[e], w0);
+    w1 = fmaf(e1, vd[e + 1] - vt[e + 1], w1);
+    w2 = fmaf(e2, vd[e + 2] - vt[e + 2], w2);
+    w3 = fmaf(e3, vd[e + 3] - vt[e + 3], w3);
+  }
+  const float f = __builtin_amdgcn_exp2f((r.m - M) * Lhi);
+  r.s = r.s * f + ((a0 + a1) + (a2 + a3));
+  W = W * f + ((w0 + w1) + (w2 + w3));
+  r.m = M;
+}
+
+// Request of a task (task index = draft row for stochastic pairs, target row
+// otherwise): offsets come from LDS (small batches) or from the prep kernel.
+struct ReqInfo {
+  int b, g, t0, d0;
+};
+
+template <int MODE>
+__device__ __forceinline__ ReqInfo locate(const Params& p, const int* s_off, bool lds, int task) {
+  ReqInfo r;
+  if (lds) {
+    // last b with off(b) <= task, off = d_off (pairs) or t_off = d_off + b (rows)
+    int lo = 0, hi = p.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      const int off = MODE == SV_MODE_STOCHASTIC ? s_off[mid] : s_off[mid] + mid;
+      if (off <= task) lo = mid; else hi = mid - 1;
+    }
+    r.b = lo;
+    r.d0 = s_off[lo];
+    r.g = s_off[lo + 1] - s_off[lo];
+  } else {
+    r.b = MODE == SV_MODE_STOCHASTIC ? p.pair2req[task] : p.row2req[task];
+    r.d0 = p.d_off[r.b];
+    r.g = p.d_off[r.b + 1] - r.d0;
+  }
+  r.t0 = r.d0 + r.b;
+  return r;
+}
+
+struct StatsShared {
+  float m[2][kWaves];
+  float s[2][kWaves];
+  float w[kWaves];
+  int i[kWaves];
+  double d[2 + kWaves];
+  int flag;
+  int refine;
+  int scan[kThreads / 64];
+  DecideShared dec;
+};
+
+// Persistent row-statistics kernel.  The (task, chunk) items, task-major, are
+// split into one contiguous range per workgroup; a workgroup streams its
+// range with the next chunk's loads in flight while it folds the current one,
+// and publishes one partial per task segment.  The last segment of a task
+// merges the partials (in vocabulary order), and the last task of a request
+// runs the decision.
 template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads) void k_rowstats(Params p) {
+__global__ __launch_bounds__(kThreads) void k_stats(Params p) {
   constexpr int P = Elem<DT>::P;
-  constexpr int NE = kUA * P;  // elements per thread per row
-  __shared__ RowShared sh;
-  // tree resolve scratch exists in the tree-mode kernel only
+  constexpr int NE = kUA * P;  // elements per thread per row per chunk
+  constexpr int64_t CH = (int64_t)kThreads * NE;
+  constexpr float kPad = Elem<DT>::kPad;
+  constexpr bool IDX = MODE != SV_MODE_STOCHASTIC;
+  __shared__ int s_off[kLdsBatch + 1];
+  __shared__ StatsShared sh;
   __shared__ int16_t tree_info[MODE == SV_MODE_TREE_GREEDY ? SV_MAX_GAMMA + 1 : 1];
   __shared__ int16_t tree_par[MODE == SV_MODE_TREE_GREEDY ? SV_MAX_GAMMA + 1 : 1];
-
-  if (p.hdr[0] != 0) return;  // layout error (found by k_prep)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int item = blockIdx.x;
-  const int task = item / p.nch_a;
-  const int chunk = item - task * p.nch_a;
   const int64_t V = p.V;
+  const bool lds = p.B <= kLdsBatch;
 
-  // task -> (request, target row, draft row)
-  int b, trow, drow;
-  bool pair;
-  if (MODE == SV_MODE_STOCHASTIC || (MODE == SV_MODE_NKL && task < p.R_d)) {
-    b = p.pair2req[task];
-    trow = task + b;
-    drow = task;
-    pair = true;
-  } else if (MODE == SV_MODE_NKL) {
-    b = task - p.R_d;
-    trow = p.d_off[b + 1] + b;  // t_off[b] + gamma_b: the bonus row
-    drow = -1;
-    pair = false;
-  } else {
-    b = p.row2req[task];
-    trow = task;
-    drow = -1;
-    pair = false;
+  // ---- packed offsets: exclusive scan of gamma in LDS (every workgroup)
+  if (lds) {
+    if (tid == 0) sh.flag = 0;
+    __syncthreads();
+    int carry = 0;
+    for (int base = 0; base < p.B; base += kThreads) {
+      const int bb = base + tid;
+      int g = bb < p.B ? p.gamma[bb] : 0;
+      if (g < 0 || g > p.R_d) {
+        sh.flag = 1;  // every writer stores 1
+        g = 0;
+      }
+      int incl = g;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      if (lane == 63) sh.scan[wv] = incl;
+      __syncthreads();
+      int before = 0, tile = 0;
+#pragma unroll
+      for (int k = 0; k < kWaves; ++k) {
+        if (k < wv) before += sh.scan[k];
+        tile += sh.scan[k];
+      }
+      if (bb < p.B) s_off[bb] = carry + before + incl - g;
+      carry += tile;  // at most B * R_d: bounded because each g <= R_d
+      __syncthreads();
+    }
+    if (tid == 0) s_off[p.B] = carry;
+    __syncthreads();
+    const bool bad = sh.flag != 0 || carry != p.R_d;
+    if (blockIdx.x == 0) {
+      // offsets for the draw kernel; layout flag
+      for (int bb = tid; bb <= p.B; bb += kThreads) {
+        p.d_off[bb] = s_off[bb];
+        p.t_off[bb] = s_off[bb] + bb;
+      }
+      if (tid == 0) p.hdr[0] = bad ? 1 : 0;
+      if (bad)
+        for (int bb = tid; bb < p.B; bb += kThreads) p.out_num[bb] = -1;
+    }
+    if (bad) return;
+  } else if (p.hdr[0] != 0) {
+    return;  // layout error found by k_prep
   }
-  const bool want_idx = MODE != SV_MODE_STOCHASTIC;
-  const bool want_soft = pair;
-  const bool want_w = pair && p.want_w;
 
-  // issue the loads
-  const int64_t e_chunk = (int64_t)chunk * (kThreads * NE);
-  uint4 qt[kUA], qd[kUA];
-#pragma unroll
-  for (int k = 0; k < kUA; ++k) qt[k] = fetch<DT, VEC>(p.target, trow, V, e_chunk + ((int64_t)k * kThreads + tid) * P);
-  if (pair) {
-#pragma unroll
-    for (int k = 0; k < kUA; ++k) qd[k] = fetch<DT, VEC>(p.draft, drow, V, e_chunk + ((int64_t)k * kThreads + tid) * P);
-  }
-  // exp((x - m)/T) = exp2((x - m) * L), L = log2(e)/T = Lhi + Llo
+  // ---- this workgroup's items
+  const int nch = p.nch_a;
+  const int64_t N = (int64_t)p.n_task * nch;
+  const int64_t G = gridDim.x;
+  const int64_t i0 = (int64_t)blockIdx.x * N / G, i1 = ((int64_t)blockIdx.x + 1) * N / G;
+  if (i0 >= i1) return;
+
+  // segment state (uniform across the workgroup)
+  int task = -1, b = 0, g = 0, t0 = 0, d0 = 0, trow = 0, drow = -1, seg_first = 0, x = -1;
+  bool pair = false;
   float T = 1.0f, Lhi = 0.0f, Llo = 0.0f;
-  if (want_soft) {
-    T = p.temp[b];
-    const double Ld = kLog2eD / (double)T;
-    Lhi = (float)Ld;
-    Llo = (float)(Ld - (double)Lhi);
-  }
-  // gather of the logits at the drafted token (one workgroup per pair holds it)
+  LaneRow rt{kPad, 0.f, INT_MAX}, rd{kPad, 0.f, INT_MAX};
+  float W = 0.f;
   float gx_t = 0.f, gx_d = 0.f;
   bool gathered = false;
-  if (pair && tid == 0) {
-    const int x = p.tokens[drow];
-    if (x >= e_chunk && x < e_chunk + (int64_t)kThreads * NE && x < V && x >= 0) {
+
+  auto rows_of = [&](int tk, int& tr, int& dr, bool& pr, ReqInfo& ri) {
+    ri = locate<MODE>(p, s_off, lds, tk);
+    if (MODE == SV_MODE_STOCHASTIC) {
+      tr = tk + ri.b;
+      dr = tk;
+      pr = true;
+    } else {
+      tr = tk;
+      const int i = tk - ri.t0;
+      pr = (MODE == SV_MODE_NKL) && i < ri.g;
+      dr = pr ? ri.d0 + i : -1;
+    }
+  };
+
+  // prefetch the first chunk
+  uint4 cur_t[kUA], cur_d[kUA], nxt_t[kUA], nxt_d[kUA];
+  int n_trow, n_drow;
+  bool n_pair;
+  {
+    ReqInfo ri;
+    rows_of((int)(i0 / nch), n_trow, n_drow, n_pair, ri);
+    const int64_t e0 = (i0 % nch) * CH;
+#pragma unroll
+    for (int k = 0; k < kUA; ++k) {
+      nxt_t[k] = fetch<DT, VEC>(p.target, n_trow, V, e0 + ((int64_t)k * kThreads + tid) * P);
+      if (n_pair) nxt_d[k] = fetch<DT, VEC>(p.draft, n_drow, V, e0 + ((int64_t)k * kThreads + tid) * P);
+    }
+  }
+
+  for (int64_t it = i0; it < i1; ++it) {
+    const int tk = (int)(it / nch);
+    const int chunk = (int)(it - (int64_t)tk * nch);
+#pragma unroll
+    for (int k = 0; k < kUA; ++k) {
+      cur_t[k] = nxt_t[k];
+      cur_d[k] = nxt_d[k];
+    }
+    if (tk != task) {  // a new task segment starts
+      ReqInfo ri;
+      rows_of(tk, trow, drow, pair, ri);
+      task = tk;
+      b = ri.b;
+      g = ri.g;
+      t0 = ri.t0;
+      d0 = ri.d0;
+      seg_first = chunk;
+      rt = LaneRow{kPad, 0.f, INT_MAX};
+      rd = LaneRow{kPad, 0.f, INT_MAX};
+      W = 0.f;
+      gathered = false;
+      if (pair) {
+        T = p.temp[b];
+        const double Ld = kLog2eD / (double)T;
+        Lhi = (float)Ld;
+        Llo = (float)(Ld - (double)Lhi);
+        x = p.tokens[drow];
+      }
+    }
+    // next chunk's loads go out before this one is folded
+    if (it + 1 < i1) {
+      const int tk2 = (int)((it + 1) / nch);
+      if (tk2 != task) {
+        ReqInfo ri;
+        rows_of(tk2, n_trow, n_drow, n_pair, ri);
+      } else {
+        n_trow = trow;
+        n_drow = drow;
+        n_pair = pair;
+      }
+      const int64_t e1 = ((it + 1) - (int64_t)tk2 * nch) * CH;
+#pragma unroll
+      for (int k = 0; k < kUA; ++k) {
+        nxt_t[k] = fetch<DT, VEC>(p.target, n_trow, V, e1 + ((int64_t)k * kThreads + tid) * P);
+        if (n_pair) nxt_d[k] = fetch<DT, VEC>(p.draft, n_drow, V, e1 + ((int64_t)k * kThreads + tid) * P);
+      }
+    }
+    const int64_t e_chunk = (int64_t)chunk * CH;
+    // gather of the logits at the drafted token
+    if (pair && tid == 0 && x >= e_chunk && x < e_chunk + CH && x < V) {
       gx_t = load_scalar<DT>(p.target, trow, V, x);
       gx_d = load_scalar<DT>(p.draft, drow, V, x);
       gathered = true;
     }
-  }
+    // fold this chunk
+    float vt[NE];
+#pragma unroll
+    for (int k = 0; k < kUA; ++k) unpack<DT>(cur_t[k], vt + k * P);
+    fold_row<NE, P, IDX>(rt, vt, Lhi, pair, e_chunk + (int64_t)tid * P, (int64_t)kThreads * P, kPad);
+    if (pair) {
+      float vd[NE];
+#pragma unroll
+      for (int k = 0; k < kUA; ++k) unpack<DT>(cur_d[k], vd + k * P);
+      if (p.want_w)
+        fold_draft_w<NE>(rd, W, vd, vt, Lhi, kPad);
+      else
+        fold_row<NE, P, false>(rd, vd, Lhi, true, 0, 0, kPad);
+    }
 
-  // ---- target row: max, argmax, sum exp (exponent from the exact difference x - m)
-  float vt[NE];
-#pragma unroll
-  for (int k = 0; k < kUA; ++k) unpack<DT>(qt[k], vt + k * P);
-  float mt = vt[0];
-#pragma unroll
-  for (int e = 1; e < NE; ++e) mt = fmaxf(mt, vt[e]);
-  int it = INT_MAX;
-  if (want_idx) {
-#pragma unroll
-    for (int k = kUA - 1; k >= 0; --k)
-#pragma unroll
-      for (int e = P - 1; e >= 0; --e)
-        if (vt[k * P + e] == mt) it = (int)(e_chunk + ((int64_t)k * kThreads + tid) * P + e);
-  }
-  float st = 0.f, md = 0.f, sd = 0.f, wd = 0.f;
-  if (want_soft) {
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-    for (int e = 0; e < NE; e += 4) {
-      a0 += __builtin_amdgcn_exp2f((vt[e] - mt) * Lhi);
-      a1 += __builtin_amdgcn_exp2f((vt[e + 1] - mt) * Lhi);
-      a2 += __builtin_amdgcn_exp2f((vt[e + 2] - mt) * Lhi);
-      a3 += __builtin_amdgcn_exp2f((vt[e + 3] - mt) * Lhi);
-    }
-    st = (a0 + a1) + (a2 + a3);
-    if (mt == Elem<DT>::kPad) st = 0.f;  // lane beyond the end of the row: no terms
-    // ---- draft row (same accumulation pattern, so identical rows give identical sums)
-    float vd[NE];
-#pragma unroll
-    for (int k = 0; k < kUA; ++k) unpack<DT>(qd[k], vd + k * P);
-    md = vd[0];
-#pragma unroll
-    for (int e = 1; e < NE; ++e) md = fmaxf(md, vd[e]);
-    float b0 = 0.f, b1 = 0.f, b2 = 0.f, b3 = 0.f;
-    if (want_w) {
-      float w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
-#pragma unroll
-      for (int e = 0; e < NE; e += 4) {
-        const float e0 = __builtin_amdgcn_exp2f((vd[e] - md) * Lhi);
-        const float e1 = __builtin_amdgcn_exp2f((vd[e + 1] - md) * Lhi);
-        const float e2 = __builtin_amdgcn_exp2f((vd[e + 2] - md) * Lhi);
-        const float e3 = __builtin_amdgcn_exp2f((vd[e + 3] - md) * Lhi);
-        b0 += e0;
-        b1 += e1;
-        b2 += e2;
-        b3 += e3;
-        w0 = fmaf(e0, vd[e] - vt[e], w0);
-        w1 = fmaf(e1, vd[e + 1] - vt[e + 1], w1);
-        w2 = fmaf(e2, vd[e + 2] - vt[e + 2], w2);
-        w3 = fmaf(e3, vd[e + 3] - vt[e + 3], w3);
-      }
-      wd = (w0 + w1) + (w2 + w3);
-    } else {
-#pragma unroll
-      for (int e = 0; e < NE; e += 4) {
-        b0 += __builtin_amdgcn_exp2f((vd[e] - md) * Lhi);
-        b1 += __builtin_amdgcn_exp2f((vd[e + 1] - md) * Lhi);
-        b2 += __builtin_amdgcn_exp2f((vd[e + 2] - md) * Lhi);
-        b3 += __builtin_amdgcn_exp2f((vd[e + 3] - md) * Lhi);
-      }
-    }
-    sd = (b0 + b1) + (b2 + b3);
-    if (md == Elem<DT>::kPad) sd = wd = 0.f;
-  }
+    const bool seg_end = (it + 1 == i1) || (chunk + 1 == nch);
+    if (!seg_end) continue;
 
-  // ---- wave reduction of the lane partials (rescale factors from exact differences)
-  const float Mt = wave_max(mt);
-  if (want_idx) it = wave_min_int(mt == Mt ? it : INT_MAX);
-  if (want_soft) {
-    st = wave_sum(st * exp_hp(mt - Mt, Lhi, Llo));
-    const float Md = wave_max(md);
-    const float f = exp_hp(md - Md, Lhi, Llo);
-    sd = wave_sum(sd * f);
-    if (want_w) wd = wave_sum(wd * f);
-    md = Md;
-  }
-  if (lane == 0) {
-    sh.m[0][wv] = Mt;
-    sh.s[0][wv] = st;
-    sh.m[1][wv] = md;
-    sh.s[1][wv] = sd;
-    sh.w[wv] = wd;
-    sh.i[wv] = it;
-  }
-  __syncthreads();
-  // ---- workgroup partial (float64 from here on)
-  if (tid == 0) {
-    PartA pa;
-    float M = sh.m[0][0], Md2 = sh.m[1][0];
-    for (int k = 1; k < kWaves; ++k) {
-      M = fmaxf(M, sh.m[0][k]);
-      Md2 = fmaxf(Md2, sh.m[1][k]);
+    // ---- end of a task segment: workgroup reduction and publication
+    const float Mt = wave_max(rt.m);
+    int It = INT_MAX;
+    if (IDX) It = wave_min_int(rt.m == Mt ? rt.idx : INT_MAX);
+    float St = 0.f, Md = kPad, Sd = 0.f, Wd = 0.f;
+    if (pair) {
+      St = wave_sum(rt.s * exp_hp(rt.m - Mt, Lhi, Llo));
+      Md = wave_max(rd.m);
+      const float f = exp_hp(rd.m - Md, Lhi, Llo);
+      Sd = wave_sum(rd.s * f);
+      if (p.want_w) Wd = wave_sum(W * f);
     }
-    int I = INT_MAX;
-    double S = 0.0, Sd = 0.0, W = 0.0;
-    for (int k = 0; k < kWaves; ++k) {
-      if (sh.m[0][k] == M) I = min(I, sh.i[k]);
-      if (want_soft) {
-        S += (double)sh.s[0][k] * (double)exp_hp(sh.m[0][k] - M, Lhi, Llo);
-        const double f = (double)exp_hp(sh.m[1][k] - Md2, Lhi, Llo);
-        Sd += (double)sh.s[1][k] * f;
-        W += (double)sh.w[k] * f;
-      }
-    }
-    pa.m_t = M;
-    pa.s_t = S;
-    pa.m_d = Md2;
-    pa.s_d = Sd;
-    pa.w = W;
-    pa.idx = I;
-    pa.pad = 0;
-    p.part_a[item] = pa;
-    if (gathered) {
-      p.gat[2 * drow] = gx_t;
-      p.gat[2 * drow + 1] = gx_d;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const unsigned old = atomicAdd(&p.cnt_task[task], 1u);
-    sh.last_chunk = (old == (unsigned)(p.nch_a - 1));
-  }
-  __syncthreads();
-  if (!sh.last_chunk) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-
-  // ---- last workgroup of the task: merge the chunk partials (wave 0, fixed order)
-  if (wv == 0) {
-    float m1 = -FLT_MAX, m2 = -FLT_MAX;
-    double s1 = 0.0, s2 = 0.0, w2 = 0.0;
-    int i1 = INT_MAX;
-    for (int ch = lane; ch < p.nch_a; ch += 64) {
-      const PartA q = p.part_a[(int64_t)task * p.nch_a + ch];
-      if (q.m_t > m1) {
-        if (want_soft) s1 = s1 * (double)exp_hp(m1 - q.m_t, Lhi, Llo) + q.s_t;
-        m1 = q.m_t;
-        i1 = q.idx;
-      } else {
-        if (want_soft) s1 += q.s_t * (double)exp_hp(q.m_t - m1, Lhi, Llo);
-        if (q.m_t == m1) i1 = min(i1, q.idx);
-      }
-      if (want_soft) {
-        if (q.m_d > m2) {
-          const double f = (double)exp_hp(m2 - q.m_d, Lhi, Llo);
-          s2 = s2 * f + q.s_d;
-          w2 = w2 * f + q.w;
-          m2 = q.m_d;
-        } else {
-          const double f = (double)exp_hp(q.m_d - m2, Lhi, Llo);
-          s2 += q.s_d * f;
-          w2 += q.w * f;
-        }
-      }
-    }
-    const float M1 = wave_max(m1);
-    const int I1 = wave_min_int(m1 == M1 ? i1 : INT_MAX);
-    double S1 = 0.0, S2 = 0.0, W2 = 0.0;
-    float M2 = 0.f;
-    if (want_soft) {
-      S1 = wave_sum_d(s1 * (double)exp_hp(m1 - M1, Lhi, Llo));
-      M2 = wave_max(m2);
-      const double f = (double)exp_hp(m2 - M2, Lhi, Llo);
-      S2 = wave_sum_d(s2 * f);
-      W2 = wave_sum_d(w2 * f);
-    }
+    __syncthreads();  // LDS of the previous segment is no longer read
     if (lane == 0) {
-      TaskStat ts;
-      ts.m_t = M1;
-      ts.s_t = S1;
-      ts.m_d = M2;
-      ts.s_d = S2;
-      ts.w = W2;
-      ts.idx = I1;
-      ts.kl = 0.0f;
-      int refine = 0;
-      if (want_w) {
-        // one-pass KL and a bound on its rounding error (a few 1e-7 of the
-        // magnitude of the terms that cancel)
-        const double a = W2 / S2 / (double)T, bm = ((double)M2 - (double)M1) / (double)T, lg = log(S2 / S1);
-        const double kl = a - bm - lg;
-        const double err = 4e-7 * (fabs(a) + fabs(bm) + fabs(lg) + 1.0);
-        refine = err > 1e-5 * kl;
-        if (MODE == SV_MODE_NKL && p.V > 1) {
-          const double lnV = log((double)p.V);
-          refine |= fabs(kl / lnV - (double)p.delta) < 2.0 * err / lnV;
-        }
-        ts.kl = (float)kl;
-      }
-      p.stat[task] = ts;
-      sh.refine = refine;
-      sh.d[0] = S1;
-      sh.d[1] = S2;
-      sh.m[0][0] = M1;
-      sh.m[1][0] = M2;
+      sh.m[0][wv] = Mt;
+      sh.s[0][wv] = St;
+      sh.m[1][wv] = Md;
+      sh.s[1][wv] = Sd;
+      sh.w[wv] = Wd;
+      sh.i[wv] = It;
     }
-  }
-  __syncthreads();
-  if (sh.refine) {
-    const double kl = kl_second_pass<DT, VEC>(p, trow, drow, sh.m[0][0], sh.m[1][0], sh.d[0], sh.d[1], T, Lhi, sh.d + 2);
-    if (tid == 0) p.stat[task].kl = (float)kl;
-  }
-  if (tid == 0) {
-    p.cnt_task[task] = 0u;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const int g = p.gamma[b];
-    const unsigned need = (unsigned)(MODE == SV_MODE_STOCHASTIC ? g : g + 1);
-    const unsigned old = atomicAdd(&p.cnt_req[b], 1u);
-    sh.last_task = (old == need - 1);
-  }
-  __syncthreads();
-  if (!sh.last_task) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __syncthreads();
+    const int64_t w_lo = (((int64_t)task * nch + 1) * G - 1) / N;  // first workgroup of the task
+    if (tid == 0) {
+      PartA pa;
+      float M = sh.m[0][0], M2 = sh.m[1][0];
+      for (int k = 1; k < kWaves; ++k) {
+        M = fmaxf(M, sh.m[0][k]);
+        M2 = fmaxf(M2, sh.m[1][k]);
+      }
+      int I = INT_MAX;
+      double S = 0.0, S2 = 0.0, W2 = 0.0;
+      for (int k = 0; k < kWaves; ++k) {
+        if (sh.m[0][k] == M) I = min(I, sh.i[k]);
+        if (pair) {
+          S += (double)sh.s[0][k] * (double)exp_hp(sh.m[0][k] - M, Lhi, Llo);
+          const double f = (double)exp_hp(sh.m[1][k] - M2, Lhi, Llo);
+          S2 += (double)sh.s[1][k] * f;
+          W2 += (double)sh.w[k] * f;
+        }
+      }
+      pa.m_t = M;
+      pa.s_t = S;
+      pa.m_d = M2;
+      pa.s_d = S2;
+      pa.w = W2;
+      pa.idx = I;
+      pa.pad = 0;
+      put_part_a(p.part_a + (int64_t)task * nch + ((int64_t)blockIdx.x - w_lo), pa);
+      if (gathered) {
+        st_dev(p.gat + 2 * drow, gx_t);
+        st_dev(p.gat + 2 * drow + 1, gx_d);
+      }
+      const unsigned mine = (unsigned)(chunk + 1 - seg_first);
+      const unsigned old = signal_n(p.cnt_task + task, mine);
+      sh.flag = (old + mine == (unsigned)nch);
+    }
+    __syncthreads();
+    if (!sh.flag) continue;
 
-  // ---- last task of the request: decide
-  if (MODE == SV_MODE_STOCHASTIC)
-    decide_stochastic(p, b, sh.dec);
-  else if (MODE == SV_MODE_TREE_GREEDY)
-    decide_tree(p, b, sh.dec, tree_info, tree_par);
-  else
-    decide_argmax_chain<MODE>(p, b, sh.dec);
-  if (tid == 0) p.cnt_req[b] = 0u;
+    // ---- this workgroup completed the task: merge the partials in order
+    const int64_t w_hi = (((int64_t)task * nch + nch) * G - 1) / N;
+    const int nseg = (int)(w_hi - w_lo + 1);
+    if (wv == 0) {
+      float m1 = -FLT_MAX, m2 = -FLT_MAX;
+      double s1 = 0.0, s2 = 0.0, w2 = 0.0;
+      int i1x = INT_MAX;
+      for (int sg = lane; sg < nseg; sg += 64) {
+        const PartA q = get_part_a(p.part_a + (int64_t)task * nch + sg);
+        if (q.m_t > m1) {
+          if (pair) s1 = s1 * (double)exp_hp(m1 - q.m_t, Lhi, Llo) + q.s_t;
+          m1 = q.m_t;
+          i1x = q.idx;
+        } else {
+          if (pair) s1 += q.s_t * (double)exp_hp(q.m_t - m1, Lhi, Llo);
+          if (q.m_t == m1) i1x = min(i1x, q.idx);
+        }
+        if (pair) {
+          if (q.m_d > m2) {
+            const double f = (double)exp_hp(m2 - q.m_d, Lhi, Llo);
+            s2 = s2 * f + q.s_d;
+            w2 = w2 * f + q.w;
+            m2 = q.m_d;
+          } else {
+            const double f = (double)exp_hp(q.m_d - m2, Lhi, Llo);
+            s2 += q.s_d * f;
+            w2 += q.w * f;
+          }
+        }
+      }
+      const float M1 = wave_max(m1);
+      const int I1 = wave_min_int(m1 == M1 ? i1x : INT_MAX);
+      double S1 = 0.0, S2 = 0.0, W2 = 0.0;
+      float M2 = 0.f;
+      if (pair) {
+        S1 = wave_sum_d(s1 * (double)exp_hp(m1 - M1, Lhi, Llo));
+        M2 = wave_max(m2);
+        const double f = (double)exp_hp(m2 - M2, Lhi, Llo);
+        S2 = wave_sum_d(s2 * f);
+        W2 = wave_sum_d(w2 * f);
+      }
+      if (lane == 0) {
+        TaskStat ts;
+        ts.m_t = M1;
+        ts.s_t = S1;
+        ts.m_d = M2;
+        ts.s_d = S2;
+        ts.w = W2;
+        ts.idx = I1;
+        ts.kl = 0.0f;
+        int refine = 0;
+        if (pair && p.want_w) {
+          // one-pass KL and a bound on its rounding error (a few 1e-7 of the
+          // magnitude of the terms that cancel)
+          const double a = W2 / S2 / (double)T, bm = ((double)M2 - (double)M1) / (double)T, lg = log(S2 / S1);
+          const double kl = a - bm - lg;
+          const double err = 4e-7 * (fabs(a) + fabs(bm) + fabs(lg) + 1.0);
+          refine = err > 1e-5 * kl;
+          if (MODE == SV_MODE_NKL && p.V > 1) {
+            const double lnV = log((double)p.V);
+            refine |= fabs(kl / lnV - (double)p.delta) < 2.0 * err / lnV;
+          }
+          ts.kl = (float)kl;
+        }
+        put_stat(p.stat + task, ts);
+        sh.refine = refine;
+        sh.d[0] = S1;
+        sh.d[1] = S2;
+        sh.m[0][0] = M1;
+        sh.m[1][0] = M2;
+      }
+    }
+    __syncthreads();
+    if (sh.refine) {
+      const double kl =
+          kl_second_pass<DT, VEC>(p, trow, drow, sh.m[0][0], sh.m[1][0], sh.d[0], sh.d[1], T, Lhi, sh.d + 2);
+      if (tid == 0) st_dev(&p.stat[task].kl, (float)kl);
+    }
+    if (tid == 0) {
+      st_dev(p.cnt_task + task, 0u);
+      const unsigned need = (unsigned)(MODE == SV_MODE_STOCHASTIC ? g : g + 1);
+      const unsigned old = signal_n(p.cnt_req + b, 1u);
+      sh.flag = (old + 1 == need);
+    }
+    __syncthreads();
+    if (!sh.flag) continue;
+
+    // ---- last task of the request: decide
+    if (MODE == SV_MODE_STOCHASTIC)
+      decide_stochastic(p, b, g, t0, d0, sh.dec);
+    else if (MODE == SV_MODE_TREE_GREEDY)
+      decide_tree(p, b, g, t0, d0, sh.dec, tree_info, tree_par);
+    else
+      decide_argmax_chain<MODE>(p, b, g, t0, d0, sh.dec);
+    if (tid == 0) st_dev(p.cnt_req + b, 0u);
+    __syncthreads();
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -995,19 +1243,17 @@ __global__ __launch_bounds__(kThreads) void k_draw(Params p) {
     pc.bp = Bp;
     pc.m = mc;
     pc.pad[0] = pc.pad[1] = pc.pad[2] = 0;
-    p.part_c[(int64_t)b * p.nch_c + chunk] = pc;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const unsigned old = atomicAdd(&p.cnt_draw[b], 1u);
+    put_part_c(p.part_c + (int64_t)b * p.nch_c + chunk, pc);
+    const unsigned old = signal(p.cnt_draw + b);
     sh.last = (old == (unsigned)(p.nch_c - 1));
   }
   __syncthreads();
   if (!sh.last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
   // ---- last workgroup of the request: choose the chunk.  Chunk partials are
   // staged through LDS a tile at a time and combined by thread 0 in chunk
   // order, so the result does not depend on which workgroup finished last.
-  const PartC* pcs = p.part_c + (int64_t)b * p.nch_c;
+  PartC* pcs = p.part_c + (int64_t)b * p.nch_c;
   const int nch = p.nch_c;
   // stage 1: totals of a and b, and the row maximum (bonus)
   {
@@ -1016,7 +1262,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(Params p) {
     for (int base = 0; base < nch; base += kThreads) {
       const int ch = base + tid;
       if (ch < nch) {
-        const PartC q = pcs[ch];
+        const PartC q = get_part_c(pcs + ch);
         sh.ta[tid] = q.a;
         sh.tb[tid] = q.b;
         sh.tm[tid] = q.m;
@@ -1053,7 +1299,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(Params p) {
     double tot = 0.0;
     for (int base = 0; base < nch; base += kThreads) {
       const int ch = base + tid;
-      if (ch < nch) sh.ta[tid] = weight(pcs[ch], 0);
+      if (ch < nch) sh.ta[tid] = weight(get_part_c(pcs + ch), 0);
       __syncthreads();
       if (tid == 0) {
         const int n = min(kThreads, nch - base);
@@ -1082,7 +1328,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(Params p) {
     double cum = 0.0;
     for (int base = 0; base < nch; base += kThreads) {
       const int ch = base + tid;
-      if (ch < nch) sh.ta[tid] = weight(pcs[ch], fallback);
+      if (ch < nch) sh.ta[tid] = weight(get_part_c(pcs + ch), fallback);
       __syncthreads();
       if (tid == 0 && sh.cstar < 0) {
         const int n = min(kThreads, nch - base);
@@ -1114,8 +1360,8 @@ __global__ __launch_bounds__(kThreads) void k_draw(Params p) {
   double r[NE];
   double tsum = 0.0;
   const double chunk_factor =
-      (kind == kTermBonus) ? exp2(((double)pcs[cstar].m - (double)Mrow) * Ld) : 1.0;
-  const float ref = (kind == kTermBonus) ? pcs[cstar].m : Mt;
+      (kind == kTermBonus) ? exp2(((double)ld_dev(&pcs[cstar].m) - (double)Mrow) * Ld) : 1.0;
+  const float ref = (kind == kTermBonus) ? ld_dev(&pcs[cstar].m) : Mt;
 #pragma unroll
   for (int k = 0; k < kUC; ++k) {
     const uint4 q = fetch<DT, VEC>(p.target, trow, V, y0 + k * P);
@@ -1166,7 +1412,7 @@ __global__ __launch_bounds__(kThreads) void k_draw(Params p) {
     p.out_tokens[t0 + j] = y;
     if (g == 0) p.out_num[b] = 0;
     if (p.out_resid) p.out_resid[b] = (kind == kTermResidual && !fallback) ? (float)(S / sh.a_tot) : 1.0f;
-    p.cnt_draw[b] = 0u;
+    st_dev(p.cnt_draw + b, 0u);
   }
 }
 
@@ -1181,27 +1427,44 @@ int launch_prep(const Params& p, void* stream) {
   return (int)hipGetLastError();
 }
 
+template <int DT, bool VEC, int MODE>
+static void stats_launch(const Params& p, hipStream_t s) {
+  // one resident wave of persistent workgroups (occupancy queried once per process)
+  static int per_cu = 0, cus = 0;
+  if (per_cu == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+      cus = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stats<DT, VEC, MODE>, kThreads, 0) != hipSuccess ||
+        per_cu < 1)
+      per_cu = 1;
+  }
+  const int64_t items = (int64_t)p.n_task * p.nch_a;
+  int64_t grid = (int64_t)per_cu * cus;
+  if (grid > items) grid = items;
+  if (grid < 1) grid = 1;  // workgroup 0 also publishes the offsets
+  hipLaunchKernelGGL((k_stats<DT, VEC, MODE>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+}
+
 template <int DT, bool VEC>
-static void rowstats_dispatch(const Params& p, hipStream_t s, dim3 grid) {
+static void rowstats_dispatch(const Params& p, hipStream_t s) {
   switch (p.mode) {
-    case SV_MODE_STOCHASTIC: hipLaunchKernelGGL((k_rowstats<DT, VEC, SV_MODE_STOCHASTIC>), grid, dim3(kThreads), 0, s, p); break;
-    case SV_MODE_GREEDY: hipLaunchKernelGGL((k_rowstats<DT, VEC, SV_MODE_GREEDY>), grid, dim3(kThreads), 0, s, p); break;
-    case SV_MODE_NKL: hipLaunchKernelGGL((k_rowstats<DT, VEC, SV_MODE_NKL>), grid, dim3(kThreads), 0, s, p); break;
-    default: hipLaunchKernelGGL((k_rowstats<DT, VEC, SV_MODE_TREE_GREEDY>), grid, dim3(kThreads), 0, s, p); break;
+    case SV_MODE_STOCHASTIC: stats_launch<DT, VEC, SV_MODE_STOCHASTIC>(p, s); break;
+    case SV_MODE_GREEDY: stats_launch<DT, VEC, SV_MODE_GREEDY>(p, s); break;
+    case SV_MODE_NKL: stats_launch<DT, VEC, SV_MODE_NKL>(p, s); break;
+    default: stats_launch<DT, VEC, SV_MODE_TREE_GREEDY>(p, s); break;
   }
 }
 
 int launch_rowstats(const Params& p, bool vec, void* stream) {
-  const int64_t n = (int64_t)p.n_task * p.nch_a;
-  if (n <= 0) return 0;
-  const dim3 grid((unsigned)n);
   hipStream_t s = (hipStream_t)stream;
   if (p.dtype == SV_DTYPE_BF16) {
-    if (vec) rowstats_dispatch<SV_DTYPE_BF16, true>(p, s, grid);
-    else rowstats_dispatch<SV_DTYPE_BF16, false>(p, s, grid);
+    if (vec) rowstats_dispatch<SV_DTYPE_BF16, true>(p, s);
+    else rowstats_dispatch<SV_DTYPE_BF16, false>(p, s);
   } else {
-    if (vec) rowstats_dispatch<SV_DTYPE_F32, true>(p, s, grid);
-    else rowstats_dispatch<SV_DTYPE_F32, false>(p, s, grid);
+    if (vec) rowstats_dispatch<SV_DTYPE_F32, true>(p, s);
+    else rowstats_dispatch<SV_DTYPE_F32, false>(p, s);
   }
   return (int)hipGetLastError();
 }

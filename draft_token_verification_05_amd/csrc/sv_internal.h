@@ -11,8 +11,9 @@ namespace sv {
 
 constexpr int kThreads = 256;    // threads per workgroup (4 wave64s)
 constexpr int kPrepThreads = 1024;
-constexpr int kUA = 4;           // 16-byte vectors per thread per row, row-statistics pass
+constexpr int kUA = 2;           // 16-byte vectors per thread per row per chunk, row-statistics pass
 constexpr int kUC = 2;           // 16-byte vectors per thread per row, draw pass
+constexpr int kLdsBatch = 4096;  // batches up to this size scan their offsets in LDS (no prep kernel)
 
 constexpr int elems_per_vec(int dtype) { return dtype == SV_DTYPE_BF16 ? 8 : 4; }
 constexpr int elem_size(int dtype) { return dtype == SV_DTYPE_BF16 ? 2 : 4; }
