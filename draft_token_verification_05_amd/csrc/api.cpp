@@ -119,28 +119,24 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   p.dtype = cfg->dtype;
   p.R_d = (int32_t)R_d;
   p.n_task = (int32_t)(mode == SV_MODE_STOCHASTIC ? R_d : R_d + B);
-  p.nch_a = (int32_t)L.nch_a;
+  p.nch = (int32_t)((V + sv::chunk_stats(cfg->dtype, mode) - 1) / sv::chunk_stats(cfg->dtype, mode));
   p.nch_c = (int32_t)L.nch_c;
   p.delta = delta;
-  p.want_w = (mode == SV_MODE_NKL || (mode == SV_MODE_STOCHASTIC && out_nkl)) ? 1 : 0;
+  p.want_kl = (mode == SV_MODE_NKL || (mode == SV_MODE_STOCHASTIC && out_nkl)) ? 1 : 0;
   p.hdr = reinterpret_cast<int32_t*>(ws + L.off_hdr);
-  p.t_off = reinterpret_cast<int32_t*>(ws + L.off_toff);
   p.d_off = reinterpret_cast<int32_t*>(ws + L.off_doff);
   p.pair2req = reinterpret_cast<int32_t*>(ws + L.off_pair2req);
   p.row2req = reinterpret_cast<int32_t*>(ws + L.off_row2req);
   p.part_a = reinterpret_cast<sv::PartA*>(ws + L.off_part_a);
-  p.stat = reinterpret_cast<sv::TaskStat*>(ws + L.off_stat);
-  p.gat = reinterpret_cast<float*>(ws + L.off_gat);
-  p.cnt_task = reinterpret_cast<uint32_t*>(ws + L.off_cnt_task);
-  p.cnt_req = reinterpret_cast<uint32_t*>(ws + L.off_cnt_req);
   p.term = reinterpret_cast<sv::Term*>(ws + L.off_term);
   p.part_c = reinterpret_cast<sv::PartC*>(ws + L.off_part_c);
-  p.cnt_draw = reinterpret_cast<uint32_t*>(ws + L.off_cnt_draw);
 
   // 16-byte vector loads need every row to start on a 16-byte boundary
   const size_t es = (size_t)sv::elem_size(cfg->dtype);
   const bool vec = ((size_t)V * es) % 16 == 0 && aligned(target_logits, 16) &&
                    (!draft_logits || aligned(draft_logits, 16));
+
+  sv::plan_stats(p, vec);
 
   hipStream_t s = static_cast<hipStream_t>(cfg->stream);
   hipEvent_t* ev = static_cast<hipEvent_t*>(cfg->phase_events);
@@ -149,8 +145,9 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   // small batches scan their offsets inside the statistics kernel
   if (B > sv::kLdsBatch && (e = (hipError_t)sv::launch_prep(p, s)) != hipSuccess) return hip_fail(e);
   if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e);
-  if ((e = (hipError_t)sv::launch_rowstats(p, vec, s)) != hipSuccess) return hip_fail(e);
+  if ((e = (hipError_t)sv::launch_stats(p, vec, s)) != hipSuccess) return hip_fail(e);
   if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e);
+  if ((e = (hipError_t)sv::launch_decide(p, vec, s)) != hipSuccess) return hip_fail(e);
   if (mode == SV_MODE_STOCHASTIC && (e = (hipError_t)sv::launch_draw(p, vec, s)) != hipSuccess) return hip_fail(e);
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e);
   return SV_OK;

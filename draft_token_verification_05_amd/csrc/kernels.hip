@@ -1,21 +1,29 @@
 // gfx950 kernels of the speculative-decoding verify step.
 //
-// Three launches per call:
-//   k_prep      one workgroup: exclusive scans of gamma (packed offsets), the
-//               row -> request maps, counter reset, layout validation.
-//   k_rowstats  one workgroup per (task, vocabulary chunk).  A task is a
-//               (target row, draft row) pair (stochastic / NKL) or a single
-//               target row (greedy / tree / NKL bonus row).  Each workgroup
-//               streams its chunk with 16-byte loads and reduces it to
-//               (max, sum exp, argmax, KL cross term); the last workgroup of a
-//               task merges the chunk partials, and the last task of a request
-//               runs the per-request decision (first-reject scan, tree
-//               resolve) and writes the outputs.
+// Launches per call (all on the caller's stream):
+//   k_prep      batches above kLdsBatch only: one workgroup scans gamma into
+//               the packed offsets, builds the row -> request maps and checks
+//               the layout.  Smaller batches do this scan in LDS inside
+//               k_stats.
+//   k_stats     the streaming pass over the logits (the HBM-bound part).  The
+//               (task, vocabulary chunk) items are split into contiguous
+//               ranges, one per workgroup of a grid sized to fill the GPU
+//               once.  A task is a (target row, draft row) pair (stochastic,
+//               NKL) or a target row (greedy, tree, NKL bonus row).  Each
+//               workgroup folds its chunks into running (max, sum exp,
+//               argmax, KL cross terms) and writes one partial per task
+//               segment with plain stores: no atomics, no waiting.
+//   k_decide    one workgroup per request: merges the partials of its tasks,
+//               evaluates acceptance (alpha = min(1, p/q) against u, argmax
+//               match, NKL < delta, tree paths), refines KL values whose
+//               one-pass form is not accurate enough with a second pass, and
+//               writes tokens, counts and diagnostics.  Stochastic requests
+//               leave the terminal slot to k_draw.
 //   k_draw      stochastic mode only: one workgroup per (request, chunk) of
 //               the terminal row; float64 chunk sums of the residual
 //               max(0, p - q) (or of p for a bonus token); the last workgroup
-//               of a request selects the chunk and draws the token by a
-//               block-wide prefix sum.
+//               of a request picks the chunk and draws the token by a
+//               workgroup-wide prefix sum.
 //
 // Formulas follow these passages:
 //   softmax(logits / T), p(x), q(x)     -- "Chain of Draft" page, section 3.2
@@ -27,6 +35,10 @@
 //   NKL = KL(q||p) / ln V, accept < delta -- "Chain of Draft" page, section 3.2.
 //   tree drafts, longest accepted path   -- "Parallel Drafting" page, section 2.2;
 //                                          Gemma-4 MTP page, section 6.2.
+//
+// Every exponential of the path is 2^((x - m) * Lhi) with Lhi = fl32(log2(e)/T),
+// in the statistics, decision and draw passes alike, so the three passes see
+// the same distributions.
 
 #include <hip/hip_runtime.h>
 
@@ -40,9 +52,8 @@ namespace sv {
 namespace {
 
 constexpr int kWaves = kThreads / 64;
-constexpr float kLog2e = 1.44269504088896340736f;
 constexpr double kLog2eD = 1.44269504088896340736;
-constexpr float kLn2 = 0.693147180559945309417f;
+constexpr double kLn2D = 0.693147180559945309417;
 
 // ----------------------------------------------------------------------------
 // element access
@@ -67,30 +78,40 @@ __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w <<
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // Raw 16 bytes holding elements [e0, e0 + P) of `row`; positions >= V hold the
-// pad pattern.  VEC: rows are 16-byte aligned, so full vectors use one load.
+// pad pattern.  Addresses are clamped into the row and the pad is selected
+// after the load, so every lane issues its loads unconditionally.
+// VEC: rows are a whole number of 16-byte vectors and 16-byte aligned.
 template <int DT, bool VEC>
 __device__ __forceinline__ uint4 fetch(const void* base, int64_t row, int64_t V, int64_t e0) {
   constexpr int P = Elem<DT>::P;
-  if (VEC && e0 + P <= V) {
-    const char* ptr = static_cast<const char*>(base) + (row * V + e0) * (DT == SV_DTYPE_BF16 ? 2 : 4);
-    return *reinterpret_cast<const uint4*>(ptr);
+  constexpr uint32_t pp = Elem<DT>::kPadPair;
+  if (VEC) {
+    const int64_t ec = e0 < V ? e0 : V - P;  // a vector is entirely inside or past the row
+    const char* ptr = static_cast<const char*>(base) + (row * V + ec) * (DT == SV_DTYPE_BF16 ? 2 : 4);
+    uint4 q = *reinterpret_cast<const uint4*>(ptr);
+    if (e0 >= V) q = make_uint4(pp, pp, pp, pp);
+    return q;
   }
-  uint32_t w[4] = {Elem<DT>::kPadPair, Elem<DT>::kPadPair, Elem<DT>::kPadPair, Elem<DT>::kPadPair};
+  uint32_t w[4];
   if (DT == SV_DTYPE_BF16) {
     const uint16_t* r = static_cast<const uint16_t*>(base) + row * V;
+    uint32_t h[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      if (e0 + e < V) {
-        const uint32_t h = r[e0 + e];
-        const int sh = (e & 1) * 16;
-        w[e >> 1] = (w[e >> 1] & ~(0xFFFFu << sh)) | (h << sh);
-      }
+      const int64_t y = e0 + e;
+      h[e] = r[y < V ? y : V - 1];
+      if (y >= V) h[e] = pp & 0xFFFFu;
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = h[2 * e] | (h[2 * e + 1] << 16);
   } else {
     const uint32_t* r = static_cast<const uint32_t*>(base) + row * V;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (e0 + e < V) w[e] = r[e0 + e];
+    for (int e = 0; e < 4; ++e) {
+      const int64_t y = e0 + e;
+      w[e] = r[y < V ? y : V - 1];
+      if (y >= V) w[e] = pp;
+    }
   }
   return make_uint4(w[0], w[1], w[2], w[3]);
 }
@@ -136,13 +157,6 @@ __device__ __forceinline__ float wave_max(float v) {
   v = fmaxf(v, dpp<0x124>(v, v));  // row_ror:4
   v = fmaxf(v, dpp<0x128>(v, v));  // row_ror:8
   return fmaxf(fmaxf(lanef(v, 0), lanef(v, 16)), fmaxf(lanef(v, 32), lanef(v, 48)));
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  v = v + dpp<0xB1>(v, 0.f);
-  v = v + dpp<0x4E>(v, 0.f);
-  v = v + dpp<0x124>(v, 0.f);
-  v = v + dpp<0x128>(v, 0.f);
-  return (lanef(v, 0) + lanef(v, 16)) + (lanef(v, 32) + lanef(v, 48));
 }
 __device__ __forceinline__ int wave_min_int(int v) {
   v = min(v, dppi<0xB1>(v, v));
@@ -213,130 +227,14 @@ __device__ __forceinline__ double block_sum_d(double v, double* sh) {
   return r;
 }
 
-// exclusive prefix sum over the workgroup's threads in float64; returns the
-// exclusive prefix of this thread, `total` receives the sum.
-__device__ __forceinline__ double block_exclusive_scan_d(double v, double* sh, double& total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  double incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const double o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
-  __syncthreads();
-  if (lane == 63) sh[w] = incl;
-  __syncthreads();
-  double before = 0.0;
-  for (int k = 0; k < w; ++k) before += sh[k];
-  double tot = 0.0;
-#pragma unroll
-  for (int k = 0; k < kWaves; ++k) tot += sh[k];
-  total = tot;
-  return before + incl - v;
-}
-
 __device__ __forceinline__ bool unit_ok(float u) { return u >= 0.0f && u < 1.0f; }
 __device__ __forceinline__ bool temp_ok(float t) { return t > 0.0f && t <= FLT_MAX; }
 
-// exp((x - m) / T) = exp2(dx * L), L = log2(e)/T split as Lhi + Llo (float32);
-// the rounding error of dx*Lhi is recovered exactly by an fma, so the
-// exponent carries no systematic rounding (no effective temperature shift).
-__device__ __forceinline__ float exp_hp(float dx, float Lhi, float Llo) {
-  const float p1 = dx * Lhi;
-  const float err = fmaf(dx, Lhi, -p1);
-  const float corr = fmaf(dx, Llo, err);
-  const float E = __builtin_amdgcn_exp2f(p1);
-  const float e = fmaf(E * kLn2, corr, E);
-  return p1 >= -160.0f ? e : 0.0f;
-}
-
+// 2^(dx * Lhi); dx = x - m <= 0 is the distance to a running maximum (exact
+// for bf16 inputs), Lhi = fl32(log2(e)/T).  dx = -inf gives 0.
+__device__ __forceinline__ float ex2(float dx, float Lhi) { return __builtin_amdgcn_exp2f(dx * Lhi); }
 // ----------------------------------------------------------------------------
-// Cross-workgroup publication.  Records that one workgroup hands to another
-// inside a launch are written and read with device-scope (sc1) accesses, which
-// go to the device-coherent level instead of an XCD's private L2; the writer
-// waits for its stores to complete before it bumps the completion counter, and
-// the reader only loads after it has seen the final count.  This gives the
-// release/acquire ordering the merge needs without an L2 writeback per
-// workgroup (an agent-scope release fence flushes the whole L2 of the XCD).
-// ----------------------------------------------------------------------------
-
-template <class T>
-__device__ __forceinline__ void st_dev(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <class T>
-__device__ __forceinline__ T ld_dev(T* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// all earlier memory operations of this thread have completed
-__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0); }
-// counter increment after the thread's published stores completed; returns the old count
-__device__ __forceinline__ unsigned signal_n(uint32_t* cnt, unsigned n) {
-  wait_stores();
-  return __hip_atomic_fetch_add(cnt, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ unsigned signal(uint32_t* cnt) { return signal_n(cnt, 1u); }
-
-__device__ __forceinline__ void put_part_a(PartA* q, const PartA& v) {
-  st_dev(&q->s_t, v.s_t);
-  st_dev(&q->s_d, v.s_d);
-  st_dev(&q->w, v.w);
-  st_dev(&q->m_t, v.m_t);
-  st_dev(&q->m_d, v.m_d);
-  st_dev(&q->idx, v.idx);
-}
-__device__ __forceinline__ PartA get_part_a(PartA* q) {
-  PartA v;
-  v.s_t = ld_dev(&q->s_t);
-  v.s_d = ld_dev(&q->s_d);
-  v.w = ld_dev(&q->w);
-  v.m_t = ld_dev(&q->m_t);
-  v.m_d = ld_dev(&q->m_d);
-  v.idx = ld_dev(&q->idx);
-  v.pad = 0;
-  return v;
-}
-__device__ __forceinline__ void put_stat(TaskStat* q, const TaskStat& v) {
-  st_dev(&q->s_t, v.s_t);
-  st_dev(&q->s_d, v.s_d);
-  st_dev(&q->w, v.w);
-  st_dev(&q->m_t, v.m_t);
-  st_dev(&q->m_d, v.m_d);
-  st_dev(&q->kl, v.kl);
-  st_dev(&q->idx, v.idx);
-}
-__device__ __forceinline__ TaskStat get_stat(TaskStat* q) {
-  TaskStat v;
-  v.s_t = ld_dev(&q->s_t);
-  v.s_d = ld_dev(&q->s_d);
-  v.w = ld_dev(&q->w);
-  v.m_t = ld_dev(&q->m_t);
-  v.m_d = ld_dev(&q->m_d);
-  v.kl = ld_dev(&q->kl);
-  v.idx = ld_dev(&q->idx);
-  return v;
-}
-__device__ __forceinline__ int get_idx(TaskStat* q) { return ld_dev(&q->idx); }
-__device__ __forceinline__ void put_part_c(PartC* q, const PartC& v) {
-  st_dev(&q->a, v.a);
-  st_dev(&q->b, v.b);
-  st_dev(&q->ap, v.ap);
-  st_dev(&q->bp, v.bp);
-  st_dev(&q->m, v.m);
-}
-__device__ __forceinline__ PartC get_part_c(PartC* q) {
-  PartC v;
-  v.a = ld_dev(&q->a);
-  v.b = ld_dev(&q->b);
-  v.ap = ld_dev(&q->ap);
-  v.bp = ld_dev(&q->bp);
-  v.m = ld_dev(&q->m);
-  v.pad[0] = v.pad[1] = v.pad[2] = 0;
-  return v;
-}
-
-// ----------------------------------------------------------------------------
-// k_prep
+// k_prep (batches above kLdsBatch)
 // ----------------------------------------------------------------------------
 
 __global__ __launch_bounds__(kPrepThreads) void k_prep(Params p) {
@@ -369,236 +267,453 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Params p) {
       if (k < w) before += sh_w[k];
       tile += sh_w[k];
     }
-    if (b < p.B) {
-      const long long excl = carry + before + incl - g;
-      // values are only used when the whole layout checks out (sum == R_d < 2^31)
-      p.d_off[b] = (int)excl;
-      p.t_off[b] = (int)(excl + b);
-    }
+    // values are only used when the whole layout checks out (sum == R_d < 2^31)
+    if (b < p.B) p.d_off[b] = (int)(carry + before + incl - g);
     carry += tile;
     __syncthreads();
   }
-  if (tid == 0) {
-    p.d_off[p.B] = (int)carry;
-    p.t_off[p.B] = (int)(carry + p.B);
-  }
+  if (tid == 0) p.d_off[p.B] = (int)carry;
   const bool bad = sh_bad != 0 || carry != (long long)p.R_d;
   if (tid == 0) p.hdr[0] = bad ? 1 : 0;
-  if (bad) {
-    for (int b = tid; b < p.B; b += kPrepThreads) p.out_num[b] = -1;
-    return;
-  }
-  for (int i = tid; i < p.n_task; i += kPrepThreads) p.cnt_task[i] = 0u;
-  for (int b = tid; b < p.B; b += kPrepThreads) {
-    p.cnt_req[b] = 0u;
-    p.cnt_draw[b] = 0u;
-  }
+  if (bad) return;
   __syncthreads();  // offsets written by other threads of this workgroup
   for (int b = tid; b < p.B; b += kPrepThreads) {
-    const int g = p.gamma[b], d0 = p.d_off[b], t0 = p.t_off[b];
-    for (int k = 0; k < g; ++k) p.pair2req[d0 + k] = b;
-    for (int k = 0; k <= g; ++k) p.row2req[t0 + k] = b;
+    const int g = p.gamma[b], d0 = p.d_off[b], t0 = d0 + b;
+    if (p.mode == SV_MODE_STOCHASTIC)
+      for (int k = 0; k < g; ++k) p.pair2req[d0 + k] = b;
+    if (p.mode == SV_MODE_NKL)
+      for (int k = 0; k <= g; ++k) p.row2req[t0 + k] = b;
   }
 }
 
 // ----------------------------------------------------------------------------
-// per-request decisions (run by the workgroup that completes a request's last
-// task; every thread of the workgroup calls them)
+// k_stats: the streaming pass
 // ----------------------------------------------------------------------------
 
-struct DecideShared {
+// Items (task, chunk) are numbered task * nch + chunk; workgroup w of G
+// streams items [w N / G, (w + 1) N / G).  The workgroup that streams item i:
+__device__ __forceinline__ int wg_of(int64_t item, int64_t N, int G) { return (int)(((item + 1) * G - 1) / N); }
+
+struct StatsShared {
+  int off[kLdsBatch + 1];  // packed draft-row offsets (small batches)
+  float temp[kLdsBatch];
+  long long wsum[kWaves];
+  float m[2][kWaves];
   int i[kWaves];
+  double d[4][kWaves];
   int bad;
 };
 
-__device__ void finish_invalid(const Params& p, int b, int t0, int g) {
-  for (int k = threadIdx.x; k <= g; k += kThreads) p.out_tokens[t0 + k] = -1;
-  if (threadIdx.x == 0) {
-    p.out_num[b] = -1;
-    if (p.out_resid) p.out_resid[b] = __builtin_nanf("");
-    if (p.out_tree_node) p.out_tree_node[b] = -1;
-  }
-}
-
-// NKL = KL(q || p) / ln V.  The KL comes from the task's merged statistics:
-// KL = (W/s_d - (m_d - m_t)) / T - log(s_d / s_t), W = sum e^{(d-m_d)/T} (d - t),
-// or from the second pass when that form loses too much to cancellation.
-// With a single token both distributions are the same point mass: NKL = 0.
-__device__ __forceinline__ float nkl_of(const TaskStat& s, int V) { return V > 1 ? s.kl / logf((float)V) : 0.0f; }
-
-__device__ void decide_stochastic(const Params& p, int b, int g, int t0, int d0, DecideShared& sh) {
-  const float T = p.temp[b];
-  bool bad = !(g <= p.max_gamma) || !temp_ok(T) || !unit_ok(p.ur[b]);
-  int first = INT_MAX;
-  for (int i = threadIdx.x; i < g; i += kThreads) {
-    const int x = p.tokens[d0 + i];
-    const float u = p.ua[d0 + i];
-    if (x < 0 || x >= p.V || !unit_ok(u)) {
-      bad = true;
-      continue;
-    }
-    const TaskStat s = get_stat(p.stat + d0 + i);
-    const float tx = ld_dev(p.gat + 2 * (d0 + i)), dx = ld_dev(p.gat + 2 * (d0 + i) + 1);
-    // log p(x) - log q(x) = ((t_x - m_t) - (d_x - m_d)) / T + log(s_d / s_t)
-    const float lr = ((tx - s.m_t) - (dx - s.m_d)) / T + (float)log(s.s_d / s.s_t);
-    const float alpha = fminf(1.0f, expf(lr));
-    if (!(u <= alpha)) first = min(first, i);
-    if (p.out_p_x) p.out_p_x[d0 + i] = (float)((double)expf((tx - s.m_t) / T) / s.s_t);
-    if (p.out_q_x) p.out_q_x[d0 + i] = (float)((double)expf((dx - s.m_d) / T) / s.s_d);
-    if (p.out_nkl) p.out_nkl[d0 + i] = nkl_of(s, p.V);
-  }
-  if (threadIdx.x == 0) sh.bad = 0;
-  __syncthreads();
-  if (bad) sh.bad = 1;
-  const int j0 = block_min_int(first, sh.i);  // contains barriers
-  const int j = j0 == INT_MAX ? g : j0;
-  if (sh.bad) {
-    finish_invalid(p, b, t0, g);
-    if (threadIdx.x == 0) p.term[b].kind = kTermNone;
-    return;
-  }
-  for (int k = threadIdx.x; k <= g; k += kThreads)
-    if (k != j) p.out_tokens[t0 + k] = k < j ? p.tokens[d0 + k] : -1;
-  if (threadIdx.x == 0) {
-    p.out_num[b] = j;
-    Term tm;
-    tm.j = j;
-    tm.trow = t0 + j;
-    tm.pad = 0;
-    if (j < g) {
-      const TaskStat s = get_stat(p.stat + d0 + j);
-      tm.kind = kTermResidual;
-      tm.drow = d0 + j;
-      tm.m_t = s.m_t;
-      tm.m_d = s.m_d;
-      tm.k0 = (float)(s.s_t / s.s_d);
-    } else {
-      tm.kind = kTermBonus;
-      tm.drow = -1;
-      tm.m_t = tm.m_d = tm.k0 = 0.0f;
-    }
-    p.term[b] = tm;
-  }
-}
-
-// greedy (mode 1) and NKL (mode 2)
-template <int MODE>
-__device__ void decide_argmax_chain(const Params& p, int b, int g, int t0, int d0, DecideShared& sh) {
-  bool bad = !(g <= p.max_gamma);
-  float T = 1.0f;
-  if (MODE == SV_MODE_NKL) {
-    T = p.temp[b];
-    bad = bad || !temp_ok(T);
-  }
-  int first = INT_MAX;
-  for (int i = threadIdx.x; i < g; i += kThreads) {
-    const int x = p.tokens[d0 + i];
-    if (x < 0 || x >= p.V) {
-      bad = true;
-      continue;
-    }
-    bool acc;
-    if (MODE == SV_MODE_GREEDY) {
-      acc = (x == get_idx(p.stat + t0 + i));
-    } else {
-      const TaskStat s = get_stat(p.stat + t0 + i);  // NKL tasks are target rows
-      const float nkl = nkl_of(s, p.V);
-      p.out_nkl[d0 + i] = nkl;
-      if (p.out_p_x || p.out_q_x) {
-        const float tx = ld_dev(p.gat + 2 * (d0 + i)), dx = ld_dev(p.gat + 2 * (d0 + i) + 1);
-        if (p.out_p_x) p.out_p_x[d0 + i] = (float)((double)expf((tx - s.m_t) / T) / s.s_t);
-        if (p.out_q_x) p.out_q_x[d0 + i] = (float)((double)expf((dx - s.m_d) / T) / s.s_d);
-      }
-      acc = nkl < p.delta;
-    }
-    if (!acc) first = min(first, i);
-  }
-  if (threadIdx.x == 0) sh.bad = 0;
-  __syncthreads();
-  if (bad) sh.bad = 1;
-  const int j0 = block_min_int(first, sh.i);
-  const int j = j0 == INT_MAX ? g : j0;
-  if (sh.bad) {
-    finish_invalid(p, b, t0, g);
-    return;
-  }
-  int term_tok;
-  if (MODE == SV_MODE_GREEDY)
-    term_tok = get_idx(p.stat + t0 + j);
-  else
-    term_tok = get_idx(p.stat + t0 + j);
-  for (int k = threadIdx.x; k <= g; k += kThreads)
-    p.out_tokens[t0 + k] = k < j ? p.tokens[d0 + k] : (k == j ? term_tok : -1);
-  if (threadIdx.x == 0) p.out_num[b] = j;
-}
-
-// Tree resolve.  node_info[n] packs (depth << 1) | accepted; parents precede
-// children, so one ordered pass settles every node.
-__device__ void decide_tree(const Params& p, int b, int g, int t0, int d0, DecideShared& sh, int16_t* node_info,
-                            int16_t* par) {
-  const int N = g + 1;
-  bool bad = !(g <= p.max_gamma);
-  if (threadIdx.x == 0) sh.bad = 0;
-  __syncthreads();
-  if (!bad) {
-    for (int n = 1 + threadIdx.x; n < N; n += kThreads) {
-      const int pa = p.parents[d0 + n - 1];
-      const int x = p.tokens[d0 + n - 1];
-      if (pa < 0 || pa >= n || x < 0 || x >= p.V) {
+// Packed offsets of a batch of at most kLdsBatch requests, scanned in LDS:
+// off[b] = sum of gamma over the requests before b.  Returns whether the layout
+// is valid (every gamma >= 0, sum == total_draft_rows).  `publish`: also write
+// the offsets and the layout flag for the later kernels.
+__device__ bool scan_offsets_lds(const Params& p, StatsShared& sh, bool soft, bool publish) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  long long g[4], loc = 0;
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int b = 4 * tid + k;
+    long long v = 0;
+    if (b < p.B) {
+      v = p.gamma[b];
+      if (v < 0) {
         bad = true;
-        continue;
+        v = 0;
       }
-      par[n] = (int16_t)pa;
-      node_info[n] = (int16_t)((x == get_idx(p.stat + t0 + pa)) ? 1 : 0);  // edge match, before ancestry
+      if (soft) sh.temp[b] = p.temp[b];
+    }
+    g[k] = v;
+    loc += v;
+  }
+  long long incl = loc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) sh.wsum[w] = incl;
+  if (tid == 0) sh.bad = 0;
+  __syncthreads();
+  long long before = 0, total = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    if (k < w) before += sh.wsum[k];
+    total += sh.wsum[k];
+  }
+  long long run = before + incl - loc;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int b = 4 * tid + k;
+    if (b < p.B) sh.off[b] = (int)run;
+    run += g[k];
+  }
+  if (tid == 0) {
+    sh.off[p.B] = (int)total;
+    if (total != (long long)p.R_d) sh.bad = 1;
+  }
+  if (bad) sh.bad = 1;  // benign race: every writer stores 1
+  __syncthreads();
+  const bool ok = sh.bad == 0;
+  if (publish) {
+    for (int b = tid; b <= p.B; b += kThreads) p.d_off[b] = sh.off[b];
+    if (tid == 0) p.hdr[0] = ok ? 0 : 1;
+  }
+  return ok;
+}
+
+// Request of a statistics task: the last b with key(b) <= task, where
+// key(b) = d_off[b] for pair tasks (stochastic: task = draft row) and
+// d_off[b] + b for row tasks (NKL: task = target row).  `hint` is the request
+// of this workgroup's previous (smaller) task, or -1.
+template <int MODE>
+__device__ __forceinline__ int find_req(const int* off, int B, int task, int hint) {
+  if (hint < 0) {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      const int key = MODE == SV_MODE_STOCHASTIC ? off[mid] : off[mid] + mid;
+      if (key <= task) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  }
+  int b = hint;
+  while (b + 1 < B && (MODE == SV_MODE_STOCHASTIC ? off[b + 1] : off[b + 1] + b + 1) <= task) ++b;
+  return b;
+}
+
+// Per-lane running statistics of the segment a workgroup streams.
+struct Lane {
+  float mt, md;  // running maxima of the target / draft elements seen
+  int idx;       // lowest position attaining mt
+  double st, sd, w, z;
+};
+
+template <int NV>
+struct Vecs {
+  uint4 v[NV];
+};
+
+// Loads of one chunk: thread t takes 16-byte vectors k * kThreads + t.
+template <int DT, bool VEC, int NV, bool PAIR>
+__device__ __forceinline__ void issue_chunk(const Params& p, int64_t trow, int64_t drow, int64_t e_chunk, Vecs<NV>& qt,
+                                            Vecs<NV>& qd) {
+  constexpr int P = Elem<DT>::P;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int64_t e0 = e_chunk + ((int64_t)k * kThreads + threadIdx.x) * P;
+    qt.v[k] = fetch<DT, VEC>(p.target, trow, p.V, e0);
+    if (PAIR) qd.v[k] = fetch<DT, VEC>(p.draft, drow, p.V, e0);
+  }
+}
+
+// Folds one chunk into the lane state.  SOFT: sums of exponentials; IDX:
+// argmax of the target row; WZ: the KL cross terms of the draft row; PAIR: a
+// draft row is streamed beside the target row.  Target and draft sums use the
+// same accumulation pattern, so identical rows give bit-identical statistics.
+template <int DT, int NV, bool SOFT, bool IDX, bool WZ, bool PAIR>
+__device__ __forceinline__ void fold_chunk(Lane& L, const Vecs<NV>& qt, const Vecs<NV>& qd, int64_t e_chunk,
+                                           float Lhi) {
+  constexpr int P = Elem<DT>::P;
+  constexpr int NE = NV * P;
+  constexpr float pad = Elem<DT>::kPad;
+  float vt[NE];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) unpack<DT>(qt.v[k], vt + k * P);
+  float mc = vt[0];
+#pragma unroll
+  for (int e = 1; e < NE; ++e) mc = fmaxf(mc, vt[e]);
+  if (mc > pad) {  // the lane holds positions < V in this chunk
+    if (IDX && mc > L.mt) {
+      int ic = NE - 1;
+#pragma unroll
+      for (int e = NE - 1; e >= 0; --e)
+        if (vt[e] == mc) ic = e;
+      L.idx = (int)(e_chunk + ((int64_t)(ic / P) * kThreads + threadIdx.x) * P + ic % P);
+    }
+    if (SOFT) {
+      const float M = fmaxf(L.mt, mc);
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+      for (int e = 0; e < NE; e += 4) {
+        a0 += ex2(vt[e] - M, Lhi);
+        a1 += ex2(vt[e + 1] - M, Lhi);
+        a2 += ex2(vt[e + 2] - M, Lhi);
+        a3 += ex2(vt[e + 3] - M, Lhi);
+      }
+      const float f = ex2(L.mt - M, Lhi);  // 0 on the first chunk (L.mt = -inf)
+      L.st = L.st * (double)f + (double)((a0 + a1) + (a2 + a3));
+      L.mt = M;
+    } else {
+      L.mt = fmaxf(L.mt, mc);
     }
   }
-  if (bad) sh.bad = 1;
-  __syncthreads();
-  if (sh.bad) {
-    finish_invalid(p, b, t0, g);
-    return;
-  }
-  if (threadIdx.x == 0) {
-    node_info[0] = 1;  // root: depth 0, accepted
-    for (int n = 1; n < N; ++n) {
-      const int pi = node_info[par[n]];
-      node_info[n] = (int16_t)((((pi >> 1) + 1) << 1) | (pi & node_info[n] & 1));
+  if (PAIR) {
+    float vd[NE];
+#pragma unroll
+    for (int k = 0; k < NV; ++k) unpack<DT>(qd.v[k], vd + k * P);
+    float md = vd[0];
+#pragma unroll
+    for (int e = 1; e < NE; ++e) md = fmaxf(md, vd[e]);
+    if (md > pad) {
+      const float M = fmaxf(L.md, md);
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, w0 = 0.f, w1 = 0.f, z0 = 0.f, z1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < NE; e += 4) {
+        const float e0 = ex2(vd[e] - M, Lhi);
+        const float e1 = ex2(vd[e + 1] - M, Lhi);
+        const float e2 = ex2(vd[e + 2] - M, Lhi);
+        const float e3 = ex2(vd[e + 3] - M, Lhi);
+        a0 += e0;
+        a1 += e1;
+        a2 += e2;
+        a3 += e3;
+        if (WZ) {
+          // positions past the end hold the pad in both rows: difference 0
+          const float g0 = vd[e] - vt[e], g1 = vd[e + 1] - vt[e + 1];
+          const float g2 = vd[e + 2] - vt[e + 2], g3 = vd[e + 3] - vt[e + 3];
+          w0 = fmaf(e0, g0, fmaf(e1, g1, w0));
+          w1 = fmaf(e2, g2, fmaf(e3, g3, w1));
+          z0 = fmaf(e0, fabsf(g0), fmaf(e1, fabsf(g1), z0));
+          z1 = fmaf(e2, fabsf(g2), fmaf(e3, fabsf(g3), z1));
+        }
+      }
+      const double f = (double)ex2(L.md - M, Lhi);
+      L.sd = L.sd * f + (double)((a0 + a1) + (a2 + a3));
+      if (WZ) {
+        L.w = L.w * f + (double)(w0 + w1);
+        L.z = L.z * f + (double)(z0 + z1);
+      }
+      L.md = M;
     }
   }
-  __syncthreads();
-  // deepest accepted node, lowest id on ties
-  int key = -1;
-  for (int n = threadIdx.x; n < N; n += kThreads) {
-    const int ni = node_info[n];
-    if (ni & 1) key = max(key, ((ni >> 1) << 13) | (8191 - n));
+}
+
+// Reduces the lane states over the workgroup and writes the segment's partial
+// (thread 0, plain stores: the consumer is a later kernel).
+template <bool SOFT, bool IDX, bool WZ, bool PAIR>
+__device__ __forceinline__ void reduce_store(const Lane& L, float Lhi, PartA* dst, StatsShared& sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const float wt = wave_max(L.mt);
+  const float wd = PAIR ? wave_max(L.md) : 0.f;
+  if (lane == 0) {
+    sh.m[0][w] = wt;
+    sh.m[1][w] = wd;
   }
-  const int best_key = block_max_int(key, sh.i);
-  const int best = 8191 - (best_key & 8191);
-  const int depth = best_key >> 13;
-  for (int k = depth + 1 + threadIdx.x; k <= g; k += kThreads) p.out_tokens[t0 + k] = -1;
+  __syncthreads();
+  float Mt = sh.m[0][0], Md = sh.m[1][0];
+#pragma unroll
+  for (int k = 1; k < kWaves; ++k) {
+    Mt = fmaxf(Mt, sh.m[0][k]);
+    Md = fmaxf(Md, sh.m[1][k]);
+  }
+  int idx = INT_MAX;
+  if (IDX) idx = wave_min_int(L.mt == Mt ? L.idx : INT_MAX);
+  double v0 = 0.0, v1 = 0.0, v2 = 0.0, v3 = 0.0;
+  if (SOFT) {
+    const double ft = L.mt == Mt ? 1.0 : (double)ex2(L.mt - Mt, Lhi);
+    v0 = wave_sum_d(L.st * ft);
+    if (PAIR) {
+      const double fd = L.md == Md ? 1.0 : (double)ex2(L.md - Md, Lhi);
+      v1 = wave_sum_d(L.sd * fd);
+      if (WZ) {
+        v2 = wave_sum_d(L.w * fd);
+        v3 = wave_sum_d(L.z * fd);
+      }
+    }
+  }
+  if (lane == 0) {
+    sh.i[w] = idx;
+    sh.d[0][w] = v0;
+    sh.d[1][w] = v1;
+    sh.d[2][w] = v2;
+    sh.d[3][w] = v3;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
-    for (int v = best; v != 0; v = par[v]) p.out_tokens[t0 + (node_info[v] >> 1) - 1] = p.tokens[d0 + v - 1];
-    p.out_tokens[t0 + depth] = get_idx(p.stat + t0 + best);
-    p.out_num[b] = depth;
-    if (p.out_tree_node) p.out_tree_node[b] = best;
+    int I = sh.i[0];
+    double s0 = sh.d[0][0], s1 = sh.d[1][0], s2 = sh.d[2][0], s3 = sh.d[3][0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) {
+      I = min(I, sh.i[k]);
+      s0 += sh.d[0][k];
+      s1 += sh.d[1][k];
+      s2 += sh.d[2][k];
+      s3 += sh.d[3][k];
+    }
+    dst->m_t = Mt;
+    if (IDX) dst->idx = I;
+    if (SOFT) dst->s_t = s0;
+    if (PAIR) {
+      dst->m_d = Md;
+      dst->s_d = s1;
+      if (WZ) {
+        dst->w = s2;
+        dst->z = s3;
+      }
+    }
+  }
+  // the next segment writes sh.m before its first barrier and sh.i / sh.d only
+  // after it, by which time thread 0 has read them: no barrier needed here
+}
+
+// Streams chunks [c0, c1) of one task: the loads of chunk c + 1 are in flight
+// while chunk c is folded.
+template <int DT, bool VEC, int NV, bool SOFT, bool IDX, bool WZ, bool PAIR>
+__device__ __forceinline__ void stream_segment(const Params& p, int64_t trow, int64_t drow, int c0, int c1, float Lhi,
+                                               PartA* dst, StatsShared& sh) {
+  constexpr int64_t CH = (int64_t)kThreads * NV * Elem<DT>::P;
+  Lane L;
+  L.mt = L.md = -INFINITY;
+  L.idx = INT_MAX;
+  L.st = L.sd = L.w = L.z = 0.0;
+  Vecs<NV> ct, cd;
+  issue_chunk<DT, VEC, NV, PAIR>(p, trow, drow, (int64_t)c0 * CH, ct, cd);
+  for (int c = c0; c < c1 - 1; ++c) {
+    Vecs<NV> nt, nd;
+    issue_chunk<DT, VEC, NV, PAIR>(p, trow, drow, (int64_t)(c + 1) * CH, nt, nd);
+    fold_chunk<DT, NV, SOFT, IDX, WZ, PAIR>(L, ct, cd, (int64_t)c * CH, Lhi);
+    ct = nt;
+    cd = nd;
+  }
+  fold_chunk<DT, NV, SOFT, IDX, WZ, PAIR>(L, ct, cd, (int64_t)(c1 - 1) * CH, Lhi);
+  reduce_store<SOFT, IDX, WZ, PAIR>(L, Lhi, dst, sh);
+}
+
+// WZ (stochastic only): also the KL cross terms, for the optional NKL output
+template <int DT, bool VEC, int MODE, bool WZ>
+__global__ __launch_bounds__(kThreads) void k_stats(Params p) {
+  constexpr bool SOFT = MODE == SV_MODE_STOCHASTIC || MODE == SV_MODE_NKL;
+  __shared__ StatsShared sh;
+  const int G = (int)gridDim.x, wg = (int)blockIdx.x;
+  const int64_t N = (int64_t)p.n_task * p.nch;
+  const bool lds = p.B <= kLdsBatch;
+  if (lds) {
+    // greedy and tree tasks are target rows: only workgroup 0 needs the scan,
+    // to publish the offsets for the decision kernel
+    if ((SOFT || wg == 0) && !scan_offsets_lds(p, sh, SOFT, wg == 0)) return;
+  } else if (SOFT && p.hdr[0] != 0) {
+    return;  // the prep kernel found a layout error
+  }
+  int64_t i = (int64_t)wg * N / G;
+  const int64_t i_end = (int64_t)(wg + 1) * N / G;
+  int b = -1;
+  while (i < i_end) {
+    const int task = (int)(i / p.nch);
+    const int c0 = (int)(i - (int64_t)task * p.nch);
+    const int c1 = (int)min((int64_t)p.nch, c0 + (i_end - i));
+    PartA* dst = p.part_a + (int64_t)task * p.nch + (wg - wg_of((int64_t)task * p.nch, N, G));
+    if (!SOFT) {
+      stream_segment<DT, VEC, 4, false, true, false, false>(p, task, 0, c0, c1, 0.f, dst, sh);
+    } else {
+      if (lds) b = find_req<MODE>(sh.off, p.B, task, b);
+      else b = MODE == SV_MODE_STOCHASTIC ? p.pair2req[task] : p.row2req[task];
+      const float T = lds ? sh.temp[b] : p.temp[b];
+      const float Lhi = (float)(kLog2eD / (double)T);
+      if (MODE == SV_MODE_STOCHASTIC) {
+        stream_segment<DT, VEC, 2, true, false, WZ, true>(p, (int64_t)task + b, task, c0, c1, Lhi, dst, sh);
+      } else {
+        const int d0 = lds ? sh.off[b] : p.d_off[b];
+        const int g = (lds ? sh.off[b + 1] : p.d_off[b + 1]) - d0;
+        if (task - (d0 + b) < g)
+          stream_segment<DT, VEC, 2, true, true, true, true>(p, task, (int64_t)task - b, c0, c1, Lhi, dst, sh);
+        else  // the bonus row: argmax only
+          stream_segment<DT, VEC, 2, false, true, false, false>(p, task, 0, c0, c1, Lhi, dst, sh);
+      }
+    }
+    i += c1 - c0;
   }
 }
 
 // ----------------------------------------------------------------------------
-// k_rowstats
+// k_decide: per-request merge and decision
 // ----------------------------------------------------------------------------
 
-struct RowShared {
-  float m[2][kWaves];
-  float s[2][kWaves];
-  float w[kWaves];
-  int i[kWaves];
-  double d[2 + kWaves];
-  int last_chunk;  // this workgroup completed the task
-  int last_task;   // ... and the request
-  int refine;
-  DecideShared dec;
+// One-pass KL values whose estimated error exceeds kKlRel of the value, or
+// that sit within the estimate of the NKL threshold, are recomputed in a
+// second pass.  The estimate is kKlErr * (E_q|d - t| / T + 1): the cross term
+// carries relative errors of a few float32 roundings per element against
+// sum q |d - t| / T, the log normaliser ratio a few roundings absolute.
+// Measured against the float64 reference over 6000 row pairs of several
+// shapes (V from 1000 to 152064, bf16 and float32, T from 0.3 to 2, draft
+// noise 0.003 to 1.5), the one-pass error stayed below 1.3e-7 times this
+// scale; kKlErr keeps a margin above that.
+constexpr double kKlErr = 3e-7;
+constexpr double kKlRel = 1e-5;
+
+// Merged statistics of one task.
+struct Merged {
+  float mt, md;
+  int idx;
+  double st, sd, w, z;
 };
+
+__device__ __forceinline__ double rescale(float m, float M, float Lhi) {
+  return m == M ? 1.0 : (double)ex2(m - M, Lhi);
+}
+
+// Merges the partials of `task` over a group of S = 2^glog lanes: lane l of
+// the group takes partial slots l, l + S, ... (vocabulary order), then the
+// group combines by an xor butterfly, so every lane of the group ends with the
+// same values.  `pair`: the task has draft statistics.  All lanes of the
+// wave must call this.
+template <bool SOFT>
+__device__ __forceinline__ Merged merge_task(const Params& p, int64_t task, bool has, bool pair, int l, int glog,
+                                             float Lhi) {
+  const int S = 1 << glog;
+  Merged r;
+  r.mt = r.md = -INFINITY;
+  r.idx = INT_MAX;
+  r.st = r.sd = r.w = r.z = 0.0;
+  if (has) {
+    const int64_t N = (int64_t)p.n_task * p.nch;
+    const int w_lo = wg_of(task * p.nch, N, p.stats_grid);
+    const int nseg = wg_of((task + 1) * p.nch - 1, N, p.stats_grid) - w_lo + 1;
+    const PartA* src = p.part_a + task * p.nch;
+    for (int s = l; s < nseg; s += S) {
+      const float mt = src[s].m_t;
+      const int ix = src[s].idx;
+      if (mt > r.mt || (mt == r.mt && ix < r.idx)) r.idx = ix;
+      if (SOFT && pair) {
+        const float Mt = fmaxf(r.mt, mt), md = src[s].m_d, Md = fmaxf(r.md, md);
+        const double fo = rescale(r.md, Md, Lhi), fn = rescale(md, Md, Lhi);
+        r.st = r.st * rescale(r.mt, Mt, Lhi) + src[s].s_t * rescale(mt, Mt, Lhi);
+        r.sd = r.sd * fo + src[s].s_d * fn;
+        r.w = r.w * fo + src[s].w * fn;
+        r.z = r.z * fo + src[s].z * fn;
+        r.md = Md;
+      }
+      r.mt = fmaxf(r.mt, mt);
+    }
+  }
+  float Mt = r.mt, Md = r.md;
+  for (int m = 1; m < S; m <<= 1) {
+    Mt = fmaxf(Mt, __shfl_xor(Mt, m, 64));
+    if (SOFT) Md = fmaxf(Md, __shfl_xor(Md, m, 64));
+  }
+  int ix = r.mt == Mt ? r.idx : INT_MAX;
+  for (int m = 1; m < S; m <<= 1) ix = min(ix, __shfl_xor(ix, m, 64));
+  if (SOFT) {
+    const double ft = rescale(r.mt, Mt, Lhi), fd = rescale(r.md, Md, Lhi);
+    double st = r.st * ft, sd = r.sd * fd, w = r.w * fd, z = r.z * fd;
+    for (int m = 1; m < S; m <<= 1) {
+      st += __shfl_xor(st, m, 64);
+      sd += __shfl_xor(sd, m, 64);
+      w += __shfl_xor(w, m, 64);
+      z += __shfl_xor(z, m, 64);
+    }
+    r.st = st;
+    r.sd = sd;
+    r.w = w;
+    r.z = z;
+  }
+  r.mt = Mt;
+  r.md = Md;
+  r.idx = ix;
+  return r;
+}
 
 // g(w) = e^w - 1 - w >= 0, accurate for small |w| (Taylor series to w^9)
 __device__ __forceinline__ float g_small(float w) {
@@ -612,18 +727,17 @@ __device__ __forceinline__ float g_small(float w) {
   return w * w * t;
 }
 
-// KL(q || p) of one row pair in a second pass, written as the sum of the
-// non-negative terms q_y * g(w_y), w_y = log(p_y / q_y).  Because
-// sum q e^w = sum p = 1, this equals sum q log(q/p) exactly, has no
-// cancellation, and an error eps in the log normaliser ratio only adds
-// g(eps) = O(eps^2).  Run by all threads of one workgroup.
+// KL(q || p) of one row pair in a second pass, as the sum of the non-negative
+// terms q_y g(w_y), w_y = log(p_y / q_y).  Because sum q e^w = sum p = 1, this
+// equals sum q log(q/p) exactly, has no cancellation, and an error eps in the
+// log normaliser ratio only adds O(eps^2).  All threads of the workgroup call.
 template <int DT, bool VEC>
-__device__ double kl_second_pass(const Params& p, int trow, int drow, float m_t, float m_d, double s_t, double s_d,
-                                 float T, float Lhi, double* shd) {
+__device__ double kl_second_pass(const Params& p, int64_t trow, int64_t drow, float m_t, float m_d, double s_t,
+                                 double s_d, float Lhi, double* shd) {
   constexpr int P = Elem<DT>::P;
   constexpr int U = 4;
   const int64_t V = p.V;
-  const float invT = (float)(1.0 / (double)T);
+  const float c = (float)((double)Lhi * kLn2D);  // d(log p)/d(logit)
   const float lr = (float)log(s_d / s_t);
   const float inv_sd = (float)(1.0 / s_d), inv_st = (float)(1.0 / s_t);
   double acc = 0.0;
@@ -644,15 +758,14 @@ __device__ double kl_second_pass(const Params& p, int trow, int drow, float m_t,
 #pragma unroll
       for (int e = 0; e < P; ++e) {
         const float dt = vt[e] - m_t, dd = vd[e] - m_d;
-        const float q = __builtin_amdgcn_exp2f(dd * Lhi) * inv_sd;
-        const float w = fmaf(dt - dd, invT, lr);
+        const float q = ex2(dd, Lhi) * inv_sd;
+        const float w = fmaf(dt - dd, c, lr);
         float term;
         if (fabsf(w) < 0.5f) {
           term = q * g_small(w);
         } else {
           // q g(w) = p - q - q w; also right where q underflows but p does not
-          const float pp = __builtin_amdgcn_exp2f(dt * Lhi) * inv_st;
-          term = (pp - q) - q * w;
+          term = (ex2(dt, Lhi) * inv_st - q) - q * w;
         }
         part += term;  // positions past the end of the row give p = q = 0
       }
@@ -662,552 +775,307 @@ __device__ double kl_second_pass(const Params& p, int trow, int drow, float m_t,
   return block_sum_d(acc, shd);
 }
 
-// Lane-level running statistics of one row over the chunks a workgroup streams.
-struct LaneRow {
-  float m;    // running maximum (raw logits)
-  float s;    // sum exp2((x - m) * L) over the lane's elements so far
-  int idx;    // lowest index attaining m (argmax rows)
-};
-
-// Folds NE new elements v (positions pos0 + e, e in vector order) into r.
-template <int NE, int P, bool IDX>
-__device__ __forceinline__ void fold_row(LaneRow& r, const float* v, float Lhi, bool soft, int64_t pos_base,
-                                         int64_t pos_stride, float pad) {
-  float mc = v[0];
-#pragma unroll
-  for (int e = 1; e < NE; ++e) mc = fmaxf(mc, v[e]);
-  if (mc == pad) return;  // every element of this lane lies past the end of the row
-  if (IDX && mc > r.m) {
-    int ic = INT_MAX;
-#pragma unroll
-    for (int e = NE - 1; e >= 0; --e)
-      if (v[e] == mc) ic = (int)(pos_base + (int64_t)(e / P) * pos_stride + (e % P));
-    r.idx = ic;
-  }
-  const float M = fmaxf(r.m, mc);
-  if (soft) {
-    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-    for (int e = 0; e < NE; e += 4) {
-      a0 += __builtin_amdgcn_exp2f((v[e] - M) * Lhi);
-      a1 += __builtin_amdgcn_exp2f((v[e + 1] - M) * Lhi);
-      a2 += __builtin_amdgcn_exp2f((v[e + 2] - M) * Lhi);
-      a3 += __builtin_amdgcn_exp2f((v[e + 3] - M) * Lhi);
-    }
-    r.s = r.s * __builtin_amdgcn_exp2f((r.m - M) * Lhi) + ((a0 + a1) + (a2 + a3));
-  }
-  r.m = M;
-}
-
-// Draft row of a pair, with the KL cross term W = sum e^{(d - m_d)/T} (d - t);
-// the same accumulation pattern as fold_row keeps identical rows bit-identical.
-template <int NE>
-__device__ __forceinline__ void fold_draft_w(LaneRow& r, float& W, const float* vd, const float* vt, float Lhi,
-                                             float pad) {
-  float mc = vd[0];
-#pragma unroll
-  for (int e = 1; e < NE; ++e) mc = fmaxf(mc, vd[e]);
-  if (mc == pad) return;
-  const float M = fmaxf(r.m, mc);
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, w0 = 0.f, w1 = 0.f, w2 = 0.f, w3 = 0.f;
-#pragma unroll
-  for (int e = 0; e < NE; e += 4) {
-    const float e0 = __builtin_amdgcn_exp2f((vd[e] - M) * Lhi);
-    const float e1 = __builtin_amdgcn_exp2f((vd[e + 1] - M) * Lhi);
-    const float e2 = __builtin_amdgcn_exp2f((vd[e + 2] - M) * Lhi);
-    const float e3 = __builtin_amdgcn_exp2f((vd[e + 3] - M) * Lhi);
-    a0 += e0;
-    a1 += e1;
-    a2 += e2;
-    a3 += e3;
-    w0 = fmaf(e0, vd[e] - vt[e], w0);
-    w1 = fmaf(e1, vd[e + 1] - vt[e + 1], w1);
-    w2 = fmaf(e2, vd[e + 2] - vt[e + 2], w2);
-    w3 = fmaf(e3, vd[e + 3] - vt[e + 3], w3);
-  }
-  const float f = __builtin_amdgcn_exp2f((r.m - M) * Lhi);
-  r.s = r.s * f + ((a0 + a1) + (a2 + a3));
-  W = W * f + ((w0 + w1) + (w2 + w3));
-  r.m = M;
-}
-
-// Request of a task (task index = draft row for stochastic pairs, target row
-// otherwise): offsets come from LDS (small batches) or from the prep kernel.
-struct ReqInfo {
-  int b, g, t0, d0;
+struct DecideShared {
+  float mt[kThreads], md[kThreads];
+  double st[kThreads], sd[kThreads];
+  int idx[kThreads];
+  int acc[kThreads];
+  float kl[kThreads];
+  int need[kThreads];
+  int list[kThreads];
+  int nlist;
+  int red_i[kWaves];
+  double red_d[kWaves];
 };
 
 template <int MODE>
-__device__ __forceinline__ ReqInfo locate(const Params& p, const int* s_off, bool lds, int task) {
-  ReqInfo r;
-  if (lds) {
-    // last b with off(b) <= task, off = d_off (pairs) or t_off = d_off + b (rows)
-    int lo = 0, hi = p.B - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      const int off = MODE == SV_MODE_STOCHASTIC ? s_off[mid] : s_off[mid] + mid;
-      if (off <= task) lo = mid; else hi = mid - 1;
-    }
-    r.b = lo;
-    r.d0 = s_off[lo];
-    r.g = s_off[lo + 1] - s_off[lo];
-  } else {
-    r.b = MODE == SV_MODE_STOCHASTIC ? p.pair2req[task] : p.row2req[task];
-    r.d0 = p.d_off[r.b];
-    r.g = p.d_off[r.b + 1] - r.d0;
-  }
-  r.t0 = r.d0 + r.b;
-  return r;
-}
-
-struct StatsShared {
-  float m[2][kWaves];
-  float s[2][kWaves];
-  float w[kWaves];
-  int i[kWaves];
-  double d[2 + kWaves];
-  int flag;
-  int refine;
-  int scan[kThreads / 64];
-  DecideShared dec;
+struct TreeShared {
+  int16_t info[1];
+  int16_t par[1];
+  int idx[1];
+};
+template <>
+struct TreeShared<SV_MODE_TREE_GREEDY> {
+  int16_t info[SV_MAX_GAMMA + 1];  // (depth << 1) | accepted
+  int16_t par[SV_MAX_GAMMA + 1];
+  int idx[SV_MAX_GAMMA + 1];  // argmax of each node's target row
 };
 
-// Persistent row-statistics kernel.  The (task, chunk) items, task-major, are
-// split into one contiguous range per workgroup; a workgroup streams its
-// range with the next chunk's loads in flight while it folds the current one,
-// and publishes one partial per task segment.  The last segment of a task
-// merges the partials (in vocabulary order), and the last task of a request
-// runs the decision.
+__device__ void finish_invalid(const Params& p, int b, int t0, int d0, int g) {
+  for (int k = threadIdx.x; k <= g; k += kThreads) p.out_tokens[t0 + k] = -1;
+  for (int k = threadIdx.x; k < g; k += kThreads) {
+    if (p.out_nkl) p.out_nkl[d0 + k] = __builtin_nanf("");
+    if (p.out_p_x) p.out_p_x[d0 + k] = __builtin_nanf("");
+    if (p.out_q_x) p.out_q_x[d0 + k] = __builtin_nanf("");
+  }
+  if (threadIdx.x == 0) {
+    p.out_num[b] = -1;
+    if (p.out_resid) p.out_resid[b] = __builtin_nanf("");
+    if (p.out_tree_node) p.out_tree_node[b] = -1;
+    if (p.mode == SV_MODE_STOCHASTIC) p.term[b].kind = kTermNone;
+  }
+}
+
+// Tree resolve over the node argmaxes in `tr.idx`: a node is accepted when its
+// token is the argmax of its parent's target row and its parent is accepted;
+// the deepest accepted node (lowest id on ties) ends the path.  Parents
+// precede children, so one ordered pass settles every node.
+__device__ void resolve_tree(const Params& p, int b, int g, int t0, int d0, TreeShared<SV_MODE_TREE_GREEDY>& tr,
+                             DecideShared& sh) {
+  const int N = g + 1;
+  for (int n = 1 + threadIdx.x; n < N; n += kThreads) {
+    const int pa = p.parents[d0 + n - 1];
+    tr.par[n] = (int16_t)pa;
+    tr.info[n] = (int16_t)(p.tokens[d0 + n - 1] == tr.idx[pa] ? 1 : 0);  // edge match, before ancestry
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    tr.info[0] = 1;  // root: depth 0, accepted
+    for (int n = 1; n < N; ++n) {
+      const int pi = tr.info[tr.par[n]];
+      tr.info[n] = (int16_t)((((pi >> 1) + 1) << 1) | (pi & tr.info[n] & 1));
+    }
+  }
+  __syncthreads();
+  int key = -1;
+  for (int n = threadIdx.x; n < N; n += kThreads) {
+    const int ni = tr.info[n];
+    if (ni & 1) key = max(key, ((ni >> 1) << 13) | (8191 - n));
+  }
+  const int best_key = block_max_int(key, sh.red_i);
+  const int best = 8191 - (best_key & 8191);
+  const int depth = best_key >> 13;
+  for (int k = depth + 1 + threadIdx.x; k <= g; k += kThreads) p.out_tokens[t0 + k] = -1;
+  if (threadIdx.x == 0) {
+    for (int v = best; v != 0; v = tr.par[v]) p.out_tokens[t0 + (tr.info[v] >> 1) - 1] = p.tokens[d0 + v - 1];
+    p.out_tokens[t0 + depth] = tr.idx[best];
+    p.out_num[b] = depth;
+    if (p.out_tree_node) p.out_tree_node[b] = best;
+  }
+}
+
 template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads) void k_stats(Params p) {
-  constexpr int P = Elem<DT>::P;
-  constexpr int NE = kUA * P;  // elements per thread per row per chunk
-  constexpr int64_t CH = (int64_t)kThreads * NE;
-  constexpr float kPad = Elem<DT>::kPad;
-  constexpr bool IDX = MODE != SV_MODE_STOCHASTIC;
-  __shared__ int s_off[kLdsBatch + 1];
-  __shared__ StatsShared sh;
-  __shared__ int16_t tree_info[MODE == SV_MODE_TREE_GREEDY ? SV_MAX_GAMMA + 1 : 1];
-  __shared__ int16_t tree_par[MODE == SV_MODE_TREE_GREEDY ? SV_MAX_GAMMA + 1 : 1];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+__global__ __launch_bounds__(kThreads) void k_decide(Params p) {
+  constexpr bool SOFT = MODE == SV_MODE_STOCHASTIC || MODE == SV_MODE_NKL;
+  __shared__ DecideShared sh;
+  __shared__ TreeShared<MODE> tr;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  // independent loads first, so that they are in flight together
+  const int hdr = p.hdr[0];
+  const int d0 = p.d_off[b];
+  const int d1 = p.d_off[b + 1];
+  const float T = SOFT ? p.temp[b] : 1.0f;
+  const float ur = MODE == SV_MODE_STOCHASTIC ? p.ur[b] : 0.0f;
+  if (hdr != 0) {  // layout error: only the counts are written
+    if (tid == 0) {
+      p.out_num[b] = -1;
+      if (MODE == SV_MODE_STOCHASTIC) p.term[b].kind = kTermNone;
+    }
+    return;
+  }
+  const int g = d1 - d0;
+  const int t0 = d0 + b;
   const int64_t V = p.V;
-  const bool lds = p.B <= kLdsBatch;
-
-  // ---- packed offsets: exclusive scan of gamma in LDS (every workgroup)
-  if (lds) {
-    if (tid == 0) sh.flag = 0;
-    __syncthreads();
-    int carry = 0;
-    for (int base = 0; base < p.B; base += kThreads) {
-      const int bb = base + tid;
-      int g = bb < p.B ? p.gamma[bb] : 0;
-      if (g < 0 || g > p.R_d) {
-        sh.flag = 1;  // every writer stores 1
-        g = 0;
-      }
-      int incl = g;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += o;
-      }
-      if (lane == 63) sh.scan[wv] = incl;
-      __syncthreads();
-      int before = 0, tile = 0;
-#pragma unroll
-      for (int k = 0; k < kWaves; ++k) {
-        if (k < wv) before += sh.scan[k];
-        tile += sh.scan[k];
-      }
-      if (bb < p.B) s_off[bb] = carry + before + incl - g;
-      carry += tile;  // at most B * R_d: bounded because each g <= R_d
-      __syncthreads();
-    }
-    if (tid == 0) s_off[p.B] = carry;
-    __syncthreads();
-    const bool bad = sh.flag != 0 || carry != p.R_d;
-    if (blockIdx.x == 0) {
-      // offsets for the draw kernel; layout flag
-      for (int bb = tid; bb <= p.B; bb += kThreads) {
-        p.d_off[bb] = s_off[bb];
-        p.t_off[bb] = s_off[bb] + bb;
-      }
-      if (tid == 0) p.hdr[0] = bad ? 1 : 0;
-      if (bad)
-        for (int bb = tid; bb < p.B; bb += kThreads) p.out_num[bb] = -1;
-    }
-    if (bad) return;
-  } else if (p.hdr[0] != 0) {
-    return;  // layout error found by k_prep
+  const float Lhi = SOFT ? (float)(kLog2eD / (double)T) : 0.0f;
+  // request-level checks; the per-position ones follow the decision passes
+  // (which only read inside the rows for valid token ids), and overwrite
+  // everything the passes wrote if they fail
+  if (g > p.max_gamma || (SOFT && !temp_ok(T)) || (MODE == SV_MODE_STOCHASTIC && !unit_ok(ur))) {
+    finish_invalid(p, b, t0, d0, g);
+    return;
   }
 
-  // ---- this workgroup's items
-  const int nch = p.nch_a;
-  const int64_t N = (int64_t)p.n_task * nch;
-  const int64_t G = gridDim.x;
-  const int64_t i0 = (int64_t)blockIdx.x * N / G, i1 = ((int64_t)blockIdx.x + 1) * N / G;
-  if (i0 >= i1) return;
+  const int glog = p.grp_log2, S = 1 << glog, TPP = kThreads >> glog;
+  const int ntask = MODE == SV_MODE_STOCHASTIC ? g : g + 1;
+  const int64_t tbase = MODE == SV_MODE_STOCHASTIC ? d0 : t0;
+  const bool diag = SOFT && (p.out_p_x || p.out_q_x || p.out_nkl);
+  const bool want_kl = SOFT && p.want_kl;
+  const double c = (double)Lhi * kLn2D;  // d(log p)/d(logit)
+  const double lnV = log((double)p.V);
+  int j = -1;
+  float jm_t = 0.f, jm_d = 0.f;
+  double js_t = 1.0, js_d = 1.0;
+  int jidx = 0;
+  for (int base = 0; base < ntask; base += TPP) {
+    const int q = tid >> glog, l = tid & (S - 1);
+    const int ti = base + q;
+    const bool has = ti < ntask;
+    const bool pair = SOFT && ti < g;
+    // the group leader's position data, issued before the partial loads
+    int x = -1;
+    float tx = 0.f, dx = 0.f, u = 0.f;
+    if (MODE != SV_MODE_TREE_GREEDY && l == 0 && ti < g) {
+      x = p.tokens[d0 + ti];
+      if (SOFT && x >= 0 && x < p.V) {
+        tx = load_scalar<DT>(p.target, t0 + ti, V, x);
+        dx = load_scalar<DT>(p.draft, d0 + ti, V, x);
+      }
+      if (MODE == SV_MODE_STOCHASTIC) u = p.ua[d0 + ti];
+    }
+    const Merged r = merge_task<SOFT>(p, tbase + ti, has, pair, l, glog, Lhi);
+    if (l == 0 && has) {
+      const int idx = r.idx == INT_MAX ? 0 : r.idx;  // no element above the pad value: position 0
+      if constexpr (MODE == SV_MODE_TREE_GREEDY) tr.idx[ti] = idx;
+      sh.mt[q] = r.mt;
+      sh.md[q] = r.md;
+      sh.st[q] = r.st;
+      sh.sd[q] = r.sd;
+      sh.idx[q] = idx;
+      int acc = 0, need = 0;
+      float kl = 0.f;
+      if (pair) {
+        // log p(x) and log q(x) from the merged statistics
+        const double lpx = (double)(tx - r.mt) * c - log(r.st);
+        const double lqx = (double)(dx - r.md) * c - log(r.sd);
+        if (p.out_p_x) p.out_p_x[d0 + ti] = (float)exp(lpx);
+        if (p.out_q_x) p.out_q_x[d0 + ti] = (float)exp(lqx);
+        if (MODE == SV_MODE_STOCHASTIC) acc = (double)u <= fmin(1.0, exp(lpx - lqx)) ? 1 : 0;
+        if (want_kl && p.V > 1) {
+          // KL(q||p) = E_q[d - t]/T - (m_d - m_t)/T - log(s_d / s_t)
+          const double lg = log(r.sd / r.st);
+          const double klv = r.w / r.sd * c - (double)(r.md - r.mt) * c - lg;
+          const double err = kKlErr * (r.z / r.sd * c + 1.0);
+          need = (err > kKlRel * klv) ? 1 : 0;
+          if (MODE == SV_MODE_NKL && fabs(klv - (double)p.delta * lnV) <= err) need = 1;
+          kl = (float)klv;
+        }
+      } else if (MODE == SV_MODE_GREEDY) {
+        acc = (ti < g && x == idx) ? 1 : 0;
+      }
+      sh.acc[q] = acc;
+      sh.kl[q] = kl;
+      sh.need[q] = need;
+    }
+    if (tid == 0) sh.nlist = 0;
+    __syncthreads();
+    if (want_kl) {
+      if (tid < TPP && base + tid < g && sh.need[tid]) sh.list[atomicAdd(&sh.nlist, 1)] = tid;
+      __syncthreads();
+      const int nl = sh.nlist;
+      for (int k = 0; k < nl; ++k) {
+        const int s = sh.list[k], i = base + s;
+        const double kl2 = kl_second_pass<DT, VEC>(p, t0 + i, d0 + i, sh.mt[s], sh.md[s], sh.st[s], sh.sd[s], Lhi,
+                                                    sh.red_d);
+        if (tid == 0) sh.kl[s] = (float)kl2;
+        __syncthreads();
+      }
+      if (tid < TPP && base + tid < g) {
+        const double nkl = p.V > 1 ? (double)sh.kl[tid] / lnV : 0.0;
+        if (p.out_nkl) p.out_nkl[d0 + base + tid] = (float)nkl;
+        if (MODE == SV_MODE_NKL) sh.acc[tid] = nkl < (double)p.delta ? 1 : 0;
+      }
+      __syncthreads();
+    }
+    if (MODE != SV_MODE_TREE_GREEDY) {
+      const int cand = (tid < TPP && base + tid < ntask && !sh.acc[tid]) ? base + tid : INT_MAX;
+      const int jp = block_min_int(cand, sh.red_i);
+      if (j < 0 && jp != INT_MAX) {
+        j = jp;
+        const int s = jp - base;
+        jm_t = sh.mt[s];
+        jm_d = sh.md[s];
+        js_t = sh.st[s];
+        js_d = sh.sd[s];
+        jidx = sh.idx[s];
+      }
+      if (j >= 0 && !diag) break;
+    }
+    __syncthreads();  // LDS of this pass is reused by the next
+  }
 
-  // segment state (uniform across the workgroup)
-  int task = -1, b = 0, g = 0, t0 = 0, d0 = 0, trow = 0, drow = -1, seg_first = 0, x = -1;
-  bool pair = false;
-  float T = 1.0f, Lhi = 0.0f, Llo = 0.0f;
-  LaneRow rt{kPad, 0.f, INT_MAX}, rd{kPad, 0.f, INT_MAX};
-  float W = 0.f;
-  float gx_t = 0.f, gx_d = 0.f;
-  bool gathered = false;
-
-  auto rows_of = [&](int tk, int& tr, int& dr, bool& pr, ReqInfo& ri) {
-    ri = locate<MODE>(p, s_off, lds, tk);
+  bool bad = false;
+  for (int k = tid; k < g; k += kThreads) {
+    const int x = p.tokens[d0 + k];
+    bool ok = x >= 0 && x < p.V;
+    if (MODE == SV_MODE_STOCHASTIC) ok = ok && unit_ok(p.ua[d0 + k]);
+    if (MODE == SV_MODE_TREE_GREEDY) {
+      const int pa = p.parents[d0 + k];  // parent of node k + 1
+      ok = ok && pa >= 0 && pa <= k;
+    }
+    if (!ok) bad = true;
+  }
+  if (__syncthreads_or(bad)) {
+    finish_invalid(p, b, t0, d0, g);
+    return;
+  }
+  if constexpr (MODE == SV_MODE_TREE_GREEDY) {
+    resolve_tree(p, b, g, t0, d0, tr, sh);
+    return;
+  }
+  if (j < 0) j = g;  // stochastic: every draft accepted
+  for (int k = tid; k <= g; k += kThreads) {
+    if (k < j) p.out_tokens[t0 + k] = p.tokens[d0 + k];
+    else if (k > j) p.out_tokens[t0 + k] = -1;
+    else if (MODE != SV_MODE_STOCHASTIC) p.out_tokens[t0 + k] = jidx;  // stochastic: the draw pass writes it
+  }
+  if (tid == 0) {
+    p.out_num[b] = j;
     if (MODE == SV_MODE_STOCHASTIC) {
-      tr = tk + ri.b;
-      dr = tk;
-      pr = true;
-    } else {
-      tr = tk;
-      const int i = tk - ri.t0;
-      pr = (MODE == SV_MODE_NKL) && i < ri.g;
-      dr = pr ? ri.d0 + i : -1;
-    }
-  };
-
-  // prefetch the first chunk
-  uint4 cur_t[kUA], cur_d[kUA], nxt_t[kUA], nxt_d[kUA];
-  int n_trow, n_drow;
-  bool n_pair;
-  {
-    ReqInfo ri;
-    rows_of((int)(i0 / nch), n_trow, n_drow, n_pair, ri);
-    const int64_t e0 = (i0 % nch) * CH;
-#pragma unroll
-    for (int k = 0; k < kUA; ++k) {
-      nxt_t[k] = fetch<DT, VEC>(p.target, n_trow, V, e0 + ((int64_t)k * kThreads + tid) * P);
-      if (n_pair) nxt_d[k] = fetch<DT, VEC>(p.draft, n_drow, V, e0 + ((int64_t)k * kThreads + tid) * P);
-    }
-  }
-
-  for (int64_t it = i0; it < i1; ++it) {
-    const int tk = (int)(it / nch);
-    const int chunk = (int)(it - (int64_t)tk * nch);
-#pragma unroll
-    for (int k = 0; k < kUA; ++k) {
-      cur_t[k] = nxt_t[k];
-      cur_d[k] = nxt_d[k];
-    }
-    if (tk != task) {  // a new task segment starts
-      ReqInfo ri;
-      rows_of(tk, trow, drow, pair, ri);
-      task = tk;
-      b = ri.b;
-      g = ri.g;
-      t0 = ri.t0;
-      d0 = ri.d0;
-      seg_first = chunk;
-      rt = LaneRow{kPad, 0.f, INT_MAX};
-      rd = LaneRow{kPad, 0.f, INT_MAX};
-      W = 0.f;
-      gathered = false;
-      if (pair) {
-        T = p.temp[b];
-        const double Ld = kLog2eD / (double)T;
-        Lhi = (float)Ld;
-        Llo = (float)(Ld - (double)Lhi);
-        x = p.tokens[drow];
-      }
-    }
-    // next chunk's loads go out before this one is folded
-    if (it + 1 < i1) {
-      const int tk2 = (int)((it + 1) / nch);
-      if (tk2 != task) {
-        ReqInfo ri;
-        rows_of(tk2, n_trow, n_drow, n_pair, ri);
+      Term tm;
+      tm.j = j;
+      tm.trow = t0 + j;
+      tm.Lhi = Lhi;
+      if (j < g) {
+        tm.kind = kTermResidual;
+        tm.drow = d0 + j;
+        tm.m_t = jm_t;
+        tm.m_d = jm_d;
+        tm.k0 = (float)(js_t / js_d);
       } else {
-        n_trow = trow;
-        n_drow = drow;
-        n_pair = pair;
+        tm.kind = kTermBonus;
+        tm.drow = -1;
+        tm.m_t = tm.m_d = tm.k0 = 0.0f;
       }
-      const int64_t e1 = ((it + 1) - (int64_t)tk2 * nch) * CH;
-#pragma unroll
-      for (int k = 0; k < kUA; ++k) {
-        nxt_t[k] = fetch<DT, VEC>(p.target, n_trow, V, e1 + ((int64_t)k * kThreads + tid) * P);
-        if (n_pair) nxt_d[k] = fetch<DT, VEC>(p.draft, n_drow, V, e1 + ((int64_t)k * kThreads + tid) * P);
-      }
+      p.term[b] = tm;
     }
-    const int64_t e_chunk = (int64_t)chunk * CH;
-    // gather of the logits at the drafted token
-    if (pair && tid == 0 && x >= e_chunk && x < e_chunk + CH && x < V) {
-      gx_t = load_scalar<DT>(p.target, trow, V, x);
-      gx_d = load_scalar<DT>(p.draft, drow, V, x);
-      gathered = true;
-    }
-    // fold this chunk
-    float vt[NE];
-#pragma unroll
-    for (int k = 0; k < kUA; ++k) unpack<DT>(cur_t[k], vt + k * P);
-    fold_row<NE, P, IDX>(rt, vt, Lhi, pair, e_chunk + (int64_t)tid * P, (int64_t)kThreads * P, kPad);
-    if (pair) {
-      float vd[NE];
-#pragma unroll
-      for (int k = 0; k < kUA; ++k) unpack<DT>(cur_d[k], vd + k * P);
-      if (p.want_w)
-        fold_draft_w<NE>(rd, W, vd, vt, Lhi, kPad);
-      else
-        fold_row<NE, P, false>(rd, vd, Lhi, true, 0, 0, kPad);
-    }
-
-    const bool seg_end = (it + 1 == i1) || (chunk + 1 == nch);
-    if (!seg_end) continue;
-
-    // ---- end of a task segment: workgroup reduction and publication
-    const float Mt = wave_max(rt.m);
-    int It = INT_MAX;
-    if (IDX) It = wave_min_int(rt.m == Mt ? rt.idx : INT_MAX);
-    float St = 0.f, Md = kPad, Sd = 0.f, Wd = 0.f;
-    if (pair) {
-      St = wave_sum(rt.s * exp_hp(rt.m - Mt, Lhi, Llo));
-      Md = wave_max(rd.m);
-      const float f = exp_hp(rd.m - Md, Lhi, Llo);
-      Sd = wave_sum(rd.s * f);
-      if (p.want_w) Wd = wave_sum(W * f);
-    }
-    __syncthreads();  // LDS of the previous segment is no longer read
-    if (lane == 0) {
-      sh.m[0][wv] = Mt;
-      sh.s[0][wv] = St;
-      sh.m[1][wv] = Md;
-      sh.s[1][wv] = Sd;
-      sh.w[wv] = Wd;
-      sh.i[wv] = It;
-    }
-    __syncthreads();
-    const int64_t w_lo = (((int64_t)task * nch + 1) * G - 1) / N;  // first workgroup of the task
-    if (tid == 0) {
-      PartA pa;
-      float M = sh.m[0][0], M2 = sh.m[1][0];
-      for (int k = 1; k < kWaves; ++k) {
-        M = fmaxf(M, sh.m[0][k]);
-        M2 = fmaxf(M2, sh.m[1][k]);
-      }
-      int I = INT_MAX;
-      double S = 0.0, S2 = 0.0, W2 = 0.0;
-      for (int k = 0; k < kWaves; ++k) {
-        if (sh.m[0][k] == M) I = min(I, sh.i[k]);
-        if (pair) {
-          S += (double)sh.s[0][k] * (double)exp_hp(sh.m[0][k] - M, Lhi, Llo);
-          const double f = (double)exp_hp(sh.m[1][k] - M2, Lhi, Llo);
-          S2 += (double)sh.s[1][k] * f;
-          W2 += (double)sh.w[k] * f;
-        }
-      }
-      pa.m_t = M;
-      pa.s_t = S;
-      pa.m_d = M2;
-      pa.s_d = S2;
-      pa.w = W2;
-      pa.idx = I;
-      pa.pad = 0;
-      put_part_a(p.part_a + (int64_t)task * nch + ((int64_t)blockIdx.x - w_lo), pa);
-      if (gathered) {
-        st_dev(p.gat + 2 * drow, gx_t);
-        st_dev(p.gat + 2 * drow + 1, gx_d);
-      }
-      const unsigned mine = (unsigned)(chunk + 1 - seg_first);
-      const unsigned old = signal_n(p.cnt_task + task, mine);
-      sh.flag = (old + mine == (unsigned)nch);
-    }
-    __syncthreads();
-    if (!sh.flag) continue;
-
-    // ---- this workgroup completed the task: merge the partials in order
-    const int64_t w_hi = (((int64_t)task * nch + nch) * G - 1) / N;
-    const int nseg = (int)(w_hi - w_lo + 1);
-    if (wv == 0) {
-      float m1 = -FLT_MAX, m2 = -FLT_MAX;
-      double s1 = 0.0, s2 = 0.0, w2 = 0.0;
-      int i1x = INT_MAX;
-      for (int sg = lane; sg < nseg; sg += 64) {
-        const PartA q = get_part_a(p.part_a + (int64_t)task * nch + sg);
-        if (q.m_t > m1) {
-          if (pair) s1 = s1 * (double)exp_hp(m1 - q.m_t, Lhi, Llo) + q.s_t;
-          m1 = q.m_t;
-          i1x = q.idx;
-        } else {
-          if (pair) s1 += q.s_t * (double)exp_hp(q.m_t - m1, Lhi, Llo);
-          if (q.m_t == m1) i1x = min(i1x, q.idx);
-        }
-        if (pair) {
-          if (q.m_d > m2) {
-            const double f = (double)exp_hp(m2 - q.m_d, Lhi, Llo);
-            s2 = s2 * f + q.s_d;
-            w2 = w2 * f + q.w;
-            m2 = q.m_d;
-          } else {
-            const double f = (double)exp_hp(q.m_d - m2, Lhi, Llo);
-            s2 += q.s_d * f;
-            w2 += q.w * f;
-          }
-        }
-      }
-      const float M1 = wave_max(m1);
-      const int I1 = wave_min_int(m1 == M1 ? i1x : INT_MAX);
-      double S1 = 0.0, S2 = 0.0, W2 = 0.0;
-      float M2 = 0.f;
-      if (pair) {
-        S1 = wave_sum_d(s1 * (double)exp_hp(m1 - M1, Lhi, Llo));
-        M2 = wave_max(m2);
-        const double f = (double)exp_hp(m2 - M2, Lhi, Llo);
-        S2 = wave_sum_d(s2 * f);
-        W2 = wave_sum_d(w2 * f);
-      }
-      if (lane == 0) {
-        TaskStat ts;
-        ts.m_t = M1;
-        ts.s_t = S1;
-        ts.m_d = M2;
-        ts.s_d = S2;
-        ts.w = W2;
-        ts.idx = I1;
-        ts.kl = 0.0f;
-        int refine = 0;
-        if (pair && p.want_w) {
-          // one-pass KL and a bound on its rounding error (a few 1e-7 of the
-          // magnitude of the terms that cancel)
-          const double a = W2 / S2 / (double)T, bm = ((double)M2 - (double)M1) / (double)T, lg = log(S2 / S1);
-          const double kl = a - bm - lg;
-          const double err = 4e-7 * (fabs(a) + fabs(bm) + fabs(lg) + 1.0);
-          refine = err > 1e-5 * kl;
-          if (MODE == SV_MODE_NKL && p.V > 1) {
-            const double lnV = log((double)p.V);
-            refine |= fabs(kl / lnV - (double)p.delta) < 2.0 * err / lnV;
-          }
-          ts.kl = (float)kl;
-        }
-        put_stat(p.stat + task, ts);
-        sh.refine = refine;
-        sh.d[0] = S1;
-        sh.d[1] = S2;
-        sh.m[0][0] = M1;
-        sh.m[1][0] = M2;
-      }
-    }
-    __syncthreads();
-    if (sh.refine) {
-      const double kl =
-          kl_second_pass<DT, VEC>(p, trow, drow, sh.m[0][0], sh.m[1][0], sh.d[0], sh.d[1], T, Lhi, sh.d + 2);
-      if (tid == 0) st_dev(&p.stat[task].kl, (float)kl);
-    }
-    if (tid == 0) {
-      st_dev(p.cnt_task + task, 0u);
-      const unsigned need = (unsigned)(MODE == SV_MODE_STOCHASTIC ? g : g + 1);
-      const unsigned old = signal_n(p.cnt_req + b, 1u);
-      sh.flag = (old + 1 == need);
-    }
-    __syncthreads();
-    if (!sh.flag) continue;
-
-    // ---- last task of the request: decide
-    if (MODE == SV_MODE_STOCHASTIC)
-      decide_stochastic(p, b, g, t0, d0, sh.dec);
-    else if (MODE == SV_MODE_TREE_GREEDY)
-      decide_tree(p, b, g, t0, d0, sh.dec, tree_info, tree_par);
-    else
-      decide_argmax_chain<MODE>(p, b, g, t0, d0, sh.dec);
-    if (tid == 0) st_dev(p.cnt_req + b, 0u);
-    __syncthreads();
   }
 }
 
 // ----------------------------------------------------------------------------
-// k_draw (stochastic mode)
+// k_draw and k_select (stochastic mode)
+//
+// k_draw: items are (request, wave-chunk) pairs numbered b * nch_c + c; a
+// wave-chunk is 64 lanes x kUC 16-byte vectors of the terminal row (and of the
+// draft row for a residual).  Every wave of the grid streams a contiguous
+// range of items on its own, without workgroup barriers, and writes one record
+// of float64 sums per item.  k_select: one wave per request combines the
+// records, picks the wave-chunk holding the draw and re-reads it.
 // ----------------------------------------------------------------------------
 
-struct DrawShared {
-  double d[kWaves];
-  float f[kWaves];
-  int i[kWaves];
-  int last;
-  double ta[kThreads], tb[kThreads];  // one tile of chunk partials
-  float tm[kThreads];
-  double a_tot, b_tot, S, base;
-  float mrow;
-  int cstar, lastpos_chunk;
-};
+__device__ __forceinline__ double wave_incl_scan_d(double v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
 
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_draw(Params p) {
+// Record of one wave-chunk: a_y = 2^((t_y - m_t) L) and b_y = 2^((d_y - m_d) L)
+// are p_y and q_y up to the factors s_t, s_d; the residual record also holds
+// the sums over {y : a_y > k0 b_y}, the support of max(0, p - q).  A bonus
+// record holds the chunk maximum and sum_y 2^((t_y - m_c) L).
+template <int DT, bool RESID>
+__device__ __forceinline__ void draw_record(const Vecs<kUC>& qt, const Vecs<kUC>& qd, const Term& tm, float Lhi,
+                                            PartC* dst) {
   constexpr int P = Elem<DT>::P;
-  constexpr int NE = kUC * P;
-  constexpr int64_t CH = (int64_t)kThreads * NE;
-  __shared__ DrawShared sh;
-  if (p.hdr[0] != 0) return;
-  const int tid = threadIdx.x;
-  const int b = blockIdx.x / p.nch_c;
-  const int chunk = blockIdx.x - b * p.nch_c;
-  const int64_t V = p.V;
-  const int g = p.gamma[b];
-  const int t0 = p.t_off[b];
-  const float T = p.temp[b];
-  const float ur = p.ur[b];
-
-  int kind, j, trow, drow;
-  float Mt = 0.f, Md = 0.f, k0 = 0.f;
-  if (g == 0) {
-    // nothing drafted: the step is a plain draw from target row 0
-    if (!temp_ok(T) || !unit_ok(ur)) {
-      if (chunk == 0 && tid == 0) {
-        p.out_num[b] = -1;
-        p.out_tokens[t0] = -1;
-        if (p.out_resid) p.out_resid[b] = __builtin_nanf("");
-      }
-      return;
-    }
-    kind = kTermBonus;
-    j = 0;
-    trow = t0;
-    drow = -1;
-  } else {
-    const Term tm = p.term[b];
-    kind = tm.kind;
-    if (kind == kTermNone) return;
-    j = tm.j;
-    trow = tm.trow;
-    drow = tm.drow;
-    Mt = tm.m_t;
-    Md = tm.m_d;
-    k0 = tm.k0;
-  }
-  const double Ld = kLog2eD / (double)T;
-  const float Lhi = (float)Ld;
-  const float Llo = (float)(Ld - (double)Lhi);
-  const int64_t e_chunk = (int64_t)chunk * CH;
-
-  // ---- chunk partial sums
-  uint4 qt[kUC], qd[kUC];
-#pragma unroll
-  for (int k = 0; k < kUC; ++k) qt[k] = fetch<DT, VEC>(p.target, trow, V, e_chunk + ((int64_t)k * kThreads + tid) * P);
-  if (kind == kTermResidual) {
-#pragma unroll
-    for (int k = 0; k < kUC; ++k) qd[k] = fetch<DT, VEC>(p.draft, drow, V, e_chunk + ((int64_t)k * kThreads + tid) * P);
-  }
-  float vt[NE];
-#pragma unroll
-  for (int k = 0; k < kUC; ++k) unpack<DT>(qt[k], vt + k * P);
   double A = 0.0, Bs = 0.0, Ap = 0.0, Bp = 0.0;
   float mc = 0.f;
-  if (kind == kTermResidual) {
-    float vd[NE];
-#pragma unroll
-    for (int k = 0; k < kUC; ++k) unpack<DT>(qd[k], vd + k * P);
+  if (RESID) {
 #pragma unroll
     for (int k = 0; k < kUC; ++k) {
+      float vt[P], vd[P];
+      unpack<DT>(qt.v[k], vt);
+      unpack<DT>(qd.v[k], vd);
       float sa = 0.f, sb = 0.f, sap = 0.f, sbp = 0.f;
 #pragma unroll
       for (int e = 0; e < P; ++e) {
-        const float a = exp_hp(vt[k * P + e] - Mt, Lhi, Llo);
-        const float bb = exp_hp(vd[k * P + e] - Md, Lhi, Llo);
+        const float a = ex2(vt[e] - tm.m_t, Lhi);
+        const float bb = ex2(vd[e] - tm.m_d, Lhi);
         sa += a;
         sb += bb;
-        const bool in = a > k0 * bb;
+        const bool in = a > tm.k0 * bb;
         sap += in ? a : 0.f;
         sbp += in ? bb : 0.f;
       }
@@ -1216,204 +1084,279 @@ __global__ __launch_bounds__(kThreads) void k_draw(Params p) {
       Ap += (double)sap;
       Bp += (double)sbp;
     }
+    A = wave_sum_d(A);
+    Bs = wave_sum_d(Bs);
+    Ap = wave_sum_d(Ap);
+    Bp = wave_sum_d(Bp);
   } else {
+    float vt[kUC * P];
+#pragma unroll
+    for (int k = 0; k < kUC; ++k) unpack<DT>(qt.v[k], vt + k * P);
     float m = vt[0];
 #pragma unroll
-    for (int e = 1; e < NE; ++e) m = fmaxf(m, vt[e]);
-    mc = block_max(m, sh.f);
+    for (int e = 1; e < kUC * P; ++e) m = fmaxf(m, vt[e]);
+    mc = wave_max(m);  // a wave-chunk starts inside the row: mc is a logit
 #pragma unroll
     for (int k = 0; k < kUC; ++k) {
       float sa = 0.f;
 #pragma unroll
-      for (int e = 0; e < P; ++e) sa += exp_hp(vt[k * P + e] - mc, Lhi, Llo);
+      for (int e = 0; e < P; ++e) sa += ex2(vt[k * P + e] - mc, Lhi);
       A += (double)sa;
     }
+    A = wave_sum_d(A);
   }
-  A = block_sum_d(A, sh.d);
-  if (kind == kTermResidual) {
-    Bs = block_sum_d(Bs, sh.d);
-    Ap = block_sum_d(Ap, sh.d);
-    Bp = block_sum_d(Bp, sh.d);
+  if ((threadIdx.x & 63) == 0) {  // plain stores: the reader is the next kernel
+    dst->a = A;
+    dst->b = Bs;
+    dst->ap = Ap;
+    dst->bp = Bp;
+    dst->m = mc;
   }
-  if (tid == 0) {
-    PartC pc;
-    pc.a = A;
-    pc.b = Bs;
-    pc.ap = Ap;
-    pc.bp = Bp;
-    pc.m = mc;
-    pc.pad[0] = pc.pad[1] = pc.pad[2] = 0;
-    put_part_c(p.part_c + (int64_t)b * p.nch_c + chunk, pc);
-    const unsigned old = signal(p.cnt_draw + b);
-    sh.last = (old == (unsigned)(p.nch_c - 1));
-  }
-  __syncthreads();
-  if (!sh.last) return;
+}
 
-  // ---- last workgroup of the request: choose the chunk.  Chunk partials are
-  // staged through LDS a tile at a time and combined by thread 0 in chunk
-  // order, so the result does not depend on which workgroup finished last.
-  PartC* pcs = p.part_c + (int64_t)b * p.nch_c;
-  const int nch = p.nch_c;
-  // stage 1: totals of a and b, and the row maximum (bonus)
-  {
-    double at = 0.0, bt = 0.0;
-    float M = -FLT_MAX;
-    for (int base = 0; base < nch; base += kThreads) {
-      const int ch = base + tid;
-      if (ch < nch) {
-        const PartC q = get_part_c(pcs + ch);
-        sh.ta[tid] = q.a;
-        sh.tb[tid] = q.b;
-        sh.tm[tid] = q.m;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        const int n = min(kThreads, nch - base);
-        for (int k = 0; k < n; ++k) {
-          at += sh.ta[k];
-          bt += sh.tb[k];
-          M = fmaxf(M, sh.tm[k]);
-        }
-      }
-      __syncthreads();
-    }
-    if (tid == 0) {
-      sh.a_tot = at;
-      sh.b_tot = bt;
-      sh.mrow = M;
-    }
-    __syncthreads();
-  }
-  const double K = kind == kTermResidual ? sh.a_tot / sh.b_tot : 0.0;
-  const float Mrow = sh.mrow;
-  // chunk weight: residual  sum_{a > k0 b}(a - K b) = A+ - K B+ ; bonus  A_c exp((m_c - M)/T)
-  auto weight = [&](const PartC& q, int fb) -> double {
-    if (kind == kTermResidual) return fb ? q.a : q.ap - K * q.bp;
-    return q.a * exp2(((double)q.m - (double)Mrow) * Ld);
-  };
-  int fallback = 0;
-  // stage 2: total mass S
-  double S;
-  {
-    double tot = 0.0;
-    for (int base = 0; base < nch; base += kThreads) {
-      const int ch = base + tid;
-      if (ch < nch) sh.ta[tid] = weight(get_part_c(pcs + ch), 0);
-      __syncthreads();
-      if (tid == 0) {
-        const int n = min(kThreads, nch - base);
-        for (int k = 0; k < n; ++k) tot += sh.ta[k];
-      }
-      __syncthreads();
-    }
-    if (tid == 0) sh.S = tot;
-    __syncthreads();
-    S = sh.S;
-    if (kind == kTermResidual && !(S > 0.0)) {
-      // max(0, p - q) vanished numerically: draw from p_j instead
-      fallback = 1;
-      S = sh.a_tot;
-    }
-  }
-  const double target = (double)ur * S;
-  // stage 3: first chunk whose cumulative weight exceeds the target
-  if (tid == 0) {
-    sh.cstar = -1;
-    sh.lastpos_chunk = -1;
-    sh.base = 0.0;
-  }
-  __syncthreads();
-  {
-    double cum = 0.0;
-    for (int base = 0; base < nch; base += kThreads) {
-      const int ch = base + tid;
-      if (ch < nch) sh.ta[tid] = weight(get_part_c(pcs + ch), fallback);
-      __syncthreads();
-      if (tid == 0 && sh.cstar < 0) {
-        const int n = min(kThreads, nch - base);
-        for (int k = 0; k < n; ++k) {
-          if (sh.ta[k] > 0.0) sh.lastpos_chunk = base + k;
-          const double nxt = cum + sh.ta[k];
-          if (nxt > target) {
-            sh.cstar = base + k;
-            sh.base = cum;
-            break;
-          }
-          cum = nxt;
-        }
-      }
-      __syncthreads();
-      if (sh.cstar >= 0) break;  // uniform: read after the barrier
-    }
-  }
-  int cstar = sh.cstar;
-  bool take_last = false;
-  if (cstar < 0) {  // rounding left the target at/after the end: last token with mass
-    cstar = sh.lastpos_chunk >= 0 ? sh.lastpos_chunk : nch - 1;
-    take_last = true;
-  }
-  const double cbase = sh.base;
-
-  // ---- re-read chunk c*: thread t owns NE consecutive tokens
-  const int64_t y0 = (int64_t)cstar * CH + (int64_t)tid * NE;
-  double r[NE];
-  double tsum = 0.0;
-  const double chunk_factor =
-      (kind == kTermBonus) ? exp2(((double)ld_dev(&pcs[cstar].m) - (double)Mrow) * Ld) : 1.0;
-  const float ref = (kind == kTermBonus) ? ld_dev(&pcs[cstar].m) : Mt;
+template <int DT, bool VEC, bool RESID>
+__device__ __forceinline__ void draw_issue(const Params& p, const Term& tm, int64_t e_chunk, Vecs<kUC>& qt,
+                                           Vecs<kUC>& qd) {
+  constexpr int P = Elem<DT>::P;
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int k = 0; k < kUC; ++k) {
-    const uint4 q = fetch<DT, VEC>(p.target, trow, V, y0 + k * P);
-    float v[P];
-    unpack<DT>(q, v);
-    float vdd[P];
-    if (kind == kTermResidual && !fallback) {
-      const uint4 qq = fetch<DT, VEC>(p.draft, drow, V, y0 + k * P);
-      unpack<DT>(qq, vdd);
+    const int64_t e0 = e_chunk + ((int64_t)k * 64 + lane) * P;
+    qt.v[k] = fetch<DT, VEC>(p.target, tm.trow, p.V, e0);
+    if (RESID) qd.v[k] = fetch<DT, VEC>(p.draft, tm.drow, p.V, e0);
+  }
+}
+
+// Streams wave-chunks [c0, c1) of request b (loads of chunk c + 1 in flight
+// while chunk c is reduced).
+template <int DT, bool VEC, bool RESID>
+__device__ __forceinline__ void draw_segment(const Params& p, int b, const Term& tm, int c0, int c1, float Lhi) {
+  constexpr int64_t CHW = (int64_t)64 * kUC * Elem<DT>::P;
+  PartC* rec = p.part_c + (int64_t)b * p.nch_c;
+  Vecs<kUC> ct, cd;
+  draw_issue<DT, VEC, RESID>(p, tm, (int64_t)c0 * CHW, ct, cd);
+  for (int c = c0; c < c1 - 1; ++c) {
+    Vecs<kUC> nt, nd;
+    draw_issue<DT, VEC, RESID>(p, tm, (int64_t)(c + 1) * CHW, nt, nd);
+    draw_record<DT, RESID>(ct, cd, tm, Lhi, rec + c);
+    ct = nt;
+    cd = nd;
+  }
+  draw_record<DT, RESID>(ct, cd, tm, Lhi, rec + (c1 - 1));
+}
+
+// Residual chunk weight sum_{a > k0 b} (a - K b) = A+ - K B+, K = A/B, i.e.
+// max(0, p - q) in units of 1/A; `fb`: the fallback draw from p_j; bonus:
+// sum_y 2^((t_y - M) L) with M the row maximum.
+__device__ __forceinline__ double chunk_weight(double a, double ap, double bp, float m, bool resid, bool fb, double K,
+                                               float M, double Ld) {
+  if (resid) return fb ? a : ap - K * bp;
+  return a * exp2(((double)m - (double)M) * Ld);
+}
+
+// Residual weight of one token (units of 1/A), or its bonus / fallback weight.
+__device__ __forceinline__ double token_weight(float t, float d, bool two, const Term& tm, float ref, float Lhi,
+                                               double K, double cf) {
+  const float a = ex2(t - ref, Lhi);
+  if (two) {
+    const float bb = ex2(d - tm.m_d, Lhi);
+    return (a > tm.k0 * bb) ? (double)a - K * (double)bb : 0.0;
+  }
+  return (double)a * cf;
+}
+
+// Token draw of request b by one wave.  CACHED: the request has at most 256
+// records; their fields are kept in registers (4 per lane) instead of being
+// read again for each sweep.  Records are combined by fixed wave-wide
+// reductions and scans in chunk order.
+template <int DT, bool VEC, bool CACHED>
+__device__ __forceinline__ void draw_select(const Params& p, int b, const Term& tm, float Lhi) {
+  constexpr int P = Elem<DT>::P;
+  constexpr int NE = kUC * P;
+  constexpr int64_t CHW = (int64_t)64 * NE;
+  constexpr int R = CACHED ? 4 : 1;
+  const int lane = threadIdx.x & 63;
+  const int nch = p.nch_c;
+  PartC* pcs = p.part_c + (int64_t)b * nch;
+  const bool resid = tm.kind == kTermResidual;
+  const double Ld = (double)Lhi;
+  double ca[R], cap[R], cbp[R];
+  float cm[R];
+  double at = 0.0, bt = 0.0;
+  float M = -INFINITY;
+  if constexpr (CACHED) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int ch = lane + 64 * r;
+      ca[r] = cap[r] = cbp[r] = 0.0;
+      cm[r] = -INFINITY;
+      if (ch < nch) {
+        const PartC q = pcs[ch];
+        ca[r] = q.a;
+        cap[r] = q.ap;
+        cbp[r] = q.bp;
+        cm[r] = q.m;
+        at += q.a;
+        bt += q.b;
+        M = fmaxf(M, q.m);
+      }
     }
+  } else {
+    for (int ch = lane; ch < nch; ch += 64) {
+      const PartC q = pcs[ch];
+      at += q.a;
+      bt += q.b;
+      M = fmaxf(M, q.m);
+    }
+  }
+  at = wave_sum_d(at);
+  bt = wave_sum_d(bt);
+  M = wave_max(M);
+  const double K = resid ? at / bt : 0.0;
+  double S = 0.0;
+  if constexpr (CACHED) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (lane + 64 * r < nch) S += chunk_weight(ca[r], cap[r], cbp[r], cm[r], resid, false, K, M, Ld);
+  } else {
+    for (int ch = lane; ch < nch; ch += 64) {
+      const PartC q = pcs[ch];
+      S += chunk_weight(q.a, q.ap, q.bp, q.m, resid, false, K, M, Ld);
+    }
+  }
+  S = wave_sum_d(S);
+  bool fb = false;
+  if (resid && !(S > 0.0)) {
+    // max(0, p - q) vanished numerically: draw from p_j instead
+    fb = true;
+    S = at;
+  }
+  const double target = (double)p.ur[b] * S;
+
+  // the wave-chunk whose cumulative weight first exceeds the target: one
+  // round per 64 consecutive chunks
+  int cstar = -1, clast = -1;
+  double cbase = 0.0, carry = 0.0;
+  const int rounds = (nch + 63) / 64;
+  for (int r = 0; r < rounds; ++r) {
+    const int ch = lane + 64 * r;
+    double w = 0.0;
+    if (ch < nch) {
+      if constexpr (CACHED) {
+        // r < R here; select the round's register without dynamic indexing
+        double a = ca[0], ap = cap[0], bp = cbp[0];
+        float m = cm[0];
+#pragma unroll
+        for (int k = 1; k < R; ++k)
+          if (r == k) {
+            a = ca[k];
+            ap = cap[k];
+            bp = cbp[k];
+            m = cm[k];
+          }
+        w = chunk_weight(a, ap, bp, m, resid, fb, K, M, Ld);
+      } else {
+        const PartC q = pcs[ch];
+        w = chunk_weight(q.a, q.ap, q.bp, q.m, resid, fb, K, M, Ld);
+      }
+    }
+    const double incl = wave_incl_scan_d(w);
+    const double excl = carry + incl - w;
+    const bool hit = w > 0.0 && excl <= target && target < excl + w;
+    const int first = wave_min_int(hit ? ch : INT_MAX);
+    const int lp = wave_max_int(w > 0.0 ? ch : -1);
+    if (lp >= 0) clast = lp;
+    if (first != INT_MAX) {
+      cstar = first;
+      cbase = __shfl(excl, first - 64 * r, 64);
+      break;
+    }
+    carry += __shfl(incl, 63, 64);
+  }
+  const bool take_last = cstar < 0;  // rounding left the target at the end
+  if (take_last) {
+    cstar = clast >= 0 ? clast : nch - 1;
+    cbase = 0.0;
+  }
+
+  // re-read wave-chunk c*: lane l owns NE consecutive tokens
+  const int64_t V = p.V;
+  const int64_t y0 = (int64_t)cstar * CHW + (int64_t)lane * NE;
+  const bool two = resid && !fb;
+  const float ref = resid ? tm.m_t : pcs[cstar].m;
+  const double cf = resid ? 1.0 : exp2(((double)ref - (double)M) * Ld);
+  Vecs<kUC> qt, qd;
+#pragma unroll
+  for (int k = 0; k < kUC; ++k) {
+    qt.v[k] = fetch<DT, VEC>(p.target, tm.trow, V, y0 + k * P);
+    qd.v[k] = two ? fetch<DT, VEC>(p.draft, tm.drow, V, y0 + k * P) : qt.v[k];
+  }
+  // positions past the end hold the pad: a = 0 there, so their weight is 0
+  double tsum = 0.0;
+#pragma unroll
+  for (int k = 0; k < kUC; ++k) {
+    float vt[P], vd[P];
+    unpack<DT>(qt.v[k], vt);
+    unpack<DT>(qd.v[k], vd);
+#pragma unroll
+    for (int e = 0; e < P; ++e) tsum += token_weight(vt[e], vd[e], two, tm, ref, Lhi, K, cf);
+  }
+  double cum = cbase + (wave_incl_scan_d(tsum) - tsum);
+  const bool mine = !take_last && cum <= target && cum + tsum > target;
+  int cand = INT_MAX, lastpos = -1;
+#pragma unroll
+  for (int k = 0; k < kUC; ++k) {
+    float vt[P], vd[P];
+    unpack<DT>(qt.v[k], vt);
+    unpack<DT>(qd.v[k], vd);
 #pragma unroll
     for (int e = 0; e < P; ++e) {
-      const float a = exp_hp(v[e] - ref, Lhi, Llo);
-      double rv;
-      if (kind == kTermResidual && !fallback) {
-        const float bb = exp_hp(vdd[e] - Md, Lhi, Llo);
-        rv = (a > k0 * bb) ? (double)a - K * (double)bb : 0.0;
-      } else {
-        rv = (double)a * chunk_factor;
-      }
-      if (y0 + k * P + e >= V) rv = 0.0;
-      r[k * P + e] = rv;
-      tsum += rv;
-    }
-  }
-  double tot;
-  const double excl = block_exclusive_scan_d(tsum, sh.d, tot);
-  (void)tot;
-  int cand = INT_MAX;
-  int lastpos = -1;
-  {
-    double cum = cbase + excl;
-    const bool mine = !take_last && cum <= target && cum + tsum > target;
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      if (r[e] > 0.0) lastpos = (int)(y0 + e);
+      const double rv = token_weight(vt[e], vd[e], two, tm, ref, Lhi, K, cf);
+      const int y = (int)(y0 + k * P + e);
+      if (rv > 0.0) lastpos = y;
       if (mine && cand == INT_MAX) {
-        cum += r[e];
-        if (cum > target) cand = (int)(y0 + e);
+        cum += rv;
+        if (cum > target) cand = y;
       }
     }
   }
-  const int ystar0 = block_min_int(cand, sh.i);
-  const int ylast = block_max_int(lastpos, sh.i);
-  if (tid == 0) {
-    int y = ystar0 != INT_MAX ? ystar0 : ylast;
-    if (y < 0 || y >= p.V) y = (int)min<int64_t>(V - 1, (int64_t)cstar * CH);
-    p.out_tokens[t0 + j] = y;
-    if (g == 0) p.out_num[b] = 0;
-    if (p.out_resid) p.out_resid[b] = (kind == kTermResidual && !fallback) ? (float)(S / sh.a_tot) : 1.0f;
-    st_dev(p.cnt_draw + b, 0u);
+  const int ystar = wave_min_int(cand);
+  const int ylast = wave_max_int(lastpos);
+  if (lane == 0) {
+    int y = ystar != INT_MAX ? ystar : ylast;
+    if (y < 0 || y >= p.V) y = (int)min(V - 1, (int64_t)cstar * CHW);
+    p.out_tokens[tm.trow] = y;
+    if (p.out_resid) p.out_resid[b] = two ? (float)(S / at) : 1.0f;
   }
+}
+
+// A layout error leaves every Term at kTermNone: nothing to draw.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_draw(Params p) {
+  const int W = (int)gridDim.x * kWaves;
+  const int wave = (int)blockIdx.x * kWaves + (int)(threadIdx.x >> 6);
+  const int64_t N = (int64_t)p.B * p.nch_c;
+  int64_t i = (int64_t)wave * N / W;
+  const int64_t i_end = (int64_t)(wave + 1) * N / W;
+  while (i < i_end) {
+    const int b = (int)(i / p.nch_c);
+    const int c0 = (int)(i - (int64_t)b * p.nch_c);
+    const int c1 = (int)min((int64_t)p.nch_c, c0 + (i_end - i));
+    i += c1 - c0;
+    const Term tm = p.term[b];
+    if (tm.kind == kTermResidual) draw_segment<DT, VEC, true>(p, b, tm, c0, c1, tm.Lhi);
+    else if (tm.kind == kTermBonus) draw_segment<DT, VEC, false>(p, b, tm, c0, c1, tm.Lhi);
+  }
+}
+
+// one wave (workgroup of 64) per request
+template <int DT, bool VEC>
+__global__ __launch_bounds__(64) void k_select(Params p) {
+  const int b = blockIdx.x;
+  const Term tm = p.term[b];
+  if (tm.kind == kTermNone) return;
+  if (p.nch_c <= 256) draw_select<DT, VEC, true>(p, b, tm, tm.Lhi);
+  else draw_select<DT, VEC, false>(p, b, tm, tm.Lhi);
 }
 
 }  // namespace
@@ -1427,59 +1370,159 @@ int launch_prep(const Params& p, void* stream) {
   return (int)hipGetLastError();
 }
 
-template <int DT, bool VEC, int MODE>
-static void stats_launch(const Params& p, hipStream_t s) {
-  // one resident wave of persistent workgroups (occupancy queried once per process)
-  static int per_cu = 0, cus = 0;
-  if (per_cu == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-      cus = 1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stats<DT, VEC, MODE>, kThreads, 0) != hipSuccess ||
-        per_cu < 1)
-      per_cu = 1;
+namespace {
+
+int num_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const int slot = dev >= 0 && dev < 64 ? dev : 0;
+  if (cache[slot] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 1;
+    cache[slot] = n;
   }
-  const int64_t items = (int64_t)p.n_task * p.nch_a;
-  int64_t grid = (int64_t)per_cu * cus;
-  if (grid > items) grid = items;
-  if (grid < 1) grid = 1;  // workgroup 0 also publishes the offsets
-  hipLaunchKernelGGL((k_stats<DT, VEC, MODE>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+  return cache[slot];
+}
+
+template <int DT, bool VEC, int MODE, bool WZ>
+int stats_occupancy() {
+  static int occ = 0;  // same value from every thread: a race is benign
+  if (occ == 0) {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, k_stats<DT, VEC, MODE, WZ>, kThreads, 0) != hipSuccess ||
+        o <= 0)
+      o = 1;
+    occ = o;
+  }
+  return occ;
 }
 
 template <int DT, bool VEC>
-static void rowstats_dispatch(const Params& p, hipStream_t s) {
-  switch (p.mode) {
-    case SV_MODE_STOCHASTIC: stats_launch<DT, VEC, SV_MODE_STOCHASTIC>(p, s); break;
-    case SV_MODE_GREEDY: stats_launch<DT, VEC, SV_MODE_GREEDY>(p, s); break;
-    case SV_MODE_NKL: stats_launch<DT, VEC, SV_MODE_NKL>(p, s); break;
-    default: stats_launch<DT, VEC, SV_MODE_TREE_GREEDY>(p, s); break;
+int draw_occupancy() {
+  static int occ = 0;
+  if (occ == 0) {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, k_draw<DT, VEC>, kThreads, 0) != hipSuccess || o <= 0) o = 1;
+    occ = o;
+  }
+  return occ;
+}
+
+template <int DT, bool VEC>
+int stats_occupancy_mode(int mode, bool wz) {
+  switch (mode) {
+    case SV_MODE_STOCHASTIC:
+      return wz ? stats_occupancy<DT, VEC, SV_MODE_STOCHASTIC, true>()
+                : stats_occupancy<DT, VEC, SV_MODE_STOCHASTIC, false>();
+    case SV_MODE_GREEDY: return stats_occupancy<DT, VEC, SV_MODE_GREEDY, false>();
+    case SV_MODE_NKL: return stats_occupancy<DT, VEC, SV_MODE_NKL, false>();
+    default: return stats_occupancy<DT, VEC, SV_MODE_TREE_GREEDY, false>();
   }
 }
 
-int launch_rowstats(const Params& p, bool vec, void* stream) {
+template <int DT, bool VEC, int MODE, bool WZ>
+void stats_launch(const Params& p, hipStream_t s) {
+  hipLaunchKernelGGL((k_stats<DT, VEC, MODE, WZ>), dim3(p.stats_grid), dim3(kThreads), 0, s, p);
+}
+template <int DT, bool VEC>
+void stats_dispatch(const Params& p, hipStream_t s) {
+  switch (p.mode) {
+    case SV_MODE_STOCHASTIC:
+      if (p.want_kl) stats_launch<DT, VEC, SV_MODE_STOCHASTIC, true>(p, s);
+      else stats_launch<DT, VEC, SV_MODE_STOCHASTIC, false>(p, s);
+      break;
+    case SV_MODE_GREEDY: stats_launch<DT, VEC, SV_MODE_GREEDY, false>(p, s); break;
+    case SV_MODE_NKL: stats_launch<DT, VEC, SV_MODE_NKL, false>(p, s); break;
+    default: stats_launch<DT, VEC, SV_MODE_TREE_GREEDY, false>(p, s); break;
+  }
+}
+template <int DT, bool VEC>
+void decide_dispatch(const Params& p, hipStream_t s) {
+  const dim3 grid(p.B), blk(kThreads);
+  switch (p.mode) {
+    case SV_MODE_STOCHASTIC: hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_STOCHASTIC>), grid, blk, 0, s, p); break;
+    case SV_MODE_GREEDY: hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_GREEDY>), grid, blk, 0, s, p); break;
+    case SV_MODE_NKL: hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_NKL>), grid, blk, 0, s, p); break;
+    default: hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_TREE_GREEDY>), grid, blk, 0, s, p); break;
+  }
+}
+
+}  // namespace
+
+int plan_stats(Params& p, bool vec) {
+  int occ;
+  const bool wz = p.want_kl != 0;
+  if (p.dtype == SV_DTYPE_BF16)
+    occ = vec ? stats_occupancy_mode<SV_DTYPE_BF16, true>(p.mode, wz)
+              : stats_occupancy_mode<SV_DTYPE_BF16, false>(p.mode, wz);
+  else
+    occ = vec ? stats_occupancy_mode<SV_DTYPE_F32, true>(p.mode, wz)
+              : stats_occupancy_mode<SV_DTYPE_F32, false>(p.mode, wz);
+  const int64_t N = (int64_t)p.n_task * p.nch;
+  int64_t G = (int64_t)occ * num_cus();
+  if (G > N) G = N;  // every workgroup gets at least one item
+  if (G < 1) G = 1;
+  p.stats_grid = (int32_t)G;
+  // a task's chunks are spread over at most this many workgroups
+  int64_t maxseg = 1;
+  if (N > 0) {
+    const int64_t ipw = N / G;
+    maxseg = 1 + (p.nch - 1 + ipw - 1) / ipw;
+    if (maxseg > p.nch) maxseg = p.nch;
+  }
+  int glog = 0;
+  while ((1 << glog) < maxseg && glog < 6) ++glog;
+  p.grp_log2 = glog;
+  return 0;
+}
+
+int launch_stats(const Params& p, bool vec, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   if (p.dtype == SV_DTYPE_BF16) {
-    if (vec) rowstats_dispatch<SV_DTYPE_BF16, true>(p, s);
-    else rowstats_dispatch<SV_DTYPE_BF16, false>(p, s);
+    if (vec) stats_dispatch<SV_DTYPE_BF16, true>(p, s);
+    else stats_dispatch<SV_DTYPE_BF16, false>(p, s);
   } else {
-    if (vec) rowstats_dispatch<SV_DTYPE_F32, true>(p, s);
-    else rowstats_dispatch<SV_DTYPE_F32, false>(p, s);
+    if (vec) stats_dispatch<SV_DTYPE_F32, true>(p, s);
+    else stats_dispatch<SV_DTYPE_F32, false>(p, s);
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_decide(const Params& p, bool vec, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (p.dtype == SV_DTYPE_BF16) {
+    if (vec) decide_dispatch<SV_DTYPE_BF16, true>(p, s);
+    else decide_dispatch<SV_DTYPE_BF16, false>(p, s);
+  } else {
+    if (vec) decide_dispatch<SV_DTYPE_F32, true>(p, s);
+    else decide_dispatch<SV_DTYPE_F32, false>(p, s);
   }
   return (int)hipGetLastError();
 }
 
 int launch_draw(const Params& p, bool vec, void* stream) {
-  const int64_t n = (int64_t)p.B * p.nch_c;
-  if (n <= 0) return 0;
-  const dim3 grid((unsigned)n);
   hipStream_t s = (hipStream_t)stream;
+  int occ;
+  if (p.dtype == SV_DTYPE_BF16) occ = vec ? draw_occupancy<SV_DTYPE_BF16, true>() : draw_occupancy<SV_DTYPE_BF16, false>();
+  else occ = vec ? draw_occupancy<SV_DTYPE_F32, true>() : draw_occupancy<SV_DTYPE_F32, false>();
+  // every wave streams a contiguous range of (request, wave-chunk) items
+  const int64_t N = (int64_t)p.B * p.nch_c;
+  int64_t G = (int64_t)occ * num_cus();
+  if (G > (N + kWaves - 1) / kWaves) G = (N + kWaves - 1) / kWaves;
+  if (G < 1) G = 1;
+  const dim3 grid((unsigned)G), blk(kThreads);
+  const dim3 sgrid(p.B), sblk(64);
   if (p.dtype == SV_DTYPE_BF16) {
-    if (vec) hipLaunchKernelGGL((k_draw<SV_DTYPE_BF16, true>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((k_draw<SV_DTYPE_BF16, false>), grid, dim3(kThreads), 0, s, p);
+    if (vec) hipLaunchKernelGGL((k_draw<SV_DTYPE_BF16, true>), grid, blk, 0, s, p);
+    else hipLaunchKernelGGL((k_draw<SV_DTYPE_BF16, false>), grid, blk, 0, s, p);
+    if (vec) hipLaunchKernelGGL((k_select<SV_DTYPE_BF16, true>), sgrid, sblk, 0, s, p);
+    else hipLaunchKernelGGL((k_select<SV_DTYPE_BF16, false>), sgrid, sblk, 0, s, p);
   } else {
-    if (vec) hipLaunchKernelGGL((k_draw<SV_DTYPE_F32, true>), grid, dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((k_draw<SV_DTYPE_F32, false>), grid, dim3(kThreads), 0, s, p);
+    if (vec) hipLaunchKernelGGL((k_draw<SV_DTYPE_F32, true>), grid, blk, 0, s, p);
+    else hipLaunchKernelGGL((k_draw<SV_DTYPE_F32, false>), grid, blk, 0, s, p);
+    if (vec) hipLaunchKernelGGL((k_select<SV_DTYPE_F32, true>), sgrid, sblk, 0, s, p);
+    else hipLaunchKernelGGL((k_select<SV_DTYPE_F32, false>), sgrid, sblk, 0, s, p);
   }
   return (int)hipGetLastError();
 }

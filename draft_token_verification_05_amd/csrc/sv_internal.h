@@ -11,49 +11,52 @@ namespace sv {
 
 constexpr int kThreads = 256;    // threads per workgroup (4 wave64s)
 constexpr int kPrepThreads = 1024;
-constexpr int kUA = 2;           // 16-byte vectors per thread per row per chunk, row-statistics pass
-constexpr int kUC = 2;           // 16-byte vectors per thread per row, draw pass
-constexpr int kLdsBatch = 4096;  // batches up to this size scan their offsets in LDS (no prep kernel)
+// 16-byte vectors per thread per row per chunk in the row-statistics pass:
+// modes that stream one row per task use larger chunks (same bytes per chunk)
+constexpr int stats_vectors_per_thread(int mode) {
+  return (mode == SV_MODE_GREEDY || mode == SV_MODE_TREE_GREEDY) ? 4 : 2;
+}
+constexpr int kUA = 2;           // smallest of the above: sizes the partial arrays
+constexpr int kUC = 2;           // 16-byte vectors per lane per row in a wave-chunk of the draw pass
+constexpr int kLdsBatch = 1024;  // batches up to this size scan their offsets in LDS (no prep kernel)
 
 constexpr int elems_per_vec(int dtype) { return dtype == SV_DTYPE_BF16 ? 8 : 4; }
 constexpr int elem_size(int dtype) { return dtype == SV_DTYPE_BF16 ? 2 : 4; }
-// vocabulary elements covered by one workgroup of each pass
+// vocabulary elements covered by one chunk of each pass
 constexpr int64_t chunk_a(int dtype) { return (int64_t)kThreads * kUA * elems_per_vec(dtype); }
-constexpr int64_t chunk_c(int dtype) { return (int64_t)kThreads * kUC * elems_per_vec(dtype); }
+constexpr int64_t chunk_stats(int dtype, int mode) {
+  return (int64_t)kThreads * stats_vectors_per_thread(mode) * elems_per_vec(dtype);
+}
+constexpr int64_t chunk_c(int dtype) { return (int64_t)64 * kUC * elems_per_vec(dtype); }
 
 enum TermKind : int32_t { kTermNone = 0, kTermResidual = 1, kTermBonus = 2 };
 
-// Partial statistics of one (task, vocabulary chunk).  m_* are raw-logit maxima,
-// s_* = sum exp((x - m)/T) over the chunk, w = sum exp((d - m_d)/T) * (d - t),
-// idx = lowest index attaining m_t.
+// Partial statistics of one task over the vocabulary chunks one workgroup of
+// the statistics pass streamed.  m_* are raw-logit maxima, s_* = sum
+// 2^((x - m) L) with L = log2(e)/T, w = sum 2^((d - m_d) L) (d - t) and
+// z = sum 2^((d - m_d) L) |d - t| over the draft row, idx = lowest index
+// attaining m_t.
 struct PartA {
-  double s_t, s_d, w;
+  double s_t, s_d, w, z;
   float m_t, m_d;
   int32_t idx;
   int32_t pad;
 };
 
-// Merged statistics of one task (a whole row, or a target/draft row pair);
-// kl = KL(q || p) in nats for pair tasks whose KL is requested.
-struct TaskStat {
-  double s_t, s_d, w;
-  float m_t, m_d, kl;
-  int32_t idx;
-};
-
-// Terminal record of a request, written by the decision step for the draw pass.
+// Terminal record of a stochastic request, written by the decision kernel for
+// the draw pass.
 struct Term {
   int32_t kind;  // TermKind
   int32_t j;     // slot of the terminal token (= number of accepted drafts)
   int32_t trow;  // target row of the terminal distribution
   int32_t drow;  // draft row (residual only)
-  float m_t;     // exact maximum of the target row (residual only)
-  float m_d;     // exact maximum of the draft row (residual only)
+  float m_t;     // maximum of the target row (residual only)
+  float m_d;     // maximum of the draft row (residual only)
   float k0;      // s_t / s_d from the statistics pass (residual only)
-  int32_t pad;
+  float Lhi;     // fl32(log2(e) / T) of the request
 };
 
-// Partial sums of the draw pass for one (request, chunk), in float64.
+// Partial sums of the draw pass for one (request, wave-chunk), in float64.
 struct PartC {
   double a, b, ap, bp;  // sum a, sum b, and the same over {y : a_y > k0 * b_y}
   float m;              // chunk maximum (bonus draws)
@@ -61,8 +64,7 @@ struct PartC {
 };
 
 struct Layout {
-  size_t off_hdr, off_toff, off_doff, off_pair2req, off_row2req, off_part_a, off_stat, off_gat, off_cnt_task,
-      off_cnt_req, off_term, off_part_c, off_cnt_draw, total;
+  size_t off_hdr, off_doff, off_pair2req, off_row2req, off_part_a, off_term, off_part_c, total;
   int64_t n_task_max;
   int64_t nch_a, nch_c;
 };
@@ -81,18 +83,12 @@ inline Layout make_layout(int64_t B, int64_t V, int dtype, int64_t R_d) {
     return at;
   };
   L.off_hdr = take(256);
-  L.off_toff = take(sizeof(int32_t) * (B + 1));
   L.off_doff = take(sizeof(int32_t) * (B + 1));
   L.off_pair2req = take(sizeof(int32_t) * (R_d > 0 ? R_d : 1));
   L.off_row2req = take(sizeof(int32_t) * (R_d + B));
   L.off_part_a = take(sizeof(PartA) * L.n_task_max * L.nch_a);
-  L.off_stat = take(sizeof(TaskStat) * L.n_task_max);
-  L.off_gat = take(sizeof(float) * 2 * (R_d > 0 ? R_d : 1));
-  L.off_cnt_task = take(sizeof(uint32_t) * L.n_task_max);
-  L.off_cnt_req = take(sizeof(uint32_t) * B);
   L.off_term = take(sizeof(Term) * B);
   L.off_part_c = take(sizeof(PartC) * B * L.nch_c);
-  L.off_cnt_draw = take(sizeof(uint32_t) * B);
   L.total = o;
   return L;
 }
@@ -115,30 +111,30 @@ struct Params {
   float* out_resid;
   int32_t* out_tree_node;
   int32_t B, V, max_gamma, mode, dtype;
-  int32_t R_d;     // total draft rows
-  int32_t n_task;  // tasks of the row-statistics pass
-  int32_t nch_a, nch_c;
+  int32_t R_d;         // total draft rows
+  int32_t n_task;      // tasks of the row-statistics pass
+  int32_t nch;         // vocabulary chunks per task in the row-statistics pass
+  int32_t stats_grid;  // workgroups of the row-statistics pass
+  int32_t grp_log2;    // log2 of the lanes that merge one task's partials
+  int32_t nch_c;       // vocabulary chunks per request in the draw pass
   float delta;
-  int32_t want_w;  // compute the KL cross term (NKL mode, or stochastic with out_nkl)
+  int32_t want_kl;  // compute KL(q || p) (NKL mode, or stochastic with out_nkl)
   // workspace
   int32_t* hdr;  // hdr[0]: layout error flag
-  int32_t* t_off;
   int32_t* d_off;
   int32_t* pair2req;
   int32_t* row2req;
   PartA* part_a;
-  TaskStat* stat;
-  float* gat;  // [2 * R_d]: target and draft logit at the drafted token
-  uint32_t* cnt_task;
-  uint32_t* cnt_req;
   Term* term;
   PartC* part_c;
-  uint32_t* cnt_draw;
 };
 
 // kernel launchers (kernels.hip); return the hipError_t of the launch as int
 int launch_prep(const Params& p, void* stream);
-int launch_rowstats(const Params& p, bool vec, void* stream);
+// picks the grid of the statistics pass: fills p.stats_grid and p.grp_log2
+int plan_stats(Params& p, bool vec);
+int launch_stats(const Params& p, bool vec, void* stream);
+int launch_decide(const Params& p, bool vec, void* stream);
 int launch_draw(const Params& p, bool vec, void* stream);
 
 }  // namespace sv
