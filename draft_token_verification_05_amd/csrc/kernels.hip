@@ -81,6 +81,44 @@ __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 
 // pad pattern.  Addresses are clamped into the row and the pad is selected
 // after the load, so every lane issues its loads unconditionally.
 // VEC: rows are a whole number of 16-byte vectors and 16-byte aligned.
+// Raw 16 bytes at clamped addresses: positions >= V hold copies of elements
+// of the row, which the caller masks by position (mask_tail) where the data is
+// consumed, so that no wait is placed right behind the load.
+template <int DT, bool VEC>
+__device__ __forceinline__ uint4 fetch_raw(const void* base, int64_t row, int64_t V, int64_t e0) {
+  if (VEC) {
+    const int64_t ec = e0 < V ? e0 : V - Elem<DT>::P;
+    return *reinterpret_cast<const uint4*>(static_cast<const char*>(base) +
+                                           (row * V + ec) * (DT == SV_DTYPE_BF16 ? 2 : 4));
+  }
+  uint32_t w[4];
+  if (DT == SV_DTYPE_BF16) {
+    const uint16_t* r = static_cast<const uint16_t*>(base) + row * V;
+    uint32_t h[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) h[e] = r[e0 + e < V ? e0 + e : V - 1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = h[2 * e] | (h[2 * e + 1] << 16);
+  } else {
+    const uint32_t* r = static_cast<const uint32_t*>(base) + row * V;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = r[e0 + e < V ? e0 + e : V - 1];
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Sets the unpacked elements of vector positions >= V to the pad value.
+// v[k * P + e] is the element at e0(k) + e, e0(k) = base + k * stride.
+template <int DT, int NV>
+__device__ __forceinline__ void mask_tail(float* v, int64_t base, int64_t stride, int64_t V) {
+  constexpr int P = Elem<DT>::P;
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+#pragma unroll
+    for (int e = 0; e < P; ++e)
+      if (base + k * stride + e >= V) v[k * P + e] = Elem<DT>::kPad;
+}
+
 template <int DT, bool VEC>
 __device__ __forceinline__ uint4 fetch(const void* base, int64_t row, int64_t V, int64_t e0) {
   constexpr int P = Elem<DT>::P;
@@ -274,7 +312,10 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Params p) {
   }
   if (tid == 0) p.d_off[p.B] = (int)carry;
   const bool bad = sh_bad != 0 || carry != (long long)p.R_d;
-  if (tid == 0) p.hdr[0] = bad ? 1 : 0;
+  if (tid == 0) {
+    p.hdr[0] = bad ? 1 : 0;
+    p.hdr[1] = 0;  // queue of the KL second pass
+  }
   if (bad) return;
   __syncthreads();  // offsets written by other threads of this workgroup
   for (int b = tid; b < p.B; b += kPrepThreads) {
@@ -291,8 +332,14 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Params p) {
 // ----------------------------------------------------------------------------
 
 // Items (task, chunk) are numbered task * nch + chunk; workgroup w of G
-// streams items [w N / G, (w + 1) N / G).  The workgroup that streams item i:
-__device__ __forceinline__ int wg_of(int64_t item, int64_t N, int G) { return (int)(((item + 1) * G - 1) / N); }
+// streams items [w N / G, (w + 1) N / G).  The workgroup that streams item i
+// is floor(((i + 1) G - 1) / N).  The float64 quotient floors exactly here:
+// the numerator is an integer below 2^53, and the quotient is below 2^13, so
+// its rounding error (< 2^-39) is far below the distance 1/N >= 2^-31 of any
+// non-integer quotient to the next integer.
+__device__ __forceinline__ int wg_of(int64_t item, int64_t N, int G) {
+  return (int)floor((double)((item + 1) * G - 1) / (double)N);
+}
 
 struct StatsShared {
   int off[kLdsBatch + 1];  // packed draft-row offsets (small batches)
@@ -312,17 +359,26 @@ __device__ bool scan_offsets_lds(const Params& p, StatsShared& sh, bool soft, bo
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   long long g[4], loc = 0;
   bool bad = false;
+  // all loads first (clamped indices, no branches), so they are in flight together
+  int gl[4];
+  float tl[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int bc = min(4 * tid + k, p.B - 1);
+    gl[k] = p.gamma[bc];
+    tl[k] = soft ? p.temp[bc] : 0.0f;
+  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int b = 4 * tid + k;
     long long v = 0;
     if (b < p.B) {
-      v = p.gamma[b];
+      v = gl[k];
       if (v < 0) {
         bad = true;
         v = 0;
       }
-      if (soft) sh.temp[b] = p.temp[b];
+      if (soft) sh.temp[b] = tl[k];
     }
     g[k] = v;
     loc += v;
@@ -358,7 +414,10 @@ __device__ bool scan_offsets_lds(const Params& p, StatsShared& sh, bool soft, bo
   const bool ok = sh.bad == 0;
   if (publish) {
     for (int b = tid; b <= p.B; b += kThreads) p.d_off[b] = sh.off[b];
-    if (tid == 0) p.hdr[0] = ok ? 0 : 1;
+    if (tid == 0) {
+      p.hdr[0] = ok ? 0 : 1;
+      p.hdr[1] = 0;  // queue of the KL second pass
+    }
   }
   return ok;
 }
@@ -396,16 +455,26 @@ struct Vecs {
   uint4 v[NV];
 };
 
+// Rows and vocabulary chunk of one item of the statistics pass.  The second
+// row of a pair is read from `dbase` (the draft logits; for the bonus row of an
+// NKL request the target row itself, whose pair statistics are not used).
+struct Desc {
+  int task, chunk;
+  int64_t trow, drow;
+  const void* dbase;
+  float Lhi;
+};
+
 // Loads of one chunk: thread t takes 16-byte vectors k * kThreads + t.
 template <int DT, bool VEC, int NV, bool PAIR>
-__device__ __forceinline__ void issue_chunk(const Params& p, int64_t trow, int64_t drow, int64_t e_chunk, Vecs<NV>& qt,
-                                            Vecs<NV>& qd) {
+__device__ __forceinline__ void issue_chunk(const Params& p, const Desc& d, Vecs<NV>& qt, Vecs<NV>& qd) {
   constexpr int P = Elem<DT>::P;
+  const int64_t e_chunk = (int64_t)d.chunk * kThreads * NV * P;
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const int64_t e0 = e_chunk + ((int64_t)k * kThreads + threadIdx.x) * P;
-    qt.v[k] = fetch<DT, VEC>(p.target, trow, p.V, e0);
-    if (PAIR) qd.v[k] = fetch<DT, VEC>(p.draft, drow, p.V, e0);
+    qt.v[k] = fetch_raw<DT, VEC>(p.target, d.trow, p.V, e0);
+    if (PAIR) qd.v[k] = fetch_raw<DT, VEC>(d.dbase, d.drow, p.V, e0);
   }
 }
 
@@ -414,14 +483,19 @@ __device__ __forceinline__ void issue_chunk(const Params& p, int64_t trow, int64
 // draft row is streamed beside the target row.  Target and draft sums use the
 // same accumulation pattern, so identical rows give bit-identical statistics.
 template <int DT, int NV, bool SOFT, bool IDX, bool WZ, bool PAIR>
-__device__ __forceinline__ void fold_chunk(Lane& L, const Vecs<NV>& qt, const Vecs<NV>& qd, int64_t e_chunk,
-                                           float Lhi) {
+__device__ __forceinline__ void fold_chunk(Lane& L, const Vecs<NV>& qt, const Vecs<NV>& qd, const Desc& d,
+                                           int64_t V) {
   constexpr int P = Elem<DT>::P;
   constexpr int NE = NV * P;
+  const int64_t e_chunk = (int64_t)d.chunk * kThreads * NE;
+  const float Lhi = d.Lhi;
   constexpr float pad = Elem<DT>::kPad;
+  const int64_t lane_base = e_chunk + (int64_t)threadIdx.x * P;
+  const bool tail = e_chunk + (int64_t)kThreads * NE > V;  // uniform: the chunk runs past the row end
   float vt[NE];
 #pragma unroll
   for (int k = 0; k < NV; ++k) unpack<DT>(qt.v[k], vt + k * P);
+  if (tail) mask_tail<DT, NV>(vt, lane_base, (int64_t)kThreads * P, V);
   float mc = vt[0];
 #pragma unroll
   for (int e = 1; e < NE; ++e) mc = fmaxf(mc, vt[e]);
@@ -454,6 +528,7 @@ __device__ __forceinline__ void fold_chunk(Lane& L, const Vecs<NV>& qt, const Ve
     float vd[NE];
 #pragma unroll
     for (int k = 0; k < NV; ++k) unpack<DT>(qd.v[k], vd + k * P);
+    if (tail) mask_tail<DT, NV>(vd, lane_base, (int64_t)kThreads * P, V);
     float md = vd[0];
 #pragma unroll
     for (int e = 1; e < NE; ++e) md = fmaxf(md, vd[e]);
@@ -559,71 +634,115 @@ __device__ __forceinline__ void reduce_store(const Lane& L, float Lhi, PartA* ds
   // after it, by which time thread 0 has read them: no barrier needed here
 }
 
-// Streams chunks [c0, c1) of one task: the loads of chunk c + 1 are in flight
-// while chunk c is folded.
-template <int DT, bool VEC, int NV, bool SOFT, bool IDX, bool WZ, bool PAIR>
-__device__ __forceinline__ void stream_segment(const Params& p, int64_t trow, int64_t drow, int c0, int c1, float Lhi,
-                                               PartA* dst, StatsShared& sh) {
-  constexpr int64_t CH = (int64_t)kThreads * NV * Elem<DT>::P;
-  Lane L;
+__device__ __forceinline__ void lane_reset(Lane& L) {
   L.mt = L.md = -INFINITY;
   L.idx = INT_MAX;
   L.st = L.sd = L.w = L.z = 0.0;
-  Vecs<NV> ct, cd;
-  issue_chunk<DT, VEC, NV, PAIR>(p, trow, drow, (int64_t)c0 * CH, ct, cd);
-  for (int c = c0; c < c1 - 1; ++c) {
-    Vecs<NV> nt, nd;
-    issue_chunk<DT, VEC, NV, PAIR>(p, trow, drow, (int64_t)(c + 1) * CH, nt, nd);
-    fold_chunk<DT, NV, SOFT, IDX, WZ, PAIR>(L, ct, cd, (int64_t)c * CH, Lhi);
-    ct = nt;
-    cd = nd;
-  }
-  fold_chunk<DT, NV, SOFT, IDX, WZ, PAIR>(L, ct, cd, (int64_t)(c1 - 1) * CH, Lhi);
-  reduce_store<SOFT, IDX, WZ, PAIR>(L, Lhi, dst, sh);
 }
 
-// WZ (stochastic only): also the KL cross terms, for the optional NKL output
-template <int DT, bool VEC, int MODE, bool WZ>
+// Rows of task d.task (request lookup for the modes whose tasks pair rows).
+template <int MODE, bool LDS>
+__device__ __forceinline__ void set_rows(const Params& p, const StatsShared& sh, int& b, Desc& d) {
+  if (MODE == SV_MODE_GREEDY || MODE == SV_MODE_TREE_GREEDY) {
+    d.trow = d.task;
+    d.drow = 0;
+    d.dbase = p.target;
+    d.Lhi = 0.0f;
+    return;
+  }
+  float T;
+  if constexpr (LDS) {
+    b = find_req<MODE>(sh.off, p.B, d.task, b);
+    T = sh.temp[b];
+  } else {
+    b = MODE == SV_MODE_STOCHASTIC ? p.pair2req[d.task] : p.row2req[d.task];
+    T = p.temp[b];
+  }
+  d.Lhi = (float)(kLog2eD / (double)T);
+  if (MODE == SV_MODE_STOCHASTIC) {
+    d.trow = (int64_t)d.task + b;
+    d.drow = d.task;
+    d.dbase = p.draft;
+  } else {
+    int d0, d1;
+    if constexpr (LDS) {
+      d0 = sh.off[b];
+      d1 = sh.off[b + 1];
+    } else {
+      d0 = p.d_off[b];
+      d1 = p.d_off[b + 1];
+    }
+    const bool pair = d.task - (d0 + b) < d1 - d0;
+    d.trow = d.task;
+    d.drow = pair ? (int64_t)d.task - b : d.task;
+    d.dbase = pair ? p.draft : p.target;
+  }
+}
+
+template <int MODE, bool LDS>
+__device__ __forceinline__ void next_desc(const Params& p, const StatsShared& sh, int& b, Desc& d) {
+  if (++d.chunk == p.nch) {
+    d.chunk = 0;
+    ++d.task;
+    set_rows<MODE, LDS>(p, sh, b, d);
+  }
+}
+
+// WZ (stochastic only): also the KL cross terms, for the optional NKL output.
+// Each workgroup streams its item range with two register buffers in turn:
+// the loads of item i + 1 (also across a task boundary) are in flight while
+// item i is folded; a task segment ends with a workgroup reduction whose
+// barriers wait on LDS only, so the next loads stay in flight through it.
+// LDS: the batch is small enough for the offsets to be scanned in LDS.
+template <int DT, bool VEC, int MODE, bool WZ, bool LDS>
 __global__ __launch_bounds__(kThreads) void k_stats(Params p) {
   constexpr bool SOFT = MODE == SV_MODE_STOCHASTIC || MODE == SV_MODE_NKL;
+  constexpr int NV = SOFT ? 2 : 4;
+  constexpr bool IDX = MODE != SV_MODE_STOCHASTIC;
+  constexpr bool WZM = MODE == SV_MODE_NKL || WZ;
   __shared__ StatsShared sh;
   const int G = (int)gridDim.x, wg = (int)blockIdx.x;
   const int64_t N = (int64_t)p.n_task * p.nch;
-  const bool lds = p.B <= kLdsBatch;
-  if (lds) {
+  if (LDS) {
     // greedy and tree tasks are target rows: only workgroup 0 needs the scan,
     // to publish the offsets for the decision kernel
     if ((SOFT || wg == 0) && !scan_offsets_lds(p, sh, SOFT, wg == 0)) return;
   } else if (SOFT && p.hdr[0] != 0) {
     return;  // the prep kernel found a layout error
   }
-  int64_t i = (int64_t)wg * N / G;
   const int64_t i_end = (int64_t)(wg + 1) * N / G;
+  int64_t i = (int64_t)wg * N / G;
+  if (i >= i_end) return;
   int b = -1;
-  while (i < i_end) {
-    const int task = (int)(i / p.nch);
-    const int c0 = (int)(i - (int64_t)task * p.nch);
-    const int c1 = (int)min((int64_t)p.nch, c0 + (i_end - i));
-    PartA* dst = p.part_a + (int64_t)task * p.nch + (wg - wg_of((int64_t)task * p.nch, N, G));
-    if (!SOFT) {
-      stream_segment<DT, VEC, 4, false, true, false, false>(p, task, 0, c0, c1, 0.f, dst, sh);
-    } else {
-      if (lds) b = find_req<MODE>(sh.off, p.B, task, b);
-      else b = MODE == SV_MODE_STOCHASTIC ? p.pair2req[task] : p.row2req[task];
-      const float T = lds ? sh.temp[b] : p.temp[b];
-      const float Lhi = (float)(kLog2eD / (double)T);
-      if (MODE == SV_MODE_STOCHASTIC) {
-        stream_segment<DT, VEC, 2, true, false, WZ, true>(p, (int64_t)task + b, task, c0, c1, Lhi, dst, sh);
-      } else {
-        const int d0 = lds ? sh.off[b] : p.d_off[b];
-        const int g = (lds ? sh.off[b + 1] : p.d_off[b + 1]) - d0;
-        if (task - (d0 + b) < g)
-          stream_segment<DT, VEC, 2, true, true, true, true>(p, task, (int64_t)task - b, c0, c1, Lhi, dst, sh);
-        else  // the bonus row: argmax only
-          stream_segment<DT, VEC, 2, false, true, false, false>(p, task, 0, c0, c1, Lhi, dst, sh);
-      }
+  Desc dA, dB;
+  dA.task = (int)(i / p.nch);
+  dA.chunk = (int)(i - (int64_t)dA.task * p.nch);
+  set_rows<MODE, LDS>(p, sh, b, dA);
+  Vecs<NV> At, Ad, Bt, Bd;
+  issue_chunk<DT, VEC, NV, SOFT>(p, dA, At, Ad);
+  Lane L;
+  lane_reset(L);
+  for (;;) {
+    dB = dA;
+    if (i + 1 < i_end) next_desc<MODE, LDS>(p, sh, b, dB);
+    issue_chunk<DT, VEC, NV, SOFT>(p, dB, Bt, Bd);  // the last item reloads itself (cache hit)
+    fold_chunk<DT, NV, SOFT, IDX, WZM, SOFT>(L, At, Ad, dA, p.V);
+    if (dA.chunk == p.nch - 1 || i + 1 == i_end) {
+      reduce_store<SOFT, IDX, WZM, SOFT>(L, dA.Lhi, p.part_a + (int64_t)dA.task * p.nch +
+                                                        (wg - wg_of((int64_t)dA.task * p.nch, N, G)), sh);
+      lane_reset(L);
     }
-    i += c1 - c0;
+    if (++i >= i_end) break;
+    dA = dB;
+    if (i + 1 < i_end) next_desc<MODE, LDS>(p, sh, b, dA);
+    issue_chunk<DT, VEC, NV, SOFT>(p, dA, At, Ad);
+    fold_chunk<DT, NV, SOFT, IDX, WZM, SOFT>(L, Bt, Bd, dB, p.V);
+    if (dB.chunk == p.nch - 1 || i + 1 == i_end) {
+      reduce_store<SOFT, IDX, WZM, SOFT>(L, dB.Lhi, p.part_a + (int64_t)dB.task * p.nch +
+                                                        (wg - wg_of((int64_t)dB.task * p.nch, N, G)), sh);
+      lane_reset(L);
+    }
+    if (++i >= i_end) break;
   }
 }
 
@@ -728,49 +847,47 @@ __device__ __forceinline__ float g_small(float w) {
 }
 
 // KL(q || p) of one row pair in a second pass, as the sum of the non-negative
-// terms q_y g(w_y), w_y = log(p_y / q_y).  Because sum q e^w = sum p = 1, this
-// equals sum q log(q/p) exactly, has no cancellation, and an error eps in the
-// log normaliser ratio only adds O(eps^2).  All threads of the workgroup call.
+// terms q_y g(w_y), w_y = log(p_y / q_y), over one chunk of kThreads x kUR
+// vectors.  Because sum q e^w = sum p = 1, the sum over the row equals
+// sum q log(q/p) exactly, has no cancellation, and an error eps in the log
+// normaliser ratio only adds O(eps^2).  All threads of the workgroup call.
 template <int DT, bool VEC>
-__device__ double kl_second_pass(const Params& p, int64_t trow, int64_t drow, float m_t, float m_d, double s_t,
-                                 double s_d, float Lhi, double* shd) {
+__device__ double kl_chunk(const Params& p, const RefIn& ri, int64_t drow, int64_t e_chunk, double* shd) {
   constexpr int P = Elem<DT>::P;
-  constexpr int U = 4;
   const int64_t V = p.V;
+  const float Lhi = ri.Lhi;
   const float c = (float)((double)Lhi * kLn2D);  // d(log p)/d(logit)
-  const float lr = (float)log(s_d / s_t);
-  const float inv_sd = (float)(1.0 / s_d), inv_st = (float)(1.0 / s_t);
+  const float lr = (float)log(ri.s_d / ri.s_t);
+  const float inv_sd = (float)(1.0 / ri.s_d), inv_st = (float)(1.0 / ri.s_t);
+  uint4 qt[kUR], qd[kUR];
+#pragma unroll
+  for (int k = 0; k < kUR; ++k) {
+    const int64_t e0 = e_chunk + ((int64_t)k * kThreads + threadIdx.x) * P;
+    qt[k] = fetch<DT, VEC>(p.target, ri.trow, V, e0);
+    qd[k] = fetch<DT, VEC>(p.draft, drow, V, e0);
+  }
   double acc = 0.0;
-  for (int64_t base = 0; base < V; base += (int64_t)kThreads * P * U) {
-    uint4 qt[U], qd[U];
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const int64_t e0 = base + ((int64_t)k * kThreads + threadIdx.x) * P;
-      qt[k] = fetch<DT, VEC>(p.target, trow, V, e0);
-      qd[k] = fetch<DT, VEC>(p.draft, drow, V, e0);
-    }
+  for (int k = 0; k < kUR; ++k) {
+    float vt[P], vd[P];
+    unpack<DT>(qt[k], vt);
+    unpack<DT>(qd[k], vd);
+    float part = 0.f;  // P non-negative terms in float32, then float64
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-      float vt[P], vd[P];
-      unpack<DT>(qt[k], vt);
-      unpack<DT>(qd[k], vd);
-      float part = 0.f;  // P non-negative terms in float32, then float64
-#pragma unroll
-      for (int e = 0; e < P; ++e) {
-        const float dt = vt[e] - m_t, dd = vd[e] - m_d;
-        const float q = ex2(dd, Lhi) * inv_sd;
-        const float w = fmaf(dt - dd, c, lr);
-        float term;
-        if (fabsf(w) < 0.5f) {
-          term = q * g_small(w);
-        } else {
-          // q g(w) = p - q - q w; also right where q underflows but p does not
-          term = (ex2(dt, Lhi) * inv_st - q) - q * w;
-        }
-        part += term;  // positions past the end of the row give p = q = 0
+    for (int e = 0; e < P; ++e) {
+      const float dt = vt[e] - ri.m_t, dd = vd[e] - ri.m_d;
+      const float q = ex2(dd, Lhi) * inv_sd;
+      const float w = fmaf(dt - dd, c, lr);
+      float term;
+      if (fabsf(w) < 0.5f) {
+        term = q * g_small(w);
+      } else {
+        // q g(w) = p - q - q w; also right where q underflows but p does not
+        term = (ex2(dt, Lhi) * inv_st - q) - q * w;
       }
-      acc += (double)part;
+      part += term;  // positions past the end of the row give p = q = 0
     }
+    acc += (double)part;
   }
   return block_sum_d(acc, shd);
 }
@@ -780,10 +897,8 @@ struct DecideShared {
   double st[kThreads], sd[kThreads];
   int idx[kThreads];
   int acc[kThreads];
-  float kl[kThreads];
+  double kl1[kThreads];
   int need[kThreads];
-  int list[kThreads];
-  int nlist;
   int red_i[kWaves];
   double red_d[kWaves];
 };
@@ -860,6 +975,8 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
   __shared__ DecideShared sh;
   __shared__ TreeShared<MODE> tr;
   const int b = blockIdx.x, tid = threadIdx.x;
+  const bool want_kl = SOFT && p.want_kl;
+  if (want_kl && tid == 0) p.pending[b] = 0;
   // independent loads first, so that they are in flight together
   const int hdr = p.hdr[0];
   const int d0 = p.d_off[b];
@@ -889,28 +1006,39 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
   const int ntask = MODE == SV_MODE_STOCHASTIC ? g : g + 1;
   const int64_t tbase = MODE == SV_MODE_STOCHASTIC ? d0 : t0;
   const bool diag = SOFT && (p.out_p_x || p.out_q_x || p.out_nkl);
-  const bool want_kl = SOFT && p.want_kl;
   const double c = (double)Lhi * kLn2D;  // d(log p)/d(logit)
   const double lnV = log((double)p.V);
   int j = -1;
   float jm_t = 0.f, jm_d = 0.f;
   double js_t = 1.0, js_d = 1.0;
   int jidx = 0;
+  bool any_need = false, bad = false;
+  int checked = 0;  // positions [0, checked) were checked inside the passes
   for (int base = 0; base < ntask; base += TPP) {
     const int q = tid >> glog, l = tid & (S - 1);
     const int ti = base + q;
     const bool has = ti < ntask;
     const bool pair = SOFT && ti < g;
     // the group leader's position data, issued before the partial loads
+    // and the per-position input checks (node ti of a tree is position ti - 1)
     int x = -1;
     float tx = 0.f, dx = 0.f, u = 0.f;
-    if (MODE != SV_MODE_TREE_GREEDY && l == 0 && ti < g) {
+    if (l == 0 && MODE != SV_MODE_TREE_GREEDY && ti < g) {
       x = p.tokens[d0 + ti];
-      if (SOFT && x >= 0 && x < p.V) {
+      const bool xok = x >= 0 && x < p.V;
+      if (SOFT && xok) {
         tx = load_scalar<DT>(p.target, t0 + ti, V, x);
         dx = load_scalar<DT>(p.draft, d0 + ti, V, x);
       }
-      if (MODE == SV_MODE_STOCHASTIC) u = p.ua[d0 + ti];
+      if (MODE == SV_MODE_STOCHASTIC) {
+        u = p.ua[d0 + ti];
+        if (!unit_ok(u)) bad = true;
+      }
+      if (!xok) bad = true;
+    }
+    if (l == 0 && MODE == SV_MODE_TREE_GREEDY && ti >= 1 && ti <= g) {
+      const int xn = p.tokens[d0 + ti - 1], pa = p.parents[d0 + ti - 1];
+      if (xn < 0 || xn >= p.V || pa < 0 || pa >= ti) bad = true;
     }
     const Merged r = merge_task<SOFT>(p, tbase + ti, has, pair, l, glog, Lhi);
     if (l == 0 && has) {
@@ -921,15 +1049,17 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
       sh.st[q] = r.st;
       sh.sd[q] = r.sd;
       sh.idx[q] = idx;
+      if (MODE == SV_MODE_NKL) p.tidx[t0 + ti] = idx;
       int acc = 0, need = 0;
-      float kl = 0.f;
+      double kl = 0.0;  // KL(q||p) = 0 for V == 1: both rows are the same point mass
       if (pair) {
-        // log p(x) and log q(x) from the merged statistics
-        const double lpx = (double)(tx - r.mt) * c - log(r.st);
-        const double lqx = (double)(dx - r.md) * c - log(r.sd);
-        if (p.out_p_x) p.out_p_x[d0 + ti] = (float)exp(lpx);
-        if (p.out_q_x) p.out_q_x[d0 + ti] = (float)exp(lqx);
-        if (MODE == SV_MODE_STOCHASTIC) acc = (double)u <= fmin(1.0, exp(lpx - lqx)) ? 1 : 0;
+        // log2 p(x) and log2 q(x) from the merged statistics (float32: the
+        // relative error of p(x), q(x) and alpha stays near 1e-7)
+        const float lpx = (tx - r.mt) * Lhi - __log2f((float)r.st);
+        const float lqx = (dx - r.md) * Lhi - __log2f((float)r.sd);
+        if (p.out_p_x) p.out_p_x[d0 + ti] = exp2f(lpx);
+        if (p.out_q_x) p.out_q_x[d0 + ti] = exp2f(lqx);
+        if (MODE == SV_MODE_STOCHASTIC) acc = u <= fminf(1.0f, exp2f(lpx - lqx)) ? 1 : 0;
         if (want_kl && p.V > 1) {
           // KL(q||p) = E_q[d - t]/T - (m_d - m_t)/T - log(s_d / s_t)
           const double lg = log(r.sd / r.st);
@@ -937,35 +1067,42 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
           const double err = kKlErr * (r.z / r.sd * c + 1.0);
           need = (err > kKlRel * klv) ? 1 : 0;
           if (MODE == SV_MODE_NKL && fabs(klv - (double)p.delta * lnV) <= err) need = 1;
-          kl = (float)klv;
+          kl = klv;
         }
       } else if (MODE == SV_MODE_GREEDY) {
         acc = (ti < g && x == idx) ? 1 : 0;
       }
       sh.acc[q] = acc;
-      sh.kl[q] = kl;
+      sh.kl1[q] = kl;
       sh.need[q] = need;
     }
-    if (tid == 0) sh.nlist = 0;
     __syncthreads();
-    if (want_kl) {
-      if (tid < TPP && base + tid < g && sh.need[tid]) sh.list[atomicAdd(&sh.nlist, 1)] = tid;
-      __syncthreads();
-      const int nl = sh.nlist;
-      for (int k = 0; k < nl; ++k) {
-        const int s = sh.list[k], i = base + s;
-        const double kl2 = kl_second_pass<DT, VEC>(p, t0 + i, d0 + i, sh.mt[s], sh.md[s], sh.st[s], sh.sd[s], Lhi,
-                                                    sh.red_d);
-        if (tid == 0) sh.kl[s] = (float)kl2;
-        __syncthreads();
-      }
-      if (tid < TPP && base + tid < g) {
-        const double nkl = p.V > 1 ? (double)sh.kl[tid] / lnV : 0.0;
-        if (p.out_nkl) p.out_nkl[d0 + base + tid] = (float)nkl;
+    if (want_kl && tid < TPP && base + tid < g) {
+      // positions whose one-pass KL is not accurate enough are queued for the
+      // grid-wide second pass; the request then waits for k_finish
+      const int pos = d0 + base + tid;
+      const int need = sh.need[tid];
+      p.kl_need[pos] = need;
+      p.kl_val[pos] = sh.kl1[tid];
+      if (need) {
+        RefIn ri;
+        ri.s_t = sh.st[tid];
+        ri.s_d = sh.sd[tid];
+        ri.m_t = sh.mt[tid];
+        ri.m_d = sh.md[tid];
+        ri.Lhi = Lhi;
+        ri.trow = t0 + base + tid;
+        p.ref_in[pos] = ri;
+        p.ref_list[atomicAdd(p.hdr + 1, 1)] = pos;
+        any_need = true;
+        if (MODE == SV_MODE_NKL) sh.acc[tid] = 0;
+      } else {
+        const double nkl = p.V > 1 ? sh.kl1[tid] / lnV : 0.0;
+        if (p.out_nkl) p.out_nkl[pos] = (float)nkl;
         if (MODE == SV_MODE_NKL) sh.acc[tid] = nkl < (double)p.delta ? 1 : 0;
       }
-      __syncthreads();
     }
+    if (want_kl) __syncthreads();
     if (MODE != SV_MODE_TREE_GREEDY) {
       const int cand = (tid < TPP && base + tid < ntask && !sh.acc[tid]) ? base + tid : INT_MAX;
       const int jp = block_min_int(cand, sh.red_i);
@@ -978,13 +1115,17 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
         js_d = sh.sd[s];
         jidx = sh.idx[s];
       }
-      if (j >= 0 && !diag) break;
+      if (j >= 0 && !diag) {
+        checked = min(g, base + TPP);
+        break;
+      }
     }
+    checked = min(g, base + TPP);
     __syncthreads();  // LDS of this pass is reused by the next
   }
 
-  bool bad = false;
-  for (int k = tid; k < g; k += kThreads) {
+  // positions the passes did not reach (an early exit) are checked here
+  for (int k = checked + tid; k < g; k += kThreads) {
     const int x = p.tokens[d0 + k];
     bool ok = x >= 0 && x < p.V;
     if (MODE == SV_MODE_STOCHASTIC) ok = ok && unit_ok(p.ua[d0 + k]);
@@ -1001,6 +1142,10 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
   if constexpr (MODE == SV_MODE_TREE_GREEDY) {
     resolve_tree(p, b, g, t0, d0, tr, sh);
     return;
+  }
+  if (want_kl && __syncthreads_or(any_need)) {
+    if (tid == 0) p.pending[b] = 1;
+    if (MODE == SV_MODE_NKL) return;  // the decision needs the second-pass values: k_finish
   }
   if (j < 0) j = g;  // stochastic: every draft accepted
   for (int k = tid; k <= g; k += kThreads) {
@@ -1028,6 +1173,63 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
       }
       p.term[b] = tm;
     }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// k_refine and k_finish (when KL values are computed)
+//
+// k_refine: the queued positions x chunks are split into contiguous ranges,
+// one per workgroup; every (position, chunk) sum is written to its own slot,
+// so the values do not depend on the queue order.  k_finish: one workgroup
+// per request that waits for second-pass values adds the chunk sums in chunk
+// order, writes the NKL values and, in NKL mode, the decision.
+// ----------------------------------------------------------------------------
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_refine(Params p) {
+  __shared__ double shd[kWaves];
+  constexpr int64_t CHR = (int64_t)kThreads * kUR * Elem<DT>::P;
+  const int64_t N = (int64_t)p.hdr[1] * p.nch_r;
+  const int G = (int)gridDim.x, wg = (int)blockIdx.x;
+  const int64_t i_end = (int64_t)(wg + 1) * N / G;
+  for (int64_t i = (int64_t)wg * N / G; i < i_end; ++i) {
+    const int k = (int)(i / p.nch_r);
+    const int c = (int)(i - (int64_t)k * p.nch_r);
+    const int pos = p.ref_list[k];
+    const RefIn ri = p.ref_in[pos];
+    const double v = kl_chunk<DT, VEC>(p, ri, pos, (int64_t)c * CHR, shd);
+    if (threadIdx.x == 0) p.kl_part[(int64_t)pos * p.nch_r + c] = v;
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void k_finish(Params p) {
+  __shared__ int red[kWaves];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  if (!p.pending[b]) return;
+  const int d0 = p.d_off[b];
+  const int g = p.d_off[b + 1] - d0;
+  const int t0 = d0 + b;
+  const double lnV = log((double)p.V);
+  int first = INT_MAX;
+  for (int i = tid; i < g; i += kThreads) {
+    const int pos = d0 + i;
+    double kl = p.kl_val[pos];
+    if (p.kl_need[pos]) {
+      kl = 0.0;
+      for (int c = 0; c < p.nch_r; ++c) kl += p.kl_part[(int64_t)pos * p.nch_r + c];
+    }
+    const double nkl = p.V > 1 ? kl / lnV : 0.0;
+    p.out_nkl[pos] = (float)nkl;
+    if (!(nkl < (double)p.delta)) first = min(first, i);
+  }
+  if (MODE == SV_MODE_NKL) {
+    const int j0 = block_min_int(first, red);
+    const int j = j0 == INT_MAX ? g : j0;
+    for (int k = tid; k <= g; k += kThreads)
+      p.out_tokens[t0 + k] = k < j ? p.tokens[d0 + k] : (k == j ? p.tidx[t0 + j] : -1);
+    if (tid == 0) p.out_num[b] = j;
   }
 }
 
@@ -1390,7 +1592,8 @@ int stats_occupancy() {
   static int occ = 0;  // same value from every thread: a race is benign
   if (occ == 0) {
     int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, k_stats<DT, VEC, MODE, WZ>, kThreads, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, k_stats<DT, VEC, MODE, WZ, true>, kThreads, 0) !=
+            hipSuccess ||
         o <= 0)
       o = 1;
     occ = o;
@@ -1423,7 +1626,8 @@ int stats_occupancy_mode(int mode, bool wz) {
 
 template <int DT, bool VEC, int MODE, bool WZ>
 void stats_launch(const Params& p, hipStream_t s) {
-  hipLaunchKernelGGL((k_stats<DT, VEC, MODE, WZ>), dim3(p.stats_grid), dim3(kThreads), 0, s, p);
+  if (p.B <= kLdsBatch) hipLaunchKernelGGL((k_stats<DT, VEC, MODE, WZ, true>), dim3(p.stats_grid), dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL((k_stats<DT, VEC, MODE, WZ, false>), dim3(p.stats_grid), dim3(kThreads), 0, s, p);
 }
 template <int DT, bool VEC>
 void stats_dispatch(const Params& p, hipStream_t s) {
@@ -1498,6 +1702,22 @@ int launch_decide(const Params& p, bool vec, void* stream) {
     if (vec) decide_dispatch<SV_DTYPE_F32, true>(p, s);
     else decide_dispatch<SV_DTYPE_F32, false>(p, s);
   }
+  return (int)hipGetLastError();
+}
+
+int launch_refine(const Params& p, bool vec, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  // the queue length is only known on the device: one wave of workgroups
+  const dim3 grid((unsigned)(4 * num_cus())), blk(kThreads), fgrid(p.B);
+  if (p.dtype == SV_DTYPE_BF16) {
+    if (vec) hipLaunchKernelGGL((k_refine<SV_DTYPE_BF16, true>), grid, blk, 0, s, p);
+    else hipLaunchKernelGGL((k_refine<SV_DTYPE_BF16, false>), grid, blk, 0, s, p);
+  } else {
+    if (vec) hipLaunchKernelGGL((k_refine<SV_DTYPE_F32, true>), grid, blk, 0, s, p);
+    else hipLaunchKernelGGL((k_refine<SV_DTYPE_F32, false>), grid, blk, 0, s, p);
+  }
+  if (p.mode == SV_MODE_NKL) hipLaunchKernelGGL((k_finish<SV_MODE_NKL>), fgrid, blk, 0, s, p);
+  else hipLaunchKernelGGL((k_finish<SV_MODE_STOCHASTIC>), fgrid, blk, 0, s, p);
   return (int)hipGetLastError();
 }
 

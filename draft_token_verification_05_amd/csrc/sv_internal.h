@@ -18,6 +18,7 @@ constexpr int stats_vectors_per_thread(int mode) {
 }
 constexpr int kUA = 2;           // smallest of the above: sizes the partial arrays
 constexpr int kUC = 2;           // 16-byte vectors per lane per row in a wave-chunk of the draw pass
+constexpr int kUR = 2;           // 16-byte vectors per thread per row per chunk, KL second pass
 constexpr int kLdsBatch = 1024;  // batches up to this size scan their offsets in LDS (no prep kernel)
 
 constexpr int elems_per_vec(int dtype) { return dtype == SV_DTYPE_BF16 ? 8 : 4; }
@@ -28,6 +29,7 @@ constexpr int64_t chunk_stats(int dtype, int mode) {
   return (int64_t)kThreads * stats_vectors_per_thread(mode) * elems_per_vec(dtype);
 }
 constexpr int64_t chunk_c(int dtype) { return (int64_t)64 * kUC * elems_per_vec(dtype); }
+constexpr int64_t chunk_r(int dtype) { return (int64_t)kThreads * kUR * elems_per_vec(dtype); }
 
 enum TermKind : int32_t { kTermNone = 0, kTermResidual = 1, kTermBonus = 2 };
 
@@ -56,6 +58,15 @@ struct Term {
   float Lhi;     // fl32(log2(e) / T) of the request
 };
 
+// A position whose one-pass KL needs the second pass: the merged statistics
+// of its rows.
+struct RefIn {
+  double s_t, s_d;
+  float m_t, m_d;
+  float Lhi;
+  int32_t trow;
+};
+
 // Partial sums of the draw pass for one (request, wave-chunk), in float64.
 struct PartC {
   double a, b, ap, bp;  // sum a, sum b, and the same over {y : a_y > k0 * b_y}
@@ -64,9 +75,10 @@ struct PartC {
 };
 
 struct Layout {
-  size_t off_hdr, off_doff, off_pair2req, off_row2req, off_part_a, off_term, off_part_c, total;
+  size_t off_hdr, off_doff, off_pair2req, off_row2req, off_part_a, off_term, off_part_c, off_ref_list, off_kl_need,
+      off_ref_in, off_kl_val, off_tidx, off_pending, off_kl_part, total;
   int64_t n_task_max;
-  int64_t nch_a, nch_c;
+  int64_t nch_a, nch_c, nch_r;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -75,7 +87,9 @@ inline Layout make_layout(int64_t B, int64_t V, int dtype, int64_t R_d) {
   Layout L{};
   L.nch_a = (V + chunk_a(dtype) - 1) / chunk_a(dtype);
   L.nch_c = (V + chunk_c(dtype) - 1) / chunk_c(dtype);
+  L.nch_r = (V + chunk_r(dtype) - 1) / chunk_r(dtype);
   L.n_task_max = R_d + B;
+  const int64_t R1 = R_d > 0 ? R_d : 1;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t at = o;
@@ -89,6 +103,13 @@ inline Layout make_layout(int64_t B, int64_t V, int dtype, int64_t R_d) {
   L.off_part_a = take(sizeof(PartA) * L.n_task_max * L.nch_a);
   L.off_term = take(sizeof(Term) * B);
   L.off_part_c = take(sizeof(PartC) * B * L.nch_c);
+  L.off_ref_list = take(sizeof(int32_t) * R1);
+  L.off_kl_need = take(sizeof(int32_t) * R1);
+  L.off_ref_in = take(sizeof(RefIn) * R1);
+  L.off_kl_val = take(sizeof(double) * R1);
+  L.off_tidx = take(sizeof(int32_t) * (R_d + B));
+  L.off_pending = take(sizeof(int32_t) * B);
+  L.off_kl_part = take(sizeof(double) * R1 * L.nch_r);
   L.total = o;
   return L;
 }
@@ -116,17 +137,25 @@ struct Params {
   int32_t nch;         // vocabulary chunks per task in the row-statistics pass
   int32_t stats_grid;  // workgroups of the row-statistics pass
   int32_t grp_log2;    // log2 of the lanes that merge one task's partials
-  int32_t nch_c;       // vocabulary chunks per request in the draw pass
+  int32_t nch_c;       // vocabulary wave-chunks per request in the draw pass
+  int32_t nch_r;       // vocabulary chunks per position in the KL second pass
   float delta;
   int32_t want_kl;  // compute KL(q || p) (NKL mode, or stochastic with out_nkl)
   // workspace
-  int32_t* hdr;  // hdr[0]: layout error flag
+  int32_t* hdr;  // hdr[0]: layout error flag, hdr[1]: positions queued for the KL second pass
   int32_t* d_off;
   int32_t* pair2req;
   int32_t* row2req;
   PartA* part_a;
   Term* term;
   PartC* part_c;
+  int32_t* ref_list;  // [R_d] positions queued for the KL second pass (hdr[1] of them)
+  int32_t* kl_need;   // [R_d] 1 where the KL of the position comes from the second pass
+  RefIn* ref_in;      // [R_d]
+  double* kl_val;     // [R_d] one-pass KL (nats)
+  int32_t* tidx;      // [R_d + B] argmax of every target row (NKL)
+  int32_t* pending;   // [B] the request waits for second-pass KL values
+  double* kl_part;    // [R_d * nch_r] second-pass KL sums per chunk
 };
 
 // kernel launchers (kernels.hip); return the hipError_t of the launch as int
@@ -136,5 +165,6 @@ int plan_stats(Params& p, bool vec);
 int launch_stats(const Params& p, bool vec, void* stream);
 int launch_decide(const Params& p, bool vec, void* stream);
 int launch_draw(const Params& p, bool vec, void* stream);
+int launch_refine(const Params& p, bool vec, void* stream);
 
 }  // namespace sv

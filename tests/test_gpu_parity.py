@@ -127,6 +127,20 @@ def test_identical_rows():
     assert (g2["nkl"] == 0).all() and (g2["num"] == w.gamma).all()
 
 
+@pytest.mark.parametrize("V,dtype,sigma,mode", [(128256, "bf16", 0.003, K), (50000, "f32", 0.01, K),
+                                                 (20000, "bf16", 0.05, K), (152064, "bf16", 0.003, S)])
+def test_small_kl_second_pass(V, dtype, sigma, mode):
+    """Draft rows within a small noise of the target rows: KL values far below
+    the one-pass error scale take the grid-wide second pass (NKL mode, and the
+    optional NKL output of stochastic mode)."""
+    w = synthetic.random_workload(seed=int(V % 89 + 1000 * sigma), mode=mode, B=24, V=V, dtype=dtype, gmax=6,
+                                  gmin=1, sigma=sigma)
+    if mode == K:
+        w = w.with_mode(K, delta=float(np.float32(2e-5)))
+    g, o, rep = check(w, out_nkl=True)
+    assert rep.max_rel_nkl < 2e-5
+
+
 def test_invalid_requests_isolated():
     w = synthetic.random_workload(seed=12, mode=S, B=10, V=3000, dtype="bf16", gmax=4, gmin=2)
     d_off = w.d_off
