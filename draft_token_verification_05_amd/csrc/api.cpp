@@ -154,9 +154,9 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e);
   // small batches scan their offsets inside the statistics kernel
   if (B > sv::kLdsBatch && (e = (hipError_t)sv::launch_prep(p, s)) != hipSuccess) return hip_fail(e);
-  if (ev && (e = hipEventRecord(ev[1], s)) != hipSuccess) return hip_fail(e);
-  if ((e = (hipError_t)sv::launch_stats(p, vec, s)) != hipSuccess) return hip_fail(e);
-  if (ev && (e = hipEventRecord(ev[2], s)) != hipSuccess) return hip_fail(e);
+  // ev[1] / ev[2] take the statistics dispatch's own start and end timestamps
+  if ((e = (hipError_t)sv::launch_stats(p, vec, s, ev ? ev[1] : nullptr, ev ? ev[2] : nullptr)) != hipSuccess)
+    return hip_fail(e);
   if ((e = (hipError_t)sv::launch_decide(p, vec, s)) != hipSuccess) return hip_fail(e);
   if (p.want_kl && (e = (hipError_t)sv::launch_refine(p, vec, s)) != hipSuccess) return hip_fail(e);
   if (mode == SV_MODE_STOCHASTIC && (e = (hipError_t)sv::launch_draw(p, vec, s)) != hipSuccess) return hip_fail(e);

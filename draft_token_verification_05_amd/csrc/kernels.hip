@@ -40,6 +40,7 @@
 // in the statistics, decision and draw passes alike, so the three passes see
 // the same distributions.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -1624,21 +1625,28 @@ int stats_occupancy_mode(int mode, bool wz) {
   }
 }
 
+// With events, the dispatch itself stamps them (kernel start and end), so the
+// timing excludes the queueing around the launch.
+template <typename K>
+void launch_timed(K kernel, dim3 grid, const Params& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (e0 && e1) hipExtLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, e0, e1, 0, p);
+  else hipLaunchKernelGGL(kernel, grid, dim3(kThreads), 0, s, p);
+}
 template <int DT, bool VEC, int MODE, bool WZ>
-void stats_launch(const Params& p, hipStream_t s) {
-  if (p.B <= kLdsBatch) hipLaunchKernelGGL((k_stats<DT, VEC, MODE, WZ, true>), dim3(p.stats_grid), dim3(kThreads), 0, s, p);
-  else hipLaunchKernelGGL((k_stats<DT, VEC, MODE, WZ, false>), dim3(p.stats_grid), dim3(kThreads), 0, s, p);
+void stats_launch(const Params& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  if (p.B <= kLdsBatch) launch_timed(k_stats<DT, VEC, MODE, WZ, true>, dim3(p.stats_grid), p, s, e0, e1);
+  else launch_timed(k_stats<DT, VEC, MODE, WZ, false>, dim3(p.stats_grid), p, s, e0, e1);
 }
 template <int DT, bool VEC>
-void stats_dispatch(const Params& p, hipStream_t s) {
+void stats_dispatch(const Params& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   switch (p.mode) {
     case SV_MODE_STOCHASTIC:
-      if (p.want_kl) stats_launch<DT, VEC, SV_MODE_STOCHASTIC, true>(p, s);
-      else stats_launch<DT, VEC, SV_MODE_STOCHASTIC, false>(p, s);
+      if (p.want_kl) stats_launch<DT, VEC, SV_MODE_STOCHASTIC, true>(p, s, e0, e1);
+      else stats_launch<DT, VEC, SV_MODE_STOCHASTIC, false>(p, s, e0, e1);
       break;
-    case SV_MODE_GREEDY: stats_launch<DT, VEC, SV_MODE_GREEDY, false>(p, s); break;
-    case SV_MODE_NKL: stats_launch<DT, VEC, SV_MODE_NKL, false>(p, s); break;
-    default: stats_launch<DT, VEC, SV_MODE_TREE_GREEDY, false>(p, s); break;
+    case SV_MODE_GREEDY: stats_launch<DT, VEC, SV_MODE_GREEDY, false>(p, s, e0, e1); break;
+    case SV_MODE_NKL: stats_launch<DT, VEC, SV_MODE_NKL, false>(p, s, e0, e1); break;
+    default: stats_launch<DT, VEC, SV_MODE_TREE_GREEDY, false>(p, s, e0, e1); break;
   }
 }
 template <int DT, bool VEC>
@@ -1681,14 +1689,15 @@ int plan_stats(Params& p, bool vec) {
   return 0;
 }
 
-int launch_stats(const Params& p, bool vec, void* stream) {
+int launch_stats(const Params& p, bool vec, void* stream, void* ev_start, void* ev_stop) {
   hipStream_t s = (hipStream_t)stream;
+  hipEvent_t e0 = (hipEvent_t)ev_start, e1 = (hipEvent_t)ev_stop;
   if (p.dtype == SV_DTYPE_BF16) {
-    if (vec) stats_dispatch<SV_DTYPE_BF16, true>(p, s);
-    else stats_dispatch<SV_DTYPE_BF16, false>(p, s);
+    if (vec) stats_dispatch<SV_DTYPE_BF16, true>(p, s, e0, e1);
+    else stats_dispatch<SV_DTYPE_BF16, false>(p, s, e0, e1);
   } else {
-    if (vec) stats_dispatch<SV_DTYPE_F32, true>(p, s);
-    else stats_dispatch<SV_DTYPE_F32, false>(p, s);
+    if (vec) stats_dispatch<SV_DTYPE_F32, true>(p, s, e0, e1);
+    else stats_dispatch<SV_DTYPE_F32, false>(p, s, e0, e1);
   }
   return (int)hipGetLastError();
 }

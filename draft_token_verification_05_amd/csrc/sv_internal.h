@@ -162,7 +162,9 @@ struct Params {
 int launch_prep(const Params& p, void* stream);
 // picks the grid of the statistics pass: fills p.stats_grid and p.grp_log2
 int plan_stats(Params& p, bool vec);
-int launch_stats(const Params& p, bool vec, void* stream);
+// ev_start / ev_stop: optional hipEvent_t handles that take the dispatch's own
+// start and end timestamps (NULL = plain launch)
+int launch_stats(const Params& p, bool vec, void* stream, void* ev_start, void* ev_stop);
 int launch_decide(const Params& p, bool vec, void* stream);
 int launch_draw(const Params& p, bool vec, void* stream);
 int launch_refine(const Params& p, bool vec, void* stream);

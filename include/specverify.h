@@ -80,9 +80,10 @@ extern "C" {
 #define SV_MAX_GAMMA 4096 /* largest accepted cfg->max_gamma (tree: nodes - 1) */
 
 /* Phase events (optional, for timing): cfg->phase_events points to
- * SV_NUM_PHASE_EVENTS hipEvent_t handles created by the caller.  They are
- * recorded on cfg->stream: [0] before the first kernel, [1] before the
- * row-statistics kernel, [2] after it, [3] after the last kernel. */
+ * SV_NUM_PHASE_EVENTS hipEvent_t handles created by the caller, all on
+ * cfg->stream: [0] is recorded before the first kernel and [3] after the last;
+ * [1] and [2] take the start and end timestamps of the row-statistics
+ * dispatch itself (the streaming pass over the logits). */
 #define SV_NUM_PHASE_EVENTS 4
 
 typedef struct sv_config {
