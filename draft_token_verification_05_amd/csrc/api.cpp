@@ -29,9 +29,9 @@ int validate(const void* target, const void* draft, const int32_t* tokens, const
   if (R_d < 0 || R_d > (int64_t)cfg->batch * cfg->max_gamma) return SV_EINVAL;
   if (R_d + cfg->batch > INT32_MAX) return SV_EUNSUPPORTED;
   const int64_t nch_a = (cfg->vocab + sv::chunk_a(cfg->dtype) - 1) / sv::chunk_a(cfg->dtype);
-  const int64_t nch_c = (cfg->vocab + sv::chunk_c(cfg->dtype) - 1) / sv::chunk_c(cfg->dtype);
-  const int64_t nch_r = (cfg->vocab + sv::chunk_r(cfg->dtype) - 1) / sv::chunk_r(cfg->dtype);
-  if ((R_d + cfg->batch) * nch_a > INT32_MAX || (int64_t)cfg->batch * nch_c > INT32_MAX || R_d * nch_r > INT32_MAX)
+  const int64_t nch_t = (cfg->vocab + sv::chunk_t(cfg->dtype) - 1) / sv::chunk_t(cfg->dtype);
+  // grids and flat indices: statistics partials, decision helpers, KL slice sums
+  if ((R_d + cfg->batch) * nch_a > INT32_MAX || (int64_t)cfg->batch * nch_t > INT32_MAX || R_d * nch_t > INT32_MAX)
     return SV_EUNSUPPORTED;
 
   const bool soft = mode == SV_MODE_STOCHASTIC || mode == SV_MODE_NKL;
@@ -122,8 +122,6 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   p.R_d = (int32_t)R_d;
   p.n_task = (int32_t)(mode == SV_MODE_STOCHASTIC ? R_d : R_d + B);
   p.nch = (int32_t)((V + sv::chunk_stats(cfg->dtype, mode) - 1) / sv::chunk_stats(cfg->dtype, mode));
-  p.nch_c = (int32_t)L.nch_c;
-  p.nch_r = (int32_t)L.nch_r;
   p.delta = delta;
   p.want_kl = (mode == SV_MODE_NKL || (mode == SV_MODE_STOCHASTIC && out_nkl)) ? 1 : 0;
   p.hdr = reinterpret_cast<int32_t*>(ws + L.off_hdr);
@@ -131,14 +129,11 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   p.pair2req = reinterpret_cast<int32_t*>(ws + L.off_pair2req);
   p.row2req = reinterpret_cast<int32_t*>(ws + L.off_row2req);
   p.part_a = reinterpret_cast<sv::PartA*>(ws + L.off_part_a);
-  p.term = reinterpret_cast<sv::Term*>(ws + L.off_term);
+  p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
   p.part_c = reinterpret_cast<sv::PartC*>(ws + L.off_part_c);
-  p.ref_list = reinterpret_cast<int32_t*>(ws + L.off_ref_list);
   p.kl_need = reinterpret_cast<int32_t*>(ws + L.off_kl_need);
-  p.ref_in = reinterpret_cast<sv::RefIn*>(ws + L.off_ref_in);
   p.kl_val = reinterpret_cast<double*>(ws + L.off_kl_val);
   p.tidx = reinterpret_cast<int32_t*>(ws + L.off_tidx);
-  p.pending = reinterpret_cast<int32_t*>(ws + L.off_pending);
   p.kl_part = reinterpret_cast<double*>(ws + L.off_kl_part);
 
   // 16-byte vector loads need every row to start on a 16-byte boundary
@@ -147,6 +142,7 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
                    (!draft_logits || aligned(draft_logits, 16));
 
   sv::plan_stats(p, vec);
+  sv::plan_decide(p, vec);
 
   hipStream_t s = static_cast<hipStream_t>(cfg->stream);
   hipEvent_t* ev = static_cast<hipEvent_t*>(cfg->phase_events);
@@ -158,8 +154,6 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   if ((e = (hipError_t)sv::launch_stats(p, vec, s, ev ? ev[1] : nullptr, ev ? ev[2] : nullptr)) != hipSuccess)
     return hip_fail(e);
   if ((e = (hipError_t)sv::launch_decide(p, vec, s)) != hipSuccess) return hip_fail(e);
-  if (p.want_kl && (e = (hipError_t)sv::launch_refine(p, vec, s)) != hipSuccess) return hip_fail(e);
-  if (mode == SV_MODE_STOCHASTIC && (e = (hipError_t)sv::launch_draw(p, vec, s)) != hipSuccess) return hip_fail(e);
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e);
   return SV_OK;
 }

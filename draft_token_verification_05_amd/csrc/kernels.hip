@@ -13,17 +13,20 @@
 //               workgroup folds its chunks into running (max, sum exp,
 //               argmax, KL cross terms) and writes one partial per task
 //               segment with plain stores: no atomics, no waiting.
-//   k_decide    one workgroup per request: merges the partials of its tasks,
-//               evaluates acceptance (alpha = min(1, p/q) against u, argmax
-//               match, NKL < delta, tree paths), refines KL values whose
-//               one-pass form is not accurate enough with a second pass, and
-//               writes tokens, counts and diagnostics.  Stochastic requests
-//               leave the terminal slot to k_draw.
-//   k_draw      stochastic mode only: one workgroup per (request, chunk) of
-//               the terminal row; float64 chunk sums of the residual
-//               max(0, p - q) (or of p for a bonus token); the last workgroup
-//               of a request picks the chunk and draws the token by a
-//               workgroup-wide prefix sum.
+//   k_decide    H workgroups ("helpers") per request, H = 1 in greedy and tree
+//               modes and one per vocabulary slice of kThreads x kUT vectors
+//               in stochastic and NKL modes.  Every helper merges the
+//               partials of the request's tasks and takes the same decision
+//               (alpha = min(1, p/q) against u, argmax match, NKL < delta,
+//               tree paths); helper 0 writes tokens, counts and diagnostics.
+//               Helper h then streams slice h of the rows that need a second
+//               look: the terminal row(s) of a stochastic request (float64
+//               sums of the residual max(0, p - q), or of p for a bonus
+//               token) and the row pairs whose one-pass KL is not accurate
+//               enough.  The last helper of a request to finish combines the
+//               slices in slice order, draws the terminal token by inverse
+//               CDF (a workgroup-wide prefix sum over the slice that holds
+//               it) and completes the KL values and the NKL decision.
 //
 // Formulas follow these passages:
 //   softmax(logits / T), p(x), q(x)     -- "Chain of Draft" page, section 3.2
@@ -46,6 +49,7 @@
 #include <cfloat>
 #include <climits>
 #include <cstdint>
+#include <type_traits>
 
 #include "sv_internal.h"
 
@@ -213,11 +217,89 @@ __device__ __forceinline__ int wave_max_int(int v) {
   return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
              max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
-// butterfly sum: every lane ends with the same bits (a + b == b + a in IEEE)
+// 64-bit DPP moves: both 32-bit halves take the same lane pattern; a lane
+// that the row / bank masks leave out, or whose source lies outside its row,
+// gets 0.
+template <int CTRL, int RM = 0xF, int BM = 0xF>
+__device__ __forceinline__ long long dpp64(long long v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)v, CTRL, RM, BM, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(v >> 32), CTRL, RM, BM, false);
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+template <int CTRL, int RM = 0xF, int BM = 0xF>
+__device__ __forceinline__ double dpp_d(double v) {
+  return __longlong_as_double(dpp64<CTRL, RM, BM>(__double_as_longlong(v)));
+}
+__device__ __forceinline__ double lane_d(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)b, l), hi = __builtin_amdgcn_readlane((int)(b >> 32), l);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
+// Sum over the wave.  Within each row of 16 lanes, partner groups of 1, 2, 4
+// and 8 lanes are added (quad permutes, half-row mirror, row mirror), so
+// every lane of a row holds the same bits (a + b == b + a in IEEE); the four
+// row sums are then added in a fixed order.  The result is wave-uniform.
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
-  return v;
+  v += dpp_d<0xB1>(v);   // quad_perm(1,0,3,2)
+  v += dpp_d<0x4E>(v);   // quad_perm(2,3,0,1)
+  v += dpp_d<0x141>(v);  // row_half_mirror
+  v += dpp_d<0x140>(v);  // row_mirror
+  return (lane_d(v, 0) + lane_d(v, 16)) + (lane_d(v, 32) + lane_d(v, 48));
+}
+
+// Inclusive prefix sums over the wave in lane order: sums of 2, 3 and 4
+// within a row (row shifts of 1..3), then of 8 and 16 (row shifts of 4 and 8
+// on the upper banks), then the rows before (row broadcasts of lanes 15 and
+// 31).  Lanes with no source add 0.
+__device__ __forceinline__ double wave_incl_scan_d(double v) {
+  double x = v + dpp_d<0x111>(v);  // row_shr:1
+  x += dpp_d<0x112>(v);            // row_shr:2
+  x += dpp_d<0x113>(v);            // row_shr:3
+  x += dpp_d<0x114, 0xF, 0xE>(x);  // row_shr:4, lanes 4..15 of each row
+  x += dpp_d<0x118, 0xF, 0xC>(x);  // row_shr:8, lanes 8..15 of each row
+  x += dpp_d<0x142, 0xA, 0xF>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_d<0x143, 0xC, 0xF>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+__device__ __forceinline__ long long wave_incl_scan_i64(long long v) {
+  long long x = v + dpp64<0x111>(v);
+  x += dpp64<0x112>(v);
+  x += dpp64<0x113>(v);
+  x += dpp64<0x114, 0xF, 0xE>(x);
+  x += dpp64<0x118, 0xF, 0xC>(x);
+  x += dpp64<0x142, 0xA, 0xF>(x);
+  x += dpp64<0x143, 0xC, 0xF>(x);
+  return x;
+}
+
+// Value of the partner group in a reduction over aligned groups of M lanes:
+// groups of M = 1, 2, 4, 8 lanes meet their neighbour inside the row (quad
+// permutes, half-row mirror, row mirror); 16 and 32 across rows.  Every lane
+// of a group must hold the same value when M > 1.
+template <int M>
+__device__ __forceinline__ double partner_d(double v) {
+  if constexpr (M == 1) return dpp_d<0xB1>(v);
+  else if constexpr (M == 2) return dpp_d<0x4E>(v);
+  else if constexpr (M == 4) return dpp_d<0x141>(v);
+  else if constexpr (M == 8) return dpp_d<0x140>(v);
+  else return __shfl_xor(v, M, 64);
+}
+template <int M>
+__device__ __forceinline__ float partner_f(float v) {
+  if constexpr (M == 1) return dpp<0xB1>(v, v);
+  else if constexpr (M == 2) return dpp<0x4E>(v, v);
+  else if constexpr (M == 4) return dpp<0x141>(v, v);
+  else if constexpr (M == 8) return dpp<0x140>(v, v);
+  else return __shfl_xor(v, M, 64);
+}
+template <int M>
+__device__ __forceinline__ int partner_i(int v) {
+  if constexpr (M == 1) return dppi<0xB1>(v, v);
+  else if constexpr (M == 2) return dppi<0x4E>(v, v);
+  else if constexpr (M == 4) return dppi<0x141>(v, v);
+  else if constexpr (M == 8) return dppi<0x140>(v, v);
+  else return __shfl_xor(v, M, 64);
 }
 
 // workgroup-wide reductions through LDS (all threads must call)
@@ -293,12 +375,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Params p) {
         g = 0;
       }
     }
-    long long incl = g;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const long long o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
-    }
+    const long long incl = wave_incl_scan_i64(g);
     if (lane == 63) sh_w[w] = incl;
     __syncthreads();
     long long before = 0, tile = 0;
@@ -313,10 +390,8 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Params p) {
   }
   if (tid == 0) p.d_off[p.B] = (int)carry;
   const bool bad = sh_bad != 0 || carry != (long long)p.R_d;
-  if (tid == 0) {
-    p.hdr[0] = bad ? 1 : 0;
-    p.hdr[1] = 0;  // queue of the KL second pass
-  }
+  if (tid == 0) p.hdr[0] = bad ? 1 : 0;
+  for (int b = tid; b < p.B; b += kPrepThreads) p.cnt[b] = 0u;  // helper counters of k_decide
   if (bad) return;
   __syncthreads();  // offsets written by other threads of this workgroup
   for (int b = tid; b < p.B; b += kPrepThreads) {
@@ -384,12 +459,7 @@ __device__ bool scan_offsets_lds(const Params& p, StatsShared& sh, bool soft, bo
     g[k] = v;
     loc += v;
   }
-  long long incl = loc;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const long long t = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += t;
-  }
+  const long long incl = wave_incl_scan_i64(loc);
   if (lane == 63) sh.wsum[w] = incl;
   if (tid == 0) sh.bad = 0;
   __syncthreads();
@@ -415,10 +485,8 @@ __device__ bool scan_offsets_lds(const Params& p, StatsShared& sh, bool soft, bo
   const bool ok = sh.bad == 0;
   if (publish) {
     for (int b = tid; b <= p.B; b += kThreads) p.d_off[b] = sh.off[b];
-    if (tid == 0) {
-      p.hdr[0] = ok ? 0 : 1;
-      p.hdr[1] = 0;  // queue of the KL second pass
-    }
+    for (int b = tid; b < p.B; b += kThreads) p.cnt[b] = 0u;  // helper counters of k_decide
+    if (tid == 0) p.hdr[0] = ok ? 0 : 1;
   }
   return ok;
 }
@@ -748,7 +816,7 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params p) {
 }
 
 // ----------------------------------------------------------------------------
-// k_decide: per-request merge and decision
+// k_decide: per-request merge, decision, terminal draw and KL second pass
 // ----------------------------------------------------------------------------
 
 // One-pass KL values whose estimated error exceeds kKlRel of the value, or
@@ -808,22 +876,32 @@ __device__ __forceinline__ Merged merge_task(const Params& p, int64_t task, bool
       r.mt = fmaxf(r.mt, mt);
     }
   }
+  // group reductions: f is applied for M = 1, 2, 4, ... below S (uniform branches)
+  const auto levels = [S](auto&& f) {
+    if (S > 1) f(std::integral_constant<int, 1>{});
+    if (S > 2) f(std::integral_constant<int, 2>{});
+    if (S > 4) f(std::integral_constant<int, 4>{});
+    if (S > 8) f(std::integral_constant<int, 8>{});
+    if (S > 16) f(std::integral_constant<int, 16>{});
+    if (S > 32) f(std::integral_constant<int, 32>{});
+  };
   float Mt = r.mt, Md = r.md;
-  for (int m = 1; m < S; m <<= 1) {
-    Mt = fmaxf(Mt, __shfl_xor(Mt, m, 64));
-    if (SOFT) Md = fmaxf(Md, __shfl_xor(Md, m, 64));
-  }
+  levels([&](auto m) {
+    Mt = fmaxf(Mt, partner_f<decltype(m)::value>(Mt));
+    if (SOFT) Md = fmaxf(Md, partner_f<decltype(m)::value>(Md));
+  });
   int ix = r.mt == Mt ? r.idx : INT_MAX;
-  for (int m = 1; m < S; m <<= 1) ix = min(ix, __shfl_xor(ix, m, 64));
+  levels([&](auto m) { ix = min(ix, partner_i<decltype(m)::value>(ix)); });
   if (SOFT) {
     const double ft = rescale(r.mt, Mt, Lhi), fd = rescale(r.md, Md, Lhi);
     double st = r.st * ft, sd = r.sd * fd, w = r.w * fd, z = r.z * fd;
-    for (int m = 1; m < S; m <<= 1) {
-      st += __shfl_xor(st, m, 64);
-      sd += __shfl_xor(sd, m, 64);
-      w += __shfl_xor(w, m, 64);
-      z += __shfl_xor(z, m, 64);
-    }
+    levels([&](auto m) {
+      constexpr int M = decltype(m)::value;
+      st += partner_d<M>(st);
+      sd += partner_d<M>(sd);
+      w += partner_d<M>(w);
+      z += partner_d<M>(z);
+    });
     r.st = st;
     r.sd = sd;
     r.w = w;
@@ -847,29 +925,56 @@ __device__ __forceinline__ float g_small(float w) {
   return w * w * t;
 }
 
+// Loads of one vocabulary slice: thread t takes 16-byte vectors
+// k * kThreads + t, k < kUT, of the target row and (TWO) of the draft row.
+template <int DT, bool VEC, bool TWO>
+__device__ __forceinline__ void slice_issue(const Params& p, int64_t trow, int64_t drow, int sl, uint4* qt,
+                                            uint4* qd) {
+  constexpr int P = Elem<DT>::P;
+  const int64_t e_base = (int64_t)sl * kThreads * kUT * P;
+#pragma unroll
+  for (int k = 0; k < kUT; ++k) {
+    const int64_t e0 = e_base + ((int64_t)k * kThreads + threadIdx.x) * P;
+    qt[k] = fetch<DT, VEC>(p.target, trow, p.V, e0);
+    if (TWO) qd[k] = fetch<DT, VEC>(p.draft, drow, p.V, e0);
+  }
+}
+
+// Streams slices [s0, s1) of the rows with the loads of slice s + 1 in flight
+// while slice s is consumed by f(qt, qd, s).  All threads call; f may hold
+// workgroup barriers.
+template <int DT, bool VEC, bool TWO, class F>
+__device__ __forceinline__ void slice_stream(const Params& p, int64_t trow, int64_t drow, int s0, int s1, F&& f) {
+  uint4 at[kUT], ad[kUT], bt[kUT], bd[kUT];
+  if (s0 >= s1) return;
+  slice_issue<DT, VEC, TWO>(p, trow, drow, s0, at, ad);
+  for (int sl = s0; sl < s1; sl += 2) {
+    if (sl + 1 < s1) slice_issue<DT, VEC, TWO>(p, trow, drow, sl + 1, bt, bd);
+    f(at, ad, sl);
+    if (sl + 1 >= s1) break;
+    if (sl + 2 < s1) slice_issue<DT, VEC, TWO>(p, trow, drow, sl + 2, at, ad);
+    f(bt, bd, sl + 1);
+  }
+}
+
 // KL(q || p) of one row pair in a second pass, as the sum of the non-negative
-// terms q_y g(w_y), w_y = log(p_y / q_y), over one chunk of kThreads x kUR
-// vectors.  Because sum q e^w = sum p = 1, the sum over the row equals
+// terms q_y g(w_y), w_y = log(p_y / q_y), over slices of the vocabulary.  Because sum q e^w = sum p = 1, the sum over the row equals
 // sum q log(q/p) exactly, has no cancellation, and an error eps in the log
 // normaliser ratio only adds O(eps^2).  All threads of the workgroup call.
-template <int DT, bool VEC>
-__device__ double kl_chunk(const Params& p, const RefIn& ri, int64_t drow, int64_t e_chunk, double* shd) {
+struct KlIn {
+  float m_t, m_d;
+  float lr;              // log(s_d / s_t)
+  float inv_st, inv_sd;  // 1 / s_t, 1 / s_d
+};
+
+// Sum over one slice (thread-local part) of q_y g(w_y).
+template <int DT>
+__device__ __forceinline__ double kl_terms(const uint4* qt, const uint4* qd, const KlIn& ri, float Lhi) {
   constexpr int P = Elem<DT>::P;
-  const int64_t V = p.V;
-  const float Lhi = ri.Lhi;
   const float c = (float)((double)Lhi * kLn2D);  // d(log p)/d(logit)
-  const float lr = (float)log(ri.s_d / ri.s_t);
-  const float inv_sd = (float)(1.0 / ri.s_d), inv_st = (float)(1.0 / ri.s_t);
-  uint4 qt[kUR], qd[kUR];
-#pragma unroll
-  for (int k = 0; k < kUR; ++k) {
-    const int64_t e0 = e_chunk + ((int64_t)k * kThreads + threadIdx.x) * P;
-    qt[k] = fetch<DT, VEC>(p.target, ri.trow, V, e0);
-    qd[k] = fetch<DT, VEC>(p.draft, drow, V, e0);
-  }
   double acc = 0.0;
 #pragma unroll
-  for (int k = 0; k < kUR; ++k) {
+  for (int k = 0; k < kUT; ++k) {
     float vt[P], vd[P];
     unpack<DT>(qt[k], vt);
     unpack<DT>(qd[k], vd);
@@ -877,20 +982,36 @@ __device__ double kl_chunk(const Params& p, const RefIn& ri, int64_t drow, int64
 #pragma unroll
     for (int e = 0; e < P; ++e) {
       const float dt = vt[e] - ri.m_t, dd = vd[e] - ri.m_d;
-      const float q = ex2(dd, Lhi) * inv_sd;
-      const float w = fmaf(dt - dd, c, lr);
+      const float q = ex2(dd, Lhi) * ri.inv_sd;
+      const float w = fmaf(dt - dd, c, ri.lr);
       float term;
       if (fabsf(w) < 0.5f) {
         term = q * g_small(w);
       } else {
         // q g(w) = p - q - q w; also right where q underflows but p does not
-        term = (ex2(dt, Lhi) * inv_st - q) - q * w;
+        term = (ex2(dt, Lhi) * ri.inv_st - q) - q * w;
       }
       part += term;  // positions past the end of the row give p = q = 0
     }
     acc += (double)part;
   }
-  return block_sum_d(acc, shd);
+  return acc;
+}
+
+// ----------------------------------------------------------------------------
+// cross-workgroup hand-over inside k_decide.  Values that another workgroup
+// reads during the same dispatch are written and read at device scope (they
+// bypass the per-XCD L2, which is not coherent between XCDs); a helper counts
+// itself only after all of its stores have completed.
+// ----------------------------------------------------------------------------
+
+template <class T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 struct DecideShared {
@@ -900,9 +1021,29 @@ struct DecideShared {
   int acc[kThreads];
   double kl1[kThreads];
   int need[kThreads];
+  int list[kThreads];  // positions of a pass that need the KL second pass
   int red_i[kWaves];
+  int red_i2[kWaves];
+  float red_f[kWaves];
   double red_d[kWaves];
+  double red_d4[4][kWaves];
+  int flag;
 };
+
+// Counts this helper on the request's counter once every store of the
+// workgroup has completed; true in the last of the `H` helpers to arrive.
+__device__ __forceinline__ bool arrive_last(uint32_t* cnt, int H, DecideShared& sh) {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
+  __asm__ __volatile__("" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.flag = old + 1 == (uint32_t)H ? 1 : 0;
+  }
+  __syncthreads();
+  return sh.flag != 0;
+}
 
 template <int MODE>
 struct TreeShared {
@@ -928,7 +1069,6 @@ __device__ void finish_invalid(const Params& p, int b, int t0, int d0, int g) {
     p.out_num[b] = -1;
     if (p.out_resid) p.out_resid[b] = __builtin_nanf("");
     if (p.out_tree_node) p.out_tree_node[b] = -1;
-    if (p.mode == SV_MODE_STOCHASTIC) p.term[b].kind = kTermNone;
   }
 }
 
@@ -970,14 +1110,402 @@ __device__ void resolve_tree(const Params& p, int b, int g, int t0, int d0, Tree
   }
 }
 
+// ----------------------------------------------------------------------------
+// terminal draw of a stochastic request
+// ----------------------------------------------------------------------------
+
+// Terminal distribution of a stochastic request, taken by every helper from
+// its own copy of the decision.
+struct Term {
+  int kind;      // TermKind
+  int64_t trow;  // target row of the terminal distribution
+  int64_t drow;  // draft row (residual only)
+  float m_t;     // maximum of the target row (residual only)
+  float m_d;     // maximum of the draft row (residual only)
+  float k0;      // s_t / s_d from the statistics pass (residual only)
+  float Lhi;     // fl32(log2(e) / T) of the request
+};
+
+// Inclusive prefix sum over the workgroup in thread order; `total` gets the
+// sum of all threads.  All threads call.
+__device__ __forceinline__ double block_incl_scan_d(double v, double* sh, double& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const double x = wave_incl_scan_d(v);
+  __syncthreads();
+  if (lane == 63) sh[w] = x;
+  __syncthreads();
+  double before = 0.0, tot = 0.0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    if (k < w) before += sh[k];
+    tot += sh[k];
+  }
+  total = tot;
+  return before + x;
+}
+
+// Slice record of the draw: over the vocabulary elements of one slice,
+// a_y = 2^((t_y - m_t) L) and b_y = 2^((d_y - m_d) L) are p_y and q_y up to the
+// factors s_t, s_d; a residual record holds sum a, sum b and the same sums over
+// {y : a_y > k0 b_y}, the support of max(0, p - q).  A bonus record holds the
+// slice maximum m and sum_y 2^((t_y - m) L).
+template <int DT, bool RESID>
+__device__ __forceinline__ void draw_record(const uint4* qt, const uint4* qd, const Term& tm, PartC* dst,
+                                            DecideShared& sh) {
+  constexpr int P = Elem<DT>::P;
+  const float Lhi = tm.Lhi;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (RESID) {
+    double A = 0.0, Bs = 0.0, Ap = 0.0, Bp = 0.0;
+#pragma unroll
+    for (int k = 0; k < kUT; ++k) {
+      float vt[P], vd[P];
+      unpack<DT>(qt[k], vt);
+      unpack<DT>(qd[k], vd);
+      float sa = 0.f, sb = 0.f, sap = 0.f, sbp = 0.f;
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        const float a = ex2(vt[e] - tm.m_t, Lhi);
+        const float bb = ex2(vd[e] - tm.m_d, Lhi);
+        sa += a;
+        sb += bb;
+        const bool in = a > tm.k0 * bb;
+        sap += in ? a : 0.f;
+        sbp += in ? bb : 0.f;
+      }
+      A += (double)sa;
+      Bs += (double)sb;
+      Ap += (double)sap;
+      Bp += (double)sbp;
+    }
+    A = wave_sum_d(A);
+    Bs = wave_sum_d(Bs);
+    Ap = wave_sum_d(Ap);
+    Bp = wave_sum_d(Bp);
+    __syncthreads();  // thread 0 has read the previous slice's sums
+    if (lane == 0) {
+      sh.red_d4[0][w] = A;
+      sh.red_d4[1][w] = Bs;
+      sh.red_d4[2][w] = Ap;
+      sh.red_d4[3][w] = Bp;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double r[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        r[f] = sh.red_d4[f][0];
+#pragma unroll
+        for (int k = 1; k < kWaves; ++k) r[f] += sh.red_d4[f][k];
+      }
+      st_dev(&dst->a, r[0]);
+      st_dev(&dst->b, r[1]);
+      st_dev(&dst->ap, r[2]);
+      st_dev(&dst->bp, r[3]);
+    }
+  } else {
+    float vt[kUT * P];
+#pragma unroll
+    for (int k = 0; k < kUT; ++k) unpack<DT>(qt[k], vt + k * P);
+    float m = vt[0];
+#pragma unroll
+    for (int e = 1; e < kUT * P; ++e) m = fmaxf(m, vt[e]);
+    const float mc = block_max(m, sh.red_f);  // the slice starts inside the row: mc is a logit
+    double A = 0.0;
+#pragma unroll
+    for (int k = 0; k < kUT; ++k) {
+      float sa = 0.f;
+#pragma unroll
+      for (int e = 0; e < P; ++e) sa += ex2(vt[k * P + e] - mc, Lhi);
+      A += (double)sa;
+    }
+    A = block_sum_d(A, sh.red_d);
+    if (threadIdx.x == 0) {
+      st_dev(&dst->a, A);
+      st_dev(&dst->m, mc);
+    }
+  }
+}
+
+// Residual slice weight sum_{a > k0 b} (a - K b) = A+ - K B+, K = A/B, i.e.
+// max(0, p - q) in units of 1/A; `fb`: the fallback draw from p_j; bonus:
+// sum_y 2^((t_y - M) L) with M the row maximum.
+__device__ __forceinline__ double slice_weight(double a, double ap, double bp, float m, bool resid, bool fb, double K,
+                                               float M, double Ld) {
+  if (resid) return fb ? a : ap - K * bp;
+  return a * exp2(((double)m - (double)M) * Ld);
+}
+
+// Residual weight of one token (units of 1/A), or its bonus / fallback weight.
+__device__ __forceinline__ double token_weight(float t, float d, bool two, const Term& tm, float ref, float Lhi,
+                                               double K, double cf) {
+  const float a = ex2(t - ref, Lhi);
+  if (two) {
+    const float bb = ex2(d - tm.m_d, Lhi);
+    return (a > tm.k0 * bb) ? (double)a - K * (double)bb : 0.0;
+  }
+  return (double)a * cf;
+}
+
+// Token draw of request b by its last helper, from the H slice records (H =
+// slices per row):
+// y* = min{y : C_y > u * C_{V-1}} in ascending token order.  The records are
+// combined by workgroup-wide reductions and scans in slice order; the slice
+// holding the draw is read again and scanned token by token.
+template <int DT, bool VEC>
+__device__ __forceinline__ void draw_select(const Params& p, int b, const Term& tm, int H, DecideShared& sh) {
+  constexpr int P = Elem<DT>::P;
+  constexpr int64_t CHT = (int64_t)kThreads * kUT * P;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const PartC* rec = p.part_c + (int64_t)b * H;
+  const bool resid = tm.kind == kTermResidual;
+  const float Lhi = tm.Lhi;
+  const double Ld = (double)Lhi;
+  const bool cached = H <= kThreads;  // one record per thread, kept in registers
+  double ca = 0.0, cap = 0.0, cbp = 0.0;
+  float cm = -INFINITY;
+  double at = 0.0, bt = 0.0;
+  float M = -INFINITY;
+  for (int s = tid; s < H; s += kThreads) {
+    const double a = ld_dev(&rec[s].a);
+    const double bb = resid ? ld_dev(&rec[s].b) : 0.0;
+    const float m = resid ? 0.0f : ld_dev(&rec[s].m);
+    at += a;
+    bt += bb;
+    M = fmaxf(M, m);
+    if (cached) {
+      ca = a;
+      cap = resid ? ld_dev(&rec[s].ap) : 0.0;
+      cbp = resid ? ld_dev(&rec[s].bp) : 0.0;
+      cm = m;
+    }
+  }
+  // sum a, sum b and max m in one workgroup round
+  at = wave_sum_d(at);
+  bt = wave_sum_d(bt);
+  M = wave_max(M);
+  if (lane == 0) {
+    sh.red_d4[0][wv] = at;
+    sh.red_d4[1][wv] = bt;
+    sh.red_f[wv] = M;
+  }
+  __syncthreads();
+  at = sh.red_d4[0][0];
+  bt = sh.red_d4[1][0];
+  M = sh.red_f[0];
+#pragma unroll
+  for (int k = 1; k < kWaves; ++k) {
+    at += sh.red_d4[0][k];
+    bt += sh.red_d4[1][k];
+    M = fmaxf(M, sh.red_f[k]);
+  }
+  const double K = resid ? at / bt : 0.0;
+  double S = 0.0;
+  for (int s = tid; s < H; s += kThreads)
+    S += cached ? slice_weight(ca, cap, cbp, cm, resid, false, K, M, Ld)
+                : slice_weight(ld_dev(&rec[s].a), resid ? ld_dev(&rec[s].ap) : 0.0,
+                               resid ? ld_dev(&rec[s].bp) : 0.0, resid ? 0.0f : ld_dev(&rec[s].m), resid, false, K,
+                               M, Ld);
+  S = block_sum_d(S, sh.red_d);
+  bool fb = false;
+  if (resid && !(S > 0.0)) {
+    // max(0, p - q) vanished numerically: draw from p_j instead
+    fb = true;
+    S = at;
+  }
+  const double target = (double)p.ur[b] * S;
+
+  // the slice whose cumulative weight first exceeds the target: one round per
+  // kThreads consecutive slices
+  int cstar = -1, clast = -1;
+  double cbase = 0.0, carry = 0.0;
+  for (int r0 = 0; r0 < H; r0 += kThreads) {
+    const int s = r0 + tid;
+    double w = 0.0;
+    if (s < H)
+      w = cached ? slice_weight(ca, cap, cbp, cm, resid, fb, K, M, Ld)
+                 : slice_weight(ld_dev(&rec[s].a), resid ? ld_dev(&rec[s].ap) : 0.0,
+                                resid ? ld_dev(&rec[s].bp) : 0.0, resid ? 0.0f : ld_dev(&rec[s].m), resid, fb, K,
+                                M, Ld);
+    double tot;
+    const double incl = block_incl_scan_d(w, sh.red_d, tot);
+    const double excl = carry + incl - w;
+    const bool hit = w > 0.0 && excl <= target && target < excl + w;
+    // lowest hit, last slice with weight, and each slice's base, in one round
+    const int h1 = wave_min_int(hit ? s : INT_MAX), l1 = wave_max_int(w > 0.0 ? s : -1);
+    sh.st[tid] = excl;
+    if (lane == 0) {
+      sh.red_i[wv] = h1;
+      sh.red_i2[wv] = l1;
+    }
+    __syncthreads();
+    int first = sh.red_i[0], lp = sh.red_i2[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) {
+      first = min(first, sh.red_i[k]);
+      lp = max(lp, sh.red_i2[k]);
+    }
+    if (lp >= 0) clast = lp;
+    if (first != INT_MAX) {
+      cstar = first;
+      cbase = sh.st[first - r0];
+      break;
+    }
+    carry += tot;
+    __syncthreads();  // sh.st and the round's reductions are rewritten by the next round
+  }
+  const bool take_last = cstar < 0;  // rounding left the target at the end
+  if (take_last) {
+    cstar = clast >= 0 ? clast : H - 1;
+    cbase = 0.0;
+  }
+
+  // slice c* again: vector k of thread t holds tokens e_base + (k kThreads + t) P + [0, P)
+  const int64_t V = p.V;
+  const int64_t e_base = (int64_t)cstar * CHT;
+  const bool two = resid && !fb;
+  const float ref = resid ? tm.m_t : ld_dev(&rec[cstar].m);
+  const double cf = resid ? 1.0 : exp2(((double)ref - (double)M) * Ld);
+  uint4 qt[kUT], qd[kUT];
+#pragma unroll
+  for (int k = 0; k < kUT; ++k) {
+    const int64_t e0 = e_base + ((int64_t)k * kThreads + tid) * P;
+    qt[k] = fetch<DT, VEC>(p.target, tm.trow, V, e0);
+    qd[k] = two ? fetch<DT, VEC>(p.draft, tm.drow, V, e0) : qt[k];
+  }
+  // positions past the end hold the pad: a = 0 there, so their weight is 0.
+  // Vector k of thread t is unit k kThreads + t in token order; the unit
+  // whose cumulative range holds the target is found first, then only its P
+  // tokens are weighed again one by one.
+  double vsum[kUT], incl[kUT];
+  int lastpos = -1;  // the last token with a positive weight (the fallback)
+#pragma unroll
+  for (int k = 0; k < kUT; ++k) {
+    float vt[P], vd[P];
+    unpack<DT>(qt[k], vt);
+    unpack<DT>(qd[k], vd);
+    double sum = 0.0;
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      const double rv = token_weight(vt[e], vd[e], two, tm, ref, Lhi, K, cf);
+      sum += rv;
+      if (rv > 0.0) lastpos = (int)(e_base + ((int64_t)k * kThreads + tid) * P + e);
+    }
+    vsum[k] = sum;
+    incl[k] = wave_incl_scan_d(sum);
+  }
+  __syncthreads();  // sh.red_d4 was last read before the slice scan
+  if (lane == 63) {
+#pragma unroll
+    for (int k = 0; k < kUT; ++k) sh.red_d4[k][wv] = incl[k];
+  }
+  __syncthreads();
+  int unit = INT_MAX;
+  double ubase = 0.0, run = cbase;
+#pragma unroll
+  for (int k = 0; k < kUT; ++k) {
+    double before = 0.0, tot = 0.0;
+#pragma unroll
+    for (int q = 0; q < kWaves; ++q) {
+      if (q < wv) before += sh.red_d4[k][q];
+      tot += sh.red_d4[k][q];
+    }
+    const double cum = run + (before + incl[k]) - vsum[k];
+    run += tot;
+    if (!take_last && unit == INT_MAX && cum <= target && cum + vsum[k] > target) {
+      unit = k * kThreads + tid;
+      ubase = cum;
+    }
+  }
+  // lowest unit holding the target and the last positive token, in one round
+  const int u1 = wave_min_int(unit), y1 = wave_max_int(lastpos);
+  __syncthreads();  // sh.red_i / red_i2 were read in the slice scan
+  if (lane == 0) {
+    sh.red_i[wv] = u1;
+    sh.red_i2[wv] = y1;
+  }
+  __syncthreads();
+  int ustar = sh.red_i[0], ylast = sh.red_i2[0];
+#pragma unroll
+  for (int k = 1; k < kWaves; ++k) {
+    ustar = min(ustar, sh.red_i[k]);
+    ylast = max(ylast, sh.red_i2[k]);
+  }
+  // the thread that owns the unit (thread 0 when there is none) writes the token
+  const bool writer = ustar != INT_MAX ? unit == ustar : tid == 0;
+  if (writer) {
+    int y = INT_MAX;
+    if (ustar != INT_MAX) {
+      // select the unit's vector without dynamic register indexing
+      const int ku = ustar / kThreads;
+      uint4 wt = qt[0], wd = qd[0];
+#pragma unroll
+      for (int k = 1; k < kUT; ++k)
+        if (k == ku) {
+          wt = qt[k];
+          wd = qd[k];
+        }
+      float vt[P], vd[P];
+      unpack<DT>(wt, vt);
+      unpack<DT>(wd, vd);
+      double cum = ubase;
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        cum += token_weight(vt[e], vd[e], two, tm, ref, Lhi, K, cf);
+        if (y == INT_MAX && cum > target) y = (int)(e_base + (int64_t)ustar * P + e);
+      }
+    }
+    if (y == INT_MAX) y = ylast;
+    if (y < 0 || y >= p.V) y = (int)min(V - 1, e_base);
+    p.out_tokens[tm.trow] = y;
+    if (p.out_resid) p.out_resid[b] = two ? (float)(S / at) : 1.0f;
+  }
+}
+
+// Second-pass KL values of a request from the helpers' slice sums, added in
+// slice order; NKL mode also takes the decision here.
+template <int MODE>
+__device__ __forceinline__ void kl_finish(const Params& p, int b, int t0, int d0, int g, int H, DecideShared& sh) {
+  const double lnV = log((double)p.V);
+  int first = INT_MAX;
+  for (int i = threadIdx.x; i < g; i += kThreads) {
+    const int pos = d0 + i;
+    double kl = ld_dev(&p.kl_val[pos]);
+    const bool need = ld_dev(&p.kl_need[pos]) != 0;
+    if (need) {
+      kl = 0.0;
+      for (int h = 0; h < H; ++h) kl += ld_dev(&p.kl_part[(int64_t)pos * H + h]);
+    }
+    const double nkl = p.V > 1 ? kl / lnV : 0.0;
+    if (need) p.out_nkl[pos] = (float)nkl;  // the other positions were written by helper 0
+    if (!(nkl < (double)p.delta)) first = min(first, i);
+  }
+  if (MODE == SV_MODE_NKL) {
+    const int j0 = block_min_int(first, sh.red_i);
+    const int j = j0 == INT_MAX ? g : j0;
+    for (int k = threadIdx.x; k <= g; k += kThreads)
+      p.out_tokens[t0 + k] = k < j ? p.tokens[d0 + k] : (k == j ? ld_dev(&p.tidx[t0 + j]) : -1);
+    if (threadIdx.x == 0) p.out_num[b] = j;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// k_decide
+// ----------------------------------------------------------------------------
+
 template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads) void k_decide(Params p) {
+__global__ __launch_bounds__(kThreads, 3) void k_decide(Params p) {
   constexpr bool SOFT = MODE == SV_MODE_STOCHASTIC || MODE == SV_MODE_NKL;
   __shared__ DecideShared sh;
   __shared__ TreeShared<MODE> tr;
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int H = p.helpers, NS = p.nslices;
+  const int b = (int)(blockIdx.x % (unsigned)p.B);
+  const int h = (int)(blockIdx.x / (unsigned)p.B);
+  // helper h streams slices [s0, s1) wherever rows get a second look
+  const int s0 = h * p.slices_per_helper, s1 = min(NS, s0 + p.slices_per_helper);
+  const bool writer = h == 0;  // helper 0 writes the outputs of the decision
+  const int tid = threadIdx.x;
   const bool want_kl = SOFT && p.want_kl;
-  if (want_kl && tid == 0) p.pending[b] = 0;
   // independent loads first, so that they are in flight together
   const int hdr = p.hdr[0];
   const int d0 = p.d_off[b];
@@ -985,10 +1513,7 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
   const float T = SOFT ? p.temp[b] : 1.0f;
   const float ur = MODE == SV_MODE_STOCHASTIC ? p.ur[b] : 0.0f;
   if (hdr != 0) {  // layout error: only the counts are written
-    if (tid == 0) {
-      p.out_num[b] = -1;
-      if (MODE == SV_MODE_STOCHASTIC) p.term[b].kind = kTermNone;
-    }
+    if (writer && tid == 0) p.out_num[b] = -1;
     return;
   }
   const int g = d1 - d0;
@@ -999,7 +1524,7 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
   // (which only read inside the rows for valid token ids), and overwrite
   // everything the passes wrote if they fail
   if (g > p.max_gamma || (SOFT && !temp_ok(T)) || (MODE == SV_MODE_STOCHASTIC && !unit_ok(ur))) {
-    finish_invalid(p, b, t0, d0, g);
+    if (writer) finish_invalid(p, b, t0, d0, g);
     return;
   }
 
@@ -1050,7 +1575,7 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
       sh.st[q] = r.st;
       sh.sd[q] = r.sd;
       sh.idx[q] = idx;
-      if (MODE == SV_MODE_NKL) p.tidx[t0 + ti] = idx;
+      if (MODE == SV_MODE_NKL && writer) st_dev(&p.tidx[t0 + ti], idx);
       int acc = 0, need = 0;
       double kl = 0.0;  // KL(q||p) = 0 for V == 1: both rows are the same point mass
       if (pair) {
@@ -1058,8 +1583,8 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
         // relative error of p(x), q(x) and alpha stays near 1e-7)
         const float lpx = (tx - r.mt) * Lhi - __log2f((float)r.st);
         const float lqx = (dx - r.md) * Lhi - __log2f((float)r.sd);
-        if (p.out_p_x) p.out_p_x[d0 + ti] = exp2f(lpx);
-        if (p.out_q_x) p.out_q_x[d0 + ti] = exp2f(lqx);
+        if (writer && p.out_p_x) p.out_p_x[d0 + ti] = exp2f(lpx);
+        if (writer && p.out_q_x) p.out_q_x[d0 + ti] = exp2f(lqx);
         if (MODE == SV_MODE_STOCHASTIC) acc = u <= fminf(1.0f, exp2f(lpx - lqx)) ? 1 : 0;
         if (want_kl && p.V > 1) {
           // KL(q||p) = E_q[d - t]/T - (m_d - m_t)/T - log(s_d / s_t)
@@ -1078,32 +1603,76 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
       sh.need[q] = need;
     }
     __syncthreads();
-    if (want_kl && tid < TPP && base + tid < g) {
-      // positions whose one-pass KL is not accurate enough are queued for the
-      // grid-wide second pass; the request then waits for k_finish
-      const int pos = d0 + base + tid;
-      const int need = sh.need[tid];
-      p.kl_need[pos] = need;
-      p.kl_val[pos] = sh.kl1[tid];
-      if (need) {
-        RefIn ri;
-        ri.s_t = sh.st[tid];
-        ri.s_d = sh.sd[tid];
-        ri.m_t = sh.mt[tid];
-        ri.m_d = sh.md[tid];
-        ri.Lhi = Lhi;
-        ri.trow = t0 + base + tid;
-        p.ref_in[pos] = ri;
-        p.ref_list[atomicAdd(p.hdr + 1, 1)] = pos;
-        any_need = true;
-        if (MODE == SV_MODE_NKL) sh.acc[tid] = 0;
-      } else {
-        const double nkl = p.V > 1 ? sh.kl1[tid] / lnV : 0.0;
-        if (p.out_nkl) p.out_nkl[pos] = (float)nkl;
-        if (MODE == SV_MODE_NKL) sh.acc[tid] = nkl < (double)p.delta ? 1 : 0;
+    if (want_kl) {
+      if (tid < TPP && base + tid < g) {
+        const int pos = d0 + base + tid;
+        const int need = sh.need[tid];
+        if (writer) {
+          st_dev(&p.kl_need[pos], need);
+          st_dev(&p.kl_val[pos], sh.kl1[tid]);
+        }
+        if (need) {
+          any_need = true;
+          if (MODE == SV_MODE_NKL) sh.acc[tid] = 0;  // decided by the last helper
+        } else {
+          const double nkl = p.V > 1 ? sh.kl1[tid] / lnV : 0.0;
+          if (writer && p.out_nkl) p.out_nkl[pos] = (float)nkl;
+          if (MODE == SV_MODE_NKL) sh.acc[tid] = nkl < (double)p.delta ? 1 : 0;
+        }
+      }
+      __syncthreads();
+      // this helper's slices of the second pass, for the positions of this
+      // pass whose one-pass KL is not accurate enough: items (position,
+      // slice) stream with the loads of the next item in flight
+      const int npos = min(TPP, g - base);
+      int nneed = 0;
+      for (int k = 0; k < npos; ++k)
+        if (sh.need[k]) sh.list[nneed++] = k;  // every thread builds the same list
+      const int nsl = s1 - s0;
+      const int nitem = nneed * nsl;
+      if (nitem > 0) {
+        const auto rows = [&](int it, int64_t& tr, int64_t& dr, int& sl) {
+          const int k = sh.list[it / nsl];
+          tr = t0 + base + k;
+          dr = d0 + base + k;
+          sl = s0 + it % nsl;
+        };
+        uint4 at[kUT], ad[kUT], bt[kUT], bd[kUT];
+        double acc = 0.0;
+        const auto consume = [&](const uint4* qt, const uint4* qd, int it) {
+          const int k = sh.list[it / nsl];
+          KlIn ri;
+          ri.m_t = sh.mt[k];
+          ri.m_d = sh.md[k];
+          ri.lr = (float)log(sh.sd[k] / sh.st[k]);
+          ri.inv_st = (float)(1.0 / sh.st[k]);
+          ri.inv_sd = (float)(1.0 / sh.sd[k]);
+          acc += kl_terms<DT>(qt, qd, ri, Lhi);
+          if (it % nsl == nsl - 1) {  // the position's last slice of this helper
+            const double v = block_sum_d(acc, sh.red_d);
+            if (tid == 0) st_dev(&p.kl_part[(int64_t)(d0 + base + k) * H + h], v);
+            acc = 0.0;
+          }
+        };
+        int64_t tr, dr;
+        int sl;
+        rows(0, tr, dr, sl);
+        slice_issue<DT, VEC, true>(p, tr, dr, sl, at, ad);
+        for (int it = 0; it < nitem; it += 2) {
+          if (it + 1 < nitem) {
+            rows(it + 1, tr, dr, sl);
+            slice_issue<DT, VEC, true>(p, tr, dr, sl, bt, bd);
+          }
+          consume(at, ad, it);
+          if (it + 1 >= nitem) break;
+          if (it + 2 < nitem) {
+            rows(it + 2, tr, dr, sl);
+            slice_issue<DT, VEC, true>(p, tr, dr, sl, at, ad);
+          }
+          consume(bt, bd, it + 1);
+        }
       }
     }
-    if (want_kl) __syncthreads();
     if (MODE != SV_MODE_TREE_GREEDY) {
       const int cand = (tid < TPP && base + tid < ntask && !sh.acc[tid]) ? base + tid : INT_MAX;
       const int jp = block_min_int(cand, sh.red_i);
@@ -1137,429 +1706,57 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
     if (!ok) bad = true;
   }
   if (__syncthreads_or(bad)) {
-    finish_invalid(p, b, t0, d0, g);
+    if (writer) finish_invalid(p, b, t0, d0, g);
     return;
   }
   if constexpr (MODE == SV_MODE_TREE_GREEDY) {
     resolve_tree(p, b, g, t0, d0, tr, sh);
     return;
   }
-  if (want_kl && __syncthreads_or(any_need)) {
-    if (tid == 0) p.pending[b] = 1;
-    if (MODE == SV_MODE_NKL) return;  // the decision needs the second-pass values: k_finish
+  const bool need_any = want_kl && __syncthreads_or(any_need);
+  if (MODE == SV_MODE_NKL && need_any) {
+    // the decision needs second-pass values: the last helper takes it
+    if (arrive_last(p.cnt + b, H, sh)) kl_finish<MODE>(p, b, t0, d0, g, H, sh);
+    return;
   }
   if (j < 0) j = g;  // stochastic: every draft accepted
-  for (int k = tid; k <= g; k += kThreads) {
-    if (k < j) p.out_tokens[t0 + k] = p.tokens[d0 + k];
-    else if (k > j) p.out_tokens[t0 + k] = -1;
-    else if (MODE != SV_MODE_STOCHASTIC) p.out_tokens[t0 + k] = jidx;  // stochastic: the draw pass writes it
-  }
-  if (tid == 0) {
-    p.out_num[b] = j;
-    if (MODE == SV_MODE_STOCHASTIC) {
-      Term tm;
-      tm.j = j;
-      tm.trow = t0 + j;
-      tm.Lhi = Lhi;
-      if (j < g) {
-        tm.kind = kTermResidual;
-        tm.drow = d0 + j;
-        tm.m_t = jm_t;
-        tm.m_d = jm_d;
-        tm.k0 = (float)(js_t / js_d);
-      } else {
-        tm.kind = kTermBonus;
-        tm.drow = -1;
-        tm.m_t = tm.m_d = tm.k0 = 0.0f;
-      }
-      p.term[b] = tm;
+  if (writer) {
+    for (int k = tid; k <= g; k += kThreads) {
+      if (k < j) p.out_tokens[t0 + k] = p.tokens[d0 + k];
+      else if (k > j) p.out_tokens[t0 + k] = -1;
+      else if (MODE != SV_MODE_STOCHASTIC) p.out_tokens[t0 + k] = jidx;  // stochastic: the draw writes it
     }
-  }
-}
-
-// ----------------------------------------------------------------------------
-// k_refine and k_finish (when KL values are computed)
-//
-// k_refine: the queued positions x chunks are split into contiguous ranges,
-// one per workgroup; every (position, chunk) sum is written to its own slot,
-// so the values do not depend on the queue order.  k_finish: one workgroup
-// per request that waits for second-pass values adds the chunk sums in chunk
-// order, writes the NKL values and, in NKL mode, the decision.
-// ----------------------------------------------------------------------------
-
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_refine(Params p) {
-  __shared__ double shd[kWaves];
-  constexpr int64_t CHR = (int64_t)kThreads * kUR * Elem<DT>::P;
-  const int64_t N = (int64_t)p.hdr[1] * p.nch_r;
-  const int G = (int)gridDim.x, wg = (int)blockIdx.x;
-  const int64_t i_end = (int64_t)(wg + 1) * N / G;
-  for (int64_t i = (int64_t)wg * N / G; i < i_end; ++i) {
-    const int k = (int)(i / p.nch_r);
-    const int c = (int)(i - (int64_t)k * p.nch_r);
-    const int pos = p.ref_list[k];
-    const RefIn ri = p.ref_in[pos];
-    const double v = kl_chunk<DT, VEC>(p, ri, pos, (int64_t)c * CHR, shd);
-    if (threadIdx.x == 0) p.kl_part[(int64_t)pos * p.nch_r + c] = v;
-  }
-}
-
-template <int MODE>
-__global__ __launch_bounds__(kThreads) void k_finish(Params p) {
-  __shared__ int red[kWaves];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  if (!p.pending[b]) return;
-  const int d0 = p.d_off[b];
-  const int g = p.d_off[b + 1] - d0;
-  const int t0 = d0 + b;
-  const double lnV = log((double)p.V);
-  int first = INT_MAX;
-  for (int i = tid; i < g; i += kThreads) {
-    const int pos = d0 + i;
-    double kl = p.kl_val[pos];
-    if (p.kl_need[pos]) {
-      kl = 0.0;
-      for (int c = 0; c < p.nch_r; ++c) kl += p.kl_part[(int64_t)pos * p.nch_r + c];
-    }
-    const double nkl = p.V > 1 ? kl / lnV : 0.0;
-    p.out_nkl[pos] = (float)nkl;
-    if (!(nkl < (double)p.delta)) first = min(first, i);
-  }
-  if (MODE == SV_MODE_NKL) {
-    const int j0 = block_min_int(first, red);
-    const int j = j0 == INT_MAX ? g : j0;
-    for (int k = tid; k <= g; k += kThreads)
-      p.out_tokens[t0 + k] = k < j ? p.tokens[d0 + k] : (k == j ? p.tidx[t0 + j] : -1);
     if (tid == 0) p.out_num[b] = j;
   }
-}
-
-// ----------------------------------------------------------------------------
-// k_draw and k_select (stochastic mode)
-//
-// k_draw: items are (request, wave-chunk) pairs numbered b * nch_c + c; a
-// wave-chunk is 64 lanes x kUC 16-byte vectors of the terminal row (and of the
-// draft row for a residual).  Every wave of the grid streams a contiguous
-// range of items on its own, without workgroup barriers, and writes one record
-// of float64 sums per item.  k_select: one wave per request combines the
-// records, picks the wave-chunk holding the draw and re-reads it.
-// ----------------------------------------------------------------------------
-
-__device__ __forceinline__ double wave_incl_scan_d(double v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-
-// Record of one wave-chunk: a_y = 2^((t_y - m_t) L) and b_y = 2^((d_y - m_d) L)
-// are p_y and q_y up to the factors s_t, s_d; the residual record also holds
-// the sums over {y : a_y > k0 b_y}, the support of max(0, p - q).  A bonus
-// record holds the chunk maximum and sum_y 2^((t_y - m_c) L).
-template <int DT, bool RESID>
-__device__ __forceinline__ void draw_record(const Vecs<kUC>& qt, const Vecs<kUC>& qd, const Term& tm, float Lhi,
-                                            PartC* dst) {
-  constexpr int P = Elem<DT>::P;
-  double A = 0.0, Bs = 0.0, Ap = 0.0, Bp = 0.0;
-  float mc = 0.f;
-  if (RESID) {
-#pragma unroll
-    for (int k = 0; k < kUC; ++k) {
-      float vt[P], vd[P];
-      unpack<DT>(qt.v[k], vt);
-      unpack<DT>(qd.v[k], vd);
-      float sa = 0.f, sb = 0.f, sap = 0.f, sbp = 0.f;
-#pragma unroll
-      for (int e = 0; e < P; ++e) {
-        const float a = ex2(vt[e] - tm.m_t, Lhi);
-        const float bb = ex2(vd[e] - tm.m_d, Lhi);
-        sa += a;
-        sb += bb;
-        const bool in = a > tm.k0 * bb;
-        sap += in ? a : 0.f;
-        sbp += in ? bb : 0.f;
-      }
-      A += (double)sa;
-      Bs += (double)sb;
-      Ap += (double)sap;
-      Bp += (double)sbp;
+  if constexpr (MODE == SV_MODE_STOCHASTIC) {
+    Term tm;
+    tm.trow = t0 + j;
+    tm.Lhi = Lhi;
+    if (j < g) {
+      tm.kind = kTermResidual;
+      tm.drow = d0 + j;
+      tm.m_t = jm_t;
+      tm.m_d = jm_d;
+      tm.k0 = (float)(js_t / js_d);
+    } else {
+      tm.kind = kTermBonus;
+      tm.drow = -1;
+      tm.m_t = tm.m_d = tm.k0 = 0.0f;
     }
-    A = wave_sum_d(A);
-    Bs = wave_sum_d(Bs);
-    Ap = wave_sum_d(Ap);
-    Bp = wave_sum_d(Bp);
-  } else {
-    float vt[kUC * P];
-#pragma unroll
-    for (int k = 0; k < kUC; ++k) unpack<DT>(qt.v[k], vt + k * P);
-    float m = vt[0];
-#pragma unroll
-    for (int e = 1; e < kUC * P; ++e) m = fmaxf(m, vt[e]);
-    mc = wave_max(m);  // a wave-chunk starts inside the row: mc is a logit
-#pragma unroll
-    for (int k = 0; k < kUC; ++k) {
-      float sa = 0.f;
-#pragma unroll
-      for (int e = 0; e < P; ++e) sa += ex2(vt[k * P + e] - mc, Lhi);
-      A += (double)sa;
-    }
-    A = wave_sum_d(A);
-  }
-  if ((threadIdx.x & 63) == 0) {  // plain stores: the reader is the next kernel
-    dst->a = A;
-    dst->b = Bs;
-    dst->ap = Ap;
-    dst->bp = Bp;
-    dst->m = mc;
-  }
-}
-
-template <int DT, bool VEC, bool RESID>
-__device__ __forceinline__ void draw_issue(const Params& p, const Term& tm, int64_t e_chunk, Vecs<kUC>& qt,
-                                           Vecs<kUC>& qd) {
-  constexpr int P = Elem<DT>::P;
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int k = 0; k < kUC; ++k) {
-    const int64_t e0 = e_chunk + ((int64_t)k * 64 + lane) * P;
-    qt.v[k] = fetch<DT, VEC>(p.target, tm.trow, p.V, e0);
-    if (RESID) qd.v[k] = fetch<DT, VEC>(p.draft, tm.drow, p.V, e0);
-  }
-}
-
-// Streams wave-chunks [c0, c1) of request b (loads of chunk c + 1 in flight
-// while chunk c is reduced).
-template <int DT, bool VEC, bool RESID>
-__device__ __forceinline__ void draw_segment(const Params& p, int b, const Term& tm, int c0, int c1, float Lhi) {
-  constexpr int64_t CHW = (int64_t)64 * kUC * Elem<DT>::P;
-  PartC* rec = p.part_c + (int64_t)b * p.nch_c;
-  Vecs<kUC> ct, cd;
-  draw_issue<DT, VEC, RESID>(p, tm, (int64_t)c0 * CHW, ct, cd);
-  for (int c = c0; c < c1 - 1; ++c) {
-    Vecs<kUC> nt, nd;
-    draw_issue<DT, VEC, RESID>(p, tm, (int64_t)(c + 1) * CHW, nt, nd);
-    draw_record<DT, RESID>(ct, cd, tm, Lhi, rec + c);
-    ct = nt;
-    cd = nd;
-  }
-  draw_record<DT, RESID>(ct, cd, tm, Lhi, rec + (c1 - 1));
-}
-
-// Residual chunk weight sum_{a > k0 b} (a - K b) = A+ - K B+, K = A/B, i.e.
-// max(0, p - q) in units of 1/A; `fb`: the fallback draw from p_j; bonus:
-// sum_y 2^((t_y - M) L) with M the row maximum.
-__device__ __forceinline__ double chunk_weight(double a, double ap, double bp, float m, bool resid, bool fb, double K,
-                                               float M, double Ld) {
-  if (resid) return fb ? a : ap - K * bp;
-  return a * exp2(((double)m - (double)M) * Ld);
-}
-
-// Residual weight of one token (units of 1/A), or its bonus / fallback weight.
-__device__ __forceinline__ double token_weight(float t, float d, bool two, const Term& tm, float ref, float Lhi,
-                                               double K, double cf) {
-  const float a = ex2(t - ref, Lhi);
-  if (two) {
-    const float bb = ex2(d - tm.m_d, Lhi);
-    return (a > tm.k0 * bb) ? (double)a - K * (double)bb : 0.0;
-  }
-  return (double)a * cf;
-}
-
-// Token draw of request b by one wave.  CACHED: the request has at most 256
-// records; their fields are kept in registers (4 per lane) instead of being
-// read again for each sweep.  Records are combined by fixed wave-wide
-// reductions and scans in chunk order.
-template <int DT, bool VEC, bool CACHED>
-__device__ __forceinline__ void draw_select(const Params& p, int b, const Term& tm, float Lhi) {
-  constexpr int P = Elem<DT>::P;
-  constexpr int NE = kUC * P;
-  constexpr int64_t CHW = (int64_t)64 * NE;
-  constexpr int R = CACHED ? 4 : 1;
-  const int lane = threadIdx.x & 63;
-  const int nch = p.nch_c;
-  PartC* pcs = p.part_c + (int64_t)b * nch;
-  const bool resid = tm.kind == kTermResidual;
-  const double Ld = (double)Lhi;
-  double ca[R], cap[R], cbp[R];
-  float cm[R];
-  double at = 0.0, bt = 0.0;
-  float M = -INFINITY;
-  if constexpr (CACHED) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int ch = lane + 64 * r;
-      ca[r] = cap[r] = cbp[r] = 0.0;
-      cm[r] = -INFINITY;
-      if (ch < nch) {
-        const PartC q = pcs[ch];
-        ca[r] = q.a;
-        cap[r] = q.ap;
-        cbp[r] = q.bp;
-        cm[r] = q.m;
-        at += q.a;
-        bt += q.b;
-        M = fmaxf(M, q.m);
-      }
-    }
-  } else {
-    for (int ch = lane; ch < nch; ch += 64) {
-      const PartC q = pcs[ch];
-      at += q.a;
-      bt += q.b;
-      M = fmaxf(M, q.m);
+    PartC* rec = p.part_c + (int64_t)b * NS;
+    if (tm.kind == kTermResidual)
+      slice_stream<DT, VEC, true>(p, tm.trow, tm.drow, s0, s1, [&](const uint4* qt, const uint4* qd, int sl) {
+        draw_record<DT, true>(qt, qd, tm, rec + sl, sh);
+      });
+    else
+      slice_stream<DT, VEC, false>(p, tm.trow, tm.drow, s0, s1, [&](const uint4* qt, const uint4* qd, int sl) {
+        draw_record<DT, false>(qt, qd, tm, rec + sl, sh);
+      });
+    if (arrive_last(p.cnt + b, H, sh)) {
+      draw_select<DT, VEC>(p, b, tm, NS, sh);
+      if (need_any) kl_finish<MODE>(p, b, t0, d0, g, H, sh);
     }
   }
-  at = wave_sum_d(at);
-  bt = wave_sum_d(bt);
-  M = wave_max(M);
-  const double K = resid ? at / bt : 0.0;
-  double S = 0.0;
-  if constexpr (CACHED) {
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-      if (lane + 64 * r < nch) S += chunk_weight(ca[r], cap[r], cbp[r], cm[r], resid, false, K, M, Ld);
-  } else {
-    for (int ch = lane; ch < nch; ch += 64) {
-      const PartC q = pcs[ch];
-      S += chunk_weight(q.a, q.ap, q.bp, q.m, resid, false, K, M, Ld);
-    }
-  }
-  S = wave_sum_d(S);
-  bool fb = false;
-  if (resid && !(S > 0.0)) {
-    // max(0, p - q) vanished numerically: draw from p_j instead
-    fb = true;
-    S = at;
-  }
-  const double target = (double)p.ur[b] * S;
-
-  // the wave-chunk whose cumulative weight first exceeds the target: one
-  // round per 64 consecutive chunks
-  int cstar = -1, clast = -1;
-  double cbase = 0.0, carry = 0.0;
-  const int rounds = (nch + 63) / 64;
-  for (int r = 0; r < rounds; ++r) {
-    const int ch = lane + 64 * r;
-    double w = 0.0;
-    if (ch < nch) {
-      if constexpr (CACHED) {
-        // r < R here; select the round's register without dynamic indexing
-        double a = ca[0], ap = cap[0], bp = cbp[0];
-        float m = cm[0];
-#pragma unroll
-        for (int k = 1; k < R; ++k)
-          if (r == k) {
-            a = ca[k];
-            ap = cap[k];
-            bp = cbp[k];
-            m = cm[k];
-          }
-        w = chunk_weight(a, ap, bp, m, resid, fb, K, M, Ld);
-      } else {
-        const PartC q = pcs[ch];
-        w = chunk_weight(q.a, q.ap, q.bp, q.m, resid, fb, K, M, Ld);
-      }
-    }
-    const double incl = wave_incl_scan_d(w);
-    const double excl = carry + incl - w;
-    const bool hit = w > 0.0 && excl <= target && target < excl + w;
-    const int first = wave_min_int(hit ? ch : INT_MAX);
-    const int lp = wave_max_int(w > 0.0 ? ch : -1);
-    if (lp >= 0) clast = lp;
-    if (first != INT_MAX) {
-      cstar = first;
-      cbase = __shfl(excl, first - 64 * r, 64);
-      break;
-    }
-    carry += __shfl(incl, 63, 64);
-  }
-  const bool take_last = cstar < 0;  // rounding left the target at the end
-  if (take_last) {
-    cstar = clast >= 0 ? clast : nch - 1;
-    cbase = 0.0;
-  }
-
-  // re-read wave-chunk c*: lane l owns NE consecutive tokens
-  const int64_t V = p.V;
-  const int64_t y0 = (int64_t)cstar * CHW + (int64_t)lane * NE;
-  const bool two = resid && !fb;
-  const float ref = resid ? tm.m_t : pcs[cstar].m;
-  const double cf = resid ? 1.0 : exp2(((double)ref - (double)M) * Ld);
-  Vecs<kUC> qt, qd;
-#pragma unroll
-  for (int k = 0; k < kUC; ++k) {
-    qt.v[k] = fetch<DT, VEC>(p.target, tm.trow, V, y0 + k * P);
-    qd.v[k] = two ? fetch<DT, VEC>(p.draft, tm.drow, V, y0 + k * P) : qt.v[k];
-  }
-  // positions past the end hold the pad: a = 0 there, so their weight is 0
-  double tsum = 0.0;
-#pragma unroll
-  for (int k = 0; k < kUC; ++k) {
-    float vt[P], vd[P];
-    unpack<DT>(qt.v[k], vt);
-    unpack<DT>(qd.v[k], vd);
-#pragma unroll
-    for (int e = 0; e < P; ++e) tsum += token_weight(vt[e], vd[e], two, tm, ref, Lhi, K, cf);
-  }
-  double cum = cbase + (wave_incl_scan_d(tsum) - tsum);
-  const bool mine = !take_last && cum <= target && cum + tsum > target;
-  int cand = INT_MAX, lastpos = -1;
-#pragma unroll
-  for (int k = 0; k < kUC; ++k) {
-    float vt[P], vd[P];
-    unpack<DT>(qt.v[k], vt);
-    unpack<DT>(qd.v[k], vd);
-#pragma unroll
-    for (int e = 0; e < P; ++e) {
-      const double rv = token_weight(vt[e], vd[e], two, tm, ref, Lhi, K, cf);
-      const int y = (int)(y0 + k * P + e);
-      if (rv > 0.0) lastpos = y;
-      if (mine && cand == INT_MAX) {
-        cum += rv;
-        if (cum > target) cand = y;
-      }
-    }
-  }
-  const int ystar = wave_min_int(cand);
-  const int ylast = wave_max_int(lastpos);
-  if (lane == 0) {
-    int y = ystar != INT_MAX ? ystar : ylast;
-    if (y < 0 || y >= p.V) y = (int)min(V - 1, (int64_t)cstar * CHW);
-    p.out_tokens[tm.trow] = y;
-    if (p.out_resid) p.out_resid[b] = two ? (float)(S / at) : 1.0f;
-  }
-}
-
-// A layout error leaves every Term at kTermNone: nothing to draw.
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_draw(Params p) {
-  const int W = (int)gridDim.x * kWaves;
-  const int wave = (int)blockIdx.x * kWaves + (int)(threadIdx.x >> 6);
-  const int64_t N = (int64_t)p.B * p.nch_c;
-  int64_t i = (int64_t)wave * N / W;
-  const int64_t i_end = (int64_t)(wave + 1) * N / W;
-  while (i < i_end) {
-    const int b = (int)(i / p.nch_c);
-    const int c0 = (int)(i - (int64_t)b * p.nch_c);
-    const int c1 = (int)min((int64_t)p.nch_c, c0 + (i_end - i));
-    i += c1 - c0;
-    const Term tm = p.term[b];
-    if (tm.kind == kTermResidual) draw_segment<DT, VEC, true>(p, b, tm, c0, c1, tm.Lhi);
-    else if (tm.kind == kTermBonus) draw_segment<DT, VEC, false>(p, b, tm, c0, c1, tm.Lhi);
-  }
-}
-
-// one wave (workgroup of 64) per request
-template <int DT, bool VEC>
-__global__ __launch_bounds__(64) void k_select(Params p) {
-  const int b = blockIdx.x;
-  const Term tm = p.term[b];
-  if (tm.kind == kTermNone) return;
-  if (p.nch_c <= 256) draw_select<DT, VEC, true>(p, b, tm, tm.Lhi);
-  else draw_select<DT, VEC, false>(p, b, tm, tm.Lhi);
 }
 
 }  // namespace
@@ -1603,17 +1800,6 @@ int stats_occupancy() {
 }
 
 template <int DT, bool VEC>
-int draw_occupancy() {
-  static int occ = 0;
-  if (occ == 0) {
-    int o = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, k_draw<DT, VEC>, kThreads, 0) != hipSuccess || o <= 0) o = 1;
-    occ = o;
-  }
-  return occ;
-}
-
-template <int DT, bool VEC>
 int stats_occupancy_mode(int mode, bool wz) {
   switch (mode) {
     case SV_MODE_STOCHASTIC:
@@ -1651,7 +1837,7 @@ void stats_dispatch(const Params& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1
 }
 template <int DT, bool VEC>
 void decide_dispatch(const Params& p, hipStream_t s) {
-  const dim3 grid(p.B), blk(kThreads);
+  const dim3 grid((unsigned)((int64_t)p.B * p.helpers)), blk(kThreads);
   switch (p.mode) {
     case SV_MODE_STOCHASTIC: hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_STOCHASTIC>), grid, blk, 0, s, p); break;
     case SV_MODE_GREEDY: hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_GREEDY>), grid, blk, 0, s, p); break;
@@ -1661,6 +1847,51 @@ void decide_dispatch(const Params& p, hipStream_t s) {
 }
 
 }  // namespace
+
+// Helpers per request: enough workgroups to fill the device once (resident
+// k_decide workgroups / B), at most one per slice; each helper then streams a
+// contiguous run of slices.
+template <int DT, bool VEC, int MODE>
+int decide_capacity() {
+  static int occ = 0;  // same value from every thread: a race is benign
+  if (occ == 0) {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, k_decide<DT, VEC, MODE>, kThreads, 0) != hipSuccess || o <= 0)
+      o = 1;
+    occ = o;
+  }
+  return occ * num_cus();
+}
+
+int plan_decide(Params& p, bool vec) {
+  p.nslices = (int32_t)((p.V + chunk_t(p.dtype) - 1) / chunk_t(p.dtype));
+  if (p.mode != SV_MODE_STOCHASTIC && p.mode != SV_MODE_NKL) {
+    p.helpers = 1;
+    p.slices_per_helper = p.nslices;
+    return 0;
+  }
+  int cap;
+  const bool st = p.mode == SV_MODE_STOCHASTIC;
+  if (p.dtype == SV_DTYPE_BF16)
+    cap = vec ? (st ? decide_capacity<SV_DTYPE_BF16, true, SV_MODE_STOCHASTIC>()
+                    : decide_capacity<SV_DTYPE_BF16, true, SV_MODE_NKL>())
+              : (st ? decide_capacity<SV_DTYPE_BF16, false, SV_MODE_STOCHASTIC>()
+                    : decide_capacity<SV_DTYPE_BF16, false, SV_MODE_NKL>());
+  else
+    cap = vec ? (st ? decide_capacity<SV_DTYPE_F32, true, SV_MODE_STOCHASTIC>()
+                    : decide_capacity<SV_DTYPE_F32, true, SV_MODE_NKL>())
+              : (st ? decide_capacity<SV_DTYPE_F32, false, SV_MODE_STOCHASTIC>()
+                    : decide_capacity<SV_DTYPE_F32, false, SV_MODE_NKL>());
+  // NKL: one slice per helper, so that the few positions whose KL needs the
+  // second pass are spread over as many workgroups as possible
+  int64_t H = st ? ((int64_t)cap + p.B - 1) / p.B : p.nslices;
+  if (H > p.nslices) H = p.nslices;
+  if (H < 1) H = 1;
+  const int64_t spp = (p.nslices + H - 1) / H;
+  p.slices_per_helper = (int32_t)spp;
+  p.helpers = (int32_t)((p.nslices + spp - 1) / spp);  // no helper without a slice
+  return 0;
+}
 
 int plan_stats(Params& p, bool vec) {
   int occ;
@@ -1710,48 +1941,6 @@ int launch_decide(const Params& p, bool vec, void* stream) {
   } else {
     if (vec) decide_dispatch<SV_DTYPE_F32, true>(p, s);
     else decide_dispatch<SV_DTYPE_F32, false>(p, s);
-  }
-  return (int)hipGetLastError();
-}
-
-int launch_refine(const Params& p, bool vec, void* stream) {
-  hipStream_t s = (hipStream_t)stream;
-  // the queue length is only known on the device: one wave of workgroups
-  const dim3 grid((unsigned)(4 * num_cus())), blk(kThreads), fgrid(p.B);
-  if (p.dtype == SV_DTYPE_BF16) {
-    if (vec) hipLaunchKernelGGL((k_refine<SV_DTYPE_BF16, true>), grid, blk, 0, s, p);
-    else hipLaunchKernelGGL((k_refine<SV_DTYPE_BF16, false>), grid, blk, 0, s, p);
-  } else {
-    if (vec) hipLaunchKernelGGL((k_refine<SV_DTYPE_F32, true>), grid, blk, 0, s, p);
-    else hipLaunchKernelGGL((k_refine<SV_DTYPE_F32, false>), grid, blk, 0, s, p);
-  }
-  if (p.mode == SV_MODE_NKL) hipLaunchKernelGGL((k_finish<SV_MODE_NKL>), fgrid, blk, 0, s, p);
-  else hipLaunchKernelGGL((k_finish<SV_MODE_STOCHASTIC>), fgrid, blk, 0, s, p);
-  return (int)hipGetLastError();
-}
-
-int launch_draw(const Params& p, bool vec, void* stream) {
-  hipStream_t s = (hipStream_t)stream;
-  int occ;
-  if (p.dtype == SV_DTYPE_BF16) occ = vec ? draw_occupancy<SV_DTYPE_BF16, true>() : draw_occupancy<SV_DTYPE_BF16, false>();
-  else occ = vec ? draw_occupancy<SV_DTYPE_F32, true>() : draw_occupancy<SV_DTYPE_F32, false>();
-  // every wave streams a contiguous range of (request, wave-chunk) items
-  const int64_t N = (int64_t)p.B * p.nch_c;
-  int64_t G = (int64_t)occ * num_cus();
-  if (G > (N + kWaves - 1) / kWaves) G = (N + kWaves - 1) / kWaves;
-  if (G < 1) G = 1;
-  const dim3 grid((unsigned)G), blk(kThreads);
-  const dim3 sgrid(p.B), sblk(64);
-  if (p.dtype == SV_DTYPE_BF16) {
-    if (vec) hipLaunchKernelGGL((k_draw<SV_DTYPE_BF16, true>), grid, blk, 0, s, p);
-    else hipLaunchKernelGGL((k_draw<SV_DTYPE_BF16, false>), grid, blk, 0, s, p);
-    if (vec) hipLaunchKernelGGL((k_select<SV_DTYPE_BF16, true>), sgrid, sblk, 0, s, p);
-    else hipLaunchKernelGGL((k_select<SV_DTYPE_BF16, false>), sgrid, sblk, 0, s, p);
-  } else {
-    if (vec) hipLaunchKernelGGL((k_draw<SV_DTYPE_F32, true>), grid, blk, 0, s, p);
-    else hipLaunchKernelGGL((k_draw<SV_DTYPE_F32, false>), grid, blk, 0, s, p);
-    if (vec) hipLaunchKernelGGL((k_select<SV_DTYPE_F32, true>), sgrid, sblk, 0, s, p);
-    else hipLaunchKernelGGL((k_select<SV_DTYPE_F32, false>), sgrid, sblk, 0, s, p);
   }
   return (int)hipGetLastError();
 }

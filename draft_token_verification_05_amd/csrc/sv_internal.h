@@ -17,8 +17,7 @@ constexpr int stats_vectors_per_thread(int mode) {
   return (mode == SV_MODE_GREEDY || mode == SV_MODE_TREE_GREEDY) ? 4 : 2;
 }
 constexpr int kUA = 2;           // smallest of the above: sizes the partial arrays
-constexpr int kUC = 2;           // 16-byte vectors per lane per row in a wave-chunk of the draw pass
-constexpr int kUR = 2;           // 16-byte vectors per thread per row per chunk, KL second pass
+constexpr int kUT = 4;           // 16-byte vectors per thread per row in one slice of k_decide's second look
 constexpr int kLdsBatch = 1024;  // batches up to this size scan their offsets in LDS (no prep kernel)
 
 constexpr int elems_per_vec(int dtype) { return dtype == SV_DTYPE_BF16 ? 8 : 4; }
@@ -28,8 +27,8 @@ constexpr int64_t chunk_a(int dtype) { return (int64_t)kThreads * kUA * elems_pe
 constexpr int64_t chunk_stats(int dtype, int mode) {
   return (int64_t)kThreads * stats_vectors_per_thread(mode) * elems_per_vec(dtype);
 }
-constexpr int64_t chunk_c(int dtype) { return (int64_t)64 * kUC * elems_per_vec(dtype); }
-constexpr int64_t chunk_r(int dtype) { return (int64_t)kThreads * kUR * elems_per_vec(dtype); }
+// vocabulary slice of one k_decide helper
+constexpr int64_t chunk_t(int dtype) { return (int64_t)kThreads * kUT * elems_per_vec(dtype); }
 
 enum TermKind : int32_t { kTermNone = 0, kTermResidual = 1, kTermBonus = 2 };
 
@@ -45,40 +44,18 @@ struct PartA {
   int32_t pad;
 };
 
-// Terminal record of a stochastic request, written by the decision kernel for
-// the draw pass.
-struct Term {
-  int32_t kind;  // TermKind
-  int32_t j;     // slot of the terminal token (= number of accepted drafts)
-  int32_t trow;  // target row of the terminal distribution
-  int32_t drow;  // draft row (residual only)
-  float m_t;     // maximum of the target row (residual only)
-  float m_d;     // maximum of the draft row (residual only)
-  float k0;      // s_t / s_d from the statistics pass (residual only)
-  float Lhi;     // fl32(log2(e) / T) of the request
-};
-
-// A position whose one-pass KL needs the second pass: the merged statistics
-// of its rows.
-struct RefIn {
-  double s_t, s_d;
-  float m_t, m_d;
-  float Lhi;
-  int32_t trow;
-};
-
-// Partial sums of the draw pass for one (request, wave-chunk), in float64.
+// Sums of the terminal draw over one (request, slice), in float64.
 struct PartC {
   double a, b, ap, bp;  // sum a, sum b, and the same over {y : a_y > k0 * b_y}
-  float m;              // chunk maximum (bonus draws)
+  float m;              // slice maximum (bonus draws)
   int32_t pad[3];
 };
 
 struct Layout {
-  size_t off_hdr, off_doff, off_pair2req, off_row2req, off_part_a, off_term, off_part_c, off_ref_list, off_kl_need,
-      off_ref_in, off_kl_val, off_tidx, off_pending, off_kl_part, total;
+  size_t off_hdr, off_doff, off_pair2req, off_row2req, off_part_a, off_cnt, off_part_c, off_kl_need, off_kl_val,
+      off_tidx, off_kl_part, total;
   int64_t n_task_max;
-  int64_t nch_a, nch_c, nch_r;
+  int64_t nch_a, nch_t;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -86,8 +63,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 inline Layout make_layout(int64_t B, int64_t V, int dtype, int64_t R_d) {
   Layout L{};
   L.nch_a = (V + chunk_a(dtype) - 1) / chunk_a(dtype);
-  L.nch_c = (V + chunk_c(dtype) - 1) / chunk_c(dtype);
-  L.nch_r = (V + chunk_r(dtype) - 1) / chunk_r(dtype);
+  L.nch_t = (V + chunk_t(dtype) - 1) / chunk_t(dtype);
   L.n_task_max = R_d + B;
   const int64_t R1 = R_d > 0 ? R_d : 1;
   size_t o = 0;
@@ -98,18 +74,15 @@ inline Layout make_layout(int64_t B, int64_t V, int dtype, int64_t R_d) {
   };
   L.off_hdr = take(256);
   L.off_doff = take(sizeof(int32_t) * (B + 1));
-  L.off_pair2req = take(sizeof(int32_t) * (R_d > 0 ? R_d : 1));
+  L.off_pair2req = take(sizeof(int32_t) * R1);
   L.off_row2req = take(sizeof(int32_t) * (R_d + B));
   L.off_part_a = take(sizeof(PartA) * L.n_task_max * L.nch_a);
-  L.off_term = take(sizeof(Term) * B);
-  L.off_part_c = take(sizeof(PartC) * B * L.nch_c);
-  L.off_ref_list = take(sizeof(int32_t) * R1);
+  L.off_cnt = take(sizeof(uint32_t) * B);
+  L.off_part_c = take(sizeof(PartC) * B * L.nch_t);
   L.off_kl_need = take(sizeof(int32_t) * R1);
-  L.off_ref_in = take(sizeof(RefIn) * R1);
   L.off_kl_val = take(sizeof(double) * R1);
   L.off_tidx = take(sizeof(int32_t) * (R_d + B));
-  L.off_pending = take(sizeof(int32_t) * B);
-  L.off_kl_part = take(sizeof(double) * R1 * L.nch_r);
+  L.off_kl_part = take(sizeof(double) * R1 * L.nch_t);
   L.total = o;
   return L;
 }
@@ -137,36 +110,34 @@ struct Params {
   int32_t nch;         // vocabulary chunks per task in the row-statistics pass
   int32_t stats_grid;  // workgroups of the row-statistics pass
   int32_t grp_log2;    // log2 of the lanes that merge one task's partials
-  int32_t nch_c;       // vocabulary wave-chunks per request in the draw pass
-  int32_t nch_r;       // vocabulary chunks per position in the KL second pass
+  int32_t helpers;     // k_decide workgroups per request (1 in greedy and tree modes)
+  int32_t nslices;     // vocabulary slices per row (chunk_t elements each)
+  int32_t slices_per_helper;
   float delta;
   int32_t want_kl;  // compute KL(q || p) (NKL mode, or stochastic with out_nkl)
   // workspace
-  int32_t* hdr;  // hdr[0]: layout error flag, hdr[1]: positions queued for the KL second pass
+  int32_t* hdr;  // hdr[0]: layout error flag
   int32_t* d_off;
   int32_t* pair2req;
   int32_t* row2req;
   PartA* part_a;
-  Term* term;
-  PartC* part_c;
-  int32_t* ref_list;  // [R_d] positions queued for the KL second pass (hdr[1] of them)
+  uint32_t* cnt;      // [B] k_decide helpers done per request (zeroed by the offsets scan of each call)
+  PartC* part_c;      // [B * nslices] draw sums per slice
   int32_t* kl_need;   // [R_d] 1 where the KL of the position comes from the second pass
-  RefIn* ref_in;      // [R_d]
   double* kl_val;     // [R_d] one-pass KL (nats)
   int32_t* tidx;      // [R_d + B] argmax of every target row (NKL)
-  int32_t* pending;   // [B] the request waits for second-pass KL values
-  double* kl_part;    // [R_d * nch_r] second-pass KL sums per chunk
+  double* kl_part;    // [R_d * helpers] second-pass KL sums per slice
 };
 
 // kernel launchers (kernels.hip); return the hipError_t of the launch as int
 int launch_prep(const Params& p, void* stream);
 // picks the grid of the statistics pass: fills p.stats_grid and p.grp_log2
 int plan_stats(Params& p, bool vec);
+// picks the k_decide grid: fills p.nslices, p.helpers and p.slices_per_helper
+int plan_decide(Params& p, bool vec);
 // ev_start / ev_stop: optional hipEvent_t handles that take the dispatch's own
 // start and end timestamps (NULL = plain launch)
 int launch_stats(const Params& p, bool vec, void* stream, void* ev_start, void* ev_stop);
 int launch_decide(const Params& p, bool vec, void* stream);
-int launch_draw(const Params& p, bool vec, void* stream);
-int launch_refine(const Params& p, bool vec, void* stream);
 
 }  // namespace sv
