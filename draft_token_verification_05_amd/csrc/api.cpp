@@ -130,7 +130,11 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   p.row2req = reinterpret_cast<int32_t*>(ws + L.off_row2req);
   p.part_a = reinterpret_cast<sv::PartA*>(ws + L.off_part_a);
   p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
+  p.cnt_kl = reinterpret_cast<uint32_t*>(ws + L.off_cnt_kl);
+  p.pending = reinterpret_cast<int32_t*>(ws + L.off_pending);
   p.part_c = reinterpret_cast<sv::PartC*>(ws + L.off_part_c);
+  p.ref_list = reinterpret_cast<int32_t*>(ws + L.off_ref_list);
+  p.ref_in = reinterpret_cast<sv::RefIn*>(ws + L.off_ref_in);
   p.kl_need = reinterpret_cast<int32_t*>(ws + L.off_kl_need);
   p.kl_val = reinterpret_cast<double*>(ws + L.off_kl_val);
   p.tidx = reinterpret_cast<int32_t*>(ws + L.off_tidx);
@@ -154,6 +158,7 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   if ((e = (hipError_t)sv::launch_stats(p, vec, s, ev ? ev[1] : nullptr, ev ? ev[2] : nullptr)) != hipSuccess)
     return hip_fail(e);
   if ((e = (hipError_t)sv::launch_decide(p, vec, s)) != hipSuccess) return hip_fail(e);
+  if (p.want_kl && (e = (hipError_t)sv::launch_refine(p, vec, s)) != hipSuccess) return hip_fail(e);
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e);
   return SV_OK;
 }

@@ -39,9 +39,10 @@
 //   tree drafts, longest accepted path   -- "Parallel Drafting" page, section 2.2;
 //                                          Gemma-4 MTP page, section 6.2.
 //
-// Every exponential of the path is 2^((x - m) * Lhi) with Lhi = fl32(log2(e)/T),
-// in the statistics, decision and draw passes alike, so the three passes see
-// the same distributions.
+// Every exponential of the path is 2^((x - m) * Lhi) with Lhi = fl32(log2(e)/T)
+// (the statistics pass forms it as 2^(x Lhi - fl(m Lhi)) and corrects the
+// rounding of m Lhi once per chunk sum), so all passes see the same
+// distributions to within float32 rounding.
 
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -59,6 +60,7 @@ namespace {
 constexpr int kWaves = kThreads / 64;
 constexpr double kLog2eD = 1.44269504088896340736;
 constexpr double kLn2D = 0.693147180559945309417;
+constexpr float kLn2F = 0.693147180559945309417f;
 
 // ----------------------------------------------------------------------------
 // element access
@@ -390,8 +392,11 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Params p) {
   }
   if (tid == 0) p.d_off[p.B] = (int)carry;
   const bool bad = sh_bad != 0 || carry != (long long)p.R_d;
-  if (tid == 0) p.hdr[0] = bad ? 1 : 0;
-  for (int b = tid; b < p.B; b += kPrepThreads) p.cnt[b] = 0u;  // helper counters of k_decide
+  if (tid == 0) {
+    p.hdr[0] = bad ? 1 : 0;
+    p.hdr[1] = 0;  // KL second-pass queue
+  }
+  for (int b = tid; b < p.B; b += kPrepThreads) p.cnt[b] = p.cnt_kl[b] = 0u;  // completion counters
   if (bad) return;
   __syncthreads();  // offsets written by other threads of this workgroup
   for (int b = tid; b < p.B; b += kPrepThreads) {
@@ -485,8 +490,11 @@ __device__ bool scan_offsets_lds(const Params& p, StatsShared& sh, bool soft, bo
   const bool ok = sh.bad == 0;
   if (publish) {
     for (int b = tid; b <= p.B; b += kThreads) p.d_off[b] = sh.off[b];
-    for (int b = tid; b < p.B; b += kThreads) p.cnt[b] = 0u;  // helper counters of k_decide
-    if (tid == 0) p.hdr[0] = ok ? 0 : 1;
+    for (int b = tid; b < p.B; b += kThreads) p.cnt[b] = p.cnt_kl[b] = 0u;  // completion counters
+    if (tid == 0) {
+      p.hdr[0] = ok ? 0 : 1;
+      p.hdr[1] = 0;  // KL second-pass queue
+    }
   }
   return ok;
 }
@@ -577,17 +585,22 @@ __device__ __forceinline__ void fold_chunk(Lane& L, const Vecs<NV>& qt, const Ve
       L.idx = (int)(e_chunk + ((int64_t)(ic / P) * kThreads + threadIdx.x) * P + ic % P);
     }
     if (SOFT) {
+      // 2^(x L - c) with c = fl(M L): one FMA per element; the chunk sum is
+      // scaled by 2^(-c_lo) ~ 1 - c_lo ln2, c_lo = M L - c (exact by FMA),
+      // so the sums are those of 2^((x - M) L)
       const float M = fmaxf(L.mt, mc);
+      const float c = M * Lhi;
+      const float corr = fmaf(-fmaf(M, Lhi, -c), kLn2F, 1.0f);
       float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
       for (int e = 0; e < NE; e += 4) {
-        a0 += ex2(vt[e] - M, Lhi);
-        a1 += ex2(vt[e + 1] - M, Lhi);
-        a2 += ex2(vt[e + 2] - M, Lhi);
-        a3 += ex2(vt[e + 3] - M, Lhi);
+        a0 += __builtin_amdgcn_exp2f(fmaf(vt[e], Lhi, -c));
+        a1 += __builtin_amdgcn_exp2f(fmaf(vt[e + 1], Lhi, -c));
+        a2 += __builtin_amdgcn_exp2f(fmaf(vt[e + 2], Lhi, -c));
+        a3 += __builtin_amdgcn_exp2f(fmaf(vt[e + 3], Lhi, -c));
       }
       const float f = ex2(L.mt - M, Lhi);  // 0 on the first chunk (L.mt = -inf)
-      L.st = L.st * (double)f + (double)((a0 + a1) + (a2 + a3));
+      L.st = L.st * (double)f + (double)(((a0 + a1) + (a2 + a3)) * corr);
       L.mt = M;
     } else {
       L.mt = fmaxf(L.mt, mc);
@@ -603,13 +616,15 @@ __device__ __forceinline__ void fold_chunk(Lane& L, const Vecs<NV>& qt, const Ve
     for (int e = 1; e < NE; ++e) md = fmaxf(md, vd[e]);
     if (md > pad) {
       const float M = fmaxf(L.md, md);
+      const float c = M * Lhi;
+      const float corr = fmaf(-fmaf(M, Lhi, -c), kLn2F, 1.0f);
       float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f, w0 = 0.f, w1 = 0.f, z0 = 0.f, z1 = 0.f;
 #pragma unroll
       for (int e = 0; e < NE; e += 4) {
-        const float e0 = ex2(vd[e] - M, Lhi);
-        const float e1 = ex2(vd[e + 1] - M, Lhi);
-        const float e2 = ex2(vd[e + 2] - M, Lhi);
-        const float e3 = ex2(vd[e + 3] - M, Lhi);
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(vd[e], Lhi, -c));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(vd[e + 1], Lhi, -c));
+        const float e2 = __builtin_amdgcn_exp2f(fmaf(vd[e + 2], Lhi, -c));
+        const float e3 = __builtin_amdgcn_exp2f(fmaf(vd[e + 3], Lhi, -c));
         a0 += e0;
         a1 += e1;
         a2 += e2;
@@ -625,10 +640,10 @@ __device__ __forceinline__ void fold_chunk(Lane& L, const Vecs<NV>& qt, const Ve
         }
       }
       const double f = (double)ex2(L.md - M, Lhi);
-      L.sd = L.sd * f + (double)((a0 + a1) + (a2 + a3));
+      L.sd = L.sd * f + (double)(((a0 + a1) + (a2 + a3)) * corr);
       if (WZ) {
-        L.w = L.w * f + (double)(w0 + w1);
-        L.z = L.z * f + (double)(z0 + z1);
+        L.w = L.w * f + (double)((w0 + w1) * corr);
+        L.z = L.z * f + (double)((z0 + z1) * corr);
       }
       L.md = M;
     }
@@ -961,13 +976,27 @@ __device__ __forceinline__ void slice_stream(const Params& p, int64_t trow, int6
 // terms q_y g(w_y), w_y = log(p_y / q_y), over slices of the vocabulary.  Because sum q e^w = sum p = 1, the sum over the row equals
 // sum q log(q/p) exactly, has no cancellation, and an error eps in the log
 // normaliser ratio only adds O(eps^2).  All threads of the workgroup call.
+// Per position constants: p_y = 2^(t_y L - ct) kt and q_y = 2^(d_y L - cd) kd
+// (ct = fl(m_t L), kt = 2^(-(m_t L - ct)) / s_t, the same for the draft row),
+// and w_y = log(p_y / q_y) = (t_y - d_y) c + lw, c = L ln 2.
 struct KlIn {
-  float m_t, m_d;
-  float lr;              // log(s_d / s_t)
-  float inv_st, inv_sd;  // 1 / s_t, 1 / s_d
+  float ct, cd, kt, kd, lw;
 };
 
-// Sum over one slice (thread-local part) of q_y g(w_y).
+__device__ __forceinline__ KlIn kl_in(float m_t, float m_d, double s_t, double s_d, float Lhi) {
+  KlIn r;
+  r.ct = m_t * Lhi;
+  r.cd = m_d * Lhi;
+  const double lo_t = (double)fmaf(m_t, Lhi, -r.ct), lo_d = (double)fmaf(m_d, Lhi, -r.cd);
+  r.kt = (float)(exp2(-lo_t) / s_t);
+  r.kd = (float)(exp2(-lo_d) / s_d);
+  const double c = (double)Lhi * kLn2D;
+  r.lw = (float)(((double)m_d - (double)m_t) * c + log(s_d / s_t));
+  return r;
+}
+
+// Sum over one slice (thread-local part) of q_y g(w_y).  Both forms of the
+// term are evaluated and one is selected (no divergent branch).
 template <int DT>
 __device__ __forceinline__ double kl_terms(const uint4* qt, const uint4* qd, const KlIn& ri, float Lhi) {
   constexpr int P = Elem<DT>::P;
@@ -981,17 +1010,12 @@ __device__ __forceinline__ double kl_terms(const uint4* qt, const uint4* qd, con
     float part = 0.f;  // P non-negative terms in float32, then float64
 #pragma unroll
     for (int e = 0; e < P; ++e) {
-      const float dt = vt[e] - ri.m_t, dd = vd[e] - ri.m_d;
-      const float q = ex2(dd, Lhi) * ri.inv_sd;
-      const float w = fmaf(dt - dd, c, ri.lr);
-      float term;
-      if (fabsf(w) < 0.5f) {
-        term = q * g_small(w);
-      } else {
-        // q g(w) = p - q - q w; also right where q underflows but p does not
-        term = (ex2(dt, Lhi) * ri.inv_st - q) - q * w;
-      }
-      part += term;  // positions past the end of the row give p = q = 0
+      const float q = __builtin_amdgcn_exp2f(fmaf(vd[e], Lhi, -ri.cd)) * ri.kd;
+      const float pp = __builtin_amdgcn_exp2f(fmaf(vt[e], Lhi, -ri.ct)) * ri.kt;
+      const float w = fmaf(vt[e] - vd[e], c, ri.lw);
+      const float small = q * g_small(w);
+      const float large = (pp - q) - q * w;  // q g(w) = p - q - q w; right also where q underflows
+      part += fabsf(w) < 0.5f ? small : large;  // positions past the end give p = q = 0
     }
     acc += (double)part;
   }
@@ -1021,7 +1045,7 @@ struct DecideShared {
   int acc[kThreads];
   double kl1[kThreads];
   int need[kThreads];
-  int list[kThreads];  // positions of a pass that need the KL second pass
+  int qbase, qcount;  // queue slots of a pass's positions for the KL second pass
   int red_i[kWaves];
   int red_i2[kWaves];
   float red_f[kWaves];
@@ -1029,6 +1053,30 @@ struct DecideShared {
   double red_d4[4][kWaves];
   int flag;
 };
+
+// Rank of this thread among the threads with `flag` (thread order), and one
+// reservation of that many slots at the end of the KL queue (sh.qbase,
+// sh.qcount).  All threads call.
+__device__ __forceinline__ int block_excl_count(bool flag, int* tail, DecideShared& sh) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const unsigned long long m = __ballot(flag);
+  const int in_wave = __popcll(m & ((1ull << lane) - 1ull));
+  __syncthreads();
+  if (lane == 0) sh.red_i[w] = __popcll(m);
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    if (k < w) before += sh.red_i[k];
+    tot += sh.red_i[k];
+  }
+  if (threadIdx.x == 0) {
+    sh.qcount = tot;
+    sh.qbase = tot > 0 ? atomicAdd(tail, tot) : 0;
+  }
+  __syncthreads();
+  return before + in_wave;
+}
 
 // Counts this helper on the request's counter once every store of the
 // workgroup has completed; true in the last of the `H` helpers to arrive.
@@ -1462,29 +1510,31 @@ __device__ __forceinline__ void draw_select(const Params& p, int b, const Term& 
   }
 }
 
-// Second-pass KL values of a request from the helpers' slice sums, added in
-// slice order; NKL mode also takes the decision here.
+// Second-pass KL values of request b from the slice sums, added in slice
+// order; NKL mode also takes the decision here.
 template <int MODE>
-__device__ __forceinline__ void kl_finish(const Params& p, int b, int t0, int d0, int g, int H, DecideShared& sh) {
+__device__ __forceinline__ void kl_finish(const Params& p, int b, DecideShared& sh) {
+  const int d0 = p.d_off[b], g = p.d_off[b + 1] - d0, t0 = d0 + b;
+  const int NS = p.nslices;
   const double lnV = log((double)p.V);
   int first = INT_MAX;
   for (int i = threadIdx.x; i < g; i += kThreads) {
     const int pos = d0 + i;
-    double kl = ld_dev(&p.kl_val[pos]);
-    const bool need = ld_dev(&p.kl_need[pos]) != 0;
+    double kl = p.kl_val[pos];
+    const bool need = p.kl_need[pos] != 0;
     if (need) {
       kl = 0.0;
-      for (int h = 0; h < H; ++h) kl += ld_dev(&p.kl_part[(int64_t)pos * H + h]);
+      for (int s = 0; s < NS; ++s) kl += ld_dev(&p.kl_part[(int64_t)pos * NS + s]);
     }
     const double nkl = p.V > 1 ? kl / lnV : 0.0;
-    if (need) p.out_nkl[pos] = (float)nkl;  // the other positions were written by helper 0
+    if (need) p.out_nkl[pos] = (float)nkl;  // the other positions were written by k_decide
     if (!(nkl < (double)p.delta)) first = min(first, i);
   }
   if (MODE == SV_MODE_NKL) {
     const int j0 = block_min_int(first, sh.red_i);
     const int j = j0 == INT_MAX ? g : j0;
     for (int k = threadIdx.x; k <= g; k += kThreads)
-      p.out_tokens[t0 + k] = k < j ? p.tokens[d0 + k] : (k == j ? ld_dev(&p.tidx[t0 + j]) : -1);
+      p.out_tokens[t0 + k] = k < j ? p.tokens[d0 + k] : (k == j ? p.tidx[t0 + j] : -1);
     if (threadIdx.x == 0) p.out_num[b] = j;
   }
 }
@@ -1539,6 +1589,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_decide(Params p) {
   double js_t = 1.0, js_d = 1.0;
   int jidx = 0;
   bool any_need = false, bad = false;
+  int n_queued = 0;  // positions queued for the KL second pass (helper 0)
   int checked = 0;  // positions [0, checked) were checked inside the passes
   for (int base = 0; base < ntask; base += TPP) {
     const int q = tid >> glog, l = tid & (S - 1);
@@ -1575,7 +1626,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_decide(Params p) {
       sh.st[q] = r.st;
       sh.sd[q] = r.sd;
       sh.idx[q] = idx;
-      if (MODE == SV_MODE_NKL && writer) st_dev(&p.tidx[t0 + ti], idx);
+      if (MODE == SV_MODE_NKL && writer) p.tidx[t0 + ti] = idx;
       int acc = 0, need = 0;
       double kl = 0.0;  // KL(q||p) = 0 for V == 1: both rows are the same point mass
       if (pair) {
@@ -1608,69 +1659,37 @@ __global__ __launch_bounds__(kThreads, 3) void k_decide(Params p) {
         const int pos = d0 + base + tid;
         const int need = sh.need[tid];
         if (writer) {
-          st_dev(&p.kl_need[pos], need);
-          st_dev(&p.kl_val[pos], sh.kl1[tid]);
+          p.kl_need[pos] = need;
+          p.kl_val[pos] = sh.kl1[tid];
         }
         if (need) {
           any_need = true;
-          if (MODE == SV_MODE_NKL) sh.acc[tid] = 0;  // decided by the last helper
+          if (MODE == SV_MODE_NKL) sh.acc[tid] = 0;  // decided after the second pass
         } else {
           const double nkl = p.V > 1 ? sh.kl1[tid] / lnV : 0.0;
           if (writer && p.out_nkl) p.out_nkl[pos] = (float)nkl;
           if (MODE == SV_MODE_NKL) sh.acc[tid] = nkl < (double)p.delta ? 1 : 0;
         }
       }
-      __syncthreads();
-      // this helper's slices of the second pass, for the positions of this
-      // pass whose one-pass KL is not accurate enough: items (position,
-      // slice) stream with the loads of the next item in flight
-      const int npos = min(TPP, g - base);
-      int nneed = 0;
-      for (int k = 0; k < npos; ++k)
-        if (sh.need[k]) sh.list[nneed++] = k;  // every thread builds the same list
-      const int nsl = s1 - s0;
-      const int nitem = nneed * nsl;
-      if (nitem > 0) {
-        const auto rows = [&](int it, int64_t& tr, int64_t& dr, int& sl) {
-          const int k = sh.list[it / nsl];
-          tr = t0 + base + k;
-          dr = d0 + base + k;
-          sl = s0 + it % nsl;
-        };
-        uint4 at[kUT], ad[kUT], bt[kUT], bd[kUT];
-        double acc = 0.0;
-        const auto consume = [&](const uint4* qt, const uint4* qd, int it) {
-          const int k = sh.list[it / nsl];
-          KlIn ri;
-          ri.m_t = sh.mt[k];
-          ri.m_d = sh.md[k];
-          ri.lr = (float)log(sh.sd[k] / sh.st[k]);
-          ri.inv_st = (float)(1.0 / sh.st[k]);
-          ri.inv_sd = (float)(1.0 / sh.sd[k]);
-          acc += kl_terms<DT>(qt, qd, ri, Lhi);
-          if (it % nsl == nsl - 1) {  // the position's last slice of this helper
-            const double v = block_sum_d(acc, sh.red_d);
-            if (tid == 0) st_dev(&p.kl_part[(int64_t)(d0 + base + k) * H + h], v);
-            acc = 0.0;
-          }
-        };
-        int64_t tr, dr;
-        int sl;
-        rows(0, tr, dr, sl);
-        slice_issue<DT, VEC, true>(p, tr, dr, sl, at, ad);
-        for (int it = 0; it < nitem; it += 2) {
-          if (it + 1 < nitem) {
-            rows(it + 1, tr, dr, sl);
-            slice_issue<DT, VEC, true>(p, tr, dr, sl, bt, bd);
-          }
-          consume(at, ad, it);
-          if (it + 1 >= nitem) break;
-          if (it + 2 < nitem) {
-            rows(it + 2, tr, dr, sl);
-            slice_issue<DT, VEC, true>(p, tr, dr, sl, at, ad);
-          }
-          consume(bt, bd, it + 1);
+      if (writer) {
+        // queue the positions of this pass whose one-pass KL is not accurate
+        // enough for the second pass (k_refine), with their merged statistics
+        const int need = (tid < TPP && base + tid < g) ? sh.need[tid] : 0;
+        const int rank = block_excl_count(need != 0, p.hdr + 1, sh);
+        if (need) {
+          const int pos = d0 + base + tid;
+          RefIn ri;
+          ri.s_t = sh.st[tid];
+          ri.s_d = sh.sd[tid];
+          ri.m_t = sh.mt[tid];
+          ri.m_d = sh.md[tid];
+          ri.Lhi = Lhi;
+          ri.trow = t0 + base + tid;
+          p.ref_in[pos] = ri;
+          p.ref_list[2 * (sh.qbase + rank)] = pos;
+          p.ref_list[2 * (sh.qbase + rank) + 1] = b;
         }
+        n_queued += sh.qcount;
       }
     }
     if (MODE != SV_MODE_TREE_GREEDY) {
@@ -1707,6 +1726,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_decide(Params p) {
   }
   if (__syncthreads_or(bad)) {
     if (writer) finish_invalid(p, b, t0, d0, g);
+    if (want_kl && writer && tid == 0) p.pending[b] = -1;  // k_refine leaves the request alone
     return;
   }
   if constexpr (MODE == SV_MODE_TREE_GREEDY) {
@@ -1714,11 +1734,8 @@ __global__ __launch_bounds__(kThreads, 3) void k_decide(Params p) {
     return;
   }
   const bool need_any = want_kl && __syncthreads_or(any_need);
-  if (MODE == SV_MODE_NKL && need_any) {
-    // the decision needs second-pass values: the last helper takes it
-    if (arrive_last(p.cnt + b, H, sh)) kl_finish<MODE>(p, b, t0, d0, g, H, sh);
-    return;
-  }
+  if (want_kl && writer && tid == 0) p.pending[b] = n_queued;  // positions k_refine completes
+  if (MODE == SV_MODE_NKL && need_any) return;  // the decision needs second-pass values: k_refine takes it
   if (j < 0) j = g;  // stochastic: every draft accepted
   if (writer) {
     for (int k = tid; k <= g; k += kThreads) {
@@ -1752,10 +1769,56 @@ __global__ __launch_bounds__(kThreads, 3) void k_decide(Params p) {
       slice_stream<DT, VEC, false>(p, tm.trow, tm.drow, s0, s1, [&](const uint4* qt, const uint4* qd, int sl) {
         draw_record<DT, false>(qt, qd, tm, rec + sl, sh);
       });
-    if (arrive_last(p.cnt + b, H, sh)) {
-      draw_select<DT, VEC>(p, b, tm, NS, sh);
-      if (need_any) kl_finish<MODE>(p, b, t0, d0, g, H, sh);
-    }
+    if (arrive_last(p.cnt + b, H, sh)) draw_select<DT, VEC>(p, b, tm, NS, sh);
+  }
+}
+
+// ----------------------------------------------------------------------------
+// k_refine: the KL second pass over the queue that k_decide filled.  Items
+// (queued position, vocabulary slice) are split into contiguous ranges, one
+// per workgroup, and stream with the loads of the next item in flight; every
+// item's sum has its own slot, so the result does not depend on the order.
+// The workgroup that completes a request's last item (per-request counter)
+// adds the sums and writes the NKL values and, in NKL mode, the decision.
+// ----------------------------------------------------------------------------
+
+template <int DT, bool VEC, int MODE>
+__global__ __launch_bounds__(kThreads) void k_refine(Params p) {
+  __shared__ DecideShared sh;
+  const int NS = p.nslices;
+  const int64_t N = (int64_t)p.hdr[1] * NS;
+  const int G = (int)gridDim.x, wg = (int)blockIdx.x;
+  const int64_t i0 = (int64_t)wg * N / G, i1 = (int64_t)(wg + 1) * N / G;
+  if (i0 >= i1) return;
+  const auto rows = [&](int64_t it, int& pos, int& b, int& sl) {
+    const int64_t q = it / NS;
+    pos = p.ref_list[2 * q];
+    b = p.ref_list[2 * q + 1];
+    sl = (int)(it % NS);
+  };
+  uint4 at[kUT], ad[kUT], bt[kUT], bd[kUT];
+  const auto issue = [&](int64_t it, uint4* qt, uint4* qd) {
+    int pos, b, sl;
+    rows(it, pos, b, sl);
+    slice_issue<DT, VEC, true>(p, p.ref_in[pos].trow, pos, sl, qt, qd);
+  };
+  const auto consume = [&](const uint4* qt, const uint4* qd, int64_t it) {
+    int pos, b, sl;
+    rows(it, pos, b, sl);
+    const RefIn r = p.ref_in[pos];
+    const KlIn ri = kl_in(r.m_t, r.m_d, r.s_t, r.s_d, r.Lhi);
+    const double v = block_sum_d(kl_terms<DT>(qt, qd, ri, r.Lhi), sh.red_d);
+    if (threadIdx.x == 0) st_dev(&p.kl_part[(int64_t)pos * NS + sl], v);
+    const int pend = p.pending[b];  // -1: the request failed its input checks
+    if (pend > 0 && arrive_last(p.cnt_kl + b, pend * NS, sh)) kl_finish<MODE>(p, b, sh);
+  };
+  issue(i0, at, ad);
+  for (int64_t it = i0; it < i1; it += 2) {
+    if (it + 1 < i1) issue(it + 1, bt, bd);
+    consume(at, ad, it);
+    if (it + 1 >= i1) break;
+    if (it + 2 < i1) issue(it + 2, at, ad);
+    consume(bt, bd, it + 1);
   }
 }
 
@@ -1865,26 +1928,19 @@ int decide_capacity() {
 
 int plan_decide(Params& p, bool vec) {
   p.nslices = (int32_t)((p.V + chunk_t(p.dtype) - 1) / chunk_t(p.dtype));
-  if (p.mode != SV_MODE_STOCHASTIC && p.mode != SV_MODE_NKL) {
+  if (p.mode != SV_MODE_STOCHASTIC) {
     p.helpers = 1;
     p.slices_per_helper = p.nslices;
     return 0;
   }
   int cap;
-  const bool st = p.mode == SV_MODE_STOCHASTIC;
   if (p.dtype == SV_DTYPE_BF16)
-    cap = vec ? (st ? decide_capacity<SV_DTYPE_BF16, true, SV_MODE_STOCHASTIC>()
-                    : decide_capacity<SV_DTYPE_BF16, true, SV_MODE_NKL>())
-              : (st ? decide_capacity<SV_DTYPE_BF16, false, SV_MODE_STOCHASTIC>()
-                    : decide_capacity<SV_DTYPE_BF16, false, SV_MODE_NKL>());
+    cap = vec ? decide_capacity<SV_DTYPE_BF16, true, SV_MODE_STOCHASTIC>()
+              : decide_capacity<SV_DTYPE_BF16, false, SV_MODE_STOCHASTIC>();
   else
-    cap = vec ? (st ? decide_capacity<SV_DTYPE_F32, true, SV_MODE_STOCHASTIC>()
-                    : decide_capacity<SV_DTYPE_F32, true, SV_MODE_NKL>())
-              : (st ? decide_capacity<SV_DTYPE_F32, false, SV_MODE_STOCHASTIC>()
-                    : decide_capacity<SV_DTYPE_F32, false, SV_MODE_NKL>());
-  // NKL: one slice per helper, so that the few positions whose KL needs the
-  // second pass are spread over as many workgroups as possible
-  int64_t H = st ? ((int64_t)cap + p.B - 1) / p.B : p.nslices;
+    cap = vec ? decide_capacity<SV_DTYPE_F32, true, SV_MODE_STOCHASTIC>()
+              : decide_capacity<SV_DTYPE_F32, false, SV_MODE_STOCHASTIC>();
+  int64_t H = ((int64_t)cap + p.B - 1) / p.B;
   if (H > p.nslices) H = p.nslices;
   if (H < 1) H = 1;
   const int64_t spp = (p.nslices + H - 1) / H;
@@ -1941,6 +1997,26 @@ int launch_decide(const Params& p, bool vec, void* stream) {
   } else {
     if (vec) decide_dispatch<SV_DTYPE_F32, true>(p, s);
     else decide_dispatch<SV_DTYPE_F32, false>(p, s);
+  }
+  return (int)hipGetLastError();
+}
+
+template <int DT, bool VEC>
+static void refine_dispatch(const Params& p, hipStream_t s, dim3 grid) {
+  if (p.mode == SV_MODE_NKL) hipLaunchKernelGGL((k_refine<DT, VEC, SV_MODE_NKL>), grid, dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL((k_refine<DT, VEC, SV_MODE_STOCHASTIC>), grid, dim3(kThreads), 0, s, p);
+}
+
+int launch_refine(const Params& p, bool vec, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  // the queue length is known on the device only: one workgroup per resident slot
+  const dim3 grid((unsigned)(4 * num_cus()));
+  if (p.dtype == SV_DTYPE_BF16) {
+    if (vec) refine_dispatch<SV_DTYPE_BF16, true>(p, s, grid);
+    else refine_dispatch<SV_DTYPE_BF16, false>(p, s, grid);
+  } else {
+    if (vec) refine_dispatch<SV_DTYPE_F32, true>(p, s, grid);
+    else refine_dispatch<SV_DTYPE_F32, false>(p, s, grid);
   }
   return (int)hipGetLastError();
 }

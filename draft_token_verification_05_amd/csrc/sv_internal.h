@@ -44,6 +44,15 @@ struct PartA {
   int32_t pad;
 };
 
+// A position whose one-pass KL needs the second pass: the merged statistics
+// of its rows.
+struct RefIn {
+  double s_t, s_d;
+  float m_t, m_d;
+  float Lhi;
+  int32_t trow;
+};
+
 // Sums of the terminal draw over one (request, slice), in float64.
 struct PartC {
   double a, b, ap, bp;  // sum a, sum b, and the same over {y : a_y > k0 * b_y}
@@ -52,8 +61,8 @@ struct PartC {
 };
 
 struct Layout {
-  size_t off_hdr, off_doff, off_pair2req, off_row2req, off_part_a, off_cnt, off_part_c, off_kl_need, off_kl_val,
-      off_tidx, off_kl_part, total;
+  size_t off_hdr, off_doff, off_pair2req, off_row2req, off_part_a, off_cnt, off_cnt_kl, off_pending, off_part_c,
+      off_ref_list, off_ref_in, off_kl_need, off_kl_val, off_tidx, off_kl_part, total;
   int64_t n_task_max;
   int64_t nch_a, nch_t;
 };
@@ -78,7 +87,11 @@ inline Layout make_layout(int64_t B, int64_t V, int dtype, int64_t R_d) {
   L.off_row2req = take(sizeof(int32_t) * (R_d + B));
   L.off_part_a = take(sizeof(PartA) * L.n_task_max * L.nch_a);
   L.off_cnt = take(sizeof(uint32_t) * B);
+  L.off_cnt_kl = take(sizeof(uint32_t) * B);
+  L.off_pending = take(sizeof(int32_t) * B);
   L.off_part_c = take(sizeof(PartC) * B * L.nch_t);
+  L.off_ref_list = take(sizeof(int32_t) * 2 * R1);
+  L.off_ref_in = take(sizeof(RefIn) * R1);
   L.off_kl_need = take(sizeof(int32_t) * R1);
   L.off_kl_val = take(sizeof(double) * R1);
   L.off_tidx = take(sizeof(int32_t) * (R_d + B));
@@ -116,17 +129,21 @@ struct Params {
   float delta;
   int32_t want_kl;  // compute KL(q || p) (NKL mode, or stochastic with out_nkl)
   // workspace
-  int32_t* hdr;  // hdr[0]: layout error flag
+  int32_t* hdr;  // hdr[0]: layout error flag, hdr[1]: positions queued for the KL second pass
   int32_t* d_off;
   int32_t* pair2req;
   int32_t* row2req;
   PartA* part_a;
   uint32_t* cnt;      // [B] k_decide helpers done per request (zeroed by the offsets scan of each call)
+  uint32_t* cnt_kl;   // [B] KL second-pass items done per request (zeroed likewise)
+  int32_t* pending;   // [B] positions of the request queued for the KL second pass
   PartC* part_c;      // [B * nslices] draw sums per slice
+  int32_t* ref_list;  // [2 R_d] queued (position, request) pairs (hdr[1] of them)
+  RefIn* ref_in;      // [R_d] merged statistics of a queued position
   int32_t* kl_need;   // [R_d] 1 where the KL of the position comes from the second pass
   double* kl_val;     // [R_d] one-pass KL (nats)
   int32_t* tidx;      // [R_d + B] argmax of every target row (NKL)
-  double* kl_part;    // [R_d * helpers] second-pass KL sums per slice
+  double* kl_part;    // [R_d * nslices] second-pass KL sums per slice
 };
 
 // kernel launchers (kernels.hip); return the hipError_t of the launch as int
@@ -139,5 +156,7 @@ int plan_decide(Params& p, bool vec);
 // start and end timestamps (NULL = plain launch)
 int launch_stats(const Params& p, bool vec, void* stream, void* ev_start, void* ev_stop);
 int launch_decide(const Params& p, bool vec, void* stream);
+// KL second pass over the queue k_decide fills (NKL mode, or stochastic with out_nkl)
+int launch_refine(const Params& p, bool vec, void* stream);
 
 }  // namespace sv

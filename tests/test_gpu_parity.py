@@ -164,6 +164,22 @@ def test_invalid_requests_isolated():
         check(wm)
 
 
+@pytest.mark.parametrize("mode", [K, S])
+def test_invalid_requests_after_kl_queue(mode):
+    """Rows within a small noise of each other queue every position for the KL
+    second pass; a request whose input check fails after some of its
+    positions were queued keeps its -1 outputs, the others complete."""
+    w = synthetic.random_workload(seed=16, mode=mode, B=12, V=20000, dtype="bf16", gmax=5, gmin=3, sigma=0.003)
+    d_off = w.d_off
+    w.draft_tokens = w.draft_tokens.copy()
+    w.draft_tokens[d_off[3] + 1] = w.vocab  # position 0 of request 3 is valid and queued first
+    w.draft_tokens[d_off[7] + int(w.gamma[7]) - 1] = -2
+    g, o, rep = check(w, out_nkl=True)
+    assert g["num"][3] == -1 and g["num"][7] == -1
+    assert (g["num"][[0, 1, 2, 4, 5, 6, 8, 9, 10, 11]] >= 0).all()
+    assert rep.max_rel_nkl < 2e-5
+
+
 def test_gamma_above_max_and_layout_errors():
     w = synthetic.random_workload(seed=13, mode=G, B=6, V=2000, dtype="bf16", gmax=5, gmin=1,
                                   greedy_drafts=True)
