@@ -436,19 +436,30 @@ struct StatsShared {
 // off[b] = sum of gamma over the requests before b.  Returns whether the layout
 // is valid (every gamma >= 0, sum == total_draft_rows).  `publish`: also write
 // the offsets and the layout flag for the later kernels.
-__device__ bool scan_offsets_lds(const Params& p, StatsShared& sh, bool soft, bool publish) {
+// Loads of gamma (and the temperatures) for the scan: issued on their own,
+// ahead of other loads, since vector loads complete in issue order.
+struct ScanIn {
+  int gl[4];
+  float tl[4];
+};
+__device__ __forceinline__ ScanIn scan_load(const Params& p, bool soft) {
+  ScanIn in;
+  // clamped indices, no branches: all loads in flight together
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int bc = min(4 * (int)threadIdx.x + k, p.B - 1);
+    in.gl[k] = p.gamma[bc];
+    in.tl[k] = soft ? p.temp[bc] : 0.0f;
+  }
+  return in;
+}
+
+__device__ bool scan_offsets_lds(const Params& p, StatsShared& sh, const ScanIn& in, bool soft, bool publish) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   long long g[4], loc = 0;
   bool bad = false;
-  // all loads first (clamped indices, no branches), so they are in flight together
-  int gl[4];
-  float tl[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int bc = min(4 * tid + k, p.B - 1);
-    gl[k] = p.gamma[bc];
-    tl[k] = soft ? p.temp[bc] : 0.0f;
-  }
+  const int* gl = in.gl;
+  const float* tl = in.tl;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int b = 4 * tid + k;
@@ -532,27 +543,30 @@ struct Vecs {
   uint4 v[NV];
 };
 
-// Rows and vocabulary chunk of one item of the statistics pass.  The second
-// row of a pair is read from `dbase` (the draft logits; for the bonus row of an
-// NKL request the target row itself, whose pair statistics are not used).
+// Rows and vocabulary chunk of one item of the statistics pass.  `pair`: a
+// draft row is streamed beside the target row (every stochastic task; NKL
+// tasks except the bonus rows).
 struct Desc {
   int task, chunk;
   int64_t trow, drow;
-  const void* dbase;
+  int pair;  // int, not bool: keeps the struct in registers
   float Lhi;
 };
 
-// Loads of one chunk: thread t takes 16-byte vectors k * kThreads + t.
+// Loads of one chunk of one row: thread t takes 16-byte vectors k * kThreads + t.
+template <int DT, bool VEC, int NV>
+__device__ __forceinline__ void issue_row(const void* base, int64_t row, int chunk, int64_t V, Vecs<NV>& q) {
+  constexpr int P = Elem<DT>::P;
+  const int64_t e_chunk = (int64_t)chunk * kThreads * NV * P;
+#pragma unroll
+  for (int k = 0; k < NV; ++k)
+    q.v[k] = fetch_raw<DT, VEC>(base, row, V, e_chunk + ((int64_t)k * kThreads + threadIdx.x) * P);
+}
+
 template <int DT, bool VEC, int NV, bool PAIR>
 __device__ __forceinline__ void issue_chunk(const Params& p, const Desc& d, Vecs<NV>& qt, Vecs<NV>& qd) {
-  constexpr int P = Elem<DT>::P;
-  const int64_t e_chunk = (int64_t)d.chunk * kThreads * NV * P;
-#pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    const int64_t e0 = e_chunk + ((int64_t)k * kThreads + threadIdx.x) * P;
-    qt.v[k] = fetch_raw<DT, VEC>(p.target, d.trow, p.V, e0);
-    if (PAIR) qd.v[k] = fetch_raw<DT, VEC>(d.dbase, d.drow, p.V, e0);
-  }
+  issue_row<DT, VEC, NV>(p.target, d.trow, d.chunk, p.V, qt);
+  if (PAIR && d.pair) issue_row<DT, VEC, NV>(p.draft, d.drow, d.chunk, p.V, qd);
 }
 
 // Folds one chunk into the lane state.  SOFT: sums of exponentials; IDX:
@@ -606,7 +620,7 @@ __device__ __forceinline__ void fold_chunk(Lane& L, const Vecs<NV>& qt, const Ve
       L.mt = fmaxf(L.mt, mc);
     }
   }
-  if (PAIR) {
+  if (PAIR && d.pair) {
     float vd[NE];
 #pragma unroll
     for (int k = 0; k < NV; ++k) unpack<DT>(qd.v[k], vd + k * P);
@@ -730,7 +744,7 @@ __device__ __forceinline__ void set_rows(const Params& p, const StatsShared& sh,
   if (MODE == SV_MODE_GREEDY || MODE == SV_MODE_TREE_GREEDY) {
     d.trow = d.task;
     d.drow = 0;
-    d.dbase = p.target;
+    d.pair = 0;
     d.Lhi = 0.0f;
     return;
   }
@@ -746,7 +760,7 @@ __device__ __forceinline__ void set_rows(const Params& p, const StatsShared& sh,
   if (MODE == SV_MODE_STOCHASTIC) {
     d.trow = (int64_t)d.task + b;
     d.drow = d.task;
-    d.dbase = p.draft;
+    d.pair = 1;
   } else {
     int d0, d1;
     if constexpr (LDS) {
@@ -756,10 +770,9 @@ __device__ __forceinline__ void set_rows(const Params& p, const StatsShared& sh,
       d0 = p.d_off[b];
       d1 = p.d_off[b + 1];
     }
-    const bool pair = d.task - (d0 + b) < d1 - d0;
+    d.pair = d.task - (d0 + b) < d1 - d0 ? 1 : 0;  // the bonus row (position gamma) has no draft row
     d.trow = d.task;
-    d.drow = pair ? (int64_t)d.task - b : d.task;
-    d.dbase = pair ? p.draft : p.target;
+    d.drow = d.pair ? (int64_t)d.task - b : 0;
   }
 }
 
@@ -787,23 +800,45 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params p) {
   __shared__ StatsShared sh;
   const int G = (int)gridDim.x, wg = (int)blockIdx.x;
   const int64_t N = (int64_t)p.n_task * p.nch;
-  if (LDS) {
-    // greedy and tree tasks are target rows: only workgroup 0 needs the scan,
-    // to publish the offsets for the decision kernel
-    if ((SOFT || wg == 0) && !scan_offsets_lds(p, sh, SOFT, wg == 0)) return;
-  } else if (SOFT && p.hdr[0] != 0) {
-    return;  // the prep kernel found a layout error
-  }
   const int64_t i_end = (int64_t)(wg + 1) * N / G;
   int64_t i = (int64_t)wg * N / G;
-  if (i >= i_end) return;
-  int b = -1;
   Desc dA, dB;
-  dA.task = (int)(i / p.nch);
-  dA.chunk = (int)(i - (int64_t)dA.task * p.nch);
-  set_rows<MODE, LDS>(p, sh, b, dA);
   Vecs<NV> At, Ad, Bt, Bd;
-  issue_chunk<DT, VEC, NV, SOFT>(p, dA, At, Ad);
+  int b = -1;
+  // soft modes with the offsets scan in LDS: the first chunk's row whose index
+  // needs no request lookup (the draft row of a stochastic pair, the target
+  // row of an NKL task) is requested right behind the scan's own loads, so
+  // that it is in flight while the scan runs
+  constexpr bool EARLY = LDS && SOFT;
+  if constexpr (EARLY) {
+    dA.task = (int)(i / p.nch);
+    dA.chunk = (int)(i - (int64_t)dA.task * p.nch);
+    const ScanIn scan_in = scan_load(p, SOFT);
+    __asm__ volatile("" ::: "memory");  // keeps the scan's loads ahead in issue order
+    // unconditional, so that the scan's waits count these loads exactly: a
+    // workgroup without items reads target row 0 (always present) instead
+    const bool has = i < i_end;
+    const void* base = (MODE == SV_MODE_STOCHASTIC && has) ? p.draft : p.target;
+    issue_row<DT, VEC, NV>(base, has ? dA.task : 0, has ? dA.chunk : 0, p.V, MODE == SV_MODE_STOCHASTIC ? Ad : At);
+    if (!scan_offsets_lds(p, sh, scan_in, SOFT, wg == 0)) return;
+    if (!has) return;
+    set_rows<MODE, LDS>(p, sh, b, dA);
+    if (MODE == SV_MODE_STOCHASTIC) issue_row<DT, VEC, NV>(p.target, dA.trow, dA.chunk, p.V, At);
+    else if (dA.pair) issue_row<DT, VEC, NV>(p.draft, dA.drow, dA.chunk, p.V, Ad);
+  } else {
+    if (LDS) {
+      // greedy and tree tasks are target rows: only workgroup 0 needs the
+      // scan, to publish the offsets for the decision kernel
+      if (wg == 0 && !scan_offsets_lds(p, sh, scan_load(p, SOFT), SOFT, true)) return;
+    } else if (SOFT && p.hdr[0] != 0) {
+      return;  // the prep kernel found a layout error
+    }
+    if (i >= i_end) return;
+    dA.task = (int)(i / p.nch);
+    dA.chunk = (int)(i - (int64_t)dA.task * p.nch);
+    set_rows<MODE, LDS>(p, sh, b, dA);
+    issue_chunk<DT, VEC, NV, SOFT>(p, dA, At, Ad);
+  }
   Lane L;
   lane_reset(L);
   for (;;) {
@@ -940,16 +975,18 @@ __device__ __forceinline__ float g_small(float w) {
   return w * w * t;
 }
 
-// Loads of one vocabulary slice: thread t takes 16-byte vectors
-// k * kThreads + t, k < kUT, of the target row and (TWO) of the draft row.
+// Loads of one vocabulary slice: wave w covers the contiguous wave-chunk w of
+// the slice (64 x kUT vectors); its lane l takes vectors k * 64 + l, k < kUT,
+// of the target row and (TWO) of the draft row.
 template <int DT, bool VEC, bool TWO>
 __device__ __forceinline__ void slice_issue(const Params& p, int64_t trow, int64_t drow, int sl, uint4* qt,
                                             uint4* qd) {
   constexpr int P = Elem<DT>::P;
   const int64_t e_base = (int64_t)sl * kThreads * kUT * P;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
   for (int k = 0; k < kUT; ++k) {
-    const int64_t e0 = e_base + ((int64_t)k * kThreads + threadIdx.x) * P;
+    const int64_t e0 = e_base + ((int64_t)(w * kUT + k) * 64 + lane) * P;
     qt[k] = fetch<DT, VEC>(p.target, trow, p.V, e0);
     if (TWO) qd[k] = fetch<DT, VEC>(p.draft, drow, p.V, e0);
   }
@@ -1046,11 +1083,12 @@ struct DecideShared {
   double kl1[kThreads];
   int need[kThreads];
   int qbase, qcount;  // queue slots of a pass's positions for the KL second pass
+  // draw records of the request kept by the token selection (one wave)
+  double sel_a[kSelCache], sel_ap[kSelCache], sel_bp[kSelCache];
+  float sel_m[kSelCache];
   int red_i[kWaves];
-  int red_i2[kWaves];
   float red_f[kWaves];
   double red_d[kWaves];
-  double red_d4[4][kWaves];
   int flag;
 };
 
@@ -1080,7 +1118,8 @@ __device__ __forceinline__ int block_excl_count(bool flag, int* tail, DecideShar
 
 // Counts this helper on the request's counter once every store of the
 // workgroup has completed; true in the last of the `H` helpers to arrive.
-__device__ __forceinline__ bool arrive_last(uint32_t* cnt, int H, DecideShared& sh) {
+template <class SH>
+__device__ __forceinline__ bool arrive_last(uint32_t* cnt, int H, SH& sh) {
   __asm__ __volatile__("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0);  // this thread's stores have completed
   __asm__ __volatile__("" ::: "memory");
@@ -1174,35 +1213,18 @@ struct Term {
   float Lhi;     // fl32(log2(e) / T) of the request
 };
 
-// Inclusive prefix sum over the workgroup in thread order; `total` gets the
-// sum of all threads.  All threads call.
-__device__ __forceinline__ double block_incl_scan_d(double v, double* sh, double& total) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const double x = wave_incl_scan_d(v);
-  __syncthreads();
-  if (lane == 63) sh[w] = x;
-  __syncthreads();
-  double before = 0.0, tot = 0.0;
-#pragma unroll
-  for (int k = 0; k < kWaves; ++k) {
-    if (k < w) before += sh[k];
-    tot += sh[k];
-  }
-  total = tot;
-  return before + x;
-}
-
-// Slice record of the draw: over the vocabulary elements of one slice,
-// a_y = 2^((t_y - m_t) L) and b_y = 2^((d_y - m_d) L) are p_y and q_y up to the
-// factors s_t, s_d; a residual record holds sum a, sum b and the same sums over
-// {y : a_y > k0 b_y}, the support of max(0, p - q).  A bonus record holds the
-// slice maximum m and sum_y 2^((t_y - m) L).
+// Wave-chunk record of the draw (each wave of a helper covers one contiguous
+// wave-chunk of the slice): a_y = 2^((t_y - m_t) L) and b_y = 2^((d_y - m_d) L)
+// are p_y and q_y up to the factors s_t, s_d; a residual record holds sum a,
+// sum b and the same sums over {y : a_y > k0 b_y}, the support of
+// max(0, p - q).  A bonus record holds the chunk maximum m and
+// sum_y 2^((t_y - m) L) (m = -inf and 0 for a chunk past the end of the row).
+// Wave-level only: no workgroup barrier.
 template <int DT, bool RESID>
-__device__ __forceinline__ void draw_record(const uint4* qt, const uint4* qd, const Term& tm, PartC* dst,
-                                            DecideShared& sh) {
+__device__ __forceinline__ void draw_record(const uint4* qt, const uint4* qd, const Term& tm, PartC* dst) {
   constexpr int P = Elem<DT>::P;
   const float Lhi = tm.Lhi;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   if (RESID) {
     double A = 0.0, Bs = 0.0, Ap = 0.0, Bp = 0.0;
 #pragma unroll
@@ -1230,26 +1252,11 @@ __device__ __forceinline__ void draw_record(const uint4* qt, const uint4* qd, co
     Bs = wave_sum_d(Bs);
     Ap = wave_sum_d(Ap);
     Bp = wave_sum_d(Bp);
-    __syncthreads();  // thread 0 has read the previous slice's sums
     if (lane == 0) {
-      sh.red_d4[0][w] = A;
-      sh.red_d4[1][w] = Bs;
-      sh.red_d4[2][w] = Ap;
-      sh.red_d4[3][w] = Bp;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      double r[4];
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        r[f] = sh.red_d4[f][0];
-#pragma unroll
-        for (int k = 1; k < kWaves; ++k) r[f] += sh.red_d4[f][k];
-      }
-      st_dev(&dst->a, r[0]);
-      st_dev(&dst->b, r[1]);
-      st_dev(&dst->ap, r[2]);
-      st_dev(&dst->bp, r[3]);
+      st_dev(&dst->a, A);
+      st_dev(&dst->b, Bs);
+      st_dev(&dst->ap, Ap);
+      st_dev(&dst->bp, Bp);
     }
   } else {
     float vt[kUT * P];
@@ -1258,7 +1265,8 @@ __device__ __forceinline__ void draw_record(const uint4* qt, const uint4* qd, co
     float m = vt[0];
 #pragma unroll
     for (int e = 1; e < kUT * P; ++e) m = fmaxf(m, vt[e]);
-    const float mc = block_max(m, sh.red_f);  // the slice starts inside the row: mc is a logit
+    const float mc = wave_max(m);
+    const bool empty = !(mc > Elem<DT>::kPad);  // the chunk lies past the end of the row
     double A = 0.0;
 #pragma unroll
     for (int k = 0; k < kUT; ++k) {
@@ -1267,10 +1275,10 @@ __device__ __forceinline__ void draw_record(const uint4* qt, const uint4* qd, co
       for (int e = 0; e < P; ++e) sa += ex2(vt[k * P + e] - mc, Lhi);
       A += (double)sa;
     }
-    A = block_sum_d(A, sh.red_d);
-    if (threadIdx.x == 0) {
-      st_dev(&dst->a, A);
-      st_dev(&dst->m, mc);
+    A = wave_sum_d(A);
+    if (lane == 0) {
+      st_dev(&dst->a, empty ? 0.0 : A);
+      st_dev(&dst->m, empty ? -INFINITY : mc);
     }
   }
 }
@@ -1295,66 +1303,53 @@ __device__ __forceinline__ double token_weight(float t, float d, bool two, const
   return (double)a * cf;
 }
 
-// Token draw of request b by its last helper, from the H slice records (H =
-// slices per row):
-// y* = min{y : C_y > u * C_{V-1}} in ascending token order.  The records are
-// combined by workgroup-wide reductions and scans in slice order; the slice
-// holding the draw is read again and scanned token by token.
-template <int DT, bool VEC>
-__device__ __forceinline__ void draw_select(const Params& p, int b, const Term& tm, int H, DecideShared& sh) {
+// Token draw of request b by one wave of its last helper, from the NW
+// wave-chunk records in token order: y* = min{y : C_y > u * C_{V-1}}.
+// CACHED: at most kSelCache records, kept in LDS after the first sweep.  The
+// records are combined by fixed wave-wide reductions and scans in chunk
+// order; the wave-chunk that holds the draw is read again, lane l taking NE
+// consecutive tokens, and scanned token by token.  No workgroup barrier.
+template <int DT, bool VEC, bool CACHED>
+__device__ __forceinline__ void draw_select(const Params& p, int b, const Term& tm, int NW, DecideShared& sh) {
   constexpr int P = Elem<DT>::P;
-  constexpr int64_t CHT = (int64_t)kThreads * kUT * P;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const PartC* rec = p.part_c + (int64_t)b * H;
+  constexpr int NE = kUT * P;
+  constexpr int64_t CHW = (int64_t)64 * NE;
+  const int lane = threadIdx.x & 63;
+  const PartC* pcs = p.part_c + (int64_t)b * NW;
   const bool resid = tm.kind == kTermResidual;
   const float Lhi = tm.Lhi;
   const double Ld = (double)Lhi;
-  const bool cached = H <= kThreads;  // one record per thread, kept in registers
-  double ca = 0.0, cap = 0.0, cbp = 0.0;
-  float cm = -INFINITY;
   double at = 0.0, bt = 0.0;
   float M = -INFINITY;
-  for (int s = tid; s < H; s += kThreads) {
-    const double a = ld_dev(&rec[s].a);
-    const double bb = resid ? ld_dev(&rec[s].b) : 0.0;
-    const float m = resid ? 0.0f : ld_dev(&rec[s].m);
+  for (int ch = lane; ch < NW; ch += 64) {
+    const double a = ld_dev(&pcs[ch].a);
+    const double bb = resid ? ld_dev(&pcs[ch].b) : 0.0;
+    const float m = resid ? 0.0f : ld_dev(&pcs[ch].m);
     at += a;
     bt += bb;
     M = fmaxf(M, m);
-    if (cached) {
-      ca = a;
-      cap = resid ? ld_dev(&rec[s].ap) : 0.0;
-      cbp = resid ? ld_dev(&rec[s].bp) : 0.0;
-      cm = m;
+    if (CACHED) {
+      // each lane reads back only the records it wrote: no barrier needed
+      sh.sel_a[ch] = a;
+      sh.sel_ap[ch] = resid ? ld_dev(&pcs[ch].ap) : 0.0;
+      sh.sel_bp[ch] = resid ? ld_dev(&pcs[ch].bp) : 0.0;
+      sh.sel_m[ch] = m;
     }
   }
-  // sum a, sum b and max m in one workgroup round
   at = wave_sum_d(at);
   bt = wave_sum_d(bt);
   M = wave_max(M);
-  if (lane == 0) {
-    sh.red_d4[0][wv] = at;
-    sh.red_d4[1][wv] = bt;
-    sh.red_f[wv] = M;
-  }
-  __syncthreads();
-  at = sh.red_d4[0][0];
-  bt = sh.red_d4[1][0];
-  M = sh.red_f[0];
-#pragma unroll
-  for (int k = 1; k < kWaves; ++k) {
-    at += sh.red_d4[0][k];
-    bt += sh.red_d4[1][k];
-    M = fmaxf(M, sh.red_f[k]);
-  }
   const double K = resid ? at / bt : 0.0;
+  const auto weight = [&](int ch, bool fb) {
+    if (CACHED) return slice_weight(sh.sel_a[ch], sh.sel_ap[ch], sh.sel_bp[ch], sh.sel_m[ch], resid, fb, K, M, Ld);
+    return slice_weight(ld_dev(&pcs[ch].a), resid ? ld_dev(&pcs[ch].ap) : 0.0, resid ? ld_dev(&pcs[ch].bp) : 0.0,
+                        resid ? 0.0f : ld_dev(&pcs[ch].m), resid, fb, K, M, Ld);
+  };
+  const int rounds = (NW + 63) / 64;
   double S = 0.0;
-  for (int s = tid; s < H; s += kThreads)
-    S += cached ? slice_weight(ca, cap, cbp, cm, resid, false, K, M, Ld)
-                : slice_weight(ld_dev(&rec[s].a), resid ? ld_dev(&rec[s].ap) : 0.0,
-                               resid ? ld_dev(&rec[s].bp) : 0.0, resid ? 0.0f : ld_dev(&rec[s].m), resid, false, K,
-                               M, Ld);
-  S = block_sum_d(S, sh.red_d);
+  for (int r = 0; r < rounds; ++r)
+    if (lane + 64 * r < NW) S += weight(lane + 64 * r, false);
+  S = wave_sum_d(S);
   bool fb = false;
   if (resid && !(S > 0.0)) {
     // max(0, p - q) vanished numerically: draw from p_j instead
@@ -1363,69 +1358,46 @@ __device__ __forceinline__ void draw_select(const Params& p, int b, const Term& 
   }
   const double target = (double)p.ur[b] * S;
 
-  // the slice whose cumulative weight first exceeds the target: one round per
-  // kThreads consecutive slices
+  // the wave-chunk whose cumulative weight first exceeds the target: one round
+  // per 64 consecutive chunks
   int cstar = -1, clast = -1;
   double cbase = 0.0, carry = 0.0;
-  for (int r0 = 0; r0 < H; r0 += kThreads) {
-    const int s = r0 + tid;
-    double w = 0.0;
-    if (s < H)
-      w = cached ? slice_weight(ca, cap, cbp, cm, resid, fb, K, M, Ld)
-                 : slice_weight(ld_dev(&rec[s].a), resid ? ld_dev(&rec[s].ap) : 0.0,
-                                resid ? ld_dev(&rec[s].bp) : 0.0, resid ? 0.0f : ld_dev(&rec[s].m), resid, fb, K,
-                                M, Ld);
-    double tot;
-    const double incl = block_incl_scan_d(w, sh.red_d, tot);
+  for (int r = 0; r < rounds; ++r) {
+    const int ch = lane + 64 * r;
+    const double w = ch < NW ? weight(ch, fb) : 0.0;
+    const double incl = wave_incl_scan_d(w);
     const double excl = carry + incl - w;
     const bool hit = w > 0.0 && excl <= target && target < excl + w;
-    // lowest hit, last slice with weight, and each slice's base, in one round
-    const int h1 = wave_min_int(hit ? s : INT_MAX), l1 = wave_max_int(w > 0.0 ? s : -1);
-    sh.st[tid] = excl;
-    if (lane == 0) {
-      sh.red_i[wv] = h1;
-      sh.red_i2[wv] = l1;
-    }
-    __syncthreads();
-    int first = sh.red_i[0], lp = sh.red_i2[0];
-#pragma unroll
-    for (int k = 1; k < kWaves; ++k) {
-      first = min(first, sh.red_i[k]);
-      lp = max(lp, sh.red_i2[k]);
-    }
+    const int first = wave_min_int(hit ? ch : INT_MAX);
+    const int lp = wave_max_int(w > 0.0 ? ch : -1);
     if (lp >= 0) clast = lp;
     if (first != INT_MAX) {
       cstar = first;
-      cbase = sh.st[first - r0];
+      cbase = lane_d(excl, first - 64 * r);
       break;
     }
-    carry += tot;
-    __syncthreads();  // sh.st and the round's reductions are rewritten by the next round
+    carry += lane_d(incl, 63);
   }
   const bool take_last = cstar < 0;  // rounding left the target at the end
   if (take_last) {
-    cstar = clast >= 0 ? clast : H - 1;
+    cstar = clast >= 0 ? clast : NW - 1;
     cbase = 0.0;
   }
 
-  // slice c* again: vector k of thread t holds tokens e_base + (k kThreads + t) P + [0, P)
+  // wave-chunk c* again: lane l owns tokens y0 .. y0 + NE - 1
   const int64_t V = p.V;
-  const int64_t e_base = (int64_t)cstar * CHT;
+  const int64_t y0 = (int64_t)cstar * CHW + (int64_t)lane * NE;
   const bool two = resid && !fb;
-  const float ref = resid ? tm.m_t : ld_dev(&rec[cstar].m);
+  const float ref = resid ? tm.m_t : ld_dev(&pcs[cstar].m);
   const double cf = resid ? 1.0 : exp2(((double)ref - (double)M) * Ld);
   uint4 qt[kUT], qd[kUT];
 #pragma unroll
   for (int k = 0; k < kUT; ++k) {
-    const int64_t e0 = e_base + ((int64_t)k * kThreads + tid) * P;
-    qt[k] = fetch<DT, VEC>(p.target, tm.trow, V, e0);
-    qd[k] = two ? fetch<DT, VEC>(p.draft, tm.drow, V, e0) : qt[k];
+    qt[k] = fetch<DT, VEC>(p.target, tm.trow, V, y0 + k * P);
+    qd[k] = two ? fetch<DT, VEC>(p.draft, tm.drow, V, y0 + k * P) : qt[k];
   }
-  // positions past the end hold the pad: a = 0 there, so their weight is 0.
-  // Vector k of thread t is unit k kThreads + t in token order; the unit
-  // whose cumulative range holds the target is found first, then only its P
-  // tokens are weighed again one by one.
-  double vsum[kUT], incl[kUT];
+  // positions past the end hold the pad: a = 0 there, so their weight is 0
+  double vs[kUT], tsum = 0.0;
   int lastpos = -1;  // the last token with a positive weight (the fallback)
 #pragma unroll
   for (int k = 0; k < kUT; ++k) {
@@ -1437,74 +1409,44 @@ __device__ __forceinline__ void draw_select(const Params& p, int b, const Term& 
     for (int e = 0; e < P; ++e) {
       const double rv = token_weight(vt[e], vd[e], two, tm, ref, Lhi, K, cf);
       sum += rv;
-      if (rv > 0.0) lastpos = (int)(e_base + ((int64_t)k * kThreads + tid) * P + e);
+      if (rv > 0.0) lastpos = (int)(y0 + k * P + e);
     }
-    vsum[k] = sum;
-    incl[k] = wave_incl_scan_d(sum);
+    vs[k] = sum;
+    tsum += sum;
   }
-  __syncthreads();  // sh.red_d4 was last read before the slice scan
-  if (lane == 63) {
-#pragma unroll
-    for (int k = 0; k < kUT; ++k) sh.red_d4[k][wv] = incl[k];
-  }
-  __syncthreads();
-  int unit = INT_MAX;
-  double ubase = 0.0, run = cbase;
+  const double cum0 = cbase + (wave_incl_scan_d(tsum) - tsum);
+  const bool mine = !take_last && cum0 <= target && cum0 + tsum > target;
+  // the lane's vector that holds the target, then its P tokens weighed again
+  int kk = -1;
+  double base = cum0;
 #pragma unroll
   for (int k = 0; k < kUT; ++k) {
-    double before = 0.0, tot = 0.0;
-#pragma unroll
-    for (int q = 0; q < kWaves; ++q) {
-      if (q < wv) before += sh.red_d4[k][q];
-      tot += sh.red_d4[k][q];
-    }
-    const double cum = run + (before + incl[k]) - vsum[k];
-    run += tot;
-    if (!take_last && unit == INT_MAX && cum <= target && cum + vsum[k] > target) {
-      unit = k * kThreads + tid;
-      ubase = cum;
+    if (mine && kk < 0) {
+      if (base + vs[k] > target) kk = k;
+      else base += vs[k];
     }
   }
-  // lowest unit holding the target and the last positive token, in one round
-  const int u1 = wave_min_int(unit), y1 = wave_max_int(lastpos);
-  __syncthreads();  // sh.red_i / red_i2 were read in the slice scan
+  int cand = INT_MAX;
+  if (kk >= 0) {
+    // vector kk read again (a cache hit) instead of kept in registers through
+    // the scan above
+    const uint4 wt = fetch<DT, VEC>(p.target, tm.trow, V, y0 + kk * P);
+    const uint4 wd = two ? fetch<DT, VEC>(p.draft, tm.drow, V, y0 + kk * P) : wt;
+    float vt[P], vd[P];
+    unpack<DT>(wt, vt);
+    unpack<DT>(wd, vd);
+    double cum = base;
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      cum += token_weight(vt[e], vd[e], two, tm, ref, Lhi, K, cf);
+      if (cand == INT_MAX && cum > target) cand = (int)(y0 + kk * P + e);
+    }
+  }
+  const int ystar = wave_min_int(cand);
+  const int ylast = wave_max_int(lastpos);
   if (lane == 0) {
-    sh.red_i[wv] = u1;
-    sh.red_i2[wv] = y1;
-  }
-  __syncthreads();
-  int ustar = sh.red_i[0], ylast = sh.red_i2[0];
-#pragma unroll
-  for (int k = 1; k < kWaves; ++k) {
-    ustar = min(ustar, sh.red_i[k]);
-    ylast = max(ylast, sh.red_i2[k]);
-  }
-  // the thread that owns the unit (thread 0 when there is none) writes the token
-  const bool writer = ustar != INT_MAX ? unit == ustar : tid == 0;
-  if (writer) {
-    int y = INT_MAX;
-    if (ustar != INT_MAX) {
-      // select the unit's vector without dynamic register indexing
-      const int ku = ustar / kThreads;
-      uint4 wt = qt[0], wd = qd[0];
-#pragma unroll
-      for (int k = 1; k < kUT; ++k)
-        if (k == ku) {
-          wt = qt[k];
-          wd = qd[k];
-        }
-      float vt[P], vd[P];
-      unpack<DT>(wt, vt);
-      unpack<DT>(wd, vd);
-      double cum = ubase;
-#pragma unroll
-      for (int e = 0; e < P; ++e) {
-        cum += token_weight(vt[e], vd[e], two, tm, ref, Lhi, K, cf);
-        if (y == INT_MAX && cum > target) y = (int)(e_base + (int64_t)ustar * P + e);
-      }
-    }
-    if (y == INT_MAX) y = ylast;
-    if (y < 0 || y >= p.V) y = (int)min(V - 1, e_base);
+    int y = ystar != INT_MAX ? ystar : ylast;
+    if (y < 0 || y >= p.V) y = (int)min(V - 1, (int64_t)cstar * CHW);
     p.out_tokens[tm.trow] = y;
     if (p.out_resid) p.out_resid[b] = two ? (float)(S / at) : 1.0f;
   }
@@ -1512,8 +1454,8 @@ __device__ __forceinline__ void draw_select(const Params& p, int b, const Term& 
 
 // Second-pass KL values of request b from the slice sums, added in slice
 // order; NKL mode also takes the decision here.
-template <int MODE>
-__device__ __forceinline__ void kl_finish(const Params& p, int b, DecideShared& sh) {
+template <int MODE, class SH>
+__device__ __forceinline__ void kl_finish(const Params& p, int b, SH& sh) {
   const int d0 = p.d_off[b], g = p.d_off[b + 1] - d0, t0 = d0 + b;
   const int NS = p.nslices;
   const double lnV = log((double)p.V);
@@ -1544,7 +1486,7 @@ __device__ __forceinline__ void kl_finish(const Params& p, int b, DecideShared& 
 // ----------------------------------------------------------------------------
 
 template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads, 3) void k_decide(Params p) {
+__global__ __launch_bounds__(kThreads) void k_decide(Params p) {
   constexpr bool SOFT = MODE == SV_MODE_STOCHASTIC || MODE == SV_MODE_NKL;
   __shared__ DecideShared sh;
   __shared__ TreeShared<MODE> tr;
@@ -1760,16 +1702,21 @@ __global__ __launch_bounds__(kThreads, 3) void k_decide(Params p) {
       tm.drow = -1;
       tm.m_t = tm.m_d = tm.k0 = 0.0f;
     }
-    PartC* rec = p.part_c + (int64_t)b * NS;
+    // one record per wave-chunk: kWaves per slice, in token order
+    PartC* rec = p.part_c + (int64_t)b * NS * kWaves + (tid >> 6);
     if (tm.kind == kTermResidual)
       slice_stream<DT, VEC, true>(p, tm.trow, tm.drow, s0, s1, [&](const uint4* qt, const uint4* qd, int sl) {
-        draw_record<DT, true>(qt, qd, tm, rec + sl, sh);
+        draw_record<DT, true>(qt, qd, tm, rec + sl * kWaves);
       });
     else
       slice_stream<DT, VEC, false>(p, tm.trow, tm.drow, s0, s1, [&](const uint4* qt, const uint4* qd, int sl) {
-        draw_record<DT, false>(qt, qd, tm, rec + sl, sh);
+        draw_record<DT, false>(qt, qd, tm, rec + sl * kWaves);
       });
-    if (arrive_last(p.cnt + b, H, sh)) draw_select<DT, VEC>(p, b, tm, NS, sh);
+    if (arrive_last(p.cnt + b, H, sh) && tid < 64) {
+      const int NW = NS * kWaves;
+      if (NW <= kSelCache) draw_select<DT, VEC, true>(p, b, tm, NW, sh);
+      else draw_select<DT, VEC, false>(p, b, tm, NW, sh);
+    }
   }
 }
 
@@ -1782,9 +1729,16 @@ __global__ __launch_bounds__(kThreads, 3) void k_decide(Params p) {
 // adds the sums and writes the NKL values and, in NKL mode, the decision.
 // ----------------------------------------------------------------------------
 
+// workgroup scratch of k_refine
+struct RefineShared {
+  int red_i[kWaves];
+  double red_d[kWaves];
+  int flag;
+};
+
 template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) void k_refine(Params p) {
-  __shared__ DecideShared sh;
+  __shared__ RefineShared sh;
   const int NS = p.nslices;
   const int64_t N = (int64_t)p.hdr[1] * NS;
   const int G = (int)gridDim.x, wg = (int)blockIdx.x;

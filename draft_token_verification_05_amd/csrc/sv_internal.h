@@ -18,6 +18,7 @@ constexpr int stats_vectors_per_thread(int mode) {
 }
 constexpr int kUA = 2;           // smallest of the above: sizes the partial arrays
 constexpr int kUT = 4;           // 16-byte vectors per thread per row in one slice of k_decide's second look
+constexpr int kSelCache = 256;   // draw records a token selection keeps in LDS
 constexpr int kLdsBatch = 1024;  // batches up to this size scan their offsets in LDS (no prep kernel)
 
 constexpr int elems_per_vec(int dtype) { return dtype == SV_DTYPE_BF16 ? 8 : 4; }
@@ -53,10 +54,11 @@ struct RefIn {
   int32_t trow;
 };
 
-// Sums of the terminal draw over one (request, slice), in float64.
+// Sums of the terminal draw over one (request, wave-chunk), in float64; a
+// slice of kThreads x kUT vectors holds four wave-chunks.
 struct PartC {
   double a, b, ap, bp;  // sum a, sum b, and the same over {y : a_y > k0 * b_y}
-  float m;              // slice maximum (bonus draws)
+  float m;              // chunk maximum (bonus draws)
   int32_t pad[3];
 };
 
@@ -89,7 +91,7 @@ inline Layout make_layout(int64_t B, int64_t V, int dtype, int64_t R_d) {
   L.off_cnt = take(sizeof(uint32_t) * B);
   L.off_cnt_kl = take(sizeof(uint32_t) * B);
   L.off_pending = take(sizeof(int32_t) * B);
-  L.off_part_c = take(sizeof(PartC) * B * L.nch_t);
+  L.off_part_c = take(sizeof(PartC) * B * L.nch_t * (kThreads / 64));
   L.off_ref_list = take(sizeof(int32_t) * 2 * R1);
   L.off_ref_in = take(sizeof(RefIn) * R1);
   L.off_kl_need = take(sizeof(int32_t) * R1);
@@ -137,7 +139,7 @@ struct Params {
   uint32_t* cnt;      // [B] k_decide helpers done per request (zeroed by the offsets scan of each call)
   uint32_t* cnt_kl;   // [B] KL second-pass items done per request (zeroed likewise)
   int32_t* pending;   // [B] positions of the request queued for the KL second pass
-  PartC* part_c;      // [B * nslices] draw sums per slice
+  PartC* part_c;      // [B * nslices * 4] draw sums per wave-chunk
   int32_t* ref_list;  // [2 R_d] queued (position, request) pairs (hdr[1] of them)
   RefIn* ref_in;      // [R_d] merged statistics of a queued position
   int32_t* kl_need;   // [R_d] 1 where the KL of the position comes from the second pass
