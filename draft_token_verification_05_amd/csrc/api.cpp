@@ -131,12 +131,10 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   p.part_a = reinterpret_cast<sv::PartA*>(ws + L.off_part_a);
   p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
   p.cnt_kl = reinterpret_cast<uint32_t*>(ws + L.off_cnt_kl);
-  p.pending = reinterpret_cast<int32_t*>(ws + L.off_pending);
+  p.req_fin = reinterpret_cast<sv::ReqFin*>(ws + L.off_req_fin);
   p.part_c = reinterpret_cast<sv::PartC*>(ws + L.off_part_c);
-  p.ref_list = reinterpret_cast<int32_t*>(ws + L.off_ref_list);
-  p.ref_in = reinterpret_cast<sv::RefIn*>(ws + L.off_ref_in);
+  p.ref_list = reinterpret_cast<sv::RefItem*>(ws + L.off_ref_list);
   p.kl_need = reinterpret_cast<int32_t*>(ws + L.off_kl_need);
-  p.kl_val = reinterpret_cast<double*>(ws + L.off_kl_val);
   p.tidx = reinterpret_cast<int32_t*>(ws + L.off_tidx);
   p.kl_part = reinterpret_cast<double*>(ws + L.off_kl_part);
 

@@ -1453,31 +1453,31 @@ __device__ __forceinline__ void draw_select(const Params& p, int b, const Term& 
 }
 
 // Second-pass KL values of request b from the slice sums, added in slice
-// order; NKL mode also takes the decision here.
+// order.  NKL mode: k_decide wrote the outputs with every queued position
+// accepted (decision jnn); the first queued position that the second-pass
+// value rejects, if it precedes jnn, becomes the decision.
 template <int MODE, class SH>
 __device__ __forceinline__ void kl_finish(const Params& p, int b, SH& sh) {
-  const int d0 = p.d_off[b], g = p.d_off[b + 1] - d0, t0 = d0 + b;
-  const int NS = p.nslices;
+  const ReqFin f = p.req_fin[b];
+  const int t0 = f.d0 + b, NS = p.nslices;
   const double lnV = log((double)p.V);
   int first = INT_MAX;
-  for (int i = threadIdx.x; i < g; i += kThreads) {
-    const int pos = d0 + i;
-    double kl = p.kl_val[pos];
+  for (int i = threadIdx.x; i < f.g; i += kThreads) {
+    const int pos = f.d0 + i;
     const bool need = p.kl_need[pos] != 0;
-    if (need) {
-      kl = 0.0;
-      for (int s = 0; s < NS; ++s) kl += ld_dev(&p.kl_part[(int64_t)pos * NS + s]);
-    }
+    double kl = 0.0;  // the slots of positions not queued hold older values: not used
+    for (int s = 0; s < NS; ++s) kl += ld_dev(&p.kl_part[(int64_t)pos * NS + s]);
+    if (!need) continue;
     const double nkl = p.V > 1 ? kl / lnV : 0.0;
-    if (need) p.out_nkl[pos] = (float)nkl;  // the other positions were written by k_decide
+    p.out_nkl[pos] = (float)nkl;  // the other positions were written by k_decide
     if (!(nkl < (double)p.delta)) first = min(first, i);
   }
   if (MODE == SV_MODE_NKL) {
-    const int j0 = block_min_int(first, sh.red_i);
-    const int j = j0 == INT_MAX ? g : j0;
-    for (int k = threadIdx.x; k <= g; k += kThreads)
-      p.out_tokens[t0 + k] = k < j ? p.tokens[d0 + k] : (k == j ? p.tidx[t0 + j] : -1);
-    if (threadIdx.x == 0) p.out_num[b] = j;
+    const int jr = block_min_int(first, sh.red_i);
+    if (jr < f.jnn) {
+      for (int k = jr + threadIdx.x; k <= f.jnn; k += kThreads) p.out_tokens[t0 + k] = k == jr ? p.tidx[t0 + jr] : -1;
+      if (threadIdx.x == 0) p.out_num[b] = jr;
+    }
   }
 }
 
@@ -1530,7 +1530,7 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
   float jm_t = 0.f, jm_d = 0.f;
   double js_t = 1.0, js_d = 1.0;
   int jidx = 0;
-  bool any_need = false, bad = false;
+  bool bad = false;
   int n_queued = 0;  // positions queued for the KL second pass (helper 0)
   int checked = 0;  // positions [0, checked) were checked inside the passes
   for (int base = 0; base < ntask; base += TPP) {
@@ -1600,13 +1600,11 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
       if (tid < TPP && base + tid < g) {
         const int pos = d0 + base + tid;
         const int need = sh.need[tid];
-        if (writer) {
-          p.kl_need[pos] = need;
-          p.kl_val[pos] = sh.kl1[tid];
-        }
+        if (writer) p.kl_need[pos] = need;
         if (need) {
-          any_need = true;
-          if (MODE == SV_MODE_NKL) sh.acc[tid] = 0;  // decided after the second pass
+          // NKL: taken as accepted here; k_refine corrects the outputs if the
+          // second-pass value rejects it
+          if (MODE == SV_MODE_NKL) sh.acc[tid] = 1;
         } else {
           const double nkl = p.V > 1 ? sh.kl1[tid] / lnV : 0.0;
           if (writer && p.out_nkl) p.out_nkl[pos] = (float)nkl;
@@ -1619,17 +1617,19 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
         const int need = (tid < TPP && base + tid < g) ? sh.need[tid] : 0;
         const int rank = block_excl_count(need != 0, p.hdr + 1, sh);
         if (need) {
-          const int pos = d0 + base + tid;
-          RefIn ri;
-          ri.s_t = sh.st[tid];
-          ri.s_d = sh.sd[tid];
-          ri.m_t = sh.mt[tid];
-          ri.m_d = sh.md[tid];
-          ri.Lhi = Lhi;
-          ri.trow = t0 + base + tid;
-          p.ref_in[pos] = ri;
-          p.ref_list[2 * (sh.qbase + rank)] = pos;
-          p.ref_list[2 * (sh.qbase + rank) + 1] = b;
+          const KlIn ri = kl_in(sh.mt[tid], sh.md[tid], sh.st[tid], sh.sd[tid], Lhi);
+          RefItem e;
+          e.pos = d0 + base + tid;
+          e.b = b;
+          e.trow = t0 + base + tid;
+          e.Lhi = Lhi;
+          e.ct = ri.ct;
+          e.cd = ri.cd;
+          e.kt = ri.kt;
+          e.kd = ri.kd;
+          e.lw = ri.lw;
+          e.pad = 0;
+          p.ref_list[sh.qbase + rank] = e;
         }
         n_queued += sh.qcount;
       }
@@ -1668,17 +1668,15 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
   }
   if (__syncthreads_or(bad)) {
     if (writer) finish_invalid(p, b, t0, d0, g);
-    if (want_kl && writer && tid == 0) p.pending[b] = -1;  // k_refine leaves the request alone
+    if (want_kl && writer && tid == 0) p.req_fin[b] = ReqFin{d0, g, g, -1};  // k_refine leaves the request alone
     return;
   }
   if constexpr (MODE == SV_MODE_TREE_GREEDY) {
     resolve_tree(p, b, g, t0, d0, tr, sh);
     return;
   }
-  const bool need_any = want_kl && __syncthreads_or(any_need);
-  if (want_kl && writer && tid == 0) p.pending[b] = n_queued;  // positions k_refine completes
-  if (MODE == SV_MODE_NKL && need_any) return;  // the decision needs second-pass values: k_refine takes it
-  if (j < 0) j = g;  // stochastic: every draft accepted
+  if (j < 0) j = g;  // every draft accepted
+  if (want_kl && writer && tid == 0) p.req_fin[b] = ReqFin{d0, g, j, n_queued};
   if (writer) {
     for (int k = tid; k <= g; k += kThreads) {
       if (k < j) p.out_tokens[t0 + k] = p.tokens[d0 + k];
@@ -1744,35 +1742,28 @@ __global__ __launch_bounds__(kThreads) void k_refine(Params p) {
   const int G = (int)gridDim.x, wg = (int)blockIdx.x;
   const int64_t i0 = (int64_t)wg * N / G, i1 = (int64_t)(wg + 1) * N / G;
   if (i0 >= i1) return;
-  const auto rows = [&](int64_t it, int& pos, int& b, int& sl) {
-    const int64_t q = it / NS;
-    pos = p.ref_list[2 * q];
-    b = p.ref_list[2 * q + 1];
-    sl = (int)(it % NS);
-  };
   uint4 at[kUT], ad[kUT], bt[kUT], bd[kUT];
-  const auto issue = [&](int64_t it, uint4* qt, uint4* qd) {
-    int pos, b, sl;
-    rows(it, pos, b, sl);
-    slice_issue<DT, VEC, true>(p, p.ref_in[pos].trow, pos, sl, qt, qd);
+  RefItem ea, eb;
+  int pa, pb;
+  // the item's queue entry, its request's queued count, then its slice
+  const auto issue = [&](int64_t it, RefItem& e, int& pend, uint4* qt, uint4* qd) {
+    e = p.ref_list[it / NS];
+    pend = p.req_fin[e.b].pending;  // -1: the request failed its input checks
+    slice_issue<DT, VEC, true>(p, e.trow, e.pos, (int)(it % NS), qt, qd);
   };
-  const auto consume = [&](const uint4* qt, const uint4* qd, int64_t it) {
-    int pos, b, sl;
-    rows(it, pos, b, sl);
-    const RefIn r = p.ref_in[pos];
-    const KlIn ri = kl_in(r.m_t, r.m_d, r.s_t, r.s_d, r.Lhi);
-    const double v = block_sum_d(kl_terms<DT>(qt, qd, ri, r.Lhi), sh.red_d);
-    if (threadIdx.x == 0) st_dev(&p.kl_part[(int64_t)pos * NS + sl], v);
-    const int pend = p.pending[b];  // -1: the request failed its input checks
-    if (pend > 0 && arrive_last(p.cnt_kl + b, pend * NS, sh)) kl_finish<MODE>(p, b, sh);
+  const auto consume = [&](const uint4* qt, const uint4* qd, const RefItem& e, int pend, int64_t it) {
+    const KlIn ri{e.ct, e.cd, e.kt, e.kd, e.lw};
+    const double v = block_sum_d(kl_terms<DT>(qt, qd, ri, e.Lhi), sh.red_d);
+    if (threadIdx.x == 0) st_dev(&p.kl_part[(int64_t)e.pos * NS + it % NS], v);
+    if (pend > 0 && arrive_last(p.cnt_kl + e.b, pend * NS, sh)) kl_finish<MODE>(p, e.b, sh);
   };
-  issue(i0, at, ad);
+  issue(i0, ea, pa, at, ad);
   for (int64_t it = i0; it < i1; it += 2) {
-    if (it + 1 < i1) issue(it + 1, bt, bd);
-    consume(at, ad, it);
+    if (it + 1 < i1) issue(it + 1, eb, pb, bt, bd);
+    consume(at, ad, ea, pa, it);
     if (it + 1 >= i1) break;
-    if (it + 2 < i1) issue(it + 2, at, ad);
-    consume(bt, bd, it + 1);
+    if (it + 2 < i1) issue(it + 2, ea, pa, at, ad);
+    consume(bt, bd, eb, pb, it + 1);
   }
 }
 

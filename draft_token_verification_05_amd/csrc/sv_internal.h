@@ -45,13 +45,23 @@ struct PartA {
   int32_t pad;
 };
 
-// A position whose one-pass KL needs the second pass: the merged statistics
-// of its rows.
-struct RefIn {
-  double s_t, s_d;
-  float m_t, m_d;
+// A position queued for the KL second pass, with the constants of its terms:
+// p_y = 2^(t_y L - ct) kt, q_y = 2^(d_y L - cd) kd and
+// log(p_y / q_y) = (t_y - d_y) L ln 2 + lw (L = Lhi = log2(e) / T).
+struct RefItem {
+  int32_t pos;   // packed position = draft row
+  int32_t b;     // request
+  int32_t trow;  // target row
   float Lhi;
-  int32_t trow;
+  float ct, cd, kt, kd, lw;
+  int32_t pad;
+};
+
+// Per request: what the KL second pass needs to complete it.
+struct ReqFin {
+  int32_t d0, g;
+  int32_t jnn;      // NKL: decision taken with every queued position accepted
+  int32_t pending;  // positions queued; -1: the request failed its input checks
 };
 
 // Sums of the terminal draw over one (request, wave-chunk), in float64; a
@@ -63,8 +73,8 @@ struct PartC {
 };
 
 struct Layout {
-  size_t off_hdr, off_doff, off_pair2req, off_row2req, off_part_a, off_cnt, off_cnt_kl, off_pending, off_part_c,
-      off_ref_list, off_ref_in, off_kl_need, off_kl_val, off_tidx, off_kl_part, total;
+  size_t off_hdr, off_doff, off_pair2req, off_row2req, off_part_a, off_cnt, off_cnt_kl, off_req_fin, off_part_c,
+      off_ref_list, off_kl_need, off_tidx, off_kl_part, total;
   int64_t n_task_max;
   int64_t nch_a, nch_t;
 };
@@ -90,12 +100,10 @@ inline Layout make_layout(int64_t B, int64_t V, int dtype, int64_t R_d) {
   L.off_part_a = take(sizeof(PartA) * L.n_task_max * L.nch_a);
   L.off_cnt = take(sizeof(uint32_t) * B);
   L.off_cnt_kl = take(sizeof(uint32_t) * B);
-  L.off_pending = take(sizeof(int32_t) * B);
+  L.off_req_fin = take(sizeof(ReqFin) * B);
   L.off_part_c = take(sizeof(PartC) * B * L.nch_t * (kThreads / 64));
-  L.off_ref_list = take(sizeof(int32_t) * 2 * R1);
-  L.off_ref_in = take(sizeof(RefIn) * R1);
+  L.off_ref_list = take(sizeof(RefItem) * R1);
   L.off_kl_need = take(sizeof(int32_t) * R1);
-  L.off_kl_val = take(sizeof(double) * R1);
   L.off_tidx = take(sizeof(int32_t) * (R_d + B));
   L.off_kl_part = take(sizeof(double) * R1 * L.nch_t);
   L.total = o;
@@ -138,12 +146,10 @@ struct Params {
   PartA* part_a;
   uint32_t* cnt;      // [B] k_decide helpers done per request (zeroed by the offsets scan of each call)
   uint32_t* cnt_kl;   // [B] KL second-pass items done per request (zeroed likewise)
-  int32_t* pending;   // [B] positions of the request queued for the KL second pass
+  ReqFin* req_fin;    // [B] completion record of the KL second pass
   PartC* part_c;      // [B * nslices * 4] draw sums per wave-chunk
-  int32_t* ref_list;  // [2 R_d] queued (position, request) pairs (hdr[1] of them)
-  RefIn* ref_in;      // [R_d] merged statistics of a queued position
+  RefItem* ref_list;  // [R_d] positions queued for the KL second pass (hdr[1] of them)
   int32_t* kl_need;   // [R_d] 1 where the KL of the position comes from the second pass
-  double* kl_val;     // [R_d] one-pass KL (nats)
   int32_t* tidx;      // [R_d + B] argmax of every target row (NKL)
   double* kl_part;    // [R_d * nslices] second-pass KL sums per slice
 };
