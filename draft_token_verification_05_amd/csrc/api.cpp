@@ -137,7 +137,6 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   p.kl_need = reinterpret_cast<int32_t*>(ws + L.off_kl_need);
   p.tidx = reinterpret_cast<int32_t*>(ws + L.off_tidx);
   p.kl_part = reinterpret_cast<double*>(ws + L.off_kl_part);
-  p.gx = reinterpret_cast<float*>(ws + L.off_gx);
 
   // 16-byte vector loads need every row to start on a 16-byte boundary
   const size_t es = (size_t)sv::elem_size(cfg->dtype);

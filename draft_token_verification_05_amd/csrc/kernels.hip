@@ -550,7 +550,6 @@ struct Desc {
   int task, chunk;
   int64_t trow, drow;
   int pair;  // int, not bool: keeps the struct in registers
-  int x;     // stochastic: the drafted token of the task
   float Lhi;
 };
 
@@ -665,38 +664,6 @@ __device__ __forceinline__ void fold_chunk(Lane& L, const Vecs<NV>& qt, const Ve
   }
 }
 
-// Stochastic: the target and draft logits at the drafted token x of task d,
-// copied to gx[task] by the thread whose vectors of this chunk hold element x,
-// so that the decision kernel needs no load that depends on x.  A token
-// outside the row is rejected by the decision kernel's input checks.
-template <int DT, int NV>
-__device__ __forceinline__ void gather_x(const Params& p, const Desc& d, const Vecs<NV>& qt, const Vecs<NV>& qd) {
-  constexpr int P = Elem<DT>::P;
-  const int64_t off = (int64_t)d.x - (int64_t)d.chunk * kThreads * NV * P;  // uniform
-  if (off < 0 || off >= (int64_t)kThreads * NV * P) return;
-  const int k = (int)(off / (kThreads * P)), t = (int)((off / P) % kThreads), e = (int)(off % P);
-  if ((int)threadIdx.x != t) return;
-  uint4 wt = qt.v[0], wd = qd.v[0];  // vector k and element e without dynamic register indexing
-#pragma unroll
-  for (int kk = 1; kk < NV; ++kk)
-    if (kk == k) {
-      wt = qt.v[kk];
-      wd = qd.v[kk];
-    }
-  float ft[P], fd[P];
-  unpack<DT>(wt, ft);
-  unpack<DT>(wd, fd);
-  float a = ft[0], c = fd[0];
-#pragma unroll
-  for (int ee = 1; ee < P; ++ee)
-    if (ee == e) {
-      a = ft[ee];
-      c = fd[ee];
-    }
-  p.gx[2 * (int64_t)d.task] = a;
-  p.gx[2 * (int64_t)d.task + 1] = c;
-}
-
 // Reduces the lane states over the workgroup and writes the segment's partial
 // (thread 0, plain stores: the consumer is a later kernel).
 template <bool SOFT, bool IDX, bool WZ, bool PAIR>
@@ -794,12 +761,6 @@ __device__ __forceinline__ void set_rows(const Params& p, const StatsShared& sh,
     d.trow = (int64_t)d.task + b;
     d.drow = d.task;
     d.pair = 1;
-    // a vector load (per-lane address): it completes in order with the chunk
-    // loads, whereas a scalar load would share its wait counter with the LDS
-    // traffic of the segment reductions and stall them
-    int lane0 = (int)threadIdx.x;
-    __asm__ volatile("" : "+v"(lane0));
-    d.x = p.tokens[d.task + (lane0 >> 30)];
   } else {
     int d0, d1;
     if constexpr (LDS) {
@@ -884,7 +845,6 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params p) {
     dB = dA;
     if (i + 1 < i_end) next_desc<MODE, LDS>(p, sh, b, dB);
     issue_chunk<DT, VEC, NV, SOFT>(p, dB, Bt, Bd);  // the last item reloads itself (cache hit)
-    if (MODE == SV_MODE_STOCHASTIC) gather_x<DT, NV>(p, dA, At, Ad);
     fold_chunk<DT, NV, SOFT, IDX, WZM, SOFT>(L, At, Ad, dA, p.V);
     if (dA.chunk == p.nch - 1 || i + 1 == i_end) {
       reduce_store<SOFT, IDX, WZM, SOFT>(L, dA.Lhi, p.part_a + (int64_t)dA.task * p.nch +
@@ -895,7 +855,6 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params p) {
     dA = dB;
     if (i + 1 < i_end) next_desc<MODE, LDS>(p, sh, b, dA);
     issue_chunk<DT, VEC, NV, SOFT>(p, dA, At, Ad);
-    if (MODE == SV_MODE_STOCHASTIC) gather_x<DT, NV>(p, dB, Bt, Bd);
     fold_chunk<DT, NV, SOFT, IDX, WZM, SOFT>(L, Bt, Bd, dB, p.V);
     if (dB.chunk == p.nch - 1 || i + 1 == i_end) {
       reduce_store<SOFT, IDX, WZM, SOFT>(L, dB.Lhi, p.part_a + (int64_t)dB.task * p.nch +
@@ -1584,13 +1543,9 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
     int x = -1;
     float tx = 0.f, dx = 0.f, u = 0.f;
     if (l == 0 && MODE != SV_MODE_TREE_GREEDY && ti < g) {
-      if (MODE == SV_MODE_STOCHASTIC) {  // gathered by the statistics pass
-        tx = p.gx[2 * (int64_t)(d0 + ti)];
-        dx = p.gx[2 * (int64_t)(d0 + ti) + 1];
-      }
       x = p.tokens[d0 + ti];
       const bool xok = x >= 0 && x < p.V;
-      if (MODE == SV_MODE_NKL && xok && (p.out_p_x || p.out_q_x)) {  // NKL uses them for p(x), q(x) only
+      if (SOFT && xok) {
         tx = load_scalar<DT>(p.target, t0 + ti, V, x);
         dx = load_scalar<DT>(p.draft, d0 + ti, V, x);
       }

@@ -74,7 +74,7 @@ struct PartC {
 
 struct Layout {
   size_t off_hdr, off_doff, off_pair2req, off_row2req, off_part_a, off_cnt, off_cnt_kl, off_req_fin, off_part_c,
-      off_ref_list, off_kl_need, off_tidx, off_kl_part, off_gx, total;
+      off_ref_list, off_kl_need, off_tidx, off_kl_part, total;
   int64_t n_task_max;
   int64_t nch_a, nch_t;
 };
@@ -106,7 +106,6 @@ inline Layout make_layout(int64_t B, int64_t V, int dtype, int64_t R_d) {
   L.off_kl_need = take(sizeof(int32_t) * R1);
   L.off_tidx = take(sizeof(int32_t) * (R_d + B));
   L.off_kl_part = take(sizeof(double) * R1 * L.nch_t);
-  L.off_gx = take(sizeof(float) * 2 * R1);
   L.total = o;
   return L;
 }
@@ -153,7 +152,6 @@ struct Params {
   int32_t* kl_need;   // [R_d] 1 where the KL of the position comes from the second pass
   int32_t* tidx;      // [R_d + B] argmax of every target row (NKL)
   double* kl_part;    // [R_d * nslices] second-pass KL sums per slice
-  float* gx;          // [2 R_d] stochastic: target and draft logit at each drafted token
 };
 
 // kernel launchers (kernels.hip); return the hipError_t of the launch as int
