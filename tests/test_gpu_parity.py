@@ -91,6 +91,26 @@ def test_ragged_small(mode, V, dtype):
 
 
 @pytest.mark.parametrize("mode", [S, G, K, TR])
+def test_batch_above_lds_scan(mode):
+    """More than 1024 requests: the offsets come from the prep kernel and the
+    statistics workgroups look requests up in the row -> request maps."""
+    w = synthetic.random_workload(seed=21 + mode, mode=mode, B=1300, V=1500, dtype="bf16", gmax=3, gmin=0,
+                                  tree=(mode == TR), greedy_drafts=(mode == G))
+    check(w, out_nkl=(mode == S))
+
+
+@pytest.mark.parametrize("mode", [S, G, K])
+def test_long_draft_several_decision_passes(mode):
+    """Drafts longer than one decision pass (hundreds of positions): the
+    per-pass first-rejection scan and the KL queue runs of several passes."""
+    w = synthetic.random_workload(seed=31 + mode, mode=mode, B=3, V=3000, dtype="bf16", gmax=600, gmin=300,
+                                  sigma=0.02, greedy_drafts=(mode == G))
+    if mode == K:
+        w = w.with_mode(K, delta=0.5)
+    check(w, out_nkl=(mode != G))
+
+
+@pytest.mark.parametrize("mode", [S, G, K, TR])
 def test_heavy_ties(mode):
     """Integer-valued logits: many tied maxima, lowest index must win
     everywhere (lanes, waves, chunks, workgroups)."""
