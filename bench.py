@@ -8,11 +8,14 @@ step reads a different copy of them (enough copies to cover > 1 GiB), so the
 256 MB Infinity Cache cannot serve the logits of the step before.
 
 Prints ONE JSON line with verified draft positions/s, the roofline of the
-dominant kernel (the row-statistics kernel k_stats, timed with HIP events that
-spec_verify records on the call's stream around it, in every
---event-every'th timed step: event records between kernels cost a few
-microseconds each, so they are not put into every step) and the CPU oracle
-timed on the host cores on a bounded sample of the same workload.
+dominant kernel and the CPU oracle timed on the host cores on a bounded sample
+of the same workload.  The dominant kernel is the single dispatch k_fused
+that runs the whole stochastic step of a short batch (the Llama-3-shaped one;
+its algorithmic bytes are those of the whole step), else the row-statistics
+kernel k_stats.  It is timed with HIP events that spec_verify records on the
+call's stream at the dispatch's own start and end, in every
+--event-every'th timed step (event records cost a few microseconds each, so
+they are not put into every step).
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3]
 """
@@ -29,7 +32,9 @@ sys.path.insert(0, ROOT)
 sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
-PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic_rowstats_llama3.txt")
+# rocprofv3 HBM counter summaries of the dominant kernel on the Llama-3-shaped workload
+PROFILE_TRAFFIC = {"k_fused": os.path.join(ROOT, "profiles", "traffic_fused_llama3.txt"),
+                   "k_stats": os.path.join(ROOT, "profiles", "traffic_rowstats_llama3.txt")}
 KERNEL_SRC = os.path.join(ROOT, "draft_token_verification_05_amd", "csrc", "kernels.hip")
 
 WORKLOADS = {
@@ -43,20 +48,26 @@ WORKLOADS = {
 
 
 def kernel_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments and whitespace do not count,
+    so a profile stays valid across edits of comments only."""
+    import re
+    text = re.sub(r"//[^\n]*", "", open(KERNEL_SRC).read())
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
 
 
-def load_traffic():
-    """HBM bytes per row-statistics launch from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source (else None)."""
-    if not os.path.exists(PROFILE_TRAFFIC):
+def load_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source for that kernel
+    (else None)."""
+    path = PROFILE_TRAFFIC.get(kernel)
+    if path is None or not os.path.exists(path):
         return None
     kv = {}
-    for line in open(PROFILE_TRAFFIC):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernels_hip_sha256_16") != kernel_hash():
+    if kv.get("kernels_hip_sha256_16") != kernel_hash() or kv.get("kernel") != kernel:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -183,9 +194,13 @@ def run_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
     hip.destroy(ev_all)
     rowstats_bytes, step_bytes = algorithmic_bytes(w, num_acc)
     positions = int(w.gamma.sum())
+    # events [1] and [2] bracket the single dispatch of the whole step when
+    # the library runs it as one kernel, else the row-statistics kernel
+    single = sv.spec_verify_single_dispatch(cfg0, mode) == 1
     return dict(w=w, desc=desc, mode=mode, steps=steps, ncopies=ncopies, total_ms=total_ms, wall_s=wall,
                 ms_per_step=total_ms / steps, rowstats_ms=float(rs.mean()), rowstats_med_ms=float(np.median(rs)),
-                rowstats_bytes=rowstats_bytes, step_bytes=step_bytes, positions=positions, sampled=len(sampled))
+                rowstats_bytes=rowstats_bytes, step_bytes=step_bytes, positions=positions, sampled=len(sampled),
+                kernel="k_fused" if single else "k_stats", kernel_bytes=step_bytes if single else rowstats_bytes)
 
 
 def cpu_baseline(name, budget_s=8.0):
@@ -238,8 +253,8 @@ def main():
     r = run_gpu(args.workload, args.steps, args.warmup, event_every=max(1, args.event_every))
     w = r["w"]
     value = r["positions"] / (r["ms_per_step"] * 1e-3)
-    achieved = r["rowstats_bytes"] / (r["rowstats_ms"] * 1e-3) / 1e9
-    traffic = load_traffic() if args.workload == "llama3" else None
+    achieved = r["kernel_bytes"] / (r["rowstats_ms"] * 1e-3) / 1e9
+    traffic = load_traffic(r["kernel"]) if args.workload == "llama3" else None
     line = {
         "metric": "verified draft positions/sec at V=128256 (bf16); achieved HBM GB/s vs peak",
         "value": round(value, 1),
@@ -258,9 +273,9 @@ def main():
                    "positions_per_step": r["positions"], "input_copies_rotated": r["ncopies"],
                    "step_GBps": round(r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1),
                    "step_frac_of_peak": round(r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-        "roofline": {"bound": "hbm", "kernel": "k_stats", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+        "roofline": {"bound": "hbm", "kernel": r["kernel"], "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "bytes_per_launch": r["rowstats_bytes"],
+                     "traffic": traffic, "bytes_per_launch": r["kernel_bytes"],
                      "avg_launch_us": round(r["rowstats_ms"] * 1e3, 3), "timed_launches": r["sampled"]},
         "cpu_baseline": None if args.no_cpu else cpu_baseline(args.workload),
     }

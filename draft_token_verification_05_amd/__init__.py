@@ -12,6 +12,7 @@ C entry points (``include/specverify.h``) and their Python counterparts:
 * ``spec_verify_workspace_size`` -> :func:`spec_verify_workspace_size`
 * ``spec_verify_status_string``  -> :func:`spec_verify_status_string`
 * ``spec_verify_version``        -> :func:`spec_verify_version`
+* ``spec_verify_single_dispatch`` -> :func:`spec_verify_single_dispatch`
 """
 from __future__ import annotations
 
@@ -38,7 +39,7 @@ class sv_config(ctypes.Structure):
         ("vocab", ctypes.c_int32),
         ("dtype", ctypes.c_int32),
         ("max_gamma", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("wait_polls", ctypes.c_int32),
         ("total_draft_rows", ctypes.c_int64),
         ("stream", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
@@ -77,6 +78,8 @@ def _load() -> ctypes.CDLL:
     lib.spec_verify_status_string.argtypes = [ctypes.c_int]
     lib.spec_verify_version.restype = ctypes.c_int
     lib.spec_verify_version.argtypes = []
+    lib.spec_verify_single_dispatch.restype = ctypes.c_int
+    lib.spec_verify_single_dispatch.argtypes = [ctypes.POINTER(sv_config), i32, i32]
     return lib
 
 
@@ -85,8 +88,9 @@ _lib = _load()
 
 def make_config(batch: int, vocab: int, dtype: int, max_gamma: int, total_draft_rows: int, stream: int = 0,
                 workspace: int = 0, workspace_bytes: int = 0, out_p_x: int = 0, out_q_x: int = 0,
-                out_resid_mass: int = 0, out_tree_node: int = 0, phase_events: int = 0) -> sv_config:
-    return sv_config(ctypes.sizeof(sv_config), int(batch), int(vocab), int(dtype), int(max_gamma), 0,
+                out_resid_mass: int = 0, out_tree_node: int = 0, phase_events: int = 0,
+                wait_polls: int = 0) -> sv_config:
+    return sv_config(ctypes.sizeof(sv_config), int(batch), int(vocab), int(dtype), int(max_gamma), int(wait_polls),
                      int(total_draft_rows), stream or None, workspace or None, int(workspace_bytes),
                      out_p_x or None, out_q_x or None, out_resid_mass or None, out_tree_node or None,
                      phase_events or None)
@@ -100,6 +104,11 @@ def spec_verify(target_logits: int, draft_logits: int, draft_tokens: int, gamma_
                                 gamma_per_req or None, temperature or None, u_accept or None, u_resample or None,
                                 int(mode), float(delta), tree_parents or None, out_tokens or None,
                                 out_num_accepted or None, out_nkl or None, ctypes.byref(cfg)))
+
+
+def spec_verify_single_dispatch(cfg: sv_config, mode: int, with_nkl: bool = False) -> int:
+    """1 if spec_verify runs this configuration as one kernel dispatch, else 0."""
+    return int(_lib.spec_verify_single_dispatch(ctypes.byref(cfg), int(mode), int(bool(with_nkl))))
 
 
 def spec_verify_workspace_size(cfg: sv_config) -> int:
@@ -171,12 +180,13 @@ def _check(t, name, dtype, numel=None, dev=None):
 def verify(target_logits, draft_logits, draft_tokens, gamma_per_req, temperature=None, u_accept=None,
            u_resample=None, mode: int | str = SV_MODE_STOCHASTIC, delta: float = 0.15, tree_parents=None, *,
            max_gamma: Optional[int] = None, workspace=None, diagnostics: bool = False, out_nkl: bool = False,
-           phase_events: int = 0, stream=None) -> VerifyOutput:
+           phase_events: int = 0, stream=None, wait_polls: int = 0) -> VerifyOutput:
     """Runs one verify step on device tensors (packed layout, see specverify.h).
 
     ``target_logits`` [sum(gamma+1), V] and ``draft_logits`` [sum(gamma), V] are
     torch.bfloat16 or torch.float32 on the GPU.  The call is asynchronous on
-    ``stream`` (default: torch's current stream)."""
+    ``stream`` (default: torch's current stream).  A ``workspace`` passed in must
+    be zero-filled before its first use (calls leave it reusable)."""
     import torch
     if isinstance(mode, str):
         mode = MODES[mode]
@@ -219,7 +229,7 @@ def verify(target_logits, draft_logits, draft_tokens, gamma_per_req, temperature
         tnode = torch.empty(B, dtype=torch.int32, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    cfg = make_config(B, V, dt, max_gamma, R_d, stream=int(stream.cuda_stream))
+    cfg = make_config(B, V, dt, max_gamma, R_d, stream=int(stream.cuda_stream), wait_polls=wait_polls)
     need = spec_verify_workspace_size(cfg)
     if workspace is None:
         workspace = workspace_for(cfg, dev)

@@ -2,6 +2,8 @@
 // launch sequence.  Declared in include/specverify.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -13,13 +15,30 @@ namespace {
 
 thread_local char g_hip_error[256] = "";
 
+// Polls of a statistics partial before a helper of the fused kernel computes
+// it itself (when cfg->wait_polls is 0): a few milliseconds, far above the
+// normal wait of a few microseconds.
+constexpr int32_t kDefaultWaitPolls = 4096;
+
+// Epochs that tag the fused kernel's partials: one per call, never 0 (the
+// value of a zero-filled workspace).  The start differs between processes, so
+// a workspace handed between them does not meet its own old tags.
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{
+      (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u};
+  uint32_t e;
+  do e = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
+  while (e == 0u);
+  return e;
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Host-side checks of everything that needs no device data.
 int validate(const void* target, const void* draft, const int32_t* tokens, const int32_t* gamma, const float* temp,
              const float* ua, const float* ur, int32_t mode, float delta, const int32_t* parents,
              const int32_t* out_tokens, const int32_t* out_num, const float* out_nkl, const sv_config* cfg) {
-  if (!cfg || cfg->struct_size != sizeof(sv_config) || cfg->reserved != 0) return SV_EINVAL;
+  if (!cfg || cfg->struct_size != sizeof(sv_config) || cfg->wait_polls < 0) return SV_EINVAL;
   if (cfg->batch <= 0 || cfg->vocab <= 0) return SV_EINVAL;
   if (cfg->dtype != SV_DTYPE_F32 && cfg->dtype != SV_DTYPE_BF16) return SV_EINVAL;
   if (mode < SV_MODE_STOCHASTIC || mode > SV_MODE_TREE_GREEDY) return SV_EINVAL;
@@ -84,6 +103,28 @@ const char* spec_verify_status_string(int status) {
 
 int spec_verify_version(void) { return SPECVERIFY_VERSION; }
 
+int spec_verify_single_dispatch(const sv_config* cfg, int32_t mode, int32_t with_nkl) {
+  if (!cfg || cfg->struct_size != sizeof(sv_config) || cfg->batch <= 0 || cfg->vocab <= 0 ||
+      cfg->total_draft_rows < 0 || (cfg->dtype != SV_DTYPE_F32 && cfg->dtype != SV_DTYPE_BF16) ||
+      mode < SV_MODE_STOCHASTIC || mode > SV_MODE_TREE_GREEDY)
+    return SV_EINVAL;
+  if (mode != SV_MODE_STOCHASTIC || with_nkl || cfg->batch > sv::kLdsBatch) return 0;
+  if (cfg->total_draft_rows * (int64_t)((cfg->vocab + sv::chunk_stats(cfg->dtype, mode) - 1) /
+                                        sv::chunk_stats(cfg->dtype, mode)) > INT32_MAX)
+    return 0;
+  sv::Params p{};
+  p.B = cfg->batch;
+  p.V = cfg->vocab;
+  p.dtype = cfg->dtype;
+  p.mode = mode;
+  p.R_d = (int32_t)cfg->total_draft_rows;
+  p.n_task = p.R_d;
+  p.nch = (int32_t)((p.V + sv::chunk_stats(p.dtype, mode) - 1) / sv::chunk_stats(p.dtype, mode));
+  // the vector-load variant: the one whose occupancy the plan uses for aligned rows
+  const bool vec = ((size_t)p.V * (size_t)sv::elem_size(p.dtype)) % 16 == 0;
+  return sv::plan_fused(p, vec) > 0 ? 1 : 0;
+}
+
 int spec_verify(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
                 const int32_t* gamma_per_req, const float* temperature, const float* u_accept,
                 const float* u_resample, int32_t mode, float delta, const int32_t* tree_parents,
@@ -143,12 +184,28 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   const bool vec = ((size_t)V * es) % 16 == 0 && aligned(target_logits, 16) &&
                    (!draft_logits || aligned(draft_logits, 16));
 
-  sv::plan_stats(p, vec);
-  sv::plan_decide(p, vec);
-
   hipStream_t s = static_cast<hipStream_t>(cfg->stream);
   hipEvent_t* ev = static_cast<hipEvent_t*>(cfg->phase_events);
   hipError_t e;
+
+  // stochastic batches that scan their offsets in LDS, want no KL output and
+  // have a short statistics pass: the whole step in one dispatch
+  const int fused_grid =
+      (mode == SV_MODE_STOCHASTIC && !p.want_kl && B <= sv::kLdsBatch) ? sv::plan_fused(p, vec) : 0;
+  if (fused_grid > 0) {
+    p.epoch = next_epoch();
+    p.wait_polls = cfg->wait_polls > 0 ? cfg->wait_polls : kDefaultWaitPolls;
+    const int grid = fused_grid;
+    if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e);
+    if ((e = (hipError_t)sv::launch_fused(p, vec, grid, s, ev ? ev[1] : nullptr, ev ? ev[2] : nullptr)) !=
+        hipSuccess)
+      return hip_fail(e);
+    if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e);
+    return SV_OK;
+  }
+
+  sv::plan_stats(p, vec);
+  sv::plan_decide(p, vec);
   if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e);
   // small batches scan their offsets inside the statistics kernel
   if (B > sv::kLdsBatch && (e = (hipError_t)sv::launch_prep(p, s)) != hipSuccess) return hip_fail(e);

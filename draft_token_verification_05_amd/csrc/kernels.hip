@@ -1,6 +1,11 @@
 // gfx950 kernels of the speculative-decoding verify step.
 //
-// Launches per call (all on the caller's stream):
+// Launches per call (all on the caller's stream).  A stochastic batch of at
+// most kLdsBatch requests without KL output and with a short statistics pass
+// runs as ONE dispatch, k_fused: its workgroups stream the statistics pass
+// exactly as k_stats does (partials tagged with the call's epoch), then take
+// the helper roles of k_decide, each waiting (bounded) for its request's
+// partials instead of a kernel boundary.  Every other call:
 //   k_prep      batches above kLdsBatch only: one workgroup scans gamma into
 //               the packed offsets, builds the row -> request maps and checks
 //               the layout.  Smaller batches do this scan in LDS inside
@@ -409,6 +414,23 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Params p) {
 }
 
 // ----------------------------------------------------------------------------
+// cross-workgroup hand-over inside one dispatch.  Values that another
+// workgroup reads during the same dispatch are written and read at device
+// scope (they bypass the per-XCD L2, which is not coherent between XCDs); a
+// writer publishes a flag or counts itself only after all of its stores have
+// completed.
+// ----------------------------------------------------------------------------
+
+template <class T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <class T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ----------------------------------------------------------------------------
 // k_stats: the streaming pass
 // ----------------------------------------------------------------------------
 
@@ -430,6 +452,7 @@ struct StatsShared {
   int i[kWaves];
   double d[4][kWaves];
   int bad;
+  PartA scratch;  // fused kernel: a recomputed partial on its way to the workspace
 };
 
 // Packed offsets of a batch of at most kLdsBatch requests, scanned in LDS:
@@ -665,9 +688,12 @@ __device__ __forceinline__ void fold_chunk(Lane& L, const Vecs<NV>& qt, const Ve
 }
 
 // Reduces the lane states over the workgroup and writes the segment's partial
-// (thread 0, plain stores: the consumer is a later kernel).
-template <bool SOFT, bool IDX, bool WZ, bool PAIR>
-__device__ __forceinline__ void reduce_store(const Lane& L, float Lhi, PartA* dst, StatsShared& sh) {
+// (thread 0).  Plain stores when the consumer is a later kernel.  FUSED
+// (stochastic, consumers in the same dispatch): device-scope stores and, once
+// they have completed, the call's epoch in dst->tag.
+template <bool SOFT, bool IDX, bool WZ, bool PAIR, bool FUSED = false>
+__device__ __forceinline__ void reduce_store(const Lane& L, float Lhi, PartA* dst, StatsShared& sh,
+                                             uint32_t epoch = 0) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const float wt = wave_max(L.mt);
   const float wd = PAIR ? wave_max(L.md) : 0.f;
@@ -716,15 +742,26 @@ __device__ __forceinline__ void reduce_store(const Lane& L, float Lhi, PartA* ds
       s2 += sh.d[2][k];
       s3 += sh.d[3][k];
     }
-    dst->m_t = Mt;
-    if (IDX) dst->idx = I;
-    if (SOFT) dst->s_t = s0;
-    if (PAIR) {
-      dst->m_d = Md;
-      dst->s_d = s1;
-      if (WZ) {
-        dst->w = s2;
-        dst->z = s3;
+    if constexpr (FUSED) {
+      st_dev(&dst->m_t, Mt);
+      st_dev(&dst->s_t, s0);
+      st_dev(&dst->m_d, Md);
+      st_dev(&dst->s_d, s1);
+      __asm__ __volatile__("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0);  // the fields have completed before the tag is stored
+      __asm__ __volatile__("" ::: "memory");
+      st_dev(&dst->tag, epoch);
+    } else {
+      dst->m_t = Mt;
+      if (IDX) dst->idx = I;
+      if (SOFT) dst->s_t = s0;
+      if (PAIR) {
+        dst->m_d = Md;
+        dst->s_d = s1;
+        if (WZ) {
+          dst->w = s2;
+          dst->z = s3;
+        }
       }
     }
   }
@@ -785,23 +822,28 @@ __device__ __forceinline__ void next_desc(const Params& p, const StatsShared& sh
   }
 }
 
-// WZ (stochastic only): also the KL cross terms, for the optional NKL output.
-// Each workgroup streams its item range with two register buffers in turn:
-// the loads of item i + 1 (also across a task boundary) are in flight while
-// item i is folded; a task segment ends with a workgroup reduction whose
-// barriers wait on LDS only, so the next loads stay in flight through it.
-// LDS: the batch is small enough for the offsets to be scanned in LDS.
-template <int DT, bool VEC, int MODE, bool WZ, bool LDS>
-__global__ __launch_bounds__(kThreads) void k_stats(Params p) {
+// The streaming pass of one workgroup.  WZ (stochastic only): also the KL
+// cross terms, for the optional NKL output.  Each workgroup streams its item
+// range with two register buffers in turn: the loads of item i + 1 (also
+// across a task boundary) are in flight while item i is folded; a task segment
+// ends with a workgroup reduction whose barriers wait on LDS only, so the next
+// loads stay in flight through it.  LDS: the batch is small enough for the
+// offsets to be scanned in LDS.  FUSED (stochastic, LDS): partials are tagged
+// for helpers of the same dispatch, workgroups numbered
+// p.stats_grid and above stream nothing, and nothing is published for later
+// kernels.  Returns false when the offsets scan found a layout error.
+template <int DT, bool VEC, int MODE, bool WZ, bool LDS, bool FUSED>
+__device__ __forceinline__ bool stats_phase(const Params& p, StatsShared& sh) {
   constexpr bool SOFT = MODE == SV_MODE_STOCHASTIC || MODE == SV_MODE_NKL;
   constexpr int NV = SOFT ? 2 : 4;
   constexpr bool IDX = MODE != SV_MODE_STOCHASTIC;
   constexpr bool WZM = MODE == SV_MODE_NKL || WZ;
-  __shared__ StatsShared sh;
-  const int G = (int)gridDim.x, wg = (int)blockIdx.x;
+  static_assert(!FUSED || (LDS && MODE == SV_MODE_STOCHASTIC && !WZ), "fused: stochastic, LDS scan, no KL");
+  const int G = p.stats_grid, wg = (int)blockIdx.x;
+  const bool streams = !FUSED || wg < G;
   const int64_t N = (int64_t)p.n_task * p.nch;
-  const int64_t i_end = (int64_t)(wg + 1) * N / G;
-  int64_t i = (int64_t)wg * N / G;
+  const int64_t i_end = streams ? (int64_t)(wg + 1) * N / G : 0;
+  int64_t i = streams ? (int64_t)wg * N / G : 0;
   Desc dA, dB;
   Vecs<NV> At, Ad, Bt, Bd;
   int b = -1;
@@ -820,8 +862,8 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params p) {
     const bool has = i < i_end;
     const void* base = (MODE == SV_MODE_STOCHASTIC && has) ? p.draft : p.target;
     issue_row<DT, VEC, NV>(base, has ? dA.task : 0, has ? dA.chunk : 0, p.V, MODE == SV_MODE_STOCHASTIC ? Ad : At);
-    if (!scan_offsets_lds(p, sh, scan_in, SOFT, wg == 0)) return;
-    if (!has) return;
+    if (!scan_offsets_lds(p, sh, scan_in, SOFT, !FUSED && wg == 0)) return false;
+    if (!has) return true;
     set_rows<MODE, LDS>(p, sh, b, dA);
     if (MODE == SV_MODE_STOCHASTIC) issue_row<DT, VEC, NV>(p.target, dA.trow, dA.chunk, p.V, At);
     else if (dA.pair) issue_row<DT, VEC, NV>(p.draft, dA.drow, dA.chunk, p.V, Ad);
@@ -829,11 +871,11 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params p) {
     if (LDS) {
       // greedy and tree tasks are target rows: only workgroup 0 needs the
       // scan, to publish the offsets for the decision kernel
-      if (wg == 0 && !scan_offsets_lds(p, sh, scan_load(p, SOFT), SOFT, true)) return;
+      if (wg == 0 && !scan_offsets_lds(p, sh, scan_load(p, SOFT), SOFT, true)) return false;
     } else if (SOFT && p.hdr[0] != 0) {
-      return;  // the prep kernel found a layout error
+      return false;  // the prep kernel found a layout error
     }
-    if (i >= i_end) return;
+    if (i >= i_end) return true;
     dA.task = (int)(i / p.nch);
     dA.chunk = (int)(i - (int64_t)dA.task * p.nch);
     set_rows<MODE, LDS>(p, sh, b, dA);
@@ -841,28 +883,33 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params p) {
   }
   Lane L;
   lane_reset(L);
+  const auto store = [&](const Desc& d) {
+    const int w_lo = wg_of((int64_t)d.task * p.nch, N, G);
+    PartA* dst = p.part_a + (int64_t)d.task * p.nch + (wg - w_lo);
+    reduce_store<SOFT, IDX, WZM, SOFT, FUSED>(L, d.Lhi, dst, sh, p.epoch);
+    lane_reset(L);
+  };
   for (;;) {
     dB = dA;
     if (i + 1 < i_end) next_desc<MODE, LDS>(p, sh, b, dB);
     issue_chunk<DT, VEC, NV, SOFT>(p, dB, Bt, Bd);  // the last item reloads itself (cache hit)
     fold_chunk<DT, NV, SOFT, IDX, WZM, SOFT>(L, At, Ad, dA, p.V);
-    if (dA.chunk == p.nch - 1 || i + 1 == i_end) {
-      reduce_store<SOFT, IDX, WZM, SOFT>(L, dA.Lhi, p.part_a + (int64_t)dA.task * p.nch +
-                                                        (wg - wg_of((int64_t)dA.task * p.nch, N, G)), sh);
-      lane_reset(L);
-    }
+    if (dA.chunk == p.nch - 1 || i + 1 == i_end) store(dA);
     if (++i >= i_end) break;
     dA = dB;
     if (i + 1 < i_end) next_desc<MODE, LDS>(p, sh, b, dA);
     issue_chunk<DT, VEC, NV, SOFT>(p, dA, At, Ad);
     fold_chunk<DT, NV, SOFT, IDX, WZM, SOFT>(L, Bt, Bd, dB, p.V);
-    if (dB.chunk == p.nch - 1 || i + 1 == i_end) {
-      reduce_store<SOFT, IDX, WZM, SOFT>(L, dB.Lhi, p.part_a + (int64_t)dB.task * p.nch +
-                                                        (wg - wg_of((int64_t)dB.task * p.nch, N, G)), sh);
-      lane_reset(L);
-    }
+    if (dB.chunk == p.nch - 1 || i + 1 == i_end) store(dB);
     if (++i >= i_end) break;
   }
+  return true;
+}
+
+template <int DT, bool VEC, int MODE, bool WZ, bool LDS>
+__global__ __launch_bounds__(kThreads) void k_stats(Params p) {
+  __shared__ StatsShared sh;
+  stats_phase<DT, VEC, MODE, WZ, LDS, false>(p, sh);
 }
 
 // ----------------------------------------------------------------------------
@@ -897,7 +944,8 @@ __device__ __forceinline__ double rescale(float m, float M, float Lhi) {
 // group combines by an xor butterfly, so every lane of the group ends with the
 // same values.  `pair`: the task has draft statistics.  All lanes of the
 // wave must call this.
-template <bool SOFT>
+// DEV: the partials were written during this dispatch (device-scope loads).
+template <bool SOFT, bool DEV = false>
 __device__ __forceinline__ Merged merge_task(const Params& p, int64_t task, bool has, bool pair, int l, int glog,
                                              float Lhi) {
   const int S = 1 << glog;
@@ -907,20 +955,20 @@ __device__ __forceinline__ Merged merge_task(const Params& p, int64_t task, bool
   r.st = r.sd = r.w = r.z = 0.0;
   if (has) {
     const int64_t N = (int64_t)p.n_task * p.nch;
-    const int w_lo = wg_of(task * p.nch, N, p.stats_grid);
-    const int nseg = wg_of((task + 1) * p.nch - 1, N, p.stats_grid) - w_lo + 1;
+    const int nseg = wg_of((task + 1) * p.nch - 1, N, p.stats_grid) - wg_of(task * p.nch, N, p.stats_grid) + 1;
     const PartA* src = p.part_a + task * p.nch;
+    const auto rd = [](const auto& v) { return DEV ? ld_dev(&v) : v; };
     for (int s = l; s < nseg; s += S) {
-      const float mt = src[s].m_t;
-      const int ix = src[s].idx;
+      const float mt = rd(src[s].m_t);
+      const int ix = rd(src[s].idx);
       if (mt > r.mt || (mt == r.mt && ix < r.idx)) r.idx = ix;
       if (SOFT && pair) {
-        const float Mt = fmaxf(r.mt, mt), md = src[s].m_d, Md = fmaxf(r.md, md);
+        const float Mt = fmaxf(r.mt, mt), md = rd(src[s].m_d), Md = fmaxf(r.md, md);
         const double fo = rescale(r.md, Md, Lhi), fn = rescale(md, Md, Lhi);
-        r.st = r.st * rescale(r.mt, Mt, Lhi) + src[s].s_t * rescale(mt, Mt, Lhi);
-        r.sd = r.sd * fo + src[s].s_d * fn;
-        r.w = r.w * fo + src[s].w * fn;
-        r.z = r.z * fo + src[s].z * fn;
+        r.st = r.st * rescale(r.mt, Mt, Lhi) + rd(src[s].s_t) * rescale(mt, Mt, Lhi);
+        r.sd = r.sd * fo + rd(src[s].s_d) * fn;
+        r.w = r.w * fo + rd(src[s].w) * fn;
+        r.z = r.z * fo + rd(src[s].z) * fn;
         r.md = Md;
       }
       r.mt = fmaxf(r.mt, mt);
@@ -961,6 +1009,93 @@ __device__ __forceinline__ Merged merge_task(const Params& p, int64_t task, bool
   r.md = Md;
   r.idx = ix;
   return r;
+}
+
+// ----------------------------------------------------------------------------
+// fused kernel: the wait of a helper for its request's statistics
+// ----------------------------------------------------------------------------
+
+// Partial of segment `seg` of stochastic task `task` (the chunks of the task
+// that statistics workgroup w_lo(task) + seg streams), computed again by the
+// calling workgroup with the same chunk order, lane mapping and reduction as
+// the statistics pass, so it is bit-identical to the original.  All threads
+// call.
+template <int DT, bool VEC>
+__device__ void recompute_segment(const Params& p, StatsShared& sh, int task, int seg) {
+  const int G = p.stats_grid;
+  const int64_t N = (int64_t)p.n_task * p.nch;
+  const int64_t first = (int64_t)task * p.nch;
+  const int w = wg_of(first, N, G) + seg;
+  const int64_t lo = max(first, (int64_t)w * N / G);
+  const int64_t hi = min(first + p.nch, (int64_t)(w + 1) * N / G);
+  Desc d;
+  int b = -1;
+  d.task = task;
+  d.chunk = (int)(lo - first);
+  set_rows<SV_MODE_STOCHASTIC, true>(p, sh, b, d);
+  Lane L;
+  lane_reset(L);
+  for (int64_t i = lo; i < hi; ++i, ++d.chunk) {
+    Vecs<2> qt, qd;
+    issue_chunk<DT, VEC, 2, true>(p, d, qt, qd);
+    fold_chunk<DT, 2, true, false, false, true>(L, qt, qd, d, p.V);
+  }
+  reduce_store<true, false, false, true>(L, d.Lhi, &sh.scratch, sh);  // into LDS first
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    PartA* dst = p.part_a + first + seg;
+    st_dev(&dst->m_t, sh.scratch.m_t);
+    st_dev(&dst->s_t, sh.scratch.s_t);
+    st_dev(&dst->m_d, sh.scratch.m_d);
+    st_dev(&dst->s_d, sh.scratch.s_d);
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);  // the fields have completed before the tag is stored
+    __asm__ __volatile__("" ::: "memory");
+    st_dev(&dst->tag, p.epoch);
+  }
+  __syncthreads();
+}
+
+// Returns once every statistics partial of tasks [t0, t0 + nt) carries this
+// call's epoch.  Each thread polls some partials, up to p.wait_polls times; a
+// partial still missing after that (its workgroup is not resident, or slow)
+// is computed by this workgroup itself, so the wait is bounded and the result
+// does not depend on which workgroups run when.  All threads call.
+template <int DT, bool VEC>
+__device__ void await_partials(const Params& p, StatsShared& sh, int t0, int nt, int* miss) {
+  const int G = p.stats_grid;
+  const int64_t N = (int64_t)p.n_task * p.nch;
+  const int S = 1 << p.grp_log2;
+  const int TPP = kThreads >> p.grp_log2;
+  bool missing = false;
+  for (int base = 0; base < nt; base += TPP) {
+    const int ti = base + ((int)threadIdx.x >> p.grp_log2), seg = threadIdx.x & (S - 1);
+    if (ti >= nt) continue;
+    const int64_t task = t0 + ti;
+    const int nseg = wg_of((task + 1) * p.nch - 1, N, G) - wg_of(task * p.nch, N, G) + 1;
+    if (seg >= nseg) continue;
+    const uint32_t* tag = &p.part_a[task * p.nch + seg].tag;
+    bool ready = ld_dev(tag) == p.epoch;
+    for (int k = 0; !ready && k < p.wait_polls; ++k) {
+      __builtin_amdgcn_s_sleep(2);
+      ready = ld_dev(tag) == p.epoch;
+    }
+    if (!ready) missing = true;
+  }
+  if (!__syncthreads_or(missing)) return;
+  // the fallback: every partial of the range is checked once more, in order,
+  // and computed here if it is still missing
+  for (int ti = 0; ti < nt; ++ti) {
+    const int64_t task = t0 + ti;
+    const int nseg = wg_of((task + 1) * p.nch - 1, N, G) - wg_of(task * p.nch, N, G) + 1;
+    for (int seg = 0; seg < nseg; ++seg) {
+      if (threadIdx.x == 0) *miss = ld_dev(&p.part_a[task * p.nch + seg].tag) != p.epoch;
+      __syncthreads();
+      const bool m = *miss != 0;
+      __syncthreads();
+      if (m) recompute_segment<DT, VEC>(p, sh, (int)task, seg);
+    }
+  }
 }
 
 // g(w) = e^w - 1 - w >= 0, accurate for small |w| (Taylor series to w^9)
@@ -1059,21 +1194,6 @@ __device__ __forceinline__ double kl_terms(const uint4* qt, const uint4* qd, con
   return acc;
 }
 
-// ----------------------------------------------------------------------------
-// cross-workgroup hand-over inside k_decide.  Values that another workgroup
-// reads during the same dispatch are written and read at device scope (they
-// bypass the per-XCD L2, which is not coherent between XCDs); a helper counts
-// itself only after all of its stores have completed.
-// ----------------------------------------------------------------------------
-
-template <class T>
-__device__ __forceinline__ void st_dev(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <class T>
-__device__ __forceinline__ T ld_dev(const T* p) {
-  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 struct DecideShared {
   float mt[kThreads], md[kThreads];
@@ -1116,8 +1236,10 @@ __device__ __forceinline__ int block_excl_count(bool flag, int* tail, DecideShar
   return before + in_wave;
 }
 
-// Counts this helper on the request's counter once every store of the
-// workgroup has completed; true in the last of the `H` helpers to arrive.
+// Counts this workgroup on the request's counter once every store of the
+// workgroup has completed; true in the last of the `H` arrivals.  The counter
+// wraps to zero on the last arrival (atomic increment modulo H), so it is
+// back at zero for the next call without a reset.
 template <class SH>
 __device__ __forceinline__ bool arrive_last(uint32_t* cnt, int H, SH& sh) {
   __asm__ __volatile__("" ::: "memory");
@@ -1125,7 +1247,7 @@ __device__ __forceinline__ bool arrive_last(uint32_t* cnt, int H, SH& sh) {
   __asm__ __volatile__("" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __builtin_amdgcn_atomic_inc32(cnt, (uint32_t)H - 1u, __ATOMIC_RELAXED, "agent");
     sh.flag = old + 1 == (uint32_t)H ? 1 : 0;
   }
   __syncthreads();
@@ -1310,7 +1432,8 @@ __device__ __forceinline__ double token_weight(float t, float d, bool two, const
 // order; the wave-chunk that holds the draw is read again, lane l taking NE
 // consecutive tokens, and scanned token by token.  No workgroup barrier.
 template <int DT, bool VEC, bool CACHED>
-__device__ __forceinline__ void draw_select(const Params& p, int b, const Term& tm, int NW, DecideShared& sh) {
+__device__ __forceinline__ void draw_select(const Params& p, int b, const Term& tm, int NW, float ur,
+                                            DecideShared& sh) {
   constexpr int P = Elem<DT>::P;
   constexpr int NE = kUT * P;
   constexpr int64_t CHW = (int64_t)64 * NE;
@@ -1356,7 +1479,7 @@ __device__ __forceinline__ void draw_select(const Params& p, int b, const Term& 
     fb = true;
     S = at;
   }
-  const double target = (double)p.ur[b] * S;
+  const double target = (double)ur * S;
 
   // the wave-chunk whose cumulative weight first exceeds the target: one round
   // per 64 consecutive chunks
@@ -1485,26 +1608,22 @@ __device__ __forceinline__ void kl_finish(const Params& p, int b, SH& sh) {
 // k_decide
 // ----------------------------------------------------------------------------
 
-template <int DT, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads) void k_decide(Params p) {
+// The decision and terminal draw of request b by its helper h.  ok: the
+// packed layout is valid; d0, d1: the request's draft-row offsets; T, ur: its
+// temperature and resample uniform (ur is first used after the decision, so
+// its load may still be in flight).  FUSED (stochastic): called in the
+// statistics kernel itself, where it waits for the request's partials.
+template <int DT, bool VEC, int MODE, bool FUSED>
+__device__ __forceinline__ void decide_request(const Params& p, int b, int h, bool ok, int d0, int d1, float T,
+                                               float ur, DecideShared& sh, TreeShared<MODE>& tr, StatsShared* ssh) {
   constexpr bool SOFT = MODE == SV_MODE_STOCHASTIC || MODE == SV_MODE_NKL;
-  __shared__ DecideShared sh;
-  __shared__ TreeShared<MODE> tr;
   const int H = p.helpers, NS = p.nslices;
-  const int b = (int)(blockIdx.x % (unsigned)p.B);
-  const int h = (int)(blockIdx.x / (unsigned)p.B);
   // helper h streams slices [s0, s1) wherever rows get a second look
   const int s0 = h * p.slices_per_helper, s1 = min(NS, s0 + p.slices_per_helper);
   const bool writer = h == 0;  // helper 0 writes the outputs of the decision
   const int tid = threadIdx.x;
   const bool want_kl = SOFT && p.want_kl;
-  // independent loads first, so that they are in flight together
-  const int hdr = p.hdr[0];
-  const int d0 = p.d_off[b];
-  const int d1 = p.d_off[b + 1];
-  const float T = SOFT ? p.temp[b] : 1.0f;
-  const float ur = MODE == SV_MODE_STOCHASTIC ? p.ur[b] : 0.0f;
-  if (hdr != 0) {  // layout error: only the counts are written
+  if (!ok) {  // layout error: only the counts are written
     if (writer && tid == 0) p.out_num[b] = -1;
     return;
   }
@@ -1512,10 +1631,10 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
   const int t0 = d0 + b;
   const int64_t V = p.V;
   const float Lhi = SOFT ? (float)(kLog2eD / (double)T) : 0.0f;
-  // request-level checks; the per-position ones follow the decision passes
-  // (which only read inside the rows for valid token ids), and overwrite
-  // everything the passes wrote if they fail
-  if (g > p.max_gamma || (SOFT && !temp_ok(T)) || (MODE == SV_MODE_STOCHASTIC && !unit_ok(ur))) {
+  // request-level checks; the per-position ones (and the resample uniform's)
+  // follow the decision passes (which only read inside the rows for valid
+  // token ids), and overwrite everything the passes wrote if they fail
+  if (g > p.max_gamma || (SOFT && !temp_ok(T))) {
     if (writer) finish_invalid(p, b, t0, d0, g);
     return;
   }
@@ -1533,33 +1652,51 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
   bool bad = false;
   int n_queued = 0;  // positions queued for the KL second pass (helper 0)
   int checked = 0;  // positions [0, checked) were checked inside the passes
+  // the group leader's position data of the pass starting at `base`
+  // (node ti of a tree is position ti - 1), and the per-position input checks
+  struct Pos {
+    int x;
+    float tx, dx, u;
+  };
+  const auto load_pos = [&](int base) {
+    const int ti = base + (tid >> glog);
+    Pos ps{-1, 0.f, 0.f, 0.f};
+    if ((tid & (S - 1)) == 0 && MODE != SV_MODE_TREE_GREEDY && ti < g) {
+      ps.x = p.tokens[d0 + ti];
+      const bool xok = ps.x >= 0 && ps.x < p.V;
+      if (SOFT && xok) {
+        ps.tx = load_scalar<DT>(p.target, t0 + ti, V, ps.x);
+        ps.dx = load_scalar<DT>(p.draft, d0 + ti, V, ps.x);
+      }
+      if (MODE == SV_MODE_STOCHASTIC) {
+        ps.u = p.ua[d0 + ti];
+        if (!unit_ok(ps.u)) bad = true;
+      }
+      if (!xok) bad = true;
+    }
+    if ((tid & (S - 1)) == 0 && MODE == SV_MODE_TREE_GREEDY && ti >= 1 && ti <= g) {
+      const int xn = p.tokens[d0 + ti - 1], pa = p.parents[d0 + ti - 1];
+      if (xn < 0 || xn >= p.V || pa < 0 || pa >= ti) bad = true;
+    }
+    return ps;
+  };
+  Pos pos0{-1, 0.f, 0.f, 0.f};
+  if constexpr (FUSED) {
+    // the first pass's position loads are in flight while this workgroup
+    // waits for every partial of the request
+    pos0 = load_pos(0);
+    await_partials<DT, VEC>(p, *ssh, (int)tbase, ntask, &sh.flag);
+  }
   for (int base = 0; base < ntask; base += TPP) {
     const int q = tid >> glog, l = tid & (S - 1);
     const int ti = base + q;
     const bool has = ti < ntask;
     const bool pair = SOFT && ti < g;
-    // the group leader's position data, issued before the partial loads
-    // and the per-position input checks (node ti of a tree is position ti - 1)
-    int x = -1;
-    float tx = 0.f, dx = 0.f, u = 0.f;
-    if (l == 0 && MODE != SV_MODE_TREE_GREEDY && ti < g) {
-      x = p.tokens[d0 + ti];
-      const bool xok = x >= 0 && x < p.V;
-      if (SOFT && xok) {
-        tx = load_scalar<DT>(p.target, t0 + ti, V, x);
-        dx = load_scalar<DT>(p.draft, d0 + ti, V, x);
-      }
-      if (MODE == SV_MODE_STOCHASTIC) {
-        u = p.ua[d0 + ti];
-        if (!unit_ok(u)) bad = true;
-      }
-      if (!xok) bad = true;
-    }
-    if (l == 0 && MODE == SV_MODE_TREE_GREEDY && ti >= 1 && ti <= g) {
-      const int xn = p.tokens[d0 + ti - 1], pa = p.parents[d0 + ti - 1];
-      if (xn < 0 || xn >= p.V || pa < 0 || pa >= ti) bad = true;
-    }
-    const Merged r = merge_task<SOFT>(p, tbase + ti, has, pair, l, glog, Lhi);
+    // issued before the partial loads
+    const Pos ps = (FUSED && base == 0) ? pos0 : load_pos(base);
+    const int x = ps.x;
+    const float tx = ps.tx, dx = ps.dx, u = ps.u;
+    const Merged r = merge_task<SOFT, FUSED>(p, tbase + ti, has, pair, l, glog, Lhi);
     if (l == 0 && has) {
       const int idx = r.idx == INT_MAX ? 0 : r.idx;  // no element above the pad value: position 0
       if constexpr (MODE == SV_MODE_TREE_GREEDY) tr.idx[ti] = idx;
@@ -1655,6 +1792,7 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
     __syncthreads();  // LDS of this pass is reused by the next
   }
 
+  if (MODE == SV_MODE_STOCHASTIC && tid == 0 && !unit_ok(ur)) bad = true;
   // positions the passes did not reach (an early exit) are checked here
   for (int k = checked + tid; k < g; k += kThreads) {
     const int x = p.tokens[d0 + k];
@@ -1712,9 +1850,50 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
       });
     if (arrive_last(p.cnt + b, H, sh) && tid < 64) {
       const int NW = NS * kWaves;
-      if (NW <= kSelCache) draw_select<DT, VEC, true>(p, b, tm, NW, sh);
-      else draw_select<DT, VEC, false>(p, b, tm, NW, sh);
+      if (NW <= kSelCache) draw_select<DT, VEC, true>(p, b, tm, NW, ur, sh);
+      else draw_select<DT, VEC, false>(p, b, tm, NW, ur, sh);
     }
+  }
+}
+
+// H workgroups ("helpers") per request (see decide_request), after k_stats.
+template <int DT, bool VEC, int MODE>
+__global__ __launch_bounds__(kThreads) void k_decide(Params p) {
+  constexpr bool SOFT = MODE == SV_MODE_STOCHASTIC || MODE == SV_MODE_NKL;
+  __shared__ DecideShared sh;
+  __shared__ TreeShared<MODE> tr;
+  const int b = (int)(blockIdx.x % (unsigned)p.B);
+  const int h = (int)(blockIdx.x / (unsigned)p.B);
+  // independent loads first, so that they are in flight together
+  const int hdr = p.hdr[0];
+  const int d0 = p.d_off[b];
+  const int d1 = p.d_off[b + 1];
+  const float T = SOFT ? p.temp[b] : 1.0f;
+  const float ur = MODE == SV_MODE_STOCHASTIC ? p.ur[b] : 0.0f;
+  decide_request<DT, VEC, MODE, false>(p, b, h, hdr == 0, d0, d1, T, ur, sh, tr, nullptr);
+}
+
+// The whole stochastic step in one dispatch (batches up to kLdsBatch, no KL
+// output).  Every workgroup first streams its share of the statistics pass
+// (stats_phase: partials tagged with the call's epoch, tasks marked done);
+// then workgroup r below
+// B x H takes the helper role (request r mod B, helper r / B) of the decision
+// kernel: it waits for its request's partials (await_partials, bounded, with
+// its own fallback) instead of a kernel boundary, and takes the offsets and
+// temperatures from its own LDS scan.  Vector-load variants are held to 128
+// registers (4 waves per SIMD) without spilling.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(VEC ? 4 : 1))) void k_fused(Params p) {
+  __shared__ StatsShared ssh;
+  __shared__ DecideShared sh;
+  __shared__ TreeShared<SV_MODE_STOCHASTIC> tr;
+  const bool ok = stats_phase<DT, VEC, SV_MODE_STOCHASTIC, false, true, true>(p, ssh);
+  const int r = (int)blockIdx.x;
+  if (r < p.B * p.helpers) {
+    const int b = r % p.B, h = r / p.B;
+    const float ur = p.ur[b];
+    decide_request<DT, VEC, SV_MODE_STOCHASTIC, true>(p, b, h, ok, ssh.off[b], ssh.off[b + 1], ssh.temp[b], ur, sh,
+                                                      tr, &ssh);
   }
 }
 
@@ -1791,6 +1970,25 @@ int num_cus() {
     cache[slot] = n;
   }
   return cache[slot];
+}
+
+// Statistics partition over G workgroups (at most one per item): fills
+// p.stats_grid and p.grp_log2, the lanes that merge one task's partials.
+void set_stats_grid(Params& p, int64_t G) {
+  const int64_t N = (int64_t)p.n_task * p.nch;
+  if (G > N) G = N;  // every workgroup gets at least one item
+  if (G < 1) G = 1;
+  p.stats_grid = (int32_t)G;
+  // a task's chunks are spread over at most this many workgroups
+  int64_t maxseg = 1;
+  if (N > 0) {
+    const int64_t ipw = N / G;
+    maxseg = 1 + (p.nch - 1 + ipw - 1) / ipw;
+    if (maxseg > p.nch) maxseg = p.nch;
+  }
+  int glog = 0;
+  while ((1 << glog) < maxseg && glog < 6) ++glog;
+  p.grp_log2 = glog;
 }
 
 template <int DT, bool VEC, int MODE, bool WZ>
@@ -1903,22 +2101,59 @@ int plan_stats(Params& p, bool vec) {
   else
     occ = vec ? stats_occupancy_mode<SV_DTYPE_F32, true>(p.mode, wz)
               : stats_occupancy_mode<SV_DTYPE_F32, false>(p.mode, wz);
-  const int64_t N = (int64_t)p.n_task * p.nch;
-  int64_t G = (int64_t)occ * num_cus();
-  if (G > N) G = N;  // every workgroup gets at least one item
-  if (G < 1) G = 1;
-  p.stats_grid = (int32_t)G;
-  // a task's chunks are spread over at most this many workgroups
-  int64_t maxseg = 1;
-  if (N > 0) {
-    const int64_t ipw = N / G;
-    maxseg = 1 + (p.nch - 1 + ipw - 1) / ipw;
-    if (maxseg > p.nch) maxseg = p.nch;
-  }
-  int glog = 0;
-  while ((1 << glog) < maxseg && glog < 6) ++glog;
-  p.grp_log2 = glog;
+  set_stats_grid(p, (int64_t)occ * num_cus());
   return 0;
+}
+
+int plan_fused(Params& p, bool vec) {
+  static int occ[2][2] = {{0, 0}, {0, 0}};  // [bf16][vec]; same value from every thread: a race is benign
+  int& o = occ[p.dtype == SV_DTYPE_BF16][vec];
+  if (o == 0) {
+    int v = 0;
+    hipError_t e;
+    if (p.dtype == SV_DTYPE_BF16)
+      e = vec ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_fused<SV_DTYPE_BF16, true>, kThreads, 0)
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_fused<SV_DTYPE_BF16, false>, kThreads, 0);
+    else
+      e = vec ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_fused<SV_DTYPE_F32, true>, kThreads, 0)
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_fused<SV_DTYPE_F32, false>, kThreads, 0);
+    o = (e == hipSuccess && v > 0) ? v : 1;
+  }
+  const int64_t cap = (int64_t)o * num_cus();
+  // Single dispatch only while the statistics pass is short: it saves the
+  // second launch and the hand-over to the decision (about 2.5 us at 5 items
+  // per workgroup, the 82 MB Llama-3-shaped batch), but its workgroups hold
+  // the decision's registers too (4 instead of 5 per CU), which costs more than
+  // that on long passes (about 10 us at 41 items per workgroup, the 680 MB
+  // ragged batch).
+  if ((int64_t)p.n_task * p.nch > kFusedItemsPerWg * cap) return 0;
+  set_stats_grid(p, cap);
+  // helpers per request: what the resident grid holds, at most one per slice
+  p.nslices = (int32_t)((p.V + chunk_t(p.dtype) - 1) / chunk_t(p.dtype));
+  int64_t H = cap / p.B;
+  if (H > p.nslices) H = p.nslices;
+  if (H < 1) H = 1;
+  const int64_t spp = (p.nslices + H - 1) / H;
+  p.slices_per_helper = (int32_t)spp;
+  p.helpers = (int32_t)((p.nslices + spp - 1) / spp);
+  // one helper role per workgroup (a role loop would cost registers), so a
+  // batch above the resident grid (B x H > cap) gets helpers that start as
+  // others finish
+  const int64_t roles = (int64_t)p.B * p.helpers;
+  return (int)(roles > p.stats_grid ? roles : p.stats_grid);
+}
+
+int launch_fused(const Params& p, bool vec, int grid, void* stream, void* ev_start, void* ev_stop) {
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t e0 = (hipEvent_t)ev_start, e1 = (hipEvent_t)ev_stop;
+  if (p.dtype == SV_DTYPE_BF16) {
+    if (vec) launch_timed(k_fused<SV_DTYPE_BF16, true>, dim3(grid), p, s, e0, e1);
+    else launch_timed(k_fused<SV_DTYPE_BF16, false>, dim3(grid), p, s, e0, e1);
+  } else {
+    if (vec) launch_timed(k_fused<SV_DTYPE_F32, true>, dim3(grid), p, s, e0, e1);
+    else launch_timed(k_fused<SV_DTYPE_F32, false>, dim3(grid), p, s, e0, e1);
+  }
+  return (int)hipGetLastError();
 }
 
 int launch_stats(const Params& p, bool vec, void* stream, void* ev_start, void* ev_stop) {

@@ -20,6 +20,7 @@ constexpr int kUA = 2;           // smallest of the above: sizes the partial arr
 constexpr int kUT = 4;           // 16-byte vectors per thread per row in one slice of k_decide's second look
 constexpr int kSelCache = 256;   // draw records a token selection keeps in LDS
 constexpr int kLdsBatch = 1024;  // batches up to this size scan their offsets in LDS (no prep kernel)
+constexpr int kFusedItemsPerWg = 12;  // longest statistics pass (items per resident workgroup) run in one dispatch
 
 constexpr int elems_per_vec(int dtype) { return dtype == SV_DTYPE_BF16 ? 8 : 4; }
 constexpr int elem_size(int dtype) { return dtype == SV_DTYPE_BF16 ? 2 : 4; }
@@ -37,12 +38,14 @@ enum TermKind : int32_t { kTermNone = 0, kTermResidual = 1, kTermBonus = 2 };
 // the statistics pass streamed.  m_* are raw-logit maxima, s_* = sum
 // 2^((x - m) L) with L = log2(e)/T, w = sum 2^((d - m_d) L) (d - t) and
 // z = sum 2^((d - m_d) L) |d - t| over the draft row, idx = lowest index
-// attaining m_t.
+// attaining m_t.  tag: the call's epoch, stored after the other fields by the
+// fused kernel, whose helpers read a partial only once it carries the epoch of
+// their own call.
 struct PartA {
   double s_t, s_d, w, z;
   float m_t, m_d;
   int32_t idx;
-  int32_t pad;
+  uint32_t tag;
 };
 
 // A position queued for the KL second pass, with the constants of its terms:
@@ -138,14 +141,18 @@ struct Params {
   int32_t slices_per_helper;
   float delta;
   int32_t want_kl;  // compute KL(q || p) (NKL mode, or stochastic with out_nkl)
+  uint32_t epoch;      // fused kernel: tag of this call's statistics partials (never 0)
+  int32_t wait_polls;  // fused kernel: polls of a partial before a helper computes it itself
   // workspace
   int32_t* hdr;  // hdr[0]: layout error flag, hdr[1]: positions queued for the KL second pass
   int32_t* d_off;
   int32_t* pair2req;
   int32_t* row2req;
   PartA* part_a;
-  uint32_t* cnt;      // [B] k_decide helpers done per request (zeroed by the offsets scan of each call)
-  uint32_t* cnt_kl;   // [B] KL second-pass items done per request (zeroed likewise)
+  // per-request arrival counters: the last arrival wraps them back to zero, so
+  // every completed call leaves them at zero (a new workspace is zero-filled)
+  uint32_t* cnt;      // [B] decision helpers done per request
+  uint32_t* cnt_kl;   // [B] KL second-pass items done per request
   ReqFin* req_fin;    // [B] completion record of the KL second pass
   PartC* part_c;      // [B * nslices * 4] draw sums per wave-chunk
   RefItem* ref_list;  // [R_d] positions queued for the KL second pass (hdr[1] of them)
@@ -166,5 +173,12 @@ int launch_stats(const Params& p, bool vec, void* stream, void* ev_start, void* 
 int launch_decide(const Params& p, bool vec, void* stream);
 // KL second pass over the queue k_decide fills (NKL mode, or stochastic with out_nkl)
 int launch_refine(const Params& p, bool vec, void* stream);
+// One kernel for the whole stochastic step (batches up to kLdsBatch, no KL
+// output, a short statistics pass): plan_fused fills p.stats_grid,
+// p.grp_log2, p.nslices, p.helpers and p.slices_per_helper and returns the
+// grid, or 0 when the step should take the separate kernels; launch_fused
+// enqueues it.
+int plan_fused(Params& p, bool vec);
+int launch_fused(const Params& p, bool vec, int grid, void* stream, void* ev_start, void* ev_stop);
 
 }  // namespace sv

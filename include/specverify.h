@@ -92,7 +92,9 @@ typedef struct sv_config {
   int32_t vocab;            /* V > 0 */
   int32_t dtype;            /* SV_DTYPE_F32 or SV_DTYPE_BF16 (both logit arrays) */
   int32_t max_gamma;        /* bound on gamma_per_req[b]; 0 <= max_gamma <= SV_MAX_GAMMA */
-  int32_t reserved;         /* must be 0 */
+  int32_t wait_polls;       /* >= 0; 0 = default.  Single-dispatch stochastic path: how often a
+                               helper polls for a statistics partial of its request before it
+                               computes that partial itself (results do not depend on it) */
   int64_t total_draft_rows; /* sum_b gamma_per_req[b], known on the host (sizes the grids) */
   void* stream;             /* hipStream_t to enqueue on; NULL = the default stream */
   void* workspace;          /* device scratch, >= spec_verify_workspace_size(cfg) bytes, 256-byte aligned */
@@ -154,6 +156,15 @@ const char* spec_verify_status_string(int status);
 
 /* SPECVERIFY_VERSION of the loaded library. */
 int spec_verify_version(void);
+
+/* 1 if spec_verify would run this configuration as one kernel dispatch (the
+ * stochastic mode with batch <= 1024, out_nkl == NULL when with_nkl == 0, and a
+ * short statistics pass), 0 if as separate kernels, SV_EINVAL for an invalid
+ * cfg or mode.  Reads batch, vocab, dtype, total_draft_rows and the device's
+ * compute-unit count (the current device); enqueues nothing.  For timing and
+ * profiling tools: phase_events [1] and [2] bracket that single dispatch, or
+ * else the row-statistics dispatch. */
+int spec_verify_single_dispatch(const sv_config* cfg, int32_t mode, int32_t with_nkl);
 
 #ifdef __cplusplus
 }

@@ -41,7 +41,7 @@ def to_device(w, dev="cuda:0"):
     )
 
 
-def run_gpu(w, d=None, diagnostics=True, out_nkl=False, max_gamma=None, workspace=None):
+def run_gpu(w, d=None, diagnostics=True, out_nkl=False, max_gamma=None, workspace=None, wait_polls=0):
     import torch
     import draft_token_verification_05_amd as sv
     if d is None:
@@ -52,7 +52,7 @@ def run_gpu(w, d=None, diagnostics=True, out_nkl=False, max_gamma=None, workspac
                     d["temp"] if soft else None, d["ua"] if mode == 0 else None, d["ur"] if mode == 0 else None,
                     mode, w.delta, d["parents"] if mode == 3 else None,
                     max_gamma=w.max_gamma if max_gamma is None else max_gamma, diagnostics=diagnostics,
-                    out_nkl=out_nkl, workspace=workspace)
+                    out_nkl=out_nkl, workspace=workspace, wait_polls=wait_polls)
     torch.cuda.synchronize()
     host = lambda t: None if t is None else t.cpu().numpy()
     return dict(tokens=host(out.tokens), num=host(out.num_accepted), nkl=host(out.nkl), p_x=host(out.p_x),

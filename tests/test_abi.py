@@ -24,9 +24,23 @@ def declared_functions():
     return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(spec_verify\w*)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_four_entry_points():
-    assert declared_functions() == ["spec_verify", "spec_verify_status_string", "spec_verify_version",
-                                    "spec_verify_workspace_size"]
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["spec_verify", "spec_verify_single_dispatch", "spec_verify_status_string",
+                                    "spec_verify_version", "spec_verify_workspace_size"]
+
+
+def test_single_dispatch_query_host_side(sv):
+    """Answers that need no device: invalid arguments, and the modes and
+    options that always take the separate kernels."""
+    cfg = sv.make_config(32, 128256, sv.SV_DTYPE_BF16, 5, 160)
+    assert sv.spec_verify_single_dispatch(cfg, 7) == sv.SV_EINVAL
+    for mode in (sv.SV_MODE_GREEDY, sv.SV_MODE_NKL, sv.SV_MODE_TREE_GREEDY):
+        assert sv.spec_verify_single_dispatch(cfg, mode) == 0
+    assert sv.spec_verify_single_dispatch(cfg, sv.SV_MODE_STOCHASTIC, with_nkl=True) == 0
+    assert sv.spec_verify_single_dispatch(sv.make_config(1300, 1500, 1, 3, 2000), sv.SV_MODE_STOCHASTIC) == 0
+    bad = sv.make_config(32, 128256, sv.SV_DTYPE_BF16, 5, 160)
+    bad.struct_size += 8
+    assert sv.spec_verify_single_dispatch(bad, sv.SV_MODE_STOCHASTIC) == sv.SV_EINVAL
 
 
 def test_library_exports_every_declared_symbol(sv):
@@ -112,7 +126,7 @@ def test_synchronous_argument_errors(sv):
     cfg.struct_size = 12
     assert sv.spec_verify(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0.1, 0, FAKE, FAKE, 0, cfg) == E
     cfg = sv.make_config(4, 1000, 1, 4, 8, 0, FAKE, 1 << 30)
-    cfg.reserved = 1
+    cfg.wait_polls = -1
     assert sv.spec_verify(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0.1, 0, FAKE, FAKE, 0, cfg) == E
 
 

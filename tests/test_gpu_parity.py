@@ -56,6 +56,12 @@ def test_tiny_single_steps_equal_batched():
 
 
 def test_llama3_stochastic():
+    # no KL output: the single-dispatch path
+    check(synthetic.make_llama3())
+
+
+def test_llama3_stochastic_with_nkl_output():
+    # with the optional KL output: statistics, decision and KL second-pass kernels
     check(synthetic.make_llama3(), out_nkl=True)
 
 
@@ -272,3 +278,54 @@ def test_losslessness_chi_square_gpu():
         reached = g["num"] >= k
         pv.append(stats.chisquare(np.bincount(tok[reached, k], minlength=V), P[k] * reached.sum()).pvalue)
     assert min(pv) > 1e-3 / len(pv), pv
+
+
+# ---------------------------------------------------------------- single-dispatch stochastic path
+
+def test_single_dispatch_choice():
+    """Short statistics passes (the Llama-3-shaped batch) run as one dispatch,
+    long ones (the ragged B=256 batch) and the KL output as separate kernels."""
+    import draft_token_verification_05_amd as sv
+    llama = sv.make_config(32, 128256, sv.SV_DTYPE_BF16, 5, 160)
+    assert sv.spec_verify_single_dispatch(llama, S) == 1
+    assert sv.spec_verify_single_dispatch(llama, S, with_nkl=True) == 0
+    w = synthetic.make_ragged()
+    ragged = sv.make_config(w.batch, w.vocab, sv.SV_DTYPE_BF16, w.max_gamma, w.total_draft_rows)
+    assert sv.spec_verify_single_dispatch(ragged, S) == 0
+
+
+@pytest.mark.parametrize("V,dtype", [(128256, "bf16"), (4099, "f32"), (8193, "bf16")])
+def test_single_dispatch_recomputed_partials_bit_identical(V, dtype):
+    """A helper that stops waiting after one poll computes the missing
+    statistics partials itself: the outputs are bit-identical to a call whose
+    helpers found every partial, and match the oracle."""
+    w = synthetic.random_workload(seed=61 + V % 7, mode=S, B=24, V=V, dtype=dtype, gmax=6, gmin=0)
+    d = to_device(w)
+    a = run_gpu(w, d)
+    b = run_gpu(w, d, wait_polls=1)
+    for k in ("tokens", "num", "p_x", "q_x", "resid"):
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+    rep = compare(w, b, oracle.verify_workload(w))
+    print(f"[parity]   wait_polls=1 {rep}", flush=True)
+    assert_parity(rep, S)
+
+
+def test_workspace_shared_by_both_stochastic_paths():
+    """One workspace used in turn by the single-dispatch path, the
+    three-kernel path (KL output) and greedy mode: every call matches the
+    oracle and the repeated single-dispatch call repeats its first answer."""
+    import torch
+    import draft_token_verification_05_amd as sv
+    w = synthetic.random_workload(seed=71, mode=S, B=40, V=30000, dtype="bf16", gmax=7, gmin=0)
+    d = to_device(w)
+    cfg = sv.make_config(w.batch, w.vocab, sv.SV_DTYPE_BF16, w.max_gamma, w.total_draft_rows)
+    ws = torch.zeros(sv.spec_verify_workspace_size(cfg), dtype=torch.uint8, device="cuda:0")
+    o = oracle.verify_workload(w)
+    first = run_gpu(w, d, workspace=ws)
+    assert_parity(compare(w, first, o), S)
+    assert_parity(compare(w, run_gpu(w, d, workspace=ws, out_nkl=True), o), S)
+    wg = w.with_mode(G)
+    assert_parity(compare(wg, run_gpu(wg, d, workspace=ws), oracle.verify_workload(wg)), G)
+    again = run_gpu(w, d, workspace=ws)
+    for k in ("tokens", "num", "p_x", "q_x", "resid"):
+        assert np.array_equal(first[k], again[k], equal_nan=True), k
