@@ -1210,6 +1210,10 @@ struct DecideShared {
   float red_f[kWaves];
   double red_d[kWaves];
   int flag;
+  // what the token selection's wave 0 hands to the workgroup
+  int sel_cstar, sel_flags;
+  float sel_ref, sel_M;
+  double sel_cbase, sel_target, sel_K, sel_ratio;
 };
 
 // Rank of this thread among the threads with `flag` (thread order), and one
@@ -1425,153 +1429,150 @@ __device__ __forceinline__ double token_weight(float t, float d, bool two, const
   return (double)a * cf;
 }
 
-// Token draw of request b by one wave of its last helper, from the NW
-// wave-chunk records in token order: y* = min{y : C_y > u * C_{V-1}}.
-// CACHED: at most kSelCache records, kept in LDS after the first sweep.  The
-// records are combined by fixed wave-wide reductions and scans in chunk
-// order; the wave-chunk that holds the draw is read again, lane l taking NE
-// consecutive tokens, and scanned token by token.  No workgroup barrier.
+// Token draw of request b by its last helper, from the NW wave-chunk records
+// in token order: y* = min{y : C_y > u * C_{V-1}}.  Wave 0 combines the
+// records by fixed wave-wide reductions and scans in chunk order and finds the
+// wave-chunk that holds the draw (CACHED: at most kSelCache records, kept in
+// LDS after the first sweep).  The whole workgroup then reads that wave-chunk
+// again, thread t taking its t-th vector (P consecutive tokens), and a
+// workgroup scan of the threads' weights, in token order, leads to the
+// thread and then the token that hold the draw.  All threads call.
 template <int DT, bool VEC, bool CACHED>
 __device__ __forceinline__ void draw_select(const Params& p, int b, const Term& tm, int NW, float ur,
                                             DecideShared& sh) {
   constexpr int P = Elem<DT>::P;
-  constexpr int NE = kUT * P;
-  constexpr int64_t CHW = (int64_t)64 * NE;
-  const int lane = threadIdx.x & 63;
-  const PartC* pcs = p.part_c + (int64_t)b * NW;
+  constexpr int64_t CHW = (int64_t)64 * kUT * P;  // tokens of one wave-chunk: kThreads vectors
+  static_assert(64 * kUT == kThreads, "one vector of the wave-chunk per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const bool resid = tm.kind == kTermResidual;
   const float Lhi = tm.Lhi;
   const double Ld = (double)Lhi;
-  double at = 0.0, bt = 0.0;
-  float M = -INFINITY;
-  for (int ch = lane; ch < NW; ch += 64) {
-    const double a = ld_dev(&pcs[ch].a);
-    const double bb = resid ? ld_dev(&pcs[ch].b) : 0.0;
-    const float m = resid ? 0.0f : ld_dev(&pcs[ch].m);
-    at += a;
-    bt += bb;
-    M = fmaxf(M, m);
-    if (CACHED) {
-      // each lane reads back only the records it wrote: no barrier needed
-      sh.sel_a[ch] = a;
-      sh.sel_ap[ch] = resid ? ld_dev(&pcs[ch].ap) : 0.0;
-      sh.sel_bp[ch] = resid ? ld_dev(&pcs[ch].bp) : 0.0;
-      sh.sel_m[ch] = m;
+  if (tid < 64) {
+    const PartC* pcs = p.part_c + (int64_t)b * NW;
+    double at = 0.0, bt = 0.0;
+    float M = -INFINITY;
+    for (int ch = lane; ch < NW; ch += 64) {
+      const double a = ld_dev(&pcs[ch].a);
+      const double bb = resid ? ld_dev(&pcs[ch].b) : 0.0;
+      const float m = resid ? 0.0f : ld_dev(&pcs[ch].m);
+      at += a;
+      bt += bb;
+      M = fmaxf(M, m);
+      if (CACHED) {
+        // each lane reads back only the records it wrote: no barrier needed
+        sh.sel_a[ch] = a;
+        sh.sel_ap[ch] = resid ? ld_dev(&pcs[ch].ap) : 0.0;
+        sh.sel_bp[ch] = resid ? ld_dev(&pcs[ch].bp) : 0.0;
+        sh.sel_m[ch] = m;
+      }
+    }
+    at = wave_sum_d(at);
+    bt = wave_sum_d(bt);
+    M = wave_max(M);
+    const double K = resid ? at / bt : 0.0;
+    const auto weight = [&](int ch, bool fb) {
+      if (CACHED) return slice_weight(sh.sel_a[ch], sh.sel_ap[ch], sh.sel_bp[ch], sh.sel_m[ch], resid, fb, K, M, Ld);
+      return slice_weight(ld_dev(&pcs[ch].a), resid ? ld_dev(&pcs[ch].ap) : 0.0, resid ? ld_dev(&pcs[ch].bp) : 0.0,
+                          resid ? 0.0f : ld_dev(&pcs[ch].m), resid, fb, K, M, Ld);
+    };
+    const int rounds = (NW + 63) / 64;
+    double S = 0.0;
+    for (int r = 0; r < rounds; ++r)
+      if (lane + 64 * r < NW) S += weight(lane + 64 * r, false);
+    S = wave_sum_d(S);
+    bool fb = false;
+    if (resid && !(S > 0.0)) {
+      // max(0, p - q) vanished numerically: draw from p_j instead
+      fb = true;
+      S = at;
+    }
+    const double target = (double)ur * S;
+
+    // the wave-chunk whose cumulative weight first exceeds the target: one
+    // round per 64 consecutive chunks
+    int cstar = -1, clast = -1;
+    double cbase = 0.0, carry = 0.0;
+    for (int r = 0; r < rounds; ++r) {
+      const int ch = lane + 64 * r;
+      const double w = ch < NW ? weight(ch, fb) : 0.0;
+      const double incl = wave_incl_scan_d(w);
+      const double excl = carry + incl - w;
+      const bool hit = w > 0.0 && excl <= target && target < excl + w;
+      const int first = wave_min_int(hit ? ch : INT_MAX);
+      const int lp = wave_max_int(w > 0.0 ? ch : -1);
+      if (lp >= 0) clast = lp;
+      if (first != INT_MAX) {
+        cstar = first;
+        cbase = lane_d(excl, first - 64 * r);
+        break;
+      }
+      carry += lane_d(incl, 63);
+    }
+    const bool take_last = cstar < 0;  // rounding left the target at the end
+    if (take_last) {
+      cstar = clast >= 0 ? clast : NW - 1;
+      cbase = 0.0;
+    }
+    if (lane == 0) {
+      sh.sel_cstar = cstar;
+      sh.sel_flags = (take_last ? 1 : 0) | (fb ? 2 : 0);
+      sh.sel_cbase = cbase;
+      sh.sel_target = target;
+      sh.sel_K = K;
+      sh.sel_M = M;
+      sh.sel_ratio = resid && !fb ? S / at : 1.0;
+      if (!resid) sh.sel_ref = ld_dev(&pcs[cstar].m);
     }
   }
-  at = wave_sum_d(at);
-  bt = wave_sum_d(bt);
-  M = wave_max(M);
-  const double K = resid ? at / bt : 0.0;
-  const auto weight = [&](int ch, bool fb) {
-    if (CACHED) return slice_weight(sh.sel_a[ch], sh.sel_ap[ch], sh.sel_bp[ch], sh.sel_m[ch], resid, fb, K, M, Ld);
-    return slice_weight(ld_dev(&pcs[ch].a), resid ? ld_dev(&pcs[ch].ap) : 0.0, resid ? ld_dev(&pcs[ch].bp) : 0.0,
-                        resid ? 0.0f : ld_dev(&pcs[ch].m), resid, fb, K, M, Ld);
-  };
-  const int rounds = (NW + 63) / 64;
-  double S = 0.0;
-  for (int r = 0; r < rounds; ++r)
-    if (lane + 64 * r < NW) S += weight(lane + 64 * r, false);
-  S = wave_sum_d(S);
-  bool fb = false;
-  if (resid && !(S > 0.0)) {
-    // max(0, p - q) vanished numerically: draw from p_j instead
-    fb = true;
-    S = at;
-  }
-  const double target = (double)ur * S;
-
-  // the wave-chunk whose cumulative weight first exceeds the target: one round
-  // per 64 consecutive chunks
-  int cstar = -1, clast = -1;
-  double cbase = 0.0, carry = 0.0;
-  for (int r = 0; r < rounds; ++r) {
-    const int ch = lane + 64 * r;
-    const double w = ch < NW ? weight(ch, fb) : 0.0;
-    const double incl = wave_incl_scan_d(w);
-    const double excl = carry + incl - w;
-    const bool hit = w > 0.0 && excl <= target && target < excl + w;
-    const int first = wave_min_int(hit ? ch : INT_MAX);
-    const int lp = wave_max_int(w > 0.0 ? ch : -1);
-    if (lp >= 0) clast = lp;
-    if (first != INT_MAX) {
-      cstar = first;
-      cbase = lane_d(excl, first - 64 * r);
-      break;
-    }
-    carry += lane_d(incl, 63);
-  }
-  const bool take_last = cstar < 0;  // rounding left the target at the end
-  if (take_last) {
-    cstar = clast >= 0 ? clast : NW - 1;
-    cbase = 0.0;
-  }
-
-  // wave-chunk c* again: lane l owns tokens y0 .. y0 + NE - 1
+  __syncthreads();
+  const int cstar = sh.sel_cstar;
+  const bool take_last = (sh.sel_flags & 1) != 0, fb = (sh.sel_flags & 2) != 0;
+  const double cbase = sh.sel_cbase, target = sh.sel_target, K = sh.sel_K;
+  // wave-chunk c* again: thread t owns tokens y0 .. y0 + P - 1
   const int64_t V = p.V;
-  const int64_t y0 = (int64_t)cstar * CHW + (int64_t)lane * NE;
+  const int64_t y0 = (int64_t)cstar * CHW + (int64_t)tid * P;
   const bool two = resid && !fb;
-  const float ref = resid ? tm.m_t : ld_dev(&pcs[cstar].m);
-  const double cf = resid ? 1.0 : exp2(((double)ref - (double)M) * Ld);
-  uint4 qt[kUT], qd[kUT];
-#pragma unroll
-  for (int k = 0; k < kUT; ++k) {
-    qt[k] = fetch<DT, VEC>(p.target, tm.trow, V, y0 + k * P);
-    qd[k] = two ? fetch<DT, VEC>(p.draft, tm.drow, V, y0 + k * P) : qt[k];
-  }
+  const float ref = resid ? tm.m_t : sh.sel_ref;
+  const double cf = resid ? 1.0 : exp2(((double)ref - (double)sh.sel_M) * Ld);
+  const uint4 qt = fetch<DT, VEC>(p.target, tm.trow, V, y0);
+  const uint4 qd = two ? fetch<DT, VEC>(p.draft, tm.drow, V, y0) : qt;
   // positions past the end hold the pad: a = 0 there, so their weight is 0
-  double vs[kUT], tsum = 0.0;
+  float vt[P], vd[P];
+  unpack<DT>(qt, vt);
+  unpack<DT>(qd, vd);
+  double wts[P], tsum = 0.0;
   int lastpos = -1;  // the last token with a positive weight (the fallback)
 #pragma unroll
-  for (int k = 0; k < kUT; ++k) {
-    float vt[P], vd[P];
-    unpack<DT>(qt[k], vt);
-    unpack<DT>(qd[k], vd);
-    double sum = 0.0;
-#pragma unroll
-    for (int e = 0; e < P; ++e) {
-      const double rv = token_weight(vt[e], vd[e], two, tm, ref, Lhi, K, cf);
-      sum += rv;
-      if (rv > 0.0) lastpos = (int)(y0 + k * P + e);
-    }
-    vs[k] = sum;
-    tsum += sum;
+  for (int e = 0; e < P; ++e) {
+    wts[e] = token_weight(vt[e], vd[e], two, tm, ref, Lhi, K, cf);
+    tsum += wts[e];
+    if (wts[e] > 0.0) lastpos = (int)(y0 + e);
   }
-  const double cum0 = cbase + (wave_incl_scan_d(tsum) - tsum);
-  const bool mine = !take_last && cum0 <= target && cum0 + tsum > target;
-  // the lane's vector that holds the target, then its P tokens weighed again
-  int kk = -1;
-  double base = cum0;
+  // workgroup exclusive scan of the threads' sums, in thread (= token) order
+  const double incl = wave_incl_scan_d(tsum);
+  if (lane == 63) sh.red_d[wv] = incl;
+  __syncthreads();
+  double before = 0.0;
 #pragma unroll
-  for (int k = 0; k < kUT; ++k) {
-    if (mine && kk < 0) {
-      if (base + vs[k] > target) kk = k;
-      else base += vs[k];
-    }
-  }
+  for (int k = 0; k < kWaves; ++k)
+    if (k < wv) before += sh.red_d[k];
+  const double cum0 = cbase + (before + (incl - tsum));
   int cand = INT_MAX;
-  if (kk >= 0) {
-    // vector kk read again (a cache hit) instead of kept in registers through
-    // the scan above
-    const uint4 wt = fetch<DT, VEC>(p.target, tm.trow, V, y0 + kk * P);
-    const uint4 wd = two ? fetch<DT, VEC>(p.draft, tm.drow, V, y0 + kk * P) : wt;
-    float vt[P], vd[P];
-    unpack<DT>(wt, vt);
-    unpack<DT>(wd, vd);
-    double cum = base;
+  if (!take_last && cum0 <= target && cum0 + tsum > target) {
+    double cum = cum0;
 #pragma unroll
     for (int e = 0; e < P; ++e) {
-      cum += token_weight(vt[e], vd[e], two, tm, ref, Lhi, K, cf);
-      if (cand == INT_MAX && cum > target) cand = (int)(y0 + kk * P + e);
+      cum += wts[e];
+      if (cand == INT_MAX && cum > target) cand = (int)(y0 + e);
     }
   }
-  const int ystar = wave_min_int(cand);
-  const int ylast = wave_max_int(lastpos);
-  if (lane == 0) {
+  const int ystar = block_min_int(cand, sh.red_i);
+  const int ylast = block_max_int(lastpos, sh.red_i);
+  if (tid == 0) {
     int y = ystar != INT_MAX ? ystar : ylast;
     if (y < 0 || y >= p.V) y = (int)min(V - 1, (int64_t)cstar * CHW);
     p.out_tokens[tm.trow] = y;
-    if (p.out_resid) p.out_resid[b] = two ? (float)(S / at) : 1.0f;
+    if (p.out_resid) p.out_resid[b] = (float)sh.sel_ratio;
   }
 }
 
@@ -1848,7 +1849,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
       slice_stream<DT, VEC, false>(p, tm.trow, tm.drow, s0, s1, [&](const uint4* qt, const uint4* qd, int sl) {
         draw_record<DT, false>(qt, qd, tm, rec + sl * kWaves);
       });
-    if (arrive_last(p.cnt + b, H, sh) && tid < 64) {
+    if (arrive_last(p.cnt + b, H, sh)) {
       const int NW = NS * kWaves;
       if (NW <= kSelCache) draw_select<DT, VEC, true>(p, b, tm, NW, ur, sh);
       else draw_select<DT, VEC, false>(p, b, tm, NW, ur, sh);
