@@ -1623,7 +1623,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
   const int s0 = h * p.slices_per_helper, s1 = min(NS, s0 + p.slices_per_helper);
   const bool writer = h == 0;  // helper 0 writes the outputs of the decision
   const int tid = threadIdx.x;
-  const bool want_kl = SOFT && p.want_kl;
+  const bool want_kl = SOFT && !FUSED && p.want_kl;  // the single dispatch has no KL output
   if (!ok) {  // layout error: only the counts are written
     if (writer && tid == 0) p.out_num[b] = -1;
     return;
