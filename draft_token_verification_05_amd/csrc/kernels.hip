@@ -2120,13 +2120,17 @@ int plan_fused(Params& p, bool vec) {
               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_fused<SV_DTYPE_F32, false>, kThreads, 0);
     o = (e == hipSuccess && v > 0) ? v : 1;
   }
-  const int64_t cap = (int64_t)o * num_cus();
+  // at most kFusedPerCu workgroups per compute unit: the units serve their
+  // workgroups' loads roughly in age order, so the newest stream last; with
+  // one fewer per unit the last ones finish sooner (Llama-3-shaped batch:
+  // 32.75 us per step at 4 per unit, 32.37 at 3, 33.0 at 2)
+  const int64_t cap = (int64_t)(o < kFusedPerCu ? o : kFusedPerCu) * num_cus();
   // Single dispatch only while the statistics pass is short: it saves the
-  // second launch and the hand-over to the decision (about 2.5 us at 5 items
-  // per workgroup, the 82 MB Llama-3-shaped batch), but its workgroups hold
-  // the decision's registers too (4 instead of 5 per CU), which costs more than
-  // that on long passes (about 10 us at 41 items per workgroup, the 680 MB
-  // ragged batch).
+  // second launch and the hand-over to the decision (the 82 MB Llama-3-shaped
+  // batch: 7 items per workgroup, about 2.5 us per step), but it streams with
+  // fewer workgroups per CU than k_stats and its helpers poll while others
+  // stream, which costs more than that on long passes (the 680 MB ragged
+  // batch, 55 items per workgroup: about 10 us).
   if ((int64_t)p.n_task * p.nch > kFusedItemsPerWg * cap) return 0;
   set_stats_grid(p, cap);
   // helpers per request: what the resident grid holds, at most one per slice

@@ -21,6 +21,7 @@ constexpr int kUT = 4;           // 16-byte vectors per thread per row in one sl
 constexpr int kSelCache = 256;   // draw records a token selection keeps in LDS
 constexpr int kLdsBatch = 1024;  // batches up to this size scan their offsets in LDS (no prep kernel)
 constexpr int kFusedItemsPerWg = 12;  // longest statistics pass (items per resident workgroup) run in one dispatch
+constexpr int kFusedPerCu = 3;        // resident workgroups per compute unit of the single dispatch
 
 constexpr int elems_per_vec(int dtype) { return dtype == SV_DTYPE_BF16 ? 8 : 4; }
 constexpr int elem_size(int dtype) { return dtype == SV_DTYPE_BF16 ? 2 : 4; }
