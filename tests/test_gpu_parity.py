@@ -329,3 +329,33 @@ def test_workspace_shared_by_both_stochastic_paths():
     again = run_gpu(w, d, workspace=ws)
     for k in ("tokens", "num", "p_x", "q_x", "resid"):
         assert np.array_equal(first[k], again[k], equal_nan=True), k
+
+
+def test_concurrent_calls_on_two_streams():
+    """Calls enqueued on two streams with their own workspaces run at the same
+    time and compete for the compute units (the single dispatch's helpers then
+    may wait for statistics workgroups that are not resident yet): every
+    output equals that of a call made alone."""
+    import torch
+    import draft_token_verification_05_amd as sv
+    wa = synthetic.make_llama3(B=16)
+    wb = synthetic.random_workload(seed=81, mode=S, B=32, V=128256, dtype="bf16", gmax=6, gmin=1)
+    da, db = to_device(wa), to_device(wb)
+    ref_a, ref_b = run_gpu(wa, da, diagnostics=False), run_gpu(wb, db, diagnostics=False)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for k in range(12):
+        for i, ((w, d), st) in enumerate(zip(((wa, da), (wb, db)), streams)):
+            with torch.cuda.stream(st):
+                outs.append((k, i, sv.verify(d["target"], d["draft"], d["tokens"], d["gamma"], d["temp"], d["ua"],
+                                                  d["ur"], S, w.delta, max_gamma=w.max_gamma,
+                                                  workspace=torch.zeros(sv.spec_verify_workspace_size(
+                                                      sv.make_config(w.batch, w.vocab, 1, w.max_gamma,
+                                                                     w.total_draft_rows)), dtype=torch.uint8,
+                                                      device="cuda:0"),
+                                                  stream=st)))
+    torch.cuda.synchronize()
+    for k, i, o in outs:
+        ref = (ref_a, ref_b)[i]
+        assert np.array_equal(o.tokens.cpu().numpy(), ref["tokens"]), (k, i)
+        assert np.array_equal(o.num_accepted.cpu().numpy(), ref["num"]), (k, i)
