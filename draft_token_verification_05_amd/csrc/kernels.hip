@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Params p) {
     p.hdr[0] = bad ? 1 : 0;
     p.hdr[1] = 0;  // KL second-pass queue
   }
-  for (int b = tid; b < p.B; b += kPrepThreads) p.cnt[b] = p.cnt_kl[b] = 0u;  // completion counters
+  for (int b = tid; b < p.B; b += kPrepThreads) p.cnt[(int64_t)b * kCntStride] = p.cnt_kl[(int64_t)b * kCntStride] = 0u;  // completion counters
   if (bad) return;
   __syncthreads();  // offsets written by other threads of this workgroup
   for (int b = tid; b < p.B; b += kPrepThreads) {
@@ -524,7 +524,7 @@ __device__ bool scan_offsets_lds(const Params& p, StatsShared& sh, const ScanIn&
   const bool ok = sh.bad == 0;
   if (publish) {
     for (int b = tid; b <= p.B; b += kThreads) p.d_off[b] = sh.off[b];
-    for (int b = tid; b < p.B; b += kThreads) p.cnt[b] = p.cnt_kl[b] = 0u;  // completion counters
+    for (int b = tid; b < p.B; b += kThreads) p.cnt[(int64_t)b * kCntStride] = p.cnt_kl[(int64_t)b * kCntStride] = 0u;  // completion counters
     if (tid == 0) {
       p.hdr[0] = ok ? 0 : 1;
       p.hdr[1] = 0;  // KL second-pass queue
@@ -832,6 +832,18 @@ __device__ __forceinline__ void next_desc(const Params& p, const StatsShared& sh
 // for helpers of the same dispatch, workgroups numbered
 // p.stats_grid and above stream nothing, and nothing is published for later
 // kernels.  Returns false when the offsets scan found a layout error.
+// Issue priority of a streaming wave from the share of its work still left
+// (rem of tot items): the waves resident on a compute unit are otherwise
+// served oldest first, so the youngest workgroups fall behind and finish last
+// with little company to keep the memory pipeline full.  Waves that are behind
+// rank first; four levels, the last for the final twentieth of the work.
+__device__ __forceinline__ void pace(int64_t rem, int64_t tot) {
+  if (rem * 2 > tot) __builtin_amdgcn_s_setprio(3);
+  else if (rem * 5 > tot) __builtin_amdgcn_s_setprio(2);
+  else if (rem * 20 > tot) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 template <int DT, bool VEC, int MODE, bool WZ, bool LDS, bool FUSED>
 __device__ __forceinline__ bool stats_phase(const Params& p, StatsShared& sh) {
   constexpr bool SOFT = MODE == SV_MODE_STOCHASTIC || MODE == SV_MODE_NKL;
@@ -844,6 +856,7 @@ __device__ __forceinline__ bool stats_phase(const Params& p, StatsShared& sh) {
   const int64_t N = (int64_t)p.n_task * p.nch;
   const int64_t i_end = streams ? (int64_t)(wg + 1) * N / G : 0;
   int64_t i = streams ? (int64_t)wg * N / G : 0;
+  const int64_t tot = i_end - i;
   Desc dA, dB;
   Vecs<NV> At, Ad, Bt, Bd;
   int b = -1;
@@ -892,12 +905,14 @@ __device__ __forceinline__ bool stats_phase(const Params& p, StatsShared& sh) {
   for (;;) {
     dB = dA;
     if (i + 1 < i_end) next_desc<MODE, LDS>(p, sh, b, dB);
+    if (SOFT) pace(i_end - i, tot);  // (measured: the greedy modes stream faster without)
     issue_chunk<DT, VEC, NV, SOFT>(p, dB, Bt, Bd);  // the last item reloads itself (cache hit)
     fold_chunk<DT, NV, SOFT, IDX, WZM, SOFT>(L, At, Ad, dA, p.V);
     if (dA.chunk == p.nch - 1 || i + 1 == i_end) store(dA);
     if (++i >= i_end) break;
     dA = dB;
     if (i + 1 < i_end) next_desc<MODE, LDS>(p, sh, b, dA);
+    if (SOFT) pace(i_end - i, tot);
     issue_chunk<DT, VEC, NV, SOFT>(p, dA, At, Ad);
     fold_chunk<DT, NV, SOFT, IDX, WZM, SOFT>(L, Bt, Bd, dB, p.V);
     if (dB.chunk == p.nch - 1 || i + 1 == i_end) store(dB);
@@ -1849,7 +1864,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
       slice_stream<DT, VEC, false>(p, tm.trow, tm.drow, s0, s1, [&](const uint4* qt, const uint4* qd, int sl) {
         draw_record<DT, false>(qt, qd, tm, rec + sl * kWaves);
       });
-    if (arrive_last(p.cnt + b, H, sh)) {
+    if (arrive_last(p.cnt + (int64_t)b * kCntStride, H, sh)) {
       const int NW = NS * kWaves;
       if (NW <= kSelCache) draw_select<DT, VEC, true>(p, b, tm, NW, ur, sh);
       else draw_select<DT, VEC, false>(p, b, tm, NW, ur, sh);
@@ -1935,7 +1950,7 @@ __global__ __launch_bounds__(kThreads) void k_refine(Params p) {
     const KlIn ri{e.ct, e.cd, e.kt, e.kd, e.lw};
     const double v = block_sum_d(kl_terms<DT>(qt, qd, ri, e.Lhi), sh.red_d);
     if (threadIdx.x == 0) st_dev(&p.kl_part[(int64_t)e.pos * NS + it % NS], v);
-    if (pend > 0 && arrive_last(p.cnt_kl + e.b, pend * NS, sh)) kl_finish<MODE>(p, e.b, sh);
+    if (pend > 0 && arrive_last(p.cnt_kl + (int64_t)e.b * kCntStride, pend * NS, sh)) kl_finish<MODE>(p, e.b, sh);
   };
   issue(i0, ea, pa, at, ad);
   for (int64_t it = i0; it < i1; it += 2) {

@@ -22,6 +22,9 @@ constexpr int kSelCache = 256;   // draw records a token selection keeps in LDS
 constexpr int kLdsBatch = 1024;  // batches up to this size scan their offsets in LDS (no prep kernel)
 constexpr int kFusedItemsPerWg = 12;  // longest statistics pass (items per resident workgroup) run in one dispatch
 constexpr int kFusedPerCu = 3;        // resident workgroups per compute unit of the single dispatch
+// per-request arrival counters sit 256 bytes apart: increments of different
+// requests' counters would otherwise queue behind each other on one line
+constexpr int kCntStride = 64;
 
 constexpr int elems_per_vec(int dtype) { return dtype == SV_DTYPE_BF16 ? 8 : 4; }
 constexpr int elem_size(int dtype) { return dtype == SV_DTYPE_BF16 ? 2 : 4; }
@@ -102,8 +105,8 @@ inline Layout make_layout(int64_t B, int64_t V, int dtype, int64_t R_d) {
   L.off_pair2req = take(sizeof(int32_t) * R1);
   L.off_row2req = take(sizeof(int32_t) * (R_d + B));
   L.off_part_a = take(sizeof(PartA) * L.n_task_max * L.nch_a);
-  L.off_cnt = take(sizeof(uint32_t) * B);
-  L.off_cnt_kl = take(sizeof(uint32_t) * B);
+  L.off_cnt = take(sizeof(uint32_t) * B * kCntStride);
+  L.off_cnt_kl = take(sizeof(uint32_t) * B * kCntStride);
   L.off_req_fin = take(sizeof(ReqFin) * B);
   L.off_part_c = take(sizeof(PartC) * B * L.nch_t * (kThreads / 64));
   L.off_ref_list = take(sizeof(RefItem) * R1);
@@ -152,8 +155,8 @@ struct Params {
   PartA* part_a;
   // per-request arrival counters: the last arrival wraps them back to zero, so
   // every completed call leaves them at zero (a new workspace is zero-filled)
-  uint32_t* cnt;      // [B] decision helpers done per request
-  uint32_t* cnt_kl;   // [B] KL second-pass items done per request
+  uint32_t* cnt;      // [B * kCntStride] decision helpers done per request (one every kCntStride)
+  uint32_t* cnt_kl;   // [B * kCntStride] KL second-pass items done per request
   ReqFin* req_fin;    // [B] completion record of the KL second pass
   PartC* part_c;      // [B * nslices * 4] draw sums per wave-chunk
   RefItem* ref_list;  // [R_d] positions queued for the KL second pass (hdr[1] of them)
