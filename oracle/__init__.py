@@ -41,8 +41,10 @@ def _load():
         P = ctypes.c_void_p
         i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         lib.sv_oracle_verify.restype = ctypes.c_int
-        lib.sv_oracle_verify.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, i32, f32, P, i32, i64,
+        lib.sv_oracle_verify.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, i32, f32, P, f32, f32, P, i32, i64,
                                          P, P, P, P, P, P, P, P, P, P, P, i32]
+        lib.sv_oracle_nkl_threshold.restype = ctypes.c_double
+        lib.sv_oracle_nkl_threshold.argtypes = [f32, f32, f32, i32]
         lib.sv_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -50,6 +52,12 @@ def _load():
 
 def max_threads() -> int:
     return int(_load().sv_oracle_max_threads())
+
+
+def nkl_threshold(delta: float, alpha: float, delta_max: float, position: int) -> float:
+    """Position-adaptive NKL threshold of a draft token at 0-based position
+    ``position`` of the generated sequence (float64)."""
+    return float(_load().sv_oracle_nkl_threshold(float(delta), float(alpha), float(delta_max), int(position)))
 
 
 @dataclass
@@ -75,8 +83,12 @@ def verify(target: np.ndarray, draft: Optional[np.ndarray], dtype: str, gamma: n
            draft_tokens: np.ndarray, temperature: Optional[np.ndarray], u_accept: Optional[np.ndarray],
            u_resample: Optional[np.ndarray], mode: int, delta: float = 0.15,
            tree_parents: Optional[np.ndarray] = None, max_gamma: Optional[int] = None,
-           total_draft_rows: Optional[int] = None, nthreads: int = 0) -> OracleResult:
-    """Runs the oracle on host arrays (the packed layout of the C ABI)."""
+           total_draft_rows: Optional[int] = None, nthreads: int = 0,
+           nkl_position: Optional[np.ndarray] = None, nkl_alpha: float = 0.0,
+           nkl_delta_max: float = 0.0) -> OracleResult:
+    """Runs the oracle on host arrays (the packed layout of the C ABI).
+    nkl_position (NKL mode): 0-based position of every draft token in the
+    generated sequence, for the position-adaptive threshold (None: constant)."""
     lib = _load()
     gamma = np.ascontiguousarray(gamma, np.int32)
     B = int(gamma.shape[0])
@@ -104,6 +116,7 @@ def verify(target: np.ndarray, draft: Optional[np.ndarray], dtype: str, gamma: n
     u_accept = c(u_accept, np.float32)
     u_resample = c(u_resample, np.float32)
     tree_parents = c(tree_parents, np.int32)
+    nkl_position = c(nkl_position, np.int32)
     out_tokens = np.full(max(R_t, 1), -7, np.int32)
     out_num = np.full(B, -7, np.int32)
     nkl = np.full(max(R_d, 1), np.nan)
@@ -117,7 +130,7 @@ def verify(target: np.ndarray, draft: Optional[np.ndarray], dtype: str, gamma: n
     dm = np.full(B, np.inf)
     rc = lib.sv_oracle_verify(_ptr(target), _ptr(draft), dt, B, V, _ptr(draft_tokens), _ptr(gamma),
                               _ptr(temperature), _ptr(u_accept), _ptr(u_resample), int(mode), float(delta),
-                              _ptr(tree_parents), int(max_gamma), int(total_draft_rows), _ptr(out_tokens),
+                              _ptr(nkl_position), float(nkl_alpha), float(nkl_delta_max), _ptr(tree_parents), int(max_gamma), int(total_draft_rows), _ptr(out_tokens),
                               _ptr(out_num), _ptr(nkl), _ptr(p_x), _ptr(q_x), _ptr(alpha), _ptr(resid),
                               _ptr(tnode), _ptr(flags), _ptr(am), _ptr(dm), int(nthreads))
     if rc != 0:
@@ -129,4 +142,5 @@ def verify(target: np.ndarray, draft: Optional[np.ndarray], dtype: str, gamma: n
 def verify_workload(w, nthreads: int = 0) -> OracleResult:
     """Convenience: runs the oracle on a ``synthetic.Workload``-like object."""
     return verify(w.target, w.draft, w.dtype, w.gamma, w.draft_tokens, w.temperature, w.u_accept,
-                  w.u_resample, w.mode, w.delta, w.tree_parents, w.max_gamma, w.total_draft_rows, nthreads)
+                  w.u_resample, w.mode, w.delta, w.tree_parents, w.max_gamma, w.total_draft_rows, nthreads,
+                  getattr(w, "nkl_position", None), getattr(w, "nkl_alpha", 0.0), getattr(w, "nkl_delta_max", 0.0))

@@ -30,7 +30,12 @@
 //    row gamma.
 //  * NKL mode ("Chain of Draft" page, section 3.2): nkl_i = KL(q_i || p_i) / ln V
 //    at the request's temperature, accepted while nkl_i < delta; at the first
-//    failure emit argmax of target row j.
+//    failure emit argmax of target row j.  With per-position positions
+//    ("Chain of Draft" page, section 4.3, position-adaptive threshold) the
+//    threshold of draft token i is
+//        delta_i = min(delta_max, delta * (1 + alpha * log2(pos_i + 1))),
+//    pos_i >= 0 being the token's 0-based position in the generated sequence
+//    (so the first token has delta_i = delta, as in the page's examples).
 //  * Tree mode ("Parallel Drafting" page, section 2.2 tree draft; Gemma-4 MTP
 //    page, section 6.2 "longest accepted path"): node n (parent pi(n)) is
 //    accepted iff its parent is accepted and its token equals argmax of the
@@ -40,7 +45,7 @@
 // Flags (stochastic mode) mark requests whose result is decided within 1e-5
 // of a boundary: an acceptance decision with |u_i - alpha_i| < 1e-5, or a draw
 // whose uniform lies within 1e-5 of a CDF step.  In NKL mode a decision with
-// |nkl_i - delta| < 1e-6*delta is flagged.
+// |nkl_i - delta_i| < 1e-6*delta_i is flagged.
 
 #include <cmath>
 #include <cstdint>
@@ -149,6 +154,8 @@ struct Args {
   const float* u_resample;
   int32_t mode;
   float delta;
+  const int32_t* nkl_position;  // NULL: the constant threshold delta
+  float nkl_alpha, nkl_delta_max;
   const int32_t* parents;
   int32_t max_gamma;
   int32_t* out_tokens;
@@ -179,6 +186,14 @@ void mark_invalid(const Args& a, int32_t b, int64_t t0, int64_t d0, int32_t g) {
 }
 
 bool u_ok(float u) { return u >= 0.0f && u < 1.0f; }  // NaN fails both
+
+// Position-adaptive NKL threshold ("Chain of Draft" page, section 4.3): the
+// base threshold grows with the log of the position in the generated
+// sequence, up to a cap.  float64 throughout.
+double nkl_threshold(float delta, float alpha, float delta_max, int32_t pos) {
+  const double grown = (double)delta * (1.0 + (double)alpha * std::log2((double)pos + 1.0));
+  return std::fmin((double)delta_max, grown);
+}
 bool t_ok(float t) { return std::isfinite(t) && t > 0.0f; }
 
 void verify_request(const Args& a, int32_t b, int64_t t0, int64_t d0) {
@@ -194,6 +209,9 @@ void verify_request(const Args& a, int32_t b, int64_t t0, int64_t d0) {
       if (!u_ok(a.u_accept[d0 + i])) return mark_invalid(a, b, t0, d0, g);
     if (!u_ok(a.u_resample[b])) return mark_invalid(a, b, t0, d0, g);
   }
+  if (a.mode == M_NKL && a.nkl_position)
+    for (int32_t i = 0; i < g; ++i)
+      if (a.nkl_position[d0 + i] < 0) return mark_invalid(a, b, t0, d0, g);
   if (a.mode == M_TREE)
     for (int32_t k = 1; k <= g; ++k) {
       const int32_t p = a.parents[d0 + k - 1];
@@ -291,8 +309,10 @@ void verify_request(const Args& a, int32_t b, int64_t t0, int64_t d0) {
       if (a.out_p_x) a.out_p_x[d0 + i] = std::exp(lt[(size_t)a.tokens[d0 + i]]);
       if (a.out_q_x) a.out_q_x[d0 + i] = std::exp(ld[(size_t)a.tokens[d0 + i]]);
     }
-    const double delta = (double)a.delta;
     for (int32_t i = 0; i < g; ++i) {
+      const double delta = a.nkl_position
+                               ? nkl_threshold(a.delta, a.nkl_alpha, a.nkl_delta_max, a.nkl_position[d0 + i])
+                               : (double)a.delta;
       if (std::fabs(nkl[(size_t)i] - delta) < 1e-6 * delta) flags |= FLAG_NKL_BAND;
       if (!(nkl[(size_t)i] < delta)) {
         j = i;
@@ -343,10 +363,15 @@ extern "C" {
 //   All arrays are host memory.  Optional outputs may be NULL.
 //   Whole-call layout errors (a negative gamma, or sum(gamma) != total_draft_rows)
 //   mark every request invalid (num_accepted = -1, tokens = -1).
+//   nkl_position (NKL mode, may be NULL): int32 [sum(gamma)], 0-based position of each
+//   draft token in the generated sequence; the threshold of token i is then
+//   min(nkl_delta_max, delta * (1 + nkl_alpha * log2(pos_i + 1))), and a negative
+//   position makes its request invalid.
 int sv_oracle_verify(const void* target_logits, const void* draft_logits, int32_t dtype, int32_t batch,
                      int32_t vocab, const int32_t* draft_tokens, const int32_t* gamma_per_req,
                      const float* temperature, const float* u_accept, const float* u_resample, int32_t mode,
-                     float delta, const int32_t* tree_parents, int32_t max_gamma, int64_t total_draft_rows,
+                     float delta, const int32_t* nkl_position, float nkl_alpha, float nkl_delta_max,
+                     const int32_t* tree_parents, int32_t max_gamma, int64_t total_draft_rows,
                      int32_t* out_tokens, int32_t* out_num_accepted, double* out_nkl, double* out_p_x,
                      double* out_q_x, double* out_alpha, double* out_resid_mass, int32_t* out_tree_node,
                      int32_t* out_flags, double* out_accept_margin, double* out_draw_margin, int32_t nthreads) {
@@ -356,10 +381,12 @@ int sv_oracle_verify(const void* target_logits, const void* draft_logits, int32_
   if (mode == M_STOCH && (!u_accept || !u_resample)) return -1;
   if (mode == M_TREE && !tree_parents) return -1;
   if (mode == M_NKL && !std::isfinite(delta)) return -1;
+  if (mode == M_NKL && nkl_position && !(std::isfinite(nkl_alpha) && std::isfinite(nkl_delta_max))) return -1;
   if (total_draft_rows > 0 && !draft_tokens) return -1;
 
   Args a{target_logits, draft_logits, dtype, batch, vocab, draft_tokens, gamma_per_req, temperature, u_accept,
-         u_resample, mode, delta, tree_parents, max_gamma, out_tokens, out_num_accepted, out_nkl, out_p_x,
+         u_resample, mode, delta, mode == M_NKL ? nkl_position : nullptr, nkl_alpha, nkl_delta_max, tree_parents,
+         max_gamma, out_tokens, out_num_accepted, out_nkl, out_p_x,
          out_q_x, out_alpha, out_resid_mass, out_tree_node, out_flags, out_accept_margin, out_draw_margin};
 
   std::vector<int64_t> t_off((size_t)batch + 1, 0), d_off((size_t)batch + 1, 0);
@@ -386,6 +413,11 @@ int sv_oracle_verify(const void* target_logits, const void* draft_logits, int32_
 #endif
   for (int32_t b = 0; b < batch; ++b) verify_request(a, b, t_off[(size_t)b], d_off[(size_t)b]);
   return 0;
+}
+
+// The position-adaptive NKL threshold of a draft token at 0-based position pos.
+double sv_oracle_nkl_threshold(float delta, float alpha, float delta_max, int32_t pos) {
+  return nkl_threshold(delta, alpha, delta_max, pos);
 }
 
 int sv_oracle_max_threads(void) {

@@ -47,7 +47,7 @@ STOCHASTIC, GREEDY, NKL, TREE_GREEDY = 0, 1, 2, 3
 MODE_NAMES = {STOCHASTIC: "stochastic", GREEDY: "greedy", NKL: "nkl", TREE_GREEDY: "tree"}
 
 # purposes of the random streams
-_P_TARGET, _P_SPIKE, _P_DNOISE, _P_DRAW, _P_UACC, _P_URES, _P_PARAM = range(7)
+_P_TARGET, _P_SPIKE, _P_DNOISE, _P_DRAW, _P_UACC, _P_URES, _P_PARAM, _P_POS = range(8)
 
 # Trees used by the tree-draft workload.  Entry k is the parent of node k
 # (node 0 is the root, whose entry is -1).  "LITERAL16": a root with 3
@@ -104,6 +104,11 @@ class Workload:
     tree_parents: Optional[np.ndarray] = None  # int32 [sum(gamma)] (tree mode)
     max_gamma: int = 0
     meta: dict = field(default_factory=dict)
+    # NKL mode, position-adaptive threshold: 0-based position of every draft
+    # token in the generated sequence (None: the constant threshold delta)
+    nkl_position: Optional[np.ndarray] = None  # int32 [sum(gamma)]
+    nkl_alpha: float = 0.0
+    nkl_delta_max: float = 0.0
 
     @property
     def total_draft_rows(self) -> int:
@@ -131,6 +136,24 @@ class Workload:
         s = 2 if self.dtype == "bf16" else 4
         n = self.target.shape[0] + (0 if self.draft is None else self.draft.shape[0])
         return s * self.vocab * n
+
+    def with_positions(self, start_max: int = 4096, alpha: float = 0.08, delta_max: float = 0.3,
+                       seed: int = BASE_SEED, wid: int = 7) -> "Workload":
+        """The same inputs with generation positions for the position-adaptive
+        NKL threshold ("Chain of Draft" page, section 4.3: long generations,
+        delta_base 0.15, alpha 0.08, cap 0.3).  Request b's drafts continue a
+        sequence at a start position ~ U{0 .. start_max-1}; draft token i of
+        request b is at start_b + i."""
+        w = Workload(**{k: getattr(self, k) for k in self.__dataclass_fields__})
+        g = _gen(wid, _P_POS, 0, seed)
+        start = g.integers(0, start_max, self.batch, dtype=np.int64)
+        d_off = self.d_off
+        pos = np.empty(self.total_draft_rows, np.int32)
+        for b in range(self.batch):
+            pos[d_off[b]:d_off[b + 1]] = start[b] + np.arange(self.gamma[b])
+        w.nkl_position, w.nkl_alpha, w.nkl_delta_max = pos, float(alpha), float(delta_max)
+        w.name = self.name + "_pos"
+        return w
 
     def with_mode(self, mode: int, delta: Optional[float] = None) -> "Workload":
         w = Workload(**{k: getattr(self, k) for k in self.__dataclass_fields__})

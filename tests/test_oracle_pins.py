@@ -327,6 +327,85 @@ def test_nkl_range_on_long_drafts():
 
 
 # --------------------------------------------------------------------------
+# NKL with the position-adaptive threshold ("Chain of Draft" page, section 4.3)
+# --------------------------------------------------------------------------
+
+def test_nkl_threshold_page_examples():
+    g = json.load(open(os.path.join(GOLD, "nkl_threshold.json")))
+    d, a, m = g["delta_base"], g["alpha"], g["delta_max"]
+    for ex in g["printed_examples"] + g["cap_examples"]:
+        got = oracle.nkl_threshold(d, a, m, ex["position_1based"] - 1)  # the oracle takes 0-based positions
+        assert abs(got / ex["delta"] - 1) < 1e-6, ex  # float32 inputs widen to float64
+    for ex in g["inconsistent_examples"]:
+        got = oracle.nkl_threshold(d, a, m, ex["position_1based"] - 1)
+        assert abs(got / ex["formula"] - 1) < 1e-6 and abs(got - ex["printed"]) > 0.01
+    # non-decreasing along the sequence for alpha >= 0, and never above the cap
+    prev = 0.0
+    for pos in list(range(0, 70)) + [2 ** k - 1 for k in range(7, 31)]:
+        t = oracle.nkl_threshold(d, a, m, pos)
+        assert prev <= t <= np.float32(m)
+        prev = t
+
+
+def _nkl_rows(seed, B, gam, V, T):
+    rng = np.random.default_rng(seed)
+    t = (3 * rng.standard_normal((B * (gam + 1), V))).astype(np.float32)
+    d = np.concatenate([t[b * (gam + 1): b * (gam + 1) + gam] for b in range(B)]) + \
+        (0.3 + 1.2 * rng.random((B * gam, 1))).astype(np.float32) * rng.standard_normal((B * gam, V)).astype(np.float32)
+    return t, d.astype(np.float32)
+
+
+def test_nkl_adaptive_alpha_zero_is_the_constant_threshold():
+    B, gam, V, T = 4, 6, 2048, 0.6
+    t, d = _nkl_rows(11, B, gam, V, T)
+    temps = np.full(B, T, np.float32)
+    ref = oracle.verify(t, d, "f32", np.full(B, gam, np.int32), np.zeros(B * gam, np.int32), temps, None, None,
+                        K, 0.15)
+    pos = np.arange(B * gam, dtype=np.int32) * 977
+    for dmax in (0.15, 0.5, 10.0):
+        r = oracle.verify(t, d, "f32", np.full(B, gam, np.int32), np.zeros(B * gam, np.int32), temps, None, None,
+                          K, 0.15, nkl_position=pos, nkl_alpha=0.0, nkl_delta_max=dmax)
+        assert (r.tokens == ref.tokens).all() and (r.num_accepted == ref.num_accepted).all()
+        assert np.array_equal(r.nkl, ref.nkl)
+
+
+def test_nkl_adaptive_threshold_decides():
+    """The decision is the first i with nkl_i >= delta_i, where nkl_i comes from
+    scipy's KL and delta_i from the pinned threshold; positions near the start
+    of a sequence get the base threshold, far ones a larger one."""
+    B, gam, V, T = 6, 8, 4096, 0.6
+    t, d = _nkl_rows(12, B, gam, V, T)
+    Td = np.float64(np.float32(T))
+    starts = np.array([0, 3, 60, 1023, 5000, 2 ** 21], np.int64)
+    pos = np.concatenate([s + np.arange(gam) for s in starts]).astype(np.int32)
+    r = oracle.verify(t, d, "f32", np.full(B, gam, np.int32), np.zeros(B * gam, np.int32), np.full(B, T, np.float32),
+                      None, None, K, 0.15, nkl_position=pos, nkl_alpha=0.08, nkl_delta_max=0.3)
+    nchanged = 0
+    for b in range(B):
+        kl = [stats.entropy(special.softmax(d[b * gam + i].astype(np.float64) / Td),
+                            special.softmax(t[b * (gam + 1) + i].astype(np.float64) / Td)) / np.log(V)
+              for i in range(gam)]
+        thr = [oracle.nkl_threshold(0.15, 0.08, 0.3, int(pos[b * gam + i])) for i in range(gam)]
+        exp_n = next((i for i in range(gam) if not kl[i] < thr[i]), gam)
+        assert r.num_accepted[b] == exp_n
+        assert r.tokens[b * (gam + 1) + exp_n] == np.argmax(t[b * (gam + 1) + exp_n])
+        const_n = next((i for i in range(gam) if not kl[i] < np.float32(0.15)), gam)
+        nchanged += exp_n != const_n
+    assert nchanged > 0  # the schedule changes some decisions on these rows
+
+
+def test_nkl_negative_position_marks_only_its_request():
+    B, gam, V, T = 3, 4, 512, 1.0
+    t, d = _nkl_rows(13, B, gam, V, T)
+    pos = np.arange(B * gam, dtype=np.int32)
+    pos[gam + 2] = -1
+    r = oracle.verify(t, d, "f32", np.full(B, gam, np.int32), np.zeros(B * gam, np.int32), np.full(B, T, np.float32),
+                      None, None, K, 0.15, nkl_position=pos, nkl_alpha=0.08, nkl_delta_max=0.3)
+    assert r.num_accepted[1] == -1 and (r.tokens[gam + 1: 2 * (gam + 1)] == -1).all()
+    assert r.num_accepted[0] >= 0 and r.num_accepted[2] >= 0
+
+
+# --------------------------------------------------------------------------
 # tree mode: golden, brute force, chain == greedy
 # --------------------------------------------------------------------------
 
