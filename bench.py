@@ -42,6 +42,9 @@ WORKLOADS = {
     "llama3": ({}, 0, "llama3-shaped stochastic verify: B=32, gamma=5, V=128256, bf16"),
     "long_greedy": ({"mode": 1}, 1, "long parallel drafts, greedy: B=64, gamma=16, V=128256, bf16"),
     "long_nkl": ({"mode": 2}, 2, "long parallel drafts, NKL delta=0.15, T=0.6: B=64, gamma=16, V=128256, bf16"),
+    "long_nkl_pos": ({"mode": 2}, 2, "long parallel drafts, NKL with the position-adaptive threshold (delta_base=0.15, "
+                                      "alpha=0.08, cap 0.3; start positions ~U{0..4095}), T=0.6: B=64, gamma=16, "
+                                      "V=128256, bf16"),
     "ragged": ({}, 0, "large-batch ragged stochastic: B=256, gamma~U{1..8}, V=152064, bf16"),
     "tree": ({}, 3, "tree draft greedy verify: B=16, 16-node trees, V=128256, bf16"),
 }
@@ -126,6 +129,15 @@ def algorithmic_bytes(w, num_accepted):
     return rowstats, rowstats
 
 
+def make_workload(name):
+    import synthetic
+    kw, _, _ = WORKLOADS[name]
+    maker = {"llama3": synthetic.make_llama3, "long_greedy": synthetic.make_long, "long_nkl": synthetic.make_long,
+             "long_nkl_pos": synthetic.make_long, "ragged": synthetic.make_ragged, "tree": synthetic.make_tree}[name]
+    w = maker(**kw)
+    return w.with_positions() if name == "long_nkl_pos" else w
+
+
 def run_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
     import numpy as np
     import torch
@@ -135,10 +147,8 @@ def run_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
 
     import draft_token_verification_05_amd as sv
 
-    kw, mode, desc = WORKLOADS[name]
-    maker = {"llama3": synthetic.make_llama3, "long_greedy": synthetic.make_long, "long_nkl": synthetic.make_long,
-             "ragged": synthetic.make_ragged, "tree": synthetic.make_tree}[name]
-    w = maker(**kw)
+    _, mode, desc = WORKLOADS[name]
+    w = make_workload(name)
     dev = torch.device("cuda:0")
     soft = mode in (0, 2)
     base = to_device(w)
@@ -157,9 +167,13 @@ def run_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
     ev = hip.events(4 * len(sampled))
     ev_all = hip.events(2)
 
+    positions = None if w.nkl_position is None else torch.from_numpy(w.nkl_position).to(dev)
+
     def make_args(d, events_ptr):
         cfg = sv.make_config(B, V, cfg0.dtype, w.max_gamma, R_d, stream.cuda_stream, ws.data_ptr(), ws.numel(),
-                             phase_events=events_ptr)
+                             phase_events=events_ptr,
+                             nkl_position=0 if positions is None else positions.data_ptr(),
+                             nkl_alpha=w.nkl_alpha, nkl_delta_max=w.nkl_delta_max)
         a = (d["target"].data_ptr(), d["draft"].data_ptr() if soft else 0, d["tokens"].data_ptr(),
              d["gamma"].data_ptr(), d["temp"].data_ptr() if soft else 0, d["ua"].data_ptr() if mode == 0 else 0,
              d["ur"].data_ptr() if mode == 0 else 0, mode, w.delta,
@@ -204,12 +218,8 @@ def run_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
 
 
 def cpu_baseline(name, budget_s=8.0):
-    import synthetic
     import oracle
-    kw, _, _ = WORKLOADS[name]
-    maker = {"llama3": synthetic.make_llama3, "long_greedy": synthetic.make_long, "long_nkl": synthetic.make_long,
-             "ragged": synthetic.make_ragged, "tree": synthetic.make_tree}[name]
-    w = maker(**kw)
+    w = make_workload(name)
     threads = oracle.max_threads()
     oracle.verify_workload(w, nthreads=threads)  # warm (page-in)
     reps, t0 = 0, time.perf_counter()

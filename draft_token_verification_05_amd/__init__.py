@@ -49,6 +49,9 @@ class sv_config(ctypes.Structure):
         ("out_resid_mass", ctypes.c_void_p),
         ("out_tree_node", ctypes.c_void_p),
         ("phase_events", ctypes.c_void_p),
+        ("nkl_position", ctypes.c_void_p),
+        ("nkl_alpha", ctypes.c_float),
+        ("nkl_delta_max", ctypes.c_float),
     ]
 
 
@@ -89,11 +92,12 @@ _lib = _load()
 def make_config(batch: int, vocab: int, dtype: int, max_gamma: int, total_draft_rows: int, stream: int = 0,
                 workspace: int = 0, workspace_bytes: int = 0, out_p_x: int = 0, out_q_x: int = 0,
                 out_resid_mass: int = 0, out_tree_node: int = 0, phase_events: int = 0,
-                wait_polls: int = 0) -> sv_config:
+                wait_polls: int = 0, nkl_position: int = 0, nkl_alpha: float = 0.0,
+                nkl_delta_max: float = 0.0) -> sv_config:
     return sv_config(ctypes.sizeof(sv_config), int(batch), int(vocab), int(dtype), int(max_gamma), int(wait_polls),
                      int(total_draft_rows), stream or None, workspace or None, int(workspace_bytes),
                      out_p_x or None, out_q_x or None, out_resid_mass or None, out_tree_node or None,
-                     phase_events or None)
+                     phase_events or None, nkl_position or None, float(nkl_alpha), float(nkl_delta_max))
 
 
 def spec_verify(target_logits: int, draft_logits: int, draft_tokens: int, gamma_per_req: int, temperature: int,
@@ -180,8 +184,14 @@ def _check(t, name, dtype, numel=None, dev=None):
 def verify(target_logits, draft_logits, draft_tokens, gamma_per_req, temperature=None, u_accept=None,
            u_resample=None, mode: int | str = SV_MODE_STOCHASTIC, delta: float = 0.15, tree_parents=None, *,
            max_gamma: Optional[int] = None, workspace=None, diagnostics: bool = False, out_nkl: bool = False,
-           phase_events: int = 0, stream=None, wait_polls: int = 0) -> VerifyOutput:
+           phase_events: int = 0, stream=None, wait_polls: int = 0, nkl_position=None, nkl_alpha: float = 0.0,
+           nkl_delta_max: float = 0.0) -> VerifyOutput:
     """Runs one verify step on device tensors (packed layout, see specverify.h).
+
+    NKL mode: ``nkl_position`` (int32 [sum(gamma)] on the GPU, optional) gives
+    every draft token's 0-based position in the generated sequence, for the
+    position-adaptive threshold min(nkl_delta_max, delta * (1 + nkl_alpha *
+    log2(position + 1))).
 
     ``target_logits`` [sum(gamma+1), V] and ``draft_logits`` [sum(gamma), V] are
     torch.bfloat16 or torch.float32 on the GPU.  The call is asynchronous on
@@ -210,6 +220,7 @@ def verify(target_logits, draft_logits, draft_tokens, gamma_per_req, temperature
     _check(u_accept, "u_accept", torch.float32, R_d, dev)
     _check(u_resample, "u_resample", torch.float32, B, dev)
     _check(tree_parents, "tree_parents", torch.int32, R_d, dev)
+    _check(nkl_position, "nkl_position", torch.int32, R_d, dev)
     if draft_logits is not None:
         _check(draft_logits, "draft_logits", target_logits.dtype, None, dev)
         if draft_logits.dim() != 2 or draft_logits.shape[1] != V or draft_logits.shape[0] != R_d:
@@ -229,7 +240,8 @@ def verify(target_logits, draft_logits, draft_tokens, gamma_per_req, temperature
         tnode = torch.empty(B, dtype=torch.int32, device=dev)
     if stream is None:
         stream = torch.cuda.current_stream(dev)
-    cfg = make_config(B, V, dt, max_gamma, R_d, stream=int(stream.cuda_stream), wait_polls=wait_polls)
+    cfg = make_config(B, V, dt, max_gamma, R_d, stream=int(stream.cuda_stream), wait_polls=wait_polls,
+                      nkl_position=_ptr(nkl_position), nkl_alpha=nkl_alpha, nkl_delta_max=nkl_delta_max)
     need = spec_verify_workspace_size(cfg)
     if workspace is None:
         workspace = workspace_for(cfg, dev)

@@ -60,6 +60,9 @@ int validate(const void* target, const void* draft, const int32_t* tokens, const
   if (soft && !temp) return SV_EINVAL;
   if (mode == SV_MODE_STOCHASTIC && (!ur || (R_d > 0 && !ua))) return SV_EINVAL;
   if (mode == SV_MODE_NKL && (!std::isfinite(delta) || (R_d > 0 && !out_nkl))) return SV_EINVAL;
+  if (mode == SV_MODE_NKL && cfg->nkl_position &&
+      !(std::isfinite(cfg->nkl_alpha) && std::isfinite(cfg->nkl_delta_max) && aligned(cfg->nkl_position, 4)))
+    return SV_EINVAL;
   if (mode == SV_MODE_TREE_GREEDY && R_d > 0 && !parents) return SV_EINVAL;
 
   const size_t es = (size_t)sv::elem_size(cfg->dtype);
@@ -164,6 +167,9 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   p.n_task = (int32_t)(mode == SV_MODE_STOCHASTIC ? R_d : R_d + B);
   p.nch = (int32_t)((V + sv::chunk_stats(cfg->dtype, mode) - 1) / sv::chunk_stats(cfg->dtype, mode));
   p.delta = delta;
+  p.nkl_pos = mode == SV_MODE_NKL ? cfg->nkl_position : nullptr;
+  p.nkl_alpha = cfg->nkl_alpha;
+  p.nkl_dmax = cfg->nkl_delta_max;
   p.want_kl = (mode == SV_MODE_NKL || (mode == SV_MODE_STOCHASTIC && out_nkl)) ? 1 : 0;
   p.hdr = reinterpret_cast<int32_t*>(ws + L.off_hdr);
   p.d_off = reinterpret_cast<int32_t*>(ws + L.off_doff);

@@ -943,6 +943,16 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params p) {
 constexpr double kKlErr = 3e-7;
 constexpr double kKlRel = 1e-5;
 
+// NKL threshold of draft row `row`: delta, or with generation positions
+// ("Chain of Draft" page, section 4.3, position-adaptive threshold)
+// min(delta_max, delta * (1 + alpha * log2(pos + 1))) for the row's 0-based
+// position pos, in float64.  k_decide and k_refine take it from here.
+__device__ __forceinline__ double nkl_delta(const Params& p, int64_t row) {
+  if (!p.nkl_pos) return (double)p.delta;
+  const double pos = (double)p.nkl_pos[row];
+  return fmin((double)p.nkl_dmax, (double)p.delta * (1.0 + (double)p.nkl_alpha * log2(pos + 1.0)));
+}
+
 // Merged statistics of one task.
 struct Merged {
   float mt, md;
@@ -1609,7 +1619,7 @@ __device__ __forceinline__ void kl_finish(const Params& p, int b, SH& sh) {
     if (!need) continue;
     const double nkl = p.V > 1 ? kl / lnV : 0.0;
     p.out_nkl[pos] = (float)nkl;  // the other positions were written by k_decide
-    if (!(nkl < (double)p.delta)) first = min(first, i);
+    if (!(nkl < nkl_delta(p, pos))) first = min(first, i);
   }
   if (MODE == SV_MODE_NKL) {
     const int jr = block_min_int(first, sh.red_i);
@@ -1689,6 +1699,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
         if (!unit_ok(ps.u)) bad = true;
       }
       if (!xok) bad = true;
+      if (MODE == SV_MODE_NKL && p.nkl_pos && p.nkl_pos[d0 + ti] < 0) bad = true;
     }
     if ((tid & (S - 1)) == 0 && MODE == SV_MODE_TREE_GREEDY && ti >= 1 && ti <= g) {
       const int xn = p.tokens[d0 + ti - 1], pa = p.parents[d0 + ti - 1];
@@ -1738,7 +1749,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
           const double klv = r.w / r.sd * c - (double)(r.md - r.mt) * c - lg;
           const double err = kKlErr * (r.z / r.sd * c + 1.0);
           need = (err > kKlRel * klv) ? 1 : 0;
-          if (MODE == SV_MODE_NKL && fabs(klv - (double)p.delta * lnV) <= err) need = 1;
+          if (MODE == SV_MODE_NKL && fabs(klv - nkl_delta(p, d0 + ti) * lnV) <= err) need = 1;
           kl = klv;
         }
       } else if (MODE == SV_MODE_GREEDY) {
@@ -1761,7 +1772,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
         } else {
           const double nkl = p.V > 1 ? sh.kl1[tid] / lnV : 0.0;
           if (writer && p.out_nkl) p.out_nkl[pos] = (float)nkl;
-          if (MODE == SV_MODE_NKL) sh.acc[tid] = nkl < (double)p.delta ? 1 : 0;
+          if (MODE == SV_MODE_NKL) sh.acc[tid] = nkl < nkl_delta(p, pos) ? 1 : 0;
         }
       }
       if (writer) {
@@ -1818,6 +1829,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
       const int pa = p.parents[d0 + k];  // parent of node k + 1
       ok = ok && pa >= 0 && pa <= k;
     }
+    if (MODE == SV_MODE_NKL && p.nkl_pos) ok = ok && p.nkl_pos[d0 + k] >= 0;
     if (!ok) bad = true;
   }
   if (__syncthreads_or(bad)) {

@@ -144,6 +144,8 @@ struct Params {
   int32_t nslices;     // vocabulary slices per row (chunk_t elements each)
   int32_t slices_per_helper;
   float delta;
+  const int32_t* nkl_pos;    // NKL: generation position of every draft row (NULL: constant delta)
+  float nkl_alpha, nkl_dmax;  // NKL with positions: growth and cap of the threshold
   int32_t want_kl;  // compute KL(q || p) (NKL mode, or stochastic with out_nkl)
   uint32_t epoch;      // fused kernel: tag of this call's statistics partials (never 0)
   int32_t wait_polls;  // fused kernel: polls of a partial before a helper computes it itself

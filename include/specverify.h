@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define SPECVERIFY_VERSION 10000 /* 1.0.0 */
+#define SPECVERIFY_VERSION 10100 /* 1.1.0: position-adaptive NKL threshold (sv_config.nkl_*) */
 
 /* status codes */
 #define SV_OK 0
@@ -105,6 +105,15 @@ typedef struct sv_config {
   float* out_resid_mass;    /* [B] stochastic: sum_y max(0, p_j - q_j) after a rejection, 1 for a bonus */
   int32_t* out_tree_node;   /* [B] tree mode: id of the deepest accepted node */
   void* phase_events;       /* optional hipEvent_t[SV_NUM_PHASE_EVENTS] (see above) */
+  /* NKL mode, optional: position-adaptive threshold ("Chain of Draft" page, section 4.3).
+   * nkl_position: device int32 [total_draft_rows], the 0-based position of each draft token
+   * in the generated sequence (NULL = the constant threshold delta for every token).  Token i
+   * is then accepted while nkl_i < min(nkl_delta_max, delta * (1 + nkl_alpha * log2(pos_i + 1))),
+   * evaluated in float64.  nkl_alpha and nkl_delta_max must be finite when nkl_position is set;
+   * a negative position is a data error of its request. */
+  const int32_t* nkl_position;
+  float nkl_alpha;
+  float nkl_delta_max;
 } sv_config;
 
 /*

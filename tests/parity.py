@@ -38,6 +38,7 @@ def to_device(w, dev="cuda:0"):
         ua=f32(w.u_accept),
         ur=f32(w.u_resample),
         parents=None if w.tree_parents is None else i32(w.tree_parents),
+        nkl_position=None if getattr(w, "nkl_position", None) is None else i32(w.nkl_position),
     )
 
 
@@ -52,7 +53,9 @@ def run_gpu(w, d=None, diagnostics=True, out_nkl=False, max_gamma=None, workspac
                     d["temp"] if soft else None, d["ua"] if mode == 0 else None, d["ur"] if mode == 0 else None,
                     mode, w.delta, d["parents"] if mode == 3 else None,
                     max_gamma=w.max_gamma if max_gamma is None else max_gamma, diagnostics=diagnostics,
-                    out_nkl=out_nkl, workspace=workspace, wait_polls=wait_polls)
+                    out_nkl=out_nkl, workspace=workspace, wait_polls=wait_polls,
+                    nkl_position=d.get("nkl_position") if mode == 2 else None,
+                    nkl_alpha=getattr(w, "nkl_alpha", 0.0), nkl_delta_max=getattr(w, "nkl_delta_max", 0.0))
     torch.cuda.synchronize()
     host = lambda t: None if t is None else t.cpu().numpy()
     return dict(tokens=host(out.tokens), num=host(out.num_accepted), nkl=host(out.nkl), p_x=host(out.p_x),

@@ -54,7 +54,7 @@ def test_library_exports_every_declared_symbol(sv):
 
 
 def test_version_and_status_strings(sv):
-    assert sv.spec_verify_version() == 10000
+    assert sv.spec_verify_version() == 10100
     for st in (0, -1, -2, -3, -4):
         assert sv.spec_verify_status_string(st).startswith("SV_")
     assert "unknown" in sv.spec_verify_status_string(7)
@@ -128,6 +128,24 @@ def test_synchronous_argument_errors(sv):
     cfg = sv.make_config(4, 1000, 1, 4, 8, 0, FAKE, 1 << 30)
     cfg.wait_polls = -1
     assert sv.spec_verify(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0.1, 0, FAKE, FAKE, 0, cfg) == E
+
+
+def test_nkl_position_arguments(sv):
+    """Position-adaptive NKL threshold: with nkl_position set in NKL mode, a
+    non-finite growth or cap, or a misaligned array, is rejected; other modes
+    never read it.  Validation reaches the (too small) workspace otherwise."""
+    E, W = sv.SV_EINVAL, sv.SV_EWORKSPACE
+
+    def nkl_call(mode=2, pos=FAKE, alpha=0.08, dmax=0.3):
+        cfg = sv.make_config(4, 1000, 1, 4, 8, 0, FAKE, 16, nkl_position=pos, nkl_alpha=alpha, nkl_delta_max=dmax)
+        return sv.spec_verify(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 0, mode, 0.15, 0, FAKE, FAKE, FAKE, cfg)
+
+    assert nkl_call() == W
+    assert nkl_call(pos=0, alpha=float("nan")) == W  # not read without positions
+    assert nkl_call(alpha=float("nan")) == E
+    assert nkl_call(dmax=float("inf")) == E
+    assert nkl_call(pos=FAKE + 2) == E
+    assert nkl_call(mode=1, alpha=float("nan"), pos=FAKE + 2) == W  # greedy ignores it
 
 
 def test_mode_specific_null_pointers_allowed(sv):

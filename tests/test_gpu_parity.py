@@ -77,6 +77,45 @@ def test_ragged_stochastic():
     check(synthetic.make_ragged())
 
 
+# ------------------------------------------- position-adaptive NKL threshold
+
+def test_long_nkl_position_adaptive():
+    """NKL with the position-adaptive threshold ("Chain of Draft" page, section
+    4.3) on the long-draft workload; the grown thresholds accept more than the
+    constant one."""
+    w = synthetic.make_long(mode=K)
+    g, _, _ = check(w.with_positions())
+    g0 = run_gpu(w, diagnostics=False)
+    assert g["num"].sum() > g0["num"].sum()
+
+
+@pytest.mark.parametrize("V,dtype", [(1000, "bf16"), (20000, "f32"), (70000, "bf16")])
+def test_nkl_position_adaptive_small(V, dtype):
+    w = synthetic.random_workload(seed=V % 61 + 5, mode=K, B=17, V=V, dtype=dtype, gmax=7, gmin=0)
+    check(w.with_positions(start_max=1 << 20))
+
+
+def test_nkl_position_adaptive_alpha_zero_equals_constant():
+    w = synthetic.random_workload(seed=77, mode=K, B=9, V=30000, dtype="bf16", gmax=6, gmin=1)
+    g0 = run_gpu(w)
+    g1 = run_gpu(w.with_positions(alpha=0.0, delta_max=1.0))
+    for k in ("tokens", "num", "nkl"):
+        assert np.array_equal(g0[k], g1[k]), k
+
+
+def test_nkl_position_adaptive_second_pass_and_invalid():
+    """Rows within a small noise of each other: positions go through the KL
+    second pass, whose decision uses the same per-position threshold; a
+    negative position marks only its own request invalid."""
+    w = synthetic.random_workload(seed=19, mode=K, B=12, V=20000, dtype="bf16", gmax=5, gmin=3, sigma=0.003)
+    w = w.with_mode(K, delta=float(np.float32(1e-6))).with_positions(start_max=1 << 16, alpha=1.0, delta_max=1.0)
+    w.nkl_position = w.nkl_position.copy()
+    w.nkl_position[w.d_off[4] + 1] = -3
+    g, o, rep = check(w, out_nkl=True)
+    assert g["num"][4] == -1 and (np.delete(g["num"], 4) >= 0).all()
+    assert rep.max_rel_nkl < 2e-5
+
+
 @pytest.mark.parametrize("name", ["tree", "tree13"])
 def test_tree(name):
     g, o, _ = check(synthetic.make(name))
