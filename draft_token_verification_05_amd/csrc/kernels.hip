@@ -946,9 +946,12 @@ constexpr double kKlRel = 1e-5;
 // NKL threshold of draft row `row`: delta, or with generation positions
 // ("Chain of Draft" page, section 4.3, position-adaptive threshold)
 // min(delta_max, delta * (1 + alpha * log2(pos + 1))) for the row's 0-based
-// position pos, in float64.  k_decide and k_refine take it from here.
+// position pos, in float64.  k_decide and k_refine take it from here; POS:
+// the call has positions (kernels compiled without them keep the registers
+// the float64 log2 would take).
+template <bool POS>
 __device__ __forceinline__ double nkl_delta(const Params& p, int64_t row) {
-  if (!p.nkl_pos) return (double)p.delta;
+  if (!POS || !p.nkl_pos) return (double)p.delta;
   const double pos = (double)p.nkl_pos[row];
   return fmin((double)p.nkl_dmax, (double)p.delta * (1.0 + (double)p.nkl_alpha * log2(pos + 1.0)));
 }
@@ -1605,7 +1608,7 @@ __device__ __forceinline__ void draw_select(const Params& p, int b, const Term& 
 // order.  NKL mode: k_decide wrote the outputs with every queued position
 // accepted (decision jnn); the first queued position that the second-pass
 // value rejects, if it precedes jnn, becomes the decision.
-template <int MODE, class SH>
+template <int MODE, bool POS, class SH>
 __device__ __forceinline__ void kl_finish(const Params& p, int b, SH& sh) {
   const ReqFin f = p.req_fin[b];
   const int t0 = f.d0 + b, NS = p.nslices;
@@ -1619,7 +1622,7 @@ __device__ __forceinline__ void kl_finish(const Params& p, int b, SH& sh) {
     if (!need) continue;
     const double nkl = p.V > 1 ? kl / lnV : 0.0;
     p.out_nkl[pos] = (float)nkl;  // the other positions were written by k_decide
-    if (!(nkl < nkl_delta(p, pos))) first = min(first, i);
+    if (!(nkl < nkl_delta<POS>(p, pos))) first = min(first, i);
   }
   if (MODE == SV_MODE_NKL) {
     const int jr = block_min_int(first, sh.red_i);
@@ -1639,7 +1642,8 @@ __device__ __forceinline__ void kl_finish(const Params& p, int b, SH& sh) {
 // temperature and resample uniform (ur is first used after the decision, so
 // its load may still be in flight).  FUSED (stochastic): called in the
 // statistics kernel itself, where it waits for the request's partials.
-template <int DT, bool VEC, int MODE, bool FUSED>
+// POS (NKL): per-position thresholds from generation positions.
+template <int DT, bool VEC, int MODE, bool FUSED, bool POS = false>
 __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bool ok, int d0, int d1, float T,
                                                float ur, DecideShared& sh, TreeShared<MODE>& tr, StatsShared* ssh) {
   constexpr bool SOFT = MODE == SV_MODE_STOCHASTIC || MODE == SV_MODE_NKL;
@@ -1699,7 +1703,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
         if (!unit_ok(ps.u)) bad = true;
       }
       if (!xok) bad = true;
-      if (MODE == SV_MODE_NKL && p.nkl_pos && p.nkl_pos[d0 + ti] < 0) bad = true;
+      if (MODE == SV_MODE_NKL && POS && p.nkl_pos[d0 + ti] < 0) bad = true;
     }
     if ((tid & (S - 1)) == 0 && MODE == SV_MODE_TREE_GREEDY && ti >= 1 && ti <= g) {
       const int xn = p.tokens[d0 + ti - 1], pa = p.parents[d0 + ti - 1];
@@ -1749,7 +1753,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
           const double klv = r.w / r.sd * c - (double)(r.md - r.mt) * c - lg;
           const double err = kKlErr * (r.z / r.sd * c + 1.0);
           need = (err > kKlRel * klv) ? 1 : 0;
-          if (MODE == SV_MODE_NKL && fabs(klv - nkl_delta(p, d0 + ti) * lnV) <= err) need = 1;
+          if (MODE == SV_MODE_NKL && fabs(klv - nkl_delta<POS>(p, d0 + ti) * lnV) <= err) need = 1;
           kl = klv;
         }
       } else if (MODE == SV_MODE_GREEDY) {
@@ -1772,7 +1776,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
         } else {
           const double nkl = p.V > 1 ? sh.kl1[tid] / lnV : 0.0;
           if (writer && p.out_nkl) p.out_nkl[pos] = (float)nkl;
-          if (MODE == SV_MODE_NKL) sh.acc[tid] = nkl < nkl_delta(p, pos) ? 1 : 0;
+          if (MODE == SV_MODE_NKL) sh.acc[tid] = nkl < nkl_delta<POS>(p, pos) ? 1 : 0;
         }
       }
       if (writer) {
@@ -1829,7 +1833,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
       const int pa = p.parents[d0 + k];  // parent of node k + 1
       ok = ok && pa >= 0 && pa <= k;
     }
-    if (MODE == SV_MODE_NKL && p.nkl_pos) ok = ok && p.nkl_pos[d0 + k] >= 0;
+    if (MODE == SV_MODE_NKL && POS) ok = ok && p.nkl_pos[d0 + k] >= 0;
     if (!ok) bad = true;
   }
   if (__syncthreads_or(bad)) {
@@ -1885,7 +1889,8 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
 }
 
 // H workgroups ("helpers") per request (see decide_request), after k_stats.
-template <int DT, bool VEC, int MODE>
+// POS: NKL with generation positions.
+template <int DT, bool VEC, int MODE, bool POS = false>
 __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
   constexpr bool SOFT = MODE == SV_MODE_STOCHASTIC || MODE == SV_MODE_NKL;
   __shared__ DecideShared sh;
@@ -1898,7 +1903,7 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
   const int d1 = p.d_off[b + 1];
   const float T = SOFT ? p.temp[b] : 1.0f;
   const float ur = MODE == SV_MODE_STOCHASTIC ? p.ur[b] : 0.0f;
-  decide_request<DT, VEC, MODE, false>(p, b, h, hdr == 0, d0, d1, T, ur, sh, tr, nullptr);
+  decide_request<DT, VEC, MODE, false, POS>(p, b, h, hdr == 0, d0, d1, T, ur, sh, tr, nullptr);
 }
 
 // The whole stochastic step in one dispatch (batches up to kLdsBatch, no KL
@@ -1941,7 +1946,7 @@ struct RefineShared {
   int flag;
 };
 
-template <int DT, bool VEC, int MODE>
+template <int DT, bool VEC, int MODE, bool POS = false>
 __global__ __launch_bounds__(kThreads) void k_refine(Params p) {
   __shared__ RefineShared sh;
   const int NS = p.nslices;
@@ -1962,7 +1967,7 @@ __global__ __launch_bounds__(kThreads) void k_refine(Params p) {
     const KlIn ri{e.ct, e.cd, e.kt, e.kd, e.lw};
     const double v = block_sum_d(kl_terms<DT>(qt, qd, ri, e.Lhi), sh.red_d);
     if (threadIdx.x == 0) st_dev(&p.kl_part[(int64_t)e.pos * NS + it % NS], v);
-    if (pend > 0 && arrive_last(p.cnt_kl + (int64_t)e.b * kCntStride, pend * NS, sh)) kl_finish<MODE>(p, e.b, sh);
+    if (pend > 0 && arrive_last(p.cnt_kl + (int64_t)e.b * kCntStride, pend * NS, sh)) kl_finish<MODE, POS>(p, e.b, sh);
   };
   issue(i0, ea, pa, at, ad);
   for (int64_t it = i0; it < i1; it += 2) {
@@ -2075,7 +2080,10 @@ void decide_dispatch(const Params& p, hipStream_t s) {
   switch (p.mode) {
     case SV_MODE_STOCHASTIC: hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_STOCHASTIC>), grid, blk, 0, s, p); break;
     case SV_MODE_GREEDY: hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_GREEDY>), grid, blk, 0, s, p); break;
-    case SV_MODE_NKL: hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_NKL>), grid, blk, 0, s, p); break;
+    case SV_MODE_NKL:
+      if (p.nkl_pos) hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_NKL, true>), grid, blk, 0, s, p);
+      else hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_NKL>), grid, blk, 0, s, p);
+      break;
     default: hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_TREE_GREEDY>), grid, blk, 0, s, p); break;
   }
 }
@@ -2215,7 +2223,10 @@ int launch_decide(const Params& p, bool vec, void* stream) {
 
 template <int DT, bool VEC>
 static void refine_dispatch(const Params& p, hipStream_t s, dim3 grid) {
-  if (p.mode == SV_MODE_NKL) hipLaunchKernelGGL((k_refine<DT, VEC, SV_MODE_NKL>), grid, dim3(kThreads), 0, s, p);
+  if (p.mode == SV_MODE_NKL && p.nkl_pos)
+    hipLaunchKernelGGL((k_refine<DT, VEC, SV_MODE_NKL, true>), grid, dim3(kThreads), 0, s, p);
+  else if (p.mode == SV_MODE_NKL)
+    hipLaunchKernelGGL((k_refine<DT, VEC, SV_MODE_NKL>), grid, dim3(kThreads), 0, s, p);
   else hipLaunchKernelGGL((k_refine<DT, VEC, SV_MODE_STOCHASTIC>), grid, dim3(kThreads), 0, s, p);
 }
 
