@@ -43,6 +43,8 @@ def _load():
         lib.sv_oracle_verify.restype = ctypes.c_int
         lib.sv_oracle_verify.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, i32, f32, P, f32, f32, P, i32, i64,
                                          P, P, P, P, P, P, P, P, P, P, P, i32]
+        lib.sv_oracle_sample_rows.restype = ctypes.c_int
+        lib.sv_oracle_sample_rows.argtypes = [P, i32, i64, i32, P, P, P, P, i32]
         lib.sv_oracle_nkl_threshold.restype = ctypes.c_double
         lib.sv_oracle_nkl_threshold.argtypes = [f32, f32, f32, i32]
         lib.sv_oracle_max_threads.restype = ctypes.c_int
@@ -52,6 +54,27 @@ def _load():
 
 def max_threads() -> int:
     return int(_load().sv_oracle_max_threads())
+
+
+def sample_rows(logits: np.ndarray, dtype: str, temperature: np.ndarray, u: np.ndarray, nthreads: int = 0):
+    """Draws one token per row from softmax(row / T) by the inverse CDF with the
+    row's uniform.  Returns (tokens int32 [rows], margins float64 [rows])."""
+    rows, V = int(logits.shape[0]), int(logits.shape[1])
+    if dtype == "bf16":
+        logits, dt = np.ascontiguousarray(logits, np.uint16), 1
+    elif dtype == "f32":
+        logits, dt = np.ascontiguousarray(logits, np.float32), 0
+    else:
+        raise ValueError(dtype)
+    temperature = np.ascontiguousarray(temperature, np.float32)
+    u = np.ascontiguousarray(u, np.float32)
+    out = np.full(max(rows, 1), -7, np.int32)
+    margin = np.full(max(rows, 1), np.nan)
+    rc = _load().sv_oracle_sample_rows(_ptr(logits), dt, rows, V, _ptr(temperature), _ptr(u), _ptr(out),
+                                       _ptr(margin), int(nthreads))
+    if rc != 0:
+        raise ValueError("sv_oracle_sample_rows rejected its arguments")
+    return out[:rows], margin[:rows]
 
 
 def nkl_threshold(delta: float, alpha: float, delta_max: float, position: int) -> float:

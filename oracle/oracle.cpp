@@ -36,6 +36,8 @@
 //        delta_i = min(delta_max, delta * (1 + alpha * log2(pos_i + 1))),
 //    pos_i >= 0 being the token's 0-based position in the generated sequence
 //    (so the first token has delta_i = delta, as in the page's examples).
+//  * Row sampling (sv_oracle_sample_rows): the drafter's draw of a token from
+//    softmax(x/T) of one row, by the same inverse CDF.
 //  * Tree mode ("Parallel Drafting" page, section 2.2 tree draft; Gemma-4 MTP
 //    page, section 6.2 "longest accepted path"): node n (parent pi(n)) is
 //    accepted iff its parent is accepted and its token equals argmax of the
@@ -412,6 +414,43 @@ int sv_oracle_verify(const void* target_logits, const void* draft_logits, int32_
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
 #endif
   for (int32_t b = 0; b < batch; ++b) verify_request(a, b, t_off[(size_t)b], d_off[(size_t)b]);
+  return 0;
+}
+
+// Draft-side sampling, the drafter's step before verification (draft tokens
+// "drawn from the draft softmax"; the "投机采样" page's draft loop draws
+// x_i ~ q_i): the token of row r is the inverse-CDF draw from
+// softmax(x_r / T_r) with the uniform u_r, y* = min{y : C_y > u*S} in ascending
+// token order (the rule of the verify step's bonus draw).  A row whose
+// temperature is not > 0 and finite, or whose uniform is outside [0, 1), gets
+// -1.  out_margin (may be NULL): the distance from u_r to the nearer edge of
+// y*'s CDF step (NaN for invalid rows).  Returns -1 on an argument error.
+int sv_oracle_sample_rows(const void* logits, int32_t dtype, int64_t rows, int32_t vocab, const float* temperature,
+                          const float* u, int32_t* out_tokens, double* out_margin, int32_t nthreads) {
+  if (rows < 0 || vocab <= 0 || (dtype != 0 && dtype != 1)) return -1;
+  if (rows > 0 && (!logits || !temperature || !u || !out_tokens)) return -1;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+  for (int64_t r = 0; r < rows; ++r) {
+    if (!t_ok(temperature[r]) || !u_ok(u[r])) {
+      out_tokens[r] = -1;
+      if (out_margin) out_margin[r] = kNaN;
+      continue;
+    }
+    std::vector<double> x, l, p((size_t)vocab);
+    load_row(logits, dtype, r, vocab, x);
+    log_softmax(x, (double)temperature[r], l);
+    NSum s;
+    for (int64_t y = 0; y < vocab; ++y) {
+      p[(size_t)y] = std::exp(l[(size_t)y]);
+      s.add(p[(size_t)y]);
+    }
+    double margin = 0.0;
+    out_tokens[r] = inverse_cdf(p, s.value(), (double)u[r], &margin);
+    if (out_margin) out_margin[r] = margin;
+  }
   return 0;
 }
 

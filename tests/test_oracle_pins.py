@@ -327,6 +327,59 @@ def test_nkl_range_on_long_drafts():
 
 
 # --------------------------------------------------------------------------
+# draft-side row sampling (the drafter's draw from softmax(x/T))
+# --------------------------------------------------------------------------
+
+def test_sample_rows_cdf_steps():
+    """p = (0.1, 0.2, 0.3, 0.4) at T = 1 (logits log p) has CDF steps at 0.1,
+    0.3, 0.6 and 1.0; y* = min{y : C_y > u}: a uniform just below a step stays
+    on the left token, just above it moves right.  The same at T = 2 with
+    logits 2 log p."""
+    p = np.array([0.1, 0.2, 0.3, 0.4])
+    u = np.array([0.0, 0.0999, 0.1001, 0.2999, 0.3001, 0.5999, 0.6001, 0.9999], np.float32)
+    want = [0, 0, 1, 1, 2, 2, 3, 3]
+    for T in (1.0, 2.0):
+        x = np.tile((T * np.log(p)).astype(np.float32), (len(u), 1))
+        tok, margin = oracle.sample_rows(x, "f32", np.full(len(u), T, np.float32), u)
+        assert tok.tolist() == want
+        assert np.allclose(margin[1:], 1e-4, rtol=0.01)  # every uniform sits 1e-4 from a step
+
+
+def test_sample_rows_is_the_bonus_draw():
+    """A verify request with gamma = 0 draws its bonus token from target row 0
+    with u_resample: the same draw as sampling that row."""
+    rng = np.random.default_rng(21)
+    B, V = 40, 3000
+    t = (3 * rng.standard_normal((B, V))).astype(np.float32)
+    T = (0.5 + rng.random(B)).astype(np.float32)
+    ur = rng.random(B, dtype=np.float32)
+    r = oracle.verify(t, np.zeros((0, V), np.float32), "f32", np.zeros(B, np.int32), np.zeros(0, np.int32), T,
+                      np.zeros(0, np.float32), ur, S)
+    tok, _ = oracle.sample_rows(t, "f32", T, ur)
+    assert (r.num_accepted == 0).all() and (r.tokens == tok).all()
+
+
+def test_sample_rows_chi_square():
+    """200k draws from one V = 8 row: token frequencies follow scipy's softmax."""
+    rng = np.random.default_rng(22)
+    V, n, T = 8, 200_000, 0.7
+    x = (2 * rng.standard_normal(V)).astype(np.float32)
+    tok, _ = oracle.sample_rows(np.tile(x, (n, 1)), "f32", np.full(n, T, np.float32),
+                                rng.random(n, dtype=np.float32))
+    P = special.softmax(x.astype(np.float64) / np.float64(np.float32(T)))
+    counts = np.bincount(tok, minlength=V)
+    assert stats.chisquare(counts, P * n).pvalue > 1e-3
+
+
+def test_sample_rows_invalid_inputs():
+    x = np.zeros((5, 16), np.float32)
+    T = np.array([1.0, 0.0, np.nan, 1.0, 1.0], np.float32)
+    u = np.array([0.5, 0.5, 0.5, 1.0, -0.1], np.float32)
+    tok, _ = oracle.sample_rows(x, "f32", T, u)
+    assert tok.tolist() == [8, -1, -1, -1, -1]  # uniform 16-token row: u = 0.5 lands on token 8
+
+
+# --------------------------------------------------------------------------
 # NKL with the position-adaptive threshold ("Chain of Draft" page, section 4.3)
 # --------------------------------------------------------------------------
 
