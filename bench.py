@@ -47,6 +47,9 @@ WORKLOADS = {
                                       "V=128256, bf16"),
     "ragged": ({}, 0, "large-batch ragged stochastic: B=256, gamma~U{1..8}, V=152064, bf16"),
     "tree": ({}, 3, "tree draft greedy verify: B=16, 16-node trees, V=128256, bf16"),
+    # draft-side sampling (the step before verify): one token per draft row of the llama3 batch
+    "sample_llama3": ({}, -1, "draft-side sampling of the llama3-shaped batch's draft rows: 160 rows, V=128256, "
+                              "bf16, per-request temperatures"),
 }
 
 
@@ -138,6 +141,69 @@ def make_workload(name):
     return w.with_positions() if name == "long_nkl_pos" else w
 
 
+def sample_inputs(name):
+    """Rows, per-row temperatures and uniforms of a sampling workload."""
+    import numpy as np
+    w = make_workload("llama3")
+    return w, w.draft, np.repeat(w.temperature, w.gamma).astype(np.float32), w.u_accept
+
+
+def run_sample_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
+    """Times spec_sample_rows on device-resident rows (rotated copies, like run_gpu)."""
+    import numpy as np
+    import torch
+
+    import draft_token_verification_05_amd as sv
+
+    _, _, desc = WORKLOADS[name]
+    w, rows_np, T_np, u_np = sample_inputs(name)
+    dev = torch.device("cuda:0")
+    rows, V = rows_np.shape
+    base = torch.from_numpy(np.ascontiguousarray(rows_np).view(np.int16)).to(dev).view(torch.bfloat16)
+    ncopies = max(2, min(64, -(-copies_bytes // (rows * V * 2))))
+    copies = [base] + [base.clone() for _ in range(ncopies - 1)]
+    T = torch.from_numpy(T_np).to(dev)
+    u = torch.from_numpy(u_np).to(dev)
+    out = torch.empty(rows, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    cfg0 = sv.make_config(rows, V, sv.SV_DTYPE_BF16, 0, 0)
+    ws = torch.zeros(sv.spec_verify_workspace_size(cfg0), dtype=torch.uint8, device=dev)
+    hip = Hip()
+    sampled = list(range(0, steps, max(1, event_every)))
+    ev = hip.events(4 * len(sampled))
+    ev_all = hip.events(2)
+    ev_base = ctypes.addressof(ev)
+
+    def cfg_for(k):
+        e = ev_base + 4 * (k // event_every) * ctypes.sizeof(ctypes.c_void_p) if (k >= 0 and k % event_every == 0) else 0
+        return sv.make_config(rows, V, sv.SV_DTYPE_BF16, 0, 0, stream.cuda_stream, ws.data_ptr(), ws.numel(),
+                              phase_events=e)
+
+    plain = cfg_for(-1)
+    timed = [cfg_for(k) for k in range(steps)]
+    for k in range(warmup):
+        st = sv.spec_sample_rows(copies[k % ncopies].data_ptr(), T.data_ptr(), u.data_ptr(), out.data_ptr(), plain)
+        if st != 0:
+            raise RuntimeError(sv.spec_verify_status_string(st))
+    torch.cuda.synchronize()
+    hip.lib.hipEventRecord(ctypes.c_void_p(ev_all[0]), ctypes.c_void_p(stream.cuda_stream))
+    for k in range(steps):
+        st = sv.spec_sample_rows(copies[k % ncopies].data_ptr(), T.data_ptr(), u.data_ptr(), out.data_ptr(),
+                                 timed[k])
+        if st != 0:
+            raise RuntimeError(sv.spec_verify_status_string(st))
+    hip.lib.hipEventRecord(ctypes.c_void_p(ev_all[1]), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    total_ms = hip.elapsed_ms(ev_all[0], ev_all[1])
+    ks = np.array([hip.elapsed_ms(ev[4 * n + 1], ev[4 * n + 2]) for n in range(len(sampled))])
+    hip.destroy(ev)
+    hip.destroy(ev_all)
+    # one read of every row, plus the selection's re-read of one wave-chunk (2048 tokens) per row
+    nbytes = rows * V * 2 + rows * min(V, 2048) * 2
+    return dict(desc=desc, rows=rows, V=V, ncopies=ncopies, ms_per_step=total_ms / steps, kernel_ms=float(ks.mean()),
+                bytes=nbytes, sampled=len(sampled))
+
+
 def run_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
     import numpy as np
     import torch
@@ -217,6 +283,22 @@ def run_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
                 kernel="k_fused" if single else "k_stats", kernel_bytes=step_bytes if single else rowstats_bytes)
 
 
+def cpu_baseline_sample(name, budget_s=8.0):
+    import oracle
+    _, rows, T, u = sample_inputs(name)
+    threads = oracle.max_threads()
+    oracle.sample_rows(rows, "bf16", T, u, nthreads=threads)  # warm (page-in)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.sample_rows(rows, "bf16", T, u, nthreads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": rows.shape[0] * reps / el, "unit": "sampled draft tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full passes over the {rows.shape[0]} rows, {el:.1f} s wall on {threads} host threads"}
+
+
 def cpu_baseline(name, budget_s=8.0):
     import oracle
     w = make_workload(name)
@@ -260,6 +342,25 @@ def main():
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(requests are independent, so more GPUs would each run their own share).", file=sys.stderr)
         sys.exit(2)
+    if args.workload.startswith("sample"):
+        r = run_sample_gpu(args.workload, args.steps, args.warmup, event_every=max(1, args.event_every))
+        achieved = r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+        print(json.dumps({
+            "metric": "sampled draft tokens/sec at V=128256 (bf16); achieved HBM GB/s vs peak",
+            "value": round(r["rows"] / (r["ms_per_step"] * 1e-3), 1), "unit": "sampled draft tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": r["desc"], "rows": r["rows"], "vocab": r["V"], "logits": "bf16",
+                       "input_copies_rotated": r["ncopies"],
+                       "step_GBps": round(r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1),
+                       "step_frac_of_peak": round(r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+            "roofline": {"bound": "hbm", "kernel": "k_sample", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                         "bytes_per_launch": r["bytes"], "avg_launch_us": round(r["kernel_ms"] * 1e3, 3),
+                         "timed_launches": r["sampled"]},
+            "cpu_baseline": None if args.no_cpu else cpu_baseline_sample(args.workload),
+        }), flush=True)
+        return
     r = run_gpu(args.workload, args.steps, args.warmup, event_every=max(1, args.event_every))
     w = r["w"]
     value = r["positions"] / (r["ms_per_step"] * 1e-3)

@@ -83,6 +83,8 @@ def _load() -> ctypes.CDLL:
     lib.spec_verify_version.argtypes = []
     lib.spec_verify_single_dispatch.restype = ctypes.c_int
     lib.spec_verify_single_dispatch.argtypes = [ctypes.POINTER(sv_config), i32, i32]
+    lib.spec_sample_rows.restype = ctypes.c_int
+    lib.spec_sample_rows.argtypes = [P, P, P, P, ctypes.POINTER(sv_config)]
     return lib
 
 
@@ -108,6 +110,12 @@ def spec_verify(target_logits: int, draft_logits: int, draft_tokens: int, gamma_
                                 gamma_per_req or None, temperature or None, u_accept or None, u_resample or None,
                                 int(mode), float(delta), tree_parents or None, out_tokens or None,
                                 out_num_accepted or None, out_nkl or None, ctypes.byref(cfg)))
+
+
+def spec_sample_rows(logits: int, temperature: int, u: int, out_tokens: int, cfg: sv_config) -> int:
+    """Raw binding of spec_sample_rows (device pointers as ints)."""
+    return int(_lib.spec_sample_rows(logits or None, temperature or None, u or None, out_tokens or None,
+                                     ctypes.byref(cfg)))
 
 
 def spec_verify_single_dispatch(cfg: sv_config, mode: int, with_nkl: bool = False) -> int:
@@ -259,3 +267,38 @@ def verify(target_logits, draft_logits, draft_tokens, gamma_per_req, temperature
         raise SpecVerifyError(st)
     return VerifyOutput(out_tokens[: R_d + B], out_num, None if nkl is None else nkl[:R_d],
                         None if p_x is None else p_x[:R_d], None if q_x is None else q_x[:R_d], resid, tnode)
+
+
+def sample_rows(logits, temperature, u, *, workspace=None, stream=None, phase_events: int = 0):
+    """Draws one token per row of ``logits`` [rows, V] (torch.bfloat16 or
+    torch.float32 on the GPU) from softmax(row / temperature[row]) with the
+    uniform ``u[row]`` (see spec_sample_rows in specverify.h).  Returns an int32
+    tensor [rows]; -1 marks a row with an invalid temperature or uniform."""
+    import torch
+    dev = logits.device
+    if dev.type != "cuda":
+        raise ValueError("logits must be a GPU tensor")
+    if logits.dtype == torch.bfloat16:
+        dt = SV_DTYPE_BF16
+    elif logits.dtype == torch.float32:
+        dt = SV_DTYPE_F32
+    else:
+        raise TypeError("logits must be bfloat16 or float32")
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [rows, V] tensor")
+    rows, V = int(logits.shape[0]), int(logits.shape[1])
+    _check(temperature, "temperature", torch.float32, rows, dev)
+    _check(u, "u", torch.float32, rows, dev)
+    out = torch.empty(rows, dtype=torch.int32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    cfg = make_config(rows, V, dt, 0, 0, stream=int(stream.cuda_stream), phase_events=phase_events)
+    if workspace is None:
+        workspace = workspace_for(cfg, dev)
+    elif workspace.numel() < spec_verify_workspace_size(cfg):
+        raise ValueError("workspace too small")
+    cfg.workspace, cfg.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    st = spec_sample_rows(_ptr(logits), _ptr(temperature), _ptr(u), _ptr(out), cfg)
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return out

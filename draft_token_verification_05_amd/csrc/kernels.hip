@@ -1906,6 +1906,39 @@ __global__ __launch_bounds__(kThreads) void k_decide(Params p) {
   decide_request<DT, VEC, MODE, false, POS>(p, b, h, hdr == 0, d0, d1, T, ur, sh, tr, nullptr);
 }
 
+// Draft-side sampling: row b's token is the inverse-CDF draw from
+// softmax(x_b / T_b) with the uniform u_b, by the same records and selection as
+// the bonus draw of the verify step.  Workgroup (row b, helper h) streams its
+// slices of the row; the last helper of the row to arrive selects the token.
+// A row with a bad temperature or uniform gets -1 (every helper of the row
+// sees the same inputs, so none of them arrives).
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_sample(Params p) {
+  __shared__ DecideShared sh;
+  const int b = (int)(blockIdx.x % (unsigned)p.B), h = (int)(blockIdx.x / (unsigned)p.B);
+  const float T = p.temp[b], u = p.ur[b];
+  if (!temp_ok(T) || !unit_ok(u)) {
+    if (h == 0 && threadIdx.x == 0) p.out_tokens[b] = -1;
+    return;
+  }
+  Term tm;
+  tm.kind = kTermBonus;
+  tm.trow = b;
+  tm.drow = -1;
+  tm.m_t = tm.m_d = tm.k0 = 0.0f;
+  tm.Lhi = (float)(kLog2eD / (double)T);
+  const int NS = p.nslices, s0 = h * p.slices_per_helper, s1 = min(NS, s0 + p.slices_per_helper);
+  PartC* rec = p.part_c + (int64_t)b * NS * kWaves + (threadIdx.x >> 6);
+  slice_stream<DT, VEC, false>(p, tm.trow, tm.drow, s0, s1, [&](const uint4* qt, const uint4* qd, int sl) {
+    draw_record<DT, false>(qt, qd, tm, rec + sl * kWaves);
+  });
+  if (arrive_last(p.cnt + (int64_t)b * kCntStride, p.helpers, sh)) {
+    const int NW = NS * kWaves;
+    if (NW <= kSelCache) draw_select<DT, VEC, true>(p, b, tm, NW, u, sh);
+    else draw_select<DT, VEC, false>(p, b, tm, NW, u, sh);
+  }
+}
+
 // The whole stochastic step in one dispatch (batches up to kLdsBatch, no KL
 // output).  Every workgroup first streams its share of the statistics pass
 // (stats_phase: partials tagged with the call's epoch, tasks marked done);
@@ -2205,6 +2238,49 @@ int launch_stats(const Params& p, bool vec, void* stream, void* ev_start, void* 
   } else {
     if (vec) stats_dispatch<SV_DTYPE_F32, true>(p, s, e0, e1);
     else stats_dispatch<SV_DTYPE_F32, false>(p, s, e0, e1);
+  }
+  return (int)hipGetLastError();
+}
+
+template <int DT, bool VEC>
+int sample_capacity() {
+  static int occ = 0;  // same value from every thread: a race is benign
+  if (occ == 0) {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, k_sample<DT, VEC>, kThreads, 0) != hipSuccess || o <= 0)
+      o = 1;
+    occ = o;
+  }
+  return occ * num_cus();
+}
+
+int plan_sample(Params& p, bool vec) {
+  p.nslices = (int32_t)((p.V + chunk_t(p.dtype) - 1) / chunk_t(p.dtype));
+  int cap;
+  if (p.dtype == SV_DTYPE_BF16)
+    cap = vec ? sample_capacity<SV_DTYPE_BF16, true>() : sample_capacity<SV_DTYPE_BF16, false>();
+  else
+    cap = vec ? sample_capacity<SV_DTYPE_F32, true>() : sample_capacity<SV_DTYPE_F32, false>();
+  // enough helpers to fill the device once, at most one per slice
+  int64_t H = ((int64_t)cap + p.B - 1) / p.B;
+  if (H > p.nslices) H = p.nslices;
+  if (H < 1) H = 1;
+  const int64_t spp = (p.nslices + H - 1) / H;
+  p.slices_per_helper = (int32_t)spp;
+  p.helpers = (int32_t)((p.nslices + spp - 1) / spp);
+  return 0;
+}
+
+int launch_sample(const Params& p, bool vec, void* stream, void* ev_start, void* ev_stop) {
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t e0 = (hipEvent_t)ev_start, e1 = (hipEvent_t)ev_stop;
+  const dim3 grid((unsigned)((int64_t)p.B * p.helpers));
+  if (p.dtype == SV_DTYPE_BF16) {
+    if (vec) launch_timed(k_sample<SV_DTYPE_BF16, true>, grid, p, s, e0, e1);
+    else launch_timed(k_sample<SV_DTYPE_BF16, false>, grid, p, s, e0, e1);
+  } else {
+    if (vec) launch_timed(k_sample<SV_DTYPE_F32, true>, grid, p, s, e0, e1);
+    else launch_timed(k_sample<SV_DTYPE_F32, false>, grid, p, s, e0, e1);
   }
   return (int)hipGetLastError();
 }

@@ -185,6 +185,10 @@ int launch_refine(const Params& p, bool vec, void* stream);
 // grid, or 0 when the step should take the separate kernels; launch_fused
 // enqueues it.
 int plan_fused(Params& p, bool vec);
+// Draft-side row sampling (rows = p.B): plan_sample fills p.nslices, p.helpers
+// and p.slices_per_helper; launch_sample enqueues k_sample.
+int plan_sample(Params& p, bool vec);
+int launch_sample(const Params& p, bool vec, void* stream, void* ev_start, void* ev_stop);
 int launch_fused(const Params& p, bool vec, int grid, void* stream, void* ev_start, void* ev_stop);
 
 }  // namespace sv

@@ -175,6 +175,29 @@ int spec_verify_version(void);
  * else the row-statistics dispatch. */
 int spec_verify_single_dispatch(const sv_config* cfg, int32_t mode, int32_t with_nkl);
 
+/*
+ * Draft-side sampling, the drafter's step before verification: one token per row, drawn from
+ * softmax(logits_r / temperature[r]) by the inverse CDF with the uniform u[r],
+ *     y_r = min{ y : C_y > u_r * S }   (C_y: cumulative mass in ascending token order, S: total),
+ * the same rule as the verify step's bonus draw (draft tokens "drawn from the draft softmax";
+ * the "投机采样" page's draft loop draws x_i ~ q_i).
+ *
+ * logits       [cfg->batch][cfg->vocab] of cfg->dtype, device, row-major (cfg->batch = rows).
+ * temperature  float32 [rows], > 0 and finite.
+ * u            float32 [rows] in [0, 1).
+ * out_tokens   int32 [rows]: the drawn token, or -1 for a row whose temperature or uniform is
+ *              invalid (a data error, found on the device; other rows are not affected).
+ * cfg          batch, vocab, dtype, stream, workspace (>= spec_verify_workspace_size(cfg), any
+ *              max_gamma and total_draft_rows; zero-filled before its first use, reusable by later
+ *              calls on the same stream) and phase_events ([1] and [2] bracket the sampling
+ *              dispatch).  The other fields are not read.
+ * Synchronous errors: SV_EINVAL (NULL or misaligned pointer, B <= 0, V <= 0, bad dtype or
+ * struct_size), SV_EUNSUPPORTED (grid above 2^31 - 1), SV_EWORKSPACE, SV_EHIP.
+ * Asynchronous on cfg->stream, like spec_verify.
+ */
+int spec_sample_rows(const void* logits, const float* temperature, const float* u, int32_t* out_tokens,
+                     const sv_config* cfg);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,12 +21,12 @@ def sv():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(spec_verify\w*)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(spec_\w*)\s*\(", text, flags=re.M)))
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["spec_verify", "spec_verify_single_dispatch", "spec_verify_status_string",
-                                    "spec_verify_version", "spec_verify_workspace_size"]
+    assert declared_functions() == ["spec_sample_rows", "spec_verify", "spec_verify_single_dispatch",
+                                    "spec_verify_status_string", "spec_verify_version", "spec_verify_workspace_size"]
 
 
 def test_single_dispatch_query_host_side(sv):
@@ -158,3 +158,25 @@ def test_mode_specific_null_pointers_allowed(sv):
     assert call(sv, mode=0, parents=0, out_nkl=0, ws_bytes=16) == W
     # no drafted rows at all: token / draft / u_accept arrays may be NULL
     assert call(sv, mode=0, R_d=0, tokens=0, draft=0, ua=0, ws_bytes=16) == W
+
+
+def test_sample_rows_argument_errors(sv):
+    """spec_sample_rows: host-side checks (nothing is enqueued); validation
+    reaches the too-small workspace when everything else is right."""
+    E, W = sv.SV_EINVAL, sv.SV_EWORKSPACE
+
+    def sample(logits=FAKE, T=FAKE, u=FAKE, out=FAKE, B=4, V=1000, dtype=1, ws=FAKE, ws_bytes=16, size_delta=0):
+        cfg = sv.make_config(B, V, dtype, 0, 0, 0, ws, ws_bytes)
+        cfg.struct_size += size_delta
+        return sv.spec_sample_rows(logits, T, u, out, cfg)
+
+    assert sample() == W
+    for kw in ({"logits": 0}, {"T": 0}, {"u": 0}, {"out": 0}, {"B": 0}, {"V": 0}, {"dtype": 3},
+               {"logits": FAKE + 1}, {"dtype": 0, "logits": FAKE + 2}, {"T": FAKE + 2}, {"u": FAKE + 1},
+               {"out": FAKE + 2}, {"size_delta": 8}):
+        assert sample(**kw) == E, kw
+    assert sample(ws=0) == W
+    assert sample(ws=FAKE + 64, ws_bytes=1 << 30) == W
+    # the verify workspace size covers sampling, whatever max_gamma and total_draft_rows say
+    need = sv.spec_verify_workspace_size(sv.make_config(4, 1000, 1, 0, 0))
+    assert need > 0 and sv.spec_verify_workspace_size(sv.make_config(4, 1000, 1, 5, 20)) >= need
