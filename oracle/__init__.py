@@ -45,6 +45,8 @@ def _load():
                                          P, P, P, P, P, P, P, P, P, P, P, i32]
         lib.sv_oracle_sample_rows.restype = ctypes.c_int
         lib.sv_oracle_sample_rows.argtypes = [P, i32, i64, i32, P, P, P, P, i32]
+        lib.sv_oracle_topk_rows.restype = ctypes.c_int
+        lib.sv_oracle_topk_rows.argtypes = [P, i32, i64, i32, i32, P, i32]
         lib.sv_oracle_nkl_threshold.restype = ctypes.c_double
         lib.sv_oracle_nkl_threshold.argtypes = [f32, f32, f32, i32]
         lib.sv_oracle_max_threads.restype = ctypes.c_int
@@ -75,6 +77,22 @@ def sample_rows(logits: np.ndarray, dtype: str, temperature: np.ndarray, u: np.n
     if rc != 0:
         raise ValueError("sv_oracle_sample_rows rejected its arguments")
     return out[:rows], margin[:rows]
+
+
+def topk_rows(logits: np.ndarray, dtype: str, k: int, nthreads: int = 0) -> np.ndarray:
+    """The k largest logits of every row: int32 [rows, k] indices, largest
+    first, the lower index first among equal logits."""
+    rows, V = int(logits.shape[0]), int(logits.shape[1])
+    if dtype == "bf16":
+        logits, dt = np.ascontiguousarray(logits, np.uint16), 1
+    elif dtype == "f32":
+        logits, dt = np.ascontiguousarray(logits, np.float32), 0
+    else:
+        raise ValueError(dtype)
+    out = np.full((max(rows, 1), k), -7, np.int32)
+    if _load().sv_oracle_topk_rows(_ptr(logits), dt, rows, V, int(k), _ptr(out), int(nthreads)) != 0:
+        raise ValueError("sv_oracle_topk_rows rejected its arguments")
+    return out[:rows]
 
 
 def nkl_threshold(delta: float, alpha: float, delta_max: float, position: int) -> float:

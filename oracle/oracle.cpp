@@ -49,6 +49,7 @@
 // whose uniform lies within 1e-5 of a CDF step.  In NKL mode a decision with
 // |nkl_i - delta_i| < 1e-6*delta_i is flagged.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -450,6 +451,31 @@ int sv_oracle_sample_rows(const void* logits, int32_t dtype, int64_t rows, int32
     double margin = 0.0;
     out_tokens[r] = inverse_cdf(p, s.value(), (double)u[r], &margin);
     if (out_margin) out_margin[r] = margin;
+  }
+  return 0;
+}
+
+// Top-k of each row (the children of a tree draft node are the top-k tokens of
+// its draft row: "Parallel Drafting" page, section 2.2 tree draft): the k
+// indices with the largest logits, largest first, the lower index first among
+// equal logits.  Returns -1 on an argument error (k outside [1, V]).
+int sv_oracle_topk_rows(const void* logits, int32_t dtype, int64_t rows, int32_t vocab, int32_t k,
+                        int32_t* out_idx, int32_t nthreads) {
+  if (rows < 0 || vocab <= 0 || (dtype != 0 && dtype != 1) || k < 1 || k > vocab) return -1;
+  if (rows > 0 && (!logits || !out_idx)) return -1;
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+  for (int64_t r = 0; r < rows; ++r) {
+    std::vector<double> x;
+    load_row(logits, dtype, r, vocab, x);
+    std::vector<int32_t> idx((size_t)vocab);
+    for (int32_t y = 0; y < vocab; ++y) idx[(size_t)y] = y;
+    std::partial_sort(idx.begin(), idx.begin() + k, idx.end(), [&](int32_t a, int32_t b) {
+      return x[(size_t)a] > x[(size_t)b] || (x[(size_t)a] == x[(size_t)b] && a < b);
+    });
+    for (int32_t i = 0; i < k; ++i) out_idx[r * k + i] = idx[(size_t)i];
   }
   return 0;
 }

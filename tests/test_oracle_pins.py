@@ -13,6 +13,7 @@ import pytest
 from scipy import special, stats
 
 import oracle
+import synthetic
 from synthetic import f32_to_bf16_bits, bf16_bits_to_f32
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
@@ -377,6 +378,35 @@ def test_sample_rows_invalid_inputs():
     u = np.array([0.5, 0.5, 0.5, 1.0, -0.1], np.float32)
     tok, _ = oracle.sample_rows(x, "f32", T, u)
     assert tok.tolist() == [8, -1, -1, -1, -1]  # uniform 16-token row: u = 0.5 lands on token 8
+
+
+def test_topk_rows_hand_cases():
+    """Hand-checked rows: distinct values, ties (the lower index first), a
+    tie straddling the k-th place, and k = V."""
+    x = np.array([[0.5, 3.0, -1.0, 3.0, 2.0, 0.5],
+                  [1.0, 1.0, 1.0, 1.0, 1.0, 1.0],
+                  [-2.0, -1.0, -3.0, -1.0, -0.5, -4.0]], np.float32)
+    assert oracle.topk_rows(x, "f32", 3).tolist() == [[1, 3, 4], [0, 1, 2], [4, 1, 3]]
+    assert oracle.topk_rows(x, "f32", 6).tolist() == [[1, 3, 4, 0, 5, 2], [0, 1, 2, 3, 4, 5],
+                                                       [4, 1, 3, 0, 2, 5]]
+
+
+def test_topk_rows_first_is_the_pinned_argmax():
+    """k = 1 is the greedy argmax (pinned by the greedy golden cases); every
+    chosen logit is at least every other logit of its row."""
+    w = synthetic.random_workload(seed=3, mode=G, B=9, V=5000, dtype="bf16", gmax=3, gmin=0, ties=True)
+    top = oracle.topk_rows(w.target, "bf16", 5)
+    r = oracle.verify_workload(w.with_mode(G))
+    t_off = w.t_off
+    xf = bf16_bits_to_f32(w.target)
+    for b in range(w.batch):
+        n = r.num_accepted[b]
+        assert top[t_off[b] + n, 0] == r.tokens[t_off[b] + n]  # the terminal token is the row argmax
+    for row in range(xf.shape[0]):
+        chosen = xf[row, top[row]]
+        assert (np.diff(chosen) <= 0).all()
+        rest = np.delete(xf[row], top[row])
+        assert chosen.min() >= rest.max()
 
 
 # --------------------------------------------------------------------------
