@@ -50,6 +50,8 @@ WORKLOADS = {
     # draft-side sampling (the step before verify): one token per draft row of the llama3 batch
     "sample_llama3": ({}, -1, "draft-side sampling of the llama3-shaped batch's draft rows: 160 rows, V=128256, "
                               "bf16, per-request temperatures"),
+    "topk_llama3": ({}, -1, "top-3 of each of the llama3-shaped batch's draft rows (tree-draft children): 160 rows, "
+                            "V=128256, bf16"),
 }
 
 
@@ -149,7 +151,8 @@ def sample_inputs(name):
 
 
 def run_sample_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
-    """Times spec_sample_rows on device-resident rows (rotated copies, like run_gpu)."""
+    """Times spec_sample_rows (or spec_topk_rows, k = 3, for topk_* workloads) on
+    device-resident rows (rotated copies, like run_gpu)."""
     import numpy as np
     import torch
 
@@ -164,9 +167,15 @@ def run_sample_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
     copies = [base] + [base.clone() for _ in range(ncopies - 1)]
     T = torch.from_numpy(T_np).to(dev)
     u = torch.from_numpy(u_np).to(dev)
-    out = torch.empty(rows, dtype=torch.int32, device=dev)
+    topk = 3 if name.startswith("topk") else 0
+    out = torch.empty(rows * max(1, topk), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
     cfg0 = sv.make_config(rows, V, sv.SV_DTYPE_BF16, 0, 0)
+
+    def call(k, cfg):
+        if topk:
+            return sv.spec_topk_rows(copies[k % ncopies].data_ptr(), topk, out.data_ptr(), cfg)
+        return sv.spec_sample_rows(copies[k % ncopies].data_ptr(), T.data_ptr(), u.data_ptr(), out.data_ptr(), cfg)
     ws = torch.zeros(sv.spec_verify_workspace_size(cfg0), dtype=torch.uint8, device=dev)
     hip = Hip()
     sampled = list(range(0, steps, max(1, event_every)))
@@ -182,14 +191,13 @@ def run_sample_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
     plain = cfg_for(-1)
     timed = [cfg_for(k) for k in range(steps)]
     for k in range(warmup):
-        st = sv.spec_sample_rows(copies[k % ncopies].data_ptr(), T.data_ptr(), u.data_ptr(), out.data_ptr(), plain)
+        st = call(k, plain)
         if st != 0:
             raise RuntimeError(sv.spec_verify_status_string(st))
     torch.cuda.synchronize()
     hip.lib.hipEventRecord(ctypes.c_void_p(ev_all[0]), ctypes.c_void_p(stream.cuda_stream))
     for k in range(steps):
-        st = sv.spec_sample_rows(copies[k % ncopies].data_ptr(), T.data_ptr(), u.data_ptr(), out.data_ptr(),
-                                 timed[k])
+        st = call(k, timed[k])
         if st != 0:
             raise RuntimeError(sv.spec_verify_status_string(st))
     hip.lib.hipEventRecord(ctypes.c_void_p(ev_all[1]), ctypes.c_void_p(stream.cuda_stream))
@@ -198,10 +206,10 @@ def run_sample_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
     ks = np.array([hip.elapsed_ms(ev[4 * n + 1], ev[4 * n + 2]) for n in range(len(sampled))])
     hip.destroy(ev)
     hip.destroy(ev_all)
-    # one read of every row, plus the selection's re-read of one wave-chunk (2048 tokens) per row
-    nbytes = rows * V * 2 + rows * min(V, 2048) * 2
+    # one read of every row (sampling: plus the selection's re-read of one wave-chunk, 2048 tokens)
+    nbytes = rows * V * 2 + (0 if topk else rows * min(V, 2048) * 2)
     return dict(desc=desc, rows=rows, V=V, ncopies=ncopies, ms_per_step=total_ms / steps, kernel_ms=float(ks.mean()),
-                bytes=nbytes, sampled=len(sampled))
+                bytes=nbytes, sampled=len(sampled), topk=topk)
 
 
 def run_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
@@ -283,19 +291,22 @@ def run_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
                 kernel="k_fused" if single else "k_stats", kernel_bytes=step_bytes if single else rowstats_bytes)
 
 
-def cpu_baseline_sample(name, budget_s=8.0):
+def cpu_baseline_sample(name, budget_s=8.0, topk=0):
     import oracle
     _, rows, T, u = sample_inputs(name)
     threads = oracle.max_threads()
-    oracle.sample_rows(rows, "bf16", T, u, nthreads=threads)  # warm (page-in)
+    run = (lambda: oracle.topk_rows(rows, "bf16", topk, nthreads=threads)) if topk else \
+        (lambda: oracle.sample_rows(rows, "bf16", T, u, nthreads=threads))
+    run()  # warm (page-in)
     reps, t0 = 0, time.perf_counter()
     while True:
-        oracle.sample_rows(rows, "bf16", T, u, nthreads=threads)
+        run()
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    return {"value": rows.shape[0] * reps / el, "unit": "sampled draft tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": rows.shape[0] * reps / el, "unit": ("top-3 draft rows/s" if topk else "sampled draft tokens/s"),
+            "cores": threads, "kind": "oracle",
             "sample": f"{reps} full passes over the {rows.shape[0]} rows, {el:.1f} s wall on {threads} host threads"}
 
 
@@ -342,23 +353,25 @@ def main():
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(requests are independent, so more GPUs would each run their own share).", file=sys.stderr)
         sys.exit(2)
-    if args.workload.startswith("sample"):
+    if args.workload.startswith(("sample", "topk")):
         r = run_sample_gpu(args.workload, args.steps, args.warmup, event_every=max(1, args.event_every))
         achieved = r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+        what = "top-3 draft rows" if r["topk"] else "sampled draft tokens"
         print(json.dumps({
-            "metric": "sampled draft tokens/sec at V=128256 (bf16); achieved HBM GB/s vs peak",
-            "value": round(r["rows"] / (r["ms_per_step"] * 1e-3), 1), "unit": "sampled draft tokens/s",
+            "metric": f"{what}/sec at V=128256 (bf16); achieved HBM GB/s vs peak",
+            "value": round(r["rows"] / (r["ms_per_step"] * 1e-3), 1), "unit": f"{what}/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": {"workload": r["desc"], "rows": r["rows"], "vocab": r["V"], "logits": "bf16",
                        "input_copies_rotated": r["ncopies"],
                        "step_GBps": round(r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1),
                        "step_frac_of_peak": round(r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-            "roofline": {"bound": "hbm", "kernel": "k_sample", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+            "roofline": {"bound": "hbm", "kernel": "k_topk" if r["topk"] else "k_sample", "achieved": round(achieved, 1),
+                         "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                          "bytes_per_launch": r["bytes"], "avg_launch_us": round(r["kernel_ms"] * 1e3, 3),
                          "timed_launches": r["sampled"]},
-            "cpu_baseline": None if args.no_cpu else cpu_baseline_sample(args.workload),
+            "cpu_baseline": None if args.no_cpu else cpu_baseline_sample(args.workload, topk=r["topk"]),
         }), flush=True)
         return
     r = run_gpu(args.workload, args.steps, args.warmup, event_every=max(1, args.event_every))

@@ -83,6 +83,8 @@ def _load() -> ctypes.CDLL:
     lib.spec_verify_version.argtypes = []
     lib.spec_verify_single_dispatch.restype = ctypes.c_int
     lib.spec_verify_single_dispatch.argtypes = [ctypes.POINTER(sv_config), i32, i32]
+    lib.spec_topk_rows.restype = ctypes.c_int
+    lib.spec_topk_rows.argtypes = [P, i32, P, ctypes.POINTER(sv_config)]
     lib.spec_sample_rows.restype = ctypes.c_int
     lib.spec_sample_rows.argtypes = [P, P, P, P, ctypes.POINTER(sv_config)]
     return lib
@@ -116,6 +118,11 @@ def spec_sample_rows(logits: int, temperature: int, u: int, out_tokens: int, cfg
     """Raw binding of spec_sample_rows (device pointers as ints)."""
     return int(_lib.spec_sample_rows(logits or None, temperature or None, u or None, out_tokens or None,
                                      ctypes.byref(cfg)))
+
+
+def spec_topk_rows(logits: int, k: int, out_idx: int, cfg: sv_config) -> int:
+    """Raw binding of spec_topk_rows (device pointers as ints)."""
+    return int(_lib.spec_topk_rows(logits or None, int(k), out_idx or None, ctypes.byref(cfg)))
 
 
 def spec_verify_single_dispatch(cfg: sv_config, mode: int, with_nkl: bool = False) -> int:
@@ -299,6 +306,35 @@ def sample_rows(logits, temperature, u, *, workspace=None, stream=None, phase_ev
         raise ValueError("workspace too small")
     cfg.workspace, cfg.workspace_bytes = workspace.data_ptr(), workspace.numel()
     st = spec_sample_rows(_ptr(logits), _ptr(temperature), _ptr(u), _ptr(out), cfg)
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return out
+
+
+def topk_rows(logits, k: int, *, workspace=None, stream=None, phase_events: int = 0):
+    """The k largest logits of every row of ``logits`` [rows, V] (GPU,
+    bfloat16 or float32): int32 [rows, k] indices, largest first, the lower
+    index first among equal logits (see spec_topk_rows in specverify.h)."""
+    import torch
+    dev = logits.device
+    if dev.type != "cuda":
+        raise ValueError("logits must be a GPU tensor")
+    dt = {torch.bfloat16: SV_DTYPE_BF16, torch.float32: SV_DTYPE_F32}.get(logits.dtype)
+    if dt is None:
+        raise TypeError("logits must be bfloat16 or float32")
+    if logits.dim() != 2 or not logits.is_contiguous():
+        raise ValueError("logits must be a contiguous [rows, V] tensor")
+    rows, V = int(logits.shape[0]), int(logits.shape[1])
+    out = torch.empty((rows, int(k)), dtype=torch.int32, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    cfg = make_config(rows, V, dt, 0, 0, stream=int(stream.cuda_stream), phase_events=phase_events)
+    if workspace is None:
+        workspace = workspace_for(cfg, dev)
+    elif workspace.numel() < spec_verify_workspace_size(cfg):
+        raise ValueError("workspace too small")
+    cfg.workspace, cfg.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    st = spec_topk_rows(_ptr(logits), int(k), _ptr(out), cfg)
     if st != SV_OK:
         raise SpecVerifyError(st)
     return out

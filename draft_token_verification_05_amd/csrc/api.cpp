@@ -263,4 +263,39 @@ int spec_sample_rows(const void* logits, const float* temperature, const float* 
   return SV_OK;
 }
 
+int spec_topk_rows(const void* logits, int32_t k, int32_t* out_idx, const sv_config* cfg) {
+  if (!cfg || cfg->struct_size != sizeof(sv_config) || cfg->wait_polls < 0) return SV_EINVAL;
+  if (cfg->batch <= 0 || cfg->vocab <= 0) return SV_EINVAL;
+  if (cfg->dtype != SV_DTYPE_F32 && cfg->dtype != SV_DTYPE_BF16) return SV_EINVAL;
+  if (k < 1 || k > sv::kTopkMax || k > cfg->vocab) return SV_EINVAL;
+  if (!logits || !out_idx) return SV_EINVAL;
+  const size_t es = (size_t)sv::elem_size(cfg->dtype);
+  if (!aligned(logits, es) || !aligned(out_idx, 4)) return SV_EINVAL;
+  const int64_t nch_t = (cfg->vocab + sv::chunk_t(cfg->dtype) - 1) / sv::chunk_t(cfg->dtype);
+  if ((int64_t)cfg->batch * nch_t > INT32_MAX || (int64_t)cfg->batch * k > INT32_MAX) return SV_EUNSUPPORTED;
+  const sv::Layout L = sv::make_layout(cfg->batch, cfg->vocab, cfg->dtype, 0);
+  if (!cfg->workspace || cfg->workspace_bytes < L.total || !aligned(cfg->workspace, 256)) return SV_EWORKSPACE;
+
+  uint8_t* ws = static_cast<uint8_t*>(cfg->workspace);
+  sv::Params p{};
+  p.target = logits;
+  p.out_tokens = out_idx;
+  p.B = cfg->batch;
+  p.V = cfg->vocab;
+  p.dtype = cfg->dtype;
+  p.topk = k;
+  p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
+  p.topk_cand = reinterpret_cast<uint64_t*>(ws + L.off_topk);
+  const bool vec = ((size_t)cfg->vocab * es) % 16 == 0 && aligned(logits, 16);
+  sv::plan_topk(p, vec);
+  hipStream_t s = static_cast<hipStream_t>(cfg->stream);
+  hipEvent_t* ev = static_cast<hipEvent_t*>(cfg->phase_events);
+  hipError_t e;
+  if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e);
+  if ((e = (hipError_t)sv::launch_topk(p, vec, s, ev ? ev[1] : nullptr, ev ? ev[2] : nullptr)) != hipSuccess)
+    return hip_fail(e);
+  if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e);
+  return SV_OK;
+}
+
 }  // extern "C"

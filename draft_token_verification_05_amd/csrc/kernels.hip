@@ -1939,6 +1939,108 @@ __global__ __launch_bounds__(kThreads) void k_sample(Params p) {
   }
 }
 
+// ----------------------------------------------------------------------------
+// top-k of each row (the children of a tree-draft node)
+// ----------------------------------------------------------------------------
+
+// Ordering key of logit x at index y: a larger x first, the lower index first
+// among equal x (-0 and +0 are equal).  0 is below every key: "no candidate".
+__device__ __forceinline__ uint64_t topk_key(float x, int y) {
+  uint32_t b = __float_as_uint(x);
+  if (b == 0x80000000u) b = 0u;
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);  // order-preserving map to unsigned
+  return ((uint64_t)b << 32) | (uint32_t)(0x7FFFFFFF - y);
+}
+__device__ __forceinline__ int topk_index(uint64_t key) { return 0x7FFFFFFF - (int)(uint32_t)key; }
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const uint64_t o = __shfl_xor(v, m);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+// Keeps the K largest keys seen by this thread, sorted, largest first.
+template <int K>
+__device__ __forceinline__ void topk_insert(uint64_t (&lst)[K], uint64_t key) {
+  if (key <= lst[K - 1]) return;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const uint64_t hi = lst[i] > key ? lst[i] : key, lo = lst[i] > key ? key : lst[i];
+    lst[i] = hi;
+    key = lo;
+  }
+}
+
+// The k largest of the keys the threads hold (each thread's list sorted,
+// largest first): k rounds of a workgroup maximum over the list heads; the
+// holder of the maximum drops its head.  Thread 0 gets them in out[0..k).
+template <int K>
+__device__ __forceinline__ void topk_merge(uint64_t (&lst)[K], int k, uint64_t* out, uint64_t* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int r = 0; r < k; ++r) {
+    const uint64_t m = wave_max_u64(lst[0]);
+    if (lane == 0) red[w] = m;
+    __syncthreads();
+    uint64_t best = red[0];
+#pragma unroll
+    for (int j = 1; j < kWaves; ++j) best = red[j] > best ? red[j] : best;
+    if (lst[0] == best && best != 0) {  // keys are unique: one holder
+#pragma unroll
+      for (int i = 0; i + 1 < K; ++i) lst[i] = lst[i + 1];
+      lst[K - 1] = 0;
+    }
+    if (threadIdx.x == 0) out[r] = best;
+    __syncthreads();
+  }
+}
+
+// Top-k of row b: helper h streams its slices of the row, keeping each
+// thread's K best keys (K: k rounded up to a power of two), merges them over
+// the workgroup and stores its k best; the last helper of the row to arrive
+// merges the helpers' candidates and writes the k indices.
+struct TopkShared {
+  uint64_t best[kTopkMax], red[kWaves];
+  int flag;
+};
+
+template <int DT, bool VEC, int K>
+__global__ __launch_bounds__(kThreads) void k_topk(Params p) {
+  __shared__ TopkShared sh;
+  constexpr int P = Elem<DT>::P;
+  const int b = (int)(blockIdx.x % (unsigned)p.B), h = (int)(blockIdx.x / (unsigned)p.B);
+  const int k = p.topk, H = p.helpers, NS = p.nslices;
+  const int s0 = h * p.slices_per_helper, s1 = min(NS, s0 + p.slices_per_helper);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint64_t lst[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) lst[i] = 0;
+  slice_stream<DT, VEC, false>(p, b, -1, s0, s1, [&](const uint4* qt, const uint4*, int sl) {
+    const int64_t e_base = (int64_t)sl * kThreads * kUT * P;
+#pragma unroll
+    for (int j = 0; j < kUT; ++j) {
+      float v[P];
+      unpack<DT>(qt[j], v);
+      const int64_t y0 = e_base + ((int64_t)(w * kUT + j) * 64 + lane) * P;
+#pragma unroll
+      for (int e = 0; e < P; ++e)
+        if (y0 + e < p.V) topk_insert<K>(lst, topk_key(v[e], (int)(y0 + e)));
+    }
+  });
+  topk_merge<K>(lst, k, sh.best, sh.red);
+  // row b's candidates: kThreads slots, helper h's k of them at h * k (H * k <= kThreads)
+  uint64_t* cand = p.topk_cand + (int64_t)b * kThreads;
+  if (threadIdx.x < k) st_dev(&cand[h * k + threadIdx.x], sh.best[threadIdx.x]);
+  if (!arrive_last(p.cnt + (int64_t)b * kCntStride, H, sh)) return;
+  // the row's last helper: one candidate per thread, then the same merge
+  uint64_t c1[1] = {0};
+  if (threadIdx.x < H * k) c1[0] = ld_dev(&cand[threadIdx.x]);
+  topk_merge<1>(c1, k, sh.best, sh.red);
+  if (threadIdx.x < k) p.out_tokens[(int64_t)b * k + threadIdx.x] = topk_index(sh.best[threadIdx.x]);
+}
+
 // The whole stochastic step in one dispatch (batches up to kLdsBatch, no KL
 // output).  Every workgroup first streams its share of the statistics pass
 // (stats_phase: partials tagged with the call's epoch, tasks marked done);
@@ -2282,6 +2384,64 @@ int launch_sample(const Params& p, bool vec, void* stream, void* ev_start, void*
     if (vec) launch_timed(k_sample<SV_DTYPE_F32, true>, grid, p, s, e0, e1);
     else launch_timed(k_sample<SV_DTYPE_F32, false>, grid, p, s, e0, e1);
   }
+  return (int)hipGetLastError();
+}
+
+template <int DT, bool VEC, int K>
+int topk_capacity() {
+  static int occ = 0;  // same value from every thread: a race is benign
+  if (occ == 0) {
+    int o = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, k_topk<DT, VEC, K>, kThreads, 0) != hipSuccess || o <= 0)
+      o = 1;
+    occ = o;
+  }
+  return occ * num_cus();
+}
+
+// the per-thread list length: k rounded up to a power of two
+int topk_lanes(int k) { return k <= 1 ? 1 : k <= 2 ? 2 : k <= 4 ? 4 : k <= 8 ? 8 : 16; }
+
+template <int DT, bool VEC>
+void topk_dispatch(const Params& p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1, int* cap) {
+  switch (topk_lanes(p.topk)) {
+    case 1: if (cap) *cap = topk_capacity<DT, VEC, 1>(); else launch_timed(k_topk<DT, VEC, 1>, grid, p, s, e0, e1); break;
+    case 2: if (cap) *cap = topk_capacity<DT, VEC, 2>(); else launch_timed(k_topk<DT, VEC, 2>, grid, p, s, e0, e1); break;
+    case 4: if (cap) *cap = topk_capacity<DT, VEC, 4>(); else launch_timed(k_topk<DT, VEC, 4>, grid, p, s, e0, e1); break;
+    case 8: if (cap) *cap = topk_capacity<DT, VEC, 8>(); else launch_timed(k_topk<DT, VEC, 8>, grid, p, s, e0, e1); break;
+    default: if (cap) *cap = topk_capacity<DT, VEC, 16>(); else launch_timed(k_topk<DT, VEC, 16>, grid, p, s, e0, e1); break;
+  }
+}
+
+void topk_any(const Params& p, bool vec, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1, int* cap) {
+  if (p.dtype == SV_DTYPE_BF16) {
+    if (vec) topk_dispatch<SV_DTYPE_BF16, true>(p, grid, s, e0, e1, cap);
+    else topk_dispatch<SV_DTYPE_BF16, false>(p, grid, s, e0, e1, cap);
+  } else {
+    if (vec) topk_dispatch<SV_DTYPE_F32, true>(p, grid, s, e0, e1, cap);
+    else topk_dispatch<SV_DTYPE_F32, false>(p, grid, s, e0, e1, cap);
+  }
+}
+
+int plan_topk(Params& p, bool vec) {
+  p.nslices = (int32_t)((p.V + chunk_t(p.dtype) - 1) / chunk_t(p.dtype));
+  int cap = 1;
+  topk_any(p, vec, dim3(1), nullptr, nullptr, nullptr, &cap);
+  // enough helpers to fill the device once, at most one per slice, and at
+  // most kThreads / k so that the last helper holds one candidate per thread
+  int64_t H = ((int64_t)cap + p.B - 1) / p.B;
+  if (H > p.nslices) H = p.nslices;
+  if (H > kThreads / p.topk) H = kThreads / p.topk;
+  if (H < 1) H = 1;
+  const int64_t spp = (p.nslices + H - 1) / H;
+  p.slices_per_helper = (int32_t)spp;
+  p.helpers = (int32_t)((p.nslices + spp - 1) / spp);
+  return 0;
+}
+
+int launch_topk(const Params& p, bool vec, void* stream, void* ev_start, void* ev_stop) {
+  topk_any(p, vec, dim3((unsigned)((int64_t)p.B * p.helpers)), (hipStream_t)stream, (hipEvent_t)ev_start,
+           (hipEvent_t)ev_stop, nullptr);
   return (int)hipGetLastError();
 }
 

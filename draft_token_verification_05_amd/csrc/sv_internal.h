@@ -25,6 +25,7 @@ constexpr int kFusedPerCu = 3;        // resident workgroups per compute unit of
 // per-request arrival counters sit 256 bytes apart: increments of different
 // requests' counters would otherwise queue behind each other on one line
 constexpr int kCntStride = 64;
+constexpr int kTopkMax = 16;  // largest k of the per-row top-k
 
 constexpr int elems_per_vec(int dtype) { return dtype == SV_DTYPE_BF16 ? 8 : 4; }
 constexpr int elem_size(int dtype) { return dtype == SV_DTYPE_BF16 ? 2 : 4; }
@@ -81,7 +82,7 @@ struct PartC {
 
 struct Layout {
   size_t off_hdr, off_doff, off_pair2req, off_row2req, off_part_a, off_cnt, off_cnt_kl, off_req_fin, off_part_c,
-      off_ref_list, off_kl_need, off_tidx, off_kl_part, total;
+      off_ref_list, off_kl_need, off_tidx, off_kl_part, off_topk, total;
   int64_t n_task_max;
   int64_t nch_a, nch_t;
 };
@@ -113,6 +114,7 @@ inline Layout make_layout(int64_t B, int64_t V, int dtype, int64_t R_d) {
   L.off_kl_need = take(sizeof(int32_t) * R1);
   L.off_tidx = take(sizeof(int32_t) * (R_d + B));
   L.off_kl_part = take(sizeof(double) * R1 * L.nch_t);
+  L.off_topk = take(sizeof(uint64_t) * B * kThreads);  // top-k candidates: kThreads per row
   L.total = o;
   return L;
 }
@@ -165,6 +167,8 @@ struct Params {
   int32_t* kl_need;   // [R_d] 1 where the KL of the position comes from the second pass
   int32_t* tidx;      // [R_d + B] argmax of every target row (NKL)
   double* kl_part;    // [R_d * nslices] second-pass KL sums per slice
+  uint64_t* topk_cand;  // [B * kThreads] top-k candidates: helper h of row b at b * kThreads + h * topk
+  int32_t topk;         // k of the per-row top-k
 };
 
 // kernel launchers (kernels.hip); return the hipError_t of the launch as int
@@ -189,6 +193,10 @@ int plan_fused(Params& p, bool vec);
 // and p.slices_per_helper; launch_sample enqueues k_sample.
 int plan_sample(Params& p, bool vec);
 int launch_sample(const Params& p, bool vec, void* stream, void* ev_start, void* ev_stop);
+// Per-row top-k (rows = p.B, k = p.topk): plan_topk fills p.nslices,
+// p.helpers and p.slices_per_helper; launch_topk enqueues k_topk.
+int plan_topk(Params& p, bool vec);
+int launch_topk(const Params& p, bool vec, void* stream, void* ev_start, void* ev_stop);
 int launch_fused(const Params& p, bool vec, int grid, void* stream, void* ev_start, void* ev_stop);
 
 }  // namespace sv

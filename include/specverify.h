@@ -198,6 +198,21 @@ int spec_verify_single_dispatch(const sv_config* cfg, int32_t mode, int32_t with
 int spec_sample_rows(const void* logits, const float* temperature, const float* u, int32_t* out_tokens,
                      const sv_config* cfg);
 
+/*
+ * Top-k of each row, for the children of a tree-draft node (the node's k children are the top-k
+ * tokens of its draft row: "Parallel Drafting" page, section 2.2 tree draft): the k indices with
+ * the largest logits, largest first, the lower index first among equal logits (-0 == +0).
+ *
+ * logits   [cfg->batch][cfg->vocab] of cfg->dtype, device, row-major (cfg->batch = rows);
+ *          finite values.
+ * k        1 <= k <= min(16, vocab).
+ * out_idx  int32 [rows][k].
+ * cfg      as for spec_sample_rows (batch, vocab, dtype, stream, workspace, phase_events).
+ * Synchronous errors: SV_EINVAL (NULL or misaligned pointer, B <= 0, V <= 0, bad dtype or
+ * struct_size, k out of range), SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP.
+ */
+int spec_topk_rows(const void* logits, int32_t k, int32_t* out_idx, const sv_config* cfg);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["spec_sample_rows", "spec_verify", "spec_verify_single_dispatch",
+    assert declared_functions() == ["spec_sample_rows", "spec_topk_rows", "spec_verify", "spec_verify_single_dispatch",
                                     "spec_verify_status_string", "spec_verify_version", "spec_verify_workspace_size"]
 
 
@@ -180,3 +180,17 @@ def test_sample_rows_argument_errors(sv):
     # the verify workspace size covers sampling, whatever max_gamma and total_draft_rows say
     need = sv.spec_verify_workspace_size(sv.make_config(4, 1000, 1, 0, 0))
     assert need > 0 and sv.spec_verify_workspace_size(sv.make_config(4, 1000, 1, 5, 20)) >= need
+
+
+def test_topk_rows_argument_errors(sv):
+    E, W = sv.SV_EINVAL, sv.SV_EWORKSPACE
+
+    def topk(logits=FAKE, k=3, out=FAKE, B=4, V=1000, dtype=1, ws=FAKE, ws_bytes=16):
+        return sv.spec_topk_rows(logits, k, out, sv.make_config(B, V, dtype, 0, 0, 0, ws, ws_bytes))
+
+    assert topk() == W
+    assert topk(k=16) == W and topk(k=1) == W and topk(V=5, k=5) == W
+    for kw in ({"k": 0}, {"k": 17}, {"V": 5, "k": 6}, {"logits": 0}, {"out": 0}, {"B": 0}, {"V": 0},
+               {"dtype": 2}, {"logits": FAKE + 1}, {"out": FAKE + 2}):
+        assert topk(**kw) == E, kw
+    assert topk(ws=0) == W

@@ -141,6 +141,51 @@ def test_sample_rows_repeat_and_zero_filled_workspace_reuse():
     assert np.array_equal(a, b)
 
 
+# ------------------------------------------- top-k of each row (tree-draft children)
+
+def _topk_parity(logits, dtype, k):
+    import torch
+    import draft_token_verification_05_amd as sv
+    if dtype == "bf16":
+        dl = torch.from_numpy(np.ascontiguousarray(logits).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    else:
+        dl = torch.from_numpy(np.ascontiguousarray(logits, np.float32)).to("cuda:0")
+    print(f"[topk] rows={logits.shape[0]} V={logits.shape[1]} dtype={dtype} k={k}", flush=True)
+    got = sv.topk_rows(dl, k)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    want = oracle.topk_rows(logits, dtype, k)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:5]
+    return got
+
+
+@pytest.mark.parametrize("V,dtype,k", [(1, "bf16", 1), (7, "f32", 7), (1000, "bf16", 3), (8193, "bf16", 16),
+                                       (20000, "f32", 5), (16387, "bf16", 2), (152064, "bf16", 8),
+                                       (128256, "bf16", 4)])
+def test_topk_rows_shapes(V, dtype, k):
+    w = synthetic.random_workload(seed=V % 79 + k, mode=S, B=11, V=V, dtype=dtype, gmax=3, gmin=0)
+    _topk_parity(w.target, dtype, k)
+
+
+@pytest.mark.parametrize("k", [1, 3, 9])
+def test_topk_rows_heavy_ties_and_signed_zeros(k):
+    """Integer-valued logits (many equal values: the lower index must win at
+    every level), and rows of +0 / -0 only (equal logits)."""
+    w = synthetic.random_workload(seed=44 + k, mode=S, B=16, V=70000, dtype="bf16", gmax=2, gmin=0, scale=1.5,
+                                  spike=0.0, ties=True)
+    _topk_parity(w.target, "bf16", k)
+    z = np.zeros((6, 5000), np.float32)
+    z[:, 1::3] = -0.0
+    z[2, 4000] = 1.0
+    _topk_parity(z, "f32", k)
+
+
+def test_topk_rows_tree_draft_rows():
+    """The Llama-3-shaped batch's draft rows, k = 3 (a tree node's children)."""
+    w = synthetic.make_llama3()
+    _topk_parity(w.draft, "bf16", 3)
+
+
 # ------------------------------------------- position-adaptive NKL threshold
 
 def test_long_nkl_position_adaptive():
