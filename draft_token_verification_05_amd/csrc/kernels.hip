@@ -1962,6 +1962,31 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// bf16 rows: a 32-bit key of the same order within one helper's range of at
+// most 65536 elements, the order-mapped bf16 bits above 0xFFFF - (index - base).
+__device__ __forceinline__ uint32_t topk_key16(uint32_t h, uint32_t local) {
+  if (h == 0x8000u) h = 0u;  // -0 == +0
+  h = (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
+  return (h << 16) | (0xFFFFu - local);
+}
+// ... and back to the 64-bit key of the element (0 stays "no candidate")
+__device__ __forceinline__ uint64_t topk_key_from16(uint32_t k16, int base) {
+  if (k16 == 0) return 0;
+  uint32_t h = k16 >> 16;
+  h = (h & 0x8000u) ? (h & 0x7FFFu) : (~h & 0xFFFFu);
+  return topk_key(__uint_as_float(h << 16), base + (int)(0xFFFFu - (k16 & 0xFFFFu)));
+}
+// Branchless insertion into a sorted (largest first) list of 32-bit keys.
+template <int K>
+__device__ __forceinline__ void topk_insert16(uint32_t (&lst)[K], uint32_t key) {
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const uint32_t hi = max(lst[i], key), lo = min(lst[i], key);
+    lst[i] = hi;
+    key = lo;
+  }
+}
+
 // Keeps the K largest keys seen by this thread, sorted, largest first.
 template <int K>
 __device__ __forceinline__ void topk_insert(uint64_t (&lst)[K], uint64_t key) {
@@ -2017,18 +2042,43 @@ __global__ __launch_bounds__(kThreads) void k_topk(Params p) {
   uint64_t lst[K];
 #pragma unroll
   for (int i = 0; i < K; ++i) lst[i] = 0;
-  slice_stream<DT, VEC, false>(p, b, -1, s0, s1, [&](const uint4* qt, const uint4*, int sl) {
-    const int64_t e_base = (int64_t)sl * kThreads * kUT * P;
+  constexpr int CH = kThreads * kUT * P;  // elements of one slice
+  if (DT == SV_DTYPE_BF16 && (s1 - s0) * CH <= 65536) {
+    // 32-bit keys relative to the helper's first element, straight from the
+    // bf16 bits; converted to the 64-bit keys for the merges
+    const int base = s0 * CH;
+    uint32_t l16[K];
 #pragma unroll
-    for (int j = 0; j < kUT; ++j) {
-      float v[P];
-      unpack<DT>(qt[j], v);
-      const int64_t y0 = e_base + ((int64_t)(w * kUT + j) * 64 + lane) * P;
+    for (int i = 0; i < K; ++i) l16[i] = 0;
+    slice_stream<DT, VEC, false>(p, b, -1, s0, s1, [&](const uint4* qt, const uint4*, int sl) {
 #pragma unroll
-      for (int e = 0; e < P; ++e)
-        if (y0 + e < p.V) topk_insert<K>(lst, topk_key(v[e], (int)(y0 + e)));
-    }
-  });
+      for (int j = 0; j < kUT; ++j) {
+        const int y0 = sl * CH + ((w * kUT + j) * 64 + lane) * P;
+        const uint32_t wd[4] = {qt[j].x, qt[j].y, qt[j].z, qt[j].w};
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+          const uint32_t h = (e & 1) ? (wd[e >> 1] >> 16) : (wd[e >> 1] & 0xFFFFu);
+          const int y = y0 + e;
+          topk_insert16<K>(l16, y < p.V ? topk_key16(h, (uint32_t)(y - base)) : 0u);
+        }
+      }
+    });
+#pragma unroll
+    for (int i = 0; i < K; ++i) lst[i] = topk_key_from16(l16[i], base);
+  } else {
+    slice_stream<DT, VEC, false>(p, b, -1, s0, s1, [&](const uint4* qt, const uint4*, int sl) {
+      const int64_t e_base = (int64_t)sl * CH;
+#pragma unroll
+      for (int j = 0; j < kUT; ++j) {
+        float v[P];
+        unpack<DT>(qt[j], v);
+        const int64_t y0 = e_base + ((int64_t)(w * kUT + j) * 64 + lane) * P;
+#pragma unroll
+        for (int e = 0; e < P; ++e)
+          if (y0 + e < p.V) topk_insert<K>(lst, topk_key(v[e], (int)(y0 + e)));
+      }
+    });
+  }
   topk_merge<K>(lst, k, sh.best, sh.red);
   // row b's candidates: kThreads slots, helper h's k of them at h * k (H * k <= kThreads)
   uint64_t* cand = p.topk_cand + (int64_t)b * kThreads;
@@ -2431,6 +2481,7 @@ int plan_topk(Params& p, bool vec) {
   // most kThreads / k so that the last helper holds one candidate per thread
   int64_t H = ((int64_t)cap + p.B - 1) / p.B;
   if (H > p.nslices) H = p.nslices;
+  if (p.dtype == SV_DTYPE_BF16 && H < (p.nslices + 7) / 8) H = (p.nslices + 7) / 8;  // 16-bit local indices
   if (H > kThreads / p.topk) H = kThreads / p.topk;
   if (H < 1) H = 1;
   const int64_t spp = (p.nslices + H - 1) / H;
