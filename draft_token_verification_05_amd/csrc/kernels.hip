@@ -2341,9 +2341,10 @@ int plan_fused(Params& p, bool vec) {
     o = (e == hipSuccess && v > 0) ? v : 1;
   }
   // at most kFusedPerCu workgroups per compute unit: the units serve their
-  // workgroups' loads roughly in age order, so the newest stream last; with
-  // one fewer per unit the last ones finish sooner (Llama-3-shaped batch:
-  // 32.75 us per step at 4 per unit, 32.37 at 3, 33.0 at 2)
+  // workgroups' loads roughly in age order, so the newest stream last.  With
+  // the statistics waves paced by their remaining work, four per unit measure
+  // best on the Llama-3-shaped batch (31.5 us per step; 31.9 at three, 32.8
+  // at two)
   const int64_t cap = (int64_t)(o < kFusedPerCu ? o : kFusedPerCu) * num_cus();
   // Single dispatch only while the statistics pass is short: it saves the
   // second launch and the hand-over to the decision (the 82 MB Llama-3-shaped
