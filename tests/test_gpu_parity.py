@@ -77,6 +77,22 @@ def test_ragged_stochastic():
     check(synthetic.make_ragged())
 
 
+@pytest.mark.parametrize("name", ["tiny", "tiny_greedy", "llama3", "long_greedy", "long_nkl", "ragged", "tree",
+                                  "tree13"])
+def test_bench_calls_match_oracle(name):
+    """The calls the benchmark times, element by element against the oracle:
+    no diagnostic outputs (in stochastic mode the decision passes then stop at
+    the first rejection) and, in stochastic mode, no NKL output (the
+    single-dispatch path where it applies)."""
+    if name == "tiny_greedy":
+        w = synthetic.make_tiny().with_mode(G)
+    elif name in ("long_greedy", "long_nkl"):
+        w = synthetic.make_long(mode=G if name == "long_greedy" else K)
+    else:
+        w = synthetic.make(name)
+    check(w, diagnostics=False)
+
+
 # ------------------------------------------- draft-side row sampling
 
 def _sample_parity(logits, dtype, T, u):
@@ -262,6 +278,82 @@ def test_long_draft_several_decision_passes(mode):
     if mode == K:
         w = w.with_mode(K, delta=0.5)
     check(w, out_nkl=(mode != G))
+
+
+@pytest.mark.parametrize("mode", [S, G])
+def test_long_draft_early_exit_without_diagnostics(mode):
+    """Without diagnostic outputs the decision passes stop at the first
+    rejection; the positions after it are checked for invalid inputs on their
+    own.  Drafts of 530-600 positions span three decision passes; forced
+    acceptances (u = 0) move the first rejection of some requests into the
+    second and third pass, and invalid tokens / uniforms sit after the first
+    rejection, in a later pass."""
+    w = synthetic.random_workload(seed=37 + mode, mode=mode, B=6, V=3000, dtype="bf16", gmax=600, gmin=530,
+                                  sigma=0.02, greedy_drafts=(mode == G))
+    d_off = w.d_off
+    w.u_accept = w.u_accept.copy()
+    w.draft_tokens = w.draft_tokens.copy()
+    if mode == S:
+        w.u_accept[d_off[0]: d_off[0] + 300] = 0.0   # request 0 decides in the second pass
+        w.u_accept[d_off[3]: d_off[3] + 520] = 0.0   # request 3 in the third
+        w.u_accept[d_off[2] + int(w.gamma[2]) - 2] = 1.0  # invalid uniform near the end
+    else:
+        # greedy: accepted drafts are the target argmax; force long accepted prefixes
+        tgt = synthetic.bf16_bits_to_f32(w.target)
+        for b, n in ((0, 300), (3, 520)):
+            t0 = int(w.t_off[b])
+            w.draft_tokens[d_off[b]: d_off[b] + n] = np.argmax(tgt[t0: t0 + n], axis=1)
+        w.draft_tokens[d_off[2] + int(w.gamma[2]) - 2] = w.vocab + 3
+    w.draft_tokens[d_off[1] + int(w.gamma[1]) - 1] = w.vocab  # invalid token at the last position
+    w.draft_tokens[d_off[4] + 290] = -1                      # invalid token in the second pass
+    g, o, _ = check(w, diagnostics=False)
+    assert g["p_x"] is None  # no diagnostic outputs were requested
+    assert (g["num"][[1, 2, 4]] == -1).all()
+    assert (g["num"][[0, 3, 5]] >= 0).all()
+    assert g["num"][0] >= 256 and g["num"][3] >= 512
+
+
+def _nkl_records(w, o):
+    """NKL values of positions that a threshold near them reaches: each is
+    larger (by 1e-4 relative) than every NKL before it in its request."""
+    out = []
+    d_off = w.d_off
+    for b in range(w.batch):
+        prev = 0.0
+        for i in range(int(w.gamma[b])):
+            n = float(o.nkl[d_off[b] + i])
+            if n > prev * (1 + 1e-4):
+                out.append(n)
+            prev = max(prev, n)
+    return out
+
+
+@pytest.mark.parametrize("case", ["long", "f32_small", "bf16_near_identical"])
+def test_nkl_decisions_just_outside_the_flag_band(case):
+    """delta set at a reached position's NKL times 1 +- 2e-6, just outside the
+    oracle's 1e-6 flag band: no decision is excused, and the GPU decisions and
+    tokens equal the oracle's bit for bit.  The one-pass KL must route every
+    such position to the exact second pass."""
+    if case == "long":
+        w = synthetic.make_long(B=4, mode=K)   # the long-draft workload's first four requests
+    elif case == "f32_small":
+        w = synthetic.random_workload(seed=23, mode=K, B=8, V=20000, dtype="f32", gmax=7, gmin=3)
+    else:
+        w = synthetic.random_workload(seed=24, mode=K, B=8, V=50000, dtype="bf16", gmax=6, gmin=3, sigma=0.05)
+    o_all = oracle.verify_workload(w.with_mode(K, delta=10.0))  # every position reached
+    rec = sorted(_nkl_records(w, o_all))
+    picks = [rec[k] for k in np.linspace(0, len(rec) - 1, min(12, len(rec))).round().astype(int)]
+    d = to_device(w)
+    for n in picks:
+        for sgn in (1, -1):
+            wd = w.with_mode(K, delta=float(np.float32(n * (1 + sgn * 2e-6))))
+            print(f"[nkl-band] {case} nkl={n:.9g} delta={wd.delta:.9g}", flush=True)
+            g = run_gpu(wd, d, diagnostics=False)
+            od = oracle.verify_workload(wd)
+            rep = compare(wd, g, od)
+            assert rep.flagged_nkl == 0, rep
+            assert rep.mismatches == 0, rep
+            assert rep.max_rel_nkl <= 2e-5, rep
 
 
 @pytest.mark.parametrize("mode", [S, G, K, TR])

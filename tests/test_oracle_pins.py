@@ -477,6 +477,57 @@ def test_nkl_adaptive_threshold_decides():
     assert nchanged > 0  # the schedule changes some decisions on these rows
 
 
+def _scipy_nkl(t_row, d_row, T):
+    Td = np.float64(np.float32(T))
+    P = special.softmax(t_row.astype(np.float64) / Td)
+    Q = special.softmax(d_row.astype(np.float64) / Td)
+    return stats.entropy(Q, P) / np.log(t_row.shape[0])
+
+
+@pytest.mark.parametrize("sign", [1, -1])
+def test_nkl_band_flag_is_relative_to_the_threshold(sign):
+    """FLAG_NKL_BAND marks a decision with |nkl_i - delta| < 1e-6 delta.  With
+    delta set at a position's NKL (from scipy) times 1 +- 5e-7 the flag is set;
+    at 1 +- 2e-6 and 1 +- 5e-6 it is not.  The NKL values are below 0.2, so an
+    absolute band of 1e-6 would flag the 5e-6 case, and the decision at the
+    position follows the side of delta."""
+    B, gam, V, T = 3, 4, 4096, 0.6
+    t, d = _nkl_rows(21, B, gam, V, T)
+    temps = np.full(B, T, np.float32)
+    for b in (1, 2):
+        n = [_scipy_nkl(t[b * (gam + 1) + i], d[b * gam + i], T) for i in range(gam)]
+        assert n[0] < 0.2 and all(abs(n[i] / n[0] - 1) > 1e-3 for i in range(1, gam))
+        for rel, flagged in ((5e-7, True), (2e-6, False), (5e-6, False)):
+            delta = float(np.float32(n[0] * (1 + sign * rel)))
+            r = oracle.verify(t, d, "f32", np.full(B, gam, np.int32), np.zeros(B * gam, np.int32), temps, None,
+                              None, K, delta)
+            assert bool(r.flags[b] & oracle.FLAG_NKL_BAND) == flagged, (b, rel)
+            assert (r.num_accepted[b] > 0) == (sign > 0), (b, rel)
+
+
+@pytest.mark.parametrize("sign", [1, -1])
+def test_nkl_band_flag_uses_the_position_threshold(sign):
+    """With generation positions the band is taken around the position's own
+    threshold delta_i = min(delta_max, delta (1 + alpha log2(pos + 1))): at
+    pos = 1023 and alpha = 1/16 the threshold is 1.625 delta exactly, and delta
+    is set so that delta_i is the position's NKL times 1 +- 5e-7 (flagged) or
+    1 +- 5e-6 (not flagged)."""
+    B, gam, V, T = 3, 4, 4096, 0.6
+    t, d = _nkl_rows(21, B, gam, V, T)
+    temps = np.full(B, T, np.float32)
+    pos = np.zeros(B * gam, np.int32)
+    for b in (1, 2):
+        pos[b * gam: (b + 1) * gam] = 1023 + np.arange(gam)
+    for b in (1, 2):
+        n0 = _scipy_nkl(t[b * (gam + 1)], d[b * gam], T)
+        for rel, flagged in ((5e-7, True), (5e-6, False)):
+            delta = float(np.float32(n0 * (1 + sign * rel) / 1.625))
+            r = oracle.verify(t, d, "f32", np.full(B, gam, np.int32), np.zeros(B * gam, np.int32), temps, None,
+                              None, K, delta, nkl_position=pos, nkl_alpha=0.0625, nkl_delta_max=10.0)
+            assert bool(r.flags[b] & oracle.FLAG_NKL_BAND) == flagged, (b, rel)
+            assert (r.num_accepted[b] > 0) == (sign > 0), (b, rel)
+
+
 def test_nkl_negative_position_marks_only_its_request():
     B, gam, V, T = 3, 4, 512, 1.0
     t, d = _nkl_rows(13, B, gam, V, T)
