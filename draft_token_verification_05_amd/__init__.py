@@ -158,21 +158,26 @@ class VerifyOutput:
 
 
 _WORKSPACES = {}
+_MAX_CACHED_WORKSPACES = 64
 
 
-def workspace_for(cfg: sv_config, device) -> "torch.Tensor":
-    """A zero-filled workspace for this configuration, cached per device and
-    configuration.  spec_verify leaves its counters at zero after every
-    completed call, so a workspace is reused as is by later calls with the
-    same configuration on the same stream."""
+def workspace_for(cfg: sv_config, device, stream=None) -> "torch.Tensor":
+    """A workspace for this configuration, cached per device, stream and
+    configuration (calls on different streams must not share one).  Its
+    contents need no initialisation.  The tensor is recorded on ``stream`` so
+    that torch's allocator does not hand its memory out again while work
+    queued there may still use it, also after the cache drops it."""
     import torch
-    key = (str(device), cfg.batch, cfg.vocab, cfg.dtype, cfg.max_gamma, cfg.total_draft_rows)
-    ws = _WORKSPACES.get(key)
+    sid = 0 if stream is None else int(stream.cuda_stream)
+    key = (str(device), sid, cfg.batch, cfg.vocab, cfg.dtype, cfg.max_gamma, cfg.total_draft_rows)
+    ws = _WORKSPACES.pop(key, None)
     if ws is None:
-        ws = torch.zeros(max(spec_verify_workspace_size(cfg), 256), dtype=torch.uint8, device=device)
-        if len(_WORKSPACES) > 64:
-            _WORKSPACES.clear()
-        _WORKSPACES[key] = ws
+        ws = torch.empty(max(spec_verify_workspace_size(cfg), 256), dtype=torch.uint8, device=device)
+        while len(_WORKSPACES) >= _MAX_CACHED_WORKSPACES:
+            _WORKSPACES.pop(next(iter(_WORKSPACES)))  # the least recently used
+    if stream is not None:
+        ws.record_stream(stream)
+    _WORKSPACES[key] = ws  # most recently used last
     return ws
 
 
@@ -210,8 +215,9 @@ def verify(target_logits, draft_logits, draft_tokens, gamma_per_req, temperature
 
     ``target_logits`` [sum(gamma+1), V] and ``draft_logits`` [sum(gamma), V] are
     torch.bfloat16 or torch.float32 on the GPU.  The call is asynchronous on
-    ``stream`` (default: torch's current stream).  A ``workspace`` passed in must
-    be zero-filled before its first use (calls leave it reusable)."""
+    ``stream`` (default: torch's current stream).  A ``workspace`` passed in
+    needs no initialisation; calls on different streams must use different
+    workspaces."""
     import torch
     if isinstance(mode, str):
         mode = MODES[mode]
@@ -259,7 +265,7 @@ def verify(target_logits, draft_logits, draft_tokens, gamma_per_req, temperature
                       nkl_position=_ptr(nkl_position), nkl_alpha=nkl_alpha, nkl_delta_max=nkl_delta_max)
     need = spec_verify_workspace_size(cfg)
     if workspace is None:
-        workspace = workspace_for(cfg, dev)
+        workspace = workspace_for(cfg, dev, stream)
     elif workspace.numel() < need:
         raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
     cfg.workspace = workspace.data_ptr()
@@ -301,7 +307,7 @@ def sample_rows(logits, temperature, u, *, workspace=None, stream=None, phase_ev
         stream = torch.cuda.current_stream(dev)
     cfg = make_config(rows, V, dt, 0, 0, stream=int(stream.cuda_stream), phase_events=phase_events)
     if workspace is None:
-        workspace = workspace_for(cfg, dev)
+        workspace = workspace_for(cfg, dev, stream)
     elif workspace.numel() < spec_verify_workspace_size(cfg):
         raise ValueError("workspace too small")
     cfg.workspace, cfg.workspace_bytes = workspace.data_ptr(), workspace.numel()
@@ -330,7 +336,7 @@ def topk_rows(logits, k: int, *, workspace=None, stream=None, phase_events: int 
         stream = torch.cuda.current_stream(dev)
     cfg = make_config(rows, V, dt, 0, 0, stream=int(stream.cuda_stream), phase_events=phase_events)
     if workspace is None:
-        workspace = workspace_for(cfg, dev)
+        workspace = workspace_for(cfg, dev, stream)
     elif workspace.numel() < spec_verify_workspace_size(cfg):
         raise ValueError("workspace too small")
     cfg.workspace, cfg.workspace_bytes = workspace.data_ptr(), workspace.numel()

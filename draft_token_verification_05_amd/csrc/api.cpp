@@ -20,15 +20,16 @@ thread_local char g_hip_error[256] = "";
 // normal wait of a few microseconds.
 constexpr int32_t kDefaultWaitPolls = 4096;
 
-// Epochs that tag the fused kernel's partials: one per call, never 0 (the
-// value of a zero-filled workspace).  The start differs between processes, so
-// a workspace handed between them does not meet its own old tags.
+// Epochs that tag the fused kernel's partials and the helpers' arrival
+// counters: one per call, never 0 or 0xFFFFFFFF (the words of a zero-filled
+// or 0xFF-filled buffer).  The start differs between processes, so a
+// workspace handed between them does not meet its own old tags.
 uint32_t next_epoch() {
   static std::atomic<uint32_t> counter{
       (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761u};
   uint32_t e;
   do e = counter.fetch_add(1u, std::memory_order_relaxed) + 1u;
-  while (e == 0u);
+  while (e == 0u || e == 0xFFFFFFFFu);
   return e;
 }
 
@@ -176,7 +177,7 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   p.pair2req = reinterpret_cast<int32_t*>(ws + L.off_pair2req);
   p.row2req = reinterpret_cast<int32_t*>(ws + L.off_row2req);
   p.part_a = reinterpret_cast<sv::PartA*>(ws + L.off_part_a);
-  p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
+  p.cnt = reinterpret_cast<uint64_t*>(ws + L.off_cnt);
   p.cnt_kl = reinterpret_cast<uint32_t*>(ws + L.off_cnt_kl);
   p.req_fin = reinterpret_cast<sv::ReqFin*>(ws + L.off_req_fin);
   p.part_c = reinterpret_cast<sv::PartC*>(ws + L.off_part_c);
@@ -198,8 +199,8 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   // have a short statistics pass: the whole step in one dispatch
   const int fused_grid =
       (mode == SV_MODE_STOCHASTIC && !p.want_kl && B <= sv::kLdsBatch) ? sv::plan_fused(p, vec) : 0;
+  p.epoch = next_epoch();
   if (fused_grid > 0) {
-    p.epoch = next_epoch();
     p.wait_polls = cfg->wait_polls > 0 ? cfg->wait_polls : kDefaultWaitPolls;
     const int grid = fused_grid;
     if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e);
@@ -249,8 +250,9 @@ int spec_sample_rows(const void* logits, const float* temperature, const float* 
   p.dtype = cfg->dtype;
   p.mode = SV_MODE_STOCHASTIC;
   p.hdr = reinterpret_cast<int32_t*>(ws + L.off_hdr);
-  p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
+  p.cnt = reinterpret_cast<uint64_t*>(ws + L.off_cnt);
   p.part_c = reinterpret_cast<sv::PartC*>(ws + L.off_part_c);
+  p.epoch = next_epoch();
   const bool vec = ((size_t)cfg->vocab * es) % 16 == 0 && aligned(logits, 16);
   sv::plan_sample(p, vec);
   hipStream_t s = static_cast<hipStream_t>(cfg->stream);
@@ -284,8 +286,9 @@ int spec_topk_rows(const void* logits, int32_t k, int32_t* out_idx, const sv_con
   p.V = cfg->vocab;
   p.dtype = cfg->dtype;
   p.topk = k;
-  p.cnt = reinterpret_cast<uint32_t*>(ws + L.off_cnt);
+  p.cnt = reinterpret_cast<uint64_t*>(ws + L.off_cnt);
   p.topk_cand = reinterpret_cast<uint64_t*>(ws + L.off_topk);
+  p.epoch = next_epoch();
   const bool vec = ((size_t)cfg->vocab * es) % 16 == 0 && aligned(logits, 16);
   sv::plan_topk(p, vec);
   hipStream_t s = static_cast<hipStream_t>(cfg->stream);

@@ -401,7 +401,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Params p) {
     p.hdr[0] = bad ? 1 : 0;
     p.hdr[1] = 0;  // KL second-pass queue
   }
-  for (int b = tid; b < p.B; b += kPrepThreads) p.cnt[(int64_t)b * kCntStride] = p.cnt_kl[(int64_t)b * kCntStride] = 0u;  // completion counters
+  for (int b = tid; b < p.B; b += kPrepThreads) p.cnt_kl[(int64_t)b * kCntStride] = 0u;  // KL second-pass counters
   if (bad) return;
   __syncthreads();  // offsets written by other threads of this workgroup
   for (int b = tid; b < p.B; b += kPrepThreads) {
@@ -524,7 +524,7 @@ __device__ bool scan_offsets_lds(const Params& p, StatsShared& sh, const ScanIn&
   const bool ok = sh.bad == 0;
   if (publish) {
     for (int b = tid; b <= p.B; b += kThreads) p.d_off[b] = sh.off[b];
-    for (int b = tid; b < p.B; b += kThreads) p.cnt[(int64_t)b * kCntStride] = p.cnt_kl[(int64_t)b * kCntStride] = 0u;  // completion counters
+    for (int b = tid; b < p.B; b += kThreads) p.cnt_kl[(int64_t)b * kCntStride] = 0u;  // KL second-pass counters
     if (tid == 0) {
       p.hdr[0] = ok ? 0 : 1;
       p.hdr[1] = 0;  // KL second-pass queue
@@ -1268,10 +1268,10 @@ __device__ __forceinline__ int block_excl_count(bool flag, int* tail, DecideShar
   return before + in_wave;
 }
 
-// Counts this workgroup on the request's counter once every store of the
-// workgroup has completed; true in the last of the `H` arrivals.  The counter
-// wraps to zero on the last arrival (atomic increment modulo H), so it is
-// back at zero for the next call without a reset.
+// Counts this workgroup on a KL second-pass counter (zeroed by the same
+// call's offsets scan) once every store of the workgroup has completed; true
+// in the last of the `H` arrivals.  The counter wraps to zero on the last
+// arrival (atomic increment modulo H).
 template <class SH>
 __device__ __forceinline__ bool arrive_last(uint32_t* cnt, int H, SH& sh) {
   __asm__ __volatile__("" ::: "memory");
@@ -1281,6 +1281,47 @@ __device__ __forceinline__ bool arrive_last(uint32_t* cnt, int H, SH& sh) {
   if (threadIdx.x == 0) {
     const uint32_t old = __builtin_amdgcn_atomic_inc32(cnt, (uint32_t)H - 1u, __ATOMIC_RELAXED, "agent");
     sh.flag = old + 1 == (uint32_t)H ? 1 : 0;
+  }
+  __syncthreads();
+  return sh.flag != 0;
+}
+
+// Helper arrival counters: (epoch << 32) | arrivals.  The thread kClaimThread
+// (lane 0 of the last wave) loads the request's word early (claim_load) and,
+// before its workgroup counts itself, claims it for this call (claim): a word
+// that carries another epoch -- left by an earlier call, or any other bytes --
+// is replaced by (epoch << 32) with a compare-and-swap.  The first helper's
+// swap succeeds; every other helper's fails or is skipped because the word
+// already carries the epoch, and from then on only this call's increments
+// change it.  No reset is needed and nothing in the workspace must start at a
+// particular value.
+constexpr int kClaimThread = kThreads - 64;
+
+__device__ __forceinline__ uint64_t claim_load(const uint64_t* c) {
+  return ld_dev(c);
+}
+__device__ __forceinline__ void claim(uint64_t* c, uint64_t cur, uint32_t epoch) {
+  const uint64_t mine = (uint64_t)epoch << 32;
+  // a failed swap returns the current word; within one call that word carries
+  // the epoch, so the loop ends after at most two swaps (bounded regardless)
+  for (int k = 0; k < 4 && (uint32_t)(cur >> 32) != epoch; ++k)
+    if (__hip_atomic_compare_exchange_strong(c, &cur, mine, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      break;
+}
+
+// Counts this workgroup on the request's claimed counter once every memory
+// operation of the workgroup (its stores and the claim) has completed; true in
+// the last of the `H` arrivals.
+template <class SH>
+__device__ __forceinline__ bool arrive_last(uint64_t* cnt, int H, SH& sh) {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores (and the claim) have completed
+  __asm__ __volatile__("" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint64_t old = __hip_atomic_fetch_add(cnt, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh.flag = (uint32_t)old + 1u == (uint32_t)H ? 1 : 0;
   }
   __syncthreads();
   return sh.flag != 0;
@@ -1653,6 +1694,10 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
   const bool writer = h == 0;  // helper 0 writes the outputs of the decision
   const int tid = threadIdx.x;
   const bool want_kl = SOFT && !FUSED && p.want_kl;  // the single dispatch has no KL output
+  // the request's arrival counter, loaded now and claimed before the draw
+  uint64_t* const arr = p.cnt + (int64_t)b * kArrStride;
+  uint64_t arr_cur = 0;
+  if (MODE == SV_MODE_STOCHASTIC && tid == kClaimThread) arr_cur = claim_load(arr);
   if (!ok) {  // layout error: only the counts are written
     if (writer && tid == 0) p.out_num[b] = -1;
     return;
@@ -1870,6 +1915,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
       tm.drow = -1;
       tm.m_t = tm.m_d = tm.k0 = 0.0f;
     }
+    if (tid == kClaimThread) claim(arr, arr_cur, p.epoch);  // completes before this helper counts itself
     // one record per wave-chunk: kWaves per slice, in token order
     PartC* rec = p.part_c + (int64_t)b * NS * kWaves + (tid >> 6);
     if (tm.kind == kTermResidual)
@@ -1880,7 +1926,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
       slice_stream<DT, VEC, false>(p, tm.trow, tm.drow, s0, s1, [&](const uint4* qt, const uint4* qd, int sl) {
         draw_record<DT, false>(qt, qd, tm, rec + sl * kWaves);
       });
-    if (arrive_last(p.cnt + (int64_t)b * kCntStride, H, sh)) {
+    if (arrive_last(arr, H, sh)) {
       const int NW = NS * kWaves;
       if (NW <= kSelCache) draw_select<DT, VEC, true>(p, b, tm, NW, ur, sh);
       else draw_select<DT, VEC, false>(p, b, tm, NW, ur, sh);
@@ -1916,6 +1962,8 @@ template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_sample(Params p) {
   __shared__ DecideShared sh;
   const int b = (int)(blockIdx.x % (unsigned)p.B), h = (int)(blockIdx.x / (unsigned)p.B);
+  uint64_t* const arr = p.cnt + (int64_t)b * kArrStride;
+  const uint64_t arr_cur = threadIdx.x == kClaimThread ? claim_load(arr) : 0;
   const float T = p.temp[b], u = p.ur[b];
   if (!temp_ok(T) || !unit_ok(u)) {
     if (h == 0 && threadIdx.x == 0) p.out_tokens[b] = -1;
@@ -1929,10 +1977,14 @@ __global__ __launch_bounds__(kThreads) void k_sample(Params p) {
   tm.Lhi = (float)(kLog2eD / (double)T);
   const int NS = p.nslices, s0 = h * p.slices_per_helper, s1 = min(NS, s0 + p.slices_per_helper);
   PartC* rec = p.part_c + (int64_t)b * NS * kWaves + (threadIdx.x >> 6);
+  // the claim is issued once the first slice's loads have arrived (the
+  // counter's load was issued before them), so that it costs no wait
   slice_stream<DT, VEC, false>(p, tm.trow, tm.drow, s0, s1, [&](const uint4* qt, const uint4* qd, int sl) {
+    if (sl == s0 && threadIdx.x == kClaimThread) claim(arr, arr_cur, p.epoch);
     draw_record<DT, false>(qt, qd, tm, rec + sl * kWaves);
   });
-  if (arrive_last(p.cnt + (int64_t)b * kCntStride, p.helpers, sh)) {
+  if (s0 >= s1 && threadIdx.x == kClaimThread) claim(arr, arr_cur, p.epoch);
+  if (arrive_last(arr, p.helpers, sh)) {
     const int NW = NS * kWaves;
     if (NW <= kSelCache) draw_select<DT, VEC, true>(p, b, tm, NW, u, sh);
     else draw_select<DT, VEC, false>(p, b, tm, NW, u, sh);
@@ -2039,6 +2091,8 @@ __global__ __launch_bounds__(kThreads) void k_topk(Params p) {
   const int k = p.topk, H = p.helpers, NS = p.nslices;
   const int s0 = h * p.slices_per_helper, s1 = min(NS, s0 + p.slices_per_helper);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint64_t* const arr = p.cnt + (int64_t)b * kArrStride;
+  const uint64_t arr_cur = threadIdx.x == kClaimThread ? claim_load(arr) : 0;
   uint64_t lst[K];
 #pragma unroll
   for (int i = 0; i < K; ++i) lst[i] = 0;
@@ -2051,6 +2105,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(Params p) {
 #pragma unroll
     for (int i = 0; i < K; ++i) l16[i] = 0;
     slice_stream<DT, VEC, false>(p, b, -1, s0, s1, [&](const uint4* qt, const uint4*, int sl) {
+      if (sl == s0 && threadIdx.x == kClaimThread) claim(arr, arr_cur, p.epoch);
 #pragma unroll
       for (int j = 0; j < kUT; ++j) {
         const int y0 = sl * CH + ((w * kUT + j) * 64 + lane) * P;
@@ -2067,6 +2122,7 @@ __global__ __launch_bounds__(kThreads) void k_topk(Params p) {
     for (int i = 0; i < K; ++i) lst[i] = topk_key_from16(l16[i], base);
   } else {
     slice_stream<DT, VEC, false>(p, b, -1, s0, s1, [&](const uint4* qt, const uint4*, int sl) {
+      if (sl == s0 && threadIdx.x == kClaimThread) claim(arr, arr_cur, p.epoch);
       const int64_t e_base = (int64_t)sl * CH;
 #pragma unroll
       for (int j = 0; j < kUT; ++j) {
@@ -2079,11 +2135,12 @@ __global__ __launch_bounds__(kThreads) void k_topk(Params p) {
       }
     });
   }
+  if (s0 >= s1 && threadIdx.x == kClaimThread) claim(arr, arr_cur, p.epoch);
   topk_merge<K>(lst, k, sh.best, sh.red);
   // row b's candidates: kThreads slots, helper h's k of them at h * k (H * k <= kThreads)
   uint64_t* cand = p.topk_cand + (int64_t)b * kThreads;
   if (threadIdx.x < k) st_dev(&cand[h * k + threadIdx.x], sh.best[threadIdx.x]);
-  if (!arrive_last(p.cnt + (int64_t)b * kCntStride, H, sh)) return;
+  if (!arrive_last(arr, H, sh)) return;
   // the row's last helper: one candidate per thread, then the same merge
   uint64_t c1[1] = {0};
   if (threadIdx.x < H * k) c1[0] = ld_dev(&cand[threadIdx.x]);

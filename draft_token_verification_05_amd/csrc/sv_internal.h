@@ -24,7 +24,8 @@ constexpr int kFusedItemsPerWg = 12;  // longest statistics pass (items per resi
 constexpr int kFusedPerCu = 4;        // resident workgroups per compute unit of the single dispatch
 // per-request arrival counters sit 256 bytes apart: increments of different
 // requests' counters would otherwise queue behind each other on one line
-constexpr int kCntStride = 64;
+constexpr int kCntStride = 64;     // in 32-bit words (KL second-pass counters)
+constexpr int kArrStride = 32;     // in 64-bit words (epoch-tagged helper counters)
 constexpr int kTopkMax = 16;  // largest k of the per-row top-k
 
 constexpr int elems_per_vec(int dtype) { return dtype == SV_DTYPE_BF16 ? 8 : 4; }
@@ -102,11 +103,12 @@ inline Layout make_layout(int64_t B, int64_t V, int dtype, int64_t R_d) {
     return at;
   };
   L.off_hdr = take(256);
+  // the helpers' arrival counters sit at an offset that depends on B only
+  L.off_cnt = take(sizeof(uint64_t) * B * kArrStride);
   L.off_doff = take(sizeof(int32_t) * (B + 1));
   L.off_pair2req = take(sizeof(int32_t) * R1);
   L.off_row2req = take(sizeof(int32_t) * (R_d + B));
   L.off_part_a = take(sizeof(PartA) * L.n_task_max * L.nch_a);
-  L.off_cnt = take(sizeof(uint32_t) * B * kCntStride);
   L.off_cnt_kl = take(sizeof(uint32_t) * B * kCntStride);
   L.off_req_fin = take(sizeof(ReqFin) * B);
   L.off_part_c = take(sizeof(PartC) * B * L.nch_t * (kThreads / 64));
@@ -149,7 +151,7 @@ struct Params {
   const int32_t* nkl_pos;    // NKL: generation position of every draft row (NULL: constant delta)
   float nkl_alpha, nkl_dmax;  // NKL with positions: growth and cap of the threshold
   int32_t want_kl;  // compute KL(q || p) (NKL mode, or stochastic with out_nkl)
-  uint32_t epoch;      // fused kernel: tag of this call's statistics partials (never 0)
+  uint32_t epoch;      // this call's tag: fused statistics partials and arrival counters (never 0 or ~0)
   int32_t wait_polls;  // fused kernel: polls of a partial before a helper computes it itself
   // workspace
   int32_t* hdr;  // hdr[0]: layout error flag, hdr[1]: positions queued for the KL second pass
@@ -157,10 +159,15 @@ struct Params {
   int32_t* pair2req;
   int32_t* row2req;
   PartA* part_a;
-  // per-request arrival counters: the last arrival wraps them back to zero, so
-  // every completed call leaves them at zero (a new workspace is zero-filled)
-  uint32_t* cnt;      // [B * kCntStride] decision helpers done per request (one every kCntStride)
-  uint32_t* cnt_kl;   // [B * kCntStride] KL second-pass items done per request
+  // Per-request arrival counters of the helpers (terminal draw, row sampling,
+  // top-k): (epoch << 32) | arrivals, one every kArrStride words.  A helper
+  // claims the word for its call (compare-and-swap of a word with another
+  // epoch to (epoch << 32)) before it counts itself, so the counters need no
+  // reset and any leftover value in the workspace is harmless.
+  uint64_t* cnt;      // [B * kArrStride]
+  // KL second-pass items done per request: zeroed by the offsets scan of the
+  // same call, wrapped back to zero by the last arrival
+  uint32_t* cnt_kl;   // [B * kCntStride]
   ReqFin* req_fin;    // [B] completion record of the KL second pass
   PartC* part_c;      // [B * nslices * 4] draw sums per wave-chunk
   RefItem* ref_list;  // [R_d] positions queued for the KL second pass (hdr[1] of them)

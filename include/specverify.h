@@ -44,9 +44,19 @@
  *
  * Memory.  Every array argument is DEVICE memory, row-major and packed.  The
  * caller owns all buffers (including the workspace); the library allocates
- * nothing, keeps no global state, and only enqueues work on cfg->stream.
- * Outputs are valid once that stream has been synchronised.  Calls on
- * different streams must use different workspaces.
+ * nothing and only enqueues work on cfg->stream.  Outputs are valid once that
+ * stream has been synchronised.  Calls on different streams must use
+ * different workspaces.  Host-side state is limited to cached device
+ * attributes (compute-unit counts, kernel occupancies) and a call counter
+ * whose values ("epochs", never 0 or 0xFFFFFFFF) tag what a call leaves in
+ * its workspace.
+ *
+ * Workspace.  Its contents need no initialisation and need not be preserved
+ * between calls: a call reads only what the same call wrote, apart from the
+ * per-request arrival counters, which it first claims for itself (a word that
+ * carries another call's epoch, or any other bytes, is replaced).  One
+ * workspace may serve successive calls of any entry point and any
+ * configuration on one stream, as long as it is large enough for each.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -97,7 +107,8 @@ typedef struct sv_config {
                                computes that partial itself (results do not depend on it) */
   int64_t total_draft_rows; /* sum_b gamma_per_req[b], known on the host (sizes the grids) */
   void* stream;             /* hipStream_t to enqueue on; NULL = the default stream */
-  void* workspace;          /* device scratch, >= spec_verify_workspace_size(cfg) bytes, 256-byte aligned */
+  void* workspace;          /* device scratch, >= spec_verify_workspace_size(cfg) bytes, 256-byte aligned;
+                               contents need no initialisation (see "Workspace" above) */
   uint64_t workspace_bytes;
   /* optional diagnostics (device pointers, NULL = not written) */
   float* out_p_x;           /* [total_draft_rows] p_i(x_i) (stochastic and NKL modes) */
@@ -155,8 +166,10 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
 
 /* Workspace bytes spec_verify needs for this configuration (any mode); 0 for an invalid cfg.
  * Reads batch, vocab, dtype, max_gamma and total_draft_rows only.  The workspace holds
- * per-chunk partial results, counters and per-request records; it may be reused by
- * successive calls on the same stream. */
+ * per-chunk partial results, arrival counters and per-request records; it needs no
+ * initialisation and may be reused by successive calls on the same stream (see
+ * "Workspace" above).  spec_sample_rows and spec_topk_rows need the size for batch =
+ * rows and total_draft_rows = 0. */
 size_t spec_verify_workspace_size(const sv_config* cfg);
 
 /* Static description of a status code.  For SV_EHIP it includes the HIP error of the
@@ -187,10 +200,9 @@ int spec_verify_single_dispatch(const sv_config* cfg, int32_t mode, int32_t with
  * u            float32 [rows] in [0, 1).
  * out_tokens   int32 [rows]: the drawn token, or -1 for a row whose temperature or uniform is
  *              invalid (a data error, found on the device; other rows are not affected).
- * cfg          batch, vocab, dtype, stream, workspace (>= spec_verify_workspace_size(cfg), any
- *              max_gamma and total_draft_rows; zero-filled before its first use, reusable by later
- *              calls on the same stream) and phase_events ([1] and [2] bracket the sampling
- *              dispatch).  The other fields are not read.
+ * cfg          batch, vocab, dtype, stream, workspace (>= spec_verify_workspace_size(cfg) with
+ *              total_draft_rows = 0; no initialisation needed) and phase_events ([1] and [2]
+ *              bracket the sampling dispatch).  The other fields are not read.
  * Synchronous errors: SV_EINVAL (NULL or misaligned pointer, B <= 0, V <= 0, bad dtype or
  * struct_size), SV_EUNSUPPORTED (grid above 2^31 - 1), SV_EWORKSPACE, SV_EHIP.
  * Asynchronous on cfg->stream, like spec_verify.

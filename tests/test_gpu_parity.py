@@ -571,6 +571,100 @@ def test_workspace_shared_by_both_stochastic_paths():
         assert np.array_equal(first[k], again[k], equal_nan=True), k
 
 
+def _ff_workspace(nbytes):
+    import torch
+    return torch.full((max(int(nbytes), 256),), 0xFF, dtype=torch.uint8, device="cuda:0")
+
+
+def test_workspace_prefilled_with_ff_bytes():
+    """The workspace needs no initialisation: every entry point and path run
+    on a workspace filled with 0xFF bytes (and again on what the previous
+    call left) matches the oracle."""
+    import torch
+    import draft_token_verification_05_amd as sv
+    w = synthetic.random_workload(seed=91, mode=S, B=24, V=40000, dtype="bf16", gmax=6, gmin=0)
+    d = to_device(w)
+    cfg = sv.make_config(w.batch, w.vocab, sv.SV_DTYPE_BF16, w.max_gamma, w.total_draft_rows)
+    n = sv.spec_verify_workspace_size(cfg)
+    for mode, kw in ((S, {}), (S, {"out_nkl": True}), (G, {}), (K, {}), (S, {"diagnostics": False})):
+        wm = w.with_mode(mode)
+        o = oracle.verify_workload(wm)
+        for fresh in (True, False):
+            ws = _ff_workspace(n) if fresh else ws
+            print(f"[ws-ff] mode={mode} {kw} fresh={fresh}", flush=True)
+            assert_parity(compare(wm, run_gpu(wm, d, workspace=ws, **kw), o), mode)
+    wt = synthetic.random_workload(seed=92, mode=TR, B=9, V=5000, dtype="bf16", gmax=7, gmin=1, tree=True)
+    cfg_t = sv.make_config(wt.batch, wt.vocab, sv.SV_DTYPE_BF16, wt.max_gamma, wt.total_draft_rows)
+    assert_parity(compare(wt, run_gpu(wt, workspace=_ff_workspace(sv.spec_verify_workspace_size(cfg_t))),
+                          oracle.verify_workload(wt)), TR)
+    # row sampling and top-k on the draft rows
+    rows = w.draft
+    dl = torch.from_numpy(np.ascontiguousarray(rows).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    T_np = np.repeat(w.temperature, w.gamma).astype(np.float32)
+    T = torch.from_numpy(T_np).to("cuda:0")
+    u = torch.from_numpy(w.u_accept).to("cuda:0")
+    cfg_r = sv.make_config(rows.shape[0], w.vocab, sv.SV_DTYPE_BF16, 0, 0)
+    ws_r = _ff_workspace(sv.spec_verify_workspace_size(cfg_r))
+    ot, margin = oracle.sample_rows(rows, "bf16", T_np, w.u_accept)
+    for _ in range(2):
+        tok = sv.sample_rows(dl, T, u, workspace=ws_r).cpu().numpy()
+        assert not ((tok != ot) & ~(np.nan_to_num(margin, nan=1.0) < 1e-5)).any()
+        assert np.array_equal(sv.topk_rows(dl, 4, workspace=ws_r).cpu().numpy(), oracle.topk_rows(rows, "bf16", 4))
+
+
+def test_workspace_shared_across_shapes_and_entry_points():
+    """One workspace, sized for the largest call, serves in turn single-dispatch
+    calls with different total draft rows (the counters' place does not move
+    with them), row sampling, top-k and the separate-kernel paths; every call
+    matches the oracle."""
+    import torch
+    import draft_token_verification_05_amd as sv
+    wa = synthetic.make_llama3(B=32, V=30000)
+    wb = synthetic.random_workload(seed=93, mode=S, B=32, V=30000, dtype="bf16", gmax=5, gmin=4)
+    sizes = [sv.spec_verify_workspace_size(sv.make_config(w.batch, w.vocab, 1, w.max_gamma, w.total_draft_rows))
+             for w in (wa, wb)]
+    sizes.append(sv.spec_verify_workspace_size(sv.make_config(wa.total_draft_rows, wa.vocab, 1, 0, 0)))
+    ws = _ff_workspace(max(sizes))
+    da, db = to_device(wa), to_device(wb)
+    oa, ob = oracle.verify_workload(wa), oracle.verify_workload(wb)
+    rows = wa.draft
+    dl = torch.from_numpy(np.ascontiguousarray(rows).view(np.int16)).to("cuda:0").view(torch.bfloat16)
+    T_np = np.repeat(wa.temperature, wa.gamma).astype(np.float32)
+    T, u = torch.from_numpy(T_np).to("cuda:0"), torch.from_numpy(wa.u_accept).to("cuda:0")
+    ot, margin = oracle.sample_rows(rows, "bf16", T_np, wa.u_accept)
+    for k in range(3):
+        print(f"[ws-shared] round {k}", flush=True)
+        assert_parity(compare(wa, run_gpu(wa, da, workspace=ws, diagnostics=False), oa), S)
+        assert_parity(compare(wb, run_gpu(wb, db, workspace=ws, diagnostics=False), ob), S)
+        tok = sv.sample_rows(dl, T, u, workspace=ws).cpu().numpy()
+        assert not ((tok != ot) & ~(np.nan_to_num(margin, nan=1.0) < 1e-5)).any()
+        assert_parity(compare(wb, run_gpu(wb, db, workspace=ws, out_nkl=True), ob), S)
+        assert np.array_equal(sv.topk_rows(dl, 3, workspace=ws).cpu().numpy(), oracle.topk_rows(rows, "bf16", 3))
+
+
+def test_default_workspaces_on_two_streams():
+    """Calls without a workspace argument on two streams get different cached
+    workspaces: concurrent calls of one configuration give the answer of a
+    call made alone."""
+    import torch
+    import draft_token_verification_05_amd as sv
+    w = synthetic.make_llama3(B=16)
+    d = to_device(w)
+    ref = run_gpu(w, d, diagnostics=False)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    torch.cuda.synchronize()
+    for k in range(10):
+        for st in streams:
+            with torch.cuda.stream(st):
+                outs.append(sv.verify(d["target"], d["draft"], d["tokens"], d["gamma"], d["temp"], d["ua"], d["ur"],
+                                      S, w.delta, max_gamma=w.max_gamma, stream=st))
+    torch.cuda.synchronize()
+    for o in outs:
+        assert np.array_equal(o.tokens.cpu().numpy(), ref["tokens"])
+        assert np.array_equal(o.num_accepted.cpu().numpy(), ref["num"])
+
+
 def test_concurrent_calls_on_two_streams():
     """Calls enqueued on two streams with their own workspaces run at the same
     time and compete for the compute units (the single dispatch's helpers then
