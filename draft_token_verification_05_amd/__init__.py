@@ -13,6 +13,8 @@ C entry points (``include/specverify.h``) and their Python counterparts:
 * ``spec_verify_status_string``  -> :func:`spec_verify_status_string`
 * ``spec_verify_version``        -> :func:`spec_verify_version`
 * ``spec_verify_single_dispatch`` -> :func:`spec_verify_single_dispatch`
+* ``spec_verify_noalloc``         -> :func:`spec_verify_noalloc` (raw pointers; no workspace)
+* ``spec_sample_rows`` / ``spec_topk_rows`` -> :func:`sample_rows` / :func:`topk_rows` (tensors)
 """
 from __future__ import annotations
 
@@ -28,6 +30,7 @@ SV_OK, SV_EINVAL, SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP = 0, -1, -2, -3, -4
 SV_MODE_STOCHASTIC, SV_MODE_GREEDY, SV_MODE_NKL, SV_MODE_TREE_GREEDY = 0, 1, 2, 3
 SV_DTYPE_F32, SV_DTYPE_BF16 = 0, 1
 SV_MAX_GAMMA = 4096
+SV_NOALLOC_SCRATCH_BYTES = 16 << 20
 SV_NUM_PHASE_EVENTS = 4
 MODES = {"stochastic": 0, "greedy": 1, "nkl": 2, "tree": 3}
 
@@ -75,6 +78,8 @@ def _load() -> ctypes.CDLL:
     P, i32 = ctypes.c_void_p, ctypes.c_int32
     lib.spec_verify.restype = ctypes.c_int
     lib.spec_verify.argtypes = [P, P, P, P, P, P, P, i32, ctypes.c_float, P, P, P, P, ctypes.POINTER(sv_config)]
+    lib.spec_verify_noalloc.restype = ctypes.c_int
+    lib.spec_verify_noalloc.argtypes = lib.spec_verify.argtypes
     lib.spec_verify_workspace_size.restype = ctypes.c_size_t
     lib.spec_verify_workspace_size.argtypes = [ctypes.POINTER(sv_config)]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
@@ -112,6 +117,18 @@ def spec_verify(target_logits: int, draft_logits: int, draft_tokens: int, gamma_
                                 gamma_per_req or None, temperature or None, u_accept or None, u_resample or None,
                                 int(mode), float(delta), tree_parents or None, out_tokens or None,
                                 out_num_accepted or None, out_nkl or None, ctypes.byref(cfg)))
+
+
+def spec_verify_noalloc(target_logits: int, draft_logits: int, draft_tokens: int, gamma_per_req: int,
+                        temperature: int, u_accept: int, u_resample: int, mode: int, delta: float, tree_parents: int,
+                        out_tokens: int, out_num_accepted: int, out_nkl: int, cfg: sv_config) -> int:
+    """spec_verify on the library's own fixed device scratch (cfg.workspace is
+    ignored; nothing is allocated).  Returns the status."""
+    return int(_lib.spec_verify_noalloc(target_logits or None, draft_logits or None, draft_tokens or None,
+                                        gamma_per_req or None, temperature or None, u_accept or None,
+                                        u_resample or None, int(mode), float(delta), tree_parents or None,
+                                        out_tokens or None, out_num_accepted or None, out_nkl or None,
+                                        ctypes.byref(cfg)))
 
 
 def spec_sample_rows(logits: int, temperature: int, u: int, out_tokens: int, cfg: sv_config) -> int:

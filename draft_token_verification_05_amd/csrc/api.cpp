@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "sv_internal.h"
 
@@ -85,6 +86,42 @@ int hip_fail(hipError_t e) {
 
 }  // namespace
 
+// Scratch of spec_verify_noalloc: file-scope device memory, one copy on every
+// GPU the library runs on, held until the process ends.  In host code this
+// name is only a handle for hipGetSymbolAddress; the device address of the
+// current GPU's copy comes from noalloc_scratch().
+static __device__ __align__(256) unsigned char scratch[SV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current GPU's copy of `scratch`, looked up once per
+// device (with that device current) and kept.
+int noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return SV_EUNSUPPORTED;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_fail(e);
+      if (!ptr) return hip_fail(hipErrorInvalidSymbol);
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return SV_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t spec_verify_workspace_size(const sv_config* cfg) {
@@ -99,7 +136,9 @@ const char* spec_verify_status_string(int status) {
     case SV_OK: return "SV_OK: success";
     case SV_EINVAL: return "SV_EINVAL: invalid argument";
     case SV_EUNSUPPORTED: return "SV_EUNSUPPORTED: configuration not supported";
-    case SV_EWORKSPACE: return "SV_EWORKSPACE: workspace missing, misaligned or too small";
+    case SV_EWORKSPACE:
+      return "SV_EWORKSPACE: workspace missing, misaligned or too small (spec_verify_noalloc: the configuration "
+             "needs more than SV_NOALLOC_SCRATCH_BYTES of scratch)";
     case SV_EHIP: return g_hip_error[0] ? g_hip_error : "SV_EHIP: HIP launch failure";
     default: return "unknown status";
   }
@@ -223,6 +262,24 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   if (p.want_kl && (e = (hipError_t)sv::launch_refine(p, vec, s)) != hipSuccess) return hip_fail(e);
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e);
   return SV_OK;
+}
+
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                        const int32_t* gamma_per_req, const float* temperature, const float* u_accept,
+                        const float* u_resample, int32_t mode, float delta, const int32_t* tree_parents,
+                        int32_t* out_tokens, int32_t* out_num_accepted, float* out_nkl, const sv_config* cfg) {
+  if (!cfg || cfg->struct_size != sizeof(sv_config)) return SV_EINVAL;
+  sv_config c = *cfg;
+  const size_t need = spec_verify_workspace_size(&c);
+  if (need == 0) return SV_EINVAL;
+  if (need > (size_t)SV_NOALLOC_SCRATCH_BYTES) return SV_EWORKSPACE;
+  void* ptr = nullptr;
+  const int st = noalloc_scratch(&ptr);
+  if (st != SV_OK) return st;
+  c.workspace = ptr;
+  c.workspace_bytes = SV_NOALLOC_SCRATCH_BYTES;
+  return spec_verify(target_logits, draft_logits, draft_tokens, gamma_per_req, temperature, u_accept, u_resample,
+                     mode, delta, tree_parents, out_tokens, out_num_accepted, out_nkl, &c);
 }
 
 int spec_sample_rows(const void* logits, const float* temperature, const float* u, int32_t* out_tokens,

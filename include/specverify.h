@@ -189,6 +189,25 @@ int spec_verify_version(void);
 int spec_verify_single_dispatch(const sv_config* cfg, int32_t mode, int32_t with_nkl);
 
 /*
+ * spec_verify without a caller-provided workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * The arguments and results are those of spec_verify; cfg->workspace and cfg->workspace_bytes
+ * are ignored.  The scratch is a fixed array of SV_NOALLOC_SCRATCH_BYTES in the library's own
+ * device memory, one copy per GPU, held until the process ends; its device address is looked
+ * up once per device on the first call (the current device, which must own cfg->stream).  The
+ * call allocates nothing.  A configuration whose spec_verify_workspace_size() exceeds
+ * SV_NOALLOC_SCRATCH_BYTES returns SV_EWORKSPACE before anything is enqueued.  Every call on a
+ * GPU shares that GPU's array: calls that overlap on one GPU (two streams, or two threads) race
+ * and give undefined results; successive calls on one stream are fine.  Nothing in the array
+ * must start at a particular value (see "Workspace" above), so it is never cleared.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                        const int32_t* gamma_per_req, const float* temperature, const float* u_accept,
+                        const float* u_resample, int32_t mode, float delta, const int32_t* tree_parents,
+                        int32_t* out_tokens, int32_t* out_num_accepted, float* out_nkl, const sv_config* cfg);
+
+/*
  * Draft-side sampling, the drafter's step before verification: one token per row, drawn from
  * softmax(logits_r / temperature[r]) by the inverse CDF with the uniform u[r],
  *     y_r = min{ y : C_y > u_r * S }   (C_y: cumulative mass in ascending token order, S: total),

@@ -25,8 +25,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["spec_sample_rows", "spec_topk_rows", "spec_verify", "spec_verify_single_dispatch",
-                                    "spec_verify_status_string", "spec_verify_version", "spec_verify_workspace_size"]
+    assert declared_functions() == ["spec_sample_rows", "spec_topk_rows", "spec_verify", "spec_verify_noalloc",
+                                    "spec_verify_single_dispatch", "spec_verify_status_string", "spec_verify_version",
+                                    "spec_verify_workspace_size"]
 
 
 def test_single_dispatch_query_host_side(sv):
