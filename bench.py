@@ -8,16 +8,21 @@ step reads a different copy of them (enough copies to cover > 1 GiB), so the
 256 MB Infinity Cache cannot serve the logits of the step before.
 
 Prints ONE JSON line with verified draft positions/s, the roofline of the
-dominant kernel and the CPU oracle timed on the host cores on a bounded sample
-of the same workload.  The dominant kernel is the single dispatch k_fused
-that runs the whole stochastic step of a short batch (the Llama-3-shaped one;
-its algorithmic bytes are those of the whole step), else the row-statistics
-kernel k_stats.  It is timed with HIP events that spec_verify records on the
-call's stream at the dispatch's own start and end, in every
---event-every'th timed step (event records cost a few microseconds each, so
-they are not put into every step).
+dominant kernel, per-call percentiles, a plain-read probe over the same bytes
+and the CPU oracle timed on the host cores on a bounded sample of the same
+workload.  The dominant kernel is the single dispatch k_fused that runs the
+whole stochastic step of a short batch (the Llama-3-shaped one; its
+algorithmic bytes are those of the whole step), else the row-statistics kernel
+k_stats.  It is timed with HIP events that spec_verify records on the call's
+stream at the dispatch's own start and end, in every --event-every'th timed
+step (event records cost a few microseconds each, so they are not put into
+every step); the percentiles come from those steps.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama3]
+
+Other workloads (context lines, not the headline): tiny, tiny_greedy (1000
+one-request calls, launch-bound: microseconds per call), long_greedy,
+long_nkl, long_nkl_pos, ragged, tree, sample_llama3, topk_llama3.
 """
 import argparse
 import ctypes
@@ -29,16 +34,18 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
-sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
-# rocprofv3 HBM counter summaries of the dominant kernel on the Llama-3-shaped workload
-PROFILE_TRAFFIC = {"k_fused": os.path.join(ROOT, "profiles", "traffic_fused_llama3.txt"),
-                   "k_stats": os.path.join(ROOT, "profiles", "traffic_rowstats_llama3.txt")}
+# rocprofv3 HBM counter summaries of the dominant kernel, per workload
+PROFILE_DIR = os.path.join(ROOT, "profiles")
 KERNEL_SRC = os.path.join(ROOT, "draft_token_verification_05_amd", "csrc", "kernels.hip")
 
 WORKLOADS = {
     # name: (maker kwargs, mode, description)
+    "tiny": ({}, 0, "tiny stochastic verify: 1000 independent one-request steps, B=1, gamma=4, V=1000, fp32; "
+                    "one call per step"),
+    "tiny_greedy": ({}, 1, "tiny greedy verify: 1000 independent one-request steps, B=1, gamma=4, V=1000, fp32; "
+                           "one call per step"),
     "llama3": ({}, 0, "llama3-shaped stochastic verify: B=32, gamma=5, V=128256, bf16"),
     "long_greedy": ({"mode": 1}, 1, "long parallel drafts, greedy: B=64, gamma=16, V=128256, bf16"),
     "long_nkl": ({"mode": 2}, 2, "long parallel drafts, NKL delta=0.15, T=0.6: B=64, gamma=16, V=128256, bf16"),
@@ -63,12 +70,12 @@ def kernel_hash() -> str:
     return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
 
 
-def load_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, if it was taken on the current kernel source for that kernel
-    (else None)."""
-    path = PROFILE_TRAFFIC.get(kernel)
-    if path is None or not os.path.exists(path):
+def load_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 counter summary profiles/traffic_<workload>.txt, if it was taken
+    on the current kernel source for that kernel (else None)."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{workload}.txt")
+    if not os.path.exists(path):
         return None
     kv = {}
     for line in open(path):
@@ -104,6 +111,10 @@ class Hip:
             arr[i] = ev.value
         return arr
 
+    def record(self, ev, stream):
+        if self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
     def elapsed_ms(self, a, b) -> float:
         ms = ctypes.c_float()
         if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
@@ -113,6 +124,14 @@ class Hip:
     def destroy(self, arr):
         for e in arr:
             self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def pct_us(ms_values):
+    """p10 / median / p90 of a list of millisecond timings, in microseconds."""
+    import numpy as np
+    a = np.asarray(ms_values, np.float64) * 1e3
+    return {"p10": round(float(np.percentile(a, 10)), 3), "p50": round(float(np.median(a)), 3),
+            "p90": round(float(np.percentile(a, 90)), 3), "n": int(a.size)}
 
 
 def algorithmic_bytes(w, num_accepted):
@@ -136,11 +155,65 @@ def algorithmic_bytes(w, num_accepted):
 
 def make_workload(name):
     import synthetic
-    kw, _, _ = WORKLOADS[name]
+    kw, mode, _ = WORKLOADS[name]
+    if name in ("tiny", "tiny_greedy"):
+        return synthetic.make_tiny().with_mode(mode)
     maker = {"llama3": synthetic.make_llama3, "long_greedy": synthetic.make_long, "long_nkl": synthetic.make_long,
              "long_nkl_pos": synthetic.make_long, "ragged": synthetic.make_ragged, "tree": synthetic.make_tree}[name]
     w = maker(**kw)
     return w.with_positions() if name == "long_nkl_pos" else w
+
+
+def cpu_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"cpu_model": model, "nproc": avail}
+
+
+def run_probe(nbytes, launches=64, wgs_per_cu=4, pool_bytes=1 << 30):
+    """A plain read of nbytes (rounded down to 16 KB items) in the statistics
+    pass's pattern, from buffers rotated through >= 1 GiB so that the Infinity
+    Cache cannot serve them: per-launch times from the dispatch's own events."""
+    import numpy as np
+    import torch
+
+    import draft_token_verification_05_amd as sv
+
+    item = 16384
+    nb = max(item, nbytes // item * item)
+    slots = max(4, -(-pool_bytes // nb))
+    pool = torch.empty(slots * nb, dtype=torch.uint8, device="cuda:0")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    hip = Hip()
+    ev = hip.events(2 * launches)
+    for k in range(4):
+        st = sv.spec_read_probe(pool.data_ptr() + (k % slots) * nb, nb, wgs_per_cu, sink.data_ptr(),
+                                stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(sv.spec_verify_status_string(st))
+    for k in range(launches):
+        st = sv.spec_read_probe(pool.data_ptr() + (k % slots) * nb, nb, wgs_per_cu, sink.data_ptr(),
+                                stream.cuda_stream, ev[2 * k], ev[2 * k + 1])
+        if st != 0:
+            raise RuntimeError(sv.spec_verify_status_string(st))
+    torch.cuda.synchronize()
+    ms = np.array([hip.elapsed_ms(ev[2 * k], ev[2 * k + 1]) for k in range(launches)])
+    hip.destroy(ev)
+    del pool
+    med = float(np.median(ms))
+    return {"bytes": int(nb), "wgs_per_cu": wgs_per_cu, "us": pct_us(ms), "GBps": round(nb / (med * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(nb / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
 
 
 def sample_inputs(name):
@@ -176,7 +249,7 @@ def run_sample_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
         if topk:
             return sv.spec_topk_rows(copies[k % ncopies].data_ptr(), topk, out.data_ptr(), cfg)
         return sv.spec_sample_rows(copies[k % ncopies].data_ptr(), T.data_ptr(), u.data_ptr(), out.data_ptr(), cfg)
-    ws = torch.zeros(sv.spec_verify_workspace_size(cfg0), dtype=torch.uint8, device=dev)
+    ws = torch.empty(sv.spec_verify_workspace_size(cfg0), dtype=torch.uint8, device=dev)
     hip = Hip()
     sampled = list(range(0, steps, max(1, event_every)))
     ev = hip.events(4 * len(sampled))
@@ -195,12 +268,12 @@ def run_sample_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
         if st != 0:
             raise RuntimeError(sv.spec_verify_status_string(st))
     torch.cuda.synchronize()
-    hip.lib.hipEventRecord(ctypes.c_void_p(ev_all[0]), ctypes.c_void_p(stream.cuda_stream))
+    hip.record(ev_all[0], stream.cuda_stream)
     for k in range(steps):
         st = call(k, timed[k])
         if st != 0:
             raise RuntimeError(sv.spec_verify_status_string(st))
-    hip.lib.hipEventRecord(ctypes.c_void_p(ev_all[1]), ctypes.c_void_p(stream.cuda_stream))
+    hip.record(ev_all[1], stream.cuda_stream)
     torch.cuda.synchronize()
     total_ms = hip.elapsed_ms(ev_all[0], ev_all[1])
     ks = np.array([hip.elapsed_ms(ev[4 * n + 1], ev[4 * n + 2]) for n in range(len(sampled))])
@@ -209,30 +282,53 @@ def run_sample_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
     # one read of every row (sampling: plus the selection's re-read of one wave-chunk, 2048 tokens)
     nbytes = rows * V * 2 + (0 if topk else rows * min(V, 2048) * 2)
     return dict(desc=desc, rows=rows, V=V, ncopies=ncopies, ms_per_step=total_ms / steps, kernel_ms=float(ks.mean()),
-                bytes=nbytes, sampled=len(sampled), topk=topk)
+                kernel_pct=pct_us(ks), bytes=nbytes, sampled=len(sampled), topk=topk)
+
+
+def _step_args(sv, w, d, mode, out_tokens, out_num, out_nkl, stream, ws, events_ptr, positions, b=None):
+    """Arguments of one spec_verify call: the whole batch, or (b given) the
+    one-request step b of a packed batch, by pointer offsets into it."""
+    soft = mode in (0, 2)
+    dt = sv.SV_DTYPE_BF16 if w.dtype == "bf16" else sv.SV_DTYPE_F32
+    es = 2 if w.dtype == "bf16" else 4
+    if b is None:
+        B, R_d, t0, d0, b0 = w.batch, w.total_draft_rows, 0, 0, 0
+    else:
+        B, R_d, t0, d0, b0 = 1, int(w.gamma[b]), int(w.t_off[b]), int(w.d_off[b]), b
+    V = w.vocab
+    cfg = sv.make_config(B, V, dt, w.max_gamma, R_d, stream, ws.data_ptr(), ws.numel(), phase_events=events_ptr,
+                         nkl_position=0 if positions is None else positions.data_ptr() + 4 * d0,
+                         nkl_alpha=w.nkl_alpha, nkl_delta_max=w.nkl_delta_max)
+    a = (d["target"].data_ptr() + t0 * V * es, d["draft"].data_ptr() + d0 * V * es if soft else 0,
+         d["tokens"].data_ptr() + 4 * d0, d["gamma"].data_ptr() + 4 * b0,
+         d["temp"].data_ptr() + 4 * b0 if soft else 0, d["ua"].data_ptr() + 4 * d0 if mode == 0 else 0,
+         d["ur"].data_ptr() + 4 * b0 if mode == 0 else 0, mode, w.delta,
+         d["parents"].data_ptr() + 4 * d0 if mode == 3 else 0, out_tokens.data_ptr() + 4 * t0,
+         out_num.data_ptr() + 4 * b0, out_nkl.data_ptr() + 4 * d0 if mode == 2 else 0)
+    return a, cfg
 
 
 def run_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
     import numpy as np
     import torch
 
-    import synthetic
-    from parity import to_device
+    from synthetic import to_device
 
     import draft_token_verification_05_amd as sv
 
     _, mode, desc = WORKLOADS[name]
     w = make_workload(name)
+    per_request = name in ("tiny", "tiny_greedy")  # one call per one-request step
     dev = torch.device("cuda:0")
-    soft = mode in (0, 2)
     base = to_device(w)
     per_copy = w.logit_bytes()
-    ncopies = max(2, min(64, -(-copies_bytes // per_copy)))
+    ncopies = 1 if per_request else max(2, min(64, -(-copies_bytes // per_copy)))
     copies = [base] + [{k: (None if v is None else v.clone()) for k, v in base.items()} for _ in range(ncopies - 1)]
     B, V, R_d = w.batch, w.vocab, w.total_draft_rows
     stream = torch.cuda.current_stream(dev)
-    cfg0 = sv.make_config(B, V, sv.SV_DTYPE_BF16 if w.dtype == "bf16" else sv.SV_DTYPE_F32, w.max_gamma, R_d)
-    ws = torch.zeros(max(sv.spec_verify_workspace_size(cfg0), 256), dtype=torch.uint8, device=dev)
+    dt = sv.SV_DTYPE_BF16 if w.dtype == "bf16" else sv.SV_DTYPE_F32
+    cfg0 = sv.make_config(1 if per_request else B, V, dt, w.max_gamma, int(w.gamma[0]) if per_request else R_d)
+    ws = torch.empty(max(sv.spec_verify_workspace_size(cfg0), 256), dtype=torch.uint8, device=dev)
     out_tokens = torch.empty(R_d + B, dtype=torch.int32, device=dev)
     out_num = torch.empty(B, dtype=torch.int32, device=dev)
     out_nkl = torch.empty(max(R_d, 1), dtype=torch.float32, device=dev)
@@ -240,54 +336,52 @@ def run_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
     sampled = list(range(0, steps, max(1, event_every)))
     ev = hip.events(4 * len(sampled))
     ev_all = hip.events(2)
-
     positions = None if w.nkl_position is None else torch.from_numpy(w.nkl_position).to(dev)
-
-    def make_args(d, events_ptr):
-        cfg = sv.make_config(B, V, cfg0.dtype, w.max_gamma, R_d, stream.cuda_stream, ws.data_ptr(), ws.numel(),
-                             phase_events=events_ptr,
-                             nkl_position=0 if positions is None else positions.data_ptr(),
-                             nkl_alpha=w.nkl_alpha, nkl_delta_max=w.nkl_delta_max)
-        a = (d["target"].data_ptr(), d["draft"].data_ptr() if soft else 0, d["tokens"].data_ptr(),
-             d["gamma"].data_ptr(), d["temp"].data_ptr() if soft else 0, d["ua"].data_ptr() if mode == 0 else 0,
-             d["ur"].data_ptr() if mode == 0 else 0, mode, w.delta,
-             d["parents"].data_ptr() if mode == 3 else 0, out_tokens.data_ptr(), out_num.data_ptr(),
-             out_nkl.data_ptr() if mode == 2 else 0)
-        return a, cfg
-
-    plain = [make_args(d, 0) for d in copies]
     ev_base = ctypes.addressof(ev)
-    timed = [make_args(copies[k % ncopies], ev_base + 4 * (k // event_every) * ctypes.sizeof(ctypes.c_void_p))
-             if k % event_every == 0 else plain[k % ncopies] for k in range(steps)]
-    for k in range(warmup):
-        a, cfg = plain[k % ncopies]
+
+    def args(k, events_ptr):
+        d = copies[k % ncopies]
+        return _step_args(sv, w, d, mode, out_tokens, out_num, out_nkl, stream.cuda_stream, ws, events_ptr, positions,
+                          b=(k % B) if per_request else None)
+
+    nplain = B if per_request else ncopies
+    plain = [args(k, 0) for k in range(nplain)]
+    timed = [args(k, ev_base + 4 * (k // event_every) * ctypes.sizeof(ctypes.c_void_p))
+             if k % event_every == 0 else plain[k % nplain] for k in range(steps)]
+    for k in range(max(warmup, B if per_request else 0)):
+        a, cfg = plain[k % nplain]
         st = sv.spec_verify(*a, cfg)
         if st != 0:
             raise RuntimeError(sv.spec_verify_status_string(st))
     torch.cuda.synchronize()
     num_acc = out_num.cpu().numpy()
     t0 = time.perf_counter()
-    hip.lib.hipEventRecord(ctypes.c_void_p(ev_all[0]), ctypes.c_void_p(stream.cuda_stream))
+    hip.record(ev_all[0], stream.cuda_stream)
     for k in range(steps):
         a, cfg = timed[k]
         st = sv.spec_verify(*a, cfg)
         if st != 0:
             raise RuntimeError(sv.spec_verify_status_string(st))
-    hip.lib.hipEventRecord(ctypes.c_void_p(ev_all[1]), ctypes.c_void_p(stream.cuda_stream))
+    hip.record(ev_all[1], stream.cuda_stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = hip.elapsed_ms(ev_all[0], ev_all[1])
-    rs = np.array([hip.elapsed_ms(ev[4 * n + 1], ev[4 * n + 2]) for n in range(len(sampled))])
+    ks = np.array([hip.elapsed_ms(ev[4 * n + 1], ev[4 * n + 2]) for n in range(len(sampled))])
+    st_ms = np.array([hip.elapsed_ms(ev[4 * n + 0], ev[4 * n + 3]) for n in range(len(sampled))])
     hip.destroy(ev)
     hip.destroy(ev_all)
     rowstats_bytes, step_bytes = algorithmic_bytes(w, num_acc)
-    positions = int(w.gamma.sum())
+    positions_total = int(w.gamma.sum())
+    if per_request:  # per call: one request's share
+        rowstats_bytes, step_bytes = rowstats_bytes / B, step_bytes / B
+        positions_total = positions_total / B
     # events [1] and [2] bracket the single dispatch of the whole step when
     # the library runs it as one kernel, else the row-statistics kernel
     single = sv.spec_verify_single_dispatch(cfg0, mode) == 1
     return dict(w=w, desc=desc, mode=mode, steps=steps, ncopies=ncopies, total_ms=total_ms, wall_s=wall,
-                ms_per_step=total_ms / steps, rowstats_ms=float(rs.mean()), rowstats_med_ms=float(np.median(rs)),
-                rowstats_bytes=rowstats_bytes, step_bytes=step_bytes, positions=positions, sampled=len(sampled),
+                ms_per_step=total_ms / steps, kernel_ms=float(ks.mean()), kernel_pct=pct_us(ks),
+                step_pct=pct_us(st_ms), rowstats_bytes=rowstats_bytes, step_bytes=step_bytes,
+                positions=positions_total, sampled=len(sampled), per_request=per_request,
                 kernel="k_fused" if single else "k_stats", kernel_bytes=step_bytes if single else rowstats_bytes)
 
 
@@ -306,7 +400,7 @@ def cpu_baseline_sample(name, budget_s=8.0, topk=0):
         if el >= budget_s:
             break
     return {"value": rows.shape[0] * reps / el, "unit": ("top-3 draft rows/s" if topk else "sampled draft tokens/s"),
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "kind": "oracle", **cpu_info(),
             "sample": f"{reps} full passes over the {rows.shape[0]} rows, {el:.1f} s wall on {threads} host threads"}
 
 
@@ -323,7 +417,7 @@ def cpu_baseline(name, budget_s=8.0):
         if el >= budget_s:
             break
     pos = int(w.gamma.sum()) * reps
-    return {"value": pos / el, "unit": "verified draft positions/s", "cores": threads, "kind": "oracle",
+    return {"value": pos / el, "unit": "verified draft positions/s", "cores": threads, "kind": "oracle", **cpu_info(),
             "sample": f"{reps} full batches of the {name} workload ({int(w.gamma.sum())} positions each), "
                       f"{el:.1f} s wall on {threads} host threads"}
 
@@ -335,6 +429,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="llama3", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-probe", action="store_true", help="skip the plain-read probe")
     ap.add_argument("--event-every", type=int, default=8, metavar="N",
                     help="record the per-kernel phase events in every N-th timed step")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
@@ -370,15 +465,25 @@ def main():
                          "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
                          "bytes_per_launch": r["bytes"], "avg_launch_us": round(r["kernel_ms"] * 1e3, 3),
-                         "timed_launches": r["sampled"]},
+                         "launch_us": r["kernel_pct"], "timed_launches": r["sampled"]},
+            "probe": None if args.no_probe else run_probe(r["bytes"]),
             "cpu_baseline": None if args.no_cpu else cpu_baseline_sample(args.workload, topk=r["topk"]),
         }), flush=True)
         return
     r = run_gpu(args.workload, args.steps, args.warmup, event_every=max(1, args.event_every))
     w = r["w"]
     value = r["positions"] / (r["ms_per_step"] * 1e-3)
-    achieved = r["kernel_bytes"] / (r["rowstats_ms"] * 1e-3) / 1e9
-    traffic = load_traffic(r["kernel"]) if args.workload == "llama3" else None
+    achieved = r["kernel_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+    traffic = load_traffic(r["kernel"], args.workload)
+    probe = None if (args.no_probe or r["per_request"]) else run_probe(int(r["kernel_bytes"]))
+    config = {"workload": r["desc"], "batch": 1 if r["per_request"] else w.batch, "gamma": int(w.gamma.max()),
+              "vocab": w.vocab, "logits": w.dtype, "mode": ["stochastic", "greedy", "nkl", "tree"][r["mode"]],
+              "positions_per_step": r["positions"], "input_copies_rotated": r["ncopies"],
+              "step_GBps": round(r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1),
+              "step_frac_of_peak": round(r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+              "step_us": r["step_pct"]}
+    if r["per_request"]:
+        config["us_per_call"] = round(r["ms_per_step"] * 1e3, 3)
     line = {
         "metric": "verified draft positions/sec at V=128256 (bf16); achieved HBM GB/s vs peak",
         "value": round(value, 1),
@@ -392,17 +497,17 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": r["desc"], "batch": w.batch, "gamma": int(w.gamma.max()), "vocab": w.vocab,
-                   "logits": w.dtype, "mode": ["stochastic", "greedy", "nkl", "tree"][r["mode"]],
-                   "positions_per_step": r["positions"], "input_copies_rotated": r["ncopies"],
-                   "step_GBps": round(r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1),
-                   "step_frac_of_peak": round(r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "config": config,
         "roofline": {"bound": "hbm", "kernel": r["kernel"], "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "bytes_per_launch": r["kernel_bytes"],
-                     "avg_launch_us": round(r["rowstats_ms"] * 1e3, 3), "timed_launches": r["sampled"]},
+                     "avg_launch_us": round(r["kernel_ms"] * 1e3, 3), "launch_us": r["kernel_pct"],
+                     "timed_launches": r["sampled"]},
+        "probe": probe,
         "cpu_baseline": None if args.no_cpu else cpu_baseline(args.workload),
     }
+    if probe:
+        line["roofline"]["frac_of_probe"] = round(achieved / probe["GBps"], 4)
     print(json.dumps(line), flush=True)
 
 

@@ -90,6 +90,8 @@ def _load() -> ctypes.CDLL:
     lib.spec_verify_single_dispatch.argtypes = [ctypes.POINTER(sv_config), i32, i32]
     lib.spec_topk_rows.restype = ctypes.c_int
     lib.spec_topk_rows.argtypes = [P, i32, P, ctypes.POINTER(sv_config)]
+    lib.spec_read_probe.restype = ctypes.c_int
+    lib.spec_read_probe.argtypes = [P, ctypes.c_uint64, i32, P, P, P, P]
     lib.spec_sample_rows.restype = ctypes.c_int
     lib.spec_sample_rows.argtypes = [P, P, P, P, ctypes.POINTER(sv_config)]
     return lib
@@ -140,6 +142,14 @@ def spec_sample_rows(logits: int, temperature: int, u: int, out_tokens: int, cfg
 def spec_topk_rows(logits: int, k: int, out_idx: int, cfg: sv_config) -> int:
     """Raw binding of spec_topk_rows (device pointers as ints)."""
     return int(_lib.spec_topk_rows(logits or None, int(k), out_idx or None, ctypes.byref(cfg)))
+
+
+def spec_read_probe(buf: int, nbytes: int, wgs_per_cu: int, sink: int, stream: int = 0, ev_start: int = 0,
+                    ev_stop: int = 0) -> int:
+    """Measurement aid (include/specverify_probe.h): a plain read of nbytes of a
+    device buffer in the row-statistics pass's pattern.  Returns the status."""
+    return int(_lib.spec_read_probe(buf or None, int(nbytes), int(wgs_per_cu), sink or None, stream or None,
+                                    ev_start or None, ev_stop or None))
 
 
 def spec_verify_single_dispatch(cfg: sv_config, mode: int, with_nkl: bool = False) -> int:

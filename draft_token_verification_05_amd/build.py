@@ -22,7 +22,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-I",
 
 def sources():
     return [os.path.join(CSRC, s) for s in SOURCES] + [os.path.join(CSRC, "sv_internal.h"),
-                                                       os.path.join(INCLUDE, "specverify.h")]
+                                                       os.path.join(INCLUDE, "specverify.h"),
+                                                       os.path.join(INCLUDE, "specverify_probe.h")]
 
 
 def build(verbose: bool = False) -> str:

@@ -10,15 +10,16 @@
 #include <cstring>
 #include <mutex>
 
+#include "specverify_probe.h"
 #include "sv_internal.h"
 
 namespace {
 
 thread_local char g_hip_error[256] = "";
 
-// Polls of a statistics partial before a helper of the fused kernel computes
-// it itself (when cfg->wait_polls is 0): a few milliseconds, far above the
-// normal wait of a few microseconds.
+// Polls of a statistics partial (single dispatch) or of another helper's draw
+// record before a workgroup computes it itself (when cfg->wait_polls is 0): a
+// few milliseconds, far above the normal wait of a few microseconds.
 constexpr int32_t kDefaultWaitPolls = 4096;
 
 // Epochs that tag the fused kernel's partials and the helpers' arrival
@@ -239,8 +240,8 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   const int fused_grid =
       (mode == SV_MODE_STOCHASTIC && !p.want_kl && B <= sv::kLdsBatch) ? sv::plan_fused(p, vec) : 0;
   p.epoch = next_epoch();
+  p.wait_polls = cfg->wait_polls > 0 ? cfg->wait_polls : kDefaultWaitPolls;
   if (fused_grid > 0) {
-    p.wait_polls = cfg->wait_polls > 0 ? cfg->wait_polls : kDefaultWaitPolls;
     const int grid = fused_grid;
     if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e);
     if ((e = (hipError_t)sv::launch_fused(p, vec, grid, s, ev ? ev[1] : nullptr, ev ? ev[2] : nullptr)) !=
@@ -310,6 +311,7 @@ int spec_sample_rows(const void* logits, const float* temperature, const float* 
   p.cnt = reinterpret_cast<uint64_t*>(ws + L.off_cnt);
   p.part_c = reinterpret_cast<sv::PartC*>(ws + L.off_part_c);
   p.epoch = next_epoch();
+  p.wait_polls = cfg->wait_polls > 0 ? cfg->wait_polls : kDefaultWaitPolls;
   const bool vec = ((size_t)cfg->vocab * es) % 16 == 0 && aligned(logits, 16);
   sv::plan_sample(p, vec);
   hipStream_t s = static_cast<hipStream_t>(cfg->stream);
@@ -356,6 +358,16 @@ int spec_topk_rows(const void* logits, int32_t k, int32_t* out_idx, const sv_con
     return hip_fail(e);
   if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e);
   return SV_OK;
+}
+
+int spec_read_probe(const void* buf, uint64_t bytes, int32_t wgs_per_cu, void* sink, void* stream,
+                    void* ev_start, void* ev_stop) {
+  if (!buf || !sink || wgs_per_cu < 1 || wgs_per_cu > 32 || !aligned(buf, 16) || !aligned(sink, 4))
+    return SV_EINVAL;
+  if (bytes < 16384) return SV_EINVAL;
+  const hipError_t e = (hipError_t)sv::launch_read_probe(buf, (int64_t)bytes, wgs_per_cu, sink, stream, ev_start,
+                                                          ev_stop);
+  return e == hipSuccess ? SV_OK : hip_fail(e);
 }
 
 }  // extern "C"

@@ -41,7 +41,10 @@ constexpr int64_t chunk_t(int dtype) { return (int64_t)kThreads * kUT * elems_pe
 enum TermKind : int32_t { kTermNone = 0, kTermResidual = 1, kTermBonus = 2 };
 
 // Partial statistics of one task over the vocabulary chunks one workgroup of
-// the statistics pass streamed.  m_* are raw-logit maxima, s_* = sum
+// the statistics pass streamed.  The single dispatch (whose helpers read the
+// partials during the same dispatch) stores the same 48 bytes as six
+// self-tagged 64-bit words instead (m_t, s_t low and high half, m_d, s_d low
+// and high half, each (epoch << 32) | 32-bit payload).  m_* are raw-logit maxima, s_* = sum
 // 2^((x - m) L) with L = log2(e)/T, w = sum 2^((d - m_d) L) (d - t) and
 // z = sum 2^((d - m_d) L) |d - t| over the draft row, idx = lowest index
 // attaining m_t.  tag: the call's epoch, stored after the other fields by the
@@ -73,12 +76,11 @@ struct ReqFin {
   int32_t pending;  // positions queued; -1: the request failed its input checks
 };
 
-// Sums of the terminal draw over one (request, wave-chunk), in float64; a
-// slice of kThreads x kUT vectors holds four wave-chunks.
+// Record space of the terminal draw for one (request, wave-chunk); a slice of
+// kThreads x kUT vectors holds four wave-chunks.  Its first 32 bytes hold the
+// record as four self-tagged words (see the draw in kernels.hip).
 struct PartC {
-  double a, b, ap, bp;  // sum a, sum b, and the same over {y : a_y > k0 * b_y}
-  float m;              // chunk maximum (bonus draws)
-  int32_t pad[3];
+  uint64_t words[6];
 };
 
 struct Layout {
@@ -144,6 +146,7 @@ struct Params {
   int32_t nch;         // vocabulary chunks per task in the row-statistics pass
   int32_t stats_grid;  // workgroups of the row-statistics pass
   int32_t grp_log2;    // log2 of the lanes that merge one task's partials
+  int32_t maxseg;      // most statistics partials (segments) of one task
   int32_t helpers;     // k_decide workgroups per request (1 in greedy and tree modes)
   int32_t nslices;     // vocabulary slices per row (chunk_t elements each)
   int32_t slices_per_helper;
@@ -169,7 +172,7 @@ struct Params {
   // same call, wrapped back to zero by the last arrival
   uint32_t* cnt_kl;   // [B * kCntStride]
   ReqFin* req_fin;    // [B] completion record of the KL second pass
-  PartC* part_c;      // [B * nslices * 4] draw sums per wave-chunk
+  PartC* part_c;      // [B * nslices * 4] draw records per wave-chunk
   RefItem* ref_list;  // [R_d] positions queued for the KL second pass (hdr[1] of them)
   int32_t* kl_need;   // [R_d] 1 where the KL of the position comes from the second pass
   int32_t* tidx;      // [R_d + B] argmax of every target row (NKL)
@@ -205,5 +208,8 @@ int launch_sample(const Params& p, bool vec, void* stream, void* ev_start, void*
 int plan_topk(Params& p, bool vec);
 int launch_topk(const Params& p, bool vec, void* stream, void* ev_start, void* ev_stop);
 int launch_fused(const Params& p, bool vec, int grid, void* stream, void* ev_start, void* ev_stop);
+// plain-read probe over `bytes` (a multiple of 16 KB is read) with wgs_per_cu workgroups per CU
+int launch_read_probe(const void* buf, int64_t bytes, int wgs_per_cu, void* sink, void* stream, void* ev_start,
+                      void* ev_stop);
 
 }  // namespace sv

@@ -386,6 +386,29 @@ def make(name: str, **kw) -> Workload:
     return WORKLOADS[name](**kw)
 
 
+def to_device(w: Workload, dev: str = "cuda:0") -> dict:
+    """Copies a workload's arrays to the GPU as torch tensors (bf16 logits keep
+    their stored bit patterns).  Plain uploads, nothing else."""
+    import torch
+    if w.dtype == "bf16":
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+    return dict(
+        target=conv(w.target),
+        draft=None if w.draft is None else conv(w.draft),
+        tokens=i32(w.draft_tokens),
+        gamma=i32(w.gamma),
+        temp=f32(w.temperature),
+        ua=f32(w.u_accept),
+        ur=f32(w.u_resample),
+        parents=None if w.tree_parents is None else i32(w.tree_parents),
+        nkl_position=None if w.nkl_position is None else i32(w.nkl_position),
+    )
+
+
 def random_workload(seed: int, mode: int, B: int, V: int, dtype: str = "bf16", gmax: int = 6,
                     gmin: int = 0, scale: float = 3.0, spike: float = 8.0, sigma: float = 0.7,
                     temp_range=(0.5, 1.2), greedy_drafts: bool = False, ties: bool = False,

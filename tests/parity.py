@@ -17,29 +17,9 @@ from dataclasses import dataclass, field
 import numpy as np
 
 import oracle
+from synthetic import to_device  # noqa: F401  (re-exported for the tests)
 
 REL_TOL = 2e-5
-
-
-def to_device(w, dev="cuda:0"):
-    import torch
-    if w.dtype == "bf16":
-        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-    else:
-        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
-    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
-    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
-    return dict(
-        target=conv(w.target),
-        draft=None if w.draft is None else conv(w.draft),
-        tokens=i32(w.draft_tokens),
-        gamma=i32(w.gamma),
-        temp=f32(w.temperature),
-        ua=f32(w.u_accept),
-        ur=f32(w.u_resample),
-        parents=None if w.tree_parents is None else i32(w.tree_parents),
-        nkl_position=None if getattr(w, "nkl_position", None) is None else i32(w.nkl_position),
-    )
 
 
 def run_gpu(w, d=None, diagnostics=True, out_nkl=False, max_gamma=None, workspace=None, wait_polls=0):
