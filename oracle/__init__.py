@@ -20,7 +20,7 @@ import numpy as np
 
 from . import build as _build
 
-STOCHASTIC, GREEDY, NKL, TREE_GREEDY = 0, 1, 2, 3
+STOCHASTIC, GREEDY, NKL, TREE_GREEDY, BLOCK = 0, 1, 2, 3, 4
 
 FLAG_ACCEPT_BAND = 1
 FLAG_DRAW_BAND = 2
@@ -41,8 +41,8 @@ def _load():
         P = ctypes.c_void_p
         i32, i64, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
         lib.sv_oracle_verify.restype = ctypes.c_int
-        lib.sv_oracle_verify.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, i32, f32, P, f32, f32, P, i32, i64,
-                                         P, P, P, P, P, P, P, P, P, P, P, i32]
+        lib.sv_oracle_verify.argtypes = [P, P, i32, i32, i32, P, P, P, P, P, i32, f32, P, f32, f32, P, i32, i32,
+                                         i64, P, P, P, P, P, P, P, P, P, P, P, i32]
         lib.sv_oracle_sample_rows.restype = ctypes.c_int
         lib.sv_oracle_sample_rows.argtypes = [P, i32, i64, i32, P, P, P, P, i32]
         lib.sv_oracle_topk_rows.restype = ctypes.c_int
@@ -126,10 +126,11 @@ def verify(target: np.ndarray, draft: Optional[np.ndarray], dtype: str, gamma: n
            tree_parents: Optional[np.ndarray] = None, max_gamma: Optional[int] = None,
            total_draft_rows: Optional[int] = None, nthreads: int = 0,
            nkl_position: Optional[np.ndarray] = None, nkl_alpha: float = 0.0,
-           nkl_delta_max: float = 0.0) -> OracleResult:
+           nkl_delta_max: float = 0.0, block_min_len: int = 3) -> OracleResult:
     """Runs the oracle on host arrays (the packed layout of the C ABI).
     nkl_position (NKL mode): 0-based position of every draft token in the
-    generated sequence, for the position-adaptive threshold (None: constant)."""
+    generated sequence, for the position-adaptive threshold (None: constant).
+    block_min_len (block-accept mode): the shortest agreeing run that is kept."""
     lib = _load()
     gamma = np.ascontiguousarray(gamma, np.int32)
     B = int(gamma.shape[0])
@@ -171,7 +172,8 @@ def verify(target: np.ndarray, draft: Optional[np.ndarray], dtype: str, gamma: n
     dm = np.full(B, np.inf)
     rc = lib.sv_oracle_verify(_ptr(target), _ptr(draft), dt, B, V, _ptr(draft_tokens), _ptr(gamma),
                               _ptr(temperature), _ptr(u_accept), _ptr(u_resample), int(mode), float(delta),
-                              _ptr(nkl_position), float(nkl_alpha), float(nkl_delta_max), _ptr(tree_parents), int(max_gamma), int(total_draft_rows), _ptr(out_tokens),
+                              _ptr(nkl_position), float(nkl_alpha), float(nkl_delta_max), _ptr(tree_parents),
+                              int(block_min_len), int(max_gamma), int(total_draft_rows), _ptr(out_tokens),
                               _ptr(out_num), _ptr(nkl), _ptr(p_x), _ptr(q_x), _ptr(alpha), _ptr(resid),
                               _ptr(tnode), _ptr(flags), _ptr(am), _ptr(dm), int(nthreads))
     if rc != 0:
@@ -184,4 +186,5 @@ def verify_workload(w, nthreads: int = 0) -> OracleResult:
     """Convenience: runs the oracle on a ``synthetic.Workload``-like object."""
     return verify(w.target, w.draft, w.dtype, w.gamma, w.draft_tokens, w.temperature, w.u_accept,
                   w.u_resample, w.mode, w.delta, w.tree_parents, w.max_gamma, w.total_draft_rows, nthreads,
-                  getattr(w, "nkl_position", None), getattr(w, "nkl_alpha", 0.0), getattr(w, "nkl_delta_max", 0.0))
+                  getattr(w, "nkl_position", None), getattr(w, "nkl_alpha", 0.0), getattr(w, "nkl_delta_max", 0.0),
+                  getattr(w, "block_min_len", 3))

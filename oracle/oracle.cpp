@@ -38,6 +38,15 @@
 //    (so the first token has delta_i = delta, as in the page's examples).
 //  * Row sampling (sv_oracle_sample_rows): the drafter's draw of a token from
 //    softmax(x/T) of one row, by the same inverse CDF.
+//  * Block-accept mode ("Chain of Draft" page, section 3.3 Block-Accept Mode,
+//    and section 2.2 "block mode": accept runs of >= 3 agreeing tokens): with
+//    agreement a_i = [d_i == argmax of target row i], i < gamma, take the
+//    first (lowest start) longest run of consecutive agreements; if it has at
+//    least min_len positions and ends at e, the draft tokens before e are kept
+//    (including any before the run, as the page's listing keeps them) and the
+//    target row e gives the next token (its argmax); with no such run nothing
+//    is kept and slot 0 gets the argmax of target row 0.  The strict
+//    token-by-token policy of the same section is greedy mode.
 //  * Tree mode ("Parallel Drafting" page, section 2.2 tree draft; Gemma-4 MTP
 //    page, section 6.2 "longest accepted path"): node n (parent pi(n)) is
 //    accepted iff its parent is accepted and its token equals argmax of the
@@ -62,7 +71,7 @@
 
 namespace {
 
-enum { M_STOCH = 0, M_GREEDY = 1, M_NKL = 2, M_TREE = 3 };
+enum { M_STOCH = 0, M_GREEDY = 1, M_NKL = 2, M_TREE = 3, M_BLOCK = 4 };
 enum { FLAG_ACCEPT_BAND = 1, FLAG_DRAW_BAND = 2, FLAG_NKL_BAND = 4, FLAG_EMPTY_RESIDUAL = 8, FLAG_INVALID = 16 };
 
 const double kNaN = std::numeric_limits<double>::quiet_NaN();
@@ -160,6 +169,7 @@ struct Args {
   const int32_t* nkl_position;  // NULL: the constant threshold delta
   float nkl_alpha, nkl_delta_max;
   const int32_t* parents;
+  int32_t block_min_len;  // block-accept mode: shortest run that is kept
   int32_t max_gamma;
   int32_t* out_tokens;
   int32_t* out_num_accepted;
@@ -223,7 +233,8 @@ void verify_request(const Args& a, int32_t b, int64_t t0, int64_t d0) {
 
   int32_t flags = 0;
   std::vector<double> xt, xd, lt, ld;
-  const double T = (double)a.temperature[b];
+  // temperatures are read in the soft modes only (greedy, tree and block modes may pass none)
+  const double T = (a.mode == M_STOCH || a.mode == M_NKL) ? (double)a.temperature[b] : 1.0;
   int32_t j = g;          // first failing position
   int32_t terminal = -1;  // token emitted at slot j
 
@@ -324,6 +335,25 @@ void verify_request(const Args& a, int32_t b, int64_t t0, int64_t d0) {
     }
     load_row(a.target, a.dtype, t0 + j, V, xt);
     terminal = argmax_row(xt);
+  } else if (a.mode == M_BLOCK) {
+    // the argmax of every target row, then the first longest run of
+    // positions whose draft token equals it
+    std::vector<int32_t> am((size_t)g + 1);
+    for (int32_t i = 0; i <= g; ++i) {
+      load_row(a.target, a.dtype, t0 + i, V, xt);
+      am[(size_t)i] = argmax_row(xt);
+    }
+    int32_t best_len = 0, best_start = 0;
+    for (int32_t start = 0; start < g; ++start) {
+      int32_t len = 0;
+      while (start + len < g && a.tokens[d0 + start + len] == am[(size_t)(start + len)]) ++len;
+      if (len > best_len) {
+        best_len = len;
+        best_start = start;
+      }
+    }
+    j = best_len >= a.block_min_len ? best_start + best_len : 0;
+    terminal = am[(size_t)j];
   } else {  // tree
     const int32_t N = g + 1;
     std::vector<int32_t> am((size_t)N), depth((size_t)N, 0);
@@ -370,15 +400,17 @@ extern "C" {
 //   draft token in the generated sequence; the threshold of token i is then
 //   min(nkl_delta_max, delta * (1 + nkl_alpha * log2(pos_i + 1))), and a negative
 //   position makes its request invalid.
+//   block_min_len (block-accept mode): the shortest run of agreeing positions that is kept (>= 1).
 int sv_oracle_verify(const void* target_logits, const void* draft_logits, int32_t dtype, int32_t batch,
                      int32_t vocab, const int32_t* draft_tokens, const int32_t* gamma_per_req,
                      const float* temperature, const float* u_accept, const float* u_resample, int32_t mode,
                      float delta, const int32_t* nkl_position, float nkl_alpha, float nkl_delta_max,
-                     const int32_t* tree_parents, int32_t max_gamma, int64_t total_draft_rows,
+                     const int32_t* tree_parents, int32_t block_min_len, int32_t max_gamma, int64_t total_draft_rows,
                      int32_t* out_tokens, int32_t* out_num_accepted, double* out_nkl, double* out_p_x,
                      double* out_q_x, double* out_alpha, double* out_resid_mass, int32_t* out_tree_node,
                      int32_t* out_flags, double* out_accept_margin, double* out_draw_margin, int32_t nthreads) {
-  if (batch <= 0 || vocab <= 0 || (dtype != 0 && dtype != 1) || mode < 0 || mode > 3) return -1;
+  if (batch <= 0 || vocab <= 0 || (dtype != 0 && dtype != 1) || mode < 0 || mode > 4) return -1;
+  if (mode == M_BLOCK && block_min_len < 1) return -1;
   if (!target_logits || !gamma_per_req || !out_tokens || !out_num_accepted) return -1;
   if ((mode == M_STOCH || mode == M_NKL) && (!draft_logits || !temperature)) return -1;
   if (mode == M_STOCH && (!u_accept || !u_resample)) return -1;
@@ -389,7 +421,7 @@ int sv_oracle_verify(const void* target_logits, const void* draft_logits, int32_
 
   Args a{target_logits, draft_logits, dtype, batch, vocab, draft_tokens, gamma_per_req, temperature, u_accept,
          u_resample, mode, delta, mode == M_NKL ? nkl_position : nullptr, nkl_alpha, nkl_delta_max, tree_parents,
-         max_gamma, out_tokens, out_num_accepted, out_nkl, out_p_x,
+         block_min_len, max_gamma, out_tokens, out_num_accepted, out_nkl, out_p_x,
          out_q_x, out_alpha, out_resid_mass, out_tree_node, out_flags, out_accept_margin, out_draw_margin};
 
   std::vector<int64_t> t_off((size_t)batch + 1, 0), d_off((size_t)batch + 1, 0);

@@ -43,8 +43,8 @@ import numpy as np
 BASE_SEED = 20261202
 
 # verify modes (same numbering as the C ABI)
-STOCHASTIC, GREEDY, NKL, TREE_GREEDY = 0, 1, 2, 3
-MODE_NAMES = {STOCHASTIC: "stochastic", GREEDY: "greedy", NKL: "nkl", TREE_GREEDY: "tree"}
+STOCHASTIC, GREEDY, NKL, TREE_GREEDY, BLOCK = 0, 1, 2, 3, 4
+MODE_NAMES = {STOCHASTIC: "stochastic", GREEDY: "greedy", NKL: "nkl", TREE_GREEDY: "tree", BLOCK: "block"}
 
 # purposes of the random streams
 _P_TARGET, _P_SPIKE, _P_DNOISE, _P_DRAW, _P_UACC, _P_URES, _P_PARAM, _P_POS = range(8)
@@ -109,6 +109,8 @@ class Workload:
     nkl_position: Optional[np.ndarray] = None  # int32 [sum(gamma)]
     nkl_alpha: float = 0.0
     nkl_delta_max: float = 0.0
+    # block-accept mode: the shortest run of agreeing positions that is kept
+    block_min_len: int = 3
 
     @property
     def total_draft_rows(self) -> int:

@@ -540,6 +540,88 @@ def test_nkl_negative_position_marks_only_its_request():
 
 
 # --------------------------------------------------------------------------
+# block-accept mode ("Chain of Draft" page, sections 2.2 and 3.3)
+# --------------------------------------------------------------------------
+
+BLK = oracle.BLOCK
+
+
+def _onehot_rows(argmax, V, tie_at=None):
+    """Target rows whose maximum is at `argmax` (and, tied, at `tie_at`)."""
+    rows = np.zeros((len(argmax), V), np.float32)
+    for i, a in enumerate(argmax):
+        rows[i, a] = 5.0
+        if tie_at is not None:
+            rows[i, tie_at[i]] = 5.0
+    return rows
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_accept_golden(dtype):
+    g = json.load(open(os.path.join(GOLD, "block_accept.json")))
+    V = g["vocab"]
+    for case in g["cases"]:
+        rows = _onehot_rows(case["argmax"], V, case.get("tie_at"))
+        tgt = f32_to_bf16_bits(rows) if dtype == "bf16" else rows
+        r = oracle.verify(tgt, None, dtype, np.array([len(case["draft"])], np.int32),
+                          np.array(case["draft"], np.int32), None, None, None, BLK, block_min_len=case["min_len"])
+        assert r.num_accepted[0] == case["num_accepted"], case["name"]
+        assert r.tokens.tolist() == case["tokens"], case["name"]
+
+
+def _runs_reference(flags, min_len):
+    """End of the first longest run of 1s (regular expression over the
+    flags), or 0 when it is shorter than min_len."""
+    import re
+    text = "".join("1" if f else "0" for f in flags)
+    best = None
+    for m in re.finditer("1+", text):
+        if best is None or len(m.group(0)) > len(best.group(0)):
+            best = m
+    return best.end() if best is not None and len(best.group(0)) >= min_len else 0
+
+
+@pytest.mark.parametrize("min_len", [1, 2, 3, 4])
+def test_block_accept_every_agreement_pattern(min_len):
+    """Every agreement pattern of gamma = 0..10 positions, packed in one call:
+    the kept length equals the end of the first longest agreeing run (found by
+    a regular expression), the kept tokens are the draft's and the next token
+    is the target row's argmax."""
+    V = 8
+    gam, tgt_rows, drafts, expect = [], [], [], []
+    rng = np.random.default_rng(min_len)
+    for g in range(11):
+        for pat in range(1 << g):
+            flags = [(pat >> i) & 1 for i in range(g)]
+            am = rng.integers(0, V, g + 1)
+            d = [int(am[i]) if flags[i] else int((am[i] + 1 + rng.integers(0, V - 1)) % V) for i in range(g)]
+            gam.append(g)
+            tgt_rows.append(_onehot_rows(am, V))
+            drafts += d
+            e = _runs_reference(flags, min_len)
+            expect.append((e, d[:e] + [int(am[e])] + [-1] * (g - e)))
+    r = oracle.verify(np.concatenate(tgt_rows), None, "f32", np.array(gam, np.int32), np.array(drafts, np.int32),
+                      None, None, None, BLK, block_min_len=min_len)
+    t_off = np.concatenate([[0], np.cumsum(np.array(gam) + 1)])
+    for b, (e, toks) in enumerate(expect):
+        assert r.num_accepted[b] == e, b
+        assert r.tokens[t_off[b]:t_off[b + 1]].tolist() == toks, b
+
+
+def test_block_accept_equals_greedy_when_every_draft_agrees_and_rejects_bad_min_len():
+    w = synthetic.random_workload(seed=51, mode=G, B=20, V=3000, dtype="bf16", gmax=7, gmin=3, greedy_drafts=True)
+    tf = w.target_f32()
+    w.draft_tokens = np.concatenate([np.argmax(tf[w.t_off[b]: w.t_off[b] + w.gamma[b]], axis=1)
+                                     for b in range(w.batch)]).astype(np.int32)
+    rg = oracle.verify_workload(w)
+    rb = oracle.verify_workload(w.with_mode(BLK))
+    assert (rg.num_accepted == w.gamma).all()
+    assert np.array_equal(rg.tokens, rb.tokens) and np.array_equal(rg.num_accepted, rb.num_accepted)
+    with pytest.raises(ValueError):
+        oracle.verify(w.target, None, "bf16", w.gamma, w.draft_tokens, None, None, None, BLK, block_min_len=0)
+
+
+# --------------------------------------------------------------------------
 # tree mode: golden, brute force, chain == greedy
 # --------------------------------------------------------------------------
 
