@@ -22,7 +22,7 @@ every step); the percentiles come from those steps.
 
 Other workloads (context lines, not the headline): tiny, tiny_greedy (1000
 one-request calls, launch-bound: microseconds per call), long_greedy,
-long_nkl, long_nkl_pos, ragged, tree, sample_llama3, topk_llama3.
+long_nkl, long_nkl_pos, long_block, ragged, tree, sample_llama3, topk_llama3.
 """
 import argparse
 import ctypes
@@ -52,6 +52,8 @@ WORKLOADS = {
     "long_nkl_pos": ({"mode": 2}, 2, "long parallel drafts, NKL with the position-adaptive threshold (delta_base=0.15, "
                                       "alpha=0.08, cap 0.3; start positions ~U{0..4095}), T=0.6: B=64, gamma=16, "
                                       "V=128256, bf16"),
+    "long_block": ({"mode": 4}, 4, "long parallel drafts, block accept (runs of >= 3 agreeing tokens): B=64, "
+                                     "gamma=16, V=128256, bf16"),
     "ragged": ({}, 0, "large-batch ragged stochastic: B=256, gamma~U{1..8}, V=152064, bf16"),
     "tree": ({}, 3, "tree draft greedy verify: B=16, 16-node trees, V=128256, bf16"),
     # draft-side sampling (the step before verify): one token per draft row of the llama3 batch
@@ -159,7 +161,8 @@ def make_workload(name):
     if name in ("tiny", "tiny_greedy"):
         return synthetic.make_tiny().with_mode(mode)
     maker = {"llama3": synthetic.make_llama3, "long_greedy": synthetic.make_long, "long_nkl": synthetic.make_long,
-             "long_nkl_pos": synthetic.make_long, "ragged": synthetic.make_ragged, "tree": synthetic.make_tree}[name]
+             "long_nkl_pos": synthetic.make_long, "long_block": synthetic.make_long, "ragged": synthetic.make_ragged,
+             "tree": synthetic.make_tree}[name]
     w = maker(**kw)
     return w.with_positions() if name == "long_nkl_pos" else w
 
@@ -477,7 +480,7 @@ def main():
     traffic = load_traffic(r["kernel"], args.workload)
     probe = None if (args.no_probe or r["per_request"]) else run_probe(int(r["kernel_bytes"]))
     config = {"workload": r["desc"], "batch": 1 if r["per_request"] else w.batch, "gamma": int(w.gamma.max()),
-              "vocab": w.vocab, "logits": w.dtype, "mode": ["stochastic", "greedy", "nkl", "tree"][r["mode"]],
+              "vocab": w.vocab, "logits": w.dtype, "mode": ["stochastic", "greedy", "nkl", "tree", "block"][r["mode"]],
               "positions_per_step": r["positions"], "input_copies_rotated": r["ncopies"],
               "step_GBps": round(r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1),
               "step_frac_of_peak": round(r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

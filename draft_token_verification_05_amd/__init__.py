@@ -27,12 +27,12 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libspecverify.so")
 
 SV_OK, SV_EINVAL, SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP = 0, -1, -2, -3, -4
-SV_MODE_STOCHASTIC, SV_MODE_GREEDY, SV_MODE_NKL, SV_MODE_TREE_GREEDY = 0, 1, 2, 3
+SV_MODE_STOCHASTIC, SV_MODE_GREEDY, SV_MODE_NKL, SV_MODE_TREE_GREEDY, SV_MODE_BLOCK = 0, 1, 2, 3, 4
 SV_DTYPE_F32, SV_DTYPE_BF16 = 0, 1
 SV_MAX_GAMMA = 4096
 SV_NOALLOC_SCRATCH_BYTES = 16 << 20
 SV_NUM_PHASE_EVENTS = 4
-MODES = {"stochastic": 0, "greedy": 1, "nkl": 2, "tree": 3}
+MODES = {"stochastic": 0, "greedy": 1, "nkl": 2, "tree": 3, "block": 4}
 
 
 class sv_config(ctypes.Structure):
@@ -55,6 +55,7 @@ class sv_config(ctypes.Structure):
         ("nkl_position", ctypes.c_void_p),
         ("nkl_alpha", ctypes.c_float),
         ("nkl_delta_max", ctypes.c_float),
+        ("block_min_len", ctypes.c_int32),
     ]
 
 
@@ -104,11 +105,12 @@ def make_config(batch: int, vocab: int, dtype: int, max_gamma: int, total_draft_
                 workspace: int = 0, workspace_bytes: int = 0, out_p_x: int = 0, out_q_x: int = 0,
                 out_resid_mass: int = 0, out_tree_node: int = 0, phase_events: int = 0,
                 wait_polls: int = 0, nkl_position: int = 0, nkl_alpha: float = 0.0,
-                nkl_delta_max: float = 0.0) -> sv_config:
+                nkl_delta_max: float = 0.0, block_min_len: int = 0) -> sv_config:
     return sv_config(ctypes.sizeof(sv_config), int(batch), int(vocab), int(dtype), int(max_gamma), int(wait_polls),
                      int(total_draft_rows), stream or None, workspace or None, int(workspace_bytes),
                      out_p_x or None, out_q_x or None, out_resid_mass or None, out_tree_node or None,
-                     phase_events or None, nkl_position or None, float(nkl_alpha), float(nkl_delta_max))
+                     phase_events or None, nkl_position or None, float(nkl_alpha), float(nkl_delta_max),
+                     int(block_min_len))
 
 
 def spec_verify(target_logits: int, draft_logits: int, draft_tokens: int, gamma_per_req: int, temperature: int,
@@ -232,13 +234,14 @@ def verify(target_logits, draft_logits, draft_tokens, gamma_per_req, temperature
            u_resample=None, mode: int | str = SV_MODE_STOCHASTIC, delta: float = 0.15, tree_parents=None, *,
            max_gamma: Optional[int] = None, workspace=None, diagnostics: bool = False, out_nkl: bool = False,
            phase_events: int = 0, stream=None, wait_polls: int = 0, nkl_position=None, nkl_alpha: float = 0.0,
-           nkl_delta_max: float = 0.0) -> VerifyOutput:
+           nkl_delta_max: float = 0.0, block_min_len: int = 0) -> VerifyOutput:
     """Runs one verify step on device tensors (packed layout, see specverify.h).
 
     NKL mode: ``nkl_position`` (int32 [sum(gamma)] on the GPU, optional) gives
     every draft token's 0-based position in the generated sequence, for the
     position-adaptive threshold min(nkl_delta_max, delta * (1 + nkl_alpha *
-    log2(position + 1))).
+    log2(position + 1))).  Block mode: ``block_min_len`` is the shortest run of
+    agreeing positions that is kept (0: the page's 3).
 
     ``target_logits`` [sum(gamma+1), V] and ``draft_logits`` [sum(gamma), V] are
     torch.bfloat16 or torch.float32 on the GPU.  The call is asynchronous on
@@ -289,7 +292,8 @@ def verify(target_logits, draft_logits, draft_tokens, gamma_per_req, temperature
     if stream is None:
         stream = torch.cuda.current_stream(dev)
     cfg = make_config(B, V, dt, max_gamma, R_d, stream=int(stream.cuda_stream), wait_polls=wait_polls,
-                      nkl_position=_ptr(nkl_position), nkl_alpha=nkl_alpha, nkl_delta_max=nkl_delta_max)
+                      nkl_position=_ptr(nkl_position), nkl_alpha=nkl_alpha, nkl_delta_max=nkl_delta_max,
+                      block_min_len=block_min_len)
     need = spec_verify_workspace_size(cfg)
     if workspace is None:
         workspace = workspace_for(cfg, dev, stream)

@@ -44,8 +44,9 @@ int validate(const void* target, const void* draft, const int32_t* tokens, const
   if (!cfg || cfg->struct_size != sizeof(sv_config) || cfg->wait_polls < 0) return SV_EINVAL;
   if (cfg->batch <= 0 || cfg->vocab <= 0) return SV_EINVAL;
   if (cfg->dtype != SV_DTYPE_F32 && cfg->dtype != SV_DTYPE_BF16) return SV_EINVAL;
-  if (mode < SV_MODE_STOCHASTIC || mode > SV_MODE_TREE_GREEDY) return SV_EINVAL;
+  if (mode < SV_MODE_STOCHASTIC || mode > SV_MODE_BLOCK) return SV_EINVAL;
   if (cfg->max_gamma < 0) return SV_EINVAL;
+  if (mode == SV_MODE_BLOCK && cfg->block_min_len < 0) return SV_EINVAL;
   if (cfg->max_gamma > SV_MAX_GAMMA) return SV_EUNSUPPORTED;
   const int64_t R_d = cfg->total_draft_rows;
   if (R_d < 0 || R_d > (int64_t)cfg->batch * cfg->max_gamma) return SV_EINVAL;
@@ -150,7 +151,7 @@ int spec_verify_version(void) { return SPECVERIFY_VERSION; }
 int spec_verify_single_dispatch(const sv_config* cfg, int32_t mode, int32_t with_nkl) {
   if (!cfg || cfg->struct_size != sizeof(sv_config) || cfg->batch <= 0 || cfg->vocab <= 0 ||
       cfg->total_draft_rows < 0 || (cfg->dtype != SV_DTYPE_F32 && cfg->dtype != SV_DTYPE_BF16) ||
-      mode < SV_MODE_STOCHASTIC || mode > SV_MODE_TREE_GREEDY)
+      mode < SV_MODE_STOCHASTIC || mode > SV_MODE_BLOCK)
     return SV_EINVAL;
   if (mode != SV_MODE_STOCHASTIC || with_nkl || cfg->batch > sv::kLdsBatch) return 0;
   if (cfg->total_draft_rows * (int64_t)((cfg->vocab + sv::chunk_stats(cfg->dtype, mode) - 1) /
@@ -212,6 +213,7 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   p.nkl_alpha = cfg->nkl_alpha;
   p.nkl_dmax = cfg->nkl_delta_max;
   p.want_kl = (mode == SV_MODE_NKL || (mode == SV_MODE_STOCHASTIC && out_nkl)) ? 1 : 0;
+  p.block_min_len = cfg->block_min_len > 0 ? cfg->block_min_len : 3;  // 3: the page's min_block_len
   p.hdr = reinterpret_cast<int32_t*>(ws + L.off_hdr);
   p.d_off = reinterpret_cast<int32_t*>(ws + L.off_doff);
   p.pair2req = reinterpret_cast<int32_t*>(ws + L.off_pair2req);

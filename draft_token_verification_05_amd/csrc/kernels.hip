@@ -820,7 +820,7 @@ __device__ __forceinline__ void lane_reset(Lane& L) {
 // Rows of task d.task (request lookup for the modes whose tasks pair rows).
 template <int MODE, bool LDS>
 __device__ __forceinline__ void set_rows(const Params& p, const StatsShared& sh, int& b, Desc& d) {
-  if (MODE == SV_MODE_GREEDY || MODE == SV_MODE_TREE_GREEDY) {
+  if (MODE == SV_MODE_GREEDY || MODE == SV_MODE_TREE_GREEDY || MODE == SV_MODE_BLOCK) {
     d.trow = d.task;
     d.drow = 0;
     d.pair = 0;
@@ -1400,6 +1400,11 @@ struct TreeShared<SV_MODE_TREE_GREEDY> {
   int16_t par[SV_MAX_GAMMA + 1];
   int idx[SV_MAX_GAMMA + 1];  // argmax of each node's target row
 };
+template <>
+struct TreeShared<SV_MODE_BLOCK> {
+  int idx[SV_MAX_GAMMA + 1];  // argmax of each position's target row
+  int keep;                   // the kept prefix e, from thread 0's run scan
+};
 
 __device__ void finish_invalid(const Params& p, int b, int t0, int d0, int g) {
   for (int k = threadIdx.x; k <= g; k += kThreads) p.out_tokens[t0 + k] = -1;
@@ -1794,6 +1799,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
   int jidx = 0;
   bool bad = false;
   int n_queued = 0;  // positions queued for the KL second pass (helper 0)
+  int run = 0, best_run = 0, best_end = 0;  // block mode: agreeing runs (thread 0)
   int checked = 0;  // positions [0, checked) were checked inside the passes
   // the group leader's position data of the pass starting at `base`
   // (node ti of a tree is position ti - 1), and the per-position input checks
@@ -1838,7 +1844,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
     else r = merge_task<SOFT>(p, tbase + ti, has, pair, l, glog, Lhi);
     if (l == 0 && has) {
       const int idx = r.idx == INT_MAX ? 0 : r.idx;  // no element above the pad value: position 0
-      if constexpr (MODE == SV_MODE_TREE_GREEDY) tr.idx[ti] = idx;
+      if constexpr (MODE == SV_MODE_TREE_GREEDY || MODE == SV_MODE_BLOCK) tr.idx[ti] = idx;
       sh.mt[q] = r.mt;
       sh.md[q] = r.md;
       sh.st[q] = r.st;
@@ -1864,7 +1870,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
           if (MODE == SV_MODE_NKL && fabs(klv - nkl_delta<POS>(p, d0 + ti) * lnV) <= err) need = 1;
           kl = klv;
         }
-      } else if (MODE == SV_MODE_GREEDY) {
+      } else if (MODE == SV_MODE_GREEDY || MODE == SV_MODE_BLOCK) {
         acc = (ti < g && x == idx) ? 1 : 0;
       }
       sh.acc[q] = acc;
@@ -1910,7 +1916,18 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
         n_queued += sh.qcount;
       }
     }
-    if (MODE != SV_MODE_TREE_GREEDY) {
+    if (MODE == SV_MODE_BLOCK) {
+      // runs of agreeing positions, continued across passes by thread 0: a run
+      // replaces the best one only when strictly longer (the first longest wins)
+      if (tid == 0)
+        for (int q = 0; q < TPP && base + q < g; ++q) {
+          run = sh.acc[q] ? run + 1 : 0;
+          if (run > best_run) {
+            best_run = run;
+            best_end = base + q + 1;
+          }
+        }
+    } else if (MODE != SV_MODE_TREE_GREEDY) {
       const int cand = (tid < TPP && base + tid < ntask && !sh.acc[tid]) ? base + tid : INT_MAX;
       const int jp = block_min_int(cand, sh.red_i);
       if (j < 0 && jp != INT_MAX) {
@@ -1951,6 +1968,14 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
   }
   if constexpr (MODE == SV_MODE_TREE_GREEDY) {
     resolve_tree(p, b, g, t0, d0, tr, sh);
+    return;
+  }
+  if constexpr (MODE == SV_MODE_BLOCK) {
+    if (tid == 0) tr.keep = best_run >= p.block_min_len ? best_end : 0;
+    __syncthreads();
+    const int e = tr.keep;
+    for (int k = tid; k <= g; k += kThreads) p.out_tokens[t0 + k] = k < e ? p.tokens[d0 + k] : k == e ? tr.idx[e] : -1;
+    if (tid == 0) p.out_num[b] = e;
     return;
   }
   if (j < 0) j = g;  // every draft accepted
@@ -2358,7 +2383,8 @@ int stats_occupancy_mode(int mode, bool wz) {
     case SV_MODE_STOCHASTIC:
       return wz ? stats_occupancy<DT, VEC, SV_MODE_STOCHASTIC, true>()
                 : stats_occupancy<DT, VEC, SV_MODE_STOCHASTIC, false>();
-    case SV_MODE_GREEDY: return stats_occupancy<DT, VEC, SV_MODE_GREEDY, false>();
+    case SV_MODE_GREEDY:
+    case SV_MODE_BLOCK: return stats_occupancy<DT, VEC, SV_MODE_GREEDY, false>();  // the same pass
     case SV_MODE_NKL: return stats_occupancy<DT, VEC, SV_MODE_NKL, false>();
     default: return stats_occupancy<DT, VEC, SV_MODE_TREE_GREEDY, false>();
   }
@@ -2383,7 +2409,8 @@ void stats_dispatch(const Params& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1
       if (p.want_kl) stats_launch<DT, VEC, SV_MODE_STOCHASTIC, true>(p, s, e0, e1);
       else stats_launch<DT, VEC, SV_MODE_STOCHASTIC, false>(p, s, e0, e1);
       break;
-    case SV_MODE_GREEDY: stats_launch<DT, VEC, SV_MODE_GREEDY, false>(p, s, e0, e1); break;
+    case SV_MODE_GREEDY:
+    case SV_MODE_BLOCK: stats_launch<DT, VEC, SV_MODE_GREEDY, false>(p, s, e0, e1); break;  // argmax of every row
     case SV_MODE_NKL: stats_launch<DT, VEC, SV_MODE_NKL, false>(p, s, e0, e1); break;
     default: stats_launch<DT, VEC, SV_MODE_TREE_GREEDY, false>(p, s, e0, e1); break;
   }
@@ -2394,6 +2421,7 @@ void decide_dispatch(const Params& p, hipStream_t s) {
   switch (p.mode) {
     case SV_MODE_STOCHASTIC: hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_STOCHASTIC>), grid, blk, 0, s, p); break;
     case SV_MODE_GREEDY: hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_GREEDY>), grid, blk, 0, s, p); break;
+    case SV_MODE_BLOCK: hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_BLOCK>), grid, blk, 0, s, p); break;
     case SV_MODE_NKL:
       if (p.nkl_pos) hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_NKL, true>), grid, blk, 0, s, p);
       else hipLaunchKernelGGL((k_decide<DT, VEC, SV_MODE_NKL>), grid, blk, 0, s, p);

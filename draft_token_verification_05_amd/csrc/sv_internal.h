@@ -14,7 +14,7 @@ constexpr int kPrepThreads = 1024;
 // 16-byte vectors per thread per row per chunk in the row-statistics pass:
 // modes that stream one row per task use larger chunks (same bytes per chunk)
 constexpr int stats_vectors_per_thread(int mode) {
-  return (mode == SV_MODE_GREEDY || mode == SV_MODE_TREE_GREEDY) ? 4 : 2;
+  return (mode == SV_MODE_GREEDY || mode == SV_MODE_TREE_GREEDY || mode == SV_MODE_BLOCK) ? 4 : 2;
 }
 constexpr int kUA = 2;           // smallest of the above: sizes the partial arrays
 constexpr int kUT = 4;           // 16-byte vectors per thread per row in one slice of k_decide's second look
@@ -154,6 +154,7 @@ struct Params {
   const int32_t* nkl_pos;    // NKL: generation position of every draft row (NULL: constant delta)
   float nkl_alpha, nkl_dmax;  // NKL with positions: growth and cap of the threshold
   int32_t want_kl;  // compute KL(q || p) (NKL mode, or stochastic with out_nkl)
+  int32_t block_min_len;  // block-accept mode: shortest kept run (>= 1)
   uint32_t epoch;      // this call's tag: fused statistics partials and arrival counters (never 0 or ~0)
   int32_t wait_polls;  // fused kernel: polls of a partial before a helper computes it itself
   // workspace

@@ -27,6 +27,15 @@
  *       3.2: nkl_i = KL(q_i || p_i) / ln V at the request's temperature; x_i is
  *       accepted while nkl_i < delta; the first failing slot (or slot gamma_b)
  *       gets argmax(target row).
+ *   SV_MODE_BLOCK       Block accept -- "Chain of Draft" page, section 3.3
+ *       (Block-Accept Mode) and section 2.2 (block mode: runs of >= 3 agreeing
+ *       tokens): position i agrees when x_i == argmax(target_i) (lowest index
+ *       on ties).  The first longest run of consecutive agreeing positions, if
+ *       it has at least cfg->block_min_len positions and ends at e, keeps the
+ *       drafted tokens x_0..x_{e-1} (those before the run too) and slot e gets
+ *       argmax(target_e); with no such run slot 0 gets argmax(target_0) and
+ *       nothing is accepted.  (The page's strict token-by-token policy is
+ *       SV_MODE_GREEDY.)
  *   SV_MODE_TREE_GREEDY Greedy tree verification -- "Parallel Drafting" page,
  *       section 2.2 (tree drafts), Gemma-4 MTP page, section 6.2 (keep the
  *       longest accepted path): node n with parent pi(n) is accepted iff pi(n)
@@ -68,7 +77,7 @@
 extern "C" {
 #endif
 
-#define SPECVERIFY_VERSION 10100 /* 1.1.0: position-adaptive NKL threshold (sv_config.nkl_*) */
+#define SPECVERIFY_VERSION 10200 /* 1.2.0: block-accept mode (SV_MODE_BLOCK, sv_config.block_min_len) */
 
 /* status codes */
 #define SV_OK 0
@@ -82,6 +91,7 @@ extern "C" {
 #define SV_MODE_GREEDY 1
 #define SV_MODE_NKL 2
 #define SV_MODE_TREE_GREEDY 3
+#define SV_MODE_BLOCK 4
 
 /* logit element types */
 #define SV_DTYPE_F32 0
@@ -126,13 +136,17 @@ typedef struct sv_config {
   const int32_t* nkl_position;
   float nkl_alpha;
   float nkl_delta_max;
+  /* block-accept mode: the shortest run of agreeing positions that is kept (>= 0; 0 = 3, the
+   * page's min_block_len) */
+  int32_t block_min_len;
 } sv_config;
 
 /*
  * Verifies one batch.
  *
  * target_logits  [sum(gamma+1)][V] of cfg->dtype (bf16 = IEEE bfloat16 bit patterns).
- * draft_logits   [sum(gamma)][V]; read in stochastic and NKL modes only (may be NULL otherwise).
+ * draft_logits   [sum(gamma)][V]; read in stochastic and NKL modes only (may be NULL otherwise;
+ *                greedy, block and tree modes read target rows only).
  * draft_tokens   int32 [sum(gamma)]; must lie in [0, V).
  * gamma_per_req  int32 [B]; 0 <= gamma_b <= cfg->max_gamma.
  * temperature    float32 [B]; > 0 and finite (stochastic and NKL modes; may be NULL otherwise).
@@ -143,7 +157,8 @@ typedef struct sv_config {
  * tree_parents   int32 [sum(gamma)] (tree mode; may be NULL otherwise).
  * out_tokens     int32 [sum(gamma+1)], same offsets as the target rows: accepted tokens, then the
  *                terminal token, then -1 in the unused slots.
- * out_num_accepted int32 [B]: number of accepted draft tokens (tree: depth of the deepest accepted node).
+ * out_num_accepted int32 [B]: number of accepted draft tokens (tree: depth of the deepest accepted node;
+ *                block: the kept prefix e).
  * out_nkl        float32 [sum(gamma)]: nkl_i for every drafted position (required in NKL mode;
  *                in stochastic mode written when non-NULL).
  * cfg            see sv_config.

@@ -35,7 +35,8 @@ def run_gpu(w, d=None, diagnostics=True, out_nkl=False, max_gamma=None, workspac
                     max_gamma=w.max_gamma if max_gamma is None else max_gamma, diagnostics=diagnostics,
                     out_nkl=out_nkl, workspace=workspace, wait_polls=wait_polls,
                     nkl_position=d.get("nkl_position") if mode == 2 else None,
-                    nkl_alpha=getattr(w, "nkl_alpha", 0.0), nkl_delta_max=getattr(w, "nkl_delta_max", 0.0))
+                    nkl_alpha=getattr(w, "nkl_alpha", 0.0), nkl_delta_max=getattr(w, "nkl_delta_max", 0.0),
+                    block_min_len=getattr(w, "block_min_len", 3))
     torch.cuda.synchronize()
     host = lambda t: None if t is None else t.cpu().numpy()
     return dict(tokens=host(out.tokens), num=host(out.num_accepted), nkl=host(out.nkl), p_x=host(out.p_x),

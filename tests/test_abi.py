@@ -55,7 +55,7 @@ def test_library_exports_every_declared_symbol(sv):
 
 
 def test_version_and_status_strings(sv):
-    assert sv.spec_verify_version() == 10100
+    assert sv.spec_verify_version() == 10200
     for st in (0, -1, -2, -3, -4):
         assert sv.spec_verify_status_string(st).startswith("SV_")
     assert "unknown" in sv.spec_verify_status_string(7)
@@ -95,7 +95,7 @@ def test_synchronous_argument_errors(sv):
     assert call(sv, B=0) == E
     assert call(sv, V=0) == E
     assert call(sv, dtype=2) == E
-    assert call(sv, mode=4) == E
+    assert call(sv, mode=5) == E
     assert call(sv, mode=-1) == E
     assert call(sv, max_gamma=-1) == E
     assert call(sv, max_gamma=sv.SV_MAX_GAMMA + 1) == sv.SV_EUNSUPPORTED
@@ -159,6 +159,21 @@ def test_mode_specific_null_pointers_allowed(sv):
     assert call(sv, mode=0, parents=0, out_nkl=0, ws_bytes=16) == W
     # no drafted rows at all: token / draft / u_accept arrays may be NULL
     assert call(sv, mode=0, R_d=0, tokens=0, draft=0, ua=0, ws_bytes=16) == W
+    # block mode reads target rows and tokens only
+    assert call(sv, mode=4, draft=0, temp=0, ua=0, ur=0, parents=0, out_nkl=0, ws_bytes=16) == W
+    assert call(sv, mode=4, tokens=0) == sv.SV_EINVAL
+
+
+def test_block_min_len_argument(sv):
+    """Block mode: a negative shortest kept run is rejected (0 means 3); other
+    modes never read it."""
+    def blk(mode, n):
+        cfg = sv.make_config(4, 1000, 1, 4, 8, 0, FAKE, 16, block_min_len=n)
+        return sv.spec_verify(FAKE, 0, FAKE, FAKE, 0, 0, 0, mode, 0.15, 0, FAKE, FAKE, 0, cfg)
+
+    assert blk(4, 0) == sv.SV_EWORKSPACE and blk(4, 5) == sv.SV_EWORKSPACE
+    assert blk(4, -1) == sv.SV_EINVAL
+    assert blk(1, -1) == sv.SV_EWORKSPACE
 
 
 def test_sample_rows_argument_errors(sv):

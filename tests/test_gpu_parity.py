@@ -9,7 +9,7 @@ from parity import assert_parity, compare, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
-S, G, K, TR = 0, 1, 2, 3
+S, G, K, TR, BL = 0, 1, 2, 3, 4
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -245,6 +245,48 @@ def test_nkl_position_adaptive_second_pass_and_invalid():
 def test_tree(name):
     g, o, _ = check(synthetic.make(name))
     assert (g["tree_node"] == o.tree_node).all()
+
+
+# ---------------------------------------------------------------- block-accept mode
+
+def test_block_long_drafts():
+    """Block accept ("Chain of Draft" page, section 3.3) on the long-draft
+    workload (argmax drafts, noise ramping along the draft): bit-exact."""
+    g, o, _ = check(synthetic.make_long(mode=BL))
+    assert (g["num"] > 0).any()
+
+
+@pytest.mark.parametrize("V,dtype", [(1, "bf16"), (7, "f32"), (1000, "bf16"), (8193, "bf16"), (20000, "f32"),
+                                     (4099, "f32"), (152064, "bf16")])
+def test_block_ragged_small(V, dtype):
+    """Ragged gamma including 0, 1 and 2 (no run of three possible), drafts
+    close to the target's argmax so that runs form and break."""
+    w = synthetic.random_workload(seed=V % 71 + 300, mode=BL, B=21, V=V, dtype=dtype, gmax=12, gmin=0,
+                                  greedy_drafts=True, sigma=0.3)
+    check(w)
+
+
+@pytest.mark.parametrize("min_len", [1, 2, 5])
+def test_block_min_len(min_len):
+    w = synthetic.random_workload(seed=310 + min_len, mode=BL, B=30, V=30000, dtype="bf16", gmax=16, gmin=4,
+                                  greedy_drafts=True, sigma=0.4)
+    w.block_min_len = min_len
+    check(w)
+
+
+def test_block_runs_across_decision_passes_and_ties():
+    """Drafts of hundreds of positions (runs continue across decision passes)
+    and integer-valued logits (tied maxima: the lowest index is the target's
+    token), with an invalid token in one request."""
+    w = synthetic.random_workload(seed=320, mode=BL, B=4, V=3000, dtype="bf16", gmax=600, gmin=300,
+                                  greedy_drafts=True, sigma=0.05)
+    w.draft_tokens = w.draft_tokens.copy()
+    w.draft_tokens[w.d_off[2] + 5] = -4
+    g, o, _ = check(w)
+    assert g["num"][2] == -1
+    wt = synthetic.random_workload(seed=321, mode=BL, B=24, V=70000, dtype="bf16", gmax=9, gmin=2, scale=1.5,
+                                   spike=0.0, ties=True, greedy_drafts=True)
+    check(wt)
 
 
 # ---------------------------------------------------------------- edge cases
