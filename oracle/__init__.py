@@ -49,6 +49,8 @@ def _load():
         lib.sv_oracle_topk_rows.argtypes = [P, i32, i64, i32, i32, P, i32]
         lib.sv_oracle_nkl_threshold.restype = ctypes.c_double
         lib.sv_oracle_nkl_threshold.argtypes = [f32, f32, f32, i32]
+        lib.sv_oracle_consensus.restype = ctypes.c_int
+        lib.sv_oracle_consensus.argtypes = [P, i32, i32, i32, i32, P, P, f32, f32, P, P, P, P, i32]
         lib.sv_oracle_max_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -93,6 +95,40 @@ def topk_rows(logits: np.ndarray, dtype: str, k: int, nthreads: int = 0) -> np.n
     if _load().sv_oracle_topk_rows(_ptr(logits), dt, rows, V, int(k), _ptr(out), int(nthreads)) != 0:
         raise ValueError("sv_oracle_topk_rows rejected its arguments")
     return out[:rows]
+
+
+@dataclass
+class ConsensusResult:
+    nkl: np.ndarray    # float64 [positions, K, K]: KL(q_a || q_b) / ln V (NaN for invalid requests)
+    state: np.ndarray  # int32 [positions]: 1 consensus, 2 divergence, 0 neither, -1 invalid request
+    pair: np.ndarray   # int32 [positions]: a * K + b of the closest pair a < b (-1 invalid)
+    flags: np.ndarray  # int32 [positions]: 1 / 2 near a threshold, 4 near tie of the closest pair
+
+
+def consensus(drafts: np.ndarray, dtype: str, gamma: np.ndarray, K: int, temperature: np.ndarray,
+              delta_c: float = 0.1, delta_d: float = 0.15, nthreads: int = 0) -> ConsensusResult:
+    """Pairwise NKL of K drafts per position (rows [sum(gamma) * K, V], the K
+    drafts of a position consecutive) and the consensus / divergence state."""
+    gamma = np.ascontiguousarray(gamma, np.int32)
+    B, V = int(gamma.shape[0]), int(drafts.shape[1])
+    if dtype == "bf16":
+        drafts, dt = np.ascontiguousarray(drafts, np.uint16), 1
+    elif dtype == "f32":
+        drafts, dt = np.ascontiguousarray(drafts, np.float32), 0
+    else:
+        raise ValueError(dtype)
+    npos = int(gamma.astype(np.int64).sum())
+    temperature = np.ascontiguousarray(temperature, np.float32)
+    nkl = np.full((max(npos, 1), K, K), np.nan)
+    state = np.full(max(npos, 1), -7, np.int32)
+    pair = np.full(max(npos, 1), -7, np.int32)
+    flags = np.zeros(max(npos, 1), np.int32)
+    rc = _load().sv_oracle_consensus(_ptr(drafts), dt, B, int(K), V, _ptr(gamma), _ptr(temperature),
+                                     float(delta_c), float(delta_d), _ptr(nkl), _ptr(state), _ptr(pair),
+                                     _ptr(flags), int(nthreads))
+    if rc != 0:
+        raise ValueError("sv_oracle_consensus rejected its arguments")
+    return ConsensusResult(nkl[:npos], state[:npos], pair[:npos], flags[:npos])
 
 
 def nkl_threshold(delta: float, alpha: float, delta_max: float, position: int) -> float:

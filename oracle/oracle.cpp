@@ -512,6 +512,96 @@ int sv_oracle_topk_rows(const void* logits, int32_t dtype, int64_t rows, int32_t
   return 0;
 }
 
+// Consensus across K drafts ("Chain of Draft" page, section 4.4, Consensus-Aware
+// Accept: the pairwise NKL matrix of the drafts; some pair below 0.1 is a
+// consensus, every pair above 0.15 a divergence).  Request b has gamma_b
+// positions; position i of request b (packed index n = d_off[b] + i) holds K
+// draft rows, row n*K + a for draft a, all at the request's temperature.  Per
+// position:
+//   M[a][b] = KL(q_a || q_b) / ln V  (log space, Neumaier sums; 0 for V == 1),
+//   the distance of a pair a < b is the symmetrised s_ab = (M[a][b] + M[b][a]) / 2,
+//   pair = the pair with the smallest distance (lowest (a, b) on ties),
+//   state = 1 (consensus) if that distance < delta_c, 2 (divergence) if it is
+//   > delta_d (so every pair is), else 0.
+// Flags: 1 if the smallest distance lies within 1e-6 relative of delta_c, 2
+// within 1e-6 of delta_d, 4 if another pair's distance lies within 1e-6
+// relative of the smallest (the closest pair is then a near tie).  A request
+// with a temperature that is not > 0 and finite gets state -1, pair -1 and NaN
+// distances.  out_nkl: [positions][K][K] (diagonal 0).  Returns -1 on an
+// argument error.
+int sv_oracle_consensus(const void* draft_logits, int32_t dtype, int32_t batch, int32_t num_drafts, int32_t vocab,
+                        const int32_t* gamma_per_req, const float* temperature, float delta_c, float delta_d,
+                        double* out_nkl, int32_t* out_state, int32_t* out_pair, int32_t* out_flags,
+                        int32_t nthreads) {
+  const int32_t K = num_drafts;
+  if (batch <= 0 || vocab <= 0 || K < 2 || (dtype != 0 && dtype != 1)) return -1;
+  if (!draft_logits || !gamma_per_req || !temperature || !out_state || !out_pair) return -1;
+  std::vector<int64_t> d_off((size_t)batch + 1, 0);
+  for (int32_t b = 0; b < batch; ++b) {
+    if (gamma_per_req[b] < 0) return -1;
+    d_off[(size_t)b + 1] = d_off[(size_t)b] + gamma_per_req[b];
+  }
+  const int64_t npos = d_off[(size_t)batch];
+  const double lnV = std::log((double)vocab);
+#ifdef _OPENMP
+  if (nthreads <= 0) nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+  for (int64_t n = 0; n < npos; ++n) {
+    int32_t b = 0;
+    while (d_off[(size_t)b + 1] <= n) ++b;
+    double* M = out_nkl ? out_nkl + n * K * K : nullptr;
+    if (!t_ok(temperature[b])) {
+      out_state[n] = -1;
+      out_pair[n] = -1;
+      if (out_flags) out_flags[n] = FLAG_INVALID;
+      if (M)
+        for (int32_t k = 0; k < K * K; ++k) M[k] = kNaN;
+      continue;
+    }
+    const double T = (double)temperature[b];
+    std::vector<std::vector<double>> l((size_t)K);
+    std::vector<double> x;
+    for (int32_t a = 0; a < K; ++a) {
+      load_row(draft_logits, dtype, n * K + a, vocab, x);
+      log_softmax(x, T, l[(size_t)a]);
+    }
+    std::vector<double> m((size_t)K * K, 0.0);
+    for (int32_t a = 0; a < K; ++a)
+      for (int32_t c = 0; c < K; ++c) {
+        if (a == c) continue;
+        NSum kl;
+        for (int64_t y = 0; y < vocab; ++y)
+          kl.add(std::exp(l[(size_t)a][(size_t)y]) * (l[(size_t)a][(size_t)y] - l[(size_t)c][(size_t)y]));
+        m[(size_t)(a * K + c)] = vocab > 1 ? kl.value() / lnV : 0.0;
+      }
+    if (M)
+      for (int32_t k = 0; k < K * K; ++k) M[k] = m[(size_t)k];
+    double best = std::numeric_limits<double>::infinity();
+    int32_t pair = -1;
+    for (int32_t a = 0; a < K; ++a)
+      for (int32_t c = a + 1; c < K; ++c) {
+        const double sd = 0.5 * (m[(size_t)(a * K + c)] + m[(size_t)(c * K + a)]);
+        if (sd < best) {
+          best = sd;
+          pair = a * K + c;
+        }
+      }
+    int32_t flags = 0;
+    for (int32_t a = 0; a < K; ++a)
+      for (int32_t c = a + 1; c < K; ++c) {
+        const double sd = 0.5 * (m[(size_t)(a * K + c)] + m[(size_t)(c * K + a)]);
+        if (a * K + c != pair && std::fabs(sd - best) <= 1e-6 * best) flags |= 4;
+      }
+    if (std::fabs(best - (double)delta_c) < 1e-6 * (double)delta_c) flags |= 1;
+    if (std::fabs(best - (double)delta_d) < 1e-6 * (double)delta_d) flags |= 2;
+    out_state[n] = best < (double)delta_c ? 1 : (best > (double)delta_d ? 2 : 0);
+    out_pair[n] = pair;
+    if (out_flags) out_flags[n] = flags;
+  }
+  return 0;
+}
+
 // The position-adaptive NKL threshold of a draft token at 0-based position pos.
 double sv_oracle_nkl_threshold(float delta, float alpha, float delta_max, int32_t pos) {
   return nkl_threshold(delta, alpha, delta_max, pos);

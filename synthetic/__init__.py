@@ -371,6 +371,51 @@ def make_tree(B: int = 16, V: int = 128256, parents: np.ndarray = TREE_LITERAL16
                     tree_parents=tp, max_gamma=N - 1)
 
 
+def chains_parents(K: int, gamma: int) -> np.ndarray:
+    """Parent array of K chains of gamma nodes each under one root: chain k's
+    node i (0-based) has id 1 + k * gamma + i and follows the root (i = 0) or
+    the chain's previous node."""
+    par = np.empty(1 + K * gamma, np.int32)
+    par[0] = -1
+    for k in range(K):
+        for i in range(gamma):
+            n = 1 + k * gamma + i
+            par[n] = 0 if i == 0 else n - 1
+    return par
+
+
+def make_multi_draft(B: int = 16, K: int = 3, gamma: int = 6, V: int = 128256, seed: int = BASE_SEED, wid: int = 6,
+                     noise=(0.3, 0.7, 1.2), dtype: str = "bf16") -> Workload:
+    """Several draft models per request, verified together ("keep the longest
+    accepted path"): K chains of gamma drafts under a shared root, laid out as
+    a tree (parent array from chains_parents).  One target row per node
+    (3*N(0,1) + 8 spike: the target at the root and after each chain's
+    prefix); chain k drafts greedily from its own noisy copy of the target,
+    node token = argmax(target row of its parent + N(0, noise[k]^2))."""
+    parents = chains_parents(K, gamma)
+    N = len(parents)
+    gam = np.full(B, N - 1, np.int32)
+    tgt32 = _target_rows(wid, B * N, V, 3.0, 8.0, seed)
+    tgt = _round_store(tgt32, dtype)
+    tstored = tgt32 if dtype == "f32" else bf16_bits_to_f32(tgt)
+    del tgt32
+    tokens = np.zeros(B * (N - 1), np.int32)
+
+    def fn(b):
+        for n in range(1, N):
+            k = (n - 1) // gamma
+            g = _gen(wid, _P_DNOISE, b * N + n, seed)
+            d = tstored[b * N + parents[n]] + np.float32(noise[k % len(noise)]) * g.standard_normal(V, dtype=np.float32)
+            d = d if dtype == "f32" else bf16_bits_to_f32(f32_to_bf16_bits(d))
+            tokens[b * (N - 1) + n - 1] = int(np.argmax(d))
+
+    _par_rows(B, fn)
+    tp = np.tile(parents[1:], B).astype(np.int32)
+    return Workload(f"multi{K}x{gamma}", TREE_GREEDY, B, V, dtype, gam, tgt, None, tokens, np.ones(B, np.float32),
+                    np.zeros(B * (N - 1), np.float32), np.zeros(B, np.float32), tree_parents=tp, max_gamma=N - 1,
+                    meta={"K": K, "gamma": gamma})
+
+
 WORKLOADS = {
     "tiny": make_tiny,
     "llama3": make_llama3,
@@ -381,6 +426,8 @@ WORKLOADS = {
 
 
 def make(name: str, **kw) -> Workload:
+    if name == "multi_draft":
+        return make_multi_draft(**kw)
     if name == "tree13":
         return make_tree(parents=TREE_P_EAGLE13, wid=5, **kw)
     if name == "long_nkl":

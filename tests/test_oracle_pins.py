@@ -622,6 +622,155 @@ def test_block_accept_equals_greedy_when_every_draft_agrees_and_rejects_bad_min_
 
 
 # --------------------------------------------------------------------------
+# consensus across K drafts ("Chain of Draft" page, section 4.4)
+# --------------------------------------------------------------------------
+
+def test_consensus_worked_example():
+    """Two-token rows with hand-derived KL values (tests/golden/consensus_v2.json)."""
+    g = json.load(open(os.path.join(GOLD, "consensus_v2.json")))
+    rows = {k: np.log(np.array(v, np.float64)).astype(np.float32) for k, v in g["rows"].items()}
+    for case in g["cases"]:
+        names = case["drafts"]
+        K = len(names)
+        r = oracle.consensus(np.stack([rows[n] for n in names]), "f32", np.array([1], np.int32), K,
+                             np.ones(1, np.float32))
+        for a in range(K):
+            assert r.nkl[0, a, a] == 0.0
+            for c in range(K):
+                if a != c:
+                    ref = g["nkl"][names[a] + names[c]]["value"]
+                    assert abs(r.nkl[0, a, c] / ref - 1) < 1e-6, (names, a, c)
+        assert r.state[0] == case["state"] and r.pair[0] == case["pair"], case
+
+
+@pytest.mark.parametrize("K,T", [(2, 1.0), (3, 0.6), (4, 1.3)])
+def test_consensus_matches_scipy_and_rules(K, T):
+    """The matrix against scipy's KL; the closest pair, the state and the flags
+    follow from those scipy values."""
+    rng = np.random.default_rng(K)
+    V, B, gam = 2048, 3, 4
+    base = 3 * rng.standard_normal((B * gam, V))
+    drafts = np.concatenate([[base[n] + s * rng.standard_normal(V) for s in (0.05, 0.3, 0.6, 1.0)[:K]]
+                             for n in range(B * gam)]).astype(np.float32)
+    r = oracle.consensus(drafts, "f32", np.full(B, gam, np.int32), K, np.full(B, T, np.float32))
+    Td = np.float64(np.float32(T))
+    for n in range(B * gam):
+        Q = [special.softmax(drafts[n * K + a].astype(np.float64) / Td) for a in range(K)]
+        M = np.zeros((K, K))
+        for a in range(K):
+            for c in range(K):
+                if a != c:
+                    M[a, c] = stats.entropy(Q[a], Q[c]) / np.log(V)
+                    assert abs(r.nkl[n, a, c] / M[a, c] - 1) < 1e-10
+        pairs = [(0.5 * (M[a, c] + M[c, a]), a * K + c) for a in range(K) for c in range(a + 1, K)]
+        best, pair = min(pairs)
+        assert r.pair[n] == pair
+        assert r.state[n] == (1 if best < np.float32(0.1) else 2 if best > np.float32(0.15) else 0)
+
+
+def test_consensus_identical_drafts_and_invalid_requests():
+    rng = np.random.default_rng(3)
+    V, K = 5000, 3
+    row = (3 * rng.standard_normal(V)).astype(np.float32)
+    drafts = np.tile(row, (2 * K, 1))
+    r = oracle.consensus(drafts, "f32", np.array([1, 1], np.int32), K, np.array([0.7, 0.0], np.float32))
+    assert (r.nkl[0] == 0.0).all() and r.state[0] == 1 and r.pair[0] == 1  # pair (0, 1)
+    assert r.state[1] == -1 and r.pair[1] == -1 and np.isnan(r.nkl[1]).all()
+    one = oracle.consensus(np.ones((K, 1), np.float32), "f32", np.array([1], np.int32), K, np.ones(1, np.float32))
+    assert (one.nkl[0] == 0.0).all() and one.state[0] == 1  # V = 1: one point mass, NKL 0
+
+
+@pytest.mark.parametrize("thr,state_below,state_above,flag", [(0.1, 1, 0, 1), (0.15, 0, 2, 2)])
+def test_consensus_threshold_crossings(thr, state_below, state_above, flag):
+    """Two drafts of a one-parameter family (the second row scaled by 1 + t):
+    scipy's root finder places the symmetrised distance at the threshold; just
+    below and above it the state switches."""
+    from scipy.optimize import brentq
+    rng = np.random.default_rng(11)
+    V = 1024
+    x = (2 * rng.standard_normal(V)).astype(np.float64)
+
+    def dist(t):
+        P = special.softmax(x)
+        Q = special.softmax(x * (1 + t))
+        return 0.5 * (stats.entropy(P, Q) + stats.entropy(Q, P)) / np.log(V)
+
+    t0 = brentq(lambda t: dist(t) - float(np.float32(thr)), 0.0, 5.0, xtol=1e-15)
+    for t, state in ((t0 * (1 - 1e-4), state_below), (t0 * (1 + 1e-4), state_above)):
+        drafts = np.stack([x, x * (1 + t)]).astype(np.float64)
+        # exact float32 rows: the distance of the stored rows is what counts
+        r = oracle.consensus(drafts.astype(np.float32), "f32", np.array([1], np.int32), 2, np.ones(1, np.float32))
+        xs = drafts.astype(np.float32).astype(np.float64)
+        d = 0.5 * (stats.entropy(special.softmax(xs[0]), special.softmax(xs[1])) +
+                   stats.entropy(special.softmax(xs[1]), special.softmax(xs[0]))) / np.log(V)
+        assert r.state[0] == state, (t, d)
+        assert not (r.flags[0] & flag)
+
+
+@pytest.mark.parametrize("which", ["consensus", "divergence"])
+def test_consensus_flag_bands(which):
+    """A threshold set at the stored rows' distance (from scipy) times
+    1 +- 5e-7 is flagged (bit 1 for the consensus threshold, 2 for the
+    divergence one); at 1 +- 5e-6 it is not; the state follows the side."""
+    rng = np.random.default_rng(17)
+    V = 3000
+    x = (2 * rng.standard_normal(V)).astype(np.float32)
+    y = (x + 0.8 * rng.standard_normal(V)).astype(np.float32)
+    P, Q = special.softmax(x.astype(np.float64)), special.softmax(y.astype(np.float64))
+    d = 0.5 * (stats.entropy(P, Q) + stats.entropy(Q, P)) / np.log(V)
+    for rel, flagged in ((5e-7, True), (-5e-7, True), (5e-6, False), (-5e-6, False)):
+        thr = float(np.float32(d * (1 + rel)))
+        dc, dd = (thr, 10.0) if which == "consensus" else (0.0, thr)
+        r = oracle.consensus(np.stack([x, y]), "f32", np.array([1], np.int32), 2, np.ones(1, np.float32), dc, dd)
+        bit = 1 if which == "consensus" else 2
+        assert bool(r.flags[0] & bit) == flagged, rel
+        if which == "consensus":
+            assert r.state[0] == (1 if rel > 0 else 0)
+        else:
+            assert r.state[0] == (2 if rel < 0 else 0)
+
+
+def test_consensus_near_tie_flag():
+    """Three identical drafts: every pair at distance 0, the first pair (0, 1)
+    chosen and the near-tie flag set; well separated drafts: not set."""
+    rng = np.random.default_rng(19)
+    x = (3 * rng.standard_normal(4000)).astype(np.float32)
+    r = oracle.consensus(np.stack([x, x, x]), "f32", np.array([1], np.int32), 3, np.ones(1, np.float32))
+    assert r.pair[0] == 1 and r.flags[0] & 4
+    z = np.stack([x, x + 0.1 * rng.standard_normal(4000), x + 2.0 * rng.standard_normal(4000)]).astype(np.float32)
+    r = oracle.consensus(z, "f32", np.array([1], np.int32), 3, np.ones(1, np.float32))
+    assert r.pair[0] == 1 and not (r.flags[0] & 4)
+
+
+def test_multi_draft_longest_path_is_tree_mode_over_chains():
+    """Several drafts verified together, keeping the longest accepted path
+    (Gemma-4 MTP page, section 6.2), as tree mode over K chains under one root:
+    the accepted length equals the longest greedy acceptance among the chains
+    run one by one as separate greedy requests, the emitted tokens are that
+    chain's (the lowest chain among equals) and the next token is the argmax of
+    its last accepted node's row."""
+    K, gam = 3, 5
+    w = synthetic.make_multi_draft(B=24, K=K, gamma=gam, V=4000, noise=(0.2, 0.6, 1.0))
+    rt = oracle.verify_workload(w)
+    N = 1 + K * gam
+    tf = w.target_f32()
+    for b in range(w.batch):
+        lens = []
+        for k in range(K):
+            rows = [b * N] + [b * N + 1 + k * gam + i for i in range(gam)]
+            toks = w.draft_tokens[b * (N - 1) + k * gam: b * (N - 1) + (k + 1) * gam]
+            rg = oracle.verify(tf[rows], None, "f32", np.array([gam], np.int32), toks, None, None, None, G)
+            lens.append((int(rg.num_accepted[0]), k, rg.tokens))
+        best = max(l for l, _, _ in lens)
+        k_best = min(k for l, k, _ in lens if l == best)
+        assert rt.num_accepted[b] == best, b
+        ts = w.t_off[b]
+        assert rt.tokens[ts: ts + best + 1].tolist() == lens[k_best][2][: best + 1].tolist(), b
+        assert (rt.tokens[ts + best + 1: ts + N] == -1).all()
+    assert len(set(int(n) for n in rt.num_accepted)) > 1  # the chains' acceptances differ
+
+
+# --------------------------------------------------------------------------
 # tree mode: golden, brute force, chain == greedy
 # --------------------------------------------------------------------------
 
