@@ -22,7 +22,8 @@ every step); the percentiles come from those steps.
 
 Other workloads (context lines, not the headline): tiny, tiny_greedy (1000
 one-request calls, launch-bound: microseconds per call), long_greedy,
-long_nkl, long_nkl_pos, long_block, ragged, tree, sample_llama3, topk_llama3.
+long_nkl, long_nkl_pos, long_block, ragged, tree, multi_draft, sample_llama3,
+topk_llama3, consensus.
 """
 import argparse
 import ctypes
@@ -61,6 +62,11 @@ WORKLOADS = {
                               "bf16, per-request temperatures"),
     "topk_llama3": ({}, -1, "top-3 of each of the llama3-shaped batch's draft rows (tree-draft children): 160 rows, "
                             "V=128256, bf16"),
+    # several draft models
+    "multi_draft": ({}, 3, "multi-draft longest path: 3 draft chains of 6 tokens under one root per request, "
+                           "verified as one tree (greedy): B=16, V=128256, bf16"),
+    "consensus": ({}, -2, "consensus across 3 drafts: pairwise NKL of the drafts at every drafted position of the "
+                          "llama3-shaped batch (B=32, gamma=5, 3 x 160 rows), V=128256, bf16, thresholds 0.1 / 0.15"),
 }
 
 
@@ -162,7 +168,7 @@ def make_workload(name):
         return synthetic.make_tiny().with_mode(mode)
     maker = {"llama3": synthetic.make_llama3, "long_greedy": synthetic.make_long, "long_nkl": synthetic.make_long,
              "long_nkl_pos": synthetic.make_long, "long_block": synthetic.make_long, "ragged": synthetic.make_ragged,
-             "tree": synthetic.make_tree}[name]
+             "tree": synthetic.make_tree, "multi_draft": synthetic.make_multi_draft}[name]
     w = maker(**kw)
     return w.with_positions() if name == "long_nkl_pos" else w
 
@@ -286,6 +292,91 @@ def run_sample_gpu(name, steps, warmup, copies_bytes=1 << 30, event_every=8):
     nbytes = rows * V * 2 + (0 if topk else rows * min(V, 2048) * 2)
     return dict(desc=desc, rows=rows, V=V, ncopies=ncopies, ms_per_step=total_ms / steps, kernel_ms=float(ks.mean()),
                 kernel_pct=pct_us(ks), bytes=nbytes, sampled=len(sampled), topk=topk)
+
+
+def run_consensus_gpu(steps, warmup, copies_bytes=1 << 30, event_every=8):
+    """Times spec_consensus on device-resident drafts (rotated copies)."""
+    import numpy as np
+    import torch
+
+    import synthetic
+    import draft_token_verification_05_amd as sv
+
+    w = synthetic.make_consensus()
+    d = synthetic.consensus_to_device(w)
+    dev = torch.device("cuda:0")
+    ncopies = max(2, min(64, -(-copies_bytes // w.logit_bytes)))
+    copies = [d["drafts"]] + [d["drafts"].clone() for _ in range(ncopies - 1)]
+    npos, K, V = w.npos, w.K, w.V
+    out_state = torch.empty(npos, dtype=torch.int32, device=dev)
+    out_pair = torch.empty(npos, dtype=torch.int32, device=dev)
+    out_nkl = torch.empty(npos * K * K, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    cfg0 = sv.make_config(w.B, V, sv.SV_DTYPE_BF16, w.max_gamma, npos)
+    ws = torch.empty(sv.spec_consensus_workspace_size(cfg0, K), dtype=torch.uint8, device=dev)
+    hip = Hip()
+    sampled = list(range(0, steps, max(1, event_every)))
+    ev = hip.events(4 * len(sampled))
+    ev_all = hip.events(2)
+    ev_base = ctypes.addressof(ev)
+
+    def cfg_for(k):
+        e = ev_base + 4 * (k // event_every) * ctypes.sizeof(ctypes.c_void_p) if (k >= 0 and k % event_every == 0) else 0
+        return sv.make_config(w.B, V, sv.SV_DTYPE_BF16, w.max_gamma, npos, stream.cuda_stream, ws.data_ptr(),
+                              ws.numel(), phase_events=e)
+
+    def call(k, cfg):
+        st = sv.spec_consensus(copies[k % ncopies].data_ptr(), K, d["gamma"].data_ptr(), d["temperature"].data_ptr(),
+                               0.1, 0.15, out_nkl.data_ptr(), out_state.data_ptr(), out_pair.data_ptr(), cfg)
+        if st != 0:
+            raise RuntimeError(sv.spec_verify_status_string(st))
+
+    plain = cfg_for(-1)
+    timed = [cfg_for(k) for k in range(steps)]
+    for k in range(warmup):
+        call(k, plain)
+    torch.cuda.synchronize()
+    hip.record(ev_all[0], stream.cuda_stream)
+    for k in range(steps):
+        call(k, timed[k])
+    hip.record(ev_all[1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    total_ms = hip.elapsed_ms(ev_all[0], ev_all[1])
+    ks = np.array([hip.elapsed_ms(ev[4 * n + 1], ev[4 * n + 2]) for n in range(len(sampled))])
+    st_ms = np.array([hip.elapsed_ms(ev[4 * n + 0], ev[4 * n + 3]) for n in range(len(sampled))])
+    states = np.bincount(out_state.cpu().numpy(), minlength=3).tolist()
+    # the workspace header's second int32 counts the positions that took the exact pass
+    refined = int(ws[4:8].view(torch.int32).item())
+    hip.destroy(ev)
+    hip.destroy(ev_all)
+    # the pass reads every draft row once and writes per (position, chunk) a
+    # 16-byte record per row and per ordered pair; one read of the drafts is
+    # the step's minimum
+    nch = -(-V // (256 * 4 * 8))
+    draft_bytes = npos * K * V * 2
+    kbytes = draft_bytes + npos * nch * (K + K * (K - 1)) * 16
+    return dict(w=w, ncopies=ncopies, ms_per_step=total_ms / steps, kernel_ms=float(ks.mean()),
+                kernel_pct=pct_us(ks), step_pct=pct_us(st_ms), kernel_bytes=kbytes, step_bytes=draft_bytes,
+                sampled=len(sampled), states=states, refined=refined)
+
+
+def cpu_baseline_consensus(budget_s=8.0):
+    import oracle
+    import synthetic
+    w = synthetic.make_consensus()
+    threads = oracle.max_threads()
+    run = lambda: oracle.consensus(w.drafts, w.dtype, w.gamma, w.K, w.temperature, nthreads=threads)
+    run()  # warm (page-in)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        run()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": w.npos * reps / el, "unit": "consensus positions/s", "cores": threads, "kind": "oracle",
+            **cpu_info(), "sample": f"{reps} full batches of the consensus workload ({w.npos} positions x {w.K} "
+                                    f"drafts each), {el:.1f} s wall on {threads} host threads"}
 
 
 def _step_args(sv, w, d, mode, out_tokens, out_num, out_nkl, stream, ws, events_ptr, positions, b=None):
@@ -451,6 +542,36 @@ def main():
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(requests are independent, so more GPUs would each run their own share).", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "consensus":
+        r = run_consensus_gpu(args.steps, args.warmup, event_every=max(1, args.event_every))
+        w = r["w"]
+        achieved = r["kernel_bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
+        probe = None if args.no_probe else run_probe(int(r["step_bytes"]))
+        line = {
+            "metric": "consensus positions/sec (3 drafts) at V=128256 (bf16); achieved HBM GB/s vs peak",
+            "value": round(w.npos / (r["ms_per_step"] * 1e-3), 1), "unit": "consensus positions/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": WORKLOADS["consensus"][2], "batch": w.B, "gamma": int(w.gamma.max()),
+                       "drafts": w.K, "vocab": w.V, "logits": w.dtype, "positions_per_step": w.npos,
+                       "states": r["states"], "positions_exact_pass": r["refined"],
+                       "input_copies_rotated": r["ncopies"],
+                       "step_GBps": round(r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1),
+                       "step_frac_of_peak": round(r["step_bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                                  4),
+                       "step_us": r["step_pct"]},
+            "roofline": {"bound": "hbm", "kernel": "k_cons_pass", "achieved": round(achieved, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                         "traffic": load_traffic("k_cons_pass", "consensus"), "bytes_per_launch": r["kernel_bytes"],
+                         "avg_launch_us": round(r["kernel_ms"] * 1e3, 3), "launch_us": r["kernel_pct"],
+                         "timed_launches": r["sampled"]},
+            "probe": probe,
+            "cpu_baseline": None if args.no_cpu else cpu_baseline_consensus(),
+        }
+        if probe:
+            line["roofline"]["frac_of_probe"] = round(achieved / probe["GBps"], 4)
+        print(json.dumps(line), flush=True)
+        return
     if args.workload.startswith(("sample", "topk")):
         r = run_sample_gpu(args.workload, args.steps, args.warmup, event_every=max(1, args.event_every))
         achieved = r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9

@@ -95,6 +95,10 @@ def _load() -> ctypes.CDLL:
     lib.spec_read_probe.argtypes = [P, ctypes.c_uint64, i32, P, P, P, P]
     lib.spec_sample_rows.restype = ctypes.c_int
     lib.spec_sample_rows.argtypes = [P, P, P, P, ctypes.POINTER(sv_config)]
+    lib.spec_consensus.restype = ctypes.c_int
+    lib.spec_consensus.argtypes = [P, i32, P, P, ctypes.c_float, ctypes.c_float, P, P, P, ctypes.POINTER(sv_config)]
+    lib.spec_consensus_workspace_size.restype = ctypes.c_size_t
+    lib.spec_consensus_workspace_size.argtypes = [ctypes.POINTER(sv_config), i32]
     return lib
 
 
@@ -139,6 +143,18 @@ def spec_sample_rows(logits: int, temperature: int, u: int, out_tokens: int, cfg
     """Raw binding of spec_sample_rows (device pointers as ints)."""
     return int(_lib.spec_sample_rows(logits or None, temperature or None, u or None, out_tokens or None,
                                      ctypes.byref(cfg)))
+
+
+def spec_consensus(draft_logits: int, num_drafts: int, gamma_per_req: int, temperature: int, delta_c: float,
+                   delta_d: float, out_nkl: int, out_state: int, out_pair: int, cfg: sv_config) -> int:
+    """Raw binding of spec_consensus (device pointers as ints)."""
+    return int(_lib.spec_consensus(draft_logits or None, int(num_drafts), gamma_per_req or None,
+                                   temperature or None, float(delta_c), float(delta_d), out_nkl or None,
+                                   out_state or None, out_pair or None, ctypes.byref(cfg)))
+
+
+def spec_consensus_workspace_size(cfg: sv_config, num_drafts: int) -> int:
+    return int(_lib.spec_consensus_workspace_size(ctypes.byref(cfg), int(num_drafts)))
 
 
 def spec_topk_rows(logits: int, k: int, out_idx: int, cfg: sv_config) -> int:
@@ -190,18 +206,20 @@ _WORKSPACES = {}
 _MAX_CACHED_WORKSPACES = 64
 
 
-def workspace_for(cfg: sv_config, device, stream=None) -> "torch.Tensor":
+def workspace_for(cfg: sv_config, device, stream=None, nbytes: Optional[int] = None) -> "torch.Tensor":
     """A workspace for this configuration, cached per device, stream and
     configuration (calls on different streams must not share one).  Its
-    contents need no initialisation.  The tensor is recorded on ``stream`` so
+    contents need no initialisation.  ``nbytes``: its size, if not
+    spec_verify_workspace_size(cfg).  The tensor is recorded on ``stream`` so
     that torch's allocator does not hand its memory out again while work
     queued there may still use it, also after the cache drops it."""
     import torch
     sid = 0 if stream is None else int(stream.cuda_stream)
-    key = (str(device), sid, cfg.batch, cfg.vocab, cfg.dtype, cfg.max_gamma, cfg.total_draft_rows)
+    nbytes = spec_verify_workspace_size(cfg) if nbytes is None else int(nbytes)
+    key = (str(device), sid, cfg.batch, cfg.vocab, cfg.dtype, cfg.max_gamma, cfg.total_draft_rows, nbytes)
     ws = _WORKSPACES.pop(key, None)
     if ws is None:
-        ws = torch.empty(max(spec_verify_workspace_size(cfg), 256), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         while len(_WORKSPACES) >= _MAX_CACHED_WORKSPACES:
             _WORKSPACES.pop(next(iter(_WORKSPACES)))  # the least recently used
     if stream is not None:
@@ -375,3 +393,52 @@ def topk_rows(logits, k: int, *, workspace=None, stream=None, phase_events: int 
     if st != SV_OK:
         raise SpecVerifyError(st)
     return out
+
+
+@dataclass
+class ConsensusOutput:
+    state: "torch.Tensor"  # int32 [positions]: 1 consensus, 2 divergence, 0 neither, -1 invalid
+    pair: "torch.Tensor"  # int32 [positions]: a * K + b of the closest pair a < b (-1 invalid)
+    nkl: Optional["torch.Tensor"] = None  # float32 [positions, K, K]: KL(q_a || q_b) / ln V
+
+
+def consensus(draft_logits, gamma_per_req, temperature, *, delta_c: float = 0.1, delta_d: float = 0.15,
+              max_gamma: Optional[int] = None, out_nkl: bool = True, workspace=None, stream=None,
+              phase_events: int = 0) -> ConsensusOutput:
+    """Pairwise NKL of the K drafts of every position and the consensus state
+    (see spec_consensus in specverify.h).  ``draft_logits`` is a contiguous
+    [positions, K, V] GPU tensor (bfloat16 or float32), positions = sum(gamma);
+    ``gamma_per_req`` int32 [B] and ``temperature`` float32 [B] on the GPU."""
+    import torch
+    dev = draft_logits.device
+    if dev.type != "cuda":
+        raise ValueError("draft_logits must be a GPU tensor")
+    dt = {torch.bfloat16: SV_DTYPE_BF16, torch.float32: SV_DTYPE_F32}.get(draft_logits.dtype)
+    if dt is None:
+        raise TypeError("draft_logits must be bfloat16 or float32")
+    if draft_logits.dim() != 3 or not draft_logits.is_contiguous():
+        raise ValueError("draft_logits must be a contiguous [positions, K, V] tensor")
+    npos, K, V = (int(x) for x in draft_logits.shape)
+    _check(gamma_per_req, "gamma_per_req", torch.int32, None, dev)
+    B = int(gamma_per_req.numel())
+    _check(temperature, "temperature", torch.float32, B, dev)
+    if max_gamma is None:
+        max_gamma = int(gamma_per_req.max().item()) if B > 0 else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    cfg = make_config(B, V, dt, max(int(max_gamma), 0), npos, stream=int(stream.cuda_stream),
+                      phase_events=phase_events)
+    need = spec_consensus_workspace_size(cfg, K)
+    if workspace is None:
+        workspace = workspace_for(cfg, dev, stream, nbytes=need)
+    elif workspace.numel() < need:
+        raise ValueError("workspace too small")
+    cfg.workspace, cfg.workspace_bytes = workspace.data_ptr(), workspace.numel()
+    state = torch.empty(max(npos, 1), dtype=torch.int32, device=dev)
+    pair = torch.empty(max(npos, 1), dtype=torch.int32, device=dev)
+    nkl = torch.empty((max(npos, 1), K, K), dtype=torch.float32, device=dev) if out_nkl else None
+    st = spec_consensus(_ptr(draft_logits), K, _ptr(gamma_per_req), _ptr(temperature), delta_c, delta_d, _ptr(nkl),
+                        _ptr(state), _ptr(pair), cfg)
+    if st != SV_OK:
+        raise SpecVerifyError(st)
+    return ConsensusOutput(state[:npos], pair[:npos], None if nkl is None else nkl[:npos])

@@ -362,6 +362,70 @@ int spec_topk_rows(const void* logits, int32_t k, int32_t* out_idx, const sv_con
   return SV_OK;
 }
 
+size_t spec_consensus_workspace_size(const sv_config* cfg, int32_t num_drafts) {
+  if (!cfg || cfg->struct_size != sizeof(sv_config)) return 0;
+  if (cfg->batch <= 0 || cfg->vocab <= 0 || cfg->total_draft_rows < 0) return 0;
+  if (cfg->dtype != SV_DTYPE_F32 && cfg->dtype != SV_DTYPE_BF16) return 0;
+  if (num_drafts < 2 || num_drafts > sv::kConsMaxDrafts) return 0;
+  return sv::make_cons_layout(cfg->batch, cfg->vocab, cfg->dtype, cfg->total_draft_rows, num_drafts).total;
+}
+
+int spec_consensus(const void* draft_logits, int32_t num_drafts, const int32_t* gamma_per_req,
+                   const float* temperature, float delta_c, float delta_d, float* out_nkl, int32_t* out_state,
+                   int32_t* out_pair, const sv_config* cfg) {
+  if (!cfg || cfg->struct_size != sizeof(sv_config)) return SV_EINVAL;
+  if (cfg->batch <= 0 || cfg->vocab <= 0 || cfg->max_gamma < 0) return SV_EINVAL;
+  if (cfg->dtype != SV_DTYPE_F32 && cfg->dtype != SV_DTYPE_BF16) return SV_EINVAL;
+  if (num_drafts < 2 || num_drafts > sv::kConsMaxDrafts) return SV_EINVAL;
+  if (!std::isfinite(delta_c) || !std::isfinite(delta_d)) return SV_EINVAL;
+  if (cfg->max_gamma > SV_MAX_GAMMA) return SV_EUNSUPPORTED;
+  const int64_t npos = cfg->total_draft_rows;
+  if (npos < 0 || npos > (int64_t)cfg->batch * cfg->max_gamma) return SV_EINVAL;
+  const int64_t K = num_drafts;
+  const sv::ConsLayout L = sv::make_cons_layout(cfg->batch, cfg->vocab, cfg->dtype, npos, K);
+  if (npos * K > INT32_MAX || npos * L.nch > INT32_MAX) return SV_EUNSUPPORTED;
+  if (!gamma_per_req || !temperature || !out_state || !out_pair || (npos > 0 && !draft_logits)) return SV_EINVAL;
+  const size_t es = (size_t)sv::elem_size(cfg->dtype);
+  if ((draft_logits && !aligned(draft_logits, es)) || !aligned(gamma_per_req, 4) || !aligned(temperature, 4) ||
+      !aligned(out_state, 4) || !aligned(out_pair, 4) || (out_nkl && !aligned(out_nkl, 4)))
+    return SV_EINVAL;
+  if (!cfg->workspace || cfg->workspace_bytes < L.total || !aligned(cfg->workspace, 256)) return SV_EWORKSPACE;
+
+  char* ws = static_cast<char*>(cfg->workspace);
+  sv::Params p{};
+  p.target = draft_logits;
+  p.gamma = gamma_per_req;
+  p.temp = temperature;
+  p.B = cfg->batch;
+  p.V = cfg->vocab;
+  p.dtype = cfg->dtype;
+  p.max_gamma = cfg->max_gamma;
+  p.mode = sv::kModeConsensus;
+  p.R_d = (int32_t)npos;
+  p.cons_k = num_drafts;
+  p.cons_dc = delta_c;
+  p.cons_dd = delta_d;
+  p.cons_nkl = out_nkl;
+  p.cons_state = out_state;
+  p.cons_pair = out_pair;
+  p.hdr = reinterpret_cast<int32_t*>(ws + L.off_hdr);
+  p.d_off = reinterpret_cast<int32_t*>(ws + L.off_doff);
+  p.pair2req = reinterpret_cast<int32_t*>(ws + L.off_pos2req);
+  p.cons_stats = reinterpret_cast<float*>(ws + L.off_stats);
+  p.cons_tz = reinterpret_cast<double*>(ws + L.off_tz);
+  p.cons_queue = reinterpret_cast<int32_t*>(ws + L.off_queue);
+  p.cons_exact = reinterpret_cast<double*>(ws + L.off_exact);
+  const bool vec = ((size_t)cfg->vocab * es) % 16 == 0 && (!draft_logits || aligned(draft_logits, 16));
+  hipStream_t s = static_cast<hipStream_t>(cfg->stream);
+  hipEvent_t* ev = static_cast<hipEvent_t*>(cfg->phase_events);
+  hipError_t e;
+  if (ev && (e = hipEventRecord(ev[0], s)) != hipSuccess) return hip_fail(e);
+  if ((e = (hipError_t)sv::launch_consensus(p, vec, s, ev ? ev[1] : nullptr, ev ? ev[2] : nullptr)) != hipSuccess)
+    return hip_fail(e);
+  if (ev && (e = hipEventRecord(ev[3], s)) != hipSuccess) return hip_fail(e);
+  return SV_OK;
+}
+
 int spec_read_probe(const void* buf, uint64_t bytes, int32_t wgs_per_cu, void* sink, void* stream,
                     void* ev_start, void* ev_stop) {
   if (!buf || !sink || wgs_per_cu < 1 || wgs_per_cu > 32 || !aligned(buf, 16) || !aligned(sink, 4))

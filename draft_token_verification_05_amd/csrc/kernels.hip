@@ -401,12 +401,13 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(Params p) {
     p.hdr[0] = bad ? 1 : 0;
     p.hdr[1] = 0;  // KL second-pass queue
   }
-  for (int b = tid; b < p.B; b += kPrepThreads) p.cnt_kl[(int64_t)b * kCntStride] = 0u;  // KL second-pass counters
+  if (p.cnt_kl)  // KL second-pass counters (verify calls)
+    for (int b = tid; b < p.B; b += kPrepThreads) p.cnt_kl[(int64_t)b * kCntStride] = 0u;
   if (bad) return;
   __syncthreads();  // offsets written by other threads of this workgroup
   for (int b = tid; b < p.B; b += kPrepThreads) {
     const int g = p.gamma[b], d0 = p.d_off[b], t0 = d0 + b;
-    if (p.mode == SV_MODE_STOCHASTIC)
+    if (p.mode == SV_MODE_STOCHASTIC || p.mode == kModeConsensus)
       for (int k = 0; k < g; ++k) p.pair2req[d0 + k] = b;
     if (p.mode == SV_MODE_NKL)
       for (int k = 0; k <= g; ++k) p.row2req[t0 + k] = b;
@@ -2283,6 +2284,510 @@ __global__ __launch_bounds__(kThreads) void k_refine(Params p) {
 }
 
 // ----------------------------------------------------------------------------
+// consensus across K drafts ("Chain of Draft" page, section 4.4,
+// Consensus-Aware Accept): per position, the NKL of every ordered pair of its
+// K draft rows, M[a][b] = KL(q_a || q_b) / ln V, and the closest pair's
+// symmetrised distance against the consensus and divergence thresholds.
+//
+// One read of the rows (k_cons_pass, one workgroup per (position, chunk)):
+// per row the chunk maximum m and s = sum 2^((x - m) L), per ordered pair
+// t = sum 2^((x_a - m_a) L) (x_a - x_b) and z, the same with |x_a - x_b|.
+// k_cons_merge (one wave per position) merges the chunks and forms
+//   KL_ab = c T_ab / S_a - (M_a - M_b) c - ln(S_a / S_b),  c = L ln 2
+// (M: the row's maximum, here an integer reference exponent in its place),
+// with the one-pass error estimate kKlErr (c Z_ab / S_a + 1) of the verify
+// KL.  A position is decided there unless an estimate exceeds kKlRel of its
+// value or the decision (a threshold, the closest pair) lies within the
+// estimates; such positions are queued, k_cons_exact sums the exact form
+// q_a g(w), w = ln(q_b / q_a), g(w) = e^w - 1 - w >= 0 (no cancellation) for
+// them -- a second read of their rows only -- and k_cons_finish decides from
+// those sums.
+// ----------------------------------------------------------------------------
+
+constexpr int kConsVec = 4;  // 16-byte vectors per thread per row per chunk
+constexpr int kConsMaxPairs = kConsMaxDrafts * (kConsMaxDrafts - 1);
+constexpr int kConsExactGrid = 2048;  // workgroups of the exact pass (a loop over the queued items)
+
+struct ConsShared {
+  float m[kConsMaxDrafts][kWaves];
+  double d[kConsMaxDrafts + 2 * kConsMaxPairs][kWaves];
+  float Mrow[kConsMaxDrafts];
+  double Srow[kConsMaxDrafts];
+};
+
+// Ordered pair (a, b), a != b, at a * (K - 1) + (b < a ? b : b - 1).
+template <int K>
+__device__ __forceinline__ constexpr int cons_pair_index(int a, int b) {
+  return a * (K - 1) + (b < a ? b : b - 1);
+}
+
+// Elements [e0, e0 + P) of draft row `row` for vector k of chunk `chunk` and thread t.
+template <int DT>
+__device__ __forceinline__ int64_t cons_e0(int64_t chunk, int k) {
+  return (chunk * kConsVec * kThreads + (int64_t)k * kThreads + threadIdx.x) * Elem<DT>::P;
+}
+
+// Sets the unpacked elements at positions >= V of the vector starting at e0
+// to the pad.  The loads themselves (fetch_raw) take no select, so that no
+// wait is placed between them.
+template <int DT, bool VEC>
+__device__ __forceinline__ void cons_mask(float* v, int64_t e0, int64_t V) {
+  constexpr int P = Elem<DT>::P;
+  if (VEC) {  // a vector lies wholly inside or wholly past the row
+    const bool in = e0 < V;
+#pragma unroll
+    for (int e = 0; e < P; ++e) v[e] = in ? v[e] : Elem<DT>::kPad;
+  } else {
+#pragma unroll
+    for (int e = 0; e < P; ++e)
+      if (e0 + e >= V) v[e] = Elem<DT>::kPad;
+  }
+}
+
+// Reference exponent of a row segment whose largest element is vm: an
+// integer near vm L (clamped so that it stays exact in float32), so that the
+// terms 2^(x L - R) are at most about 1 and rescaling between references is
+// an exact power of two.
+constexpr int kConsRNone = -(1 << 30);  // no element seen yet
+__device__ __forceinline__ int cons_ref(float vm, float Lhi) {
+  const float r = ceilf(vm * Lhi);
+  return (int)fminf(fmaxf(r, -16000000.0f), 16000000.0f);  // NaN (an invalid T) gives the lower bound
+}
+
+// Pass over the rows, one vector of every row at a time with the next
+// vector's loads in flight.  Each thread keeps per row a running reference
+// exponent R and sums s = sum 2^(x L - R) (fmaf(x, L, -R): R is an integer,
+// so the single rounding is relative to the small exponent where the mass
+// is), t and z; when R grows the sums are rescaled by an exact power of two.
+// The workgroup then rescales to the chunk's largest R, also exactly.
+// Vectors wholly past the row's end are skipped; partial ones hold the pad,
+// which gives 0.
+template <int DT, bool VEC, int K>
+__global__ __launch_bounds__(kThreads) void k_cons_pass(Params p) {
+  __shared__ ConsShared sh;
+  constexpr int P = Elem<DT>::P;
+  constexpr int NP = K * (K - 1);
+  constexpr int NV = K + 2 * NP;  // s per row, then t and z per ordered pair
+  const int64_t nch = (p.V + chunk_cons(DT) - 1) / chunk_cons(DT);
+  const int64_t pos = blockIdx.x / nch, chunk = blockIdx.x % nch;
+  if (p.hdr[0] != 0) return;  // layout error (k_prep)
+  const int b = p.pair2req[pos];
+  const float Lhi = (float)(kLog2eD / (double)p.temp[b]);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const auto load_vec = [&](int k, uint4* q) {
+    const int64_t e0 = cons_e0<DT>(chunk, k);
+#pragma unroll
+    for (int a = 0; a < K; ++a) q[a] = fetch_raw<DT, VEC>(p.target, pos * K + a, p.V, e0);
+  };
+  const auto rescale = [&](double* acc, int a, int sh_exp) {
+    acc[a] = ldexp(acc[a], sh_exp);
+#pragma unroll
+    for (int bb = 0; bb < K; ++bb)
+      if (bb != a) {
+        const int q = K + 2 * cons_pair_index<K>(a, bb);
+        acc[q] = ldexp(acc[q], sh_exp);
+        acc[q + 1] = ldexp(acc[q + 1], sh_exp);
+      }
+  };
+  int R[K];
+  double acc[NV];
+#pragma unroll
+  for (int a = 0; a < K; ++a) R[a] = kConsRNone;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) acc[i] = 0.0;
+  uint4 cur[K], nxt[K];
+  load_vec(0, cur);
+#pragma unroll 1
+  for (int k = 0; k < kConsVec; ++k) {
+    if (k + 1 < kConsVec) load_vec(k + 1, nxt);
+    const int64_t e0 = cons_e0<DT>(chunk, k);
+    if (e0 < p.V) {
+      float v[K][P];
+      float nr[K];  // -R of each row after this vector
+#pragma unroll
+      for (int a = 0; a < K; ++a) {
+        unpack<DT>(cur[a], v[a]);
+        cons_mask<DT, VEC>(v[a], e0, p.V);
+        float vm = v[a][0];
+#pragma unroll
+        for (int e = 1; e < P; ++e) vm = fmaxf(vm, v[a][e]);
+        const int rn = max(R[a], cons_ref(vm, Lhi));
+        rescale(acc, a, max(R[a] - rn, -2000));  // 0 when unchanged; the first vector scales zeros
+        R[a] = rn;
+        nr[a] = -(float)rn;
+      }
+      float part[NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i) part[i] = 0.f;
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        float ev[K];
+#pragma unroll
+        for (int a = 0; a < K; ++a) {
+          ev[a] = __builtin_amdgcn_exp2f(fmaf(v[a][e], Lhi, nr[a]));
+          part[a] += ev[a];
+        }
+#pragma unroll
+        for (int a = 0; a < K; ++a)
+#pragma unroll
+          for (int bb = a + 1; bb < K; ++bb) {
+            const float d = v[a][e] - v[bb][e];
+            const int qa = K + 2 * cons_pair_index<K>(a, bb), qb = K + 2 * cons_pair_index<K>(bb, a);
+            part[qa] = fmaf(ev[a], d, part[qa]);
+            part[qa + 1] = fmaf(ev[a], fabsf(d), part[qa + 1]);
+            part[qb] = fmaf(-ev[bb], d, part[qb]);
+            part[qb + 1] = fmaf(ev[bb], fabsf(d), part[qb + 1]);
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) acc[i] += (double)part[i];
+    }
+#pragma unroll
+    for (int a = 0; a < K; ++a) cur[a] = nxt[a];
+  }
+  // the chunk's reference of every row, then each thread's sums rescaled to it
+#pragma unroll
+  for (int a = 0; a < K; ++a) {
+    const int rw = wave_max_int(R[a]);
+    if (lane == 0) sh.m[a][w] = (float)rw;  // integers below 2^24: exact
+  }
+  __syncthreads();
+#pragma unroll
+  for (int a = 0; a < K; ++a) {
+    float Rc = sh.m[a][0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) Rc = fmaxf(Rc, sh.m[a][k]);
+    rescale(acc, a, max(R[a] - (int)Rc, -2000));  // threads that saw no element hold zeros
+    if (threadIdx.x == 0) sh.Mrow[a] = Rc;
+  }
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const double t = wave_sum_d(acc[i]);
+    if (lane == 0) sh.d[i][w] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x < NV) {
+    const int i = threadIdx.x;
+    double t = sh.d[i][0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) t += sh.d[i][k];
+    if (i < K) {
+      float* dst = p.cons_stats + ((pos * K + i) * nch + chunk) * 4;
+      dst[0] = sh.Mrow[i];
+      *reinterpret_cast<double*>(dst + 2) = t;
+    } else {
+      p.cons_tz[(pos * nch + chunk) * 2 * NP + (i - K)] = t;
+    }
+  }
+}
+
+// Writes the outputs of position `pos` from its K x K matrix (lane 0 of the
+// calling wave): the closest pair a < b (lowest on ties) and its state.
+template <int K>
+__device__ __forceinline__ void cons_write(const Params& p, int64_t pos, const double (&m)[K][K], const double (&dist)[K][K]) {
+  if (p.cons_nkl)
+#pragma unroll
+    for (int a = 0; a < K; ++a)
+#pragma unroll
+      for (int bb = 0; bb < K; ++bb) p.cons_nkl[pos * K * K + a * K + bb] = (float)m[a][bb];
+  double best = INFINITY;
+  int pair = -1;
+#pragma unroll
+  for (int a = 0; a < K; ++a)
+#pragma unroll
+    for (int bb = a + 1; bb < K; ++bb)
+      if (dist[a][bb] < best) {
+        best = dist[a][bb];
+        pair = a * K + bb;
+      }
+  p.cons_pair[pos] = pair;
+  p.cons_state[pos] = best < (double)p.cons_dc ? 1 : (best > (double)p.cons_dd ? 2 : 0);
+}
+
+// -1 (and NaN in the matrix) for a position that has no valid answer.
+template <int K>
+__device__ __forceinline__ void cons_write_invalid(const Params& p, int64_t pos) {
+  p.cons_state[pos] = -1;
+  p.cons_pair[pos] = -1;
+  if (p.cons_nkl)
+    for (int k = 0; k < K * K; ++k) p.cons_nkl[pos * K * K + k] = __builtin_nanf("");
+}
+
+// Merge (one wave per position): the one-pass matrix and its error
+// estimates; decides the position or queues it for the exact pass.  With
+// q_a = 2^(x_a L - R_a) / S_a:
+//   KL_ab = c T_ab / S_a - (R_a - R_b) ln 2 - ln(S_a / S_b).
+template <int K>
+__global__ __launch_bounds__(kThreads) void k_cons_merge(Params p, int64_t nch) {
+  constexpr int NP = K * (K - 1);
+  const int lane = threadIdx.x & 63;
+  const int64_t pos = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (pos >= p.R_d) return;  // wave-uniform
+  const bool layout_ok = p.hdr[0] == 0;
+  const int b = layout_ok ? p.pair2req[pos] : 0;
+  if (!layout_ok || !temp_ok(p.temp[b])) {
+    if (lane == 0) cons_write_invalid<K>(p, pos);
+    return;
+  }
+  const float Lhi = (float)(kLog2eD / (double)p.temp[b]);
+  const double c = (double)Lhi * kLn2D;
+  double S[K], T[NP], Z[NP];
+  float R[K];  // the row's largest chunk reference: S = sum 2^(x L - R)
+#pragma unroll
+  for (int a = 0; a < K; ++a) {
+    const float* src = p.cons_stats + (pos * K + a) * nch * 4;
+    float mx = -INFINITY;
+    for (int64_t ch = lane; ch < nch; ch += 64) mx = fmaxf(mx, src[ch * 4]);
+    R[a] = wave_max(mx);
+  }
+  double sl[K], tl[NP], zl[NP];
+#pragma unroll
+  for (int a = 0; a < K; ++a) sl[a] = 0.0;
+#pragma unroll
+  for (int q = 0; q < NP; ++q) tl[q] = zl[q] = 0.0;
+  for (int64_t ch = lane; ch < nch; ch += 64) {
+    double f[K];
+#pragma unroll
+    for (int a = 0; a < K; ++a) {
+      const float* src = p.cons_stats + ((pos * K + a) * nch + ch) * 4;
+      f[a] = ldexp(1.0, max((int)(src[0] - R[a]), -2000));  // exact
+      sl[a] += *reinterpret_cast<const double*>(src + 2) * f[a];
+    }
+    const double* tz = p.cons_tz + (pos * nch + ch) * 2 * NP;
+#pragma unroll
+    for (int a = 0; a < K; ++a)
+#pragma unroll
+      for (int bb = 0; bb < K; ++bb)
+        if (bb != a) {
+          const int q = cons_pair_index<K>(a, bb);
+          tl[q] += tz[2 * q] * f[a];
+          zl[q] += tz[2 * q + 1] * f[a];
+        }
+  }
+#pragma unroll
+  for (int a = 0; a < K; ++a) S[a] = wave_sum_d(sl[a]);
+#pragma unroll
+  for (int q = 0; q < NP; ++q) {
+    T[q] = wave_sum_d(tl[q]);
+    Z[q] = wave_sum_d(zl[q]);
+  }
+  if (lane != 0) return;
+  const double lnV = log((double)p.V);
+  double m[K][K], err[K][K];
+  bool need = false;
+#pragma unroll
+  for (int a = 0; a < K; ++a)
+#pragma unroll
+    for (int bb = 0; bb < K; ++bb) {
+      m[a][bb] = 0.0;
+      err[a][bb] = 0.0;
+      if (a == bb || p.V == 1) continue;  // one token: both rows are the same point mass
+      const int q = cons_pair_index<K>(a, bb);
+      const double kl = T[q] / S[a] * c - (double)(R[a] - R[bb]) * kLn2D - log(S[a] / S[bb]);
+      const double e = kKlErr * (Z[q] / S[a] * c + 1.0);
+      need = need || !(e <= kKlRel * kl);
+      m[a][bb] = kl / lnV;
+      err[a][bb] = e / lnV;
+    }
+  double dist[K][K], derr[K][K];
+  double db = INFINITY, eb = 0.0;  // the closest pair's distance and estimate (lowest pair on ties)
+  int best = -1;
+#pragma unroll
+  for (int a = 0; a < K; ++a)
+#pragma unroll
+    for (int bb = a + 1; bb < K; ++bb) {
+      dist[a][bb] = 0.5 * (m[a][bb] + m[bb][a]);
+      derr[a][bb] = 0.5 * (err[a][bb] + err[bb][a]);
+      if (dist[a][bb] < db) {
+        db = dist[a][bb];
+        eb = derr[a][bb];
+        best = a * K + bb;
+      }
+    }
+  need = need || best < 0 || fabs(db - (double)p.cons_dc) <= eb || fabs(db - (double)p.cons_dd) <= eb;
+#pragma unroll
+  for (int a = 0; a < K; ++a)
+#pragma unroll
+    for (int bb = a + 1; bb < K; ++bb)  // another pair within the estimates of the closest one
+      if (a * K + bb != best && dist[a][bb] - db <= derr[a][bb] + eb) need = true;
+  if (need) {
+    const int slot = atomicAdd(p.hdr + 1, 1);
+    p.cons_queue[slot] = (int)pos;
+  } else {
+    cons_write<K>(p, pos, m, dist);
+  }
+}
+
+// Reference exponents and sums of the position's K rows, merged over the
+// chunks: wave a < K takes row a, lane l the chunks l, l + 64, ..., then a
+// fixed-order wave reduction, so every workgroup of the position gets the
+// same bits.  All threads call; results in sh.Mrow (R) / sh.Srow (S).
+template <int K>
+__device__ __forceinline__ void cons_row_stats(const Params& p, int64_t pos, int64_t nch, ConsShared& sh) {
+  static_assert(K <= kWaves, "one wave per draft row");
+  const int lane = threadIdx.x & 63, a = threadIdx.x >> 6;
+  if (a < K) {
+    const float* src = p.cons_stats + (pos * K + a) * nch * 4;
+    float R = -INFINITY;
+    for (int64_t c = lane; c < nch; c += 64) R = fmaxf(R, src[c * 4]);
+    R = wave_max(R);
+    double S = 0.0;
+    for (int64_t c = lane; c < nch; c += 64)
+      S += ldexp(*reinterpret_cast<const double*>(src + c * 4 + 2), max((int)(src[c * 4] - R), -2000));
+    S = wave_sum_d(S);
+    if (lane == 0) {
+      sh.Mrow[a] = R;
+      sh.Srow[a] = S;
+    }
+  }
+  __syncthreads();
+}
+
+// Exact pass over the queued positions: per (queued position, chunk) item
+// and ordered pair (a, b), a != b, the chunk's sum of q_a g(w), w = ln(q_b /
+// q_a), with q_a(y) = 2^(x_a L - R_a) / S_a and w = (x_b - x_a) L ln2 +
+// lw_ab.  The workgroups loop over the items (their number is read from the
+// queue's count).
+template <int DT, bool VEC, int K>
+__global__ __launch_bounds__(kThreads) void k_cons_exact(Params p) {
+  __shared__ ConsShared sh;
+  constexpr int P = Elem<DT>::P;
+  constexpr int NP = K * (K - 1);
+  const int64_t nch = (p.V + chunk_cons(DT) - 1) / chunk_cons(DT);
+  const int64_t items = (int64_t)p.hdr[1] * nch;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int64_t pos = p.cons_queue[it / nch], chunk = it % nch;
+    const int b = p.pair2req[pos];
+    const float Lhi = (float)(kLog2eD / (double)p.temp[b]);
+    const float c = (float)((double)Lhi * kLn2D);
+    // one vector of every row at a time (a rolled loop keeps the registers of
+    // the pair terms bounded), the next vector's loads in flight meanwhile
+    const auto load_vec = [&](int k, uint4* q) {
+      const int64_t e0 = cons_e0<DT>(chunk, k);
+#pragma unroll
+      for (int a = 0; a < K; ++a) q[a] = fetch_raw<DT, VEC>(p.target, pos * K + a, p.V, e0);
+    };
+    uint4 cur[K], nxt[K];
+    load_vec(0, cur);
+    cons_row_stats<K>(p, pos, nch, sh);
+    float ct[K], kt[K];
+#pragma unroll
+    for (int a = 0; a < K; ++a) {
+      ct[a] = sh.Mrow[a];
+      kt[a] = (float)(1.0 / sh.Srow[a]);
+    }
+    // Per unordered pair a < b: lw = ln(q_b / q_a) - (x_b - x_a) L ln2, so that
+    // w_ab = (x_b - x_a) c + lw and w_ba = -w_ab exactly; q_a g(w_ab) and
+    // q_b g(w_ba) share the even and odd parts of g's series.
+    constexpr int NU = NP / 2;
+    float lw[NU];
+    {
+      int u = 0;
+#pragma unroll
+      for (int a = 0; a < K; ++a)
+#pragma unroll
+        for (int bb = a + 1; bb < K; ++bb)
+          lw[u++] = (float)((double)(sh.Mrow[a] - sh.Mrow[bb]) * kLn2D + log(sh.Srow[a] / sh.Srow[bb]));
+    }
+    double acc[NP];
+#pragma unroll
+    for (int q = 0; q < NP; ++q) acc[q] = 0.0;
+#pragma unroll 1
+    for (int k = 0; k < kConsVec; ++k) {  // fp32 partial sums over one vector (P elements), fp64 beyond
+      if (k + 1 < kConsVec) load_vec(k + 1, nxt);
+      float v[K][P];
+#pragma unroll
+      for (int a = 0; a < K; ++a) {
+        unpack<DT>(cur[a], v[a]);
+        cons_mask<DT, VEC>(v[a], cons_e0<DT>(chunk, k), p.V);
+      }
+      float part[NP];
+#pragma unroll
+      for (int q = 0; q < NP; ++q) part[q] = 0.f;
+#pragma unroll
+      for (int e = 0; e < P; ++e) {
+        float qv[K];
+#pragma unroll
+        for (int a = 0; a < K; ++a) qv[a] = __builtin_amdgcn_exp2f(fmaf(v[a][e], Lhi, -ct[a])) * kt[a];
+        int u = 0;
+#pragma unroll
+        for (int a = 0; a < K; ++a)
+#pragma unroll
+          for (int bb = a + 1; bb < K; ++bb) {
+            const float wv = fmaf(v[bb][e] - v[a][e], c, lw[u++]);
+            const float w2 = wv * wv;
+            float ev = fmaf(w2, 1.0f / 40320.0f, 1.0f / 720.0f);  // g(w) = E + O, g(-w) = E - O (series to w^9)
+            ev = fmaf(w2, ev, 1.0f / 24.0f);
+            ev = fmaf(w2, ev, 0.5f) * w2;
+            float od = fmaf(w2, 1.0f / 362880.0f, 1.0f / 5040.0f);
+            od = fmaf(w2, od, 1.0f / 120.0f);
+            od = fmaf(w2, od, 1.0f / 6.0f) * (w2 * wv);
+            const bool sm = fabsf(wv) < 0.5f;
+            const float dq = qv[bb] - qv[a];
+            // q_a g(w) = q_b - q_a - q_a w and q_b g(-w) = q_a - q_b + q_b w away from 0
+            const float ab = sm ? qv[a] * (ev + od) : fmaf(-qv[a], wv, dq);
+            const float ba = sm ? qv[bb] * (ev - od) : fmaf(qv[bb], wv, -dq);
+            part[cons_pair_index<K>(a, bb)] += ab;  // positions past the end give 0
+            part[cons_pair_index<K>(bb, a)] += ba;
+          }
+      }
+#pragma unroll
+      for (int q = 0; q < NP; ++q) acc[q] += (double)part[q];
+#pragma unroll
+      for (int a = 0; a < K; ++a) cur[a] = nxt[a];
+    }
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      const double t = wave_sum_d(acc[q]);
+      if (lane == 0) sh.d[q][w] = t;
+    }
+    __syncthreads();
+    if (threadIdx.x < NP) {
+      const int q = threadIdx.x;
+      double t = sh.d[q][0];
+#pragma unroll
+      for (int k = 1; k < kWaves; ++k) t += sh.d[q][k];
+      p.cons_exact[(pos * nch + chunk) * NP + q] = t;
+    }
+    __syncthreads();  // LDS is reused by the next item
+  }
+}
+
+// Finish (one wave per queue slot): the matrix from the exact chunk sums
+// (a fixed-order wave reduction), the closest pair and the state.
+template <int K>
+__global__ __launch_bounds__(kThreads) void k_cons_finish(Params p, int64_t nch) {
+  constexpr int NP = K * (K - 1);
+  const int lane = threadIdx.x & 63;
+  const int64_t slot = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  if (slot >= p.hdr[1]) return;  // wave-uniform
+  const int64_t pos = p.cons_queue[slot];
+  double sl[NP];
+#pragma unroll
+  for (int q = 0; q < NP; ++q) sl[q] = 0.0;
+  for (int64_t ch = lane; ch < nch; ch += 64)
+#pragma unroll
+    for (int q = 0; q < NP; ++q) sl[q] += p.cons_exact[(pos * nch + ch) * NP + q];
+  double kl[NP];
+#pragma unroll
+  for (int q = 0; q < NP; ++q) kl[q] = wave_sum_d(sl[q]);
+  if (lane != 0) return;
+  const double lnV = log((double)p.V);
+  double m[K][K], dist[K][K];
+#pragma unroll
+  for (int a = 0; a < K; ++a)
+#pragma unroll
+    for (int bb = 0; bb < K; ++bb)
+      m[a][bb] = (a == bb || p.V == 1) ? 0.0 : kl[cons_pair_index<K>(a, bb)] / lnV;
+#pragma unroll
+  for (int a = 0; a < K; ++a)
+#pragma unroll
+    for (int bb = a + 1; bb < K; ++bb) dist[a][bb] = 0.5 * (m[a][bb] + m[bb][a]);
+  cons_write<K>(p, pos, m, dist);
+}
+
+// ----------------------------------------------------------------------------
 // plain-read probe (measurement aid): streams a buffer with the statistics
 // pass's partition -- static contiguous ranges of 16 KB items, one per
 // workgroup, the next item's loads in flight while the current one is folded
@@ -2665,6 +3170,51 @@ int launch_read_probe(const void* buf, int64_t bytes, int wgs_per_cu, void* sink
   uint32_t* k = static_cast<uint32_t*>(sink);
   if (e0 && e1) hipExtLaunchKernelGGL(k_read_probe, grid, dim3(kThreads), 0, s, e0, e1, 0, b, nitems, k);
   else hipLaunchKernelGGL(k_read_probe, grid, dim3(kThreads), 0, s, b, nitems, k);
+  return (int)hipGetLastError();
+}
+
+namespace {
+template <int DT, bool VEC, int K>
+void cons_launch(const Params& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  const int64_t nch = (p.V + chunk_cons(DT) - 1) / chunk_cons(DT);
+  const dim3 blk(kThreads), gp((unsigned)((int64_t)p.R_d * nch));
+  // e0 / e1 take the pass's own start and end timestamps
+  if (e0 && e1) hipExtLaunchKernelGGL((k_cons_pass<DT, VEC, K>), gp, blk, 0, s, e0, e1, 0, p);
+  else hipLaunchKernelGGL((k_cons_pass<DT, VEC, K>), gp, blk, 0, s, p);
+  const dim3 gw((unsigned)((p.R_d + kWaves - 1) / kWaves));  // one wave per position
+  hipLaunchKernelGGL((k_cons_merge<K>), gw, blk, 0, s, p, nch);
+  const dim3 ge((unsigned)std::min<int64_t>((int64_t)p.R_d * nch, kConsExactGrid));
+  hipLaunchKernelGGL((k_cons_exact<DT, VEC, K>), ge, blk, 0, s, p);
+  hipLaunchKernelGGL((k_cons_finish<K>), gw, blk, 0, s, p, nch);
+}
+template <int DT, bool VEC>
+void cons_k(const Params& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  switch (p.cons_k) {
+    case 2: cons_launch<DT, VEC, 2>(p, s, e0, e1); break;
+    case 3: cons_launch<DT, VEC, 3>(p, s, e0, e1); break;
+    default: cons_launch<DT, VEC, 4>(p, s, e0, e1); break;
+  }
+}
+}  // namespace
+
+int launch_consensus(const Params& p, bool vec, void* stream, void* ev_start, void* ev_stop) {
+  hipStream_t s = (hipStream_t)stream;
+  hipEvent_t e0 = (hipEvent_t)ev_start, e1 = (hipEvent_t)ev_stop;
+  hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, s, p);
+  if (p.R_d == 0 && e0 && e1) {  // nothing to stream: the two events become plain markers
+    hipError_t e = hipEventRecord(e0, s);
+    if (e == hipSuccess) e = hipEventRecord(e1, s);
+    if (e != hipSuccess) return (int)e;
+  }
+  if (p.R_d > 0) {
+    if (p.dtype == SV_DTYPE_BF16) {
+      if (vec) cons_k<SV_DTYPE_BF16, true>(p, s, e0, e1);
+      else cons_k<SV_DTYPE_BF16, false>(p, s, e0, e1);
+    } else {
+      if (vec) cons_k<SV_DTYPE_F32, true>(p, s, e0, e1);
+      else cons_k<SV_DTYPE_F32, false>(p, s, e0, e1);
+    }
+  }
   return (int)hipGetLastError();
 }
 

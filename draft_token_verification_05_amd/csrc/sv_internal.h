@@ -27,8 +27,13 @@ constexpr int kFusedPerCu = 4;        // resident workgroups per compute unit of
 constexpr int kCntStride = 64;     // in 32-bit words (KL second-pass counters)
 constexpr int kArrStride = 32;     // in 64-bit words (epoch-tagged helper counters)
 constexpr int kTopkMax = 16;  // largest k of the per-row top-k
+constexpr int kConsMaxDrafts = 4;  // largest number of drafts of the consensus pass
+constexpr int kModeConsensus = 16;  // internal mode value of the consensus calls (k_prep builds the position map)
+// vocabulary elements of one consensus chunk: kThreads x 4 vectors of each row
 
 constexpr int elems_per_vec(int dtype) { return dtype == SV_DTYPE_BF16 ? 8 : 4; }
+// Elements of one consensus chunk (one workgroup, four vectors per thread).
+constexpr int64_t chunk_cons(int dtype) { return (int64_t)kThreads * 4 * elems_per_vec(dtype); }
 constexpr int elem_size(int dtype) { return dtype == SV_DTYPE_BF16 ? 2 : 4; }
 // vocabulary elements covered by one chunk of each pass
 constexpr int64_t chunk_a(int dtype) { return (int64_t)kThreads * kUA * elems_per_vec(dtype); }
@@ -91,6 +96,32 @@ struct Layout {
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace of a consensus call (B requests, npos positions, K drafts each).
+struct ConsLayout {
+  size_t off_hdr, off_doff, off_pos2req, off_stats, off_tz, off_queue, off_exact, total;
+  int64_t nch;
+};
+inline ConsLayout make_cons_layout(int64_t B, int64_t V, int dtype, int64_t npos, int64_t K) {
+  ConsLayout L{};
+  L.nch = (V + chunk_cons(dtype) - 1) / chunk_cons(dtype);
+  const int64_t P1 = npos > 0 ? npos : 1;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  L.off_hdr = take(256);
+  L.off_doff = take(sizeof(int32_t) * (B + 1));
+  L.off_pos2req = take(sizeof(int32_t) * P1);
+  L.off_stats = take(16 * (size_t)(P1 * K * L.nch));
+  L.off_tz = take(2 * sizeof(double) * (size_t)(P1 * L.nch * K * (K - 1)));
+  L.off_queue = take(sizeof(int32_t) * P1);
+  L.off_exact = take(sizeof(double) * (size_t)(P1 * L.nch * K * (K - 1)));
+  L.total = o;
+  return L;
+}
 
 inline Layout make_layout(int64_t B, int64_t V, int dtype, int64_t R_d) {
   Layout L{};
@@ -180,6 +211,16 @@ struct Params {
   double* kl_part;    // [R_d * nslices] second-pass KL sums per slice
   uint64_t* topk_cand;  // [B * kThreads] top-k candidates: helper h of row b at b * kThreads + h * topk
   int32_t topk;         // k of the per-row top-k
+  // consensus across drafts: K draft rows per position (row pos * K + a)
+  int32_t cons_k;
+  float cons_dc, cons_dd;   // consensus / divergence thresholds of the closest pair's distance
+  float* cons_nkl;          // [positions][K][K] (NULL: not written)
+  int32_t* cons_state;      // [positions]
+  int32_t* cons_pair;       // [positions]
+  float* cons_stats;        // [positions][K][nch] x {m, pad, S (2 floats as a double)}: row-chunk statistics
+  double* cons_tz;          // [positions][nch][K(K-1)] x {t, z}: one-pass cross sums per chunk and ordered pair
+  int32_t* cons_queue;      // [positions]: positions whose one-pass values are not accurate enough (count: hdr[1])
+  double* cons_exact;       // [positions][nch][K(K-1)]: exact KL sums per chunk and ordered pair
 };
 
 // kernel launchers (kernels.hip); return the hipError_t of the launch as int
@@ -209,6 +250,9 @@ int launch_sample(const Params& p, bool vec, void* stream, void* ev_start, void*
 int plan_topk(Params& p, bool vec);
 int launch_topk(const Params& p, bool vec, void* stream, void* ev_start, void* ev_stop);
 int launch_fused(const Params& p, bool vec, int grid, void* stream, void* ev_start, void* ev_stop);
+// Consensus across drafts: k_prep (position -> request map), then the row
+// statistics, the exact KL sums and the final per-position decision.
+int launch_consensus(const Params& p, bool vec, void* stream, void* ev_start, void* ev_stop);
 // plain-read probe over `bytes` (a multiple of 16 KB is read) with wgs_per_cu workgroups per CU
 int launch_read_probe(const void* buf, int64_t bytes, int wgs_per_cu, void* sink, void* stream, void* ev_start,
                       void* ev_stop);

@@ -77,7 +77,7 @@
 extern "C" {
 #endif
 
-#define SPECVERIFY_VERSION 10200 /* 1.2.0: block-accept mode (SV_MODE_BLOCK, sv_config.block_min_len) */
+#define SPECVERIFY_VERSION 10300 /* 1.3.0: consensus across drafts (spec_consensus) */
 
 /* status codes */
 #define SV_OK 0
@@ -259,6 +259,43 @@ int spec_sample_rows(const void* logits, const float* temperature, const float* 
  * struct_size, k out of range), SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP.
  */
 int spec_topk_rows(const void* logits, int32_t k, int32_t* out_idx, const sv_config* cfg);
+
+/*
+ * Consensus across several drafts ("Chain of Draft" page, section 4.4, Consensus-Aware Accept:
+ * the pairwise NKL distance matrix of the drafts; a pair below 0.1 is a consensus, every pair
+ * above 0.15 a divergence).  Request b has gamma_b positions; each position holds num_drafts
+ * draft rows (one per draft model), all at the request's temperature.  Per position:
+ *     M[a][b] = KL(q_a || q_b) / ln V    (q_a = softmax(row a / T); 0 when V == 1),
+ *     distance of a pair a < b = (M[a][b] + M[b][a]) / 2,
+ *     pair  = a * num_drafts + b of the closest pair (lowest (a, b) on ties),
+ *     state = 1 (consensus) if that distance < delta_c, 2 (divergence) if it is > delta_d (so
+ *             every pair is), else 0.
+ * One read of the rows gives each KL value with an error estimate; positions where an estimate
+ * exceeds 1e-5 of its value, or where a threshold or a near tie of the closest pair lies within
+ * the estimates, are recomputed in the exact form (sum_y q_a (e^w - 1 - w), w = ln(q_b / q_a),
+ * no cancellation) by a second read of their rows.
+ *
+ * draft_logits [total_draft_rows][num_drafts][V] of cfg->dtype: the drafts of one position are
+ *              consecutive rows (position n, draft a: row n * num_drafts + a).
+ * num_drafts   2 .. 4.
+ * gamma_per_req int32 [B] (positions per request), temperature float32 [B].
+ * out_nkl      float32 [total_draft_rows][num_drafts][num_drafts] (may be NULL).
+ * out_state, out_pair int32 [total_draft_rows].
+ * cfg          batch, vocab, dtype, max_gamma, total_draft_rows (= sum of gamma), stream,
+ *              workspace (>= spec_consensus_workspace_size(cfg, num_drafts); no initialisation
+ *              needed), phase_events ([1] and [2] take the start and end of the pass over
+ *              all the rows).
+ * Data errors: a request whose temperature is not > 0 and finite gets state -1, pair -1 and
+ * NaN in out_nkl at its positions; a negative gamma or sum(gamma) != total_draft_rows gives -1
+ * everywhere.  Synchronous errors: SV_EINVAL (NULL or misaligned pointer, bad cfg, num_drafts
+ * out of range, non-finite threshold), SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP.
+ */
+int spec_consensus(const void* draft_logits, int32_t num_drafts, const int32_t* gamma_per_req,
+                   const float* temperature, float delta_c, float delta_d, float* out_nkl, int32_t* out_state,
+                   int32_t* out_pair, const sv_config* cfg);
+
+/* Workspace bytes of spec_consensus (0 for an invalid cfg or num_drafts). */
+size_t spec_consensus_workspace_size(const sv_config* cfg, int32_t num_drafts);
 
 #ifdef __cplusplus
 }

@@ -416,6 +416,68 @@ def make_multi_draft(B: int = 16, K: int = 3, gamma: int = 6, V: int = 128256, s
                     meta={"K": K, "gamma": gamma})
 
 
+@dataclass
+class ConsensusWorkload:
+    """Inputs of the consensus pass: K draft rows per position (the drafts of
+    one position consecutive), one temperature per request."""
+    name: str
+    B: int
+    K: int
+    V: int
+    dtype: str  # "bf16" (uint16 bit patterns) or "f32"
+    gamma: np.ndarray  # int32 [B]
+    drafts: np.ndarray  # [sum(gamma) * K, V] stored values
+    temperature: np.ndarray  # float32 [B]
+    max_gamma: int = 0
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def npos(self) -> int:
+        return int(self.gamma.astype(np.int64).sum())
+
+    @property
+    def logit_bytes(self) -> int:
+        return int(self.drafts.nbytes)
+
+
+def make_consensus(B: int = 32, K: int = 3, gamma=5, V: int = 128256, dtype: str = "bf16",
+                   spread=(0.3, 2.0), temps=(0.7, 1.0, 1.3), seed: int = BASE_SEED,
+                   wid: int = 7) -> ConsensusWorkload:
+    """K draft models' rows at every drafted position.  Position n has a base
+    row 3*N(0,1) + 8 spike (the target-like shape of the other workloads); its
+    spread s_n is log-uniform in ``spread``; draft a's row is the base plus
+    s_n (1 + a/4) N(0,1).  At T = 1 and the Llama-3 vocabulary the closest
+    pair's NKL is about 0.09 at s = 1 and 0.23 at s = 1.5, so the default range
+    gives consensus, divergence and in-between positions.  Temperatures are
+    drawn per request from ``temps``; ``gamma`` is an int or an int32 [B]."""
+    gam = np.full(B, int(gamma), np.int32) if np.isscalar(gamma) else np.ascontiguousarray(gamma, np.int32)
+    assert gam.shape == (B,)
+    npos = int(np.maximum(gam, 0).astype(np.int64).sum())
+    base = _target_rows(wid, npos, V, 3.0, 8.0, seed)
+    lo, hi = np.log(spread[0]), np.log(spread[1])
+    s = np.array([np.exp(lo + (hi - lo) * _gen(wid, _P_PARAM, n, seed).random()) for n in range(npos)], np.float32)
+    rows = np.repeat(np.arange(npos), K)
+    sigma = (s[rows] * (1.0 + 0.25 * np.tile(np.arange(K), npos))).astype(np.float32)
+    drafts = _round_store(_draft_rows(wid, base, rows, sigma, seed), dtype)
+    del base
+    tsel = _gen(wid, _P_PARAM, npos + 1, seed).integers(0, len(temps), B)
+    temperature = np.asarray(temps, np.float32)[tsel]
+    return ConsensusWorkload(f"consensus{K}", B, K, V, dtype, gam, drafts, temperature,
+                             int(max(0, gam.max()) if B else 0), {"spread": spread})
+
+
+def consensus_to_device(w: ConsensusWorkload, dev: str = "cuda:0") -> dict:
+    """Uploads a consensus workload (drafts as a [positions, K, V] tensor)."""
+    import torch
+    if w.dtype == "bf16":
+        d = torch.from_numpy(np.ascontiguousarray(w.drafts).view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        d = torch.from_numpy(np.ascontiguousarray(w.drafts, np.float32)).to(dev)
+    return {"drafts": d.view(w.npos, w.K, w.V),
+            "gamma": torch.from_numpy(np.ascontiguousarray(w.gamma, np.int32)).to(dev),
+            "temperature": torch.from_numpy(np.ascontiguousarray(w.temperature, np.float32)).to(dev)}
+
+
 WORKLOADS = {
     "tiny": make_tiny,
     "llama3": make_llama3,

@@ -25,7 +25,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["spec_sample_rows", "spec_topk_rows", "spec_verify", "spec_verify_noalloc",
+    assert declared_functions() == ["spec_consensus", "spec_consensus_workspace_size", "spec_sample_rows",
+                                    "spec_topk_rows", "spec_verify", "spec_verify_noalloc",
                                     "spec_verify_single_dispatch", "spec_verify_status_string", "spec_verify_version",
                                     "spec_verify_workspace_size"]
 
@@ -55,7 +56,7 @@ def test_library_exports_every_declared_symbol(sv):
 
 
 def test_version_and_status_strings(sv):
-    assert sv.spec_verify_version() == 10200
+    assert sv.spec_verify_version() == 10300
     for st in (0, -1, -2, -3, -4):
         assert sv.spec_verify_status_string(st).startswith("SV_")
     assert "unknown" in sv.spec_verify_status_string(7)
@@ -210,3 +211,42 @@ def test_topk_rows_argument_errors(sv):
                {"dtype": 2}, {"logits": FAKE + 1}, {"out": FAKE + 2}):
         assert topk(**kw) == E, kw
     assert topk(ws=0) == W
+
+
+def test_consensus_argument_errors(sv):
+    """spec_consensus: host-side checks (nothing is enqueued); validation
+    reaches the too-small workspace when everything else is right."""
+    E, W, U = sv.SV_EINVAL, sv.SV_EWORKSPACE, sv.SV_EUNSUPPORTED
+
+    def cons(d=FAKE, K=3, g=FAKE, T=FAKE, dc=0.1, dd=0.15, nkl=FAKE, st=FAKE, pr=FAKE, B=4, V=1000, dtype=1,
+             mg=6, npos=24, ws=FAKE, ws_bytes=16, size_delta=0):
+        cfg = sv.make_config(B, V, dtype, mg, npos, 0, ws, ws_bytes)
+        cfg.struct_size += size_delta
+        return sv.spec_consensus(d, K, g, T, dc, dd, nkl, st, pr, cfg)
+
+    assert cons() == W
+    assert cons(nkl=0) == W  # the matrix output is optional
+    assert cons(d=0, npos=0) == W  # no positions: no rows to read
+    for kw in ({"K": 1}, {"K": 5}, {"K": 0}, {"d": 0}, {"g": 0}, {"T": 0}, {"st": 0}, {"pr": 0},
+               {"dc": float("nan")}, {"dd": float("inf")}, {"B": 0}, {"V": 0}, {"dtype": 2}, {"mg": -1},
+               {"npos": -1}, {"npos": 25}, {"d": FAKE + 1}, {"dtype": 0, "d": FAKE + 2}, {"g": FAKE + 2},
+               {"T": FAKE + 1}, {"nkl": FAKE + 2}, {"st": FAKE + 1}, {"pr": FAKE + 3}, {"size_delta": 8}):
+        assert cons(**kw) == E, kw
+    assert cons(mg=4097, npos=24) == U
+    assert cons(ws=0) == W
+    assert cons(ws=FAKE + 64, ws_bytes=1 << 30) == W
+
+
+def test_consensus_workspace_size(sv):
+    cfg = sv.make_config(16, 128256, sv.SV_DTYPE_BF16, 6, 96)
+    sizes = [sv.spec_consensus_workspace_size(cfg, k) for k in (2, 3, 4)]
+    assert all(n > 0 and n % 256 == 0 for n in sizes)
+    assert sizes[0] < sizes[1] < sizes[2]
+    for k in (0, 1, 5):
+        assert sv.spec_consensus_workspace_size(cfg, k) == 0
+    bad = sv.make_config(16, 128256, sv.SV_DTYPE_BF16, 6, 96)
+    bad.struct_size += 8
+    assert sv.spec_consensus_workspace_size(bad, 3) == 0
+    assert sv.spec_consensus_workspace_size(sv.make_config(16, 128256, 2, 6, 96), 3) == 0
+    # no positions still needs the header and offsets
+    assert sv.spec_consensus_workspace_size(sv.make_config(16, 128256, 1, 6, 0), 3) > 0

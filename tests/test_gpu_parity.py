@@ -78,7 +78,7 @@ def test_ragged_stochastic():
 
 
 @pytest.mark.parametrize("name", ["tiny", "tiny_greedy", "llama3", "long_greedy", "long_nkl", "ragged", "tree",
-                                  "tree13"])
+                                  "tree13", "multi_draft"])
 def test_bench_calls_match_oracle(name):
     """The calls the benchmark times, element by element against the oracle:
     no diagnostic outputs (in stochastic mode the decision passes then stop at
