@@ -24,7 +24,8 @@ from dataclasses import dataclass
 from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libspecverify.so")
+# SPECVERIFY_LIB: another build of the library (default: the one in this package)
+LIB_PATH = os.environ.get("SPECVERIFY_LIB") or os.path.join(_PKG, "libspecverify.so")
 
 SV_OK, SV_EINVAL, SV_EUNSUPPORTED, SV_EWORKSPACE, SV_EHIP = 0, -1, -2, -3, -4
 SV_MODE_STOCHASTIC, SV_MODE_GREEDY, SV_MODE_NKL, SV_MODE_TREE_GREEDY, SV_MODE_BLOCK = 0, 1, 2, 3, 4

@@ -413,8 +413,10 @@ int spec_consensus(const void* draft_logits, int32_t num_drafts, const int32_t* 
   p.pair2req = reinterpret_cast<int32_t*>(ws + L.off_pos2req);
   p.cons_stats = reinterpret_cast<float*>(ws + L.off_stats);
   p.cons_tz = reinterpret_cast<double*>(ws + L.off_tz);
-  p.cons_queue = reinterpret_cast<int32_t*>(ws + L.off_queue);
-  p.cons_exact = reinterpret_cast<double*>(ws + L.off_exact);
+  p.cnt = reinterpret_cast<uint64_t*>(ws + L.off_cnt);
+  p.cons_lds = cfg->batch <= sv::kLdsBatch ? 1 : 0;
+  p.epoch = next_epoch();
+  p.wait_polls = kDefaultWaitPolls;
   const bool vec = ((size_t)cfg->vocab * es) % 16 == 0 && (!draft_logits || aligned(draft_logits, 16));
   hipStream_t s = static_cast<hipStream_t>(cfg->stream);
   hipEvent_t* ev = static_cast<hipEvent_t*>(cfg->phase_events);

@@ -1372,6 +1372,17 @@ __device__ __forceinline__ void claim(uint64_t* c, uint64_t cur, uint32_t epoch)
       break;
 }
 
+// The same claim without waiting for the swap's result: only a word that
+// carries another epoch is swapped, and a swap that fails because another
+// workgroup of the call claimed the word first changes nothing.  The swap
+// still completes before the workgroup counts itself (arrive_last waits for
+// all of its memory operations).
+__device__ __forceinline__ void claim_nowait(uint64_t* c, uint64_t cur, uint32_t epoch) {
+  if ((uint32_t)(cur >> 32) != epoch)
+    __hip_atomic_compare_exchange_strong(c, &cur, (uint64_t)epoch << 32, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Counts this workgroup on the request's claimed counter once every memory
 // operation of the workgroup (its stores and the claim) has completed; true in
 // the last of the `H` arrivals.
@@ -2304,15 +2315,19 @@ __global__ __launch_bounds__(kThreads) void k_refine(Params p) {
 // those sums.
 // ----------------------------------------------------------------------------
 
-constexpr int kConsVec = 4;  // 16-byte vectors per thread per row per chunk
 constexpr int kConsMaxPairs = kConsMaxDrafts * (kConsMaxDrafts - 1);
-constexpr int kConsExactGrid = 2048;  // workgroups of the exact pass (a loop over the queued items)
+constexpr int kConsRing = 2;  // vectors of every row in flight per thread
+static_assert(kConsVec % kConsRing == 0, "whole rounds of the ring");
 
 struct ConsShared {
   float m[kConsMaxDrafts][kWaves];
   double d[kConsMaxDrafts + 2 * kConsMaxPairs][kWaves];
   float Mrow[kConsMaxDrafts];
   double Srow[kConsMaxDrafts];
+  double tot[kConsMaxPairs];  // exact sums of the position (the last workgroup)
+  long long scan[kWaves];
+  float T;
+  int req, bad, need, flag;
 };
 
 // Ordered pair (a, b), a != b, at a * (K - 1) + (b < a ? b : b - 1).
@@ -2321,7 +2336,7 @@ __device__ __forceinline__ constexpr int cons_pair_index(int a, int b) {
   return a * (K - 1) + (b < a ? b : b - 1);
 }
 
-// Elements [e0, e0 + P) of draft row `row` for vector k of chunk `chunk` and thread t.
+// First element of vector k of chunk `chunk` for this thread.
 template <int DT>
 __device__ __forceinline__ int64_t cons_e0(int64_t chunk, int k) {
   return (chunk * kConsVec * kThreads + (int64_t)k * kThreads + threadIdx.x) * Elem<DT>::P;
@@ -2354,32 +2369,396 @@ __device__ __forceinline__ int cons_ref(float vm, float Lhi) {
   return (int)fminf(fmaxf(r, -16000000.0f), 16000000.0f);  // NaN (an invalid T) gives the lower bound
 }
 
-// Pass over the rows, one vector of every row at a time with the next
-// vector's loads in flight.  Each thread keeps per row a running reference
-// exponent R and sums s = sum 2^(x L - R) (fmaf(x, L, -R): R is an integer,
-// so the single rounding is relative to the small exponent where the mass
-// is), t and z; when R grows the sums are rescaled by an exact power of two.
-// The workgroup then rescales to the chunk's largest R, also exactly.
-// Vectors wholly past the row's end are skipped; partial ones hold the pad,
-// which gives 0.
+// The request of position `pos` by a scan of gamma in LDS (batches of at most
+// kLdsBatch requests: thread t holds requests 4t .. 4t + 3, whose gamma and
+// temperature it loaded before the rows, so that the scan waits for those
+// loads only), with the layout check: sh.bad = 1 for a negative gamma or
+// sum(gamma) != R_d.  The thread that holds the request publishes its
+// temperature in sh.T.  All threads call.
+struct ConsReqIn {
+  int g[4];
+  float t[4];
+};
+__device__ __forceinline__ ConsReqIn cons_req_load(const Params& p) {
+  ConsReqIn in;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int b = 4 * threadIdx.x + j;
+    in.g[j] = b < p.B ? p.gamma[b] : 0;
+    in.t[j] = b < p.B ? p.temp[b] : 1.0f;
+  }
+  return in;
+}
+__device__ __forceinline__ void cons_find_request(const Params& p, int64_t pos, const ConsReqIn& in, ConsShared& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid == 0) {
+    sh.req = -1;
+    sh.bad = 0;
+  }
+  long long g[4], tot = 0;
+  bool neg = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    g[j] = in.g[j];
+    neg = neg || g[j] < 0;
+    g[j] = g[j] < 0 ? 0 : g[j];
+    tot += g[j];
+  }
+  const long long incl = wave_incl_scan_i64(tot);
+  if (lane == 63) sh.scan[w] = incl;
+  __syncthreads();
+  long long before = incl - tot, all = 0;
+#pragma unroll
+  for (int k = 0; k < kWaves; ++k) {
+    if (k < w) before += sh.scan[k];
+    all += sh.scan[k];
+  }
+  if (neg) sh.bad = 1;  // benign race: every writer stores 1
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (pos >= before && pos < before + g[j]) {
+      sh.req = 4 * tid + j;
+      sh.T = in.t[j];
+    }
+    before += g[j];
+  }
+  __syncthreads();
+  if (tid == 0 && (all != (long long)p.R_d || sh.req < 0)) sh.bad = 1;
+  __syncthreads();
+}
+
+// Reference exponents and sums of the position's K rows, merged over the
+// chunks: wave a < K takes row a, lane l the chunks l, l + 64, ..., then a
+// fixed-order wave reduction, so the result does not depend on which
+// workgroup computes it.  All threads call; results in sh.Mrow (R) / sh.Srow (S).
+template <int K>
+__device__ __forceinline__ void cons_row_stats(const Params& p, int64_t pos, int64_t nch, ConsShared& sh) {
+  static_assert(K <= kWaves, "one wave per draft row");
+  const int lane = threadIdx.x & 63, a = threadIdx.x >> 6;
+  if (a < K) {
+    const float* src = p.cons_stats + (pos * K + a) * nch * 4;
+    float R = -INFINITY;
+    for (int64_t c = lane; c < nch; c += 64) R = fmaxf(R, ld_dev(src + c * 4));
+    R = wave_max(R);
+    double S = 0.0;
+    for (int64_t c = lane; c < nch; c += 64)
+      S += ldexp(ld_dev(reinterpret_cast<const double*>(src + c * 4 + 2)), max((int)(ld_dev(src + c * 4) - R), -2000));
+    S = wave_sum_d(S);
+    if (lane == 0) {
+      sh.Mrow[a] = R;
+      sh.Srow[a] = S;
+    }
+  }
+  __syncthreads();
+}
+
+// Writes the outputs of position `pos` from its K x K matrix (one thread):
+// the closest pair a < b (lowest on ties) and its state.
+template <int K>
+__device__ __forceinline__ void cons_write(const Params& p, int64_t pos, const double (&m)[K][K]) {
+  if (p.cons_nkl)
+#pragma unroll
+    for (int a = 0; a < K; ++a)
+#pragma unroll
+      for (int bb = 0; bb < K; ++bb) p.cons_nkl[pos * K * K + a * K + bb] = (float)m[a][bb];
+  double best = INFINITY;
+  int pair = -1;
+#pragma unroll
+  for (int a = 0; a < K; ++a)
+#pragma unroll
+    for (int bb = a + 1; bb < K; ++bb) {
+      const double d = 0.5 * (m[a][bb] + m[bb][a]);
+      if (d < best) {
+        best = d;
+        pair = a * K + bb;
+      }
+    }
+  p.cons_pair[pos] = pair;
+  p.cons_state[pos] = best < (double)p.cons_dc ? 1 : (best > (double)p.cons_dd ? 2 : 0);
+}
+
+// -1 (and NaN in the matrix) for a position that has no valid answer.
+template <int K>
+__device__ __forceinline__ void cons_write_invalid(const Params& p, int64_t pos) {
+  p.cons_state[pos] = -1;
+  p.cons_pair[pos] = -1;
+  if (p.cons_nkl)
+    for (int k = 0; k < K * K; ++k) p.cons_nkl[pos * K * K + k] = __builtin_nanf("");
+}
+
+// Merge of the position's chunk records (one wave; the lanes take chunks l,
+// l + 64, ..., then fixed-order wave reductions) into the one-pass matrix
+// and its error estimates.  With q_a = 2^(x_a L - R_a) / S_a:
+//   KL_ab = c T_ab / S_a - (R_a - R_b) ln 2 - ln(S_a / S_b),
+// estimate kKlErr (c Z_ab / S_a + 1) as for the verify KL.  Returns (in every
+// lane) whether the exact pass is needed: an estimate above kKlRel of its
+// value, or the decision -- a threshold, the closest pair -- within the
+// estimates.  Otherwise lane 0 writes the outputs.
+template <int K>
+__device__ __forceinline__ bool cons_merge(const Params& p, int64_t pos, int64_t nch, float Lhi) {
+  constexpr int NP = K * (K - 1);
+  const int lane = threadIdx.x & 63;
+  const double c = (double)Lhi * kLn2D;
+  float R[K];
+  double sl[K], tl[NP], zl[NP];
+#pragma unroll
+  for (int a = 0; a < K; ++a) sl[a] = 0.0;
+#pragma unroll
+  for (int q = 0; q < NP; ++q) tl[q] = zl[q] = 0.0;
+  if (nch <= 64) {  // one chunk per lane: all records in one round of loads
+    const int64_t ch = lane;
+    const bool has = ch < nch;
+    float rc[K];
+    double sc[K], tc[NP], zc[NP];
+#pragma unroll
+    for (int a = 0; a < K; ++a) {
+      const float* src = p.cons_stats + ((pos * K + a) * nch + (has ? ch : 0)) * 4;
+      rc[a] = ld_dev(src);
+      sc[a] = ld_dev(reinterpret_cast<const double*>(src + 2));
+    }
+    const double* tz = p.cons_tz + (pos * nch + (has ? ch : 0)) * 2 * NP;
+#pragma unroll
+    for (int q = 0; q < NP; ++q) {
+      tc[q] = ld_dev(tz + 2 * q);
+      zc[q] = ld_dev(tz + 2 * q + 1);
+    }
+#pragma unroll
+    for (int a = 0; a < K; ++a) R[a] = wave_max(has ? rc[a] : -INFINITY);
+    if (has) {
+#pragma unroll
+      for (int a = 0; a < K; ++a) {
+        const double f = ldexp(1.0, max((int)(rc[a] - R[a]), -2000));  // exact
+        sl[a] = sc[a] * f;
+#pragma unroll
+        for (int bb = 0; bb < K; ++bb)
+          if (bb != a) {
+            const int q = cons_pair_index<K>(a, bb);
+            tl[q] = tc[q] * f;
+            zl[q] = zc[q] * f;
+          }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int a = 0; a < K; ++a) {
+      const float* src = p.cons_stats + (pos * K + a) * nch * 4;
+      float mx = -INFINITY;
+      for (int64_t ch = lane; ch < nch; ch += 64) mx = fmaxf(mx, ld_dev(src + ch * 4));
+      R[a] = wave_max(mx);
+    }
+    for (int64_t ch = lane; ch < nch; ch += 64) {
+      double f[K];
+#pragma unroll
+      for (int a = 0; a < K; ++a) {
+        const float* src = p.cons_stats + ((pos * K + a) * nch + ch) * 4;
+        f[a] = ldexp(1.0, max((int)(ld_dev(src) - R[a]), -2000));  // exact
+        sl[a] += ld_dev(reinterpret_cast<const double*>(src + 2)) * f[a];
+      }
+      const double* tz = p.cons_tz + (pos * nch + ch) * 2 * NP;
+#pragma unroll
+      for (int a = 0; a < K; ++a)
+#pragma unroll
+        for (int bb = 0; bb < K; ++bb)
+          if (bb != a) {
+            const int q = cons_pair_index<K>(a, bb);
+            tl[q] += ld_dev(tz + 2 * q) * f[a];
+            zl[q] += ld_dev(tz + 2 * q + 1) * f[a];
+          }
+    }
+  }
+  double S[K], T[NP], Z[NP];
+#pragma unroll
+  for (int a = 0; a < K; ++a) S[a] = wave_sum_d(sl[a]);
+#pragma unroll
+  for (int q = 0; q < NP; ++q) {
+    T[q] = wave_sum_d(tl[q]);
+    Z[q] = wave_sum_d(zl[q]);
+  }
+  const double lnV = log((double)p.V);
+  double m[K][K], err[K][K];
+  bool need = false;
+#pragma unroll
+  for (int a = 0; a < K; ++a)
+#pragma unroll
+    for (int bb = 0; bb < K; ++bb) {
+      m[a][bb] = 0.0;
+      err[a][bb] = 0.0;
+      if (a == bb || p.V == 1) continue;  // one token: both rows are the same point mass
+      const int q = cons_pair_index<K>(a, bb);
+      const double kl = T[q] / S[a] * c - (double)(R[a] - R[bb]) * kLn2D - log(S[a] / S[bb]);
+      const double e = kKlErr * (Z[q] / S[a] * c + 1.0);
+      need = need || !(e <= kKlRel * kl);
+      m[a][bb] = kl / lnV;
+      err[a][bb] = e / lnV;
+    }
+  double db = INFINITY, eb = 0.0;  // the closest pair's distance and estimate (lowest pair on ties)
+  int best = -1;
+#pragma unroll
+  for (int a = 0; a < K; ++a)
+#pragma unroll
+    for (int bb = a + 1; bb < K; ++bb) {
+      const double d = 0.5 * (m[a][bb] + m[bb][a]);
+      if (d < db) {
+        db = d;
+        eb = 0.5 * (err[a][bb] + err[bb][a]);
+        best = a * K + bb;
+      }
+    }
+  need = need || best < 0 || fabs(db - (double)p.cons_dc) <= eb || fabs(db - (double)p.cons_dd) <= eb;
+#pragma unroll
+  for (int a = 0; a < K; ++a)
+#pragma unroll
+    for (int bb = a + 1; bb < K; ++bb)  // another pair within the estimates of the closest one
+      if (a * K + bb != best && 0.5 * (m[a][bb] + m[bb][a]) - db <= 0.5 * (err[a][bb] + err[bb][a]) + eb) need = true;
+  if (!need && lane == 0) cons_write<K>(p, pos, m);
+  return need;
+}
+
+// Exact sums of one chunk of a position: per ordered pair (a, b), a != b,
+// the sum of q_a g(w), w = ln(q_b / q_a) = (x_b - x_a) c + lw_ab, with
+// q_a(y) = 2^(x_a L - R_a) / S_a (row statistics in sh.Mrow / sh.Srow).
+// One vector of every row at a time, the next vector's loads in flight;
+// q_a g(w_ab) and q_b g(w_ba) share the even and odd parts of g's series
+// (w_ba = -w_ab exactly).  The workgroup's sums end in sh.d[q][wave].
 template <int DT, bool VEC, int K>
-__global__ __launch_bounds__(kThreads) void k_cons_pass(Params p) {
+__device__ __forceinline__ void cons_exact_chunk(const Params& p, int64_t pos, int64_t chunk, float Lhi, ConsShared& sh) {
+  constexpr int P = Elem<DT>::P;
+  constexpr int NP = K * (K - 1);
+  constexpr int NU = NP / 2;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const float c = (float)((double)Lhi * kLn2D);
+  const auto load_vec = [&](int k, uint4* q) {
+    const int64_t e0 = cons_e0<DT>(chunk, k);
+#pragma unroll
+    for (int a = 0; a < K; ++a) q[a] = fetch_raw<DT, VEC>(p.target, pos * K + a, p.V, e0);
+  };
+  uint4 cur[K], nxt[K];
+  load_vec(0, cur);
+  float ct[K], kt[K], lw[NU];
+#pragma unroll
+  for (int a = 0; a < K; ++a) {
+    ct[a] = sh.Mrow[a];
+    kt[a] = (float)(1.0 / sh.Srow[a]);
+  }
+  {
+    int u = 0;
+#pragma unroll
+    for (int a = 0; a < K; ++a)
+#pragma unroll
+      for (int bb = a + 1; bb < K; ++bb)
+        lw[u++] = (float)((double)(sh.Mrow[a] - sh.Mrow[bb]) * kLn2D + log(sh.Srow[a] / sh.Srow[bb]));
+  }
+  double acc[NP];
+#pragma unroll
+  for (int q = 0; q < NP; ++q) acc[q] = 0.0;
+#pragma unroll 1
+  for (int k = 0; k < kConsVec; ++k) {  // fp32 partial sums over one vector (P elements), fp64 beyond
+    if (k + 1 < kConsVec) load_vec(k + 1, nxt);
+    float v[K][P];
+#pragma unroll
+    for (int a = 0; a < K; ++a) {
+      unpack<DT>(cur[a], v[a]);
+      cons_mask<DT, VEC>(v[a], cons_e0<DT>(chunk, k), p.V);
+    }
+    float part[NP];
+#pragma unroll
+    for (int q = 0; q < NP; ++q) part[q] = 0.f;
+#pragma unroll
+    for (int e = 0; e < P; ++e) {
+      float qv[K];
+#pragma unroll
+      for (int a = 0; a < K; ++a) qv[a] = __builtin_amdgcn_exp2f(fmaf(v[a][e], Lhi, -ct[a])) * kt[a];
+      int u = 0;
+#pragma unroll
+      for (int a = 0; a < K; ++a)
+#pragma unroll
+        for (int bb = a + 1; bb < K; ++bb) {
+          const float wv = fmaf(v[bb][e] - v[a][e], c, lw[u++]);
+          const float w2 = wv * wv;
+          float ev = fmaf(w2, 1.0f / 40320.0f, 1.0f / 720.0f);  // g(w) = E + O, g(-w) = E - O (series to w^9)
+          ev = fmaf(w2, ev, 1.0f / 24.0f);
+          ev = fmaf(w2, ev, 0.5f) * w2;
+          float od = fmaf(w2, 1.0f / 362880.0f, 1.0f / 5040.0f);
+          od = fmaf(w2, od, 1.0f / 120.0f);
+          od = fmaf(w2, od, 1.0f / 6.0f) * (w2 * wv);
+          const bool sm = fabsf(wv) < 0.5f;
+          const float dq = qv[bb] - qv[a];
+          // q_a g(w) = q_b - q_a - q_a w and q_b g(-w) = q_a - q_b + q_b w away from 0
+          const float ab = sm ? qv[a] * (ev + od) : fmaf(-qv[a], wv, dq);
+          const float ba = sm ? qv[bb] * (ev - od) : fmaf(qv[bb], wv, -dq);
+          part[cons_pair_index<K>(a, bb)] += ab;  // positions past the end give 0
+          part[cons_pair_index<K>(bb, a)] += ba;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < NP; ++q) acc[q] += (double)part[q];
+#pragma unroll
+    for (int a = 0; a < K; ++a) cur[a] = nxt[a];
+  }
+#pragma unroll
+  for (int q = 0; q < NP; ++q) {
+    const double t = wave_sum_d(acc[q]);
+    if (lane == 0) sh.d[q][w] = t;
+  }
+  __syncthreads();
+}
+
+// The whole consensus step in one dispatch: one workgroup per (position,
+// chunk).  Each sums its chunk of the K rows in one read -- per row s =
+// sum 2^(x L - R), per ordered pair t = sum 2^(x_a L - R_a) (x_a - x_b) and
+// z, the same with |x_a - x_b| -- against a running integer reference
+// exponent R per thread (fmaf(x, L, -R): the single rounding is relative to
+// the small exponent where the mass is; when R grows the sums are rescaled by
+// an exact power of two, and again to the chunk's largest R).  It writes the
+// chunk's records at device scope and counts itself on the position's
+// arrival counter; the last workgroup of the position merges the records
+// (cons_merge) and, where the one-pass values are not accurate enough, sums
+// the exact form over the position's chunks itself.  LDS: the request comes
+// from a scan of gamma in LDS (else from k_prep's map and layout flag).
+template <int DT, bool VEC, int K, bool LDS>
+__global__ __launch_bounds__(kThreads) void k_cons(Params p) {
   __shared__ ConsShared sh;
   constexpr int P = Elem<DT>::P;
   constexpr int NP = K * (K - 1);
   constexpr int NV = K + 2 * NP;  // s per row, then t and z per ordered pair
   const int64_t nch = (p.V + chunk_cons(DT) - 1) / chunk_cons(DT);
   const int64_t pos = blockIdx.x / nch, chunk = blockIdx.x % nch;
-  if (p.hdr[0] != 0) return;  // layout error (k_prep)
-  const int b = p.pair2req[pos];
-  const float Lhi = (float)(kLog2eD / (double)p.temp[b]);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const auto load_vec = [&](int k, uint4* q) {
+  uint64_t* cnt = p.cnt + pos * kArrStride;
+  const uint64_t cnt_cur = threadIdx.x == kClaimThread ? claim_load(cnt) : 0;  // issued before the rows
+  ConsReqIn rin{};
+  if (LDS) rin = cons_req_load(p);  // issued before the rows: the scan waits for these only
+  // a ring of kConsRing vectors of every row in flight: slot k % kConsRing
+  // is reloaded with vector k + kConsRing as soon as vector k is unpacked
+  uint4 raw[kConsRing][K];
+#pragma unroll
+  for (int k = 0; k < kConsRing; ++k) {
     const int64_t e0 = cons_e0<DT>(chunk, k);
 #pragma unroll
-    for (int a = 0; a < K; ++a) q[a] = fetch_raw<DT, VEC>(p.target, pos * K + a, p.V, e0);
-  };
-  const auto rescale = [&](double* acc, int a, int sh_exp) {
+    for (int a = 0; a < K; ++a) raw[k][a] = fetch_raw<DT, VEC>(p.target, pos * K + a, p.V, e0);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // the loads go out before any of them is used
+  // claimed now (its swap runs meanwhile), before this workgroup counts itself
+  if (threadIdx.x == kClaimThread) claim_nowait(cnt, cnt_cur, p.epoch);
+  bool bad;
+  float T;
+  if (LDS) {
+    cons_find_request(p, pos, rin, sh);
+    bad = sh.bad != 0;
+    T = bad ? 1.0f : sh.T;
+  } else {
+    bad = p.hdr[0] != 0;
+    T = bad ? 1.0f : p.temp[p.pair2req[pos]];
+  }
+  const bool valid = !bad && temp_ok(T);
+  const float Lhi = valid ? (float)(kLog2eD / (double)T) : 1.0f;
+  int R[K];
+  double acc[NV];
+#pragma unroll
+  for (int a = 0; a < K; ++a) R[a] = kConsRNone;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) acc[i] = 0.0;
+  const auto rescale = [&](int a, int sh_exp) {
     acc[a] = ldexp(acc[a], sh_exp);
 #pragma unroll
     for (int bb = 0; bb < K; ++bb)
@@ -2389,30 +2768,27 @@ __global__ __launch_bounds__(kThreads) void k_cons_pass(Params p) {
         acc[q + 1] = ldexp(acc[q + 1], sh_exp);
       }
   };
-  int R[K];
-  double acc[NV];
 #pragma unroll
-  for (int a = 0; a < K; ++a) R[a] = kConsRNone;
-#pragma unroll
-  for (int i = 0; i < NV; ++i) acc[i] = 0.0;
-  uint4 cur[K], nxt[K];
-  load_vec(0, cur);
-#pragma unroll 1
   for (int k = 0; k < kConsVec; ++k) {
-    if (k + 1 < kConsVec) load_vec(k + 1, nxt);
     const int64_t e0 = cons_e0<DT>(chunk, k);
-    if (e0 < p.V) {
-      float v[K][P];
+    float v[K][P];
+#pragma unroll
+    for (int a = 0; a < K; ++a) unpack<DT>(raw[k % kConsRing][a], v[a]);
+    if (k + kConsRing < kConsVec) {
+      const int64_t e1 = cons_e0<DT>(chunk, k + kConsRing);
+#pragma unroll
+      for (int a = 0; a < K; ++a) raw[k % kConsRing][a] = fetch_raw<DT, VEC>(p.target, pos * K + a, p.V, e1);
+    }
+    if (e0 < p.V) {  // vectors wholly past the row's end add nothing
       float nr[K];  // -R of each row after this vector
 #pragma unroll
       for (int a = 0; a < K; ++a) {
-        unpack<DT>(cur[a], v[a]);
-        cons_mask<DT, VEC>(v[a], e0, p.V);
+        if (!VEC) cons_mask<DT, VEC>(v[a], e0, p.V);  // rows of whole vectors: this one is inside
         float vm = v[a][0];
 #pragma unroll
         for (int e = 1; e < P; ++e) vm = fmaxf(vm, v[a][e]);
         const int rn = max(R[a], cons_ref(vm, Lhi));
-        rescale(acc, a, max(R[a] - rn, -2000));  // 0 when unchanged; the first vector scales zeros
+        rescale(a, max(R[a] - rn, -2000));  // 0 when unchanged; the first vector scales zeros
         R[a] = rn;
         nr[a] = -(float)rn;
       }
@@ -2442,8 +2818,7 @@ __global__ __launch_bounds__(kThreads) void k_cons_pass(Params p) {
 #pragma unroll
       for (int i = 0; i < NV; ++i) acc[i] += (double)part[i];
     }
-#pragma unroll
-    for (int a = 0; a < K; ++a) cur[a] = nxt[a];
+    __builtin_amdgcn_sched_barrier(0);  // one vector's terms at a time: bounded registers
   }
   // the chunk's reference of every row, then each thread's sums rescaled to it
 #pragma unroll
@@ -2457,7 +2832,7 @@ __global__ __launch_bounds__(kThreads) void k_cons_pass(Params p) {
     float Rc = sh.m[a][0];
 #pragma unroll
     for (int k = 1; k < kWaves; ++k) Rc = fmaxf(Rc, sh.m[a][k]);
-    rescale(acc, a, max(R[a] - (int)Rc, -2000));  // threads that saw no element hold zeros
+    rescale(a, max(R[a] - (int)Rc, -2000));  // threads that saw no element hold zeros
     if (threadIdx.x == 0) sh.Mrow[a] = Rc;
   }
 #pragma unroll
@@ -2466,325 +2841,54 @@ __global__ __launch_bounds__(kThreads) void k_cons_pass(Params p) {
     if (lane == 0) sh.d[i][w] = t;
   }
   __syncthreads();
-  if (threadIdx.x < NV) {
+  if (threadIdx.x < NV) {  // the chunk's records, read by the position's last workgroup
     const int i = threadIdx.x;
     double t = sh.d[i][0];
 #pragma unroll
     for (int k = 1; k < kWaves; ++k) t += sh.d[i][k];
     if (i < K) {
       float* dst = p.cons_stats + ((pos * K + i) * nch + chunk) * 4;
-      dst[0] = sh.Mrow[i];
-      *reinterpret_cast<double*>(dst + 2) = t;
+      st_dev(dst, sh.Mrow[i]);
+      st_dev(reinterpret_cast<double*>(dst + 2), t);
     } else {
-      p.cons_tz[(pos * nch + chunk) * 2 * NP + (i - K)] = t;
+      st_dev(p.cons_tz + (pos * nch + chunk) * 2 * NP + (i - K), t);
     }
   }
-}
-
-// Writes the outputs of position `pos` from its K x K matrix (lane 0 of the
-// calling wave): the closest pair a < b (lowest on ties) and its state.
-template <int K>
-__device__ __forceinline__ void cons_write(const Params& p, int64_t pos, const double (&m)[K][K], const double (&dist)[K][K]) {
-  if (p.cons_nkl)
-#pragma unroll
-    for (int a = 0; a < K; ++a)
-#pragma unroll
-      for (int bb = 0; bb < K; ++bb) p.cons_nkl[pos * K * K + a * K + bb] = (float)m[a][bb];
-  double best = INFINITY;
-  int pair = -1;
-#pragma unroll
-  for (int a = 0; a < K; ++a)
-#pragma unroll
-    for (int bb = a + 1; bb < K; ++bb)
-      if (dist[a][bb] < best) {
-        best = dist[a][bb];
-        pair = a * K + bb;
-      }
-  p.cons_pair[pos] = pair;
-  p.cons_state[pos] = best < (double)p.cons_dc ? 1 : (best > (double)p.cons_dd ? 2 : 0);
-}
-
-// -1 (and NaN in the matrix) for a position that has no valid answer.
-template <int K>
-__device__ __forceinline__ void cons_write_invalid(const Params& p, int64_t pos) {
-  p.cons_state[pos] = -1;
-  p.cons_pair[pos] = -1;
-  if (p.cons_nkl)
-    for (int k = 0; k < K * K; ++k) p.cons_nkl[pos * K * K + k] = __builtin_nanf("");
-}
-
-// Merge (one wave per position): the one-pass matrix and its error
-// estimates; decides the position or queues it for the exact pass.  With
-// q_a = 2^(x_a L - R_a) / S_a:
-//   KL_ab = c T_ab / S_a - (R_a - R_b) ln 2 - ln(S_a / S_b).
-template <int K>
-__global__ __launch_bounds__(kThreads) void k_cons_merge(Params p, int64_t nch) {
-  constexpr int NP = K * (K - 1);
-  const int lane = threadIdx.x & 63;
-  const int64_t pos = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (pos >= p.R_d) return;  // wave-uniform
-  const bool layout_ok = p.hdr[0] == 0;
-  const int b = layout_ok ? p.pair2req[pos] : 0;
-  if (!layout_ok || !temp_ok(p.temp[b])) {
-    if (lane == 0) cons_write_invalid<K>(p, pos);
+  if (!arrive_last(cnt, (int)nch, sh)) return;
+  // the position's last workgroup
+  if (!valid) {
+    if (threadIdx.x == 0) cons_write_invalid<K>(p, pos);
     return;
   }
-  const float Lhi = (float)(kLog2eD / (double)p.temp[b]);
-  const double c = (double)Lhi * kLn2D;
-  double S[K], T[NP], Z[NP];
-  float R[K];  // the row's largest chunk reference: S = sum 2^(x L - R)
-#pragma unroll
-  for (int a = 0; a < K; ++a) {
-    const float* src = p.cons_stats + (pos * K + a) * nch * 4;
-    float mx = -INFINITY;
-    for (int64_t ch = lane; ch < nch; ch += 64) mx = fmaxf(mx, src[ch * 4]);
-    R[a] = wave_max(mx);
+  if (w == 0) {
+    const bool need = cons_merge<K>(p, pos, nch, Lhi);
+    if (lane == 0) sh.need = need ? 1 : 0;
   }
-  double sl[K], tl[NP], zl[NP];
+  __syncthreads();
+  if (!sh.need) return;
+  // exact form over the position's chunks, summed in chunk order
+  cons_row_stats<K>(p, pos, nch, sh);
+  if (threadIdx.x < NP) sh.tot[threadIdx.x] = 0.0;
+  for (int64_t ch = 0; ch < nch; ++ch) {
+    cons_exact_chunk<DT, VEC, K>(p, pos, ch, Lhi, sh);
+    if (threadIdx.x < NP) {
+      double t = sh.d[threadIdx.x][0];
 #pragma unroll
-  for (int a = 0; a < K; ++a) sl[a] = 0.0;
-#pragma unroll
-  for (int q = 0; q < NP; ++q) tl[q] = zl[q] = 0.0;
-  for (int64_t ch = lane; ch < nch; ch += 64) {
-    double f[K];
-#pragma unroll
-    for (int a = 0; a < K; ++a) {
-      const float* src = p.cons_stats + ((pos * K + a) * nch + ch) * 4;
-      f[a] = ldexp(1.0, max((int)(src[0] - R[a]), -2000));  // exact
-      sl[a] += *reinterpret_cast<const double*>(src + 2) * f[a];
+      for (int k = 1; k < kWaves; ++k) t += sh.d[threadIdx.x][k];
+      sh.tot[threadIdx.x] += t;
     }
-    const double* tz = p.cons_tz + (pos * nch + ch) * 2 * NP;
+    __syncthreads();  // sh.d is reused by the next chunk
+  }
+  if (threadIdx.x == 0) {
+    const double lnV = log((double)p.V);
+    double m[K][K];
 #pragma unroll
     for (int a = 0; a < K; ++a)
 #pragma unroll
       for (int bb = 0; bb < K; ++bb)
-        if (bb != a) {
-          const int q = cons_pair_index<K>(a, bb);
-          tl[q] += tz[2 * q] * f[a];
-          zl[q] += tz[2 * q + 1] * f[a];
-        }
+        m[a][bb] = (a == bb || p.V == 1) ? 0.0 : sh.tot[cons_pair_index<K>(a, bb)] / lnV;
+    cons_write<K>(p, pos, m);
   }
-#pragma unroll
-  for (int a = 0; a < K; ++a) S[a] = wave_sum_d(sl[a]);
-#pragma unroll
-  for (int q = 0; q < NP; ++q) {
-    T[q] = wave_sum_d(tl[q]);
-    Z[q] = wave_sum_d(zl[q]);
-  }
-  if (lane != 0) return;
-  const double lnV = log((double)p.V);
-  double m[K][K], err[K][K];
-  bool need = false;
-#pragma unroll
-  for (int a = 0; a < K; ++a)
-#pragma unroll
-    for (int bb = 0; bb < K; ++bb) {
-      m[a][bb] = 0.0;
-      err[a][bb] = 0.0;
-      if (a == bb || p.V == 1) continue;  // one token: both rows are the same point mass
-      const int q = cons_pair_index<K>(a, bb);
-      const double kl = T[q] / S[a] * c - (double)(R[a] - R[bb]) * kLn2D - log(S[a] / S[bb]);
-      const double e = kKlErr * (Z[q] / S[a] * c + 1.0);
-      need = need || !(e <= kKlRel * kl);
-      m[a][bb] = kl / lnV;
-      err[a][bb] = e / lnV;
-    }
-  double dist[K][K], derr[K][K];
-  double db = INFINITY, eb = 0.0;  // the closest pair's distance and estimate (lowest pair on ties)
-  int best = -1;
-#pragma unroll
-  for (int a = 0; a < K; ++a)
-#pragma unroll
-    for (int bb = a + 1; bb < K; ++bb) {
-      dist[a][bb] = 0.5 * (m[a][bb] + m[bb][a]);
-      derr[a][bb] = 0.5 * (err[a][bb] + err[bb][a]);
-      if (dist[a][bb] < db) {
-        db = dist[a][bb];
-        eb = derr[a][bb];
-        best = a * K + bb;
-      }
-    }
-  need = need || best < 0 || fabs(db - (double)p.cons_dc) <= eb || fabs(db - (double)p.cons_dd) <= eb;
-#pragma unroll
-  for (int a = 0; a < K; ++a)
-#pragma unroll
-    for (int bb = a + 1; bb < K; ++bb)  // another pair within the estimates of the closest one
-      if (a * K + bb != best && dist[a][bb] - db <= derr[a][bb] + eb) need = true;
-  if (need) {
-    const int slot = atomicAdd(p.hdr + 1, 1);
-    p.cons_queue[slot] = (int)pos;
-  } else {
-    cons_write<K>(p, pos, m, dist);
-  }
-}
-
-// Reference exponents and sums of the position's K rows, merged over the
-// chunks: wave a < K takes row a, lane l the chunks l, l + 64, ..., then a
-// fixed-order wave reduction, so every workgroup of the position gets the
-// same bits.  All threads call; results in sh.Mrow (R) / sh.Srow (S).
-template <int K>
-__device__ __forceinline__ void cons_row_stats(const Params& p, int64_t pos, int64_t nch, ConsShared& sh) {
-  static_assert(K <= kWaves, "one wave per draft row");
-  const int lane = threadIdx.x & 63, a = threadIdx.x >> 6;
-  if (a < K) {
-    const float* src = p.cons_stats + (pos * K + a) * nch * 4;
-    float R = -INFINITY;
-    for (int64_t c = lane; c < nch; c += 64) R = fmaxf(R, src[c * 4]);
-    R = wave_max(R);
-    double S = 0.0;
-    for (int64_t c = lane; c < nch; c += 64)
-      S += ldexp(*reinterpret_cast<const double*>(src + c * 4 + 2), max((int)(src[c * 4] - R), -2000));
-    S = wave_sum_d(S);
-    if (lane == 0) {
-      sh.Mrow[a] = R;
-      sh.Srow[a] = S;
-    }
-  }
-  __syncthreads();
-}
-
-// Exact pass over the queued positions: per (queued position, chunk) item
-// and ordered pair (a, b), a != b, the chunk's sum of q_a g(w), w = ln(q_b /
-// q_a), with q_a(y) = 2^(x_a L - R_a) / S_a and w = (x_b - x_a) L ln2 +
-// lw_ab.  The workgroups loop over the items (their number is read from the
-// queue's count).
-template <int DT, bool VEC, int K>
-__global__ __launch_bounds__(kThreads) void k_cons_exact(Params p) {
-  __shared__ ConsShared sh;
-  constexpr int P = Elem<DT>::P;
-  constexpr int NP = K * (K - 1);
-  const int64_t nch = (p.V + chunk_cons(DT) - 1) / chunk_cons(DT);
-  const int64_t items = (int64_t)p.hdr[1] * nch;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int64_t pos = p.cons_queue[it / nch], chunk = it % nch;
-    const int b = p.pair2req[pos];
-    const float Lhi = (float)(kLog2eD / (double)p.temp[b]);
-    const float c = (float)((double)Lhi * kLn2D);
-    // one vector of every row at a time (a rolled loop keeps the registers of
-    // the pair terms bounded), the next vector's loads in flight meanwhile
-    const auto load_vec = [&](int k, uint4* q) {
-      const int64_t e0 = cons_e0<DT>(chunk, k);
-#pragma unroll
-      for (int a = 0; a < K; ++a) q[a] = fetch_raw<DT, VEC>(p.target, pos * K + a, p.V, e0);
-    };
-    uint4 cur[K], nxt[K];
-    load_vec(0, cur);
-    cons_row_stats<K>(p, pos, nch, sh);
-    float ct[K], kt[K];
-#pragma unroll
-    for (int a = 0; a < K; ++a) {
-      ct[a] = sh.Mrow[a];
-      kt[a] = (float)(1.0 / sh.Srow[a]);
-    }
-    // Per unordered pair a < b: lw = ln(q_b / q_a) - (x_b - x_a) L ln2, so that
-    // w_ab = (x_b - x_a) c + lw and w_ba = -w_ab exactly; q_a g(w_ab) and
-    // q_b g(w_ba) share the even and odd parts of g's series.
-    constexpr int NU = NP / 2;
-    float lw[NU];
-    {
-      int u = 0;
-#pragma unroll
-      for (int a = 0; a < K; ++a)
-#pragma unroll
-        for (int bb = a + 1; bb < K; ++bb)
-          lw[u++] = (float)((double)(sh.Mrow[a] - sh.Mrow[bb]) * kLn2D + log(sh.Srow[a] / sh.Srow[bb]));
-    }
-    double acc[NP];
-#pragma unroll
-    for (int q = 0; q < NP; ++q) acc[q] = 0.0;
-#pragma unroll 1
-    for (int k = 0; k < kConsVec; ++k) {  // fp32 partial sums over one vector (P elements), fp64 beyond
-      if (k + 1 < kConsVec) load_vec(k + 1, nxt);
-      float v[K][P];
-#pragma unroll
-      for (int a = 0; a < K; ++a) {
-        unpack<DT>(cur[a], v[a]);
-        cons_mask<DT, VEC>(v[a], cons_e0<DT>(chunk, k), p.V);
-      }
-      float part[NP];
-#pragma unroll
-      for (int q = 0; q < NP; ++q) part[q] = 0.f;
-#pragma unroll
-      for (int e = 0; e < P; ++e) {
-        float qv[K];
-#pragma unroll
-        for (int a = 0; a < K; ++a) qv[a] = __builtin_amdgcn_exp2f(fmaf(v[a][e], Lhi, -ct[a])) * kt[a];
-        int u = 0;
-#pragma unroll
-        for (int a = 0; a < K; ++a)
-#pragma unroll
-          for (int bb = a + 1; bb < K; ++bb) {
-            const float wv = fmaf(v[bb][e] - v[a][e], c, lw[u++]);
-            const float w2 = wv * wv;
-            float ev = fmaf(w2, 1.0f / 40320.0f, 1.0f / 720.0f);  // g(w) = E + O, g(-w) = E - O (series to w^9)
-            ev = fmaf(w2, ev, 1.0f / 24.0f);
-            ev = fmaf(w2, ev, 0.5f) * w2;
-            float od = fmaf(w2, 1.0f / 362880.0f, 1.0f / 5040.0f);
-            od = fmaf(w2, od, 1.0f / 120.0f);
-            od = fmaf(w2, od, 1.0f / 6.0f) * (w2 * wv);
-            const bool sm = fabsf(wv) < 0.5f;
-            const float dq = qv[bb] - qv[a];
-            // q_a g(w) = q_b - q_a - q_a w and q_b g(-w) = q_a - q_b + q_b w away from 0
-            const float ab = sm ? qv[a] * (ev + od) : fmaf(-qv[a], wv, dq);
-            const float ba = sm ? qv[bb] * (ev - od) : fmaf(qv[bb], wv, -dq);
-            part[cons_pair_index<K>(a, bb)] += ab;  // positions past the end give 0
-            part[cons_pair_index<K>(bb, a)] += ba;
-          }
-      }
-#pragma unroll
-      for (int q = 0; q < NP; ++q) acc[q] += (double)part[q];
-#pragma unroll
-      for (int a = 0; a < K; ++a) cur[a] = nxt[a];
-    }
-#pragma unroll
-    for (int q = 0; q < NP; ++q) {
-      const double t = wave_sum_d(acc[q]);
-      if (lane == 0) sh.d[q][w] = t;
-    }
-    __syncthreads();
-    if (threadIdx.x < NP) {
-      const int q = threadIdx.x;
-      double t = sh.d[q][0];
-#pragma unroll
-      for (int k = 1; k < kWaves; ++k) t += sh.d[q][k];
-      p.cons_exact[(pos * nch + chunk) * NP + q] = t;
-    }
-    __syncthreads();  // LDS is reused by the next item
-  }
-}
-
-// Finish (one wave per queue slot): the matrix from the exact chunk sums
-// (a fixed-order wave reduction), the closest pair and the state.
-template <int K>
-__global__ __launch_bounds__(kThreads) void k_cons_finish(Params p, int64_t nch) {
-  constexpr int NP = K * (K - 1);
-  const int lane = threadIdx.x & 63;
-  const int64_t slot = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-  if (slot >= p.hdr[1]) return;  // wave-uniform
-  const int64_t pos = p.cons_queue[slot];
-  double sl[NP];
-#pragma unroll
-  for (int q = 0; q < NP; ++q) sl[q] = 0.0;
-  for (int64_t ch = lane; ch < nch; ch += 64)
-#pragma unroll
-    for (int q = 0; q < NP; ++q) sl[q] += p.cons_exact[(pos * nch + ch) * NP + q];
-  double kl[NP];
-#pragma unroll
-  for (int q = 0; q < NP; ++q) kl[q] = wave_sum_d(sl[q]);
-  if (lane != 0) return;
-  const double lnV = log((double)p.V);
-  double m[K][K], dist[K][K];
-#pragma unroll
-  for (int a = 0; a < K; ++a)
-#pragma unroll
-    for (int bb = 0; bb < K; ++bb)
-      m[a][bb] = (a == bb || p.V == 1) ? 0.0 : kl[cons_pair_index<K>(a, bb)] / lnV;
-#pragma unroll
-  for (int a = 0; a < K; ++a)
-#pragma unroll
-    for (int bb = a + 1; bb < K; ++bb) dist[a][bb] = 0.5 * (m[a][bb] + m[bb][a]);
-  cons_write<K>(p, pos, m, dist);
 }
 
 // ----------------------------------------------------------------------------
@@ -3177,15 +3281,15 @@ namespace {
 template <int DT, bool VEC, int K>
 void cons_launch(const Params& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int64_t nch = (p.V + chunk_cons(DT) - 1) / chunk_cons(DT);
-  const dim3 blk(kThreads), gp((unsigned)((int64_t)p.R_d * nch));
-  // e0 / e1 take the pass's own start and end timestamps
-  if (e0 && e1) hipExtLaunchKernelGGL((k_cons_pass<DT, VEC, K>), gp, blk, 0, s, e0, e1, 0, p);
-  else hipLaunchKernelGGL((k_cons_pass<DT, VEC, K>), gp, blk, 0, s, p);
-  const dim3 gw((unsigned)((p.R_d + kWaves - 1) / kWaves));  // one wave per position
-  hipLaunchKernelGGL((k_cons_merge<K>), gw, blk, 0, s, p, nch);
-  const dim3 ge((unsigned)std::min<int64_t>((int64_t)p.R_d * nch, kConsExactGrid));
-  hipLaunchKernelGGL((k_cons_exact<DT, VEC, K>), ge, blk, 0, s, p);
-  hipLaunchKernelGGL((k_cons_finish<K>), gw, blk, 0, s, p, nch);
+  const dim3 grid((unsigned)((int64_t)p.R_d * nch)), blk(kThreads);
+  // e0 / e1 take the dispatch's own start and end timestamps
+  if (p.cons_lds) {
+    if (e0 && e1) hipExtLaunchKernelGGL((k_cons<DT, VEC, K, true>), grid, blk, 0, s, e0, e1, 0, p);
+    else hipLaunchKernelGGL((k_cons<DT, VEC, K, true>), grid, blk, 0, s, p);
+  } else {
+    if (e0 && e1) hipExtLaunchKernelGGL((k_cons<DT, VEC, K, false>), grid, blk, 0, s, e0, e1, 0, p);
+    else hipLaunchKernelGGL((k_cons<DT, VEC, K, false>), grid, blk, 0, s, p);
+  }
 }
 template <int DT, bool VEC>
 void cons_k(const Params& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
@@ -3200,7 +3304,7 @@ void cons_k(const Params& p, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
 int launch_consensus(const Params& p, bool vec, void* stream, void* ev_start, void* ev_stop) {
   hipStream_t s = (hipStream_t)stream;
   hipEvent_t e0 = (hipEvent_t)ev_start, e1 = (hipEvent_t)ev_stop;
-  hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, s, p);
+  if (!p.cons_lds) hipLaunchKernelGGL(k_prep, dim3(1), dim3(kPrepThreads), 0, s, p);
   if (p.R_d == 0 && e0 && e1) {  // nothing to stream: the two events become plain markers
     hipError_t e = hipEventRecord(e0, s);
     if (e == hipSuccess) e = hipEventRecord(e1, s);

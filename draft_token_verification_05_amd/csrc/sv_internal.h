@@ -32,8 +32,9 @@ constexpr int kModeConsensus = 16;  // internal mode value of the consensus call
 // vocabulary elements of one consensus chunk: kThreads x 4 vectors of each row
 
 constexpr int elems_per_vec(int dtype) { return dtype == SV_DTYPE_BF16 ? 8 : 4; }
-// Elements of one consensus chunk (one workgroup, four vectors per thread).
-constexpr int64_t chunk_cons(int dtype) { return (int64_t)kThreads * 4 * elems_per_vec(dtype); }
+// Elements of one consensus chunk (one workgroup, kConsVec vectors per thread and row).
+constexpr int kConsVec = 16;
+constexpr int64_t chunk_cons(int dtype) { return (int64_t)kThreads * kConsVec * elems_per_vec(dtype); }
 constexpr int elem_size(int dtype) { return dtype == SV_DTYPE_BF16 ? 2 : 4; }
 // vocabulary elements covered by one chunk of each pass
 constexpr int64_t chunk_a(int dtype) { return (int64_t)kThreads * kUA * elems_per_vec(dtype); }
@@ -99,7 +100,7 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace of a consensus call (B requests, npos positions, K drafts each).
 struct ConsLayout {
-  size_t off_hdr, off_doff, off_pos2req, off_stats, off_tz, off_queue, off_exact, total;
+  size_t off_hdr, off_doff, off_pos2req, off_cnt, off_stats, off_tz, total;
   int64_t nch;
 };
 inline ConsLayout make_cons_layout(int64_t B, int64_t V, int dtype, int64_t npos, int64_t K) {
@@ -115,10 +116,9 @@ inline ConsLayout make_cons_layout(int64_t B, int64_t V, int dtype, int64_t npos
   L.off_hdr = take(256);
   L.off_doff = take(sizeof(int32_t) * (B + 1));
   L.off_pos2req = take(sizeof(int32_t) * P1);
+  L.off_cnt = take(sizeof(uint64_t) * (size_t)P1 * kArrStride);  // per-position arrival counters
   L.off_stats = take(16 * (size_t)(P1 * K * L.nch));
   L.off_tz = take(2 * sizeof(double) * (size_t)(P1 * L.nch * K * (K - 1)));
-  L.off_queue = take(sizeof(int32_t) * P1);
-  L.off_exact = take(sizeof(double) * (size_t)(P1 * L.nch * K * (K - 1)));
   L.total = o;
   return L;
 }
@@ -219,8 +219,7 @@ struct Params {
   int32_t* cons_pair;       // [positions]
   float* cons_stats;        // [positions][K][nch] x {m, pad, S (2 floats as a double)}: row-chunk statistics
   double* cons_tz;          // [positions][nch][K(K-1)] x {t, z}: one-pass cross sums per chunk and ordered pair
-  int32_t* cons_queue;      // [positions]: positions whose one-pass values are not accurate enough (count: hdr[1])
-  double* cons_exact;       // [positions][nch][K(K-1)]: exact KL sums per chunk and ordered pair
+  int32_t cons_lds;         // 1: each workgroup finds its position's request by a scan of gamma in LDS
 };
 
 // kernel launchers (kernels.hip); return the hipError_t of the launch as int

@@ -117,6 +117,23 @@ def test_consensus_layout_errors(sv, gamma):
     assert (state == -1).all() and (pair == -1).all() and np.isnan(nkl).all()
 
 
+@pytest.mark.parametrize("bad", [False, True])
+def test_consensus_batch_above_lds_scan(sv, bad):
+    """More than 1024 requests: the request map comes from the prep kernel
+    instead of each workgroup's scan of gamma."""
+    B = 1100
+    gamma = np.zeros(B, np.int32)
+    gamma[[0, 7, 513, 1024, 1099]] = [2, 1, 3, 1, 2]
+    w = synthetic.make_consensus(B=B, K=2, gamma=gamma, V=3000, wid=89)
+    if not bad:
+        check(sv, w)
+    else:
+        g2 = gamma.copy()
+        g2[1050] = -1
+        state, pair, _ = run(sv, w, gamma=g2)
+        assert (state == -1).all() and (pair == -1).all()
+
+
 def test_consensus_no_positions(sv):
     w = synthetic.make_consensus(B=4, K=3, gamma=0, V=5000, wid=85)
     state, pair, nkl = run(sv, w)
