@@ -2300,19 +2300,17 @@ __global__ __launch_bounds__(kThreads) void k_refine(Params p) {
 // K draft rows, M[a][b] = KL(q_a || q_b) / ln V, and the closest pair's
 // symmetrised distance against the consensus and divergence thresholds.
 //
-// One read of the rows (k_cons_pass, one workgroup per (position, chunk)):
-// per row the chunk maximum m and s = sum 2^((x - m) L), per ordered pair
-// t = sum 2^((x_a - m_a) L) (x_a - x_b) and z, the same with |x_a - x_b|.
-// k_cons_merge (one wave per position) merges the chunks and forms
-//   KL_ab = c T_ab / S_a - (M_a - M_b) c - ln(S_a / S_b),  c = L ln 2
-// (M: the row's maximum, here an integer reference exponent in its place),
+// One dispatch (k_cons), one workgroup per (position, chunk).  One read of
+// the rows gives per row s = sum 2^(x L - R) and per ordered pair t = sum
+// 2^(x_a L - R_a) (x_a - x_b) and z, the same with |x_a - x_b| (R: integer
+// reference exponents).  The position's last workgroup merges the chunks:
+//   KL_ab = c T_ab / S_a - (R_a - R_b) ln 2 - ln(S_a / S_b),  c = L ln 2,
 // with the one-pass error estimate kKlErr (c Z_ab / S_a + 1) of the verify
-// KL.  A position is decided there unless an estimate exceeds kKlRel of its
-// value or the decision (a threshold, the closest pair) lies within the
-// estimates; such positions are queued, k_cons_exact sums the exact form
-// q_a g(w), w = ln(q_b / q_a), g(w) = e^w - 1 - w >= 0 (no cancellation) for
-// them -- a second read of their rows only -- and k_cons_finish decides from
-// those sums.
+// KL.  It decides there unless an estimate exceeds kKlRel of its value or the
+// decision (a threshold, the closest pair) lies within the estimates; then it
+// sums the exact form q_a g(w), w = ln(q_b / q_a), g(w) = e^w - 1 - w >= 0
+// (no cancellation) over the position's chunks itself -- a second read of that
+// position's rows only -- and decides from those sums.
 // ----------------------------------------------------------------------------
 
 constexpr int kConsMaxPairs = kConsMaxDrafts * (kConsMaxDrafts - 1);

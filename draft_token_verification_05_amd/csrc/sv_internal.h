@@ -20,7 +20,7 @@ constexpr int kUA = 2;           // smallest of the above: sizes the partial arr
 constexpr int kUT = 4;           // 16-byte vectors per thread per row in one slice of k_decide's second look
 constexpr int kSelCache = 256;   // draw records a token selection keeps in LDS
 constexpr int kLdsBatch = 1024;  // batches up to this size scan their offsets in LDS (no prep kernel)
-constexpr int kFusedItemsPerWg = 12;  // longest statistics pass (items per resident workgroup) run in one dispatch
+constexpr int kFusedItemsPerWg = 64;  // longest statistics pass (items per resident workgroup) run in one dispatch
 constexpr int kFusedPerCu = 4;        // resident workgroups per compute unit of the single dispatch
 // per-request arrival counters sit 256 bytes apart: increments of different
 // requests' counters would otherwise queue behind each other on one line

@@ -565,15 +565,18 @@ def test_losslessness_chi_square_gpu():
 # ---------------------------------------------------------------- single-dispatch stochastic path
 
 def test_single_dispatch_choice():
-    """Short statistics passes (the Llama-3-shaped batch) run as one dispatch,
-    long ones (the ragged B=256 batch) and the KL output as separate kernels."""
+    """Statistics passes of up to 64 items per resident workgroup (the
+    Llama-3-shaped batch: 5, the ragged B=256 batch: 41) run as one dispatch;
+    longer ones and the KL output as separate kernels."""
     import draft_token_verification_05_amd as sv
     llama = sv.make_config(32, 128256, sv.SV_DTYPE_BF16, 5, 160)
     assert sv.spec_verify_single_dispatch(llama, S) == 1
     assert sv.spec_verify_single_dispatch(llama, S, with_nkl=True) == 0
     w = synthetic.make_ragged()
     ragged = sv.make_config(w.batch, w.vocab, sv.SV_DTYPE_BF16, w.max_gamma, w.total_draft_rows)
-    assert sv.spec_verify_single_dispatch(ragged, S) == 0
+    assert sv.spec_verify_single_dispatch(ragged, S) == 1
+    long_pass = sv.make_config(1024, 152064, sv.SV_DTYPE_BF16, 16, 1024 * 16)  # ~300 items per workgroup
+    assert sv.spec_verify_single_dispatch(long_pass, S) == 0
 
 
 @pytest.mark.parametrize("V,dtype", [(128256, "bf16"), (4099, "f32"), (8193, "bf16")])
