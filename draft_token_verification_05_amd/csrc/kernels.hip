@@ -332,17 +332,6 @@ __device__ __forceinline__ int block_max_int(int v, int* sh) {
   for (int k = 1; k < kWaves; ++k) r = max(r, sh[k]);
   return r;
 }
-__device__ __forceinline__ float block_max(float v, float* sh) {
-  v = wave_max(v);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  __syncthreads();
-  if (lane == 0) sh[w] = v;
-  __syncthreads();
-  float r = sh[0];
-#pragma unroll
-  for (int k = 1; k < kWaves; ++k) r = fmaxf(r, sh[k]);
-  return r;
-}
 __device__ __forceinline__ double block_sum_d(double v, double* sh) {
   v = wave_sum_d(v);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -467,8 +456,9 @@ struct PartVals {
 __device__ __forceinline__ bool ld_tagged_part(const uint64_t* t, uint32_t epoch, PartVals& v) {
   const uint64_t w0 = ld_dev(t + 0), w1 = ld_dev(t + 1), w2 = ld_dev(t + 2);
   const uint64_t w3 = ld_dev(t + 3), w4 = ld_dev(t + 4), w5 = ld_dev(t + 5);
-  const bool ok = tag_ok(w0, epoch) & tag_ok(w1, epoch) & tag_ok(w2, epoch) & tag_ok(w3, epoch) &
-                  tag_ok(w4, epoch) & tag_ok(w5, epoch);
+  // bitwise: one test of all six tags, no branches between them
+  const bool ok = ((int)tag_ok(w0, epoch) & (int)tag_ok(w1, epoch) & (int)tag_ok(w2, epoch) &
+                   (int)tag_ok(w3, epoch) & (int)tag_ok(w4, epoch) & (int)tag_ok(w5, epoch)) != 0;
   v.mt = tagged_f(w0);
   v.st = tagged_d(w1, w2);
   v.md = tagged_f(w3);
@@ -1773,7 +1763,7 @@ template <int DT, bool VEC, int MODE, bool FUSED, bool POS = false>
 __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bool ok, int d0, int d1, float T,
                                                float ur, DecideShared& sh, TreeShared<MODE>& tr, StatsShared* ssh) {
   constexpr bool SOFT = MODE == SV_MODE_STOCHASTIC || MODE == SV_MODE_NKL;
-  const int H = p.helpers, NS = p.nslices;
+  const int NS = p.nslices;
   // helper h streams slices [s0, s1) wherever rows get a second look
   const int s0 = h * p.slices_per_helper, s1 = min(NS, s0 + p.slices_per_helper);
   const bool writer = h == 0;  // helper 0 writes the outputs of the decision
@@ -2212,13 +2202,14 @@ __global__ __launch_bounds__(kThreads) void k_topk(Params p) {
   topk_merge<K>(lst, k, sh.best, sh.red);
   // row b's candidates: kThreads slots, helper h's k of them at h * k (H * k <= kThreads)
   uint64_t* cand = p.topk_cand + (int64_t)b * kThreads;
-  if (threadIdx.x < k) st_dev(&cand[h * k + threadIdx.x], sh.best[threadIdx.x]);
+  const int tid = (int)threadIdx.x;
+  if (tid < k) st_dev(&cand[h * k + tid], sh.best[tid]);
   if (!arrive_last(arr, H, sh)) return;
   // the row's last helper: one candidate per thread, then the same merge
   uint64_t c1[1] = {0};
-  if (threadIdx.x < H * k) c1[0] = ld_dev(&cand[threadIdx.x]);
+  if (tid < H * k) c1[0] = ld_dev(&cand[tid]);
   topk_merge<1>(c1, k, sh.best, sh.red);
-  if (threadIdx.x < k) p.out_tokens[(int64_t)b * k + threadIdx.x] = topk_index(sh.best[threadIdx.x]);
+  if (tid < k) p.out_tokens[(int64_t)b * k + tid] = topk_index(sh.best[tid]);
 }
 
 // The whole stochastic step in one dispatch (batches up to kLdsBatch, no KL
