@@ -2078,28 +2078,52 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 }
 
 // bf16 rows: a 32-bit key of the same order within one helper's range of at
-// most 65536 elements, the order-mapped bf16 bits above 0xFFFF - (index - base).
-__device__ __forceinline__ uint32_t topk_key16(uint32_t h, uint32_t local) {
-  if (h == 0x8000u) h = 0u;  // -0 == +0
-  h = (h & 0x8000u) ? (~h & 0xFFFFu) : (h | 0x8000u);
-  return (h << 16) | (0xFFFFu - local);
-}
-// ... and back to the 64-bit key of the element (0 stays "no candidate")
+// most 65536 elements, the order-mapped bf16 bits (topk_map16x2) above
+// 0xFFFF - (index - base); back to the 64-bit key of the element (0 stays "no
+// candidate"):
 __device__ __forceinline__ uint64_t topk_key_from16(uint32_t k16, int base) {
   if (k16 == 0) return 0;
   uint32_t h = k16 >> 16;
-  h = (h & 0x8000u) ? (h & 0x7FFFu) : (~h & 0xFFFFu);
+  h = (h & 0x8000u) ? (h & 0x7FFFu) : ((0x10000u - h) & 0xFFFFu);
   return topk_key(__uint_as_float(h << 16), base + (int)(0xFFFFu - (k16 & 0xFFFFu)));
 }
-// Branchless insertion into a sorted (largest first) list of 32-bit keys.
+// Branchless insertion into a sorted (largest first) list of 32-bit keys:
+// the new i-th key is the middle one of the old (i-1)-th, the old i-th and the
+// new key (one median-of-three per entry).
+__device__ __forceinline__ uint32_t med3u(uint32_t a, uint32_t b, uint32_t c) {
+  return max(min(a, b), min(max(a, b), c));
+}
 template <int K>
 __device__ __forceinline__ void topk_insert16(uint32_t (&lst)[K], uint32_t key) {
+  if constexpr (K <= 4) {
+    uint32_t nl[K];
+    nl[0] = max(lst[0], key);
 #pragma unroll
-  for (int i = 0; i < K; ++i) {
-    const uint32_t hi = max(lst[i], key), lo = min(lst[i], key);
-    lst[i] = hi;
-    key = lo;
+    for (int i = 1; i < K; ++i) nl[i] = med3u(lst[i - 1], lst[i], key);
+#pragma unroll
+    for (int i = 0; i < K; ++i) lst[i] = nl[i];
+  } else {  // (longer lists: the compare-and-swap chain, which compiles far faster)
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const uint32_t hi = max(lst[i], key), lo = min(lst[i], key);
+      lst[i] = hi;
+      key = lo;
+    }
   }
+}
+
+// The order-preserving 16-bit maps of the two bf16 values of a word, both at
+// once with 16-bit lane arithmetic: h -> h | 0x8000 for h >= +0 and h ->
+// 0x10000 - h for negative h.  -0 and +0 both map to 0x8000, and no value maps
+// to 0 (the "no candidate" key).
+typedef short sv_i16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short sv_u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t topk_map16x2(uint32_t wd) {
+  const sv_i16x2 sgn = __builtin_bit_cast(sv_i16x2, wd) >> (short)15;  // per half: all ones if negative
+  const sv_u16x2 h = __builtin_bit_cast(sv_u16x2, wd);
+  const sv_u16x2 neg = (unsigned short)0 - h, pos = h | (unsigned short)0x8000;
+  const uint32_t m = __builtin_bit_cast(uint32_t, sgn);
+  return (__builtin_bit_cast(uint32_t, neg) & m) | (__builtin_bit_cast(uint32_t, pos) & ~m);
 }
 
 // Keeps the K largest keys seen by this thread, sorted, largest first.
@@ -2167,17 +2191,20 @@ __global__ __launch_bounds__(kThreads) void k_topk(Params p) {
     uint32_t l16[K];
 #pragma unroll
     for (int i = 0; i < K; ++i) l16[i] = 0;
+    // element y gets the key (map16(x_y) << 16) | (0xFFFF - (y - base)), 0 past the row's end
     slice_stream<DT, VEC, false>(p, b, -1, s0, s1, [&](const uint4* qt, const uint4*, int sl) {
       if (sl == s0 && threadIdx.x == kClaimThread) claim(arr, arr_cur, p.epoch);
 #pragma unroll
       for (int j = 0; j < kUT; ++j) {
         const int y0 = sl * CH + ((w * kUT + j) * 64 + lane) * P;
-        const uint32_t wd[4] = {qt[j].x, qt[j].y, qt[j].z, qt[j].w};
+        const uint32_t c0 = 0xFFFFu - (uint32_t)(y0 - base);
+        const int lim = p.V - y0;  // elements e < lim lie inside the row
+        const uint32_t wd[4] = {topk_map16x2(qt[j].x), topk_map16x2(qt[j].y), topk_map16x2(qt[j].z),
+                                topk_map16x2(qt[j].w)};
 #pragma unroll
         for (int e = 0; e < P; ++e) {
-          const uint32_t h = (e & 1) ? (wd[e >> 1] >> 16) : (wd[e >> 1] & 0xFFFFu);
-          const int y = y0 + e;
-          topk_insert16<K>(l16, y < p.V ? topk_key16(h, (uint32_t)(y - base)) : 0u);
+          const uint32_t hi = (e & 1) ? (wd[e >> 1] & 0xFFFF0000u) : (wd[e >> 1] << 16);
+          topk_insert16<K>(l16, e < lim ? (hi | (c0 - (uint32_t)e)) : 0u);
         }
       }
     });
