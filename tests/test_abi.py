@@ -250,3 +250,49 @@ def test_consensus_workspace_size(sv):
     assert sv.spec_consensus_workspace_size(sv.make_config(16, 128256, 2, 6, 96), 3) == 0
     # no positions still needs the header and offsets
     assert sv.spec_consensus_workspace_size(sv.make_config(16, 128256, 1, 6, 0), 3) > 0
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "specverify.h"
+#include "specverify_probe.h"
+
+int main(void) {
+  sv_config cfg;
+  memset(&cfg, 0, sizeof cfg);
+  cfg.struct_size = sizeof(sv_config);
+  cfg.batch = 32;
+  cfg.vocab = 128256;
+  cfg.dtype = SV_DTYPE_BF16;
+  cfg.max_gamma = 5;
+  cfg.total_draft_rows = 160;
+  size_t ws = spec_verify_workspace_size(&cfg);
+  size_t cs = spec_consensus_workspace_size(&cfg, 3);
+  /* a call without its arrays is rejected on the host, before anything is enqueued */
+  int st = spec_verify(NULL, NULL, NULL, NULL, NULL, NULL, NULL, SV_MODE_GREEDY, 0.0f, NULL, NULL, NULL, NULL, &cfg);
+  printf("%d %zu %zu %d %s\n", spec_verify_version(), ws, cs, st, spec_verify_status_string(SV_EWORKSPACE));
+  return 0;
+}
+"""
+
+
+def test_header_is_c99_and_links(sv, tmp_path):
+    """The public headers compile as C99 (no C++ in them) and a C program
+    links against the library and makes host-side calls through it."""
+    import shutil
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi"
+    libdir = os.path.dirname(sv.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe), "-L", libdir, "-lspecverify", "-Wl,-rpath," + libdir],
+                   check=True, capture_output=True, text=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()
+    assert int(out[0]) == sv.spec_verify_version()
+    assert int(out[1]) == sv.spec_verify_workspace_size(sv.make_config(32, 128256, sv.SV_DTYPE_BF16, 5, 160))
+    assert int(out[2]) == sv.spec_consensus_workspace_size(sv.make_config(32, 128256, sv.SV_DTYPE_BF16, 5, 160), 3)
+    assert int(out[3]) == sv.SV_EINVAL
+    assert out[4].startswith("SV_EWORKSPACE")
