@@ -589,7 +589,9 @@ def main():
         r = run_sample_gpu(args.workload, args.steps, args.warmup, event_every=max(1, args.event_every))
         achieved = r["bytes"] / (r["kernel_ms"] * 1e-3) / 1e9
         what = "top-3 draft rows" if r["topk"] else "sampled draft tokens"
-        print(json.dumps({
+        kern = "k_topk" if r["topk"] else "k_sample"
+        probe = None if args.no_probe else run_probe(r["bytes"])
+        line = {
             "metric": f"{what}/sec at V=128256 (bf16); achieved HBM GB/s vs peak",
             "value": round(r["rows"] / (r["ms_per_step"] * 1e-3), 1), "unit": f"{what}/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(r["ms_per_step"], 5),
@@ -598,14 +600,17 @@ def main():
                        "input_copies_rotated": r["ncopies"],
                        "step_GBps": round(r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9, 1),
                        "step_frac_of_peak": round(r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
-            "roofline": {"bound": "hbm", "kernel": "k_topk" if r["topk"] else "k_sample", "achieved": round(achieved, 1),
-                         "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+            "roofline": {"bound": "hbm", "kernel": kern, "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                         "traffic": load_traffic(kern, args.workload),
                          "bytes_per_launch": r["bytes"], "avg_launch_us": round(r["kernel_ms"] * 1e3, 3),
                          "launch_us": r["kernel_pct"], "timed_launches": r["sampled"]},
-            "probe": None if args.no_probe else run_probe(r["bytes"]),
+            "probe": probe,
             "cpu_baseline": None if args.no_cpu else cpu_baseline_sample(args.workload, topk=r["topk"]),
-        }), flush=True)
+        }
+        if probe:
+            line["roofline"]["frac_of_probe"] = round(achieved / probe["GBps"], 4)
+        print(json.dumps(line), flush=True)
         return
     r = run_gpu(args.workload, args.steps, args.warmup, event_every=max(1, args.event_every))
     w = r["w"]

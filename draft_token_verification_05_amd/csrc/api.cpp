@@ -17,9 +17,9 @@ namespace {
 
 thread_local char g_hip_error[256] = "";
 
-// Polls of a statistics partial (single dispatch) or of another helper's draw
-// record before a workgroup computes it itself (when cfg->wait_polls is 0): a
-// few milliseconds, far above the normal wait of a few microseconds.
+// Polls of a statistics partial (single dispatch) before a helper computes it
+// itself (when cfg->wait_polls is 0): a few milliseconds, far above the normal
+// wait of a few microseconds.
 constexpr int32_t kDefaultWaitPolls = 4096;
 
 // Epochs that tag the fused kernel's partials and the helpers' arrival

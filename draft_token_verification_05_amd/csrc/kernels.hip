@@ -1725,8 +1725,7 @@ __device__ __forceinline__ void terminal_draw(const Params& p, int b, const Term
 // accepted (decision jnn); the first queued position that the second-pass
 // value rejects, if it precedes jnn, becomes the decision.
 template <int MODE, bool POS, class SH>
-__device__ __forceinline__ void kl_finish(const Params& p, int b, SH& sh) {
-  const ReqFin f = p.req_fin[b];
+__device__ __forceinline__ void kl_finish(const Params& p, int b, const ReqFin& f, SH& sh) {
   const int t0 = f.d0 + b, NS = p.nslices;
   const double lnV = log((double)p.V);
   int first = INT_MAX;
@@ -2265,8 +2264,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(VEC ? 
 
 // ----------------------------------------------------------------------------
 // k_refine: the KL second pass over the queue that k_decide filled.  Items
-// (queued position, vocabulary slice) are split into contiguous ranges, one
-// per workgroup, and stream with the loads of the next item in flight; every
+// (queued position, vocabulary slice) are dealt round-robin to the
+// workgroups and stream with the loads of the next item in flight; every
 // item's sum has its own slot, so the result does not depend on the order.
 // The workgroup that completes a request's last item (per-request counter)
 // adds the sums and writes the NKL values and, in NKL mode, the decision.
@@ -2283,32 +2282,45 @@ template <int DT, bool VEC, int MODE, bool POS = false>
 __global__ __launch_bounds__(kThreads) void k_refine(Params p) {
   __shared__ RefineShared sh;
   const int NS = p.nslices;
+  const int64_t G = gridDim.x, wg = blockIdx.x;
+  // Items are dealt round-robin (item it to workgroup it mod G), so the queue
+  // entry of this workgroup's first item is known before the queue length and
+  // both loads are in flight together; the entry is used only if the item
+  // exists (the index is clamped into the queue's storage).
+  const RefItem first = p.ref_list[min(wg / NS, (int64_t)max(p.R_d, 1) - 1)];
   const int64_t N = (int64_t)p.hdr[1] * NS;
-  const int G = (int)gridDim.x, wg = (int)blockIdx.x;
-  const int64_t i0 = (int64_t)wg * N / G, i1 = (int64_t)(wg + 1) * N / G;
-  if (i0 >= i1) return;
+  if (wg >= N) return;
   uint4 at[kUT], ad[kUT], bt[kUT], bd[kUT];
   RefItem ea, eb;
-  int pa, pb;
-  // the item's queue entry, its request's queued count, then its slice
-  const auto issue = [&](int64_t it, RefItem& e, int& pend, uint4* qt, uint4* qd) {
-    e = p.ref_list[it / NS];
-    pend = p.req_fin[e.b].pending;  // -1: the request failed its input checks
+  ReqFin fa, fb;
+  // the request's completion record (its queued count, -1 if it failed its
+  // input checks) travels with the item, then the slice
+  const auto issue = [&](int64_t it, const RefItem& e, ReqFin& f, uint4* qt, uint4* qd) {
+    f = p.req_fin[e.b];
     slice_issue<DT, VEC, true>(p, e.trow, e.pos, (int)(it % NS), qt, qd);
   };
-  const auto consume = [&](const uint4* qt, const uint4* qd, const RefItem& e, int pend, int64_t it) {
+  const auto consume = [&](const uint4* qt, const uint4* qd, const RefItem& e, const ReqFin& f, int64_t it) {
     const KlIn ri{e.ct, e.cd, e.kt, e.kd, e.lw};
     const double v = block_sum_d(kl_terms<DT>(qt, qd, ri, e.Lhi), sh.red_d);
     if (threadIdx.x == 0) st_dev(&p.kl_part[(int64_t)e.pos * NS + it % NS], v);
-    if (pend > 0 && arrive_last(p.cnt_kl + (int64_t)e.b * kCntStride, pend * NS, sh)) kl_finish<MODE, POS>(p, e.b, sh);
+    if (f.pending > 0 && arrive_last(p.cnt_kl + (int64_t)e.b * kCntStride, f.pending * NS, sh))
+      kl_finish<MODE, POS>(p, e.b, f, sh);
   };
-  issue(i0, ea, pa, at, ad);
-  for (int64_t it = i0; it < i1; it += 2) {
-    if (it + 1 < i1) issue(it + 1, eb, pb, bt, bd);
-    consume(at, ad, ea, pa, it);
-    if (it + 1 >= i1) break;
-    if (it + 2 < i1) issue(it + 2, ea, pa, at, ad);
-    consume(bt, bd, eb, pb, it + 1);
+  ea = first;
+  issue(wg, ea, fa, at, ad);
+  for (int64_t it = wg; it < N; it += 2 * G) {
+    const bool second = it + G < N;
+    if (second) {
+      eb = p.ref_list[(it + G) / NS];
+      issue(it + G, eb, fb, bt, bd);
+    }
+    consume(at, ad, ea, fa, it);
+    if (!second) break;
+    if (it + 2 * G < N) {
+      ea = p.ref_list[(it + 2 * G) / NS];
+      issue(it + 2 * G, ea, fa, at, ad);
+    }
+    consume(bt, bd, eb, fb, it + G);
   }
 }
 

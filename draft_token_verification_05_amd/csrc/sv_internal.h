@@ -83,8 +83,8 @@ struct ReqFin {
 };
 
 // Record space of the terminal draw for one (request, wave-chunk); a slice of
-// kThreads x kUT vectors holds four wave-chunks.  Its first 32 bytes hold the
-// record as four self-tagged words (see the draw in kernels.hip).
+// kThreads x kUT vectors holds four wave-chunks.  The record (DrawRec in
+// kernels.hip) takes its first 24 bytes.
 struct PartC {
   uint64_t words[6];
 };

@@ -112,10 +112,10 @@ typedef struct sv_config {
   int32_t vocab;            /* V > 0 */
   int32_t dtype;            /* SV_DTYPE_F32 or SV_DTYPE_BF16 (both logit arrays) */
   int32_t max_gamma;        /* bound on gamma_per_req[b]; 0 <= max_gamma <= SV_MAX_GAMMA */
-  int32_t wait_polls;       /* >= 0; 0 = default.  How often a workgroup polls for a result of
-                               another workgroup of the same dispatch (a statistics partial of
-                               the single dispatch, another helper's draw record) before it
-                               computes that result itself (results do not depend on it) */
+  int32_t wait_polls;       /* >= 0; 0 = default.  How often a helper of the single dispatch
+                               polls for a statistics partial that another workgroup of the same
+                               dispatch writes before it computes that partial itself (results
+                               do not depend on it) */
   int64_t total_draft_rows; /* sum_b gamma_per_req[b], known on the host (sizes the grids) */
   void* stream;             /* hipStream_t to enqueue on; NULL = the default stream */
   void* workspace;          /* device scratch, >= spec_verify_workspace_size(cfg) bytes, 256-byte aligned;
