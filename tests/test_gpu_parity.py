@@ -435,14 +435,20 @@ def test_identical_rows():
     assert (g2["nkl"] == 0).all() and (g2["num"] == w.gamma).all()
 
 
-@pytest.mark.parametrize("V,dtype,sigma,mode", [(128256, "bf16", 0.003, K), (50000, "f32", 0.01, K),
-                                                 (20000, "bf16", 0.05, K), (152064, "bf16", 0.003, S)])
-def test_small_kl_second_pass(V, dtype, sigma, mode):
+@pytest.mark.parametrize("V,dtype,sigma,mode,B,gmin", [(128256, "bf16", 0.003, K, 24, 1),
+                                                        (50000, "f32", 0.01, K, 24, 1),
+                                                        (20000, "bf16", 0.05, K, 24, 1),
+                                                        (152064, "bf16", 0.003, S, 24, 1),
+                                                        (128256, "bf16", 0.003, K, 48, 6)])
+def test_small_kl_second_pass(V, dtype, sigma, mode, B, gmin):
     """Draft rows within a small noise of the target rows: KL values far below
     the one-pass error scale take the grid-wide second pass (NKL mode, and the
-    optional NKL output of stochastic mode)."""
-    w = synthetic.random_workload(seed=int(V % 89 + 1000 * sigma), mode=mode, B=24, V=V, dtype=dtype, gmax=6,
-                                  gmin=1, sigma=sigma)
+    optional NKL output of stochastic mode).  The V >= 50000 cases queue more
+    (position, slice) items than the second pass has workgroups (4 per CU);
+    the last (288 positions x 16 slices) gives each of 1024 workgroups four
+    or five."""
+    w = synthetic.random_workload(seed=int(V % 89 + 1000 * sigma) + B - 24, mode=mode, B=B, V=V, dtype=dtype, gmax=6,
+                                  gmin=gmin, sigma=sigma)
     if mode == K:
         w = w.with_mode(K, delta=float(np.float32(2e-5)))
     g, o, rep = check(w, out_nkl=True)
