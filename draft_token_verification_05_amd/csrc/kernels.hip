@@ -1500,8 +1500,11 @@ __device__ __forceinline__ float resid_weight(float t, float d, const Term& tm) 
   return fmaxf(fmaf(-tm.k0, bb, a), 0.0f);  // one rounding of a - k0 b: its sign is exact
 }
 
-template <int DT, bool RESID>
-__device__ __forceinline__ void draw_record(const uint4* qt, const uint4* qd, const Term& tm, DrawRec* dst) {
+// OWN: the record goes to this workgroup's LDS cache (slot ch) instead of the
+// workspace (the request's only helper keeps its records).
+template <int DT, bool RESID, bool OWN = false>
+__device__ __forceinline__ void draw_record(const uint4* qt, const uint4* qd, const Term& tm, DrawRec* dst,
+                                            DecideShared* own = nullptr, int ch = 0) {
   constexpr int P = Elem<DT>::P;
   const float Lhi = tm.Lhi;
   const int lane = threadIdx.x & 63;
@@ -1524,8 +1527,13 @@ __device__ __forceinline__ void draw_record(const uint4* qt, const uint4* qd, co
     S = wave_sum_d(S);
     A = wave_sum_d(A);
     if (lane == 0) {
-      st_dev(&dst->s, S);
-      st_dev(&dst->a, A);
+      if (OWN) {
+        own->sel_s[ch] = S;
+        own->sel_a[ch] = A;
+      } else {
+        st_dev(&dst->s, S);
+        st_dev(&dst->a, A);
+      }
     }
   } else {
     float vt[kUT * P];
@@ -1546,8 +1554,13 @@ __device__ __forceinline__ void draw_record(const uint4* qt, const uint4* qd, co
     }
     S = wave_sum_d(S);
     if (lane == 0) {
-      st_dev(&dst->s, empty ? 0.0 : S);
-      st_dev(&dst->m, empty ? -INFINITY : mc);
+      if (OWN) {
+        own->sel_s[ch] = empty ? 0.0 : S;
+        own->sel_m[ch] = empty ? -INFINITY : mc;
+      } else {
+        st_dev(&dst->s, empty ? 0.0 : S);
+        st_dev(&dst->m, empty ? -INFINITY : mc);
+      }
     }
   }
 }
@@ -1556,13 +1569,15 @@ __device__ __forceinline__ void draw_record(const uint4* qt, const uint4* qd, co
 // in token order: y* = min{y : C_y > u * C_{V-1}}.  Wave 0 combines the
 // records by fixed wave-wide reductions and scans in chunk order and finds the
 // wave-chunk that holds the draw (CACHED: at most kSelCache records, kept in
-// LDS after the first sweep).  The whole workgroup then reads that wave-chunk
+// LDS after the first sweep; OWN: all of them already there, written by this
+// workgroup before a barrier).  The whole workgroup then reads that wave-chunk
 // again, thread t taking its t-th vector (P consecutive tokens), and a
 // workgroup scan of the threads' weights, in token order, leads to the thread
 // and then the token that hold the draw.  All threads call.
-template <int DT, bool VEC, bool CACHED>
+template <int DT, bool VEC, bool CACHED, bool OWN = false>
 __device__ __forceinline__ void draw_select(const Params& p, int b, const Term& tm, int NW, float ur,
                                             DecideShared& sh) {
+  static_assert(CACHED || !OWN, "own records live in the LDS cache");
   constexpr int P = Elem<DT>::P;
   constexpr int64_t CHW = (int64_t)64 * kUT * P;  // tokens of one wave-chunk: kThreads vectors
   static_assert(64 * kUT == kThreads, "one vector of the wave-chunk per thread");
@@ -1575,13 +1590,13 @@ __device__ __forceinline__ void draw_select(const Params& p, int b, const Term& 
     double st = 0.0, at = 0.0;
     float M = -INFINITY;
     for (int ch = lane; ch < NW; ch += 64) {
-      const double s0 = ld_dev(&rec[ch].s);
-      const double a0 = resid ? ld_dev(&rec[ch].a) : 0.0;
-      const float m0 = resid ? 0.0f : ld_dev(&rec[ch].m);
+      const double s0 = OWN ? sh.sel_s[ch] : ld_dev(&rec[ch].s);
+      const double a0 = resid ? (OWN ? sh.sel_a[ch] : ld_dev(&rec[ch].a)) : 0.0;
+      const float m0 = resid ? 0.0f : (OWN ? sh.sel_m[ch] : ld_dev(&rec[ch].m));
       st += s0;
       at += a0;
       M = fmaxf(M, m0);
-      if (CACHED) {  // each lane reads back only the records it wrote: no barrier needed
+      if (CACHED && !OWN) {  // each lane reads back only the records it wrote: no barrier needed
         sh.sel_s[ch] = s0;
         sh.sel_a[ch] = a0;
         sh.sel_m[ch] = m0;
@@ -1698,12 +1713,28 @@ __device__ __forceinline__ void draw_select(const Params& p, int b, const Term& 
 // terminal row or row pair): stream the slices and write one record per
 // wave-chunk, then count in on the request's arrival counter (claimed for this
 // call: `arr_cur` is its early load); the last helper to arrive selects the
-// token.  All threads call.
+// token.  A request's only helper keeps its records in LDS and selects at
+// once.  All threads call.
 template <int DT, bool VEC>
 __device__ __forceinline__ void terminal_draw(const Params& p, int b, const Term& tm, int s0, int s1, float ur,
                                               DecideShared& sh, uint64_t* arr, uint64_t arr_cur) {
   const int NS = p.nslices, NW = NS * kWaves;
   const int wv = threadIdx.x >> 6;
+  if (p.helpers == 1 && NW <= kSelCache) {
+    // the request's only helper (slices [0, NS)): its records stay in LDS,
+    // with no counter and no round trip through the workspace
+    if (tm.kind == kTermResidual)
+      slice_stream<DT, VEC, true>(p, tm.trow, tm.drow, s0, s1, [&](const uint4* qt, const uint4* qd, int sl) {
+        draw_record<DT, true, true>(qt, qd, tm, nullptr, &sh, sl * kWaves + wv);
+      });
+    else
+      slice_stream<DT, VEC, false>(p, tm.trow, tm.drow, s0, s1, [&](const uint4* qt, const uint4* qd, int sl) {
+        draw_record<DT, false, true>(qt, qd, tm, nullptr, &sh, sl * kWaves + wv);
+      });
+    __syncthreads();
+    draw_select<DT, VEC, true, true>(p, b, tm, NW, ur, sh);
+    return;
+  }
   if (threadIdx.x == kClaimThread) claim(arr, arr_cur, p.epoch);  // completes before this helper counts itself
   DrawRec* rec = reinterpret_cast<DrawRec*>(p.part_c) + (int64_t)b * NW + wv;
   if (tm.kind == kTermResidual)
