@@ -153,7 +153,7 @@ int spec_verify_single_dispatch(const sv_config* cfg, int32_t mode, int32_t with
       cfg->total_draft_rows < 0 || (cfg->dtype != SV_DTYPE_F32 && cfg->dtype != SV_DTYPE_BF16) ||
       mode < SV_MODE_STOCHASTIC || mode > SV_MODE_BLOCK)
     return SV_EINVAL;
-  if (mode != SV_MODE_STOCHASTIC || with_nkl || cfg->batch > sv::kLdsBatch) return 0;
+  if (mode == SV_MODE_NKL || (mode == SV_MODE_STOCHASTIC && with_nkl) || cfg->batch > sv::kLdsBatch) return 0;
   if (cfg->total_draft_rows * (int64_t)((cfg->vocab + sv::chunk_stats(cfg->dtype, mode) - 1) /
                                         sv::chunk_stats(cfg->dtype, mode)) > INT32_MAX)
     return 0;
@@ -163,7 +163,8 @@ int spec_verify_single_dispatch(const sv_config* cfg, int32_t mode, int32_t with
   p.dtype = cfg->dtype;
   p.mode = mode;
   p.R_d = (int32_t)cfg->total_draft_rows;
-  p.n_task = p.R_d;
+  p.max_gamma = cfg->max_gamma;
+  p.n_task = mode == SV_MODE_STOCHASTIC ? p.R_d : p.R_d + p.B;
   p.nch = (int32_t)((p.V + sv::chunk_stats(p.dtype, mode) - 1) / sv::chunk_stats(p.dtype, mode));
   // the vector-load variant: the one whose occupancy the plan uses for aligned rows
   const bool vec = ((size_t)p.V * (size_t)sv::elem_size(p.dtype)) % 16 == 0;
@@ -237,10 +238,9 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
   hipEvent_t* ev = static_cast<hipEvent_t*>(cfg->phase_events);
   hipError_t e;
 
-  // stochastic batches that scan their offsets in LDS, want no KL output and
-  // have a short statistics pass: the whole step in one dispatch
-  const int fused_grid =
-      (mode == SV_MODE_STOCHASTIC && !p.want_kl && B <= sv::kLdsBatch) ? sv::plan_fused(p, vec) : 0;
+  // batches that scan their offsets in LDS, want no KL output and have a
+  // short statistics pass: the whole step in one dispatch (not NKL mode)
+  const int fused_grid = (!p.want_kl && B <= sv::kLdsBatch) ? sv::plan_fused(p, vec) : 0;
   p.epoch = next_epoch();
   p.wait_polls = cfg->wait_polls > 0 ? cfg->wait_polls : kDefaultWaitPolls;
   if (fused_grid > 0) {

@@ -1,11 +1,12 @@
 // gfx950 kernels of the speculative-decoding verify step.
 //
-// Launches per call (all on the caller's stream).  A stochastic batch of at
-// most kLdsBatch requests without KL output and with a short statistics pass
-// runs as ONE dispatch, k_fused: its workgroups stream the statistics pass
-// exactly as k_stats does (partials tagged with the call's epoch), then take
-// the helper roles of k_decide, each waiting (bounded) for its request's
-// partials instead of a kernel boundary.  Every other call:
+// Launches per call (all on the caller's stream).  A batch of at most
+// kLdsBatch requests with a short statistics pass and no KL output (any mode
+// but NKL; tree and block requests of at most kFusedNodes - 1 positions) runs
+// as ONE dispatch, k_fused: its workgroups stream the statistics pass exactly
+// as k_stats does (partials tagged with the call's epoch), then take the
+// helper roles of k_decide, each waiting (bounded) for its request's partials
+// instead of a kernel boundary.  Every other call:
 //   k_prep      batches above kLdsBatch only: one workgroup scans gamma into
 //               the packed offsets, builds the row -> request maps and checks
 //               the layout.  Smaller batches do this scan in LDS inside
@@ -453,6 +454,19 @@ struct PartVals {
   float mt, md;
   double st, sd;
 };
+// A greedy-family partial in the single dispatch: the target row maximum and
+// its lowest index as two self-tagged words.
+__device__ __forceinline__ void st_tagged_idx(uint64_t* t, float mt, int idx, uint32_t epoch) {
+  st_tagged_f(t + 0, mt, epoch);
+  st_dev(t + 1, tagged((uint32_t)idx, epoch));
+}
+__device__ __forceinline__ bool ld_tagged_idx(const uint64_t* t, uint32_t epoch, float& mt, int& idx) {
+  const uint64_t w0 = ld_dev(t + 0), w1 = ld_dev(t + 1);
+  const bool ok = ((int)tag_ok(w0, epoch) & (int)tag_ok(w1, epoch)) != 0;
+  mt = tagged_f(w0);
+  idx = (int)(uint32_t)w1;
+  return ok;
+}
 __device__ __forceinline__ bool ld_tagged_part(const uint64_t* t, uint32_t epoch, PartVals& v) {
   const uint64_t w0 = ld_dev(t + 0), w1 = ld_dev(t + 1), w2 = ld_dev(t + 2);
   const uint64_t w3 = ld_dev(t + 3), w4 = ld_dev(t + 4), w5 = ld_dev(t + 5);
@@ -728,8 +742,8 @@ __device__ __forceinline__ void fold_chunk(Lane& L, const Vecs<NV>& qt, const Ve
 
 // Reduces the lane states over the workgroup and writes the segment's partial
 // (thread 0).  Plain stores when the consumer is a later kernel.  FUSED
-// (stochastic, consumers in the same dispatch): device-scope stores and, once
-// they have completed, the call's epoch in dst->tag.
+// (consumers in the same dispatch): self-tagged words, (m_t, s_t, m_d, s_d)
+// for a stochastic pair, (m_t, argmax) for a greedy-family row.
 template <bool SOFT, bool IDX, bool WZ, bool PAIR, bool FUSED = false>
 __device__ __forceinline__ void reduce_store(const Lane& L, float Lhi, PartA* dst, StatsShared& sh,
                                              uint32_t epoch = 0) {
@@ -783,7 +797,8 @@ __device__ __forceinline__ void reduce_store(const Lane& L, float Lhi, PartA* ds
     }
     if constexpr (FUSED) {
       // self-tagged words: no wait for the stores, the next loads stay in flight
-      st_tagged_part(reinterpret_cast<uint64_t*>(dst), Mt, s0, Md, s1, epoch);
+      if constexpr (SOFT) st_tagged_part(reinterpret_cast<uint64_t*>(dst), Mt, s0, Md, s1, epoch);
+      else st_tagged_idx(reinterpret_cast<uint64_t*>(dst), Mt, I, epoch);
     } else {
       dst->m_t = Mt;
       if (IDX) dst->idx = I;
@@ -861,7 +876,7 @@ __device__ __forceinline__ void next_desc(const Params& p, const StatsShared& sh
 // across a task boundary) are in flight while item i is folded; a task segment
 // ends with a workgroup reduction whose barriers wait on LDS only, so the next
 // loads stay in flight through it.  LDS: the batch is small enough for the
-// offsets to be scanned in LDS.  FUSED (stochastic, LDS): partials are tagged
+// offsets to be scanned in LDS.  FUSED (LDS, not NKL): partials are tagged
 // for helpers of the same dispatch, workgroups numbered
 // p.stats_grid and above stream nothing, and nothing is published for later
 // kernels.  Returns false when the offsets scan found a layout error.
@@ -883,7 +898,7 @@ __device__ __forceinline__ bool stats_phase(const Params& p, StatsShared& sh) {
   constexpr int NV = SOFT ? 2 : 4;
   constexpr bool IDX = MODE != SV_MODE_STOCHASTIC;
   constexpr bool WZM = MODE == SV_MODE_NKL || WZ;
-  static_assert(!FUSED || (LDS && MODE == SV_MODE_STOCHASTIC && !WZ), "fused: stochastic, LDS scan, no KL");
+  static_assert(!FUSED || (LDS && MODE != SV_MODE_NKL && !WZ), "fused: LDS scan, no KL");
   const int G = p.stats_grid, wg = (int)blockIdx.x;
   const bool streams = !FUSED || wg < G;
   const int64_t N = (int64_t)p.n_task * p.nch;
@@ -913,6 +928,23 @@ __device__ __forceinline__ bool stats_phase(const Params& p, StatsShared& sh) {
     set_rows<MODE, LDS>(p, sh, b, dA);
     if (MODE == SV_MODE_STOCHASTIC) issue_row<DT, VEC, NV>(p.target, dA.trow, dA.chunk, p.V, At);
     else if (dA.pair) issue_row<DT, VEC, NV>(p.draft, dA.drow, dA.chunk, p.V, Ad);
+  } else if constexpr (FUSED) {
+    // greedy family in one dispatch: tasks are target rows (no lookup), so the
+    // first item's loads go out right behind the offsets scan's own; only the
+    // helper workgroups need the scan, for their decisions
+    const bool helper = wg < p.B * p.helpers;
+    ScanIn scan_in{};
+    if (helper) scan_in = scan_load(p, SOFT);
+    __asm__ volatile("" ::: "memory");  // keeps the scan's loads ahead in issue order
+    // unconditional, so that the scan's waits count these loads exactly: a
+    // workgroup without items reads the first chunk of target row 0 instead
+    const bool has = i < i_end;
+    dA.task = has ? (int)(i / p.nch) : 0;
+    dA.chunk = has ? (int)(i - (int64_t)dA.task * p.nch) : 0;
+    set_rows<MODE, LDS>(p, sh, b, dA);
+    issue_chunk<DT, VEC, NV, SOFT>(p, dA, At, Ad);
+    if (helper && !scan_offsets_lds(p, sh, scan_in, SOFT, false)) return false;
+    if (!has) return true;
   } else {
     if (LDS) {
       // greedy and tree tasks are target rows: only workgroup 0 needs the
@@ -935,17 +967,22 @@ __device__ __forceinline__ bool stats_phase(const Params& p, StatsShared& sh) {
     reduce_store<SOFT, IDX, WZM, SOFT, FUSED>(L, d.Lhi, dst, sh, p.epoch);
     lane_reset(L);
   };
+  // issue priorities by remaining work: always in the soft modes; in the
+  // greedy family only for the single dispatch's longer shares (measured: the
+  // separate greedy pass, and single-dispatch shares of a few items, stream
+  // faster without)
+  const bool paced = SOFT || (FUSED && tot >= 4);
   for (;;) {
     dB = dA;
     if (i + 1 < i_end) next_desc<MODE, LDS>(p, sh, b, dB);
-    if (SOFT) pace(i_end - i, tot);  // (measured: the greedy modes stream faster without)
+    if (paced) pace(i_end - i, tot);
     issue_chunk<DT, VEC, NV, SOFT>(p, dB, Bt, Bd);  // the last item reloads itself (cache hit)
     fold_chunk<DT, NV, SOFT, IDX, WZM, SOFT>(L, At, Ad, dA, p.V);
     if (dA.chunk == p.nch - 1 || i + 1 == i_end) store(dA);
     if (++i >= i_end) break;
     dA = dB;
     if (i + 1 < i_end) next_desc<MODE, LDS>(p, sh, b, dA);
-    if (SOFT) pace(i_end - i, tot);
+    if (paced) pace(i_end - i, tot);
     issue_chunk<DT, VEC, NV, SOFT>(p, dA, At, Ad);
     fold_chunk<DT, NV, SOFT, IDX, WZM, SOFT>(L, Bt, Bd, dB, p.V);
     if (dB.chunk == p.nch - 1 || i + 1 == i_end) store(dB);
@@ -1097,8 +1134,10 @@ __device__ __forceinline__ Merged merge_task(const Params& p, int64_t task, bool
 // calling workgroup with the same chunk order, lane mapping and reduction as
 // the statistics pass, so it is bit-identical to the original: left in
 // sh.scratch and published as self-tagged words.  All threads call.
-template <int DT, bool VEC>
+template <int DT, bool VEC, int MODE>
 __device__ void recompute_segment(const Params& p, StatsShared& sh, int task, int seg) {
+  constexpr bool SOFT = MODE == SV_MODE_STOCHASTIC;
+  constexpr int NV = SOFT ? 2 : 4;
   const int G = p.stats_grid;
   const int64_t N = (int64_t)p.n_task * p.nch;
   const int64_t first = (int64_t)task * p.nch;
@@ -1109,19 +1148,21 @@ __device__ void recompute_segment(const Params& p, StatsShared& sh, int task, in
   int b = -1;
   d.task = task;
   d.chunk = (int)(lo - first);
-  set_rows<SV_MODE_STOCHASTIC, true>(p, sh, b, d);
+  set_rows<MODE, true>(p, sh, b, d);
   Lane L;
   lane_reset(L);
   for (int64_t i = lo; i < hi; ++i, ++d.chunk) {
-    Vecs<2> qt, qd;
-    issue_chunk<DT, VEC, 2, true>(p, d, qt, qd);
-    fold_chunk<DT, 2, true, false, false, true>(L, qt, qd, d, p.V);
+    Vecs<NV> qt, qd;
+    issue_chunk<DT, VEC, NV, SOFT>(p, d, qt, qd);
+    fold_chunk<DT, NV, SOFT, !SOFT, false, SOFT>(L, qt, qd, d, p.V);
   }
-  reduce_store<true, false, false, true>(L, d.Lhi, &sh.scratch, sh);  // into LDS first
+  reduce_store<SOFT, !SOFT, false, SOFT>(L, d.Lhi, &sh.scratch, sh);  // into LDS first
   __syncthreads();
-  if (threadIdx.x == 0)
-    st_tagged_part(reinterpret_cast<uint64_t*>(p.part_a + first + seg), sh.scratch.m_t, sh.scratch.s_t,
-                   sh.scratch.m_d, sh.scratch.s_d, p.epoch);
+  if (threadIdx.x == 0) {
+    uint64_t* t = reinterpret_cast<uint64_t*>(p.part_a + first + seg);
+    if (SOFT) st_tagged_part(t, sh.scratch.m_t, sh.scratch.s_t, sh.scratch.m_d, sh.scratch.s_d, p.epoch);
+    else st_tagged_idx(t, sh.scratch.m_t, sh.scratch.idx, p.epoch);
+  }
 }
 
 // The running merge of this lane's partial slots of one task in the single
@@ -1132,9 +1173,10 @@ __device__ void recompute_segment(const Params& p, StatsShared& sh, int task, in
 // this workgroup itself, so the wait is bounded and the result does not
 // depend on which workgroups run when.  All threads call (the slot rounds are
 // uniform: ceil(maxseg / S)).
-template <int DT, bool VEC>
+template <int DT, bool VEC, int MODE>
 __device__ Merged fused_task_merge(const Params& p, StatsShared& ssh, int64_t task, bool has, int l, int glog,
                                    float Lhi) {
+  constexpr bool SOFT = MODE == SV_MODE_STOCHASTIC;
   const int G = p.stats_grid, S = 1 << glog;
   const int64_t N = (int64_t)p.n_task * p.nch;
   const int nseg = has ? wg_of((task + 1) * p.nch - 1, N, G) - wg_of(task * p.nch, N, G) + 1 : 0;
@@ -1145,10 +1187,12 @@ __device__ Merged fused_task_merge(const Params& p, StatsShared& ssh, int64_t ta
     const bool active = seg < nseg;
     const uint64_t* t = reinterpret_cast<const uint64_t*>(p.part_a + task * p.nch + seg);
     PartVals v{-INFINITY, -INFINITY, 0.0, 0.0};
-    bool ready = !active || ld_tagged_part(t, p.epoch, v);
+    int vix = INT_MAX;
+    const auto load = [&]() { return SOFT ? ld_tagged_part(t, p.epoch, v) : ld_tagged_idx(t, p.epoch, v.mt, vix); };
+    bool ready = !active || load();
     for (int n = 0; !ready && n < p.wait_polls; ++n) {
       __builtin_amdgcn_s_sleep(2);
-      ready = ld_tagged_part(t, p.epoch, v);
+      ready = load();
     }
     // the fallback: missing slots are computed by the whole workgroup, one by one
     bool miss = !ready;
@@ -1163,19 +1207,20 @@ __device__ Merged fused_task_merge(const Params& p, StatsShared& ssh, int64_t ta
         ssh.pick_seg = seg;
       }
       __syncthreads();
-      recompute_segment<DT, VEC>(p, ssh, (int)ssh.pick_task, ssh.pick_seg);
+      recompute_segment<DT, VEC, MODE>(p, ssh, (int)ssh.pick_task, ssh.pick_seg);
       __syncthreads();
       if ((int)threadIdx.x == owner) {
         v.mt = ssh.scratch.m_t;
         v.st = ssh.scratch.s_t;
         v.md = ssh.scratch.m_d;
         v.sd = ssh.scratch.s_d;
+        vix = ssh.scratch.idx;
         miss = false;
       }
     }
-    if (active) merge_fold<true>(r, v.mt, INT_MAX, v.st, v.md, v.sd, 0.0, 0.0, true, Lhi);
+    if (active) merge_fold<SOFT>(r, v.mt, SOFT ? INT_MAX : vix, v.st, v.md, v.sd, 0.0, 0.0, SOFT, Lhi);
   }
-  return merge_group<true>(r, glog, Lhi);
+  return merge_group<SOFT>(r, glog, Lhi);
 }
 
 // g(w) = e^w - 1 - w >= 0, accurate for small |w| (Taylor series to w^9)
@@ -1390,22 +1435,24 @@ __device__ __forceinline__ bool arrive_last(uint64_t* cnt, int H, SH& sh) {
   return sh.flag != 0;
 }
 
-template <int MODE>
+// Decision scratch of the tree and block modes for requests of up to N - 1
+// draft positions (N nodes).
+template <int MODE, int N = SV_MAX_GAMMA + 1>
 struct TreeShared {
   int16_t info[1];
   int16_t par[1];
   int idx[1];
 };
-template <>
-struct TreeShared<SV_MODE_TREE_GREEDY> {
-  int16_t info[SV_MAX_GAMMA + 1];  // (depth << 1) | accepted
-  int16_t par[SV_MAX_GAMMA + 1];
-  int idx[SV_MAX_GAMMA + 1];  // argmax of each node's target row
+template <int N>
+struct TreeShared<SV_MODE_TREE_GREEDY, N> {
+  int16_t info[N];  // (depth << 1) | accepted
+  int16_t par[N];
+  int idx[N];  // argmax of each node's target row
 };
-template <>
-struct TreeShared<SV_MODE_BLOCK> {
-  int idx[SV_MAX_GAMMA + 1];  // argmax of each position's target row
-  int keep;                   // the kept prefix e, from thread 0's run scan
+template <int N>
+struct TreeShared<SV_MODE_BLOCK, N> {
+  int idx[N];  // argmax of each position's target row
+  int keep;    // the kept prefix e, from thread 0's run scan
 };
 
 __device__ void finish_invalid(const Params& p, int b, int t0, int d0, int g) {
@@ -1426,8 +1473,8 @@ __device__ void finish_invalid(const Params& p, int b, int t0, int d0, int g) {
 // token is the argmax of its parent's target row and its parent is accepted;
 // the deepest accepted node (lowest id on ties) ends the path.  Parents
 // precede children, so one ordered pass settles every node.
-__device__ void resolve_tree(const Params& p, int b, int g, int t0, int d0, TreeShared<SV_MODE_TREE_GREEDY>& tr,
-                             DecideShared& sh) {
+template <class TS>
+__device__ void resolve_tree(const Params& p, int b, int g, int t0, int d0, TS& tr, DecideShared& sh) {
   const int N = g + 1;
   for (int n = 1 + threadIdx.x; n < N; n += kThreads) {
     const int pa = p.parents[d0 + n - 1];
@@ -1789,9 +1836,9 @@ __device__ __forceinline__ void kl_finish(const Params& p, int b, const ReqFin& 
 // its load may still be in flight).  FUSED (stochastic): called in the
 // statistics kernel itself, where it waits for the request's partials.
 // POS (NKL): per-position thresholds from generation positions.
-template <int DT, bool VEC, int MODE, bool FUSED, bool POS = false>
+template <int DT, bool VEC, int MODE, bool FUSED, bool POS = false, class TS>
 __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bool ok, int d0, int d1, float T,
-                                               float ur, DecideShared& sh, TreeShared<MODE>& tr, StatsShared* ssh) {
+                                               float ur, DecideShared& sh, TS& tr, StatsShared* ssh) {
   constexpr bool SOFT = MODE == SV_MODE_STOCHASTIC || MODE == SV_MODE_NKL;
   const int NS = p.nslices;
   // helper h streams slices [s0, s1) wherever rows get a second look
@@ -1872,7 +1919,7 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
     const int x = ps.x;
     const float tx = ps.tx, dx = ps.dx, u = ps.u;
     Merged r;
-    if constexpr (FUSED) r = fused_task_merge<DT, VEC>(p, *ssh, tbase + ti, has, l, glog, Lhi);
+    if constexpr (FUSED) r = fused_task_merge<DT, VEC, MODE>(p, *ssh, tbase + ti, has, l, glog, Lhi);
     else r = merge_task<SOFT>(p, tbase + ti, has, pair, l, glog, Lhi);
     if (l == 0 && has) {
       const int idx = r.idx == INT_MAX ? 0 : r.idx;  // no element above the pad value: position 0
@@ -2269,27 +2316,29 @@ __global__ __launch_bounds__(kThreads) void k_topk(Params p) {
   if (tid < k) p.out_tokens[(int64_t)b * k + tid] = topk_index(sh.best[tid]);
 }
 
-// The whole stochastic step in one dispatch (batches up to kLdsBatch, no KL
-// output).  Every workgroup first streams its share of the statistics pass
-// (stats_phase: partials tagged with the call's epoch, tasks marked done);
-// then workgroup r below
-// B x H takes the helper role (request r mod B, helper r / B) of the decision
-// kernel: it reads its request's partials as they arrive (fused_task_merge,
-// a bounded wait with its own fallback) instead of after a kernel boundary, and takes the offsets and
-// temperatures from its own LDS scan.  Vector-load variants are held to 128
+// The whole step in one dispatch (batches up to kLdsBatch; stochastic without
+// KL output, greedy, tree and block).  Every workgroup first streams its share
+// of the statistics pass (stats_phase: partials tagged with the call's epoch);
+// then workgroup r below B x H takes the helper role (request r mod B, helper
+// r / B; H = 1 outside the stochastic mode) of the decision kernel: it reads
+// its request's partials as they arrive (fused_task_merge, a bounded wait with
+// its own fallback) instead of after a kernel boundary, and takes the offsets
+// and temperatures from its own LDS scan.  Tree and block requests hold at
+// most kFusedNodes - 1 positions here.  Vector-load variants are held to 128
 // registers (4 waves per SIMD) without spilling.
-template <int DT, bool VEC>
+template <int DT, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(VEC ? 4 : 1))) void k_fused(Params p) {
+  constexpr bool SOFT = MODE == SV_MODE_STOCHASTIC;
   __shared__ StatsShared ssh;
   __shared__ DecideShared sh;
-  __shared__ TreeShared<SV_MODE_STOCHASTIC> tr;
-  const bool ok = stats_phase<DT, VEC, SV_MODE_STOCHASTIC, false, true, true>(p, ssh);
+  __shared__ TreeShared<MODE, kFusedNodes> tr;
+  const bool ok = stats_phase<DT, VEC, MODE, false, true, true>(p, ssh);
   const int r = (int)blockIdx.x;
   if (r < p.B * p.helpers) {
     const int b = r % p.B, h = r / p.B;
-    const float ur = p.ur[b];
-    decide_request<DT, VEC, SV_MODE_STOCHASTIC, true>(p, b, h, ok, ssh.off[b], ssh.off[b + 1], ssh.temp[b], ur, sh,
-                                                      tr, &ssh);
+    const float ur = SOFT ? p.ur[b] : 0.0f;
+    decide_request<DT, VEC, MODE, true>(p, b, h, ok, ssh.off[b], ssh.off[b + 1], SOFT ? ssh.temp[b] : 1.0f, ur, sh,
+                                        tr, &ssh);
   }
 }
 
@@ -3151,20 +3200,40 @@ int plan_stats(Params& p, bool vec) {
   return 0;
 }
 
-int plan_fused(Params& p, bool vec) {
-  static int occ[2][2] = {{0, 0}, {0, 0}};  // [bf16][vec]; same value from every thread: a race is benign
-  int& o = occ[p.dtype == SV_DTYPE_BF16][vec];
+template <int DT, bool VEC>
+int fused_occupancy(int mode) {
+  static int occ[SV_MODE_BLOCK + 1] = {0, 0, 0, 0, 0};  // same value from every thread: a race is benign
+  int& o = occ[mode];
   if (o == 0) {
     int v = 0;
     hipError_t e;
-    if (p.dtype == SV_DTYPE_BF16)
-      e = vec ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_fused<SV_DTYPE_BF16, true>, kThreads, 0)
-              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_fused<SV_DTYPE_BF16, false>, kThreads, 0);
-    else
-      e = vec ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_fused<SV_DTYPE_F32, true>, kThreads, 0)
-              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_fused<SV_DTYPE_F32, false>, kThreads, 0);
+    switch (mode) {
+      case SV_MODE_STOCHASTIC:
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_fused<DT, VEC, SV_MODE_STOCHASTIC>, kThreads, 0);
+        break;
+      case SV_MODE_GREEDY:
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_fused<DT, VEC, SV_MODE_GREEDY>, kThreads, 0);
+        break;
+      case SV_MODE_TREE_GREEDY:
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_fused<DT, VEC, SV_MODE_TREE_GREEDY>, kThreads, 0);
+        break;
+      default:
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, k_fused<DT, VEC, SV_MODE_BLOCK>, kThreads, 0);
+        break;
+    }
     o = (e == hipSuccess && v > 0) ? v : 1;
   }
+  return o;
+}
+
+int plan_fused(Params& p, bool vec) {
+  if (p.mode == SV_MODE_NKL) return 0;
+  // tree and block requests keep one entry per position in LDS
+  if ((p.mode == SV_MODE_TREE_GREEDY || p.mode == SV_MODE_BLOCK) && p.max_gamma >= kFusedNodes) return 0;
+  const int o = p.dtype == SV_DTYPE_BF16 ? (vec ? fused_occupancy<SV_DTYPE_BF16, true>(p.mode)
+                                                : fused_occupancy<SV_DTYPE_BF16, false>(p.mode))
+                                         : (vec ? fused_occupancy<SV_DTYPE_F32, true>(p.mode)
+                                                : fused_occupancy<SV_DTYPE_F32, false>(p.mode));
   // at most kFusedPerCu workgroups per compute unit: the units serve their
   // workgroups' loads roughly in age order, so the newest stream last.  With
   // the statistics waves paced by their remaining work, four per unit measure
@@ -3179,14 +3248,20 @@ int plan_fused(Params& p, bool vec) {
   // batch, 55 items per workgroup: about 10 us).
   if ((int64_t)p.n_task * p.nch > kFusedItemsPerWg * cap) return 0;
   set_stats_grid(p, cap);
-  // helpers per request: what the resident grid holds, at most one per slice
   p.nslices = (int32_t)((p.V + chunk_t(p.dtype) - 1) / chunk_t(p.dtype));
-  int64_t H = cap / p.B;
-  if (H > p.nslices) H = p.nslices;
-  if (H < 1) H = 1;
-  const int64_t spp = (p.nslices + H - 1) / H;
-  p.slices_per_helper = (int32_t)spp;
-  p.helpers = (int32_t)((p.nslices + spp - 1) / spp);
+  if (p.mode != SV_MODE_STOCHASTIC) {
+    // one helper per request: no terminal draw
+    p.helpers = 1;
+    p.slices_per_helper = p.nslices;
+  } else {
+    // helpers per request: what the resident grid holds, at most one per slice
+    int64_t H = cap / p.B;
+    if (H > p.nslices) H = p.nslices;
+    if (H < 1) H = 1;
+    const int64_t spp = (p.nslices + H - 1) / H;
+    p.slices_per_helper = (int32_t)spp;
+    p.helpers = (int32_t)((p.nslices + spp - 1) / spp);
+  }
   // one helper role per workgroup (a role loop would cost registers), so a
   // batch above the resident grid (B x H > cap) gets helpers that start as
   // others finish
@@ -3194,15 +3269,25 @@ int plan_fused(Params& p, bool vec) {
   return (int)(roles > p.stats_grid ? roles : p.stats_grid);
 }
 
+template <int DT, bool VEC>
+void fused_dispatch(const Params& p, dim3 grid, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
+  switch (p.mode) {
+    case SV_MODE_STOCHASTIC: launch_timed(k_fused<DT, VEC, SV_MODE_STOCHASTIC>, grid, p, s, e0, e1); break;
+    case SV_MODE_GREEDY: launch_timed(k_fused<DT, VEC, SV_MODE_GREEDY>, grid, p, s, e0, e1); break;
+    case SV_MODE_TREE_GREEDY: launch_timed(k_fused<DT, VEC, SV_MODE_TREE_GREEDY>, grid, p, s, e0, e1); break;
+    default: launch_timed(k_fused<DT, VEC, SV_MODE_BLOCK>, grid, p, s, e0, e1); break;
+  }
+}
+
 int launch_fused(const Params& p, bool vec, int grid, void* stream, void* ev_start, void* ev_stop) {
   hipStream_t s = (hipStream_t)stream;
   hipEvent_t e0 = (hipEvent_t)ev_start, e1 = (hipEvent_t)ev_stop;
   if (p.dtype == SV_DTYPE_BF16) {
-    if (vec) launch_timed(k_fused<SV_DTYPE_BF16, true>, dim3(grid), p, s, e0, e1);
-    else launch_timed(k_fused<SV_DTYPE_BF16, false>, dim3(grid), p, s, e0, e1);
+    if (vec) fused_dispatch<SV_DTYPE_BF16, true>(p, dim3(grid), s, e0, e1);
+    else fused_dispatch<SV_DTYPE_BF16, false>(p, dim3(grid), s, e0, e1);
   } else {
-    if (vec) launch_timed(k_fused<SV_DTYPE_F32, true>, dim3(grid), p, s, e0, e1);
-    else launch_timed(k_fused<SV_DTYPE_F32, false>, dim3(grid), p, s, e0, e1);
+    if (vec) fused_dispatch<SV_DTYPE_F32, true>(p, dim3(grid), s, e0, e1);
+    else fused_dispatch<SV_DTYPE_F32, false>(p, dim3(grid), s, e0, e1);
   }
   return (int)hipGetLastError();
 }

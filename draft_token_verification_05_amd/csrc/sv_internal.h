@@ -22,6 +22,7 @@ constexpr int kSelCache = 256;   // draw records a token selection keeps in LDS
 constexpr int kLdsBatch = 1024;  // batches up to this size scan their offsets in LDS (no prep kernel)
 constexpr int kFusedItemsPerWg = 64;  // longest statistics pass (items per resident workgroup) run in one dispatch
 constexpr int kFusedPerCu = 4;        // resident workgroups per compute unit of the single dispatch
+constexpr int kFusedNodes = 257;      // tree / block requests of the single dispatch: at most 256 positions
 // per-request arrival counters sit 256 bytes apart: increments of different
 // requests' counters would otherwise queue behind each other on one line
 constexpr int kCntStride = 64;     // in 32-bit words (KL second-pass counters)
@@ -47,20 +48,19 @@ constexpr int64_t chunk_t(int dtype) { return (int64_t)kThreads * kUT * elems_pe
 enum TermKind : int32_t { kTermNone = 0, kTermResidual = 1, kTermBonus = 2 };
 
 // Partial statistics of one task over the vocabulary chunks one workgroup of
-// the statistics pass streamed.  The single dispatch (whose helpers read the
-// partials during the same dispatch) stores the same 48 bytes as six
-// self-tagged 64-bit words instead (m_t, s_t low and high half, m_d, s_d low
-// and high half, each (epoch << 32) | 32-bit payload).  m_* are raw-logit maxima, s_* = sum
+// the statistics pass streamed.  m_* are raw-logit maxima, s_* = sum
 // 2^((x - m) L) with L = log2(e)/T, w = sum 2^((d - m_d) L) (d - t) and
 // z = sum 2^((d - m_d) L) |d - t| over the draft row, idx = lowest index
-// attaining m_t.  tag: the call's epoch, stored after the other fields by the
-// fused kernel, whose helpers read a partial only once it carries the epoch of
-// their own call.
+// attaining m_t.  The single dispatch (whose helpers read the partials during
+// the same dispatch) stores self-tagged 64-bit words, (epoch << 32) | 32-bit
+// payload, in the same 48 bytes instead: six for a stochastic pair (m_t, s_t
+// low and high half, m_d, s_d low and high half), two for a greedy-family row
+// (m_t, idx).
 struct PartA {
   double s_t, s_d, w, z;
   float m_t, m_d;
   int32_t idx;
-  uint32_t tag;
+  uint32_t pad;
 };
 
 // A position queued for the KL second pass, with the constants of its terms:
@@ -187,7 +187,7 @@ struct Params {
   int32_t want_kl;  // compute KL(q || p) (NKL mode, or stochastic with out_nkl)
   int32_t block_min_len;  // block-accept mode: shortest kept run (>= 1)
   uint32_t epoch;      // this call's tag: fused statistics partials and arrival counters (never 0 or ~0)
-  int32_t wait_polls;  // fused kernel: polls of a partial before a helper computes it itself
+  int32_t wait_polls;  // single dispatch: polls of a partial before a helper computes it itself
   // workspace
   int32_t* hdr;  // hdr[0]: layout error flag, hdr[1]: positions queued for the KL second pass
   int32_t* d_off;
@@ -234,8 +234,9 @@ int launch_stats(const Params& p, bool vec, void* stream, void* ev_start, void* 
 int launch_decide(const Params& p, bool vec, void* stream);
 // KL second pass over the queue k_decide fills (NKL mode, or stochastic with out_nkl)
 int launch_refine(const Params& p, bool vec, void* stream);
-// One kernel for the whole stochastic step (batches up to kLdsBatch, no KL
-// output, a short statistics pass): plan_fused fills p.stats_grid,
+// One kernel for the whole step (batches up to kLdsBatch, a short statistics
+// pass, not NKL mode and no KL output; tree and block requests of at most
+// kFusedNodes - 1 positions): plan_fused fills p.stats_grid,
 // p.grp_log2, p.nslices, p.helpers and p.slices_per_helper and returns the
 // grid, or 0 when the step should take the separate kernels; launch_fused
 // enqueues it.

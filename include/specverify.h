@@ -195,11 +195,13 @@ const char* spec_verify_status_string(int status);
 /* SPECVERIFY_VERSION of the loaded library. */
 int spec_verify_version(void);
 
-/* 1 if spec_verify would run this configuration as one kernel dispatch (the
- * stochastic mode with batch <= 1024, out_nkl == NULL when with_nkl == 0, and a
- * short statistics pass), 0 if as separate kernels, SV_EINVAL for an invalid
- * cfg or mode.  Reads batch, vocab, dtype, total_draft_rows and the device's
- * compute-unit count (the current device); enqueues nothing.  For timing and
+/* 1 if spec_verify would run this configuration as one kernel dispatch (batch
+ * <= 1024 and a short statistics pass, in the stochastic mode with out_nkl ==
+ * NULL (with_nkl == 0), the greedy mode, or the tree and block modes with
+ * max_gamma <= 256; never in the NKL mode), 0 if as separate kernels,
+ * SV_EINVAL for an invalid cfg or mode.  Reads batch, vocab, dtype, max_gamma,
+ * total_draft_rows and the device's compute-unit count (the current device);
+ * enqueues nothing.  For timing and
  * profiling tools: phase_events [1] and [2] bracket that single dispatch, or
  * else the row-statistics dispatch. */
 int spec_verify_single_dispatch(const sv_config* cfg, int32_t mode, int32_t with_nkl);

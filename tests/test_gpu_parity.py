@@ -573,7 +573,7 @@ def test_losslessness_chi_square_gpu():
 def test_single_dispatch_choice():
     """Statistics passes of up to 64 items per resident workgroup (the
     Llama-3-shaped batch: 5, the ragged B=256 batch: 41) run as one dispatch;
-    longer ones and the KL output as separate kernels."""
+    longer ones, the KL output and NKL mode as separate kernels."""
     import draft_token_verification_05_amd as sv
     llama = sv.make_config(32, 128256, sv.SV_DTYPE_BF16, 5, 160)
     assert sv.spec_verify_single_dispatch(llama, S) == 1
@@ -583,6 +583,47 @@ def test_single_dispatch_choice():
     assert sv.spec_verify_single_dispatch(ragged, S) == 1
     long_pass = sv.make_config(1024, 152064, sv.SV_DTYPE_BF16, 16, 1024 * 16)  # ~300 items per workgroup
     assert sv.spec_verify_single_dispatch(long_pass, S) == 0
+    # the greedy family too; NKL never (its KL second pass is a kernel of its own)
+    long_drafts = sv.make_config(64, 128256, sv.SV_DTYPE_BF16, 16, 64 * 16)
+    for mode in (G, TR, BL):
+        assert sv.spec_verify_single_dispatch(long_drafts, mode) == 1, mode
+    assert sv.spec_verify_single_dispatch(long_drafts, K) == 0
+    # tree and block requests of more than 256 positions take the separate kernels
+    for mode in (TR, BL):
+        assert sv.spec_verify_single_dispatch(sv.make_config(4, 1000, sv.SV_DTYPE_F32, 256, 40), mode) == 1
+        assert sv.spec_verify_single_dispatch(sv.make_config(4, 1000, sv.SV_DTYPE_F32, 257, 40), mode) == 0
+    assert sv.spec_verify_single_dispatch(sv.make_config(4, 1000, sv.SV_DTYPE_F32, 4000, 40), G) == 1
+
+
+@pytest.mark.parametrize("mode", [G, TR, BL])
+@pytest.mark.parametrize("V,dtype", [(128256, "bf16"), (4099, "f32")])
+def test_greedy_family_recomputed_partials_bit_identical(mode, V, dtype):
+    """The greedy family's single dispatch: a helper that stops waiting after
+    one poll computes the missing (max, argmax) partials itself; the outputs
+    are bit-identical to a call that found them all, and match the oracle."""
+    w = synthetic.random_workload(seed=90 + mode + V % 5, mode=mode, B=24, V=V, dtype=dtype, gmax=9, gmin=0,
+                                  greedy_drafts=True, sigma=0.3, tree=mode == TR)
+    d = to_device(w)
+    a = run_gpu(w, d)
+    b = run_gpu(w, d, wait_polls=1)
+    for k in ("tokens", "num", "tree_node"):
+        assert np.array_equal(a[k], b[k]), k
+    rep = compare(w, b, oracle.verify_workload(w))
+    print(f"[parity]   wait_polls=1 {rep}", flush=True)
+    assert_parity(rep, mode)
+
+
+@pytest.mark.parametrize("gmax", [256, 257])
+@pytest.mark.parametrize("mode", [TR, BL])
+def test_tree_and_block_at_the_single_dispatch_node_bound(mode, gmax):
+    """Requests of up to 256 positions (257 tree nodes) run in the single
+    dispatch, which keeps one entry per node in LDS; a larger max_gamma takes
+    the separate kernels.  Both match the oracle."""
+    w = synthetic.random_workload(seed=95 + gmax + mode, mode=mode, B=3, V=1000, dtype="f32", gmax=gmax,
+                                  gmin=gmax - 1, greedy_drafts=True, sigma=0.2, tree=mode == TR)
+    g, o, _ = check(w)
+    if mode == TR:
+        assert (g["tree_node"] == o.tree_node).all()
 
 
 @pytest.mark.parametrize("V,dtype", [(128256, "bf16"), (4099, "f32"), (8193, "bf16")])
