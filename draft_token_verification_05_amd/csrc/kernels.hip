@@ -1129,10 +1129,11 @@ __device__ __forceinline__ Merged merge_task(const Params& p, int64_t task, bool
 // fused kernel: the wait of a helper for its request's statistics
 // ----------------------------------------------------------------------------
 
-// Partial of segment `seg` of stochastic task `task` (the chunks of the task
-// that statistics workgroup w_lo(task) + seg streams), computed again by the
-// calling workgroup with the same chunk order, lane mapping and reduction as
-// the statistics pass, so it is bit-identical to the original: left in
+// Partial of segment `seg` of task `task` (a stochastic pair or a
+// greedy-family row; the chunks of the task that statistics workgroup
+// w_lo(task) + seg streams), computed again by the calling workgroup with the
+// same chunk order, lane mapping and reduction as the statistics pass, so it
+// is bit-identical to the original: left in
 // sh.scratch and published as self-tagged words.  All threads call.
 template <int DT, bool VEC, int MODE>
 __device__ void recompute_segment(const Params& p, StatsShared& sh, int task, int seg) {
@@ -1833,8 +1834,9 @@ __device__ __forceinline__ void kl_finish(const Params& p, int b, const ReqFin& 
 // The decision and terminal draw of request b by its helper h.  ok: the
 // packed layout is valid; d0, d1: the request's draft-row offsets; T, ur: its
 // temperature and resample uniform (ur is first used after the decision, so
-// its load may still be in flight).  FUSED (stochastic): called in the
-// statistics kernel itself, where it waits for the request's partials.
+// its load may still be in flight).  FUSED (any mode but NKL): called in the
+// statistics kernel itself, where it waits for the request's partials.  TS:
+// the tree / block decision scratch, sized for the call's requests.
 // POS (NKL): per-position thresholds from generation positions.
 template <int DT, bool VEC, int MODE, bool FUSED, bool POS = false, class TS>
 __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bool ok, int d0, int d1, float T,
