@@ -1894,7 +1894,9 @@ __device__ __forceinline__ void decide_request(const Params& p, int b, int h, bo
     if ((tid & (S - 1)) == 0 && MODE != SV_MODE_TREE_GREEDY && ti < g) {
       ps.x = p.tokens[d0 + ti];
       const bool xok = ps.x >= 0 && ps.x < p.V;
-      if (SOFT && xok) {
+      // the logits at the drafted token: the stochastic test, and p(x), q(x)
+      // when asked for (the NKL decision does not use them)
+      if (SOFT && xok && (MODE == SV_MODE_STOCHASTIC || p.out_p_x || p.out_q_x)) {
         ps.tx = load_scalar<DT>(p.target, t0 + ti, V, ps.x);
         ps.dx = load_scalar<DT>(p.draft, d0 + ti, V, ps.x);
       }
