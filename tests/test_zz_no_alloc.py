@@ -33,7 +33,7 @@ def _outputs(sv, entry, w, d, workspace=None):
     return (out_tokens.cpu().numpy(), out_num.cpu().numpy(), None if out_nkl is None else out_nkl[:R_d].cpu().numpy())
 
 
-@pytest.mark.parametrize("mode", [0, 1, 2, 3])
+@pytest.mark.parametrize("mode", [0, 1, 2, 3, 4])
 def test_noalloc_equals_spec_verify_twice_second_smaller(mode):
     import torch
     import draft_token_verification_05_amd as sv
@@ -42,7 +42,7 @@ def test_noalloc_equals_spec_verify_twice_second_smaller(mode):
     else:
         big = synthetic.make_llama3().with_mode(mode)   # stochastic: the single dispatch
         small = synthetic.random_workload(seed=201 + mode, mode=mode, B=7, V=20000, dtype="f32", gmax=5, gmin=0,
-                                          greedy_drafts=(mode == 1))
+                                          greedy_drafts=(mode in (1, 4)))
     for w in (big, small):
         print(f"[noalloc] mode={mode} B={w.batch} V={w.vocab} R_d={w.total_draft_rows}", flush=True)
         d = to_device(w)
