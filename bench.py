@@ -548,7 +548,7 @@ def main():
         print(json.dumps({"calib_copy_bytes": args.calib_copy << 20, "launches": 10}), flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the benchmark runs on one GPU only; --gpus {args.gpus} is not supported "
               "(requests are independent, so more GPUs would each run their own share).", file=sys.stderr)
         sys.exit(2)
     if args.workload == "consensus":
