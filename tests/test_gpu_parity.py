@@ -311,6 +311,19 @@ def test_batch_above_lds_scan(mode):
     check(w, out_nkl=(mode == S))
 
 
+@pytest.mark.parametrize("mode", [S, G, TR, BL])
+def test_single_dispatch_at_the_largest_lds_batch(mode):
+    """1024 requests, the most the single dispatch takes: one helper role per
+    request (per slice in stochastic mode) on a grid of at least 1024
+    workgroups, every request's offsets from each helper's own LDS scan."""
+    import draft_token_verification_05_amd as sv
+    w = synthetic.random_workload(seed=41 + mode, mode=mode, B=1024, V=1500, dtype="bf16", gmax=3, gmin=0,
+                                  tree=(mode == TR), greedy_drafts=(mode in (G, BL)))
+    cfg = sv.make_config(w.batch, w.vocab, sv.SV_DTYPE_BF16, w.max_gamma, w.total_draft_rows)
+    assert sv.spec_verify_single_dispatch(cfg, mode) == 1
+    check(w)
+
+
 @pytest.mark.parametrize("mode", [S, G, K])
 def test_long_draft_several_decision_passes(mode):
     """Drafts longer than one decision pass (hundreds of positions): the
