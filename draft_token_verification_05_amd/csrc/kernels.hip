@@ -968,10 +968,10 @@ __device__ __forceinline__ bool stats_phase(const Params& p, StatsShared& sh) {
     lane_reset(L);
   };
   // issue priorities by remaining work: always in the soft modes; in the
-  // greedy family only for the single dispatch's longer shares (measured: the
-  // separate greedy pass, and single-dispatch shares of a few items, stream
-  // faster without)
-  const bool paced = SOFT || (FUSED && tot >= 4);
+  // greedy family only for the single dispatch's shares of five items or more
+  // (measured: the separate greedy pass, and single-dispatch shares of four
+  // items or fewer, stream faster without)
+  const bool paced = SOFT || (FUSED && tot >= 5);
   for (;;) {
     dB = dA;
     if (i + 1 < i_end) next_desc<MODE, LDS>(p, sh, b, dB);
